@@ -1,0 +1,99 @@
+"""Offline learning of patterns and codebooks (oracle; test infrastructure only).
+
+The pages: patterns and codebooks are learned once, offline, on calibration
+data (Ecco review, "Load-bearing premise"; "Assumptions & free parameters":
+S = 64 patterns and H = 4 codebooks per pattern chosen by design-space
+exploration, 15 centroids per pattern).  How codebooks are learned is not
+stated; neither is the length-limiting construction (referee report, major
+comment 1).
+
+Readings (the plainest ones consistent with the encoder):
+  1. normalise each group exactly as the encoder does (scale element, FP8
+     group scale, a = |S|) and keep the other 127 values divided by a;
+  2. exact 1-D k-means (15 clusters) of each group's normalised values;
+  3. Lloyd k-means (K = 64, k-means++ start) of the sorted 15-vectors; the
+     means of sorted vectors are sorted; round to FP16, sort, clamp to [-1, 1];
+  4. assign the training groups with the encoder's own min/max rule and
+     quantiser, and count symbols per group;
+  5. per pattern, 4 codebooks by Lloyd iterations on code length: start from
+     the entropy quartiles of the pattern's groups, give each codebook the
+     optimal 2..8-bit lengths for its summed counts plus one, move every group
+     to the codebook that codes it shortest (lowest id on ties), repeat until
+     nothing moves; a pattern no group uses gets all lengths 4.
+"""
+
+import numpy as np
+
+from . import fp
+from .codec import Tables, encode_groups, tensor_scale, GROUP, N_CENTROIDS
+from .huffman import limited_lengths
+from .kmeans import kmeans_1d_exact, lloyd
+
+
+def normalised_groups(x, t):
+    """x [G,128] float16 -> [G,127] float64 values divided by the group scale a.
+    Groups with a == 0 are dropped."""
+    x32 = x.astype(np.float32)
+    G = x32.shape[0]
+    rows = np.arange(G)
+    inv_t = np.float32(np.float32(1.0) / np.float32(t))
+    istar = np.argmax(np.abs(x32), axis=1)
+    s8 = fp.fp8_encode((x32[rows, istar] * inv_t).astype(np.float32))
+    a = np.abs((fp.fp8_decode(s8) * np.float32(t)).astype(np.float32)).astype(np.float64)
+    keep = a > 0
+    mask = np.ones_like(x32, dtype=bool)
+    mask[rows, istar] = False
+    others = x32[mask].reshape(G, GROUP - 1).astype(np.float64)
+    return others[keep] / a[keep, None]
+
+
+def _entropy(counts):
+    p = counts / np.maximum(counts.sum(axis=-1, keepdims=True), 1)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        return -np.sum(np.where(p > 0, p * np.log2(p), 0.0), axis=-1)
+
+
+def learn_codebooks(counts, n_codebooks=4, iters=10):
+    """counts [N, 16] symbol counts of one pattern's groups -> [H, 16] lengths."""
+    N = counts.shape[0]
+    if N == 0:
+        return np.full((n_codebooks, 16), 4, dtype=np.uint8)
+    order = np.argsort(_entropy(counts.astype(np.float64)), kind="stable")
+    assign = np.empty(N, dtype=np.int64)
+    assign[order] = (np.arange(N) * n_codebooks) // N                # entropy quartiles
+    lengths = None
+    for _ in range(max(1, iters)):
+        lengths = np.array([limited_lengths(counts[assign == h].sum(axis=0) + 1)
+                            for h in range(n_codebooks)], dtype=np.int64)
+        cost = counts.astype(np.int64) @ lengths.T                    # [N, H]
+        new = np.argmin(cost, axis=1)
+        if np.array_equal(new, assign):
+            break
+        assign = new
+    return lengths.astype(np.uint8)
+
+
+def train_tables(sample_fp16, n_patterns=64, n_codebooks=4, kmeans_iters=25, huff_iters=10, seed=0):
+    """Learn Tables from an FP16 sample whose size is a multiple of 128."""
+    x = np.asarray(sample_fp16, dtype=np.float16).reshape(-1, GROUP)
+    amax = float(np.max(np.abs(x.astype(np.float32)))) if x.size else 0.0
+    t, _ = tensor_scale(amax)
+    y = normalised_groups(x, t)
+    if y.shape[0] == 0:
+        cent = np.tile(np.linspace(-1, 1, N_CENTROIDS), (n_patterns, 1))
+    else:
+        vecs, _ = kmeans_1d_exact(y, N_CENTROIDS)
+        K = min(n_patterns, vecs.shape[0])
+        cent, _ = lloyd(vecs, K, kmeans_iters, seed)
+        if K < n_patterns:                                            # tiny samples
+            cent = np.concatenate([cent, np.repeat(cent[-1:], n_patterns - K, axis=0)])
+    cent = np.clip(np.sort(cent.astype(np.float16).astype(np.float32), axis=1), -1.0, 1.0)
+    cent = cent.astype(np.float16).astype(np.float32)
+    flat = Tables(cent, np.full((n_patterns, n_codebooks, 16), 4, dtype=np.uint8))
+    _, info = encode_groups(x, flat, t, return_info=True)
+    counts = np.zeros((x.shape[0], 16), dtype=np.int64)
+    np.add.at(counts, (np.repeat(np.arange(x.shape[0]), GROUP), info["sym"].ravel()), 1)
+    code_len = np.zeros((n_patterns, n_codebooks, 16), dtype=np.uint8)
+    for p in range(n_patterns):
+        code_len[p] = learn_codebooks(counts[info["p"] == p], n_codebooks, huff_iters)
+    return Tables(cent, code_len)

@@ -1,0 +1,169 @@
+"""Seeded synthetic inputs shaped like the workloads the Ecco pages evaluate on.
+
+The pages measure on LLaMA / LLaMA-2 / LLaMA-3.1 / Mistral weights and KV
+caches, calibrated on The Pile and evaluated on WikiText-2 (Ecco review,
+"Assumptions & free parameters"; referee report).  Neither trained weights nor
+datasets are available, so these generators stand in for them with the shapes
+of a LLaMA-3-8B decoder layer, a GQA KV cache and 70B-shaped FFN matrices, and
+with heavy-tailed value distributions (per-channel scales, sparse large
+outliers, outlier channels in K).
+
+This module holds no arithmetic of the codec: it only draws numbers.  Every
+tensor is drawn on the CPU with a seeded ``torch.Generator`` in float32 and
+cast to float16 with round-to-nearest-even, so both the GPU path and the CPU
+oracle see identical inputs on any machine.
+"""
+
+import numpy as np
+import torch
+
+GROUP = 128
+
+# LLaMA-3-8B decoder layer, weights [out, in]
+LLAMA3_8B_LAYER = {
+    "q": (4096, 4096),
+    "k": (1024, 4096),
+    "v": (1024, 4096),
+    "o": (4096, 4096),
+    "gate": (14336, 4096),
+    "up": (14336, 4096),
+    "down": (4096, 14336),
+}
+LAYER_ORDER = ["q", "k", "v", "o", "gate", "up", "down"]
+
+# 70B-shaped FFN matrices for the fused decode+GEMV
+FFN70B = {"w1": (28672, 8192), "w2": (8192, 28672)}
+
+# KV cache [batch, kv_heads, seq, head_dim]
+KV_SHAPE = (16, 8, 8192, 128)
+KV_APPEND = 256
+
+
+def _gen(seed):
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    return g
+
+
+def _laplace(n, scale, g):
+    u = torch.rand(n, generator=g, dtype=torch.float64) - 0.5
+    return (-scale * torch.sign(u) * torch.log1p(-2.0 * u.abs())).to(torch.float32)
+
+
+def _outlier_index(n, frac, g):
+    m = int(round(frac * n))
+    return torch.randperm(n, generator=g)[:m]
+
+
+def c1_weight(seed=0, shape=(1024, 1024), std=0.02, frac=0.001, lap_scale=0.2):
+    """Single weight matrix: N(0, std) with a fraction of entries replaced by
+    Laplace(0, lap_scale) draws."""
+    g = _gen(seed)
+    n = shape[0] * shape[1]
+    w = torch.randn(n, generator=g, dtype=torch.float32) * std
+    idx = _outlier_index(n, frac, g)
+    w[idx] = _laplace(idx.numel(), lap_scale, g)
+    return w.reshape(shape).to(torch.float16)
+
+
+def c1_sample(seed=1, n_values=1 << 20):
+    """Calibration sample for c1_weight (same recipe, separate seed)."""
+    return c1_weight(seed=seed, shape=(n_values // 1024, 1024))
+
+
+def llama_matrix(shape, seed, sigma=0.5, frac=0.0005, boost=20.0):
+    """W = s_o * z with per-output-row s_o ~ LogNormal(0, sigma), z ~ N(0, 1),
+    then a fraction of entries multiplied by `boost`."""
+    g = _gen(seed)
+    out_f, in_f = shape
+    s = torch.exp(sigma * torch.randn(out_f, 1, generator=g, dtype=torch.float32))
+    z = torch.randn(out_f, in_f, generator=g, dtype=torch.float32)
+    w = (s * z).reshape(-1)
+    idx = _outlier_index(w.numel(), frac, g)
+    w[idx] = w[idx] * boost
+    return w.reshape(shape).to(torch.float16)
+
+
+def llama_sample(in_features, seed, n_values=1 << 20):
+    """Calibration sample of the llama_matrix recipe with the given input width."""
+    rows = max(1, n_values // in_features)
+    return llama_matrix((rows, in_features), seed)
+
+
+def c2_layer(layer=0, names=None):
+    """One LLaMA-3-8B-shaped decoder layer; matrix m of layer l uses seed 100 + 10 l + m."""
+    names = names or LAYER_ORDER
+    return {nm: llama_matrix(LLAMA3_8B_LAYER[nm], 100 + 10 * layer + LAYER_ORDER.index(nm))
+            for nm in names}
+
+
+def c2_sample(name):
+    """Calibration sample for matrix type `name` (seed 900 + m)."""
+    m = LAYER_ORDER.index(name)
+    return llama_sample(LLAMA3_8B_LAYER[name][1], 900 + m)
+
+
+def kv_tensor(kind, shape=KV_SHAPE, seed=None, outlier_seed=2, n_outlier_ch=4, boost=10.0):
+    """K or V cache [B, H, S, D]: N(0, 1); K gets n_outlier_ch fixed channels per
+    kv-head scaled by `boost`."""
+    if seed is None:
+        seed = 0 if kind == "k" else 1
+    g = _gen(seed)
+    B, H, S, D = shape
+    x = torch.randn(shape, generator=g, dtype=torch.float32)
+    if kind == "k":
+        go = _gen(outlier_seed)
+        for hh in range(H):
+            ch = torch.randperm(D, generator=go)[:n_outlier_ch]
+            x[:, hh, :, ch] *= boost
+    return x.to(torch.float16)
+
+
+def kv_sample(kind, n_vectors=8192):
+    """Calibration sample for the KV codec: n_vectors head vectors of the same
+    recipe (seed 3 for K, 4 for V), with the same outlier channels."""
+    seed = 3 if kind == "k" else 4
+    B, H, S, D = KV_SHAPE
+    s = max(1, n_vectors // H)
+    return kv_tensor(kind, shape=(1, H, s, D), seed=seed)
+
+
+def c5_matrix(name):
+    return llama_matrix(FFN70B[name], 500 if name == "w1" else 501)
+
+
+def c5_sample(name):
+    return llama_sample(FFN70B[name][1], 510 if name == "w1" else 511)
+
+
+def c5_x(batch, in_features, seed=502):
+    g = _gen(seed)
+    return torch.randn(batch, in_features, generator=g, dtype=torch.float32).to(torch.float16)
+
+
+def random_blocks(n_blocks, seed):
+    """Uniformly random 512-bit blocks (decoder totality checks)."""
+    g = _gen(seed)
+    return torch.randint(0, 256, (n_blocks, 64), generator=g, dtype=torch.int64).to(torch.uint8)
+
+
+def random_groups(n_groups, seed, kind="normal"):
+    """Small assorted groups for parity sweeps: normal, heavy-tailed or special."""
+    g = _gen(seed)
+    if kind == "normal":
+        x = torch.randn(n_groups, GROUP, generator=g, dtype=torch.float32)
+    elif kind == "laplace":
+        x = _laplace(n_groups * GROUP, 1.0, g).reshape(n_groups, GROUP)
+    elif kind == "wide":
+        e = torch.randint(-20, 12, (n_groups, GROUP), generator=g).to(torch.float32)
+        x = torch.randn(n_groups, GROUP, generator=g, dtype=torch.float32) * torch.exp2(e)
+    else:
+        raise ValueError(kind)
+    return x.to(torch.float16)
+
+
+def as_numpy(t):
+    return t.contiguous().numpy()
+
+
+__all__ = [n for n in dir() if not n.startswith("_")]
