@@ -1,0 +1,199 @@
+"""Python binding of libecco, the MI355X (gfx950) Ecco block codec.
+
+A thin ctypes layer over the C ABI declared in include/ecco.h: every function
+here has the name of the C entry point it calls and only marshals arguments
+(NumPy arrays and torch tensors to pointers, the current torch stream to a
+hipStream_t).  All codec work runs in the library's HIP kernels; if the
+shared library is missing or fails to load, every call raises.
+
+Device buffers are torch CUDA tensors (device memory and streams are the only
+things torch is used for).
+"""
+
+import ctypes
+import os
+
+import numpy as np
+
+__all__ = [
+    "EccoError", "lib", "library_path",
+    "ecco_tables_size", "ecco_tables_build", "ecco_tables_validate", "ecco_tables_get",
+    "ecco_train_patterns", "ecco_tensor_scale_from_amax", "ecco_amax", "ecco_encode",
+    "ecco_decode", "ecco_decode_gemv", "ecco_strerror", "ecco_version",
+    "STATS_FIELDS", "tables_to_device",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libecco.so")
+
+GROUP = 128
+BLOCK_BYTES = 64
+STATS_FIELDS = ("groups", "clipped_groups", "clipped_values", "padded_outliers", "pad_bits",
+                "fill_bits", "nonfinite_groups")
+
+_ERRORS = {0: "ECCO_OK", -1: "ECCO_EINVAL", -2: "ECCO_EALIGN", -3: "ECCO_ESIZE",
+           -4: "ECCO_ETABLES", -5: "ECCO_EHIP", -6: "ECCO_EDEVICE"}
+
+
+class EccoError(RuntimeError):
+    def __init__(self, code, where):
+        self.code = code
+        super().__init__("%s failed: %s (%s)" % (where, _ERRORS.get(code, code), ecco_strerror(code)))
+
+
+class TrainOpts(ctypes.Structure):
+    _fields_ = [("kmeans_iters", ctypes.c_uint32), ("huff_iters", ctypes.c_uint32),
+                ("seed", ctypes.c_uint64), ("max_groups", ctypes.c_uint32), ("threads", ctypes.c_uint32)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libecco (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(library_path):
+            raise ImportError("libecco.so is not built; run `python -m entropy_coded_group_amd.build`")
+        L = ctypes.CDLL(library_path)
+        vp, u64, i64, f32, i32 = ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int64, ctypes.c_float, ctypes.c_int
+        sig = {
+            "ecco_tables_size": (ctypes.c_size_t, []),
+            "ecco_tables_build": (i32, [vp, vp, vp]),
+            "ecco_tables_validate": (i32, [vp]),
+            "ecco_tables_get": (i32, [vp, vp, vp]),
+            "ecco_train_patterns": (i32, [vp, u64, vp, vp]),
+            "ecco_tensor_scale_from_amax": (f32, [f32]),
+            "ecco_amax": (i32, [vp, u64, vp, vp]),
+            "ecco_encode": (i32, [vp, u64, u64, u64, u64, vp, f32, vp, vp, vp]),
+            "ecco_decode": (i32, [vp, u64, u64, u64, u64, vp, f32, vp, vp]),
+            "ecco_decode_gemv": (i32, [vp, vp, f32, i64, i64, vp, i64, vp, vp]),
+            "ecco_strerror": (ctypes.c_char_p, [i32]),
+            "ecco_version": (ctypes.c_char_p, []),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(rc, where):
+    if rc != 0:
+        raise EccoError(rc, where)
+
+
+def _ptr(obj):
+    """Address of a torch tensor's data or of a NumPy array's buffer."""
+    if obj is None:
+        return None
+    if hasattr(obj, "data_ptr"):
+        return obj.data_ptr()
+    if isinstance(obj, np.ndarray):
+        if not obj.flags["C_CONTIGUOUS"]:
+            raise ValueError("array must be C-contiguous")
+        return obj.ctypes.data
+    if isinstance(obj, int):
+        return obj
+    raise TypeError("expected a torch tensor, NumPy array or address, got %r" % type(obj))
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+# ----------------------------------------------------------------- tables
+
+def ecco_tables_size():
+    return int(lib().ecco_tables_size())
+
+
+def ecco_tables_build(centroids, code_len):
+    """centroids [64, 15] float32, code_len [64, 4, 16] uint8 -> host blob (uint8 array)."""
+    c = np.ascontiguousarray(centroids, dtype=np.float32)
+    l = np.ascontiguousarray(code_len, dtype=np.uint8)
+    if c.shape != (64, 15) or l.shape != (64, 4, 16):
+        raise ValueError("bad table shapes")
+    blob = _aligned_host(ecco_tables_size())
+    _check(lib().ecco_tables_build(_ptr(c), _ptr(l), _ptr(blob)), "ecco_tables_build")
+    return blob
+
+
+def ecco_tables_validate(blob):
+    return int(lib().ecco_tables_validate(_ptr(np.ascontiguousarray(blob, dtype=np.uint8))))
+
+
+def ecco_tables_get(blob):
+    c = np.zeros((64, 15), np.float32)
+    l = np.zeros((64, 4, 16), np.uint8)
+    _check(lib().ecco_tables_get(_ptr(np.ascontiguousarray(blob, dtype=np.uint8)), _ptr(c), _ptr(l)),
+           "ecco_tables_get")
+    return c, l
+
+
+def ecco_train_patterns(sample_fp16, kmeans_iters=25, huff_iters=10, seed=0, max_groups=0, threads=0):
+    """Learn a host blob from an FP16 sample (NumPy float16/uint16 or CPU torch tensor)."""
+    if hasattr(sample_fp16, "numpy"):
+        sample_fp16 = sample_fp16.contiguous().numpy()
+    s = np.ascontiguousarray(sample_fp16).view(np.uint16).ravel()
+    opts = TrainOpts(kmeans_iters, huff_iters, seed, max_groups, threads)
+    blob = _aligned_host(ecco_tables_size())
+    _check(lib().ecco_train_patterns(_ptr(s), s.size, ctypes.byref(opts), _ptr(blob)), "ecco_train_patterns")
+    return blob
+
+
+def ecco_tensor_scale_from_amax(amax):
+    return float(np.float32(lib().ecco_tensor_scale_from_amax(float(amax))))
+
+
+def _aligned_host(n, align=256):
+    raw = np.zeros(n + align, np.uint8)
+    off = (-raw.ctypes.data) % align
+    return raw[off:off + n]
+
+
+def tables_to_device(blob, device="cuda"):
+    """Copy a host blob into a fresh device tensor (torch allocations are 256-byte aligned)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(blob, dtype=np.uint8).copy()).to(device)
+    if t.data_ptr() % 256:
+        raise RuntimeError("device allocation not 256-byte aligned")
+    return t
+
+
+# ----------------------------------------------------------------- device
+
+def ecco_amax(x, n_values, amax_out, stream=None):
+    _check(lib().ecco_amax(_ptr(x), int(n_values), _ptr(amax_out), _stream(stream)), "ecco_amax")
+
+
+def ecco_encode(x, n_rows, groups_per_row, x_row_stride_elems, blk_row_stride_blocks, tables_dev,
+                tensor_scale, blocks, stats=None, stream=None):
+    _check(lib().ecco_encode(_ptr(x), int(n_rows), int(groups_per_row), int(x_row_stride_elems),
+                             int(blk_row_stride_blocks), _ptr(tables_dev), float(tensor_scale), _ptr(blocks),
+                             _ptr(stats), _stream(stream)), "ecco_encode")
+
+
+def ecco_decode(blocks, n_rows, groups_per_row, blk_row_stride_blocks, y_row_stride_elems, tables_dev,
+                tensor_scale, y, stream=None):
+    _check(lib().ecco_decode(_ptr(blocks), int(n_rows), int(groups_per_row), int(blk_row_stride_blocks),
+                             int(y_row_stride_elems), _ptr(tables_dev), float(tensor_scale), _ptr(y),
+                             _stream(stream)), "ecco_decode")
+
+
+def ecco_decode_gemv(blocks, tables_dev, tensor_scale, out_features, in_features, x, batch, y, stream=None):
+    _check(lib().ecco_decode_gemv(_ptr(blocks), _ptr(tables_dev), float(tensor_scale), int(out_features),
+                                  int(in_features), _ptr(x), int(batch), _ptr(y), _stream(stream)),
+           "ecco_decode_gemv")
+
+
+def ecco_strerror(code):
+    return lib().ecco_strerror(int(code)).decode()
+
+
+def ecco_version():
+    return lib().ecco_version().decode()

@@ -1,0 +1,312 @@
+// Device helpers and the block-decode core shared by the decode and fused
+// decode+GEMV kernels of libecco (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "ecco_internal.h"
+
+namespace ecco {
+
+// ------------------------------------------------------------------ helpers
+
+__device__ __forceinline__ uint32_t lane_id() {
+  return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+}
+
+// Wave-level ordering of LDS traffic: all lanes of the wave reach this point
+// and their earlier LDS writes are visible to later LDS reads.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// DPP controls (GFX9 encoding)
+constexpr int kQuadXor1 = 0xB1;       // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;
+constexpr int kRowMirror = 0x140;
+constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __uint_as_float(dpp_u32<CTRL>(__float_as_uint(v)));
+}
+
+// All-reduce over the 16 lanes of a DPP row.
+__device__ __forceinline__ uint32_t row_max_u32(uint32_t v) {
+  v = max(v, dpp_u32<kQuadXor1>(v));
+  v = max(v, dpp_u32<kQuadXor2>(v));
+  v = max(v, dpp_u32<kRowHalfMirror>(v));
+  v = max(v, dpp_u32<kRowMirror>(v));
+  return v;
+}
+__device__ __forceinline__ uint32_t row_add_u32(uint32_t v) {
+  v += dpp_u32<kQuadXor1>(v);
+  v += dpp_u32<kQuadXor2>(v);
+  v += dpp_u32<kRowHalfMirror>(v);
+  v += dpp_u32<kRowMirror>(v);
+  return v;
+}
+__device__ __forceinline__ float row_min_f32(float v) {
+  v = fminf(v, dpp_f32<kQuadXor1>(v));
+  v = fminf(v, dpp_f32<kQuadXor2>(v));
+  v = fminf(v, dpp_f32<kRowHalfMirror>(v));
+  v = fminf(v, dpp_f32<kRowMirror>(v));
+  return v;
+}
+__device__ __forceinline__ float row_max_f32(float v) {
+  v = fmaxf(v, dpp_f32<kQuadXor1>(v));
+  v = fmaxf(v, dpp_f32<kQuadXor2>(v));
+  v = fmaxf(v, dpp_f32<kRowHalfMirror>(v));
+  v = fmaxf(v, dpp_f32<kRowMirror>(v));
+  return v;
+}
+template <int CTRL>
+__device__ __forceinline__ uint64_t min_u64_dpp(uint64_t v) {
+  uint32_t lo = dpp_u32<CTRL>((uint32_t)v), hi = dpp_u32<CTRL>((uint32_t)(v >> 32));
+  uint64_t o = ((uint64_t)hi << 32) | lo;
+  return o < v ? o : v;
+}
+__device__ __forceinline__ uint64_t row_min_u64(uint64_t v) {
+  v = min_u64_dpp<kQuadXor1>(v);
+  v = min_u64_dpp<kQuadXor2>(v);
+  v = min_u64_dpp<kRowHalfMirror>(v);
+  v = min_u64_dpp<kRowMirror>(v);
+  return v;
+}
+// Inclusive prefix sum over the 16 lanes of a row (Hillis-Steele).
+__device__ __forceinline__ uint32_t row_scan_add(uint32_t v) {
+  v += dpp_u32<kRowShr1>(v);
+  v += dpp_u32<kRowShr2>(v);
+  v += dpp_u32<kRowShr4>(v);
+  v += dpp_u32<kRowShr8>(v);
+  return v;
+}
+
+// OCP FP8 E4M3FN encode of a finite float: saturate to +-448, round to nearest
+// even (the subnormal grid is 2^-9); NaN gives 0x7F.
+__device__ __forceinline__ uint32_t fp8_encode(float v) {
+  uint32_t u = __float_as_uint(v);
+  uint32_t sign = (u >> 24) & 0x80u, a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return 0x7fu;
+  if (a >= 0x43e00000u) return sign | 0x7eu;
+  if (a < 0x3c800000u) return sign | (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
+  uint32_t r = a - (120u << 23);
+  r += 0x7ffffu + ((r >> 20) & 1u);
+  return sign | (r >> 20);
+}
+
+// FP16 <-> FP32 through the native half type: v_cvt_f16_f32 rounds to nearest
+// even, v_cvt_f32_f16 is exact.
+// The empty asm pins v as a rounded binary32 value: without it the compiler
+// may fuse a preceding multiply into v_fma_mixlo_f16, which rounds the exact
+// product to FP16 once instead of rounding to FP32 first as the format defines.
+__device__ __forceinline__ uint32_t f16_bits(float v) {
+  asm volatile("" : "+v"(v));
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v);
+}
+__device__ __forceinline__ float f16_value(uint32_t bits) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+}
+
+// 64-bit window shift: bits [r, r + 32) of hi:lo, r < 64.
+__device__ __forceinline__ uint32_t window(uint32_t lo, uint32_t hi, uint32_t r) {
+  return (uint32_t)((((uint64_t)hi << 32) | lo) >> r);
+}
+
+// Row / column of a linear group index by a precomputed reciprocal
+// (n / d = (n + umulhi(n, m)) >> s, exact for every 32-bit n).
+struct DivMagic {
+  uint32_t d, m, s;
+};
+inline __host__ DivMagic make_magic(uint32_t d) {
+  uint32_t s = 0;
+  while ((1ull << s) < d) ++s;
+  uint64_t M = ((1ull << (32 + s)) / d) + 1;     // in (2^32, 2^33]
+  return DivMagic{d, (uint32_t)(M - (1ull << 32)), s};
+}
+__device__ __forceinline__ uint32_t div_magic(uint32_t n, DivMagic q) {
+  return (uint32_t)(((uint64_t)n + __umulhi(n, q.m)) >> q.s);
+}
+
+
+// ------------------------------------------------------------- decode core
+//
+// One wavefront decodes a batch of up to 64 blocks.  Tables live in LDS for
+// the whole workgroup; every wave has a private staging area.
+
+constexpr int kDecWaves = 8;
+constexpr int kBlkStride = 17;                   // dwords per staged block: 16 + 1 pad (column reads hit 32 banks)
+constexpr int kBlkWords = 64 * kBlkStride + 48;  // slack for reads past the last block
+constexpr int kDeadLut = S * H * 256;            // byte offset of the all-"clipped" look-up table
+
+struct DecodeSmem {
+  uint8_t lut[S * H * 256 + 256];   // decode look-up tables + the clipped-stream table
+  float cent[S * 16];
+  float fp8[256];
+  uint32_t blk[kDecWaves][kBlkWords];   // staged blocks, later symbol bytes
+  uint32_t vtab[kDecWaves][64 * 16];    // per block: 32 FP16 reconstruction values
+  uint64_t aux[kDecWaves][64];          // per block: caller data (output offset)
+};
+
+__device__ __forceinline__ void stage_decode_tables(DecodeSmem& sm, const Tables* tab) {
+  const uint32_t tid = threadIdx.x;
+  const uint4* src = reinterpret_cast<const uint4*>(&tab->lut[0][0][0]);
+  uint4* dst = reinterpret_cast<uint4*>(sm.lut);
+  for (uint32_t i = tid; i < S * H * 256 / 16; i += blockDim.x) dst[i] = src[i];
+  // a clipped stream reads as symbol 16 ("+0" in a clipped block), one bit per step
+  if (tid < 16) dst[S * H * 256 / 16 + tid] = make_uint4(0x10101010u, 0x10101010u, 0x10101010u, 0x10101010u);
+  const float* c = &tab->centroids[0][0];
+  for (uint32_t i = tid; i < S * 16; i += blockDim.x) sm.cent[i] = c[i];
+  for (uint32_t i = tid; i < 256; i += blockDim.x) sm.fp8[i] = tab->fp8_value[i];
+  for (uint32_t i = tid; i < kDecWaves * kBlkWords; i += blockDim.x) (&sm.blk[0][0])[i] = 0;
+}
+
+// Decode one batch.
+//   n_valid          blocks 0..n_valid-1 of the batch exist
+//   load(b, q)       16-byte chunk q (0..3) of block b (only called for valid b)
+//   prep(b)          per-block caller value, kept in sm.aux (called by lane b)
+//   sink(b, tq, half, aux, v)   8 decoded FP16 values (v.x = values 0,1 ...) of
+//                    block b at positions 64 * half + 8 * tq .. + 7
+// Steps: coalesced load to LDS; each lane decodes one block's stream with the
+// 8-bit-window look-up table, four codewords per bit-window refill, and
+// detects a clipped stream; builds the block's value table (15 centroids * a,
+// the scale S, then up to 16 outlier values -- or +0 for a clipped block);
+// stages symbol bytes (outlier positions overwritten by 16 + r) in two halves
+// and hands 8 values per lane to the sink, 8 lanes per block.
+template <class Load, class Prep, class Sink>
+__device__ __forceinline__ void decode_batch(DecodeSmem& sm, uint32_t wave, uint32_t lane, uint32_t n_valid,
+                                             float t, Load load, Prep prep, Sink sink) {
+  uint32_t* blk = sm.blk[wave];
+  uint32_t* vt = sm.vtab[wave];
+  // 1. coalesced load: lane l takes 16 bytes of block l/4 + 16 i
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t b = (lane >> 2) + 16u * i, q = lane & 3u;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (b < n_valid) v = load(b, q);
+    uint32_t* d = blk + b * kBlkStride + 4u * q;
+    d[0] = v.x;
+    d[1] = v.y;
+    d[2] = v.z;
+    d[3] = v.w;
+  }
+  wave_sync();
+
+  // 2. lane-serial decode of block `lane`
+  const uint32_t* W = blk + lane * kBlkStride;
+  uint32_t lo = W[0], hi = W[1];
+  const uint32_t head = lo;
+  uint32_t lutb = ((head & 63u) * 4u + ((head >> 6) & 3u)) * 256u;   // lut[p][h]
+  uint32_t r = 16, kw = 2, lim = 512;
+  uint32_t E[32];
+#pragma unroll
+  for (int c = 0; c < 32; ++c) {
+    const uint32_t nxt = W[kw];
+    const uint32_t base = (kw - 2u) * 32u;
+    uint32_t x = window(lo, hi, r);
+    const uint32_t e0 = sm.lut[lutb + (x & 255u)];
+    const uint32_t r1 = r + (e0 >> 5) + 1u;
+    x = window(lo, hi, r1);
+    const uint32_t e1 = sm.lut[lutb + (x & 255u)];
+    const uint32_t r2 = r1 + (e1 >> 5) + 1u;
+    x = window(lo, hi, r2);
+    const uint32_t e2 = sm.lut[lutb + (x & 255u)];
+    const uint32_t r3 = r2 + (e2 >> 5) + 1u;
+    x = window(lo, hi, r3);
+    const uint32_t e3 = sm.lut[lutb + (x & 255u)];
+    const uint32_t r4 = r3 + (e3 >> 5) + 1u;
+    uint32_t ev = e0 | (e1 << 8) | (e2 << 16) | (e3 << 24);
+    if (base + r4 > lim) {
+      // a codeword of this chunk ends past bit 512: the stream is clipped here
+      const uint32_t m = (base + r1 > 512u ? 0x000000ffu : 0u) | (base + r2 > 512u ? 0x0000ff00u : 0u) |
+                         (base + r3 > 512u ? 0x00ff0000u : 0u) | 0xff000000u;
+      ev = (ev & ~m) | (0x10101010u & m);
+      lim = 0xffffffffu;
+      lutb = kDeadLut;
+    }
+    E[c] = ev;
+    const bool adv = r4 >= 32u;
+    lo = adv ? hi : lo;
+    hi = adv ? nxt : hi;
+    r = r4 & 31u;
+    kw += adv ? 1u : 0u;
+  }
+  const bool full = lim == 512u;
+  const uint32_t end = (kw - 2u) * 32u + r;
+  const uint32_t n = full ? min(16u, (512u - end) / 15u) : 0u;
+
+  // 3. value table: [0..14] fp16(c * a), [15] fp16(S), [16 + r] outlier r (or +0 if clipped)
+  const uint32_t p = head & 63u;
+  const float S = sm.fp8[(head >> 8) & 255u] * t;
+  const float aa = fabsf(S);
+  uint32_t vtab[16];
+  {
+    const float* cp = sm.cent + p * 16u;
+#pragma unroll
+    for (int s = 0; s < 15; s += 2) {
+      const float v0 = cp[s] * aa;
+      const float v1 = s + 1 < 15 ? cp[s + 1] * aa : S;
+      vtab[s / 2] = f16_bits(v0) | (f16_bits(v1) << 16);
+    }
+#pragma unroll
+    for (int i = 8; i < 16; ++i) vtab[i] = 0;
+  }
+  uint32_t jp[4] = {0, 0, 0, 0};               // outlier positions, byte r of jp[r / 4]
+#pragma unroll
+  for (int rr = 0; rr < 16; ++rr) {
+    if (!__any((uint32_t)rr < n)) break;
+    if ((uint32_t)rr < n) {
+      const uint32_t pos = 512u - 15u * (rr + 1);
+      const uint32_t wi = pos >> 5, sh = pos & 31u;
+      const uint32_t rec = window(W[wi], W[wi + 1], sh) & 0x7fffu;
+      const float v = sm.fp8[rec >> 7] * t;
+      vtab[8 + rr / 2] |= f16_bits(v) << (16 * (rr & 1));
+      jp[rr / 4] |= (rec & 127u) << (8 * (rr & 3));
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 16; i += 4)
+    *reinterpret_cast<uint4*>(vt + lane * 16 + i) = make_uint4(vtab[i], vtab[i + 1], vtab[i + 2], vtab[i + 3]);
+  if (lane < n_valid) sm.aux[wave][lane] = prep(lane);
+  wave_sync();
+
+  // 4. two halves of 64 symbols each
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    uint32_t* Wm = blk + lane * kBlkStride;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) Wm[i] = E[16 * half + i];
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      if ((uint32_t)rr < n) {
+        const uint32_t j = (jp[rr / 4] >> (8 * (rr & 3))) & 127u;
+        if ((j >> 6) == (uint32_t)half) reinterpret_cast<uint8_t*>(Wm)[j & 63u] = (uint8_t)(16 + rr);
+      }
+    }
+    wave_sync();
+#pragma unroll 2
+    for (int it = 0; it < 8; ++it) {
+      const uint32_t bl = it * 8u + (lane >> 3), tq = lane & 7u;
+      const uint32_t* sw = blk + bl * kBlkStride + 2u * tq;
+      const uint32_t s0 = sw[0], s1 = sw[1];
+      const uint16_t* tb = reinterpret_cast<const uint16_t*>(vt + bl * 16u);
+      uint4 o;
+      o.x = (uint32_t)tb[s0 & 31u] | ((uint32_t)tb[(s0 >> 8) & 31u] << 16);
+      o.y = (uint32_t)tb[(s0 >> 16) & 31u] | ((uint32_t)tb[(s0 >> 24) & 31u] << 16);
+      o.z = (uint32_t)tb[s1 & 31u] | ((uint32_t)tb[(s1 >> 8) & 31u] << 16);
+      o.w = (uint32_t)tb[(s1 >> 16) & 31u] | ((uint32_t)tb[(s1 >> 24) & 31u] << 16);
+      if (bl < n_valid) sink(bl, tq, (uint32_t)half, sm.aux[wave][bl], o);
+    }
+    wave_sync();
+  }
+}
+
+}  // namespace ecco

@@ -1,0 +1,438 @@
+// HIP kernels of libecco for gfx950 (MI355X) and the device entry points of
+// the C ABI.
+//
+// Method: the Ecco block codec (pith.science review of arXiv 2505.06901).
+// A group of 128 FP16 values becomes one self-contained 512-bit block: FP8
+// group scale, pattern id chosen by min/max comparison, codebook id, canonical
+// Huffman codewords of the 128 centroid indices, clipped at the block end or
+// followed by zero fill and 15-bit outlier records ("What carries the
+// argument"; "Core claim"; Fig. 4 caption; referee report major comment 1).
+//
+// Kernel design (the pages' decoder is a 64-way hardware unit; on a GPU the
+// parallelism comes from decoding many independent blocks at once):
+//   decode  one wavefront owns a batch of 64 blocks.  The batch is loaded with
+//           coalesced 16-byte loads into LDS; each lane then decodes one
+//           block's codeword stream through an 8-bit-window look-up table
+//           staged in LDS (all 256 codebooks, 64 KiB), four codewords per
+//           64-bit bit-window refill.  Symbols are written back to LDS and the
+//           wave turns around: eight lanes per block look up reconstruction
+//           values from a per-block 32-entry FP16 table (15 centroids * a, the
+//           scale, outliers) and write 128-bit stores.
+//   encode  sixteen lanes (one DPP row) per group, four groups per wave:
+//           row-wide max/min/argmin/sum/scan through DPP, LDS-resident
+//           thresholds for a branch-free binary search, codewords merged into
+//           the block with LDS atomic OR.
+//   amax    grid-stride max of |x|.
+// All floating-point steps that decide a bit of the output are single IEEE
+// binary32 operations (the library is built with -ffp-contract=off).
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+#include <mutex>
+
+#include "ecco_device.h"
+
+namespace ecco {
+
+// -------------------------------------------------------------------- decode
+
+struct DecodeArgs {
+  const uint8_t* blocks;
+  uint16_t* y;
+  const Tables* tab;
+  uint64_t blk_stride;   // blocks per row
+  uint64_t y_stride;     // elements per row
+  DivMagic gpr;          // groups per row
+  uint32_t n_groups;
+  uint32_t n_batches;
+  float t;
+  uint32_t contiguous;
+};
+
+__global__ __launch_bounds__(kDecWaves * 64) void decode_kernel(DecodeArgs a) {
+  __shared__ DecodeSmem sm;
+  stage_decode_tables(sm, a.tab);
+  __syncthreads();
+  const uint32_t lane = lane_id(), wave = threadIdx.x >> 6;
+  for (uint32_t batch = blockIdx.x * kDecWaves + wave; batch < a.n_batches; batch += gridDim.x * kDecWaves) {
+    const uint32_t g0 = batch * 64u;
+    const uint32_t n_valid = min(64u, a.n_groups - g0);
+    auto load = [&](uint32_t b, uint32_t q) -> uint4 {
+      const uint32_t gidx = g0 + b;
+      const uint8_t* src;
+      if (a.contiguous) {
+        src = a.blocks + (uint64_t)gidx * 64u;
+      } else {
+        const uint32_t r = div_magic(gidx, a.gpr), g = gidx - r * a.gpr.d;
+        src = a.blocks + ((uint64_t)r * a.blk_stride + g) * 64u;
+      }
+      return *reinterpret_cast<const uint4*>(src + 16u * q);
+    };
+    auto prep = [&](uint32_t b) -> uint64_t {
+      const uint32_t gidx = g0 + b;
+      if (a.contiguous) return (uint64_t)gidx * 128u;
+      const uint32_t r = div_magic(gidx, a.gpr), g = gidx - r * a.gpr.d;
+      return (uint64_t)r * a.y_stride + (uint64_t)g * 128u;
+    };
+    auto sink = [&](uint32_t, uint32_t tq, uint32_t half, uint64_t yoff, uint4 v) {
+      *reinterpret_cast<uint4*>(a.y + yoff + 64u * half + 8u * tq) = v;
+    };
+    decode_batch(sm, wave, lane, n_valid, a.t, load, prep, sink);
+  }
+}
+
+// -------------------------------------------------------------------- encode
+
+struct EncodeArgs {
+  const uint16_t* x;
+  uint8_t* blocks;
+  const Tables* tab;
+  ecco_stats_t* stats;
+  uint64_t x_stride;     // elements per row
+  uint64_t blk_stride;   // blocks per row
+  DivMagic gpr;
+  uint32_t n_groups;
+  uint32_t n_quads;      // groups / 4, rounded up
+  float t, inv_t;
+};
+
+constexpr int kEncWaves = 4;
+
+struct EncodeSmem {
+  float mid[S * 16];
+  float c0c14[S * 2];
+  uint32_t len4[S * A];
+  uint16_t enc[S * H * A];
+  float fp8[256];
+  float thr[kEncWaves][4][16];
+  uint32_t out[kEncWaves][4][16];
+};
+
+__global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(EncodeArgs a) {
+  __shared__ EncodeSmem sm;
+  const uint32_t tid = threadIdx.x;
+  for (uint32_t i = tid; i < S * 16; i += blockDim.x) sm.mid[i] = (&a.tab->midpoints[0][0])[i];
+  for (uint32_t i = tid; i < S * 2; i += blockDim.x) sm.c0c14[i] = (&a.tab->c0c14[0][0])[i];
+  for (uint32_t i = tid; i < S * A; i += blockDim.x) sm.len4[i] = (&a.tab->len4[0][0])[i];
+  for (uint32_t i = tid; i < S * H * A; i += blockDim.x) sm.enc[i] = (&a.tab->enc[0][0][0])[i];
+  for (uint32_t i = tid; i < 256; i += blockDim.x) sm.fp8[i] = a.tab->fp8_value[i];
+  __syncthreads();
+
+  const uint32_t lane = lane_id(), wave = tid >> 6;
+  const uint32_t q = lane >> 4, t16 = lane & 15u;
+  const float t = a.t, inv_t = a.inv_t;
+  float* thr = sm.thr[wave][q];
+  uint32_t* out = sm.out[wave][q];
+  // per-lane statistics (kept by lane t16 == 0 of each group)
+  uint64_t st_groups = 0, st_clip = 0, st_clipv = 0, st_pad = 0, st_fill = 0, st_nonfin = 0;
+
+  for (uint32_t quad = blockIdx.x * kEncWaves + wave; quad < a.n_quads; quad += gridDim.x * kEncWaves) {
+    const uint32_t gidx = quad * 4u + q;
+    const bool valid = gidx < a.n_groups;
+    uint32_t row = 0, col = 0;
+    if (valid) {
+      row = div_magic(gidx, a.gpr);
+      col = gidx - row * a.gpr.d;
+    }
+    uint4 raw = make_uint4(0, 0, 0, 0);
+    if (valid) raw = *reinterpret_cast<const uint4*>(a.x + (uint64_t)row * a.x_stride + (uint64_t)col * 128u + 8u * t16);
+    uint32_t hb[8] = {raw.x & 0xffffu, raw.x >> 16, raw.y & 0xffffu, raw.y >> 16,
+                      raw.z & 0xffffu, raw.z >> 16, raw.w & 0xffffu, raw.w >> 16};
+    float xf[8];
+    uint32_t key[8];
+    bool nonfin = false;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      xf[i] = f16_value(hb[i]);
+      nonfin |= (hb[i] & 0x7c00u) == 0x7c00u;
+      const uint32_t j = 8u * t16 + i;
+      key[i] = ((hb[i] & 0x7fffu) << 8) | ((127u - j) << 1) | (hb[i] >> 15);
+    }
+    // 1. scale element: largest |x|, lowest index on ties
+    uint32_t km = key[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) km = max(km, key[i]);
+    km = row_max_u32(km);
+    const uint32_t jstar = 127u - ((km >> 1) & 127u);
+    const float xs = f16_value((km >> 8) | ((km & 1u) << 15));
+    const uint32_t s8 = fp8_encode(xs * inv_t);
+    const float S = sm.fp8[s8] * t;
+    const float aa = fabsf(S);
+    // 2. min / max of the other 127 values
+    float mn = __builtin_inff(), mx = -__builtin_inff();
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (8u * t16 + i != jstar) {
+        mn = fminf(mn, xf[i]);
+        mx = fmaxf(mx, xf[i]);
+      }
+    }
+    mn = row_min_f32(mn);
+    mx = row_max_f32(mx);
+    // 3. pattern: min/max squared error, lowest p on ties
+    uint64_t best = ~0ull;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t p = t16 + 16u * k;
+      const float d1 = mn - sm.c0c14[2 * p] * aa;
+      const float d2 = mx - sm.c0c14[2 * p + 1] * aa;
+      const float f = d1 * d1 + d2 * d2;
+      const uint64_t kk = ((uint64_t)__float_as_uint(f) << 32) | p;
+      best = kk < best ? kk : best;
+    }
+    best = row_min_u64(best);
+    const uint32_t pstar = (uint32_t)best & 63u;
+    // 4. quantise: thresholds m_pk * a in LDS, binary search per value
+    thr[t16] = t16 < 14u ? sm.mid[pstar * 16u + t16] * aa : __builtin_inff();
+    wave_sync();
+    uint32_t sym[8];
+    uint32_t l4 = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint32_t idx = 0;
+      idx += xf[i] > thr[idx + 7] ? 8u : 0u;
+      idx += xf[i] > thr[idx + 3] ? 4u : 0u;
+      idx += xf[i] > thr[idx + 1] ? 2u : 0u;
+      idx += xf[i] > thr[idx] ? 1u : 0u;
+      sym[i] = (8u * t16 + i == jstar) ? 15u : idx;
+      l4 += sm.len4[pstar * 16u + sym[i]];
+    }
+    // 5. codebook with the shortest stream, lowest h on ties
+    uint32_t l02 = row_add_u32(l4 & 0x00ff00ffu), l13 = row_add_u32((l4 >> 8) & 0x00ff00ffu);
+    uint32_t Lh[4] = {l02 & 0xffffu, l13 & 0xffffu, l02 >> 16, l13 >> 16};
+    uint32_t hstar = 0, L = Lh[0];
+#pragma unroll
+    for (int h = 1; h < 4; ++h)
+      if (Lh[h] < L) { L = Lh[h]; hstar = h; }
+    // 6. codewords: lane-local concatenation, row scan for positions, OR into the block
+    uint64_t acc = 0;
+    uint32_t off = 0;
+    uint32_t ends = 0;                     // codewords of this lane ending within the block (stats)
+    const uint32_t eb = (pstar * 4u + hstar) * 16u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t e = sm.enc[eb + sym[i]];
+      acc |= (uint64_t)(e & 0xffu) << off;
+      off += e >> 8;
+    }
+    out[t16] = 0;
+    const uint32_t incl = row_scan_add(off);
+    const uint32_t pos = 16u + incl - off;
+    wave_sync();
+    {
+      // the lane's <= 64 bits land in words w, w + 1, w + 2; words past 15 are
+      // beyond bit 512 and dropped, which is exactly the clipping rule
+      const uint32_t w = pos >> 5, sh = pos & 31u;
+      const uint64_t low = acc << sh;
+      const uint32_t top = sh ? (uint32_t)(acc >> (64u - sh)) : 0u;
+      if (w < 16u && (uint32_t)low) atomicOr(&out[w], (uint32_t)low);
+      if (w + 1u < 16u && (uint32_t)(low >> 32)) atomicOr(&out[w + 1u], (uint32_t)(low >> 32));
+      if (w + 2u < 16u && top) atomicOr(&out[w + 2u], top);
+    }
+    const bool clipped = 16u + L > 512u;
+    const uint32_t n = clipped ? 0u : min(16u, (496u - L) / 15u);
+    // 7. outliers: n largest |x| (j != i*), lower j first on ties
+    if (8u * t16 <= jstar && jstar < 8u * t16 + 8u) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (8u * t16 + i == jstar) key[i] = 0;
+    }
+    uint32_t myrec = 0;
+    for (uint32_t rr = 0; rr < 16u; ++rr) {
+      if (!__any(rr < n)) break;
+      uint32_t m = key[0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) m = max(m, key[i]);
+      m = row_max_u32(m);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) key[i] = key[i] == m ? 0u : key[i];
+      if (t16 == rr) {
+        const uint32_t j = 127u - ((m >> 1) & 127u);
+        const float xv = f16_value((m >> 8) | ((m & 1u) << 15));
+        myrec = j | (fp8_encode(xv * inv_t) << 7);
+      }
+    }
+    if (t16 < n) {
+      const uint32_t rp = 497u - 15u * t16;
+      const uint32_t w = rp >> 5, sh = rp & 31u;
+      atomicOr(&out[w], myrec << sh);
+      if (sh > 17u) atomicOr(&out[w + 1u], myrec >> (32u - sh));
+    }
+    if (t16 == 0) atomicOr(&out[0], pstar | (hstar << 6) | (s8 << 8));
+    wave_sync();
+    if (valid) {
+      uint32_t* dst = reinterpret_cast<uint32_t*>(a.blocks + ((uint64_t)row * a.blk_stride + col) * 64u);
+      dst[t16] = out[t16];
+    }
+    if (a.stats) {
+      // whole codewords inside the block (k of a clipped group)
+      uint32_t e = pos;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        e += sm.enc[eb + sym[i]] >> 8;
+        ends += e <= 512u ? 1u : 0u;
+      }
+      const uint32_t k = row_add_u32(ends);
+      const uint32_t nf = row_max_u32(nonfin ? 1u : 0u);
+      if (valid && t16 == 0) {
+        st_groups += 1;
+        st_clip += clipped;
+        st_clipv += 128u - k;
+        st_pad += n;
+        st_fill += clipped ? 0u : (496u - L - 15u * n);
+        st_nonfin += nf;
+      }
+    }
+    wave_sync();
+  }
+  if (a.stats && t16 == 0 && st_groups) {
+    atomicAdd(&a.stats->groups, (unsigned long long)st_groups);
+    atomicAdd(&a.stats->clipped_groups, (unsigned long long)st_clip);
+    atomicAdd(&a.stats->clipped_values, (unsigned long long)st_clipv);
+    atomicAdd(&a.stats->padded_outliers, (unsigned long long)st_pad);
+    atomicAdd(&a.stats->pad_bits, (unsigned long long)(15u * st_pad));
+    atomicAdd(&a.stats->fill_bits, (unsigned long long)st_fill);
+    atomicAdd(&a.stats->nonfinite_groups, (unsigned long long)st_nonfin);
+  }
+}
+
+// ---------------------------------------------------------------------- amax
+
+__global__ void amax_init_kernel(float* out) { *out = 0.0f; }
+
+__global__ __launch_bounds__(256) void amax_kernel(const uint16_t* x, uint64_t n, float* out) {
+  uint32_t m = 0;
+  const uint64_t n8 = n / 8;
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8; i += stride) {
+    const uint4 v = reinterpret_cast<const uint4*>(x)[i];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      uint32_t a0 = w[k] & 0x7fffu, a1 = (w[k] >> 16) & 0x7fffu;
+      a0 = a0 > 0x7c00u ? 0u : a0;   // NaN ignored
+      a1 = a1 > 0x7c00u ? 0u : a1;
+      m = max(m, max(a0, a1));
+    }
+  }
+  for (uint64_t i = n8 * 8 + (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+    uint32_t a0 = x[i] & 0x7fffu;
+    m = max(m, a0 > 0x7c00u ? 0u : a0);
+  }
+  // wave reduction, then one atomic per wave (|x| bit patterns order like values)
+  for (int o = 32; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
+  if (lane_id() == 0 && m) {
+    const float f = f16_value(m);
+    atomicMax(reinterpret_cast<unsigned int*>(out), __float_as_uint(f));
+  }
+}
+
+}  // namespace ecco
+
+// ------------------------------------------------------------ entry points
+
+using namespace ecco;
+
+namespace {
+struct DeviceInfo {
+  int ok = 0;        // 1 gfx950, -1 other
+  int cus = 0;
+};
+std::mutex g_mu;
+DeviceInfo g_dev[64];
+int launch_status() { return hipGetLastError() == hipSuccess ? ECCO_OK : ECCO_EHIP; }
+}  // namespace
+
+namespace ecco {
+int check_gfx950(int* cus) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return ECCO_EHIP;
+  std::lock_guard<std::mutex> lk(g_mu);
+  DeviceInfo& d = g_dev[dev];
+  if (d.ok == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return ECCO_EHIP;
+    d.ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    d.cus = prop.multiProcessorCount;
+  }
+  if (d.ok != 1) return ECCO_EDEVICE;
+  *cus = d.cus;
+  return ECCO_OK;
+}
+}  // namespace ecco
+
+extern "C" int ecco_amax(const uint16_t* x, uint64_t n, float* amax, void* stream) {
+  if (!x || !amax) return ECCO_EINVAL;
+  if (n == 0) return ECCO_ESIZE;
+  if (!host_aligned(x, 16) || !host_aligned(amax, 4)) return ECCO_EALIGN;
+  int cus = 0, rc = check_gfx950(&cus);
+  if (rc) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(amax_init_kernel, dim3(1), dim3(1), 0, s, amax);
+  uint64_t want = (n / 8 + 255) / 256;
+  uint32_t grid = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(want, (uint64_t)cus * 8));
+  hipLaunchKernelGGL(amax_kernel, dim3(grid), dim3(256), 0, s, x, n, amax);
+  return launch_status();
+}
+
+extern "C" int ecco_encode(const uint16_t* x, uint64_t n_rows, uint64_t gpr, uint64_t x_stride,
+                           uint64_t blk_stride, const void* tables, float tensor_scale, void* blocks,
+                           ecco_stats_t* stats, void* stream) {
+  if (!x || !tables || !blocks) return ECCO_EINVAL;
+  if (!(tensor_scale > 0.0f) || !(tensor_scale < __builtin_huge_valf())) return ECCO_EINVAL;
+  const uint64_t total = n_rows * gpr;
+  if (n_rows == 0 || gpr == 0 || total >= (1ull << 32) || gpr >= (1ull << 32)) return ECCO_ESIZE;
+  if (n_rows > 1 && (x_stride < gpr * 128 || blk_stride < gpr)) return ECCO_ESIZE;
+  if (!host_aligned(x, 16) || (x_stride % 8) != 0 || !host_aligned(blocks, 64) || !host_aligned(tables, 256) ||
+      (stats && !host_aligned(stats, 8)))
+    return ECCO_EALIGN;
+  int cus = 0, rc = check_gfx950(&cus);
+  if (rc) return rc;
+  EncodeArgs a;
+  a.x = x;
+  a.blocks = static_cast<uint8_t*>(blocks);
+  a.tab = static_cast<const Tables*>(tables);
+  a.stats = stats;
+  a.x_stride = x_stride;
+  a.blk_stride = blk_stride;
+  a.gpr = make_magic((uint32_t)gpr);
+  a.n_groups = (uint32_t)total;
+  a.n_quads = (uint32_t)((total + 3) / 4);
+  a.t = tensor_scale;
+  volatile float inv = 1.0f / tensor_scale;
+  a.inv_t = inv;
+  uint32_t want = (a.n_quads + kEncWaves - 1) / kEncWaves;
+  uint32_t grid = std::max<uint32_t>(1, std::min<uint32_t>(want, (uint32_t)cus * 8));
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(encode_kernel, dim3(grid), dim3(kEncWaves * 64), 0, static_cast<hipStream_t>(stream), a);
+  return launch_status();
+}
+
+extern "C" int ecco_decode(const void* blocks, uint64_t n_rows, uint64_t gpr, uint64_t blk_stride,
+                           uint64_t y_stride, const void* tables, float tensor_scale, uint16_t* y, void* stream) {
+  if (!blocks || !tables || !y) return ECCO_EINVAL;
+  if (!(tensor_scale > 0.0f) || !(tensor_scale < __builtin_huge_valf())) return ECCO_EINVAL;
+  const uint64_t total = n_rows * gpr;
+  if (n_rows == 0 || gpr == 0 || total >= (1ull << 32) || gpr >= (1ull << 32)) return ECCO_ESIZE;
+  if (n_rows > 1 && (y_stride < gpr * 128 || blk_stride < gpr)) return ECCO_ESIZE;
+  if (!host_aligned(y, 16) || (y_stride % 8) != 0 || !host_aligned(blocks, 64) || !host_aligned(tables, 256)) return ECCO_EALIGN;
+  int cus = 0, rc = check_gfx950(&cus);
+  if (rc) return rc;
+  DecodeArgs a;
+  a.blocks = static_cast<const uint8_t*>(blocks);
+  a.y = y;
+  a.tab = static_cast<const Tables*>(tables);
+  a.blk_stride = blk_stride;
+  a.y_stride = y_stride;
+  a.gpr = make_magic((uint32_t)gpr);
+  a.n_groups = (uint32_t)total;
+  a.n_batches = (uint32_t)((total + 63) / 64);
+  a.t = tensor_scale;
+  a.contiguous = (n_rows == 1 || (blk_stride == gpr && y_stride == gpr * 128)) ? 1u : 0u;
+  uint32_t want = (a.n_batches + kDecWaves - 1) / kDecWaves;
+  uint32_t grid = std::max<uint32_t>(1, std::min<uint32_t>(want, (uint32_t)cus));
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(decode_kernel, dim3(grid), dim3(kDecWaves * 64), 0, static_cast<hipStream_t>(stream), a);
+  return launch_status();
+}

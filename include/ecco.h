@@ -1,0 +1,202 @@
+/*
+ * ecco.h -- C ABI of libecco, an MI355X (gfx950) implementation of the Ecco
+ * entropy-coded block codec for LLM weights and KV caches.
+ *
+ * Source of the method: the pith.science review of "Ecco: Improving Memory
+ * Bandwidth and Capacity for LLMs via Entropy-aware Cache Compression"
+ * (arXiv 2505.06901).  Each group of 128 FP16 values is normalised by a
+ * per-group FP8 scale derived from a per-tensor FP16-to-FP8 scale (Fig. 4
+ * caption), quantised onto one of 64 shared patterns of 15 sorted k-means
+ * centroids with index 15 reserved for the scale ("What carries the
+ * argument"; "free parameters"), the pattern being chosen by comparing only
+ * the group's min and max with each pattern's (same section; compressor,
+ * section 4.3), Huffman coded with the shortest of 4 codebooks per pattern
+ * whose code lengths are 2..8 bits (referee report, major comment 1), clipped
+ * to, or padded with the largest remaining values up to, a fixed 512-bit
+ * block ("Core claim"; "free parameters": top-16 outliers, 240 bits at most).
+ *
+ * ------------------------------------------------------------------------
+ * BLOCK FORMAT v1 (64 bytes per group of 128 values)
+ * ------------------------------------------------------------------------
+ * Bit i of a block is bit (i & 7) of byte (i >> 3).  Integer fields are
+ * stored least-significant bit first.
+ *
+ *   bits   0..5    pattern p            (0..63)
+ *   bits   6..7    codebook h           (0..3)
+ *   bits   8..15   group scale s8       FP8 E4M3FN of x[i*] * inv_t (signed)
+ *   bits  16..E-1  codewords of symbols 0..127 in position order; each
+ *                  canonical codeword (RFC 1951 3.2.2 ordering) is written
+ *                  most-significant code bit first.  L = total code length.
+ *                  Unclipped: E = 16 + L <= 512.  Clipped (16 + L > 512):
+ *                  the stream fills bits 16..511 and ends with a proper
+ *                  prefix of the first codeword that did not fit; k < 128
+ *                  whole codewords are decodable.
+ *   bits   E..512-15n-1  zero
+ *   bits   512-15(r+1) .. 512-15r-1   outlier record r, r = 0..n-1:
+ *                  bits 0..6 = position j, bits 7..14 = FP8 E4M3FN(x_j * inv_t)
+ *   n = min(16, floor((512 - E) / 15)) for an unclipped block, 0 if clipped.
+ *
+ * Encode of a group x[0..127] (FP16 promoted exactly to FP32; every step
+ * below is one IEEE binary32 operation, round-to-nearest-even, no FMA):
+ *   t      per-tensor scale (amax / 448, see ecco_tensor_scale_from_amax);
+ *          inv_t = 1.0f / t computed by the library on the host
+ *   i*     = argmax_j |x_j|, lowest j on ties; s8 = FP8(x_i* * inv_t)
+ *            (saturating to +-448, round to nearest even, never NaN)
+ *   S      = f32(s8) * t; a = |S|
+ *   p      = argmin_p (gmin - c_p0*a)^2 + (gmax - c_p14*a)^2 (squares summed
+ *            in that order), gmin/gmax over the 127 values j != i*; lowest p
+ *   sym_j  = #{k in 0..13 : x_j > m_pk * a}, m_pk = (c_pk + c_p,k+1) * 0.5f;
+ *            sym_i* = 15
+ *   h      = argmin_h sum_j len[p][h][sym_j]; lowest h on ties
+ *   outliers: the n values j != i* of largest |x_j| (lower j first on ties),
+ *            record r holding the r-th of them
+ * Decode: symbols are read while a whole codeword fits in bits 16..511, at
+ * most 128 of them; value j = fp16(S) for symbol 15, fp16(c[p][sym] * a)
+ * otherwise, +0 for j >= k; if k == 128 the n records are applied in order
+ * r = 0..n-1: value[j_r] = fp16(f32(v8_r) * t).  Any 512 bits decode.
+ *
+ * ------------------------------------------------------------------------
+ * CONVENTIONS
+ * ------------------------------------------------------------------------
+ * - "_dev" pointers are HIP device memory owned by the caller; "_host"
+ *   pointers are host memory owned by the caller.  The library allocates,
+ *   frees and synchronises nothing: every device call only enqueues kernels
+ *   on `stream` (a hipStream_t, passed as void*; NULL = the default stream)
+ *   and returns.  Calls are reentrant; overlapping calls that write the same
+ *   memory race.
+ * - Return value: ECCO_OK (0) or a negative ECCO_E* code.  Arguments are
+ *   checked before anything is enqueued; no C++ exception crosses the ABI.
+ * - Alignment: FP16 tensors and row strides 16-byte aligned, blocks 64-byte
+ *   aligned, the table blob 256-byte aligned (ECCO_EALIGN otherwise).
+ * - Device entry points require a gfx950 device (ECCO_EDEVICE otherwise).
+ */
+#ifndef ECCO_H
+#define ECCO_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ECCO_GROUP 128
+#define ECCO_BLOCK_BYTES 64
+#define ECCO_N_PATTERNS 64
+#define ECCO_N_CENTROIDS 15
+#define ECCO_N_CODEBOOKS 4
+#define ECCO_N_SYMBOLS 16
+#define ECCO_LEN_MIN 2
+#define ECCO_LEN_MAX 8
+#define ECCO_GEMV_MAX_BATCH 8
+
+enum {
+  ECCO_OK = 0,
+  ECCO_EINVAL = -1,   /* null pointer where one is required, bad option value   */
+  ECCO_EALIGN = -2,   /* pointer or stride alignment violated                   */
+  ECCO_ESIZE = -3,    /* size out of range (see each call)                      */
+  ECCO_ETABLES = -4,  /* table blob or table contents invalid                   */
+  ECCO_EHIP = -5,     /* a HIP runtime call or kernel launch failed             */
+  ECCO_EDEVICE = -6   /* current device is not gfx950                           */
+};
+
+/* Device-side counters accumulated by ecco_encode (atomics; caller zeroes). */
+typedef struct {
+  unsigned long long groups;           /* groups encoded                                */
+  unsigned long long clipped_groups;   /* groups with 16 + L > 512                      */
+  unsigned long long clipped_values;   /* sum over groups of 128 - k                    */
+  unsigned long long padded_outliers;  /* sum of n                                      */
+  unsigned long long pad_bits;         /* sum of 15 n                                   */
+  unsigned long long fill_bits;        /* zero bits between stream end and records      */
+  unsigned long long nonfinite_groups; /* groups holding Inf/NaN (their blocks are unspecified) */
+} ecco_stats_t;
+
+/* Options of ecco_train_patterns; NULL selects the defaults shown. */
+typedef struct {
+  uint32_t kmeans_iters;  /* Lloyd iterations of the 64-pattern k-means (25)      */
+  uint32_t huff_iters;    /* codebook Lloyd iterations per pattern (10)           */
+  uint64_t seed;          /* k-means++ seed (0)                                   */
+  uint32_t max_groups;    /* use at most this many sample groups, 0 = all (0)     */
+  uint32_t threads;       /* host threads, 0 = hardware concurrency (0)           */
+} ecco_train_opts_t;
+
+/* ---- tables --------------------------------------------------------------
+ * The per-tensor side data is an opaque, position-independent blob of
+ * ecco_tables_size() bytes: the inputs (centroids, code lengths) plus tables
+ * the kernels derive from them (canonical codes, decode look-up table,
+ * midpoints).  Build it on the host, then copy the bytes to device memory
+ * (256-byte aligned) for the device calls.
+ */
+size_t ecco_tables_size(void);
+
+/* Build a blob from centroids[64][15] (float32, each exactly representable in
+ * FP16, non-decreasing per pattern, within [-1, 1]) and code_len[64][4][16]
+ * (each in [2, 8], every codebook a complete prefix code: Kraft sum exactly
+ * 1).  Returns ECCO_ETABLES if the contents violate these rules (the blob is
+ * then left unspecified), ECCO_EINVAL for NULL pointers. */
+int ecco_tables_build(const float* centroids_host, const uint8_t* code_len_host, void* tables_host);
+
+/* Check a host blob: header, checksum, and the rules of ecco_tables_build. */
+int ecco_tables_validate(const void* tables_host);
+
+/* Copy the centroids and code lengths back out of a valid host blob. */
+int ecco_tables_get(const void* tables_host, float* centroids_host, uint8_t* code_len_host);
+
+/* Learn tables offline from an FP16 sample (n_values a positive multiple of
+ * 128) -- the calibration step of the pages ("patterns ... learned once on a
+ * calibration set"; S = 64, H = 4): exact 1-D k-means of each normalised
+ * group, Lloyd k-means of those 15-vectors into 64 patterns, then per pattern
+ * 4 codebooks by Lloyd iterations on code length with optimal 2..8-bit
+ * lengths.  Host only; writes a valid blob to tables_host. */
+int ecco_train_patterns(const uint16_t* sample_fp16_host, uint64_t n_values,
+                        const ecco_train_opts_t* opts, void* tables_host);
+
+/* Per-tensor scale t = amax / 448 (1 if amax == 0 or not finite) -- the
+ * "per-tensor FP16-to-FP8 scale factor" (Fig. 4 caption). */
+float ecco_tensor_scale_from_amax(float amax);
+
+/* ---- device calls ---------------------------------------------------------- */
+
+/* amax_dev[0] = max |x| over n_values FP16 values (n_values >= 1; NaN ignored). */
+int ecco_amax(const uint16_t* x_dev, uint64_t n_values, float* amax_dev, void* stream);
+
+/* Encode n_rows x groups_per_row groups.  Group (r, g) is the 128 FP16
+ * values at x_dev + r * x_row_stride_elems + g * 128; its block goes to
+ * blocks_dev + (r * blk_row_stride_blocks + g) * 64.  Weights [out, in]:
+ * n_rows = out, groups_per_row = in / 128.  KV append in [B, H, S, D=128]:
+ * n_rows = B * H, groups_per_row = tokens, x_row_stride_elems = S * 128,
+ * blk_row_stride_blocks = S, pointers offset to the first new token.
+ * tensor_scale must be finite and > 0.  stats_dev may be NULL.
+ * ECCO_ESIZE if n_rows * groups_per_row is 0 or >= 2^32. */
+int ecco_encode(const uint16_t* x_dev, uint64_t n_rows, uint64_t groups_per_row,
+                uint64_t x_row_stride_elems, uint64_t blk_row_stride_blocks,
+                const void* tables_dev, float tensor_scale, void* blocks_dev,
+                ecco_stats_t* stats_dev, void* stream);
+
+/* Decode: the inverse layout of ecco_encode; group (r, g) is written to
+ * y_dev + r * y_row_stride_elems + g * 128.  Every block decodes (the
+ * decoder is total on arbitrary bits).  Same size rules as ecco_encode. */
+int ecco_decode(const void* blocks_dev, uint64_t n_rows, uint64_t groups_per_row,
+                uint64_t blk_row_stride_blocks, uint64_t y_row_stride_elems,
+                const void* tables_dev, float tensor_scale, uint16_t* y_dev, void* stream);
+
+/* Fused decode + GEMV: y[b][o] = sum_i W[o][i] * x[b][i] with W the decoded
+ * FP16 weights, products and sums in FP32 (plain FMA on the vector ALUs).
+ * blocks_dev holds W as [out_features][in_features / 128] blocks; x_dev is
+ * [batch][in_features] FP16; y_dev is [batch][out_features] FP32 and is
+ * overwritten.  ECCO_ESIZE unless in_features is a positive multiple of 128,
+ * out_features >= 1 and 1 <= batch <= ECCO_GEMV_MAX_BATCH. */
+int ecco_decode_gemv(const void* blocks_dev, const void* tables_dev, float tensor_scale,
+                     int64_t out_features, int64_t in_features,
+                     const uint16_t* x_dev, int64_t batch, float* y_dev, void* stream);
+
+const char* ecco_strerror(int code);
+
+/* Library version string, e.g. "ecco 1.0 (format v1, gfx950)". */
+const char* ecco_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ECCO_H */

@@ -1,0 +1,149 @@
+"""The C ABI on the CPU: the library loads, exports what include/ecco.h
+declares, and its host logic (table derivation and validation, argument
+checks, training) behaves; no kernel is launched."""
+
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import codec, huffman
+import workloads as W
+
+ecco = pytest.importorskip("entropy_coded_group_amd")
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+GOLD = os.path.join(ROOT, "tests", "golden", "tables.npz")
+
+
+def _golden(name="c1"):
+    z = np.load(GOLD)
+    return codec.Tables(z[name + "_centroids"], z[name + "_code_len"])
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    L = ecco.lib()
+    hdr = open(os.path.join(ROOT, "include", "ecco.h")).read()
+    names = sorted(set(re.findall(r"\b(ecco_[a-z0-9_]+)\s*\(", hdr)))
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(L, n), n
+    assert "gfx950" in ecco.ecco_version()
+
+
+def test_strerror_covers_codes():
+    for c in range(-6, 1):
+        assert ecco.ecco_strerror(c) != "unknown error"
+
+
+# byte offsets of the blob (ecco_internal.h): header 256, centroids 4096,
+# code_len 4096, midpoints 4096, c0c14 512, len4 4096, enc 8192, fp8 1024, lut 65536
+OFF_CENT, OFF_LEN, OFF_MID, OFF_C0, OFF_LEN4, OFF_ENC, OFF_FP8, OFF_LUT = (
+    256, 4352, 8448, 12544, 13056, 17152, 25344, 26368)
+
+
+def test_blob_size_and_layout():
+    assert ecco.ecco_tables_size() == OFF_LUT + 65536
+
+
+def test_tables_build_roundtrip_and_derived_tables_match_oracle():
+    tb = _golden()
+    blob = ecco.ecco_tables_build(tb.centroids, tb.code_len)
+    assert ecco.ecco_tables_validate(blob) == 0
+    c, l = ecco.ecco_tables_get(blob)
+    assert np.array_equal(c, tb.centroids) and np.array_equal(l, tb.code_len)
+    mids = np.frombuffer(blob[OFF_MID:OFF_MID + 4096].tobytes(), np.float32).reshape(64, 16)
+    assert np.array_equal(mids[:, :14].view(np.uint32), tb.midpoints().view(np.uint32))
+    assert np.all(np.isinf(mids[:, 14:]))
+    enc = np.frombuffer(blob[OFF_ENC:OFF_ENC + 8192].tobytes(), np.uint16).reshape(64, 4, 16)
+    lut = blob[OFF_LUT:OFF_LUT + 65536].reshape(64, 4, 256)
+    codes = tb.codes()
+    for p in range(0, 64, 7):
+        for h in range(4):
+            for s in range(16):
+                ln = int(tb.code_len[p, h, s])
+                rev = int(format(int(codes[p, h, s]), "0%db" % ln)[::-1], 2)   # stream order
+                assert enc[p, h, s] == (rev | (ln << 8))
+                for w in range(rev, 256, 1 << ln):
+                    assert lut[p, h, w] == (s | ((ln - 1) << 5))
+    fp8 = np.frombuffer(blob[OFF_FP8:OFF_FP8 + 1024].tobytes(), np.float32)
+    ref = oracle.fp.fp8_decode(np.arange(256, dtype=np.uint8))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(fp8[ok].view(np.uint32), ref[ok].view(np.uint32)) and np.all(np.isnan(fp8[~ok]))
+
+
+def test_tables_build_rejects_bad_inputs():
+    tb = _golden()
+    bad_len = tb.code_len.copy()
+    bad_len[3, 1, 5] = 1
+    with pytest.raises(ecco.EccoError):
+        ecco.ecco_tables_build(tb.centroids, bad_len)
+    incomplete = tb.code_len.copy()
+    incomplete[0, 0, :] = 8                               # Kraft 1/16 < 1
+    with pytest.raises(ecco.EccoError):
+        ecco.ecco_tables_build(tb.centroids, incomplete)
+    unsorted = tb.centroids.copy()
+    unsorted[2, [4, 5]] = unsorted[2, [5, 4]] + np.float32([0.5, 0])
+    with pytest.raises(ecco.EccoError):
+        ecco.ecco_tables_build(unsorted, tb.code_len)
+    not_half = tb.centroids.copy()
+    not_half[1, 7] = np.float32(0.1)                       # not exact in FP16
+    with pytest.raises(ecco.EccoError):
+        ecco.ecco_tables_build(not_half, tb.code_len)
+
+
+def test_tables_validate_detects_corruption():
+    tb = _golden()
+    blob = ecco.ecco_tables_build(tb.centroids, tb.code_len)
+    bad = blob.copy()
+    bad[OFF_LUT + 1000] ^= 1
+    assert ecco.ecco_tables_validate(bad) == -4
+    bad = blob.copy()
+    bad[0] ^= 1
+    assert ecco.ecco_tables_validate(bad) == -4
+
+
+def test_tensor_scale_matches_oracle():
+    for amax in (0.0, 1e-8, 0.37, 1.0, 448.0, 65504.0, 3.3e-5):
+        t_lib = ecco.ecco_tensor_scale_from_amax(amax)
+        t_or, _ = codec.tensor_scale(amax)
+        assert np.float32(t_lib) == t_or, amax
+
+
+def test_device_entry_points_check_arguments_before_touching_the_device():
+    blob = ecco.ecco_tables_build(*(_golden().centroids, _golden().code_len))
+    L = ecco.lib()
+    A = 1 << 20                                            # a well-aligned fake address
+    assert L.ecco_encode(None, 1, 1, 128, 1, A, 1.0, A, None, None) == -1
+    assert L.ecco_encode(A, 1, 1, 128, 1, A, 0.0, A, None, None) == -1          # t must be > 0
+    assert L.ecco_encode(A, 0, 1, 128, 1, A, 1.0, A, None, None) == -3
+    assert L.ecco_encode(A, 1 << 20, 1 << 12, 1 << 19, 1 << 12, A, 1.0, A, None, None) == -3
+    assert L.ecco_encode(A + 2, 1, 1, 128, 1, A, 1.0, A, None, None) == -2
+    assert L.ecco_encode(A, 1, 1, 128, 1, A, 1.0, A + 16, None, None) == -2
+    assert L.ecco_decode(A, 1, 1, 1, 128, A + 64, 1.0, A, None) == -2
+    assert L.ecco_decode(A, 2, 4, 3, 512, A, 1.0, A, None) == -3                 # row stride < groups
+    assert L.ecco_decode_gemv(A, A, 1.0, 16, 100, A, 1, A, None) == -3          # in % 128
+    assert L.ecco_decode_gemv(A, A, 1.0, 16, 128, A, 9, A, None) == -3          # batch > 8
+    assert L.ecco_amax(A, 0, A, None) == -3
+    del blob
+
+
+def test_library_training_gives_valid_tables_of_oracle_quality():
+    sample = W.c1_sample(n_values=512 * 128).numpy()
+    blob = ecco.ecco_train_patterns(sample, kmeans_iters=10, huff_iters=5, threads=4)
+    assert ecco.ecco_tables_validate(blob) == 0
+    c, l = ecco.ecco_tables_get(blob)
+    lib_tabs = codec.Tables(c, l)
+    lib_tabs.check()
+    for p in range(64):
+        for h in range(4):
+            assert huffman.kraft_sum(l[p, h]) == 1
+    ora_tabs = oracle.train.train_tables(sample, kmeans_iters=10, huff_iters=5)
+    x = W.c1_weight().numpy().reshape(-1, 128)[:1024]
+    t, _ = codec.tensor_scale(float(np.max(np.abs(x.astype(np.float32)))))
+    mse = []
+    for tb in (lib_tabs, ora_tabs):
+        y = codec.decode_blocks(codec.encode_groups(x, tb, t), tb, t)
+        mse.append(oracle.metrics.reconstruction(x, y)["mse"])
+    assert mse[0] <= 1.25 * mse[1], mse

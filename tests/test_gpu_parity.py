@@ -1,0 +1,355 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bar: block bytes and decoded FP16 bits identical to the oracle (NaN compared
+as NaN: only garbage blocks produce it), encode statistics identical, and the
+fused decode+GEMV within |y - y_ref| <= 1e-3 * max(|y_ref|, sum|w x| / sqrt(in))
+of a float64 GEMV over oracle-decoded weights.  Small cases are compared
+element by element over several tiles and ragged tails; the full-size
+workloads (a LLaMA-3-8B layer's matrices, a 16x8x8192x128 KV cache, 70B FFN
+matrices) are compared on deterministic samples of groups / rows.
+"""
+
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import codec, gemv as ogemv
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+ecco = pytest.importorskip("entropy_coded_group_amd")
+
+GOLD = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "tables.npz")
+
+
+def say(msg):
+    print("[gpu-parity] " + msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    name = torch.cuda.get_device_properties(0).gcnArchName
+    if not name.startswith("gfx950"):
+        pytest.skip("not gfx950: %s" % name)
+    ecco.lib()
+    return torch.device("cuda:0")
+
+
+def golden(name):
+    z = np.load(GOLD)
+    return codec.Tables(z[name + "_centroids"], z[name + "_code_len"])
+
+
+def golden_t(name):
+    return np.float32(np.load(GOLD)[name + "_t"])
+
+
+def dev_tables(tb):
+    return ecco.tables_to_device(ecco.ecco_tables_build(tb.centroids, tb.code_len))
+
+
+def scale_of(x):
+    return codec.tensor_scale(float(np.max(np.abs(np.asarray(x, np.float32)))))[0]
+
+
+def gpu_encode(x_groups, tdev, t, stats=False):
+    """x_groups: [G, 128] float16 (numpy) -> blocks [G, 64] uint8 (numpy)."""
+    G = x_groups.shape[0]
+    xd = torch.from_numpy(np.ascontiguousarray(x_groups)).cuda()
+    bd = torch.full((G, 64), 0xAB, dtype=torch.uint8, device="cuda")
+    sd = torch.zeros(7, dtype=torch.int64, device="cuda") if stats else None
+    ecco.ecco_encode(xd, 1, G, G * 128, G, tdev, t, bd, sd)
+    torch.cuda.synchronize()
+    if stats:
+        return bd.cpu().numpy(), dict(zip(ecco.STATS_FIELDS, sd.cpu().tolist()))
+    return bd.cpu().numpy()
+
+
+def gpu_decode(blocks, tdev, t):
+    G = blocks.shape[0]
+    bd = torch.from_numpy(np.ascontiguousarray(blocks)).cuda()
+    yd = torch.full((G, 128), 0x7FFF, dtype=torch.int16, device="cuda")
+    ecco.ecco_decode(bd, 1, G, G, G * 128, tdev, t, yd)
+    torch.cuda.synchronize()
+    return yd.cpu().numpy().view(np.float16)
+
+
+def assert_fp16_equal(a, b, what):
+    a = np.asarray(a, np.float16)
+    b = np.asarray(b, np.float16)
+    na, nb = np.isnan(a), np.isnan(b)
+    assert np.array_equal(na, nb), "%s: NaN positions differ" % what
+    ua, ub = a.view(np.uint16)[~na], b.view(np.uint16)[~nb]
+    bad = np.nonzero(ua != ub)[0]
+    assert bad.size == 0, "%s: %d mismatches, first at flat index %d: gpu %04x oracle %04x" % (
+        what, bad.size, bad[0], ua[bad[0]], ub[bad[0]])
+
+
+def assert_blocks_equal(g, o, what):
+    bad = np.nonzero(np.any(g != o, axis=1))[0]
+    assert bad.size == 0, "%s: %d of %d blocks differ, first group %d\n gpu %s\n ora %s" % (
+        what, bad.size, g.shape[0], bad[0], g[bad[0]].tobytes().hex(), o[bad[0]].tobytes().hex())
+
+
+def adversarial_tables(seed):
+    """Complete codes whose lengths are assigned at random: long codes for common
+    symbols, so many groups clip."""
+    rng = np.random.default_rng(seed)
+    base = np.array([2, 3, 4, 5, 6, 7, 8, 8] + [4] * 8, np.uint8)
+    L = np.stack([np.stack([rng.permutation(base) for _ in range(4)]) for _ in range(64)])
+    c = np.sort(rng.uniform(-1, 1, (64, 15)), axis=1).astype(np.float16).astype(np.float32)
+    return codec.Tables(c, L)
+
+
+def random_tables(seed):
+    rng = np.random.default_rng(seed)
+    c = np.sort(rng.uniform(-1, 1, (64, 15)), axis=1).astype(np.float16).astype(np.float32)
+    L = np.zeros((64, 4, 16), np.uint8)
+    for p in range(64):
+        for h in range(4):
+            L[p, h] = oracle.huffman.limited_lengths(rng.integers(1, 300, 16) ** (1 + (h & 1)))
+    return codec.Tables(c, L)
+
+
+# ------------------------------------------------------------------ small, exact
+
+def test_amax_and_tensor_scale(dev):
+    x = W.c1_weight()
+    say("amax c1")
+    out = torch.zeros(1, dtype=torch.float32, device="cuda")
+    xd = x.cuda()
+    ecco.ecco_amax(xd, xd.numel(), out)
+    torch.cuda.synchronize()
+    ref = np.max(np.abs(x.numpy().astype(np.float32)))
+    assert out.item() == ref
+    assert np.float32(ecco.ecco_tensor_scale_from_amax(out.item())) == scale_of(x.numpy())
+    for n in (1, 7, 8, 9, 1000, 4099):                    # tails of the vector loop
+        y = W.random_groups(40, n, "wide").numpy().ravel()[:n].copy()
+        yd = torch.from_numpy(y).cuda()
+        ecco.ecco_amax(yd, n, out)
+        torch.cuda.synchronize()
+        assert out.item() == np.max(np.abs(y.astype(np.float32))), n
+
+
+def test_c1_encode_decode_bitexact(dev):
+    tb = golden("c1")
+    tdev = dev_tables(tb)
+    x = W.c1_weight().numpy().reshape(-1, 128)
+    t = scale_of(x)
+    say("c1 encode 8192 groups")
+    g_blocks, g_stats = gpu_encode(x, tdev, t, stats=True)
+    o_blocks, info = codec.encode_groups(x, tb, t, return_info=True)
+    assert_blocks_equal(g_blocks, o_blocks, "c1 encode")
+    assert g_stats == info["stats"]
+    say("c1 decode 8192 groups")
+    assert_fp16_equal(gpu_decode(o_blocks, tdev, t), codec.decode_blocks(o_blocks, tb, t), "c1 decode")
+
+
+@pytest.mark.parametrize("kind,seed,n", [("normal", 1, 1), ("normal", 2, 63), ("laplace", 3, 64),
+                                         ("wide", 4, 65), ("normal", 5, 129), ("laplace", 6, 1000),
+                                         ("wide", 7, 4097)])
+def test_random_groups_random_tables(dev, kind, seed, n):
+    tb = random_tables(seed)
+    tdev = dev_tables(tb)
+    x = W.random_groups(n, seed, kind).numpy()
+    t = scale_of(x)
+    say("random %s n=%d" % (kind, n))
+    g_blocks, g_stats = gpu_encode(x, tdev, t, stats=True)
+    o_blocks, info = codec.encode_groups(x, tb, t, return_info=True)
+    assert_blocks_equal(g_blocks, o_blocks, "encode %s %d" % (kind, n))
+    assert g_stats == info["stats"]
+    assert_fp16_equal(gpu_decode(o_blocks, tdev, t), codec.decode_blocks(o_blocks, tb, t), "decode")
+
+
+def test_heavily_clipped_groups(dev):
+    tb = adversarial_tables(11)
+    tdev = dev_tables(tb)
+    x = np.concatenate([W.random_groups(700, 12, "normal").numpy(), W.random_groups(300, 13, "wide").numpy()])
+    t = scale_of(x)
+    say("clipping tables, 1000 groups")
+    g_blocks, g_stats = gpu_encode(x, tdev, t, stats=True)
+    o_blocks, info = codec.encode_groups(x, tb, t, return_info=True)
+    assert info["clipped"].mean() > 0.3
+    assert_blocks_equal(g_blocks, o_blocks, "clipped encode")
+    assert g_stats == info["stats"]
+    assert_fp16_equal(gpu_decode(o_blocks, tdev, t), codec.decode_blocks(o_blocks, tb, t), "clipped decode")
+
+
+def test_special_groups(dev):
+    tb = golden("c1")
+    tdev = dev_tables(tb)
+    c = tb.centroids[9]
+    rows = [np.zeros(128), np.full(128, 0.25), np.full(128, -3.0), np.r_[1.0, np.resize(c, 127)],
+            np.r_[-1.0, np.resize(c[::-1], 127)], np.linspace(-1, 1, 128), np.r_[np.zeros(127), 5e-6],
+            np.r_[65504.0, np.zeros(127)], np.r_[np.full(64, 1e-7), np.full(64, -1e-7)]]
+    x = np.array(rows, dtype=np.float16)
+    for t in (np.float32(1.0), scale_of(x), np.float32(1e-3)):
+        say("special groups t=%g" % t)
+        g_blocks = gpu_encode(x, tdev, t)
+        o_blocks = codec.encode_groups(x, tb, t)
+        assert_blocks_equal(g_blocks, o_blocks, "special encode t=%g" % t)
+        assert_fp16_equal(gpu_decode(o_blocks, tdev, t), codec.decode_blocks(o_blocks, tb, t), "special decode")
+
+
+def test_fuzz_decode_random_blocks(dev):
+    for name, tb in (("c1", golden("c1")), ("adversarial", adversarial_tables(5))):
+        tdev = dev_tables(tb)
+        blocks = W.random_blocks(40000, 99).numpy()
+        for t in (np.float32(1.0), np.float32(0.0173)):
+            say("fuzz decode %s t=%g" % (name, t))
+            assert_fp16_equal(gpu_decode(blocks, tdev, t), codec.decode_blocks(blocks, tb, t),
+                              "fuzz %s t=%g" % (name, t))
+
+
+def test_strided_kv_append_and_decode(dev):
+    tb = golden("c3_k")
+    t = golden_t("c3_k")
+    tdev = dev_tables(tb)
+    B, H, S, D = 2, 3, 512, 128
+    kv = W.kv_tensor("k", shape=(B, H, S, D), seed=21)
+    first, ntok = 256, 200
+    say("strided KV append")
+    kvd = kv.cuda()
+    blocks = torch.full((B, H, S, 64), 0xAB, dtype=torch.uint8, device="cuda")
+    xs = kvd[:, :, first:, :]
+    bs = blocks[:, :, first:, :]
+    ecco.ecco_encode(xs, B * H, ntok, S * D, S, tdev, t, bs)
+    torch.cuda.synchronize()
+    gb = blocks.cpu().numpy()
+    new = kv.numpy()[:, :, first:first + ntok, :].reshape(-1, 128)
+    ob = codec.encode_groups(new, tb, t)
+    assert_blocks_equal(gb[:, :, first:first + ntok, :].reshape(-1, 64), ob, "kv append")
+    assert np.all(gb[:, :, :first] == 0xAB) and np.all(gb[:, :, first + ntok:] == 0xAB)
+    say("strided KV decode")
+    y = torch.full((B, H, S, D), 0x7FFF, dtype=torch.int16, device="cuda")
+    ecco.ecco_decode(bs, B * H, ntok, S, S * D, tdev, t, y[:, :, first:, :])
+    torch.cuda.synchronize()
+    gy = y.cpu().numpy().view(np.float16)
+    assert_fp16_equal(gy[:, :, first:first + ntok].reshape(-1, 128), codec.decode_blocks(ob, tb, t), "kv decode")
+    assert np.all(y.cpu().numpy()[:, :, :first] == 0x7FFF) and np.all(y.cpu().numpy()[:, :, first + ntok:] == 0x7FFF)
+
+
+@pytest.mark.parametrize("out_f,in_f,batch", [(1, 128, 1), (37, 1024, 3), (300, 1024, 8), (64, 8192, 4),
+                                              (20, 28672, 2)])
+def test_gemv_small(dev, out_f, in_f, batch):
+    tb = golden("c5_w1")
+    tdev = dev_tables(tb)
+    w = W.llama_matrix((out_f, in_f), seed=700 + out_f).numpy()
+    t = scale_of(w)
+    blocks = codec.encode_groups(w.reshape(-1, 128), tb, t)
+    x = W.c5_x(batch, in_f, seed=701).numpy()
+    say("gemv %dx%d b=%d" % (out_f, in_f, batch))
+    y = torch.full((batch, out_f), float("nan"), dtype=torch.float32, device="cuda")
+    ecco.ecco_decode_gemv(torch.from_numpy(blocks).cuda(), tdev, t, out_f, in_f,
+                          torch.from_numpy(x).cuda(), batch, y)
+    torch.cuda.synchronize()
+    w_hat = codec.decode_blocks(blocks, tb, t).reshape(out_f, in_f)
+    y_ref, mag = ogemv.gemv_ref(w_hat, x)
+    ok, worst = ogemv.gemv_tolerance_ok(y.cpu().numpy(), y_ref, mag, in_f)
+    assert ok, "worst error / bound = %g" % worst
+
+
+# -------------------------------------------------------------- full-size, sampled
+
+def sample_index(G, stride=97):
+    idx = np.unique(np.r_[np.arange(0, G, stride), np.arange(min(64, G)), np.arange(max(0, G - 64), G)])
+    return idx
+
+
+@pytest.mark.parametrize("name", ["q", "k", "gate", "down"])
+def test_llama_layer_matrix_full_size_sampled(dev, name):
+    tb = golden("c2_" + name)
+    tdev = dev_tables(tb)
+    w = W.c2_layer(0, names=[name])[name]
+    out_f, in_f = w.shape
+    wd = w.cuda()
+    amax = torch.zeros(1, dtype=torch.float32, device="cuda")
+    ecco.ecco_amax(wd, wd.numel(), amax)
+    torch.cuda.synchronize()
+    t = np.float32(ecco.ecco_tensor_scale_from_amax(amax.item()))
+    assert t == scale_of(w.numpy())
+    G = out_f * in_f // 128
+    say("c2 %s encode %d groups" % (name, G))
+    bd = torch.empty((out_f, in_f // 128, 64), dtype=torch.uint8, device="cuda")
+    ecco.ecco_encode(wd, out_f, in_f // 128, in_f, in_f // 128, tdev, t, bd)
+    yd = torch.empty_like(wd)
+    ecco.ecco_decode(bd, out_f, in_f // 128, in_f // 128, in_f, tdev, t, yd)
+    torch.cuda.synchronize()
+    idx = sample_index(G)
+    xg = w.numpy().reshape(-1, 128)[idx]
+    ob = codec.encode_groups(xg, tb, t)
+    gb = bd.cpu().numpy().reshape(-1, 64)
+    assert_blocks_equal(gb[idx], ob, "c2 %s encode (sampled)" % name)
+    assert_fp16_equal(yd.cpu().numpy().reshape(-1, 128)[idx], codec.decode_blocks(ob, tb, t),
+                      "c2 %s decode (sampled)" % name)
+
+
+def test_kv_cache_full_size_sampled(dev):
+    B, H, S, D = W.KV_SHAPE
+    for kind in ("k", "v"):
+        tb = golden("c3_" + kind)
+        t = golden_t("c3_" + kind)
+        tdev = dev_tables(tb)
+        say("kv %s generate" % kind)
+        kv = W.kv_tensor(kind)
+        kvd = kv.cuda()
+        blocks = torch.empty((B, H, S, 64), dtype=torch.uint8, device="cuda")
+        say("kv %s encode prefix + append" % kind)
+        ecco.ecco_encode(kvd, B * H, S - W.KV_APPEND, S * D, S, tdev, t, blocks)
+        ecco.ecco_encode(kvd[:, :, S - W.KV_APPEND:], B * H, W.KV_APPEND, S * D, S, tdev, t,
+                         blocks[:, :, S - W.KV_APPEND:])
+        y = torch.empty_like(kvd)
+        say("kv %s decode whole cache" % kind)
+        ecco.ecco_decode(blocks, 1, B * H * S, B * H * S, B * H * S * D, tdev, t, y)
+        torch.cuda.synchronize()
+        gb = blocks.cpu().numpy()
+        app = kv.numpy()[:, :, S - W.KV_APPEND:].reshape(-1, 128)
+        ob_app = codec.encode_groups(app, tb, t)
+        assert_blocks_equal(gb[:, :, S - W.KV_APPEND:].reshape(-1, 64), ob_app, "kv %s append" % kind)
+        idx = sample_index(B * H * S, 193)
+        xg = kv.numpy().reshape(-1, 128)[idx]
+        ob = codec.encode_groups(xg, tb, t)
+        assert_blocks_equal(gb.reshape(-1, 64)[idx], ob, "kv %s prefix (sampled)" % kind)
+        assert_fp16_equal(y.cpu().numpy().reshape(-1, 128)[idx], codec.decode_blocks(ob, tb, t),
+                          "kv %s decode (sampled)" % kind)
+        del kvd, y, blocks
+        torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name", ["w1", "w2"])
+def test_ffn70b_gemv_full_size_sampled(dev, name):
+    tb = golden("c5_" + name)
+    tdev = dev_tables(tb)
+    say("c5 %s generate" % name)
+    w = W.c5_matrix(name)
+    out_f, in_f = w.shape
+    t = scale_of(w.numpy())
+    wd = w.cuda()
+    bd = torch.empty((out_f, in_f // 128, 64), dtype=torch.uint8, device="cuda")
+    say("c5 %s encode" % name)
+    ecco.ecco_encode(wd, out_f, in_f // 128, in_f, in_f // 128, tdev, t, bd)
+    torch.cuda.synchronize()
+    gb = bd.cpu().numpy()
+    rows = np.unique(np.r_[np.arange(0, out_f, 131 if name == "w1" else 41), out_f - 1])
+    wr = w.numpy()[rows].reshape(-1, 128)
+    ob = codec.encode_groups(wr, tb, t)
+    assert_blocks_equal(gb[rows].reshape(-1, 64), ob, "c5 %s encode (sampled rows)" % name)
+    w_hat = codec.decode_blocks(ob, tb, t).reshape(len(rows), in_f)
+    for batch in (1, 4, 8):
+        x = W.c5_x(batch, in_f).numpy()
+        say("c5 %s gemv b=%d" % (name, batch))
+        y = torch.full((batch, out_f), float("nan"), dtype=torch.float32, device="cuda")
+        ecco.ecco_decode_gemv(bd, tdev, t, out_f, in_f, torch.from_numpy(x).cuda(), batch, y)
+        torch.cuda.synchronize()
+        y_ref, mag = ogemv.gemv_ref(w_hat, x)
+        ok, worst = ogemv.gemv_tolerance_ok(y.cpu().numpy()[:, rows], y_ref, mag, in_f)
+        assert ok, "c5 %s b=%d worst error / bound = %g" % (name, batch, worst)
+        assert not np.any(np.isnan(y.cpu().numpy()))
