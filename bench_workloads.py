@@ -1,0 +1,182 @@
+"""Secondary workloads of bench.py (see its docstring): kv, model, ffn."""
+
+import os
+import time
+
+import numpy as np
+
+HBM_PEAK_GBPS = 8000.0
+BYTES_PER_GROUP = 64 + 256
+
+
+def _events(torch, n):
+    return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+
+def _timed(torch, fn, steps, warmup):
+    """Run fn() warmup + steps times; per-call HIP event durations (seconds)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    evs = []
+    for _ in range(steps):
+        a, b = _events(torch, 2)
+        a.record()
+        fn()
+        b.record()
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) * 1e-3 for a, b in evs]
+
+
+def _line(metric, value, unit, args, ms_per_step, config, **extra):
+    d = {"metric": metric, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": args.steps,
+         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+         "scaling": "weak", "vs_baseline": None, "dtype": "fp16 tensors, fp32 arithmetic, u8 blocks",
+         "data": "synthetic", "config": config}
+    d.update(extra)
+    return d
+
+
+def bench_kv(args, torch, ecco, W):
+    B, H, S, D = W.KV_SHAPE
+    T = W.KV_APPEND
+    caches = {}
+    for kind in ("k", "v"):
+        sample = W.kv_sample(kind)
+        blob = ecco.ecco_train_patterns(sample, threads=min(16, os.cpu_count() or 1))
+        amax = float(np.max(np.abs(sample.numpy().astype(np.float32))))
+        t = ecco.ecco_tensor_scale_from_amax(amax)          # fixed ahead of time (online codec)
+        x = W.kv_tensor(kind).cuda()
+        tdev = ecco.tables_to_device(blob)
+        blocks = torch.empty((B, H, S, 64), dtype=torch.uint8, device="cuda")
+        ecco.ecco_encode(x, B * H, S - T, S * D, S, tdev, t, blocks)
+        caches[kind] = dict(x=x, t=t, tdev=tdev, blocks=blocks, y=torch.empty_like(x))
+    torch.cuda.synchronize()
+
+    def append():
+        for c in caches.values():
+            ecco.ecco_encode(c["x"][:, :, S - T:], B * H, T, S * D, S, c["tdev"], c["t"], c["blocks"][:, :, S - T:])
+
+    def decode():
+        for c in caches.values():
+            ecco.ecco_decode(c["blocks"], 1, B * H * S, B * H * S, B * H * S * D, c["tdev"], c["t"], c["y"])
+
+    t_app = _timed(torch, append, args.steps, args.warmup)
+    t_dec = _timed(torch, decode, args.steps, args.warmup)
+    g_dec = 2 * B * H * S
+    g_app = 2 * B * H * T
+    dec = g_dec * BYTES_PER_GROUP / np.mean(t_dec) / 1e9
+    app = g_app * BYTES_PER_GROUP / np.mean(t_app) / 1e9
+    return _line("decode GB/s (compressed in + fp16 out), 1 GPU", dec, "GB/s", args,
+                 (np.mean(t_dec) + np.mean(t_app)) * 1e3,
+                 {"workload": "kv-cache K,V [16,8,8192,128]: append-encode 256 tokens, decode whole cache",
+                  "decode_groups": g_dec, "append_groups": g_app},
+                 decode_frac_of_hbm_peak=round(dec / HBM_PEAK_GBPS, 4),
+                 append_encode_GBps=round(app, 1), append_encode_us=round(np.mean(t_app) * 1e6, 2),
+                 decode_us=round(np.mean(t_dec) * 1e6, 2))
+
+
+def bench_model(args, torch, ecco, W):
+    """32 LLaMA-3-8B-shaped layers encoded once; sustained decode of all 224
+    matrices into one reused FP16 buffer.  Weights are drawn on the GPU (the
+    same recipe as workloads.llama_matrix, with torch's device generator) to
+    keep start-up short; the seven table sets of one layer are reused."""
+    tabs = {}
+    for nm in W.LAYER_ORDER:
+        blob = ecco.ecco_train_patterns(W.c2_sample(nm), threads=min(16, os.cpu_count() or 1))
+        tabs[nm] = ecco.tables_to_device(blob)
+    mats = []
+    gen = torch.Generator(device="cuda")
+    amax = torch.zeros(1, dtype=torch.float32, device="cuda")
+    t0 = time.time()
+    for layer in range(32):
+        for m, nm in enumerate(W.LAYER_ORDER):
+            out_f, in_f = W.LLAMA3_8B_LAYER[nm]
+            gen.manual_seed(100 + 10 * layer + m)
+            s = torch.exp(0.5 * torch.randn(out_f, 1, generator=gen, device="cuda"))
+            w = (s * torch.randn(out_f, in_f, generator=gen, device="cuda")).reshape(-1)
+            idx = torch.randint(0, w.numel(), (int(round(0.0005 * w.numel())),), generator=gen, device="cuda")
+            w[idx] *= 20.0
+            w = w.to(torch.float16).reshape(out_f, in_f)
+            ecco.ecco_amax(w, w.numel(), amax)
+            torch.cuda.synchronize()
+            t = ecco.ecco_tensor_scale_from_amax(amax.item())
+            blocks = torch.empty((out_f, in_f // 128, 64), dtype=torch.uint8, device="cuda")
+            ecco.ecco_encode(w, out_f, in_f // 128, in_f, in_f // 128, tabs[nm], t, blocks)
+            mats.append(dict(blocks=blocks, out_f=out_f, in_f=in_f, t=t, tdev=tabs[nm]))
+            del w, s, idx
+    torch.cuda.synchronize()
+    setup = time.time() - t0
+    ybuf = torch.empty(14336 * 4096, dtype=torch.float16, device="cuda")
+    groups = sum(m["out_f"] * m["in_f"] // 128 for m in mats)
+
+    def decode_all():
+        for m in mats:
+            g = m["in_f"] // 128
+            ecco.ecco_decode(m["blocks"], m["out_f"], g, g, m["in_f"], m["tdev"], m["t"], ybuf)
+
+    steps = max(3, args.steps // 4)
+    ts = _timed(torch, decode_all, steps, max(1, args.warmup // 2))
+    dec = groups * BYTES_PER_GROUP / np.mean(ts) / 1e9
+    args.steps = steps
+    return _line("decode GB/s (compressed in + fp16 out), 1 GPU", dec, "GB/s", args, np.mean(ts) * 1e3,
+                 {"workload": "32-layer LLaMA-3-8B-shaped weights (224 matrices), sustained decode",
+                  "groups": groups, "params": groups * 128,
+                  "weights": "device generator, same recipe as the layer workload"},
+                 decode_frac_of_hbm_peak=round(dec / HBM_PEAK_GBPS, 4),
+                 compressed_GB=round(groups * 64 / 1e9, 3), setup_s=round(setup, 1))
+
+
+def bench_ffn(args, torch, ecco, W):
+    out = {}
+    for name in ("w1", "w2"):
+        w = W.c5_matrix(name)
+        out_f, in_f = w.shape
+        blob = ecco.ecco_train_patterns(W.c5_sample(name), threads=min(16, os.cpu_count() or 1))
+        tdev = ecco.tables_to_device(blob)
+        wd = w.cuda()
+        amax = torch.zeros(1, dtype=torch.float32, device="cuda")
+        ecco.ecco_amax(wd, wd.numel(), amax)
+        torch.cuda.synchronize()
+        t = ecco.ecco_tensor_scale_from_amax(amax.item())
+        blocks = torch.empty((out_f, in_f // 128, 64), dtype=torch.uint8, device="cuda")
+        ecco.ecco_encode(wd, out_f, in_f // 128, in_f, in_f // 128, tdev, t, blocks)
+        del wd
+        wbuf = torch.empty((out_f, in_f), dtype=torch.float16, device="cuda")
+        for b in (1, 4, 8):
+            x = W.c5_x(b, in_f).cuda()
+            y = torch.empty((b, out_f), dtype=torch.float32, device="cuda")
+            tf = _timed(torch, lambda: ecco.ecco_decode_gemv(blocks, tdev, t, out_f, in_f, x, b, y),
+                        args.steps, args.warmup)
+
+            def unfused():
+                ecco.ecco_decode(blocks, out_f, in_f // 128, in_f // 128, in_f, tdev, t, wbuf)
+                torch.matmul(x, wbuf.t())
+
+            tu = _timed(torch, unfused, args.steps, args.warmup)
+            out["%s_b%d" % (name, b)] = dict(fused_us=round(np.mean(tf) * 1e6, 2),
+                                             decode_then_gemv_us=round(np.mean(tu) * 1e6, 2),
+                                             compressed_GBps=round(out_f * in_f / 2 / np.mean(tf) / 1e9, 1))
+        del wbuf
+    tot_f = sum(v["fused_us"] for v in out.values())
+    tot_u = sum(v["decode_then_gemv_us"] for v in out.values())
+    return _line("fused decode+GEMV speedup over decode then dense GEMV", tot_u / tot_f, "x", args,
+                 tot_f / 1e3, {"workload": "70B FFN [28672,8192] and [8192,28672], batch 1/4/8"},
+                 per_case=out)
+
+
+def bench_copy(args, torch, ecco, W):
+    nbytes = 1 << 30
+    a = torch.ones(nbytes // 2, dtype=torch.float16, device="cuda")
+    b = torch.empty_like(a)
+    ts = _timed(torch, lambda: b.copy_(a), args.steps, args.warmup)
+    gbps = 2 * nbytes / np.mean(ts) / 1e9
+    return _line("device-to-device copy GB/s (read + write)", gbps, "GB/s", args, np.mean(ts) * 1e3,
+                 {"workload": "copy 1 GiB fp16 buffer (torch copy_)", "bytes_read": nbytes,
+                  "bytes_written": nbytes}, frac_of_hbm_peak=round(gbps / HBM_PEAK_GBPS, 4))
+
+
+def run_workload(args, torch, ecco, W):
+    return {"kv": bench_kv, "model": bench_model, "ffn": bench_ffn,
+            "copy": bench_copy}[args.workload](args, torch, ecco, W)

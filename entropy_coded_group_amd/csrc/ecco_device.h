@@ -116,6 +116,20 @@ __device__ __forceinline__ float f16_value(uint32_t bits) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
 }
 
+// Streaming (non-temporal) 16-byte global accesses: decoded rows and
+// compressed blocks are touched once, and marking them so keeps them from
+// displacing cached lines; for a stream that is 80 % writes this matters
+// more than anything else in the memory system.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store_stream(void* p, uint4 v) {
+  const u32x4 w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(p));
+}
+__device__ __forceinline__ uint4 load_stream(const void* p) {
+  const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(w.x, w.y, w.z, w.w);
+}
+
 // 64-bit window shift: bits [r, r + 32) of hi:lo, r < 64.
 __device__ __forceinline__ uint32_t window(uint32_t lo, uint32_t hi, uint32_t r) {
   return (uint32_t)((((uint64_t)hi << 32) | lo) >> r);
@@ -139,24 +153,34 @@ __device__ __forceinline__ uint32_t div_magic(uint32_t n, DivMagic q) {
 
 // ------------------------------------------------------------- decode core
 //
-// One wavefront decodes a batch of up to 64 blocks.  Tables live in LDS for
-// the whole workgroup; every wave has a private staging area.
+// A wavefront decodes batches of up to 64 blocks.  The look-up tables live in
+// LDS for the whole workgroup; each wave has a private staging area:
+//   blk   64 x 17 dwords: the batch's blocks; after a lane has decoded its
+//         block, the block's 32-entry FP16 value table overwrites its words
+//   qsym  8 x 36 dwords: the 128 symbol bytes of 8 blocks at a time
 
-constexpr int kDecWaves = 8;
-constexpr int kBlkStride = 17;                   // dwords per staged block: 16 + 1 pad (column reads hit 32 banks)
+constexpr int kDecWaves = 16;                    // decode kernel: waves per workgroup (one workgroup per CU)
+constexpr int kGemvWaves = 12;                   // fused GEMV: its dot products need more registers
+constexpr int kBlkStride = 17;                   // dwords per staged block: 16 + 1 pad (column reads spread over banks)
 constexpr int kBlkWords = 64 * kBlkStride + 48;  // slack for reads past the last block
 constexpr int kDeadLut = S * H * 256;            // byte offset of the all-"clipped" look-up table
+constexpr int kSymStride = 36;                   // dwords per staged symbol row: 32 + 4 pad, keeps 16-byte
+                                                 // row writes of several lanes off a single group of banks
+constexpr int kPassBlocks = 8;                   // blocks whose symbols are staged at a time
+constexpr int kPasses = 64 / kPassBlocks;
+constexpr int kPassIters = kPassBlocks / 4;      // the transposed step handles 4 blocks per instruction
 
+template <int NW>
 struct DecodeSmem {
   uint8_t lut[S * H * 256 + 256];   // decode look-up tables + the clipped-stream table
   float cent[S * 16];
   float fp8[256];
-  uint32_t blk[kDecWaves][kBlkWords];   // staged blocks, later symbol bytes
-  uint32_t vtab[kDecWaves][64 * 16];    // per block: 32 FP16 reconstruction values
-  uint64_t aux[kDecWaves][64];          // per block: caller data (output offset)
+  uint32_t blk[NW][kBlkWords];
+  uint32_t qsym[NW][kPassBlocks * kSymStride];
 };
 
-__device__ __forceinline__ void stage_decode_tables(DecodeSmem& sm, const Tables* tab) {
+template <int NW>
+__device__ __forceinline__ void stage_decode_tables(DecodeSmem<NW>& sm, const Tables* tab) {
   const uint32_t tid = threadIdx.x;
   const uint4* src = reinterpret_cast<const uint4*>(&tab->lut[0][0][0]);
   uint4* dst = reinterpret_cast<uint4*>(sm.lut);
@@ -166,42 +190,60 @@ __device__ __forceinline__ void stage_decode_tables(DecodeSmem& sm, const Tables
   const float* c = &tab->centroids[0][0];
   for (uint32_t i = tid; i < S * 16; i += blockDim.x) sm.cent[i] = c[i];
   for (uint32_t i = tid; i < 256; i += blockDim.x) sm.fp8[i] = tab->fp8_value[i];
-  for (uint32_t i = tid; i < kDecWaves * kBlkWords; i += blockDim.x) (&sm.blk[0][0])[i] = 0;
+  for (uint32_t i = tid; i < NW * kBlkWords; i += blockDim.x) (&sm.blk[0][0])[i] = 0;
 }
 
-// Decode one batch.
-//   n_valid          blocks 0..n_valid-1 of the batch exist
-//   load(b, q)       16-byte chunk q (0..3) of block b (only called for valid b)
-//   prep(b)          per-block caller value, kept in sm.aux (called by lane b)
-//   sink(b, tq, half, aux, v)   8 decoded FP16 values (v.x = values 0,1 ...) of
-//                    block b at positions 64 * half + 8 * tq .. + 7
-// Steps: coalesced load to LDS; each lane decodes one block's stream with the
-// 8-bit-window look-up table, four codewords per bit-window refill, and
-// detects a clipped stream; builds the block's value table (15 centroids * a,
-// the scale S, then up to 16 outlier values -- or +0 for a clipped block);
-// stages symbol bytes (outlier positions overwritten by 16 + r) in two halves
-// and hands 8 values per lane to the sink, 8 lanes per block.
-template <class Load, class Prep, class Sink>
-__device__ __forceinline__ void decode_batch(DecodeSmem& sm, uint32_t wave, uint32_t lane, uint32_t n_valid,
-                                             float t, Load load, Prep prep, Sink sink) {
-  uint32_t* blk = sm.blk[wave];
-  uint32_t* vt = sm.vtab[wave];
-  // 1. coalesced load: lane l takes 16 bytes of block l/4 + 16 i
+// The 64 blocks of a batch as four 16-byte chunks per lane: chunk i of lane l
+// is bytes 16 (l & 3) .. + 15 of block l / 4 + 16 i (coalesced when the
+// blocks are contiguous).  Issued early so the loads overlap the previous
+// batch's decode.
+struct BatchRegs {
+  uint4 v[4];
+};
+
+// Blocks past n_valid read the last valid block instead (their output is
+// never stored), so the loads are unconditional: a conditional load would
+// make the compiler wait for it at once instead of letting it overlap.
+template <class Load>
+__device__ __forceinline__ BatchRegs fetch_batch(uint32_t lane, uint32_t n_valid, Load load) {
+  BatchRegs r;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const uint32_t b = (lane >> 2) + 16u * i, q = lane & 3u;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (b < n_valid) v = load(b, q);
-    uint32_t* d = blk + b * kBlkStride + 4u * q;
-    d[0] = v.x;
-    d[1] = v.y;
-    d[2] = v.z;
-    d[3] = v.w;
+    const uint32_t b = (lane >> 2) + 16u * i;
+    r.v[i] = load(min(b, n_valid - 1u), lane & 3u);
+  }
+  return r;
+}
+
+// Decode one staged batch (FULL: all 64 blocks exist, so no store is
+// predicated).
+//   sink(b, j0, v)            8 decoded FP16 values of block b at positions
+//                             j0 .. j0 + 7 (v.x holds values j0, j0 + 1, ...)
+// Steps: stage the batch in LDS; each lane decodes one block's codeword
+// stream with the 8-bit-window look-up table, four codewords per bit-window
+// refill, and marks a clipped stream; builds the block's value table (15
+// centroids * a, the scale S, up to 16 outlier values, or +0 for a clipped
+// block); then, 8 blocks at a time, stages the symbol bytes (outlier
+// positions overwritten by 16 + r) and hands 8 values per lane to the sink,
+// sixteen lanes per block and four blocks per instruction, so every store
+// instruction writes four whole 256-byte rows.
+template <bool FULL, int NW, class Sink>
+__device__ __forceinline__ void decode_batch(DecodeSmem<NW>& sm, uint32_t wave, uint32_t lane, uint32_t n_valid,
+                                             float t, const BatchRegs& in, Sink sink) {
+  uint32_t* blk = sm.blk[wave];
+  uint32_t* qs = sm.qsym[wave];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t* d = blk + ((lane >> 2) + 16u * i) * kBlkStride + 4u * (lane & 3u);
+    d[0] = in.v[i].x;
+    d[1] = in.v[i].y;
+    d[2] = in.v[i].z;
+    d[3] = in.v[i].w;
   }
   wave_sync();
 
-  // 2. lane-serial decode of block `lane`
-  const uint32_t* W = blk + lane * kBlkStride;
+  // 1. lane-serial decode of block `lane`
+  uint32_t* W = blk + lane * kBlkStride;
   uint32_t lo = W[0], hi = W[1];
   const uint32_t head = lo;
   uint32_t lutb = ((head & 63u) * 4u + ((head >> 6) & 3u)) * 256u;   // lut[p][h]
@@ -224,6 +266,7 @@ __device__ __forceinline__ void decode_batch(DecodeSmem& sm, uint32_t wave, uint
     const uint32_t e3 = sm.lut[lutb + (x & 255u)];
     const uint32_t r4 = r3 + (e3 >> 5) + 1u;
     uint32_t ev = e0 | (e1 << 8) | (e2 << 16) | (e3 << 24);
+    asm volatile("" : "+v"(ev));                 // pack now: keeps one register per 4 symbols
     if (base + r4 > lim) {
       // a codeword of this chunk ends past bit 512: the stream is clipped here
       const uint32_t m = (base + r1 > 512u ? 0x000000ffu : 0u) | (base + r2 > 512u ? 0x0000ff00u : 0u) |
@@ -243,7 +286,7 @@ __device__ __forceinline__ void decode_batch(DecodeSmem& sm, uint32_t wave, uint
   const uint32_t end = (kw - 2u) * 32u + r;
   const uint32_t n = full ? min(16u, (512u - end) / 15u) : 0u;
 
-  // 3. value table: [0..14] fp16(c * a), [15] fp16(S), [16 + r] outlier r (or +0 if clipped)
+  // 2. value table: [0..14] fp16(c * a), [15] fp16(S), [16 + r] outlier r (or +0 if clipped)
   const uint32_t p = head & 63u;
   const float S = sm.fp8[(head >> 8) & 255u] * t;
   const float aa = fabsf(S);
@@ -256,56 +299,69 @@ __device__ __forceinline__ void decode_batch(DecodeSmem& sm, uint32_t wave, uint
       const float v1 = s + 1 < 15 ? cp[s + 1] * aa : S;
       vtab[s / 2] = f16_bits(v0) | (f16_bits(v1) << 16);
     }
-#pragma unroll
-    for (int i = 8; i < 16; ++i) vtab[i] = 0;
   }
+  // all 16 record slots at once (records sit in words 8..15 at fixed places);
+  // slots r >= n are dropped
+  uint32_t tail[9];
+#pragma unroll
+  for (int i = 0; i < 9; ++i) tail[i] = W[8 + i];
   uint32_t jp[4] = {0, 0, 0, 0};               // outlier positions, byte r of jp[r / 4]
 #pragma unroll
+  for (int i = 8; i < 16; ++i) vtab[i] = 0;
+#pragma unroll
   for (int rr = 0; rr < 16; ++rr) {
-    if (!__any((uint32_t)rr < n)) break;
-    if ((uint32_t)rr < n) {
-      const uint32_t pos = 512u - 15u * (rr + 1);
-      const uint32_t wi = pos >> 5, sh = pos & 31u;
-      const uint32_t rec = window(W[wi], W[wi + 1], sh) & 0x7fffu;
-      const float v = sm.fp8[rec >> 7] * t;
-      vtab[8 + rr / 2] |= f16_bits(v) << (16 * (rr & 1));
-      jp[rr / 4] |= (rec & 127u) << (8 * (rr & 3));
-    }
+    if ((rr & 3) == 0 && !__any((uint32_t)rr < n)) break;
+    const uint32_t pos = 512u - 15u * (rr + 1);
+    const uint32_t wi = (pos >> 5) - 8u, sh = pos & 31u;
+    const uint32_t rec = window(tail[wi], tail[wi + 1], sh) & 0x7fffu;
+    const uint32_t hv = f16_bits(sm.fp8[rec >> 7] * t);
+    const bool use = (uint32_t)rr < n;
+    vtab[8 + rr / 2] |= (use ? hv : 0u) << (16 * (rr & 1));
+    jp[rr / 4] |= (rec & 127u) << (8 * (rr & 3));
   }
+  // the block's words are consumed: its value table takes their place
 #pragma unroll
-  for (int i = 0; i < 16; i += 4)
-    *reinterpret_cast<uint4*>(vt + lane * 16 + i) = make_uint4(vtab[i], vtab[i + 1], vtab[i + 2], vtab[i + 3]);
-  if (lane < n_valid) sm.aux[wave][lane] = prep(lane);
-  wave_sync();
+  for (int i = 0; i < 16; ++i) W[i] = vtab[i];
 
-  // 4. two halves of 64 symbols each
+  // 3. passes of kPassBlocks blocks
 #pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    uint32_t* Wm = blk + lane * kBlkStride;
+  for (int k = 0; k < kPasses; ++k) {
+    if (lane / kPassBlocks == (uint32_t)k) {
+      uint32_t* Q = qs + (lane % kPassBlocks) * kSymStride;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) Wm[i] = E[16 * half + i];
+      for (int i = 0; i < 32; i += 4) *reinterpret_cast<uint4*>(Q + i) = make_uint4(E[i], E[i + 1], E[i + 2], E[i + 3]);
+      // outlier positions take symbol 16 + r, in record order so that a
+      // later record wins a repeated position; slots r >= n write to the
+      // row's pad bytes instead
+      uint8_t* Qb = reinterpret_cast<uint8_t*>(Q);
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) {
-      if ((uint32_t)rr < n) {
+      for (int rr = 0; rr < 16; ++rr) {
         const uint32_t j = (jp[rr / 4] >> (8 * (rr & 3))) & 127u;
-        if ((j >> 6) == (uint32_t)half) reinterpret_cast<uint8_t*>(Wm)[j & 63u] = (uint8_t)(16 + rr);
+        Qb[(uint32_t)rr < n ? j : 128u + (rr & 15u)] = (uint8_t)(16 + rr);
       }
     }
     wave_sync();
-#pragma unroll 2
-    for (int it = 0; it < 8; ++it) {
-      const uint32_t bl = it * 8u + (lane >> 3), tq = lane & 7u;
-      const uint32_t* sw = blk + bl * kBlkStride + 2u * tq;
-      const uint32_t s0 = sw[0], s1 = sw[1];
-      const uint16_t* tb = reinterpret_cast<const uint16_t*>(vt + bl * 16u);
-      uint4 o;
-      o.x = (uint32_t)tb[s0 & 31u] | ((uint32_t)tb[(s0 >> 8) & 31u] << 16);
-      o.y = (uint32_t)tb[(s0 >> 16) & 31u] | ((uint32_t)tb[(s0 >> 24) & 31u] << 16);
-      o.z = (uint32_t)tb[s1 & 31u] | ((uint32_t)tb[(s1 >> 8) & 31u] << 16);
-      o.w = (uint32_t)tb[(s1 >> 16) & 31u] | ((uint32_t)tb[(s1 >> 24) & 31u] << 16);
-      if (bl < n_valid) sink(bl, tq, (uint32_t)half, sm.aux[wave][bl], o);
+    uint2 sv[kPassIters];
+#pragma unroll
+    for (int it = 0; it < kPassIters; ++it)
+      sv[it] = *reinterpret_cast<const uint2*>(qs + (it * 4u + (lane >> 4)) * kSymStride + 2u * (lane & 15u));
+    uint4 o[kPassIters];
+#pragma unroll
+    for (int it = 0; it < kPassIters; ++it) {
+      const uint32_t bl = kPassBlocks * k + it * 4u + (lane >> 4);
+      const uint16_t* tb = reinterpret_cast<const uint16_t*>(blk + bl * kBlkStride);
+      const uint32_t s0 = sv[it].x, s1 = sv[it].y;
+      o[it].x = (uint32_t)tb[s0 & 31u] | ((uint32_t)tb[(s0 >> 8) & 31u] << 16);
+      o[it].y = (uint32_t)tb[(s0 >> 16) & 31u] | ((uint32_t)tb[(s0 >> 24) & 31u] << 16);
+      o[it].z = (uint32_t)tb[s1 & 31u] | ((uint32_t)tb[(s1 >> 8) & 31u] << 16);
+      o[it].w = (uint32_t)tb[(s1 >> 16) & 31u] | ((uint32_t)tb[(s1 >> 24) & 31u] << 16);
     }
     wave_sync();
+#pragma unroll
+    for (int it = 0; it < kPassIters; ++it) {
+      const uint32_t bl = kPassBlocks * k + it * 4u + (lane >> 4);
+      if (FULL || bl < n_valid) sink(bl, 8u * (lane & 15u), o[it]);
+    }
   }
 }
 

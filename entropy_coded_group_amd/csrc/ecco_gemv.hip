@@ -36,41 +36,61 @@ struct GemvArgs {
 };
 
 template <int BM>
-__global__ __launch_bounds__(kDecWaves * 64) void gemv_kernel(GemvArgs a) {
-  __shared__ DecodeSmem sm;
+__global__ __launch_bounds__(kGemvWaves * 64) void gemv_kernel(GemvArgs a) {
+  __shared__ DecodeSmem<kGemvWaves> sm;
   stage_decode_tables(sm, a.tab);
   __syncthreads();
   const uint32_t lane = lane_id(), wave = threadIdx.x >> 6;
-  for (uint32_t row = blockIdx.x * kDecWaves + wave; row < a.out_f; row += gridDim.x * kDecWaves) {
-    float part[BM];
+  const uint32_t stride = gridDim.x * kGemvWaves;
+  uint32_t row = wave * gridDim.x + blockIdx.x;   // rows go round the CUs first
+  if (row >= a.out_f) return;
+  auto fetch = [&](uint32_t rw, uint32_t c0) {
+    const uint8_t* rowblk = a.blocks + ((uint64_t)rw * a.gpr + c0) * 64u;
+    return fetch_batch(lane, min(64u, a.gpr - c0), [&](uint32_t b, uint32_t q) {
+      return *reinterpret_cast<const uint4*>(rowblk + (uint64_t)b * 64u + 16u * q);
+    });
+  };
+  float part[BM];
 #pragma unroll
-    for (int b = 0; b < BM; ++b) part[b] = 0.0f;
-    const uint8_t* rowblk = a.blocks + (uint64_t)row * a.gpr * 64u;
-    for (uint32_t c0 = 0; c0 < a.gpr; c0 += 64u) {
-      const uint32_t n_valid = min(64u, a.gpr - c0);
-      auto load = [&](uint32_t b, uint32_t q) -> uint4 {
-        return *reinterpret_cast<const uint4*>(rowblk + (uint64_t)(c0 + b) * 64u + 16u * q);
-      };
-      auto prep = [&](uint32_t b) -> uint64_t { return (uint64_t)(c0 + b) * 128u; };
-      auto sink = [&](uint32_t, uint32_t tq, uint32_t half, uint64_t col, uint4 w) {
-        const uint16_t* xp = a.x + col + 64u * half + 8u * tq;
+  for (int b = 0; b < BM; ++b) part[b] = 0.0f;
+  uint32_t c0 = 0;
+  BatchRegs cur = fetch(row, 0);
+  while (true) {
+    uint32_t nrow = row, nc0 = c0 + 64u;
+    if (nc0 >= a.gpr) {
+      nrow = row + stride;
+      nc0 = 0;
+    }
+    const BatchRegs nxt = nrow < a.out_f ? fetch(nrow, nc0) : fetch(row, c0);
+    auto sink = [&](uint32_t b, uint32_t j0, uint4 w) {
+      const uint16_t* xp = a.x + (uint64_t)(c0 + b) * 128u + j0;
 #pragma unroll
-        for (int b = 0; b < BM; ++b) {
-          if ((uint32_t)b < a.batch) {
-            const uint4 xv = *reinterpret_cast<const uint4*>(xp + (uint64_t)b * a.in_f);
-            part[b] = dot8(w, xv, part[b]);
-          }
+      for (int b2 = 0; b2 < BM; ++b2) {
+        if ((uint32_t)b2 < a.batch) {
+          const uint4 xv = *reinterpret_cast<const uint4*>(xp + (uint64_t)b2 * a.in_f);
+          part[b2] = dot8(w, xv, part[b2]);
         }
-      };
-      decode_batch(sm, wave, lane, n_valid, a.t, load, prep, sink);
-    }
+      }
+    };
+    const uint32_t n_valid = min(64u, a.gpr - c0);
+    if (n_valid == 64u)
+      decode_batch<true>(sm, wave, lane, 64u, a.t, cur, sink);
+    else
+      decode_batch<false>(sm, wave, lane, n_valid, a.t, cur, sink);
+    if (c0 + 64u >= a.gpr) {
 #pragma unroll
-    for (int b = 0; b < BM; ++b) {
-      float v = part[b];
+      for (int b = 0; b < BM; ++b) {
+        float v = part[b];
 #pragma unroll
-      for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-      if (lane == 0 && (uint32_t)b < a.batch) a.y[(uint64_t)b * a.out_f + row] = v;
+        for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+        if (lane == 0 && (uint32_t)b < a.batch) a.y[(uint64_t)b * a.out_f + row] = v;
+        part[b] = 0.0f;
+      }
     }
+    if (nrow >= a.out_f) break;
+    row = nrow;
+    c0 = nc0;
+    cur = nxt;
   }
 }
 
@@ -98,17 +118,16 @@ extern "C" int ecco_decode_gemv(const void* blocks, const void* tables, float te
   a.gpr = (uint32_t)(in_f / 128);
   a.batch = (uint32_t)batch;
   a.t = tensor_scale;
-  const uint32_t want = (a.out_f + kDecWaves - 1) / kDecWaves;
-  const uint32_t grid = std::max<uint32_t>(1, std::min<uint32_t>(want, (uint32_t)cus));
+  const uint32_t grid = std::max<uint32_t>(1, std::min<uint32_t>(a.out_f, (uint32_t)cus));
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   if (batch == 1)
-    hipLaunchKernelGGL(gemv_kernel<1>, dim3(grid), dim3(kDecWaves * 64), 0, s, a);
+    hipLaunchKernelGGL(gemv_kernel<1>, dim3(grid), dim3(kGemvWaves * 64), 0, s, a);
   else if (batch <= 2)
-    hipLaunchKernelGGL(gemv_kernel<2>, dim3(grid), dim3(kDecWaves * 64), 0, s, a);
+    hipLaunchKernelGGL(gemv_kernel<2>, dim3(grid), dim3(kGemvWaves * 64), 0, s, a);
   else if (batch <= 4)
-    hipLaunchKernelGGL(gemv_kernel<4>, dim3(grid), dim3(kDecWaves * 64), 0, s, a);
+    hipLaunchKernelGGL(gemv_kernel<4>, dim3(grid), dim3(kGemvWaves * 64), 0, s, a);
   else
-    hipLaunchKernelGGL(gemv_kernel<8>, dim3(grid), dim3(kDecWaves * 64), 0, s, a);
+    hipLaunchKernelGGL(gemv_kernel<8>, dim3(grid), dim3(kGemvWaves * 64), 0, s, a);
   return hipGetLastError() == hipSuccess ? ECCO_OK : ECCO_EHIP;
 }

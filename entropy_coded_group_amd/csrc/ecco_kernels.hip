@@ -50,34 +50,48 @@ struct DecodeArgs {
 };
 
 __global__ __launch_bounds__(kDecWaves * 64) void decode_kernel(DecodeArgs a) {
-  __shared__ DecodeSmem sm;
+  __shared__ DecodeSmem<kDecWaves> sm;
   stage_decode_tables(sm, a.tab);
   __syncthreads();
   const uint32_t lane = lane_id(), wave = threadIdx.x >> 6;
-  for (uint32_t batch = blockIdx.x * kDecWaves + wave; batch < a.n_batches; batch += gridDim.x * kDecWaves) {
+  const uint32_t stride = gridDim.x * kDecWaves;
+  auto src_of = [&](uint32_t gidx) -> const uint8_t* {
+    if (a.contiguous) return a.blocks + (uint64_t)gidx * 64u;
+    const uint32_t r = div_magic(gidx, a.gpr), g = gidx - r * a.gpr.d;
+    return a.blocks + ((uint64_t)r * a.blk_stride + g) * 64u;
+  };
+  auto fetch = [&](uint32_t batch) {
     const uint32_t g0 = batch * 64u;
-    const uint32_t n_valid = min(64u, a.n_groups - g0);
-    auto load = [&](uint32_t b, uint32_t q) -> uint4 {
+    return fetch_batch(lane, min(64u, a.n_groups - g0), [&](uint32_t b, uint32_t q) {
+      return load_stream(src_of(g0 + b) + 16u * q);
+    });
+  };
+  // batches go round the CUs first, so a small tensor still spreads over all of them
+  uint32_t batch = wave * gridDim.x + blockIdx.x;
+  if (batch >= a.n_batches) return;
+  BatchRegs cur = fetch(batch);
+  for (; batch < a.n_batches; batch += stride) {
+    // prefetch the next batch (a valid one even past the end: loads stay unconditional)
+    const uint32_t nb = batch + stride;
+    const BatchRegs nxt = fetch(nb < a.n_batches ? nb : batch);
+    const uint32_t g0 = batch * 64u;
+    auto sink = [&](uint32_t b, uint32_t j0, uint4 v) {
       const uint32_t gidx = g0 + b;
-      const uint8_t* src;
+      uint64_t yoff;
       if (a.contiguous) {
-        src = a.blocks + (uint64_t)gidx * 64u;
+        yoff = (uint64_t)gidx * 128u;
       } else {
         const uint32_t r = div_magic(gidx, a.gpr), g = gidx - r * a.gpr.d;
-        src = a.blocks + ((uint64_t)r * a.blk_stride + g) * 64u;
+        yoff = (uint64_t)r * a.y_stride + (uint64_t)g * 128u;
       }
-      return *reinterpret_cast<const uint4*>(src + 16u * q);
+      store_stream(a.y + yoff + j0, v);
     };
-    auto prep = [&](uint32_t b) -> uint64_t {
-      const uint32_t gidx = g0 + b;
-      if (a.contiguous) return (uint64_t)gidx * 128u;
-      const uint32_t r = div_magic(gidx, a.gpr), g = gidx - r * a.gpr.d;
-      return (uint64_t)r * a.y_stride + (uint64_t)g * 128u;
-    };
-    auto sink = [&](uint32_t, uint32_t tq, uint32_t half, uint64_t yoff, uint4 v) {
-      *reinterpret_cast<uint4*>(a.y + yoff + 64u * half + 8u * tq) = v;
-    };
-    decode_batch(sm, wave, lane, n_valid, a.t, load, prep, sink);
+    const uint32_t n_valid = min(64u, a.n_groups - g0);
+    if (n_valid == 64u)
+      decode_batch<true>(sm, wave, lane, 64u, a.t, cur, sink);
+    else
+      decode_batch<false>(sm, wave, lane, n_valid, a.t, cur, sink);
+    cur = nxt;
   }
 }
 
@@ -301,6 +315,8 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(EncodeArgs a) {
 __global__ void amax_init_kernel(float* out) { *out = 0.0f; }
 
 __global__ __launch_bounds__(256) void amax_kernel(const uint16_t* x, uint64_t n, float* out) {
+  // |x| bit patterns of finite FP16 values order like the values (NaN ignored)
+  __shared__ uint32_t red[4];
   uint32_t m = 0;
   const uint64_t n8 = n / 8;
   const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
@@ -310,20 +326,22 @@ __global__ __launch_bounds__(256) void amax_kernel(const uint16_t* x, uint64_t n
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       uint32_t a0 = w[k] & 0x7fffu, a1 = (w[k] >> 16) & 0x7fffu;
-      a0 = a0 > 0x7c00u ? 0u : a0;   // NaN ignored
+      a0 = a0 > 0x7c00u ? 0u : a0;
       a1 = a1 > 0x7c00u ? 0u : a1;
       m = max(m, max(a0, a1));
     }
   }
   for (uint64_t i = n8 * 8 + (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
-    uint32_t a0 = x[i] & 0x7fffu;
+    const uint32_t a0 = x[i] & 0x7fffu;
     m = max(m, a0 > 0x7c00u ? 0u : a0);
   }
-  // wave reduction, then one atomic per wave (|x| bit patterns order like values)
+  // wave, then workgroup reduction: one atomic per workgroup
   for (int o = 32; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
-  if (lane_id() == 0 && m) {
-    const float f = f16_value(m);
-    atomicMax(reinterpret_cast<unsigned int*>(out), __float_as_uint(f));
+  if (lane_id() == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    m = max(max(red[0], red[1]), max(red[2], red[3]));
+    if (m) atomicMax(reinterpret_cast<unsigned int*>(out), __float_as_uint(f16_value(m)));
   }
 }
 
@@ -371,7 +389,7 @@ extern "C" int ecco_amax(const uint16_t* x, uint64_t n, float* amax, void* strea
   (void)hipGetLastError();
   hipLaunchKernelGGL(amax_init_kernel, dim3(1), dim3(1), 0, s, amax);
   uint64_t want = (n / 8 + 255) / 256;
-  uint32_t grid = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(want, (uint64_t)cus * 8));
+  uint32_t grid = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(want, (uint64_t)cus * 2));
   hipLaunchKernelGGL(amax_kernel, dim3(grid), dim3(256), 0, s, x, n, amax);
   return launch_status();
 }
@@ -430,8 +448,7 @@ extern "C" int ecco_decode(const void* blocks, uint64_t n_rows, uint64_t gpr, ui
   a.n_batches = (uint32_t)((total + 63) / 64);
   a.t = tensor_scale;
   a.contiguous = (n_rows == 1 || (blk_stride == gpr && y_stride == gpr * 128)) ? 1u : 0u;
-  uint32_t want = (a.n_batches + kDecWaves - 1) / kDecWaves;
-  uint32_t grid = std::max<uint32_t>(1, std::min<uint32_t>(want, (uint32_t)cus));
+  const uint32_t grid = std::max<uint32_t>(1, std::min<uint32_t>(a.n_batches, (uint32_t)cus));
   (void)hipGetLastError();
   hipLaunchKernelGGL(decode_kernel, dim3(grid), dim3(kDecWaves * 64), 0, static_cast<hipStream_t>(stream), a);
   return launch_status();
