@@ -94,6 +94,34 @@ def d2d_copy_gbps(torch, nbytes=1 << 30, reps=20):
     return 2 * nbytes / sec / 1e9
 
 
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "decode_kernel__llama3-8b-layer__traffic.json")
+DECODE_SOURCES = ["entropy_coded_group_amd/csrc/ecco_device.h", "entropy_coded_group_amd/csrc/ecco_kernels.hip",
+                  "entropy_coded_group_amd/csrc/ecco_internal.h"]
+
+
+def decode_sources_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for f in DECODE_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per decode launch from the calibrated FETCH_SIZE / WRITE_SIZE
+    counters of a profiled run, or None when the decode sources have changed
+    since those counters were taken."""
+    try:
+        with open(TRAFFIC_RECORD) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if rec.get("sources_sha256") != decode_sources_sha256():
+        return None
+    return round(rec["bytes_per_launch"], 0)
+
+
 def cpu_baseline(x_groups, tables_blob, t, n_groups):
     """The oracle (vectorised NumPy, one process) on the first n_groups groups."""
     import entropy_coded_group_amd as ecco
@@ -234,7 +262,7 @@ def main():
                      "frac": round(res["decode_GBps"] / HBM_PEAK_GBPS, 4),
                      "bytes_per_launch": res["decode_bytes_per_launch"],
                      "avg_launch_us": round(res["decode_launch_us"], 3),
-                     "traffic": None},
+                     "traffic": measured_traffic()},
     }
     if not args.no_cpu_baseline:
         cb = cpu_baseline(x0, blob0, t0, args.cpu_groups)

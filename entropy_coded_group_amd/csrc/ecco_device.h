@@ -157,16 +157,16 @@ __device__ __forceinline__ uint32_t div_magic(uint32_t n, DivMagic q) {
 // LDS for the whole workgroup; each wave has a private staging area:
 //   blk   64 x 17 dwords: the batch's blocks; after a lane has decoded its
 //         block, the block's 32-entry FP16 value table overwrites its words
-//   qsym  8 x 36 dwords: the 128 symbol bytes of 8 blocks at a time
+//   qsym  16 x 36 dwords: the 128 symbol bytes of 16 blocks at a time
 
-constexpr int kDecWaves = 16;                    // decode kernel: waves per workgroup (one workgroup per CU)
-constexpr int kGemvWaves = 12;                   // fused GEMV: its dot products need more registers
+constexpr int kDecWaves = 12;                    // decode kernel: waves per workgroup (one workgroup per CU)
+constexpr int kGemvWaves = 12;                   // fused decode+GEMV: waves per workgroup
 constexpr int kBlkStride = 17;                   // dwords per staged block: 16 + 1 pad (column reads spread over banks)
 constexpr int kBlkWords = 64 * kBlkStride + 48;  // slack for reads past the last block
 constexpr int kDeadLut = S * H * 256;            // byte offset of the all-"clipped" look-up table
 constexpr int kSymStride = 36;                   // dwords per staged symbol row: 32 + 4 pad, keeps 16-byte
                                                  // row writes of several lanes off a single group of banks
-constexpr int kPassBlocks = 8;                   // blocks whose symbols are staged at a time
+constexpr int kPassBlocks = 16;                  // blocks whose symbols are staged at a time
 constexpr int kPasses = 64 / kPassBlocks;
 constexpr int kPassIters = kPassBlocks / 4;      // the transposed step handles 4 blocks per instruction
 
@@ -223,7 +223,7 @@ __device__ __forceinline__ BatchRegs fetch_batch(uint32_t lane, uint32_t n_valid
 // stream with the 8-bit-window look-up table, four codewords per bit-window
 // refill, and marks a clipped stream; builds the block's value table (15
 // centroids * a, the scale S, up to 16 outlier values, or +0 for a clipped
-// block); then, 8 blocks at a time, stages the symbol bytes (outlier
+// block); then, 16 blocks at a time, stages the symbol bytes (outlier
 // positions overwritten by 16 + r) and hands 8 values per lane to the sink,
 // sixteen lanes per block and four blocks per instruction, so every store
 // instruction writes four whole 256-byte rows.
@@ -336,6 +336,7 @@ __device__ __forceinline__ void decode_batch(DecodeSmem<NW>& sm, uint32_t wave, 
       uint8_t* Qb = reinterpret_cast<uint8_t*>(Q);
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) {
+        if ((rr & 3) == 0 && !__any((uint32_t)rr < n)) break;
         const uint32_t j = (jp[rr / 4] >> (8 * (rr & 3))) & 127u;
         Qb[(uint32_t)rr < n ? j : 128u + (rr & 15u)] = (uint8_t)(16 + rr);
       }
