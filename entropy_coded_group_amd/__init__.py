@@ -19,8 +19,8 @@ __all__ = [
     "EccoError", "lib", "library_path",
     "ecco_tables_size", "ecco_tables_build", "ecco_tables_validate", "ecco_tables_get",
     "ecco_train_patterns", "ecco_tensor_scale_from_amax", "ecco_amax", "ecco_encode",
-    "ecco_decode", "ecco_decode_gemv", "ecco_strerror", "ecco_version",
-    "STATS_FIELDS", "tables_to_device",
+    "ecco_decode", "ecco_decode_many", "ecco_decode_gemv", "ecco_strerror", "ecco_version",
+    "STATS_FIELDS", "DECODE_MAX_JOBS", "tables_to_device",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -46,6 +46,17 @@ class TrainOpts(ctypes.Structure):
                 ("seed", ctypes.c_uint64), ("max_groups", ctypes.c_uint32), ("threads", ctypes.c_uint32)]
 
 
+DECODE_MAX_JOBS = 16
+
+
+class DecodeJob(ctypes.Structure):
+    """ecco_decode_job_t."""
+    _fields_ = [("blocks_dev", ctypes.c_void_p), ("y_dev", ctypes.c_void_p), ("tables_dev", ctypes.c_void_p),
+                ("n_rows", ctypes.c_uint64), ("groups_per_row", ctypes.c_uint64),
+                ("blk_row_stride_blocks", ctypes.c_uint64), ("y_row_stride_elems", ctypes.c_uint64),
+                ("tensor_scale", ctypes.c_float), ("reserved", ctypes.c_uint32)]
+
+
 _lib = None
 
 
@@ -67,6 +78,7 @@ def lib():
             "ecco_amax": (i32, [vp, u64, vp, vp]),
             "ecco_encode": (i32, [vp, u64, u64, u64, u64, vp, f32, vp, vp, vp]),
             "ecco_decode": (i32, [vp, u64, u64, u64, u64, vp, f32, vp, vp]),
+            "ecco_decode_many": (i32, [vp, ctypes.c_uint32, vp]),
             "ecco_decode_gemv": (i32, [vp, vp, f32, i64, i64, vp, i64, vp, vp]),
             "ecco_strerror": (ctypes.c_char_p, [i32]),
             "ecco_version": (ctypes.c_char_p, []),
@@ -183,6 +195,18 @@ def ecco_decode(blocks, n_rows, groups_per_row, blk_row_stride_blocks, y_row_str
     _check(lib().ecco_decode(_ptr(blocks), int(n_rows), int(groups_per_row), int(blk_row_stride_blocks),
                              int(y_row_stride_elems), _ptr(tables_dev), float(tensor_scale), _ptr(y),
                              _stream(stream)), "ecco_decode")
+
+
+def ecco_decode_many(jobs, stream=None):
+    """jobs: a sequence of (blocks, n_rows, groups_per_row, blk_row_stride_blocks,
+    y_row_stride_elems, tables_dev, tensor_scale, y) tuples -- the arguments of
+    ecco_decode, one tuple per tensor -- decoded in one launch."""
+    arr = (DecodeJob * max(1, len(jobs)))()
+    for i, (blocks, n_rows, gpr, bstride, ystride, tables_dev, t, y) in enumerate(jobs):
+        arr[i] = DecodeJob(_ptr(blocks), _ptr(y), _ptr(tables_dev), int(n_rows), int(gpr), int(bstride),
+                           int(ystride), float(t), 0)
+    _check(lib().ecco_decode_many(ctypes.cast(arr, ctypes.c_void_p), len(jobs), _stream(stream)),
+           "ecco_decode_many")
 
 
 def ecco_decode_gemv(blocks, tables_dev, tensor_scale, out_features, in_features, x, batch, y, stream=None):

@@ -27,6 +27,7 @@
 // binary32 operations (the library is built with -ffp-contract=off).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstring>
 #include <mutex>
 
@@ -36,7 +37,9 @@ namespace ecco {
 
 // -------------------------------------------------------------------- decode
 
-struct DecodeArgs {
+// One tensor of a decode launch, and the contiguous range of workgroups that
+// decode it.
+struct DecodeJob {
   const uint8_t* blocks;
   uint16_t* y;
   const Tables* tab;
@@ -47,33 +50,47 @@ struct DecodeArgs {
   uint32_t n_batches;
   float t;
   uint32_t contiguous;
+  uint32_t wg_first, wg_count;
 };
 
-__global__ __launch_bounds__(kDecWaves * 64) void decode_kernel(DecodeArgs a) {
+constexpr int kMaxJobs = ECCO_DECODE_MAX_JOBS;
+
+struct DecodeArgs {
+  DecodeJob job[kMaxJobs];
+  uint32_t n_jobs;
+};
+
+// Each workgroup decodes one tensor, so the look-up tables it stages in LDS
+// serve every block it sees; a tensor's batches are split into contiguous
+// ranges over its workgroups and interleaved over the waves of each.
+__global__ __launch_bounds__(kDecWaves * 64) void decode_kernel(DecodeArgs args) {
   __shared__ DecodeSmem<kDecWaves> sm;
+  uint32_t j = 0;
+  while (j + 1 < args.n_jobs && blockIdx.x >= args.job[j + 1].wg_first) ++j;
+  const DecodeJob& a = args.job[j];
   stage_decode_tables(sm, a.tab);
   __syncthreads();
   const uint32_t lane = lane_id(), wave = threadIdx.x >> 6;
-  const uint32_t stride = gridDim.x * kDecWaves;
+  const uint32_t lw = blockIdx.x - a.wg_first;
+  const uint32_t b_end = (uint32_t)((uint64_t)a.n_batches * (lw + 1) / a.wg_count);
+  uint32_t batch = (uint32_t)((uint64_t)a.n_batches * lw / a.wg_count) + wave;
   auto src_of = [&](uint32_t gidx) -> const uint8_t* {
     if (a.contiguous) return a.blocks + (uint64_t)gidx * 64u;
     const uint32_t r = div_magic(gidx, a.gpr), g = gidx - r * a.gpr.d;
     return a.blocks + ((uint64_t)r * a.blk_stride + g) * 64u;
   };
-  auto fetch = [&](uint32_t batch) {
-    const uint32_t g0 = batch * 64u;
-    return fetch_batch(lane, min(64u, a.n_groups - g0), [&](uint32_t b, uint32_t q) {
-      return load_stream(src_of(g0 + b) + 16u * q);
+  auto fetch = [&](uint32_t b) {
+    const uint32_t g0 = b * 64u;
+    return fetch_batch(lane, min(64u, a.n_groups - g0), [&](uint32_t i, uint32_t q) {
+      return load_stream(src_of(g0 + i) + 16u * q);
     });
   };
-  // batches go round the CUs first, so a small tensor still spreads over all of them
-  uint32_t batch = wave * gridDim.x + blockIdx.x;
-  if (batch >= a.n_batches) return;
+  if (batch >= b_end) return;
   BatchRegs cur = fetch(batch);
-  for (; batch < a.n_batches; batch += stride) {
+  for (; batch < b_end; batch += kDecWaves) {
     // prefetch the next batch (a valid one even past the end: loads stay unconditional)
-    const uint32_t nb = batch + stride;
-    const BatchRegs nxt = fetch(nb < a.n_batches ? nb : batch);
+    const uint32_t nb = batch + kDecWaves;
+    const BatchRegs nxt = fetch(nb < b_end ? nb : batch);
     const uint32_t g0 = batch * 64u;
     auto sink = [&](uint32_t b, uint32_t j0, uint4 v) {
       const uint32_t gidx = g0 + b;
@@ -427,17 +444,19 @@ extern "C" int ecco_encode(const uint16_t* x, uint64_t n_rows, uint64_t gpr, uin
   return launch_status();
 }
 
-extern "C" int ecco_decode(const void* blocks, uint64_t n_rows, uint64_t gpr, uint64_t blk_stride,
-                           uint64_t y_stride, const void* tables, float tensor_scale, uint16_t* y, void* stream) {
+namespace {
+
+// Checks one decode job and fills its kernel descriptor (all but the
+// workgroup range).
+int make_decode_job(const void* blocks, uint64_t n_rows, uint64_t gpr, uint64_t blk_stride, uint64_t y_stride,
+                    const void* tables, float tensor_scale, uint16_t* y, DecodeJob* out) {
   if (!blocks || !tables || !y) return ECCO_EINVAL;
   if (!(tensor_scale > 0.0f) || !(tensor_scale < __builtin_huge_valf())) return ECCO_EINVAL;
   const uint64_t total = n_rows * gpr;
   if (n_rows == 0 || gpr == 0 || total >= (1ull << 32) || gpr >= (1ull << 32)) return ECCO_ESIZE;
   if (n_rows > 1 && (y_stride < gpr * 128 || blk_stride < gpr)) return ECCO_ESIZE;
   if (!host_aligned(y, 16) || (y_stride % 8) != 0 || !host_aligned(blocks, 64) || !host_aligned(tables, 256)) return ECCO_EALIGN;
-  int cus = 0, rc = check_gfx950(&cus);
-  if (rc) return rc;
-  DecodeArgs a;
+  DecodeJob& a = *out;
   a.blocks = static_cast<const uint8_t*>(blocks);
   a.y = y;
   a.tab = static_cast<const Tables*>(tables);
@@ -448,8 +467,72 @@ extern "C" int ecco_decode(const void* blocks, uint64_t n_rows, uint64_t gpr, ui
   a.n_batches = (uint32_t)((total + 63) / 64);
   a.t = tensor_scale;
   a.contiguous = (n_rows == 1 || (blk_stride == gpr && y_stride == gpr * 128)) ? 1u : 0u;
-  const uint32_t grid = std::max<uint32_t>(1, std::min<uint32_t>(a.n_batches, (uint32_t)cus));
+  a.wg_first = a.wg_count = 0;
+  return ECCO_OK;
+}
+
+// Splits the workgroups (at most one per CU, as many as there are batches)
+// among the jobs: one each, then each further workgroup to the job whose
+// workgroups carry the most batches.
+void assign_workgroups(DecodeArgs& args, uint32_t cus) {
+  uint64_t total = 0;
+  for (uint32_t j = 0; j < args.n_jobs; ++j) total += args.job[j].n_batches;
+  const uint32_t grid = (uint32_t)std::max<uint64_t>(args.n_jobs, std::min<uint64_t>(total, cus));
+  for (uint32_t j = 0; j < args.n_jobs; ++j) args.job[j].wg_count = 1;
+  for (uint32_t k = args.n_jobs; k < grid; ++k) {
+    uint32_t best = 0;
+    uint64_t best_load = 0;
+    for (uint32_t j = 0; j < args.n_jobs; ++j) {
+      const DecodeJob& a = args.job[j];
+      if (a.wg_count >= a.n_batches) continue;
+      const uint64_t load = (a.n_batches + a.wg_count - 1) / a.wg_count;
+      if (load > best_load) best_load = load, best = j;
+    }
+    if (best_load == 0) break;
+    args.job[best].wg_count++;
+  }
+  uint32_t first = 0;
+  for (uint32_t j = 0; j < args.n_jobs; ++j) {
+    args.job[j].wg_first = first;
+    first += args.job[j].wg_count;
+  }
+}
+
+int launch_decode(DecodeArgs& args, void* stream) {
+  int cus = 0, rc = check_gfx950(&cus);
+  if (rc) return rc;
+  assign_workgroups(args, (uint32_t)cus);
+  const DecodeJob& last = args.job[args.n_jobs - 1];
+  const uint32_t grid = last.wg_first + last.wg_count;
   (void)hipGetLastError();
-  hipLaunchKernelGGL(decode_kernel, dim3(grid), dim3(kDecWaves * 64), 0, static_cast<hipStream_t>(stream), a);
+  hipLaunchKernelGGL(decode_kernel, dim3(grid), dim3(kDecWaves * 64), 0, static_cast<hipStream_t>(stream), args);
   return launch_status();
+}
+
+}  // namespace
+
+extern "C" int ecco_decode(const void* blocks, uint64_t n_rows, uint64_t gpr, uint64_t blk_stride,
+                           uint64_t y_stride, const void* tables, float tensor_scale, uint16_t* y, void* stream) {
+  DecodeArgs args;
+  std::memset(&args, 0, sizeof(args));
+  args.n_jobs = 1;
+  int rc = make_decode_job(blocks, n_rows, gpr, blk_stride, y_stride, tables, tensor_scale, y, &args.job[0]);
+  if (rc) return rc;
+  return launch_decode(args, stream);
+}
+
+extern "C" int ecco_decode_many(const ecco_decode_job_t* jobs, uint32_t n_jobs, void* stream) {
+  if (!jobs) return ECCO_EINVAL;
+  if (n_jobs == 0 || n_jobs > (uint32_t)kMaxJobs) return ECCO_ESIZE;
+  DecodeArgs args;
+  std::memset(&args, 0, sizeof(args));
+  args.n_jobs = n_jobs;
+  for (uint32_t j = 0; j < n_jobs; ++j) {
+    const ecco_decode_job_t& q = jobs[j];
+    if (q.reserved != 0) return ECCO_EINVAL;
+    int rc = make_decode_job(q.blocks_dev, q.n_rows, q.groups_per_row, q.blk_row_stride_blocks,
+                             q.y_row_stride_elems, q.tables_dev, q.tensor_scale, q.y_dev, &args.job[j]);
+    if (rc) return rc;
+  }
+  return launch_decode(args, stream);
 }

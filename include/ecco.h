@@ -89,6 +89,7 @@ extern "C" {
 #define ECCO_LEN_MIN 2
 #define ECCO_LEN_MAX 8
 #define ECCO_GEMV_MAX_BATCH 8
+#define ECCO_DECODE_MAX_JOBS 16
 
 enum {
   ECCO_OK = 0,
@@ -179,6 +180,31 @@ int ecco_encode(const uint16_t* x_dev, uint64_t n_rows, uint64_t groups_per_row,
 int ecco_decode(const void* blocks_dev, uint64_t n_rows, uint64_t groups_per_row,
                 uint64_t blk_row_stride_blocks, uint64_t y_row_stride_elems,
                 const void* tables_dev, float tensor_scale, uint16_t* y_dev, void* stream);
+
+/* One tensor of an ecco_decode_many call: the arguments of ecco_decode. */
+typedef struct {
+  const void* blocks_dev;
+  uint16_t* y_dev;
+  const void* tables_dev;
+  uint64_t n_rows;
+  uint64_t groups_per_row;
+  uint64_t blk_row_stride_blocks;
+  uint64_t y_row_stride_elems;
+  float tensor_scale;
+  uint32_t reserved;          /* must be 0 */
+} ecco_decode_job_t;
+
+/* Decode several tensors, each with its own tables and scale, in one launch
+ * -- e.g. every weight matrix of a decoder layer.  Blocks carry everything
+ * their decode needs except the per-tensor side data ("Core claim"), so
+ * tensors with different tables can share one launch.  Each job follows the
+ * rules of ecco_decode; jobs_host (n_jobs in 1..ECCO_DECODE_MAX_JOBS) is read
+ * before the call returns.  If any job is invalid the call returns that
+ * job's error and enqueues nothing.  Outputs of different jobs must not
+ * overlap.  The GPU's workgroups are shared out in proportion to the jobs'
+ * sizes, so small tensors are decoded beside large ones rather than after
+ * them. */
+int ecco_decode_many(const ecco_decode_job_t* jobs_host, uint32_t n_jobs, void* stream);
 
 /* Fused decode + GEMV: y[b][o] = sum_i W[o][i] * x[b][i] with W the decoded
  * FP16 weights, products and sums in FP32 (plain FMA on the vector ALUs).

@@ -5,6 +5,8 @@ checks, training) behaves; no kernel is launched."""
 import os
 import re
 
+import ctypes
+
 import numpy as np
 import pytest
 
@@ -126,6 +128,27 @@ def test_device_entry_points_check_arguments_before_touching_the_device():
     assert L.ecco_decode_gemv(A, A, 1.0, 16, 100, A, 1, A, None) == -3          # in % 128
     assert L.ecco_decode_gemv(A, A, 1.0, 16, 128, A, 9, A, None) == -3          # batch > 8
     assert L.ecco_amax(A, 0, A, None) == -3
+    # ecco_decode_many: count, reserved field, and every job checked before launch
+    jobs = (ecco.DecodeJob * 3)()
+    for j in jobs:
+        j.blocks_dev, j.y_dev, j.tables_dev = A, A, A
+        j.n_rows, j.groups_per_row, j.blk_row_stride_blocks, j.y_row_stride_elems = 1, 4, 4, 512
+        j.tensor_scale = 1.0
+    jp = ctypes.cast(jobs, ctypes.c_void_p)
+    assert L.ecco_decode_many(None, 1, None) == -1
+    assert L.ecco_decode_many(jp, 0, None) == -3
+    assert L.ecco_decode_many(jp, ecco.DECODE_MAX_JOBS + 1, None) == -3
+    jobs[2].reserved = 1
+    assert L.ecco_decode_many(jp, 3, None) == -1
+    jobs[2].reserved = 0
+    jobs[1].y_dev = A + 2
+    assert L.ecco_decode_many(jp, 3, None) == -2
+    jobs[1].y_dev = A
+    jobs[2].tensor_scale = float("inf")
+    assert L.ecco_decode_many(jp, 3, None) == -1
+    jobs[2].tensor_scale = 1.0
+    jobs[0].n_rows, jobs[0].blk_row_stride_blocks = 2, 3
+    assert L.ecco_decode_many(jp, 3, None) == -3
     del blob
 
 

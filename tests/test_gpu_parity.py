@@ -237,6 +237,83 @@ def test_strided_kv_append_and_decode(dev):
     assert np.all(y.cpu().numpy()[:, :, :first] == 0x7FFF) and np.all(y.cpu().numpy()[:, :, first + ntok:] == 0x7FFF)
 
 
+def test_decode_many_mixed_jobs_exact(dev):
+    """Several tensors with their own tables, scales and layouts in one launch:
+    sizes from one group to several batches with ragged tails, a strided job,
+    clipping tables; every output element against the oracle, and nothing
+    written outside the jobs' outputs."""
+    specs = [("golden", 1, 1), ("random", 63, 2), ("adversarial", 64, 3), ("random", 65, 4),
+             ("golden", 1000, 5), ("random", 4097, 6), ("adversarial", 777, 7)]
+    jobs, refs, keep = [], [], []
+    for i, (kind, n, seed) in enumerate(specs):
+        tb = {"golden": lambda s: golden("c1"), "random": random_tables,
+              "adversarial": adversarial_tables}[kind](seed)
+        x = W.random_groups(n, 300 + seed, ("normal", "laplace", "wide")[i % 3]).numpy()
+        t = scale_of(x) * np.float32(1.0 + 0.25 * i)
+        ob = codec.encode_groups(x, tb, t)
+        tdev = dev_tables(tb)
+        bd = torch.from_numpy(ob).cuda()
+        yd = torch.full((n + 2, 128), 0x7FFF, dtype=torch.int16, device="cuda")
+        jobs.append((bd, 1, n, n, n * 128, tdev, t, yd[1:n + 1]))
+        refs.append(codec.decode_blocks(ob, tb, t))
+        keep.append((tdev, yd))
+    # a strided job: 5 rows of 300 groups inside rows of 320 blocks / 320*128 + 64 elements
+    tb = random_tables(8)
+    rows, gpr, bstride, ystride = 5, 300, 320, 320 * 128 + 64
+    x = W.random_groups(rows * gpr, 308, "laplace").numpy()
+    t = scale_of(x)
+    ob = codec.encode_groups(x, tb, t)
+    bfull = np.zeros((rows, bstride, 64), np.uint8)
+    bfull[:, :gpr] = ob.reshape(rows, gpr, 64)
+    tdev = dev_tables(tb)
+    bd = torch.from_numpy(bfull).cuda()
+    yd = torch.full((rows * ystride,), 0x7FFF, dtype=torch.int16, device="cuda")
+    jobs.append((bd, rows, gpr, bstride, ystride, tdev, t, yd))
+    keep.append((tdev, yd))
+    say("decode_many %d jobs" % len(jobs))
+    ecco.ecco_decode_many(jobs)
+    torch.cuda.synchronize()
+    for i, (ref, (_, yd)) in enumerate(zip(refs, keep)):
+        got = yd.cpu().numpy()
+        assert np.all(got[0] == 0x7FFF) and np.all(got[-1] == 0x7FFF), "job %d wrote outside its output" % i
+        assert_fp16_equal(got[1:-1].view(np.float16), ref, "decode_many job %d" % i)
+    got = keep[-1][1].cpu().numpy()
+    g2 = got.reshape(rows, ystride)
+    assert_fp16_equal(g2[:, :gpr * 128].reshape(-1, 128).view(np.float16), codec.decode_blocks(ob, tb, t),
+                      "decode_many strided job")
+    assert np.all(g2[:, gpr * 128:] == 0x7FFF)
+
+
+def test_decode_many_full_layer_sampled(dev):
+    """All seven matrices of a LLaMA-3-8B layer decoded in one launch, each
+    with its own tables and scale (the layer workload's decode step)."""
+    jobs, checks = [], []
+    for name in W.LAYER_ORDER:
+        tb = golden("c2_" + name)
+        tdev = dev_tables(tb)
+        say("layer %s generate + encode" % name)
+        w = W.c2_layer(0, names=[name])[name]
+        out_f, in_f = w.shape
+        t = scale_of(w.numpy())
+        wd = w.cuda()
+        bd = torch.empty((out_f, in_f // 128, 64), dtype=torch.uint8, device="cuda")
+        ecco.ecco_encode(wd, out_f, in_f // 128, in_f, in_f // 128, tdev, t, bd)
+        del wd
+        yd = torch.empty((out_f, in_f), dtype=torch.int16, device="cuda")
+        jobs.append((bd, out_f, in_f // 128, in_f // 128, in_f, tdev, t, yd))
+        G = out_f * in_f // 128
+        idx = sample_index(G, 211)
+        checks.append((name, tb, t, idx, w.numpy().reshape(-1, 128)[idx], bd, yd))
+    say("layer decode_many")
+    ecco.ecco_decode_many(jobs)
+    torch.cuda.synchronize()
+    for name, tb, t, idx, xg, bd, yd in checks:
+        ob = codec.encode_groups(xg, tb, t)
+        assert_blocks_equal(bd.cpu().numpy().reshape(-1, 64)[idx], ob, "layer %s encode (sampled)" % name)
+        assert_fp16_equal(yd.cpu().numpy().reshape(-1, 128)[idx].view(np.float16), codec.decode_blocks(ob, tb, t),
+                          "layer %s decode_many (sampled)" % name)
+
+
 @pytest.mark.parametrize("out_f,in_f,batch", [(1, 128, 1), (37, 1024, 3), (300, 1024, 8), (64, 8192, 4),
                                               (20, 28672, 2)])
 def test_gemv_small(dev, out_f, in_f, batch):
