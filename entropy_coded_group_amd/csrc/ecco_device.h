@@ -103,6 +103,13 @@ __device__ __forceinline__ uint32_t fp8_encode(float v) {
   return sign | (r >> 20);
 }
 
+// OCP FP8 E4M3FN decode of byte B of x (exact; 0x7F / 0xFF give NaN) with
+// gfx950's v_cvt_f32_fp8, which implements that format.
+template <int B>
+__device__ __forceinline__ float fp8_decode(uint32_t x) {
+  return __builtin_amdgcn_cvt_f32_fp8((int)x, B);
+}
+
 // FP16 <-> FP32 through the native half type: v_cvt_f16_f32 rounds to nearest
 // even, v_cvt_f32_f16 is exact.
 // The empty asm pins v as a rounded binary32 value: without it the compiler
@@ -174,7 +181,6 @@ template <int NW>
 struct DecodeSmem {
   uint8_t lut[S * H * 256 + 256];   // decode look-up tables + the clipped-stream table
   float cent[S * 16];
-  float fp8[256];
   uint32_t blk[NW][kBlkWords];
   uint32_t qsym[NW][kPassBlocks * kSymStride];
 };
@@ -189,7 +195,6 @@ __device__ __forceinline__ void stage_decode_tables(DecodeSmem<NW>& sm, const Ta
   if (tid < 16) dst[S * H * 256 / 16 + tid] = make_uint4(0x10101010u, 0x10101010u, 0x10101010u, 0x10101010u);
   const float* c = &tab->centroids[0][0];
   for (uint32_t i = tid; i < S * 16; i += blockDim.x) sm.cent[i] = c[i];
-  for (uint32_t i = tid; i < 256; i += blockDim.x) sm.fp8[i] = tab->fp8_value[i];
   for (uint32_t i = tid; i < NW * kBlkWords; i += blockDim.x) (&sm.blk[0][0])[i] = 0;
 }
 
@@ -223,8 +228,9 @@ __device__ __forceinline__ BatchRegs fetch_batch(uint32_t lane, uint32_t n_valid
 // stream with the 8-bit-window look-up table, four codewords per bit-window
 // refill, and marks a clipped stream; builds the block's value table (15
 // centroids * a, the scale S, up to 16 outlier values, or +0 for a clipped
-// block); then, 16 blocks at a time, stages the symbol bytes (outlier
-// positions overwritten by 16 + r) and hands 8 values per lane to the sink,
+// block); then, 16 blocks at a time, stages the symbol bytes -- each as the
+// byte offset of its value-table entry, outlier positions overwritten by that
+// of entry 16 + r -- and hands 8 values per lane to the sink,
 // sixteen lanes per block and four blocks per instruction, so every store
 // instruction writes four whole 256-byte rows.
 template <bool FULL, int NW, class Sink>
@@ -275,7 +281,7 @@ __device__ __forceinline__ void decode_batch(DecodeSmem<NW>& sm, uint32_t wave, 
       lim = 0xffffffffu;
       lutb = kDeadLut;
     }
-    E[c] = ev;
+    E[c] = (ev & 0x1f1f1f1fu) << 1;             // symbol -> byte offset of its FP16 value-table entry
     const bool adv = r4 >= 32u;
     lo = adv ? hi : lo;
     hi = adv ? nxt : hi;
@@ -288,7 +294,7 @@ __device__ __forceinline__ void decode_batch(DecodeSmem<NW>& sm, uint32_t wave, 
 
   // 2. value table: [0..14] fp16(c * a), [15] fp16(S), [16 + r] outlier r (or +0 if clipped)
   const uint32_t p = head & 63u;
-  const float S = sm.fp8[(head >> 8) & 255u] * t;
+  const float S = fp8_decode<1>(head) * t;
   const float aa = fabsf(S);
   uint32_t vtab[16];
   {
@@ -305,7 +311,9 @@ __device__ __forceinline__ void decode_batch(DecodeSmem<NW>& sm, uint32_t wave, 
   uint32_t tail[9];
 #pragma unroll
   for (int i = 0; i < 9; ++i) tail[i] = W[8 + i];
-  uint32_t jp[4] = {0, 0, 0, 0};               // outlier positions, byte r of jp[r / 4]
+  // jp: byte r of jp[r / 4] is the symbol-row byte that slot r patches: the
+  // record's position, or a pad byte past the row's 128 symbols if r >= n
+  uint32_t jp[4] = {0, 0, 0, 0};
 #pragma unroll
   for (int i = 8; i < 16; ++i) vtab[i] = 0;
 #pragma unroll
@@ -314,10 +322,10 @@ __device__ __forceinline__ void decode_batch(DecodeSmem<NW>& sm, uint32_t wave, 
     const uint32_t pos = 512u - 15u * (rr + 1);
     const uint32_t wi = (pos >> 5) - 8u, sh = pos & 31u;
     const uint32_t rec = window(tail[wi], tail[wi + 1], sh) & 0x7fffu;
-    const uint32_t hv = f16_bits(sm.fp8[rec >> 7] * t);
+    const uint32_t hv = f16_bits(fp8_decode<0>(rec >> 7) * t);
     const bool use = (uint32_t)rr < n;
     vtab[8 + rr / 2] |= (use ? hv : 0u) << (16 * (rr & 1));
-    jp[rr / 4] |= (rec & 127u) << (8 * (rr & 3));
+    jp[rr / 4] |= (use ? (rec & 127u) : 128u + (uint32_t)rr) << (8 * (rr & 3));
   }
   // the block's words are consumed: its value table takes their place
 #pragma unroll
@@ -330,15 +338,13 @@ __device__ __forceinline__ void decode_batch(DecodeSmem<NW>& sm, uint32_t wave, 
       uint32_t* Q = qs + (lane % kPassBlocks) * kSymStride;
 #pragma unroll
       for (int i = 0; i < 32; i += 4) *reinterpret_cast<uint4*>(Q + i) = make_uint4(E[i], E[i + 1], E[i + 2], E[i + 3]);
-      // outlier positions take symbol 16 + r, in record order so that a
-      // later record wins a repeated position; slots r >= n write to the
-      // row's pad bytes instead
+      // outlier positions take value-table entry 16 + r, in record order so
+      // that a later record wins a repeated position
       uint8_t* Qb = reinterpret_cast<uint8_t*>(Q);
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) {
         if ((rr & 3) == 0 && !__any((uint32_t)rr < n)) break;
-        const uint32_t j = (jp[rr / 4] >> (8 * (rr & 3))) & 127u;
-        Qb[(uint32_t)rr < n ? j : 128u + (rr & 15u)] = (uint8_t)(16 + rr);
+        Qb[(jp[rr / 4] >> (8 * (rr & 3))) & 0xffu] = (uint8_t)(2 * (16 + rr));
       }
     }
     wave_sync();
@@ -350,12 +356,23 @@ __device__ __forceinline__ void decode_batch(DecodeSmem<NW>& sm, uint32_t wave, 
 #pragma unroll
     for (int it = 0; it < kPassIters; ++it) {
       const uint32_t bl = kPassBlocks * k + it * 4u + (lane >> 4);
-      const uint16_t* tb = reinterpret_cast<const uint16_t*>(blk + bl * kBlkStride);
+      const uint8_t* tb = reinterpret_cast<const uint8_t*>(blk + bl * kBlkStride);
+      // each staged byte is already the entry's byte offset (< 64)
+      typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+      auto v = [&](uint32_t s, int b) -> _Float16 {
+        return *reinterpret_cast<const _Float16*>(tb + ((s >> (8 * b)) & 0xffu));
+      };
+      auto pr = [&](uint32_t s, int b) -> uint32_t {
+        h2 q;
+        q.x = v(s, b);
+        q.y = v(s, b + 1);
+        return __builtin_bit_cast(uint32_t, q);
+      };
       const uint32_t s0 = sv[it].x, s1 = sv[it].y;
-      o[it].x = (uint32_t)tb[s0 & 31u] | ((uint32_t)tb[(s0 >> 8) & 31u] << 16);
-      o[it].y = (uint32_t)tb[(s0 >> 16) & 31u] | ((uint32_t)tb[(s0 >> 24) & 31u] << 16);
-      o[it].z = (uint32_t)tb[s1 & 31u] | ((uint32_t)tb[(s1 >> 8) & 31u] << 16);
-      o[it].w = (uint32_t)tb[(s1 >> 16) & 31u] | ((uint32_t)tb[(s1 >> 24) & 31u] << 16);
+      o[it].x = pr(s0, 0);
+      o[it].y = pr(s0, 2);
+      o[it].z = pr(s1, 0);
+      o[it].w = pr(s1, 2);
     }
     wave_sync();
 #pragma unroll

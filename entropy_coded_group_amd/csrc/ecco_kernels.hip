@@ -15,9 +15,10 @@
 //           block's codeword stream through an 8-bit-window look-up table
 //           staged in LDS (all 256 codebooks, 64 KiB), four codewords per
 //           64-bit bit-window refill.  Symbols are written back to LDS and the
-//           wave turns around: eight lanes per block look up reconstruction
+//           wave turns around: sixteen lanes per block look up reconstruction
 //           values from a per-block 32-entry FP16 table (15 centroids * a, the
-//           scale, outliers) and write 128-bit stores.
+//           scale, outliers) and write 128-bit stores, four whole rows per
+//           store instruction.
 //   encode  sixteen lanes (one DPP row) per group, four groups per wave:
 //           row-wide max/min/argmin/sum/scan through DPP, LDS-resident
 //           thresholds for a branch-free binary search, codewords merged into
@@ -60,22 +61,15 @@ struct DecodeArgs {
   uint32_t n_jobs;
 };
 
-// Each workgroup decodes one tensor, so the look-up tables it stages in LDS
-// serve every block it sees; a tensor's batches are split into contiguous
-// ranges over its workgroups and interleaved over the waves of each.
-__global__ __launch_bounds__(kDecWaves * 64) void decode_kernel(DecodeArgs args) {
-  __shared__ DecodeSmem<kDecWaves> sm;
-  uint32_t j = 0;
-  while (j + 1 < args.n_jobs && blockIdx.x >= args.job[j + 1].wg_first) ++j;
-  const DecodeJob& a = args.job[j];
-  stage_decode_tables(sm, a.tab);
-  __syncthreads();
+// Decode of workgroup lw's share of one job: a contiguous range of the
+// job's batches, interleaved over the waves.
+template <bool CONTIG>
+__device__ __forceinline__ void decode_job(DecodeSmem<kDecWaves>& sm, const DecodeJob& a, uint32_t lw) {
   const uint32_t lane = lane_id(), wave = threadIdx.x >> 6;
-  const uint32_t lw = blockIdx.x - a.wg_first;
   const uint32_t b_end = (uint32_t)((uint64_t)a.n_batches * (lw + 1) / a.wg_count);
   uint32_t batch = (uint32_t)((uint64_t)a.n_batches * lw / a.wg_count) + wave;
   auto src_of = [&](uint32_t gidx) -> const uint8_t* {
-    if (a.contiguous) return a.blocks + (uint64_t)gidx * 64u;
+    if (CONTIG) return a.blocks + (uint64_t)gidx * 64u;
     const uint32_t r = div_magic(gidx, a.gpr), g = gidx - r * a.gpr.d;
     return a.blocks + ((uint64_t)r * a.blk_stride + g) * 64u;
   };
@@ -95,7 +89,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_kernel(DecodeArgs args)
     auto sink = [&](uint32_t b, uint32_t j0, uint4 v) {
       const uint32_t gidx = g0 + b;
       uint64_t yoff;
-      if (a.contiguous) {
+      if (CONTIG) {
         yoff = (uint64_t)gidx * 128u;
       } else {
         const uint32_t r = div_magic(gidx, a.gpr), g = gidx - r * a.gpr.d;
@@ -110,6 +104,22 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_kernel(DecodeArgs args)
       decode_batch<false>(sm, wave, lane, n_valid, a.t, cur, sink);
     cur = nxt;
   }
+}
+
+// Each workgroup decodes one tensor, so the look-up tables it stages in LDS
+// serve every block it sees.
+__global__ __launch_bounds__(kDecWaves * 64) void decode_kernel(DecodeArgs args) {
+  __shared__ DecodeSmem<kDecWaves> sm;
+  uint32_t j = 0;
+  while (j + 1 < args.n_jobs && blockIdx.x >= args.job[j + 1].wg_first) ++j;
+  const DecodeJob a = args.job[j];          // one copy, kept in scalar registers
+  stage_decode_tables(sm, a.tab);
+  __syncthreads();
+  const uint32_t lw = blockIdx.x - a.wg_first;
+  if (a.contiguous)
+    decode_job<true>(sm, a, lw);
+  else
+    decode_job<false>(sm, a, lw);
 }
 
 // -------------------------------------------------------------------- encode
@@ -134,7 +144,6 @@ struct EncodeSmem {
   float c0c14[S * 2];
   uint32_t len4[S * A];
   uint16_t enc[S * H * A];
-  float fp8[256];
   float thr[kEncWaves][4][16];
   uint32_t out[kEncWaves][4][16];
 };
@@ -146,7 +155,6 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(EncodeArgs a) {
   for (uint32_t i = tid; i < S * 2; i += blockDim.x) sm.c0c14[i] = (&a.tab->c0c14[0][0])[i];
   for (uint32_t i = tid; i < S * A; i += blockDim.x) sm.len4[i] = (&a.tab->len4[0][0])[i];
   for (uint32_t i = tid; i < S * H * A; i += blockDim.x) sm.enc[i] = (&a.tab->enc[0][0][0])[i];
-  for (uint32_t i = tid; i < 256; i += blockDim.x) sm.fp8[i] = a.tab->fp8_value[i];
   __syncthreads();
 
   const uint32_t lane = lane_id(), wave = tid >> 6;
@@ -187,7 +195,7 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(EncodeArgs a) {
     const uint32_t jstar = 127u - ((km >> 1) & 127u);
     const float xs = f16_value((km >> 8) | ((km & 1u) << 15));
     const uint32_t s8 = fp8_encode(xs * inv_t);
-    const float S = sm.fp8[s8] * t;
+    const float S = fp8_decode<0>(s8) * t;
     const float aa = fabsf(S);
     // 2. min / max of the other 127 values
     float mn = __builtin_inff(), mx = -__builtin_inff();
