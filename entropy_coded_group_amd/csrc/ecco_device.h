@@ -47,6 +47,13 @@ __device__ __forceinline__ uint32_t row_max_u32(uint32_t v) {
   v = max(v, dpp_u32<kRowMirror>(v));
   return v;
 }
+__device__ __forceinline__ uint32_t row_min_u32(uint32_t v) {
+  v = min(v, dpp_u32<kQuadXor1>(v));
+  v = min(v, dpp_u32<kQuadXor2>(v));
+  v = min(v, dpp_u32<kRowHalfMirror>(v));
+  v = min(v, dpp_u32<kRowMirror>(v));
+  return v;
+}
 __device__ __forceinline__ uint32_t row_add_u32(uint32_t v) {
   v += dpp_u32<kQuadXor1>(v);
   v += dpp_u32<kQuadXor2>(v);
@@ -90,17 +97,14 @@ __device__ __forceinline__ uint32_t row_scan_add(uint32_t v) {
   return v;
 }
 
-// OCP FP8 E4M3FN encode of a finite float: saturate to +-448, round to nearest
-// even (the subnormal grid is 2^-9); NaN gives 0x7F.
+// OCP FP8 E4M3FN encode of a non-NaN float: saturate to +-448, round to
+// nearest even (the subnormal grid is 2^-9).  gfx950's v_cvt_pk_fp8_f32
+// converts to that format with round-to-nearest-even; the clamp first makes
+// out-of-range values saturate.  (Checked against a bit-level software
+// encoder over every non-NaN binary32 input.)
 __device__ __forceinline__ uint32_t fp8_encode(float v) {
-  uint32_t u = __float_as_uint(v);
-  uint32_t sign = (u >> 24) & 0x80u, a = u & 0x7fffffffu;
-  if (a > 0x7f800000u) return 0x7fu;
-  if (a >= 0x43e00000u) return sign | 0x7eu;
-  if (a < 0x3c800000u) return sign | (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
-  uint32_t r = a - (120u << 23);
-  r += 0x7ffffu + ((r >> 20) & 1u);
-  return sign | (r >> 20);
+  const float c = __builtin_amdgcn_fmed3f(v, -448.0f, 448.0f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, c, 0, false) & 0xffu;
 }
 
 // OCP FP8 E4M3FN decode of byte B of x (exact; 0x7F / 0xFF give NaN) with

@@ -161,29 +161,39 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(EncodeArgs a) {
   const uint32_t q = lane >> 4, t16 = lane & 15u;
   const float t = a.t, inv_t = a.inv_t;
   float* thr = sm.thr[wave][q];
+  // tree node of threshold t16 (t16 < 15): with v = t16 + 1 = odd * 2^z, the
+  // node sits on level 3 - z at index 2^(3 - z) + (v >> (z + 1))
+  const uint32_t enode = (8u >> __builtin_ctz(t16 + 1u)) + ((t16 + 1u) >> (__builtin_ctz(t16 + 1u) + 1u));
   uint32_t* out = sm.out[wave][q];
   // per-lane statistics (kept by lane t16 == 0 of each group)
   uint64_t st_groups = 0, st_clip = 0, st_clipv = 0, st_pad = 0, st_fill = 0, st_nonfin = 0;
 
-  for (uint32_t quad = blockIdx.x * kEncWaves + wave; quad < a.n_quads; quad += gridDim.x * kEncWaves) {
+  // the 16 bytes of group g (clamped to the last group) that lane t16 holds
+  auto load_group = [&](uint32_t g) -> uint4 {
+    g = min(g, a.n_groups - 1u);
+    const uint32_t row = div_magic(g, a.gpr), col = g - row * a.gpr.d;
+    return load_stream(a.x + (uint64_t)row * a.x_stride + (uint64_t)col * 128u + 8u * t16);
+  };
+  const uint32_t qstride = gridDim.x * kEncWaves;
+  uint32_t quad = blockIdx.x * kEncWaves + wave;
+  uint4 raw = load_group(quad * 4u + q);
+  for (; quad < a.n_quads; quad += qstride) {
     const uint32_t gidx = quad * 4u + q;
     const bool valid = gidx < a.n_groups;
+    // the next quad's input is loaded before this one is worked on
+    const uint4 nraw = load_group((quad + qstride) * 4u + q);
     uint32_t row = 0, col = 0;
     if (valid) {
       row = div_magic(gidx, a.gpr);
       col = gidx - row * a.gpr.d;
     }
-    uint4 raw = make_uint4(0, 0, 0, 0);
-    if (valid) raw = *reinterpret_cast<const uint4*>(a.x + (uint64_t)row * a.x_stride + (uint64_t)col * 128u + 8u * t16);
     uint32_t hb[8] = {raw.x & 0xffffu, raw.x >> 16, raw.y & 0xffffu, raw.y >> 16,
                       raw.z & 0xffffu, raw.z >> 16, raw.w & 0xffffu, raw.w >> 16};
     float xf[8];
     uint32_t key[8];
-    bool nonfin = false;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       xf[i] = f16_value(hb[i]);
-      nonfin |= (hb[i] & 0x7c00u) == 0x7c00u;
       const uint32_t j = 8u * t16 + i;
       key[i] = ((hb[i] & 0x7fffu) << 8) | ((127u - j) << 1) | (hb[i] >> 15);
     }
@@ -197,43 +207,51 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(EncodeArgs a) {
     const uint32_t s8 = fp8_encode(xs * inv_t);
     const float S = fp8_decode<0>(s8) * t;
     const float aa = fabsf(S);
-    // 2. min / max of the other 127 values
-    float mn = __builtin_inff(), mx = -__builtin_inff();
+    // 2. min / max of the other 127 values: the lane holding i* uses a
+    //    neighbour's value in its place (a duplicate does not move either)
+    float xo[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if (8u * t16 + i != jstar) {
-        mn = fminf(mn, xf[i]);
-        mx = fmaxf(mx, xf[i]);
-      }
-    }
+    for (int i = 0; i < 8; ++i) xo[i] = key[i] == km ? xf[i ^ 1] : xf[i];
+    float mn = fminf(fminf(fminf(xo[0], xo[1]), fminf(xo[2], xo[3])), fminf(fminf(xo[4], xo[5]), fminf(xo[6], xo[7])));
+    float mx = fmaxf(fmaxf(fmaxf(xo[0], xo[1]), fmaxf(xo[2], xo[3])), fmaxf(fmaxf(xo[4], xo[5]), fmaxf(xo[6], xo[7])));
     mn = row_min_f32(mn);
     mx = row_max_f32(mx);
-    // 3. pattern: min/max squared error, lowest p on ties
-    uint64_t best = ~0ull;
+    // 3. pattern: min/max squared error, lowest p on ties.  Each lane keeps its
+    //    best of 4 (p rising, so a strict < keeps the lowest); the row then
+    //    takes the least fitness (non-negative, so its bits order like it)
+    //    and the least p among the lanes that reach it.
+    float bf = __builtin_inff();
+    uint32_t bp = t16;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const uint32_t p = t16 + 16u * k;
       const float d1 = mn - sm.c0c14[2 * p] * aa;
       const float d2 = mx - sm.c0c14[2 * p + 1] * aa;
       const float f = d1 * d1 + d2 * d2;
-      const uint64_t kk = ((uint64_t)__float_as_uint(f) << 32) | p;
-      best = kk < best ? kk : best;
+      if (f < bf) {
+        bf = f;
+        bp = p;
+      }
     }
-    best = row_min_u64(best);
-    const uint32_t pstar = (uint32_t)best & 63u;
-    // 4. quantise: thresholds m_pk * a in LDS, binary search per value
-    thr[t16] = t16 < 14u ? sm.mid[pstar * 16u + t16] * aa : __builtin_inff();
+    const uint32_t fmin = row_min_u32(__float_as_uint(bf));
+    const uint32_t pstar = row_min_u32(__float_as_uint(bf) == fmin ? bp : 63u) & 63u;
+    // 4. quantise: sym = #{k : x > m_pk * a}.  The 15 thresholds (m_p14 * a
+    //    taken as +inf) sit in LDS as an implicit binary tree, node 1 the
+    //    root and node u's children 2u and 2u + 1 (lane k writes threshold k
+    //    to its node, precomputed as enode); four compares walk it, the root
+    //    one against a register copy.
+    if (t16 < 15u) thr[enode] = t16 < 14u ? sm.mid[pstar * 16u + t16] * aa : __builtin_inff();
     wave_sync();
+    const float root = thr[1];
     uint32_t sym[8];
     uint32_t l4 = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      uint32_t idx = 0;
-      idx += xf[i] > thr[idx + 7] ? 8u : 0u;
-      idx += xf[i] > thr[idx + 3] ? 4u : 0u;
-      idx += xf[i] > thr[idx + 1] ? 2u : 0u;
-      idx += xf[i] > thr[idx] ? 1u : 0u;
-      sym[i] = (8u * t16 + i == jstar) ? 15u : idx;
+      uint32_t u = xf[i] > root ? 3u : 2u;
+      u = u + u + (xf[i] > thr[u] ? 1u : 0u);
+      u = u + u + (xf[i] > thr[u] ? 1u : 0u);
+      u = u + u + (xf[i] > thr[u] ? 1u : 0u);
+      sym[i] = key[i] == km ? 15u : u - 16u;
       l4 += sm.len4[pstar * 16u + sym[i]];
     }
     // 5. codebook with the shortest stream, lowest h on ties
@@ -270,28 +288,28 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(EncodeArgs a) {
     }
     const bool clipped = 16u + L > 512u;
     const uint32_t n = clipped ? 0u : min(16u, (496u - L) / 15u);
-    // 7. outliers: n largest |x| (j != i*), lower j first on ties
-    if (8u * t16 <= jstar && jstar < 8u * t16 + 8u) {
+    // 7. outliers: n largest |x| (j != i*), lower j first on ties.  Keys are
+    //    unique and the scale element holds the row's largest (km), so the
+    //    outliers are the next n keys: after removing km, each round takes
+    //    the row's largest remaining key (lane r keeps round r's) and removes
+    //    it unless no group of the wave needs another round.
+    uint32_t mykey = 0;
+    if (__any(n > 0u)) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        if (8u * t16 + i == jstar) key[i] = 0;
-    }
-    uint32_t myrec = 0;
-    for (uint32_t rr = 0; rr < 16u; ++rr) {
-      if (!__any(rr < n)) break;
-      uint32_t m = key[0];
+      for (int i = 0; i < 8; ++i) key[i] = key[i] == km ? 0u : key[i];
+      for (uint32_t rr = 0;; ++rr) {
+        uint32_t m = max(max(max(key[0], key[1]), max(key[2], key[3])), max(max(key[4], key[5]), max(key[6], key[7])));
+        m = row_max_u32(m);
+        mykey = t16 == rr ? m : mykey;
+        if (!__any(rr + 1u < n)) break;
 #pragma unroll
-      for (int i = 1; i < 8; ++i) m = max(m, key[i]);
-      m = row_max_u32(m);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) key[i] = key[i] == m ? 0u : key[i];
-      if (t16 == rr) {
-        const uint32_t j = 127u - ((m >> 1) & 127u);
-        const float xv = f16_value((m >> 8) | ((m & 1u) << 15));
-        myrec = j | (fp8_encode(xv * inv_t) << 7);
+        for (int i = 0; i < 8; ++i) key[i] = key[i] == m ? 0u : key[i];
       }
     }
     if (t16 < n) {
+      const uint32_t j = 127u - ((mykey >> 1) & 127u);
+      const float xv = f16_value((mykey >> 8) | ((mykey & 1u) << 15));
+      const uint32_t myrec = j | (fp8_encode(xv * inv_t) << 7);
       const uint32_t rp = 497u - 15u * t16;
       const uint32_t w = rp >> 5, sh = rp & 31u;
       atomicOr(&out[w], myrec << sh);
@@ -312,6 +330,9 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(EncodeArgs a) {
         ends += e <= 512u ? 1u : 0u;
       }
       const uint32_t k = row_add_u32(ends);
+      bool nonfin = false;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) nonfin |= (hb[i] & 0x7c00u) == 0x7c00u;
       const uint32_t nf = row_max_u32(nonfin ? 1u : 0u);
       if (valid && t16 == 0) {
         st_groups += 1;
@@ -322,6 +343,7 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(EncodeArgs a) {
         st_nonfin += nf;
       }
     }
+    raw = nraw;
     wave_sync();
   }
   if (a.stats && t16 == 0 && st_groups) {
@@ -339,34 +361,54 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(EncodeArgs a) {
 
 __global__ void amax_init_kernel(float* out) { *out = 0.0f; }
 
+constexpr int kAmaxUnroll = 8;   // 16-byte loads in flight per thread
+
+__device__ __forceinline__ uint32_t abs_max_bits(uint32_t m, uint32_t w) {
+  uint32_t a0 = w & 0x7fffu, a1 = (w >> 16) & 0x7fffu;
+  a0 = a0 > 0x7c00u ? 0u : a0;
+  a1 = a1 > 0x7c00u ? 0u : a1;
+  return max(m, max(a0, a1));
+}
+
 __global__ __launch_bounds__(256) void amax_kernel(const uint16_t* x, uint64_t n, float* out) {
   // |x| bit patterns of finite FP16 values order like the values (NaN ignored)
   __shared__ uint32_t red[4];
   uint32_t m = 0;
+  const uint4* x4 = reinterpret_cast<const uint4*>(x);
   const uint64_t n8 = n / 8;
   const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
-  for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8; i += stride) {
-    const uint4 v = reinterpret_cast<const uint4*>(x)[i];
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  // several independent loads per thread before any is used
+  for (; i + (kAmaxUnroll - 1) * stride < n8; i += kAmaxUnroll * stride) {
+    uint4 v[kAmaxUnroll];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      uint32_t a0 = w[k] & 0x7fffu, a1 = (w[k] >> 16) & 0x7fffu;
-      a0 = a0 > 0x7c00u ? 0u : a0;
-      a1 = a1 > 0x7c00u ? 0u : a1;
-      m = max(m, max(a0, a1));
+    for (int u = 0; u < kAmaxUnroll; ++u) v[u] = load_stream(x4 + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < kAmaxUnroll; ++u) {
+      m = abs_max_bits(m, v[u].x);
+      m = abs_max_bits(m, v[u].y);
+      m = abs_max_bits(m, v[u].z);
+      m = abs_max_bits(m, v[u].w);
     }
   }
-  for (uint64_t i = n8 * 8 + (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
-    const uint32_t a0 = x[i] & 0x7fffu;
-    m = max(m, a0 > 0x7c00u ? 0u : a0);
+  for (; i < n8; i += stride) {
+    const uint4 v = load_stream(x4 + i);
+    m = abs_max_bits(abs_max_bits(m, v.x), v.y);
+    m = abs_max_bits(abs_max_bits(m, v.z), v.w);
   }
+  for (uint64_t k = n8 * 8 + (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; k < n; k += stride)
+    m = abs_max_bits(m, x[k]);
   // wave, then workgroup reduction: one atomic per workgroup
   for (int o = 32; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
   if (lane_id() == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
   if (threadIdx.x == 0) {
     m = max(max(red[0], red[1]), max(red[2], red[3]));
-    if (m) atomicMax(reinterpret_cast<unsigned int*>(out), __float_as_uint(f16_value(m)));
+    // the result only grows, so a workgroup whose maximum does not exceed a
+    // value already read from it has nothing to add (saves most atomics)
+    unsigned int* o = reinterpret_cast<unsigned int*>(out);
+    const uint32_t mb = __float_as_uint(f16_value(m));
+    if (m && mb > __hip_atomic_load(o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) atomicMax(o, mb);
   }
 }
 
