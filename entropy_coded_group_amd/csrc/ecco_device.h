@@ -88,6 +88,20 @@ __device__ __forceinline__ uint64_t row_min_u64(uint64_t v) {
   v = min_u64_dpp<kRowMirror>(v);
   return v;
 }
+// Sum over the whole wave, in a fixed order: rows first, then the four row
+// totals read back in row order.  The result is uniform.
+__device__ __forceinline__ float wave_sum_f32(float v) {
+  v += dpp_f32<kQuadXor1>(v);
+  v += dpp_f32<kQuadXor2>(v);
+  v += dpp_f32<kRowHalfMirror>(v);
+  v += dpp_f32<kRowMirror>(v);
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+  return ((r0 + r1) + r2) + r3;
+}
+
 // Inclusive prefix sum over the 16 lanes of a row (Hillis-Steele).
 __device__ __forceinline__ uint32_t row_scan_add(uint32_t v) {
   v += dpp_u32<kRowShr1>(v);
@@ -226,7 +240,7 @@ __device__ __forceinline__ BatchRegs fetch_batch(uint32_t lane, uint32_t n_valid
 
 // Decode one staged batch (FULL: all 64 blocks exist, so no store is
 // predicated).
-//   sink(b, j0, v)            8 decoded FP16 values of block b at positions
+//   sink(b, j0, v, k)         8 decoded FP16 values of block b at positions
 //                             j0 .. j0 + 7 (v.x holds values j0, j0 + 1, ...)
 // Steps: stage the batch in LDS; each lane decodes one block's codeword
 // stream with the 8-bit-window look-up table, four codewords per bit-window
@@ -382,7 +396,7 @@ __device__ __forceinline__ void decode_batch(DecodeSmem<NW>& sm, uint32_t wave, 
 #pragma unroll
     for (int it = 0; it < kPassIters; ++it) {
       const uint32_t bl = kPassBlocks * k + it * 4u + (lane >> 4);
-      if (FULL || bl < n_valid) sink(bl, 8u * (lane & 15u), o[it]);
+      if (FULL || bl < n_valid) sink(bl, 8u * (lane & 15u), o[it], (uint32_t)k);
     }
   }
 }

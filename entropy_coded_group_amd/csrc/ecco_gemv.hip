@@ -6,10 +6,15 @@
 // are multiplied on the vector ALUs (v_dot2_f32_f16: two FP16 products summed
 // into an FP32 accumulator) straight out of the decoder, without writing W.
 //
-// Work split: a wavefront owns one output row at a time and decodes the row's
-// blocks 64 at a time with the shared decode core; each lane accumulates the
-// products of the 8 weights it is handed for every batch column, and a wave
-// reduction finishes the row.
+// Work split at batch 1 with rows of 16, 32 or 64 blocks (in_features 2048,
+// 4096, 8192): the matrix is cut into batches of 64 consecutive blocks, i.e.
+// 4, 2 or 1 whole rows, dealt round the waves of all CUs.  The decode core
+// hands the weights over in four passes of 16 blocks and each pass lies inside
+// one row, so every lane keeps one accumulator per row of the batch; wave sums
+// finish the rows.  Otherwise a wavefront owns one output row at a time and
+// decodes its blocks 64 at a time (the last batch of a row partly filled).
+// Either way each lane accumulates the products of the 8 weights it is
+// handed, and the sums are taken in a fixed order.
 #include <hip/hip_runtime.h>
 
 #include "ecco_device.h"
@@ -62,7 +67,7 @@ __global__ __launch_bounds__(kGemvWaves * 64) void gemv_kernel(GemvArgs a) {
       nc0 = 0;
     }
     const BatchRegs nxt = nrow < a.out_f ? fetch(nrow, nc0) : fetch(row, c0);
-    auto sink = [&](uint32_t b, uint32_t j0, uint4 w) {
+    auto sink = [&](uint32_t b, uint32_t j0, uint4 w, uint32_t) {
       const uint16_t* xp = a.x + (uint64_t)(c0 + b) * 128u + j0;
 #pragma unroll
       for (int b2 = 0; b2 < BM; ++b2) {
@@ -80,9 +85,7 @@ __global__ __launch_bounds__(kGemvWaves * 64) void gemv_kernel(GemvArgs a) {
     if (c0 + 64u >= a.gpr) {
 #pragma unroll
       for (int b = 0; b < BM; ++b) {
-        float v = part[b];
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+        const float v = wave_sum_f32(part[b]);
         if (lane == 0 && (uint32_t)b < a.batch) a.y[(uint64_t)b * a.out_f + row] = v;
         part[b] = 0.0f;
       }
@@ -94,9 +97,97 @@ __global__ __launch_bounds__(kGemvWaves * 64) void gemv_kernel(GemvArgs a) {
   }
 }
 
+// Rows of 64 / RB blocks: RB whole rows per 64-block batch.
+template <int BM, int RB>
+__global__ __launch_bounds__(kGemvWaves * 64) void gemv_rows_kernel(GemvArgs a) {
+  __shared__ DecodeSmem<kGemvWaves> sm;
+  stage_decode_tables(sm, a.tab);
+  __syncthreads();
+  constexpr uint32_t kGpr = 64 / RB;
+  const uint32_t lane = lane_id(), wave = threadIdx.x >> 6;
+  const uint32_t n_groups = a.out_f * kGpr;
+  const uint32_t n_batches = (n_groups + 63u) / 64u;
+  const uint32_t stride = gridDim.x * kGemvWaves;
+  uint32_t batch = wave * gridDim.x + blockIdx.x;   // batches go round the CUs first
+  if (batch >= n_batches) return;
+  auto fetch = [&](uint32_t bt) {
+    const uint32_t g0 = bt * 64u;
+    return fetch_batch(lane, min(64u, n_groups - g0), [&](uint32_t i, uint32_t q) {
+      return load_stream(a.blocks + (uint64_t)(g0 + i) * 64u + 16u * q);
+    });
+  };
+  BatchRegs cur = fetch(batch);
+  for (; batch < n_batches; batch += stride) {
+    const uint32_t nb = batch + stride;
+    const BatchRegs nxt = fetch(nb < n_batches ? nb : batch);
+    float acc[RB][BM];
+#pragma unroll
+    for (int r = 0; r < RB; ++r)
+#pragma unroll
+      for (int b2 = 0; b2 < BM; ++b2) acc[r][b2] = 0.0f;
+    // pass k covers blocks 16 k .. 16 k + 15: row k * RB / 4 of the batch
+    // an opaque copy of x per batch: otherwise the compiler hoists the 16
+    // loop-invariant x addresses of a batch out of the loop (32 registers)
+    const uint16_t* xb = a.x;
+    asm volatile("" : "+s"(xb));
+    auto sink = [&](uint32_t b, uint32_t j0, uint4 w, uint32_t k) {
+      const uint16_t* xp = xb + (uint64_t)(b & (kGpr - 1u)) * 128u + j0;
+      const uint32_t r = k * RB / 4u;
+#pragma unroll
+      for (int b2 = 0; b2 < BM; ++b2) {
+        if ((uint32_t)b2 < a.batch) {
+          const uint4 xv = *reinterpret_cast<const uint4*>(xp + (uint64_t)b2 * a.in_f);
+#pragma unroll
+          for (int rr = 0; rr < RB; ++rr)
+            if ((uint32_t)rr == r) acc[rr][b2] = dot8(w, xv, acc[rr][b2]);
+        }
+      }
+    };
+    const uint32_t n_valid = min(64u, n_groups - batch * 64u);
+    if (n_valid == 64u)
+      decode_batch<true>(sm, wave, lane, 64u, a.t, cur, sink);
+    else
+      decode_batch<false>(sm, wave, lane, n_valid, a.t, cur, sink);
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+      const uint32_t row = batch * RB + r;
+#pragma unroll
+      for (int b2 = 0; b2 < BM; ++b2) {
+        const float v = wave_sum_f32(acc[r][b2]);
+        if (lane == 0 && (uint32_t)b2 < a.batch && row < a.out_f) a.y[(uint64_t)b2 * a.out_f + row] = v;
+      }
+    }
+    cur = nxt;
+  }
+}
+
 }  // namespace ecco
 
 using namespace ecco;
+
+namespace {
+template <int BM>
+void launch_gemv(const GemvArgs& a, uint32_t cus, hipStream_t s) {
+  // (one accumulator per row and batch column: with more columns the
+  // registers run out, and those launches use the row-per-wave kernel)
+  if constexpr (BM == 1) {
+    if (a.gpr == 16 || a.gpr == 32 || a.gpr == 64) {
+      const uint32_t rb = 64u / a.gpr;
+      const uint32_t n_batches = (a.out_f * a.gpr + 63u) / 64u;
+      const uint32_t grid = std::max<uint32_t>(1, std::min<uint32_t>(n_batches, cus));
+      if (rb == 4)
+        hipLaunchKernelGGL((gemv_rows_kernel<1, 4>), dim3(grid), dim3(kGemvWaves * 64), 0, s, a);
+      else if (rb == 2)
+        hipLaunchKernelGGL((gemv_rows_kernel<1, 2>), dim3(grid), dim3(kGemvWaves * 64), 0, s, a);
+      else
+        hipLaunchKernelGGL((gemv_rows_kernel<1, 1>), dim3(grid), dim3(kGemvWaves * 64), 0, s, a);
+      return;
+    }
+  }
+  const uint32_t grid = std::max<uint32_t>(1, std::min<uint32_t>(a.out_f, cus));
+  hipLaunchKernelGGL(gemv_kernel<BM>, dim3(grid), dim3(kGemvWaves * 64), 0, s, a);
+}
+}  // namespace
 
 extern "C" int ecco_decode_gemv(const void* blocks, const void* tables, float tensor_scale, int64_t out_f,
                                 int64_t in_f, const uint16_t* x, int64_t batch, float* y, void* stream) {
@@ -118,16 +209,15 @@ extern "C" int ecco_decode_gemv(const void* blocks, const void* tables, float te
   a.gpr = (uint32_t)(in_f / 128);
   a.batch = (uint32_t)batch;
   a.t = tensor_scale;
-  const uint32_t grid = std::max<uint32_t>(1, std::min<uint32_t>(a.out_f, (uint32_t)cus));
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   if (batch == 1)
-    hipLaunchKernelGGL(gemv_kernel<1>, dim3(grid), dim3(kGemvWaves * 64), 0, s, a);
+    launch_gemv<1>(a, (uint32_t)cus, s);
   else if (batch <= 2)
-    hipLaunchKernelGGL(gemv_kernel<2>, dim3(grid), dim3(kGemvWaves * 64), 0, s, a);
+    launch_gemv<2>(a, (uint32_t)cus, s);
   else if (batch <= 4)
-    hipLaunchKernelGGL(gemv_kernel<4>, dim3(grid), dim3(kGemvWaves * 64), 0, s, a);
+    launch_gemv<4>(a, (uint32_t)cus, s);
   else
-    hipLaunchKernelGGL(gemv_kernel<8>, dim3(grid), dim3(kGemvWaves * 64), 0, s, a);
+    launch_gemv<8>(a, (uint32_t)cus, s);
   return hipGetLastError() == hipSuccess ? ECCO_OK : ECCO_EHIP;
 }

@@ -73,20 +73,23 @@ __device__ __forceinline__ void decode_job(DecodeSmem<kDecWaves>& sm, const Deco
     const uint32_t r = div_magic(gidx, a.gpr), g = gidx - r * a.gpr.d;
     return a.blocks + ((uint64_t)r * a.blk_stride + g) * 64u;
   };
-  auto fetch = [&](uint32_t b) {
+  // A prefetch past the wave's last batch reads the (cached) table blob
+  // instead: the loads stay unconditional without re-reading blocks.
+  const uint8_t* idle = reinterpret_cast<const uint8_t*>(a.tab);
+  auto fetch = [&](uint32_t b, bool live) {
     const uint32_t g0 = b * 64u;
     return fetch_batch(lane, min(64u, a.n_groups - g0), [&](uint32_t i, uint32_t q) {
-      return load_stream(src_of(g0 + i) + 16u * q);
+      return load_stream((live ? src_of(g0 + i) : idle + 64u * (i & 63u)) + 16u * q);
     });
   };
   if (batch >= b_end) return;
-  BatchRegs cur = fetch(batch);
+  BatchRegs cur = fetch(batch, true);
   for (; batch < b_end; batch += kDecWaves) {
-    // prefetch the next batch (a valid one even past the end: loads stay unconditional)
     const uint32_t nb = batch + kDecWaves;
-    const BatchRegs nxt = fetch(nb < b_end ? nb : batch);
+    const bool more = nb < b_end;
+    const BatchRegs nxt = fetch(more ? nb : batch, more);
     const uint32_t g0 = batch * 64u;
-    auto sink = [&](uint32_t b, uint32_t j0, uint4 v) {
+    auto sink = [&](uint32_t b, uint32_t j0, uint4 v, uint32_t) {
       const uint32_t gidx = g0 + b;
       uint64_t yoff;
       if (CONTIG) {

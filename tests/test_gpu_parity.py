@@ -315,7 +315,8 @@ def test_decode_many_full_layer_sampled(dev):
 
 
 @pytest.mark.parametrize("out_f,in_f,batch", [(1, 128, 1), (37, 1024, 3), (300, 1024, 8), (64, 8192, 4),
-                                              (20, 28672, 2)])
+                                              (20, 28672, 2), (1, 4096, 1), (999, 4096, 1), (5, 2048, 1),
+                                              (1000, 2048, 1), (33, 8192, 1), (50, 14336, 1)])
 def test_gemv_small(dev, out_f, in_f, batch):
     tb = golden("c5_w1")
     tdev = dev_tables(tb)
