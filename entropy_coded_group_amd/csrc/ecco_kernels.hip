@@ -210,13 +210,17 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(EncodeArgs a) {
     const uint32_t s8 = fp8_encode(xs * inv_t);
     const float S = fp8_decode<0>(s8) * t;
     const float aa = fabsf(S);
-    // 2. min / max of the other 127 values: the lane holding i* uses a
-    //    neighbour's value in its place (a duplicate does not move either)
-    float xo[8];
+    // 2. min / max of the other 127 values (the scale element, whose key is
+    //    km, counts as +inf for the min and -inf for the max)
+    float lo[8], hi[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) xo[i] = key[i] == km ? xf[i ^ 1] : xf[i];
-    float mn = fminf(fminf(fminf(xo[0], xo[1]), fminf(xo[2], xo[3])), fminf(fminf(xo[4], xo[5]), fminf(xo[6], xo[7])));
-    float mx = fmaxf(fmaxf(fmaxf(xo[0], xo[1]), fmaxf(xo[2], xo[3])), fmaxf(fmaxf(xo[4], xo[5]), fmaxf(xo[6], xo[7])));
+    for (int i = 0; i < 8; ++i) {
+      const bool s = key[i] == km;
+      lo[i] = s ? __builtin_inff() : xf[i];
+      hi[i] = s ? -__builtin_inff() : xf[i];
+    }
+    float mn = fminf(fminf(fminf(lo[0], lo[1]), fminf(lo[2], lo[3])), fminf(fminf(lo[4], lo[5]), fminf(lo[6], lo[7])));
+    float mx = fmaxf(fmaxf(fmaxf(hi[0], hi[1]), fmaxf(hi[2], hi[3])), fmaxf(fmaxf(hi[4], hi[5]), fmaxf(hi[6], hi[7])));
     mn = row_min_f32(mn);
     mx = row_max_f32(mx);
     // 3. pattern: min/max squared error, lowest p on ties.  Each lane keeps its
