@@ -43,7 +43,8 @@ class EccoError(RuntimeError):
 
 class TrainOpts(ctypes.Structure):
     _fields_ = [("kmeans_iters", ctypes.c_uint32), ("huff_iters", ctypes.c_uint32),
-                ("seed", ctypes.c_uint64), ("max_groups", ctypes.c_uint32), ("threads", ctypes.c_uint32)]
+                ("seed", ctypes.c_uint64), ("max_groups", ctypes.c_uint32), ("threads", ctypes.c_uint32),
+                ("n_patterns", ctypes.c_uint32)]
 
 
 DECODE_MAX_JOBS = 16
@@ -147,12 +148,14 @@ def ecco_tables_get(blob):
     return c, l
 
 
-def ecco_train_patterns(sample_fp16, kmeans_iters=25, huff_iters=10, seed=0, max_groups=0, threads=0):
-    """Learn a host blob from an FP16 sample (NumPy float16/uint16 or CPU torch tensor)."""
+def ecco_train_patterns(sample_fp16, kmeans_iters=25, huff_iters=10, seed=0, max_groups=0, threads=0,
+                        n_patterns=0):
+    """Learn a host blob from an FP16 sample (NumPy float16/uint16 or CPU torch tensor);
+    n_patterns distinct patterns (16, 32 or 64; 0 = 64) repeated over the 64 slots."""
     if hasattr(sample_fp16, "numpy"):
         sample_fp16 = sample_fp16.contiguous().numpy()
     s = np.ascontiguousarray(sample_fp16).view(np.uint16).ravel()
-    opts = TrainOpts(kmeans_iters, huff_iters, seed, max_groups, threads)
+    opts = TrainOpts(kmeans_iters, huff_iters, seed, max_groups, threads, n_patterns)
     blob = _aligned_host(ecco_tables_size())
     _check(lib().ecco_train_patterns(_ptr(s), s.size, ctypes.byref(opts), _ptr(blob)), "ecco_train_patterns")
     return blob

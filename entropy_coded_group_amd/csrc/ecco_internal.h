@@ -35,7 +35,8 @@ struct alignas(256) Tables {
   uint32_t version;
   uint32_t size;
   uint32_t checksum;        // FNV-1a over every byte after the header
-  uint32_t reserved[60];
+  uint32_t n_search;        // patterns the encoder searches (16, 32 or 64), derived from the centroids
+  uint32_t reserved[59];
   // inputs
   float centroids[S][16];       // [p][0..14] centroid, [15] = 0
   uint8_t code_len[S][H][A];    // 2..8
@@ -53,6 +54,7 @@ static_assert(offsetof(Tables, lut) % 256 == 0, "lut alignment");
 static_assert(offsetof(Tables, centroids) % 16 == 0, "centroid alignment");
 
 uint32_t checksum_of(const Tables* t);
+uint32_t search_width(const Tables* t);
 
 // Device checks used by every device entry point (defined with the kernels):
 // ECCO_OK and the current device's compute-unit count if it is a gfx950.

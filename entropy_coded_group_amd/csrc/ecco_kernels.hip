@@ -163,6 +163,7 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(EncodeArgs a) {
   const uint32_t lane = lane_id(), wave = tid >> 6;
   const uint32_t q = lane >> 4, t16 = lane & 15u;
   const float t = a.t, inv_t = a.inv_t;
+  const int n_search16 = (int)(a.tab->n_search / 16u);
   float* thr = sm.thr[wave][q];
   // tree node of threshold t16 (t16 < 15): with v = t16 + 1 = odd * 2^z, the
   // node sits on level 3 - z at index 2^(3 - z) + (v >> (z + 1))
@@ -231,6 +232,7 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(EncodeArgs a) {
     uint32_t bp = t16;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
+      if (k >= n_search16) break;       // later patterns repeat earlier ones' end centroids
       const uint32_t p = t16 + 16u * k;
       const float d1 = mn - sm.c0c14[2 * p] * aa;
       const float d2 = mx - sm.c0c14[2 * p + 1] * aa;

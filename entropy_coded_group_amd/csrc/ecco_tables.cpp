@@ -14,6 +14,19 @@
 
 namespace ecco {
 
+// Least n in {16, 32, 64} such that every pattern p >= n has the first and
+// last centroid of pattern p mod n: patterns past n then never win the
+// min/max search (equal fitness, lower index first).
+uint32_t search_width(const Tables* t) {
+  for (uint32_t n = 16; n < (uint32_t)S; n *= 2) {
+    bool rep = true;
+    for (uint32_t p = n; p < (uint32_t)S && rep; ++p)
+      rep = t->c0c14[p][0] == t->c0c14[p % n][0] && t->c0c14[p][1] == t->c0c14[p % n][1];
+    if (rep) return n;
+  }
+  return S;
+}
+
 uint32_t checksum_of(const Tables* t) {
   const uint8_t* p = reinterpret_cast<const uint8_t*>(t) + offsetof(Tables, centroids);
   const uint8_t* e = reinterpret_cast<const uint8_t*>(t) + sizeof(Tables);
@@ -143,6 +156,7 @@ extern "C" int ecco_tables_build(const float* centroids, const uint8_t* code_len
     }
   }
   for (int b = 0; b < 256; ++b) t->fp8_value[b] = fp8_code_value(b);
+  t->n_search = search_width(t);
   t->checksum = checksum_of(t);
   return ECCO_OK;
 }
@@ -152,6 +166,7 @@ extern "C" int ecco_tables_validate(const void* blob) {
   const Tables* t = static_cast<const Tables*>(blob);
   if (t->magic != kMagic || t->version != kVersion || t->size != sizeof(Tables)) return ECCO_ETABLES;
   if (t->checksum != checksum_of(t)) return ECCO_ETABLES;
+  if (t->n_search != search_width(t)) return ECCO_ETABLES;
   float c[S * C];
   uint8_t l[S * H * A];
   for (int p = 0; p < S; ++p)

@@ -199,8 +199,11 @@ extern "C" int ecco_train_patterns(const uint16_t* sample, uint64_t n_values, co
                                    void* tables_host) {
   if (!sample || !tables_host) return ECCO_EINVAL;
   if (n_values == 0 || n_values % G != 0) return ECCO_ESIZE;
-  ecco_train_opts_t o = {25, 10, 0, 0, 0};
+  ecco_train_opts_t o = {25, 10, 0, 0, 0, 0};
   if (opts) o = *opts;
+  if (o.n_patterns == 0) o.n_patterns = S;
+  if (o.n_patterns != 16 && o.n_patterns != 32 && o.n_patterns != (uint32_t)S) return ECCO_EINVAL;
+  const int D = int(o.n_patterns);
   if (o.kmeans_iters == 0) o.kmeans_iters = 25;
   if (o.huff_iters == 0) o.huff_iters = 10;
   unsigned threads = o.threads ? o.threads : std::max(1u, std::thread::hardware_concurrency());
@@ -261,7 +264,7 @@ extern "C" int ecco_train_patterns(const uint16_t* sample, uint64_t n_values, co
       for (int k = 0; k < C; ++k) { double d = vec[i * C + k] - c[k]; s += d * d; }
       return s;
     };
-    int K = int(std::min<size_t>(S, N));
+    int K = int(std::min<size_t>(D, N));
     size_t first = rng.next() % N;
     std::copy(&vec[first * C], &vec[first * C] + C, &cent[0]);
     for (int c = 1; c < K; ++c) {
@@ -274,7 +277,7 @@ extern "C" int ecco_train_patterns(const uint16_t* sample, uint64_t n_values, co
       }
       std::copy(&vec[pick * C], &vec[pick * C] + C, &cent[c * C]);
     }
-    for (int c = K; c < S; ++c) std::copy(&cent[(K - 1) * C], &cent[(K - 1) * C] + C, &cent[c * C]);
+    for (int c = K; c < D; ++c) std::copy(&cent[(K - 1) * C], &cent[(K - 1) * C] + C, &cent[c * C]);
     std::vector<int> asg(N, -1);
     for (uint32_t it = 0; it < o.kmeans_iters; ++it) {
       std::atomic<size_t> moved(0);
@@ -304,6 +307,8 @@ extern "C" int ecco_train_patterns(const uint16_t* sample, uint64_t n_values, co
       }
     }
   }
+  // slots D..63 repeat the D learned patterns
+  for (int p = D; p < S; ++p) std::copy(&cent[(p % D) * C], &cent[(p % D) * C] + C, &cent[p * C]);
   std::vector<float> c32(S * C);
   for (int p = 0; p < S; ++p) {
     float row[C];

@@ -119,6 +119,11 @@ typedef struct {
   uint64_t seed;          /* k-means++ seed (0)                                   */
   uint32_t max_groups;    /* use at most this many sample groups, 0 = all (0)     */
   uint32_t threads;       /* host threads, 0 = hardware concurrency (0)           */
+  uint32_t n_patterns;    /* distinct patterns learned: 16, 32 or 64, 0 = 64 (0);
+                             the blob's 64 slots repeat them (slot p holds
+                             pattern p mod n_patterns), so blocks keep the
+                             6-bit pattern field and the encoder searches only
+                             the distinct ones                                  */
 } ecco_train_opts_t;
 
 /* ---- tables --------------------------------------------------------------
@@ -134,7 +139,11 @@ size_t ecco_tables_size(void);
  * FP16, non-decreasing per pattern, within [-1, 1]) and code_len[64][4][16]
  * (each in [2, 8], every codebook a complete prefix code: Kraft sum exactly
  * 1).  Returns ECCO_ETABLES if the contents violate these rules (the blob is
- * then left unspecified), ECCO_EINVAL for NULL pointers. */
+ * then left unspecified), ECCO_EINVAL for NULL pointers.
+ * The blob records how many patterns the encoder has to search: the least
+ * of 16, 32 and 64 such that every later pattern p has the same first and
+ * last centroid as pattern p mod that number (the min/max fitness then ties
+ * and the lower pattern wins, so the shorter search gives the same blocks). */
 int ecco_tables_build(const float* centroids_host, const uint8_t* code_len_host, void* tables_host);
 
 /* Check a host blob: header, checksum, and the rules of ecco_tables_build. */

@@ -1,0 +1,110 @@
+"""Pattern-selection study (oracle; test infrastructure only).
+
+The pages choose a group's pattern by comparing only the group's min and max
+with each pattern's end centroids, and call a full MSE search too expensive
+for the online (KV-cache) compressor; the referee report asks how often the
+cheap rule picks a different pattern than the MSE-optimal one and what that
+costs, and the free parameter "number of shared patterns" sets S = 64 while
+the online compressor is described with 16 (Ecco review, "What carries the
+argument"; referee report; "Assumptions & free parameters", section 4.3).
+
+pattern_errors(x, tables, t) -> [G, S] quantisation error of every group under
+every pattern: the sum over the 127 values other than the scale element of
+(x_j - q_j)^2 in float64, where q_j = fp16(c_p[sym_j] * a) and sym_j is the
+encoder's midpoint rule (#{k : x_j > m_pk * a}) -- the reconstruction a block
+gives before entropy coding (no clipping, no outlier padding).
+selection_study(...) compares the encoder's min/max choice with the argmin of
+those errors.
+
+    python -m oracle.study     prints the study for the weight and KV
+                               workloads with 64 and 16 patterns
+"""
+
+import numpy as np
+
+from . import fp
+from .codec import encode_groups, decode_blocks, GROUP
+
+F32 = np.float32
+
+
+def pattern_errors(x, tables, t, chunk=2048):
+    x = np.asarray(x, dtype=np.float16).reshape(-1, GROUP)
+    G = x.shape[0]
+    out = np.empty((G, tables.centroids.shape[0]), dtype=np.float64)
+    m = tables.midpoints()[:, :14]                                   # [S, 14]
+    c = tables.centroids                                              # [S, 15]
+    t = F32(t)
+    inv_t = F32(F32(1.0) / t)
+    for g0 in range(0, G, chunk):
+        xx = x[g0:g0 + chunk].astype(np.float32)
+        n = xx.shape[0]
+        rows = np.arange(n)
+        istar = np.argmax(np.abs(xx), axis=1)
+        s8 = fp.fp8_encode((xx[rows, istar] * inv_t).astype(np.float32))
+        a = np.abs((fp.fp8_decode(s8) * t).astype(np.float32))
+        thr = (m[None, :, :] * a[:, None, None]).astype(np.float32)          # [n, S, 14]
+        sym = np.sum(xx[:, None, :, None] > thr[:, :, None, :], axis=3)       # [n, S, 128]
+        rec = (c[None, :, :] * a[:, None, None]).astype(np.float32)          # [n, S, 15]
+        q = np.take_along_axis(rec, np.minimum(sym, 14), axis=2)              # [n, S, 128]
+        q = fp.fp16_rne(q).astype(np.float64)
+        d = (xx[:, None, :].astype(np.float64) - q) ** 2
+        d[rows, :, istar] = 0.0
+        out[g0:g0 + n] = d.sum(axis=2)
+    return out
+
+
+def selection_study(x, tables, t):
+    """Fractions and errors of the min/max choice against the MSE-optimal one."""
+    x = np.asarray(x, dtype=np.float16).reshape(-1, GROUP)
+    err = pattern_errors(x, tables, t)
+    _, info = encode_groups(x, tables, t, return_info=True)
+    p_mm = info["p"]
+    rows = np.arange(x.shape[0])
+    e_mm = err[rows, p_mm]
+    e_opt = err.min(axis=1)
+    differs = e_mm > e_opt                     # a different, strictly better pattern exists
+    n_vals = x.shape[0] * (GROUP - 1)
+    return dict(groups=int(x.shape[0]), frac_differs=float(differs.mean()),
+                mse_minmax=float(e_mm.sum() / n_vals), mse_optimal=float(e_opt.sum() / n_vals),
+                gap=float(e_mm.sum() / max(e_opt.sum(), 1e-300) - 1.0))
+
+
+def codec_report(x, tables, t):
+    """End-to-end numbers of the block codec on x: reconstruction MSE relative
+    to the variance, clipped fraction and padded outliers per group."""
+    x = np.asarray(x, dtype=np.float16).reshape(-1, GROUP)
+    blocks, info = encode_groups(x, tables, t, return_info=True)
+    y = decode_blocks(blocks, tables, t).astype(np.float64)
+    xf = x.astype(np.float64)
+    mse = float(np.mean((xf - y) ** 2))
+    return dict(rel_mse=mse / float(np.var(xf)), clipped=float(info["clipped"].mean()),
+                outliers_per_group=float(info["n"].mean()))
+
+
+def main():
+    import workloads as W
+    from .train import train_tables
+    from .codec import tensor_scale
+    cases = []
+    w = W.c2_layer(0, names=["gate"])["gate"].numpy().reshape(-1, GROUP)[:8192]
+    tw = tensor_scale(float(np.max(np.abs(W.c2_layer(0, names=["gate"])["gate"].numpy().astype(np.float32)))))[0]
+    cases.append(("llama3-8b gate weights", W.c2_sample("gate").numpy(), w, tw))
+    for kind in ("k", "v"):
+        smp = W.kv_sample(kind).numpy()
+        t = tensor_scale(float(np.max(np.abs(smp.astype(np.float32)))))[0]
+        x = W.kv_tensor(kind, shape=(1, 8, 1024, 128)).numpy().reshape(-1, GROUP)
+        cases.append(("kv-cache " + kind.upper(), smp, x, t))
+    for name, sample, x, t in cases:
+        for D in (64, 16):
+            tb = train_tables(sample, distinct=D)
+            s = selection_study(x, tb, t)
+            r = codec_report(x, tb, t)
+            print("%-24s S=%2d  groups %d  min/max differs from MSE-optimal in %.1f %%  MSE min/max %.4g  "
+                  "optimal %.4g  gap %+.1f %%  | codec rel. MSE %.4g  clipped %.1f %%  outliers/group %.2f"
+                  % (name, D, s["groups"], 100 * s["frac_differs"], s["mse_minmax"], s["mse_optimal"],
+                     100 * s["gap"], r["rel_mse"], 100 * r["clipped"], r["outliers_per_group"]), flush=True)
+
+
+if __name__ == "__main__":
+    main()

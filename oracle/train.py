@@ -73,8 +73,17 @@ def learn_codebooks(counts, n_codebooks=4, iters=10):
     return lengths.astype(np.uint8)
 
 
-def train_tables(sample_fp16, n_patterns=64, n_codebooks=4, kmeans_iters=25, huff_iters=10, seed=0):
-    """Learn Tables from an FP16 sample whose size is a multiple of 128."""
+def train_tables(sample_fp16, n_patterns=64, n_codebooks=4, kmeans_iters=25, huff_iters=10, seed=0, distinct=None):
+    """Learn Tables from an FP16 sample whose size is a multiple of 128.
+
+    distinct (default: n_patterns) patterns are learned and slot p of the
+    n_patterns holds pattern p mod distinct -- the 16-pattern variant the pages
+    weigh against 64 (free parameter "number of shared patterns"; section 4.3
+    compressor) in a table of the full width, whose extra slots never win the
+    min/max search because they tie with a lower slot."""
+    D = n_patterns if distinct is None else int(distinct)
+    if D < 1 or D > n_patterns:
+        raise ValueError("distinct must be in 1..n_patterns")
     x = np.asarray(sample_fp16, dtype=np.float16).reshape(-1, GROUP)
     amax = float(np.max(np.abs(x.astype(np.float32)))) if x.size else 0.0
     t, _ = tensor_scale(amax)
@@ -83,10 +92,11 @@ def train_tables(sample_fp16, n_patterns=64, n_codebooks=4, kmeans_iters=25, huf
         cent = np.tile(np.linspace(-1, 1, N_CENTROIDS), (n_patterns, 1))
     else:
         vecs, _ = kmeans_1d_exact(y, N_CENTROIDS)
-        K = min(n_patterns, vecs.shape[0])
+        K = min(D, vecs.shape[0])
         cent, _ = lloyd(vecs, K, kmeans_iters, seed)
-        if K < n_patterns:                                            # tiny samples
-            cent = np.concatenate([cent, np.repeat(cent[-1:], n_patterns - K, axis=0)])
+        if K < D:                                                     # tiny samples
+            cent = np.concatenate([cent, np.repeat(cent[-1:], D - K, axis=0)])
+        cent = cent[np.arange(n_patterns) % D]
     cent = np.clip(np.sort(cent.astype(np.float16).astype(np.float32), axis=1), -1.0, 1.0)
     cent = cent.astype(np.float16).astype(np.float32)
     flat = Tables(cent, np.full((n_patterns, n_codebooks, 16), 4, dtype=np.uint8))

@@ -170,3 +170,35 @@ def test_library_training_gives_valid_tables_of_oracle_quality():
         y = codec.decode_blocks(codec.encode_groups(x, tb, t), tb, t)
         mse.append(oracle.metrics.reconstruction(x, y)["mse"])
     assert mse[0] <= 1.25 * mse[1], mse
+
+
+def _n_search(blob):
+    return int(np.frombuffer(bytes(blob[16:20]), dtype=np.uint32)[0])
+
+
+def test_tables_record_how_many_patterns_the_encoder_searches():
+    tb = _golden()
+    assert _n_search(ecco.ecco_tables_build(tb.centroids, tb.code_len)) == 64
+    for d in (16, 32):
+        blob = ecco.ecco_tables_build(tb.centroids[np.arange(64) % d], tb.code_len)
+        assert _n_search(blob) == d and ecco.ecco_tables_validate(blob) == 0
+    # only the end centroids decide it (the search compares min and max only)
+    c = tb.centroids[np.arange(64) % 16].copy()
+    c[40, 7] = c[40, 6]
+    assert _n_search(ecco.ecco_tables_build(c, tb.code_len)) == 16
+    c[40, 14] = np.float32(np.float16(c[40, 14] * 0.5 + 0.5))
+    assert _n_search(ecco.ecco_tables_build(c, tb.code_len)) == 64
+    # a blob whose recorded width disagrees with its centroids is rejected
+    blob = ecco.ecco_tables_build(tb.centroids, tb.code_len)
+    blob[16:20] = np.frombuffer(np.uint32(16).tobytes(), np.uint8)
+    assert ecco.ecco_tables_validate(blob) == -4
+
+
+def test_library_trainer_sixteen_patterns():
+    sample = W.c1_sample(n_values=512 * 128).numpy()
+    blob = ecco.ecco_train_patterns(sample, kmeans_iters=5, huff_iters=3, threads=4, n_patterns=16)
+    assert ecco.ecco_tables_validate(blob) == 0 and _n_search(blob) == 16
+    c, _ = ecco.ecco_tables_get(blob)
+    assert np.array_equal(c, c[np.arange(64) % 16])
+    with pytest.raises(ecco.EccoError):
+        ecco.ecco_train_patterns(sample, kmeans_iters=2, huff_iters=2, threads=2, n_patterns=8)

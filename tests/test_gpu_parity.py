@@ -169,6 +169,24 @@ def test_random_groups_random_tables(dev, kind, seed, n):
     assert_fp16_equal(gpu_decode(o_blocks, tdev, t), codec.decode_blocks(o_blocks, tb, t), "decode")
 
 
+@pytest.mark.parametrize("distinct", [16, 32])
+def test_repeated_pattern_tables_encode_exact(dev, distinct):
+    """Tables whose 64 slots repeat 16 or 32 patterns: the encoder searches only
+    the distinct ones and must still give the oracle's blocks (which search
+    all 64)."""
+    base = random_tables(50 + distinct)
+    tb = codec.Tables(base.centroids[np.arange(64) % distinct], base.code_len)
+    tdev = dev_tables(tb)
+    x = np.concatenate([W.random_groups(1500, 51, "normal").numpy(), W.random_groups(500, 52, "laplace").numpy()])
+    t = scale_of(x)
+    say("repeated patterns %d" % distinct)
+    g_blocks, g_stats = gpu_encode(x, tdev, t, stats=True)
+    o_blocks, info = codec.encode_groups(x, tb, t, return_info=True)
+    assert info["p"].max() < distinct
+    assert_blocks_equal(g_blocks, o_blocks, "encode, %d distinct patterns" % distinct)
+    assert g_stats == info["stats"]
+
+
 def test_heavily_clipped_groups(dev):
     tb = adversarial_tables(11)
     tdev = dev_tables(tb)
