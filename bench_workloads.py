@@ -186,6 +186,55 @@ def bench_ffn(args, torch, ecco, W):
                  per_case=out)
 
 
+def bench_attn(args, torch, ecco, W):
+    """Decode-phase attention over the compressed [16, 8, 8192, 128] K and V
+    caches, 4 query heads per kv head (LLaMA-3-8B GQA): ecco_attention_decode
+    against decoding both caches (ecco_decode_many) then torch's fused
+    scaled-dot-product attention on the FP16 caches."""
+    import torch.nn.functional as F
+    B, H, S, D = W.KV_SHAPE
+    G = 4
+    c = {}
+    for kind in ("k", "v"):
+        sample = W.kv_sample(kind)
+        blob = ecco.ecco_train_patterns(sample, threads=min(16, os.cpu_count() or 1))
+        amax = float(np.max(np.abs(sample.numpy().astype(np.float32))))
+        t = ecco.ecco_tensor_scale_from_amax(amax)
+        x = W.kv_tensor(kind).cuda()
+        tdev = ecco.tables_to_device(blob)
+        blocks = torch.empty((B, H, S, 64), dtype=torch.uint8, device="cuda")
+        ecco.ecco_encode(x, 1, B * H * S, B * H * S * D, B * H * S, tdev, t, blocks)
+        c[kind] = dict(t=t, tdev=tdev, blocks=blocks, y=torch.empty_like(x))
+        del x
+    q = W.c5_x(B * H * G, D, seed=77).cuda().reshape(B, H * G, D)
+    ws = torch.empty(ecco.ecco_attention_workspace_size(B, H, G, S), dtype=torch.uint8, device="cuda")
+    out = torch.empty((B, H * G, D), dtype=torch.float32, device="cuda")
+    scale = 1.0 / np.sqrt(D)
+
+    def fused():
+        ecco.ecco_attention_decode(c["k"]["blocks"], c["k"]["tdev"], c["k"]["t"], c["v"]["blocks"], c["v"]["tdev"],
+                                   c["v"]["t"], q, B, H, G, S, S, scale, ws, out)
+
+    jobs = [(c[k]["blocks"], 1, B * H * S, B * H * S, B * H * S * D, c[k]["tdev"], c[k]["t"], c[k]["y"])
+            for k in ("k", "v")]
+    q4 = q.reshape(B, H * G, 1, D)
+
+    def unfused():
+        ecco.ecco_decode_many(jobs)
+        F.scaled_dot_product_attention(q4, c["k"]["y"], c["v"]["y"], scale=scale, enable_gqa=True)
+
+    tf = _timed(torch, fused, args.steps, args.warmup)
+    tu = _timed(torch, unfused, args.steps, args.warmup)
+    comp = 2 * B * H * S * 64
+    fused_us, unfused_us = np.mean(tf) * 1e6, np.mean(tu) * 1e6
+    return _line("fused decode+attention speedup over decode then SDPA", unfused_us / fused_us, "x", args,
+                 fused_us / 1e3, {"workload": "decode-phase attention, K,V caches [16,8,8192,128], 4 query heads "
+                                              "per kv head, one query token per sequence"},
+                 fused_us=round(fused_us, 2), decode_then_sdpa_us=round(unfused_us, 2),
+                 compressed_GBps=round(comp / (fused_us * 1e-6) / 1e9, 1),
+                 compressed_bytes=comp)
+
+
 def bench_copy(args, torch, ecco, W):
     nbytes = 1 << 30
     a = torch.ones(nbytes // 2, dtype=torch.float16, device="cuda")
@@ -198,5 +247,5 @@ def bench_copy(args, torch, ecco, W):
 
 
 def run_workload(args, torch, ecco, W):
-    return {"kv": bench_kv, "model": bench_model, "ffn": bench_ffn,
+    return {"kv": bench_kv, "model": bench_model, "ffn": bench_ffn, "attn": bench_attn,
             "copy": bench_copy}[args.workload](args, torch, ecco, W)

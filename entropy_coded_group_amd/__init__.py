@@ -19,7 +19,8 @@ __all__ = [
     "EccoError", "lib", "library_path",
     "ecco_tables_size", "ecco_tables_build", "ecco_tables_validate", "ecco_tables_get",
     "ecco_train_patterns", "ecco_tensor_scale_from_amax", "ecco_amax", "ecco_encode",
-    "ecco_decode", "ecco_decode_many", "ecco_decode_gemv", "ecco_strerror", "ecco_version",
+    "ecco_decode", "ecco_decode_many", "ecco_decode_gemv", "ecco_attention_workspace_size",
+    "ecco_attention_decode", "ecco_strerror", "ecco_version",
     "STATS_FIELDS", "DECODE_MAX_JOBS", "tables_to_device",
 ]
 
@@ -81,6 +82,9 @@ def lib():
             "ecco_decode": (i32, [vp, u64, u64, u64, u64, vp, f32, vp, vp]),
             "ecco_decode_many": (i32, [vp, ctypes.c_uint32, vp]),
             "ecco_decode_gemv": (i32, [vp, vp, f32, i64, i64, vp, i64, vp, vp]),
+            "ecco_attention_workspace_size": (ctypes.c_size_t, [u64, u64, u64, u64]),
+            "ecco_attention_decode": (i32, [vp, vp, f32, vp, vp, f32, vp, u64, u64, u64, u64, u64, f32, vp, vp,
+                                            vp]),
             "ecco_strerror": (ctypes.c_char_p, [i32]),
             "ecco_version": (ctypes.c_char_p, []),
         }
@@ -216,6 +220,18 @@ def ecco_decode_gemv(blocks, tables_dev, tensor_scale, out_features, in_features
     _check(lib().ecco_decode_gemv(_ptr(blocks), _ptr(tables_dev), float(tensor_scale), int(out_features),
                                   int(in_features), _ptr(x), int(batch), _ptr(y), _stream(stream)),
            "ecco_decode_gemv")
+
+
+def ecco_attention_workspace_size(batch, kv_heads, group, seq):
+    return int(lib().ecco_attention_workspace_size(int(batch), int(kv_heads), int(group), int(seq)))
+
+
+def ecco_attention_decode(k_blocks, k_tables_dev, k_scale, v_blocks, v_tables_dev, v_scale, q, batch, kv_heads,
+                          group, seq, kv_stride_tokens, scale, workspace, out, stream=None):
+    _check(lib().ecco_attention_decode(_ptr(k_blocks), _ptr(k_tables_dev), float(k_scale), _ptr(v_blocks),
+                                       _ptr(v_tables_dev), float(v_scale), _ptr(q), int(batch), int(kv_heads),
+                                       int(group), int(seq), int(kv_stride_tokens), float(scale), _ptr(workspace),
+                                       _ptr(out), _stream(stream)), "ecco_attention_decode")
 
 
 def ecco_strerror(code):

@@ -88,6 +88,26 @@ __device__ __forceinline__ uint64_t row_min_u64(uint64_t v) {
   v = min_u64_dpp<kRowMirror>(v);
   return v;
 }
+// acc + sum of the products of 8 FP16 pairs, FP32 accumulation
+// (v_dot2_f32_f16: two products summed into an FP32 accumulator).
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float dot8(uint4 w, uint4 x, float acc) {
+  acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, w.x), __builtin_bit_cast(half2_t, x.x), acc, false);
+  acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, w.y), __builtin_bit_cast(half2_t, x.y), acc, false);
+  acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, w.z), __builtin_bit_cast(half2_t, x.z), acc, false);
+  acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, w.w), __builtin_bit_cast(half2_t, x.w), acc, false);
+  return acc;
+}
+
+// Sum over the 16 lanes of a DPP row; every lane of the row gets it.
+__device__ __forceinline__ float row_sum_f32(float v) {
+  v += dpp_f32<kQuadXor1>(v);
+  v += dpp_f32<kQuadXor2>(v);
+  v += dpp_f32<kRowHalfMirror>(v);
+  v += dpp_f32<kRowMirror>(v);
+  return v;
+}
+
 // Sum over the whole wave, in a fixed order: rows first, then the four row
 // totals read back in row order.  The result is uniform.
 __device__ __forceinline__ float wave_sum_f32(float v) {
@@ -100,6 +120,18 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
   const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
   const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
   return ((r0 + r1) + r2) + r3;
+}
+
+__device__ __forceinline__ float wave_max_f32(float v) {
+  v = fmaxf(v, dpp_f32<kQuadXor1>(v));
+  v = fmaxf(v, dpp_f32<kQuadXor2>(v));
+  v = fmaxf(v, dpp_f32<kRowHalfMirror>(v));
+  v = fmaxf(v, dpp_f32<kRowMirror>(v));
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
 // Inclusive prefix sum over the 16 lanes of a row (Hillis-Steele).

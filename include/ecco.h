@@ -225,6 +225,28 @@ int ecco_decode_gemv(const void* blocks_dev, const void* tables_dev, float tenso
                      int64_t out_features, int64_t in_features,
                      const uint16_t* x_dev, int64_t batch, float* y_dev, void* stream);
 
+/* Decode-phase attention over Ecco-compressed K and V caches, one query token
+ * per sequence -- the consumer of the online KV codec ("Core claim": KV cache
+ * blocks decompressed on load).  For b < B, kv head h < H_kv and g < G (query
+ * heads per kv head, query head hq = h * G + g):
+ *   s_t   = scale * sum_d q[b][hq][d] * K[b][h][t][d]        t < S
+ *   p_t   = exp(s_t - max_t s_t) / sum_t exp(s_t - max_t s_t)
+ *   out[b][hq][d] = sum_t p_t * V[b][h][t][d]
+ * with K and V the decoded FP16 values; products and sums in FP32.
+ * k_blocks_dev / v_blocks_dev: [B][H_kv][kv_stride_tokens] blocks (the layout
+ * ecco_encode writes for a [B, H_kv, S_max, 128] cache, kv_stride_tokens =
+ * S_max >= S); q_dev: [B][H_kv * G][128] FP16; out_dev: [B][H_kv * G][128]
+ * FP32, overwritten.  workspace_dev (256-byte aligned) holds
+ * ecco_attention_workspace_size(B, H_kv, G, S) bytes of caller memory that
+ * the call uses for scores and partial sums; its contents are unspecified
+ * afterwards.  ECCO_ESIZE unless B, H_kv, S >= 1 and G is 1, 2, 4 or 8. */
+size_t ecco_attention_workspace_size(uint64_t batch, uint64_t kv_heads, uint64_t group, uint64_t seq);
+int ecco_attention_decode(const void* k_blocks_dev, const void* k_tables_dev, float k_scale,
+                          const void* v_blocks_dev, const void* v_tables_dev, float v_scale,
+                          const uint16_t* q_dev, uint64_t batch, uint64_t kv_heads, uint64_t group,
+                          uint64_t seq, uint64_t kv_stride_tokens, float scale,
+                          void* workspace_dev, float* out_dev, void* stream);
+
 const char* ecco_strerror(int code);
 
 /* Library version string, e.g. "ecco 1.0 (format v1, gfx950)". */

@@ -202,3 +202,30 @@ def test_library_trainer_sixteen_patterns():
     assert np.array_equal(c, c[np.arange(64) % 16])
     with pytest.raises(ecco.EccoError):
         ecco.ecco_train_patterns(sample, kmeans_iters=2, huff_iters=2, threads=2, n_patterns=8)
+
+
+def test_attention_checks_arguments_before_touching_the_device():
+    L = ecco.lib()
+    A = 1 << 20
+    args = [A, A, 1.0, A, A, 1.0, A, 2, 3, 4, 100, 128, 0.1, A, A, None]
+    def call(**kw):
+        a = list(args)
+        names = ["k", "kt", "ks", "v", "vt", "vs", "q", "b", "h", "g", "s", "stride", "scale", "ws", "out", "st"]
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return L.ecco_attention_decode(*a)
+    assert call(k=None) == -1
+    assert call(ws=None) == -1
+    assert call(vs=0.0) == -1
+    assert call(g=3) == -3
+    assert call(s=0) == -3
+    assert call(stride=99) == -3
+    assert call(ws=A + 64) == -2
+    assert call(q=A + 2) == -2
+    assert call(k=A + 32) == -2
+    # workspace: scores [B*H][S][G] floats and partial sums [B*H][ceil(S/128)][G][128] floats, 256-aligned
+    def up(v):
+        return (v + 255) // 256 * 256
+    for (b, h, g, s) in [(2, 3, 4, 100), (16, 8, 4, 8192), (1, 1, 1, 1), (1, 2, 8, 129)]:
+        want = up(b * h * s * g * 4) + up(b * h * ((s + 127) // 128) * g * 128 * 4)
+        assert ecco.ecco_attention_workspace_size(b, h, g, s) == want

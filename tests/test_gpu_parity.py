@@ -449,3 +449,94 @@ def test_ffn70b_gemv_full_size_sampled(dev, name):
         ok, worst = ogemv.gemv_tolerance_ok(y.cpu().numpy()[:, rows], y_ref, mag, in_f)
         assert ok, "c5 %s b=%d worst error / bound = %g" % (name, batch, worst)
         assert not np.any(np.isnan(y.cpu().numpy()))
+
+
+# ------------------------------------------------------------ fused attention
+
+def _attention_case(B, H, G, S, stride, seed):
+    """Oracle-encoded K/V caches [B, H, stride] x 64 B (first S tokens used),
+    their oracle-decoded values, q, and the scales."""
+    tbk, tbv = golden("c3_k"), golden("c3_v")
+    tk, tv = golden_t("c3_k"), golden_t("c3_v")
+    k = W.kv_tensor("k", shape=(B, H, S, 128), seed=seed).numpy()
+    v = W.kv_tensor("v", shape=(B, H, S, 128), seed=seed + 1).numpy()
+    kb = codec.encode_groups(k.reshape(-1, 128), tbk, tk).reshape(B, H, S, 64)
+    vb = codec.encode_groups(v.reshape(-1, 128), tbv, tv).reshape(B, H, S, 64)
+    kd = codec.decode_blocks(kb.reshape(-1, 64), tbk, tk).reshape(B, H, S, 128)
+    vd = codec.decode_blocks(vb.reshape(-1, 64), tbv, tv).reshape(B, H, S, 128)
+    full_k = np.zeros((B, H, stride, 64), np.uint8)
+    full_v = np.zeros((B, H, stride, 64), np.uint8)
+    full_k[:, :, :S] = kb
+    full_v[:, :, :S] = vb
+    q = W.c5_x(B * H * G, 128, seed=seed + 2).numpy().reshape(B, H * G, 128)
+    return dict(tbk=tbk, tbv=tbv, tk=tk, tv=tv, kb=full_k, vb=full_v, kd=kd, vd=vd, q=q)
+
+
+def _gpu_attention(c, B, H, G, S, stride, scale):
+    ws = torch.empty(ecco.ecco_attention_workspace_size(B, H, G, S), dtype=torch.uint8, device="cuda")
+    out = torch.full((B, H * G, 128), float("nan"), dtype=torch.float32, device="cuda")
+    ecco.ecco_attention_decode(torch.from_numpy(c["kb"]).cuda(), dev_tables(c["tbk"]), c["tk"],
+                               torch.from_numpy(c["vb"]).cuda(), dev_tables(c["tbv"]), c["tv"],
+                               torch.from_numpy(np.ascontiguousarray(c["q"])).cuda(), B, H, G, S, stride, scale,
+                               ws, out)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+@pytest.mark.parametrize("B,H,G,S,extra", [(1, 1, 1, 1, 0), (2, 3, 4, 63, 5), (2, 2, 2, 200, 0),
+                                           (1, 3, 8, 1000, 37), (3, 1, 4, 129, 0), (1, 2, 1, 4096, 64)])
+def test_attention_small(dev, B, H, G, S, extra):
+    from oracle import attention
+    stride = S + extra
+    c = _attention_case(B, H, G, S, stride, 60 + S)
+    scale = 1.0 / np.sqrt(128.0)
+    say("attention B=%d H=%d G=%d S=%d" % (B, H, G, S))
+    got = _gpu_attention(c, B, H, G, S, stride, scale)
+    ref, mag = attention.attention_ref(c["kd"], c["vd"], c["q"], scale)
+    ok, worst = attention.attention_tolerance_ok(got, ref, mag)
+    assert ok, "attention outside tolerance: worst error / bound = %g" % worst
+
+
+def test_attention_kv_cache_full_size_sampled(dev):
+    """The full [16, 8, 8192, 128] caches encoded on the GPU, attention for all
+    512 query heads; three (sequence, kv head) pairs checked against the oracle
+    (blocks re-encoded by the oracle from the same values)."""
+    from oracle import attention
+    B, H, S, D = W.KV_SHAPE
+    G = 4
+    tbk, tbv = golden("c3_k"), golden("c3_v")
+    tk, tv = golden_t("c3_k"), golden_t("c3_v")
+    say("attention full size: generate + encode")
+    k = W.kv_tensor("k")
+    v = W.kv_tensor("v")
+    kb = torch.empty((B, H, S, 64), dtype=torch.uint8, device="cuda")
+    vb = torch.empty((B, H, S, 64), dtype=torch.uint8, device="cuda")
+    tkd, tvd = dev_tables(tbk), dev_tables(tbv)
+    kd_ = k.cuda()
+    ecco.ecco_encode(kd_, 1, B * H * S, B * H * S * D, B * H * S, tkd, tk, kb)
+    del kd_
+    vd_ = v.cuda()
+    ecco.ecco_encode(vd_, 1, B * H * S, B * H * S * D, B * H * S, tvd, tv, vb)
+    del vd_
+    q = W.c5_x(B * H * G, 128, seed=77).numpy().reshape(B, H * G, 128)
+    ws = torch.empty(ecco.ecco_attention_workspace_size(B, H, G, S), dtype=torch.uint8, device="cuda")
+    out = torch.full((B, H * G, 128), float("nan"), dtype=torch.float32, device="cuda")
+    scale = 1.0 / np.sqrt(128.0)
+    say("attention full size: run")
+    ecco.ecco_attention_decode(kb, tkd, tk, vb, tvd, tv, torch.from_numpy(q).cuda(), B, H, G, S, S, scale, ws, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.all(np.isfinite(got))
+    gkb, gvb = kb.cpu().numpy(), vb.cpu().numpy()
+    kn, vn = k.numpy(), v.numpy()
+    for (b, h) in [(0, 0), (7, 3), (15, 7)]:
+        say("attention full size: oracle pair (%d, %d)" % (b, h))
+        okb = codec.encode_groups(kn[b, h], tbk, tk)
+        ovb = codec.encode_groups(vn[b, h], tbv, tv)
+        assert_blocks_equal(gkb[b, h], okb, "K blocks (%d, %d)" % (b, h))
+        assert_blocks_equal(gvb[b, h], ovb, "V blocks (%d, %d)" % (b, h))
+        kd = codec.decode_blocks(okb, tbk, tk).reshape(1, 1, S, D)
+        vd = codec.decode_blocks(ovb, tbv, tv).reshape(1, 1, S, D)
+        ref, mag = attention.attention_ref(kd, vd, q[b:b + 1, h * G:(h + 1) * G], scale)
+        ok, worst = attention.attention_tolerance_ok(got[b:b + 1, h * G:(h + 1) * G], ref, mag)
+        assert ok, "pair (%d, %d): worst error / bound = %g" % (b, h, worst)
