@@ -9,7 +9,7 @@
 //            decode core hands each lane 8 values of one token's K row;
 //            v_dot2_f32_f16 against the G query heads' matching 8 values, a
 //            DPP row sum over the token's 16 lanes, scale -> s[pair][t][g]
-//   softmax  one wave per (pair, g) row: max, sum of exp, normalise in place
+//   softmax  one workgroup per pair: max, sum of exp, normalise in place
 //   p . V    one wave per 128 tokens of one pair: decoded V values times the
 //            token's probabilities, FP32 accumulators for the G heads and the
 //            lane's 8 positions, a cross-row reduction, partial sums per unit
@@ -26,7 +26,8 @@
 namespace ecco {
 
 constexpr uint32_t kUnitTokens = 128;   // tokens per p . V work unit (two batches)
-constexpr int kAttnWaves = 8;           // waves per workgroup of the scores and p . V kernels
+constexpr int kScoreWaves = 8;          // waves per workgroup of the scores kernel
+constexpr int kPvWaves = 8;             // waves per workgroup of the p . V kernel
 
 struct AttnArgs {
   const uint8_t* kb;
@@ -52,13 +53,13 @@ __device__ __forceinline__ BatchRegs fetch_tokens(uint32_t lane, const uint8_t* 
 }
 
 template <int G>
-__global__ __launch_bounds__(kAttnWaves * 64) void attn_scores_kernel(AttnArgs a) {
-  __shared__ DecodeSmem<kAttnWaves> sm;
+__global__ __launch_bounds__(kScoreWaves * 64) void attn_scores_kernel(AttnArgs a) {
+  __shared__ DecodeSmem<kScoreWaves> sm;
   stage_decode_tables(sm, a.kt);
   __syncthreads();
   const uint32_t lane = lane_id(), wave = threadIdx.x >> 6;
   const uint32_t total = a.pairs * a.n_kb;
-  const uint32_t stride = gridDim.x * kAttnWaves;
+  const uint32_t stride = gridDim.x * kScoreWaves;
   const uint8_t* idle = reinterpret_cast<const uint8_t*>(a.kt);
   uint32_t batch = wave * gridDim.x + blockIdx.x;   // batches go round the CUs first
   if (batch >= total) return;
@@ -95,35 +96,70 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_scores_kernel(AttnArgs a
   }
 }
 
-// One wave per softmax row (pair, g); the row is read with stride G.
-__global__ __launch_bounds__(256) void attn_softmax_kernel(AttnArgs a) {
-  const uint32_t lane = lane_id();
-  const uint32_t row = blockIdx.x * 4u + (threadIdx.x >> 6);
-  if (row >= a.pairs * a.G) return;
-  const uint32_t pair = row / a.G, g = row % a.G;
-  float* sp = a.probs + (uint64_t)pair * a.S * a.G + g;
-  float m = -__builtin_inff();
-  for (uint32_t t = lane; t < a.S; t += 64u) m = fmaxf(m, sp[(uint64_t)t * a.G]);
-  m = wave_max_f32(m);
-  float z = 0.0f;
-  for (uint32_t t = lane; t < a.S; t += 64u) {
-    const float e = expf(sp[(uint64_t)t * a.G] - m);
-    sp[(uint64_t)t * a.G] = e;
-    z += e;
-  }
-  const float inv = 1.0f / wave_sum_f32(z);
-  for (uint32_t t = lane; t < a.S; t += 64u) sp[(uint64_t)t * a.G] *= inv;
+// Softmax of one pair's G rows, [S][G] with g innermost, by one workgroup:
+// three coalesced passes over the pair's scores (max, sum of exp,
+// normalise), which stay in the L2 cache between them; workgroup reductions
+// through LDS.
+constexpr int kSmThreads = 1024;
+
+template <int G>
+__global__ __launch_bounds__(kSmThreads) void attn_softmax_kernel(AttnArgs a) {
+  __shared__ float red[kSmThreads / 64][G];
+  __shared__ float fin[G];
+  const uint32_t tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  float* base = a.probs + (uint64_t)blockIdx.x * a.S * G;
+  auto wg_reduce = [&](float (&v)[G], bool is_max) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float w = is_max ? wave_max_f32(v[g]) : wave_sum_f32(v[g]);
+      if (lane == 0) red[wave][g] = w;
+    }
+    __syncthreads();
+    if (tid < (uint32_t)G) {
+      float r = red[0][tid];
+      for (int w = 1; w < kSmThreads / 64; ++w) r = is_max ? fmaxf(r, red[w][tid]) : r + red[w][tid];
+      fin[tid] = r;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int g = 0; g < G; ++g) v[g] = fin[g];
+    __syncthreads();
+  };
+  float m[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) m[g] = -__builtin_inff();
+  for (uint32_t t = tid; t < a.S; t += kSmThreads)
+#pragma unroll
+    for (int g = 0; g < G; ++g) m[g] = fmaxf(m[g], base[(uint64_t)t * G + g]);
+  wg_reduce(m, true);
+  float z[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) z[g] = 0.0f;
+  for (uint32_t t = tid; t < a.S; t += kSmThreads)
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float e = expf(base[(uint64_t)t * G + g] - m[g]);
+      base[(uint64_t)t * G + g] = e;
+      z[g] += e;
+    }
+  wg_reduce(z, false);
+  float inv[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) inv[g] = 1.0f / z[g];
+  for (uint32_t t = tid; t < a.S; t += kSmThreads)
+#pragma unroll
+    for (int g = 0; g < G; ++g) base[(uint64_t)t * G + g] *= inv[g];
 }
 
 // p . V for heads g_off .. g_off + GH - 1 of G.
 template <int GH>
-__global__ __launch_bounds__(kAttnWaves * 64) void attn_pv_kernel(AttnArgs a, uint32_t g_off) {
-  __shared__ DecodeSmem<kAttnWaves> sm;
+__global__ __launch_bounds__(kPvWaves * 64) void attn_pv_kernel(AttnArgs a, uint32_t g_off) {
+  __shared__ DecodeSmem<kPvWaves> sm;
   stage_decode_tables(sm, a.vt);
   __syncthreads();
   const uint32_t lane = lane_id(), wave = threadIdx.x >> 6;
   const uint32_t total = a.pairs * a.n_units;
-  const uint32_t stride = gridDim.x * kAttnWaves;
+  const uint32_t stride = gridDim.x * kPvWaves;
   const uint8_t* idle = reinterpret_cast<const uint8_t*>(a.vt);
   uint32_t unit = wave * gridDim.x + blockIdx.x;
   if (unit >= total) return;
@@ -209,6 +245,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   const uint32_t pair = (uint32_t)(row / a.G), g = (uint32_t)(row % a.G);
   const float* src = a.part + ((uint64_t)pair * a.n_units * a.G + g) * 128u + d;
   float s = 0.0f;
+#pragma unroll 8
   for (uint32_t u = 0; u < a.n_units; ++u) s += src[(uint64_t)u * a.G * 128u];
   a.out[row * 128u + d] = s;
 }
@@ -273,21 +310,26 @@ extern "C" int ecco_attention_decode(const void* k_blocks, const void* k_tables,
   (void)hipGetLastError();
   const uint32_t kgrid = std::max<uint32_t>(1, std::min<uint32_t>(a.pairs * a.n_kb, (uint32_t)cus));
   switch (group) {
-    case 1: hipLaunchKernelGGL(attn_scores_kernel<1>, dim3(kgrid), dim3(kAttnWaves * 64), 0, s, a); break;
-    case 2: hipLaunchKernelGGL(attn_scores_kernel<2>, dim3(kgrid), dim3(kAttnWaves * 64), 0, s, a); break;
-    case 4: hipLaunchKernelGGL(attn_scores_kernel<4>, dim3(kgrid), dim3(kAttnWaves * 64), 0, s, a); break;
-    default: hipLaunchKernelGGL(attn_scores_kernel<8>, dim3(kgrid), dim3(kAttnWaves * 64), 0, s, a); break;
+    case 1: hipLaunchKernelGGL(attn_scores_kernel<1>, dim3(kgrid), dim3(kScoreWaves * 64), 0, s, a); break;
+    case 2: hipLaunchKernelGGL(attn_scores_kernel<2>, dim3(kgrid), dim3(kScoreWaves * 64), 0, s, a); break;
+    case 4: hipLaunchKernelGGL(attn_scores_kernel<4>, dim3(kgrid), dim3(kScoreWaves * 64), 0, s, a); break;
+    default: hipLaunchKernelGGL(attn_scores_kernel<8>, dim3(kgrid), dim3(kScoreWaves * 64), 0, s, a); break;
   }
   const uint32_t rows = a.pairs * a.G;
-  hipLaunchKernelGGL(attn_softmax_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, a);
+  switch (group) {
+    case 1: hipLaunchKernelGGL(attn_softmax_kernel<1>, dim3(a.pairs), dim3(kSmThreads), 0, s, a); break;
+    case 2: hipLaunchKernelGGL(attn_softmax_kernel<2>, dim3(a.pairs), dim3(kSmThreads), 0, s, a); break;
+    case 4: hipLaunchKernelGGL(attn_softmax_kernel<4>, dim3(a.pairs), dim3(kSmThreads), 0, s, a); break;
+    default: hipLaunchKernelGGL(attn_softmax_kernel<8>, dim3(a.pairs), dim3(kSmThreads), 0, s, a); break;
+  }
   const uint32_t vgrid = std::max<uint32_t>(1, std::min<uint32_t>(a.pairs * a.n_units, (uint32_t)cus));
   switch (group) {
-    case 1: hipLaunchKernelGGL(attn_pv_kernel<1>, dim3(vgrid), dim3(kAttnWaves * 64), 0, s, a, 0u); break;
-    case 2: hipLaunchKernelGGL(attn_pv_kernel<2>, dim3(vgrid), dim3(kAttnWaves * 64), 0, s, a, 0u); break;
-    case 4: hipLaunchKernelGGL(attn_pv_kernel<4>, dim3(vgrid), dim3(kAttnWaves * 64), 0, s, a, 0u); break;
+    case 1: hipLaunchKernelGGL(attn_pv_kernel<1>, dim3(vgrid), dim3(kPvWaves * 64), 0, s, a, 0u); break;
+    case 2: hipLaunchKernelGGL(attn_pv_kernel<2>, dim3(vgrid), dim3(kPvWaves * 64), 0, s, a, 0u); break;
+    case 4: hipLaunchKernelGGL(attn_pv_kernel<4>, dim3(vgrid), dim3(kPvWaves * 64), 0, s, a, 0u); break;
     default:   // eight heads as two launches of four (accumulators for all eight do not fit)
-      hipLaunchKernelGGL(attn_pv_kernel<4>, dim3(vgrid), dim3(kAttnWaves * 64), 0, s, a, 0u);
-      hipLaunchKernelGGL(attn_pv_kernel<4>, dim3(vgrid), dim3(kAttnWaves * 64), 0, s, a, 4u);
+      hipLaunchKernelGGL(attn_pv_kernel<4>, dim3(vgrid), dim3(kPvWaves * 64), 0, s, a, 0u);
+      hipLaunchKernelGGL(attn_pv_kernel<4>, dim3(vgrid), dim3(kPvWaves * 64), 0, s, a, 4u);
       break;
   }
   const uint64_t n = (uint64_t)rows * 128u;
