@@ -18,6 +18,13 @@ those errors.
 
     python -m oracle.study     prints the study for the weight and KV
                                workloads with 64 and 16 patterns
+    python -m oracle.study design-space
+                               the S x H sweep: quantisation MSE, coded
+                               bits per group and clipped fraction for
+                               S in {16, 32, 64, 128}, H in {1, 2, 4, 8}
+                               (header log2 S + log2 H + 8 bits); S = 128
+                               and H = 8 do not fit the v1 header and are
+                               evaluated without building blocks
 """
 
 import numpy as np
@@ -82,6 +89,92 @@ def codec_report(x, tables, t):
                 outliers_per_group=float(info["n"].mean()))
 
 
+def assign_groups(x, centroids, t):
+    """The encoder's steps 1-4 for an arbitrary number of patterns: pattern p
+    (min/max rule, lowest on ties), symbols (scale element = 15) and the
+    quantisation error of each group (as pattern_errors, chosen pattern)."""
+    x = np.asarray(x, dtype=np.float16).reshape(-1, GROUP)
+    c = np.asarray(centroids, np.float32)
+    m = ((c[:, :-1] + c[:, 1:]).astype(np.float32) * F32(0.5)).astype(np.float32)       # [S, 14]
+    t = F32(t)
+    inv_t = F32(F32(1.0) / t)
+    xx = x.astype(np.float32)
+    n = xx.shape[0]
+    rows = np.arange(n)
+    istar = np.argmax(np.abs(xx), axis=1)
+    s8 = fp.fp8_encode((xx[rows, istar] * inv_t).astype(np.float32))
+    a = np.abs((fp.fp8_decode(s8) * t).astype(np.float32))
+    others = np.ones_like(xx, dtype=bool)
+    others[rows, istar] = False
+    gmin = np.min(np.where(others, xx, F32(np.inf)), axis=1).astype(np.float32)
+    gmax = np.max(np.where(others, xx, F32(-np.inf)), axis=1).astype(np.float32)
+    d1 = (gmin[:, None] - (c[None, :, 0] * a[:, None]).astype(np.float32)).astype(np.float32)
+    d2 = (gmax[:, None] - (c[None, :, -1] * a[:, None]).astype(np.float32)).astype(np.float32)
+    p = np.argmin((d1 * d1 + d2 * d2).astype(np.float32), axis=1)
+    thr = (m[p] * a[:, None]).astype(np.float32)
+    sym = np.sum(xx[:, :, None] > thr[:, None, :], axis=2)
+    q = fp.fp16_rne((c[p][rows[:, None], sym] * a[:, None]).astype(np.float32)).astype(np.float64)
+    err = (xx.astype(np.float64) - q) ** 2
+    err[rows, istar] = 0.0
+    sym[rows, istar] = 15
+    return p, sym, err.sum(axis=1)
+
+
+def design_point(x, centroids, code_len, t):
+    """Bits and error of the block codec with S patterns and H codebooks
+    (header log2 S + log2 H + 8 bits, 512-bit blocks): mean quantisation MSE,
+    mean coded bits per group (header + shortest codebook), clipped fraction."""
+    S, H = np.asarray(code_len).shape[:2]
+    p, sym, err = assign_groups(x, centroids, t)
+    lens = np.asarray(code_len, np.int64)[p]                                    # [G, H, 16]
+    Lh = np.stack([np.take_along_axis(lens[:, h, :], sym, axis=1).sum(axis=1) for h in range(H)], axis=1)
+    L = Lh.min(axis=1)
+    header = int(np.ceil(np.log2(S))) + int(np.ceil(np.log2(H))) + 8
+    return dict(mse=float(err.sum() / (len(p) * (GROUP - 1))), bits_per_group=float(np.mean(header + L)),
+                clipped=float(np.mean(header + L > 512)), header_bits=header)
+
+
+def design_space(sample, x, t_sample, t, S_list=(16, 32, 64, 128), H_list=(1, 2, 4, 8), kmeans_iters=25,
+                 huff_iters=10, seed=0):
+    """Learn tables for every (S, H) from one sample (the 1-D k-means runs
+    once) and evaluate each on x.  Codebooks are learned with the trainer's
+    rule (oracle/train.py) on the groups the min/max rule gives each pattern."""
+    from .kmeans import kmeans_1d_exact, lloyd
+    from .train import normalised_groups, learn_codebooks
+    xs = np.asarray(sample, np.float16).reshape(-1, GROUP)
+    vecs, _ = kmeans_1d_exact(normalised_groups(xs, t_sample), 15)
+    out = {}
+    for S in S_list:
+        cent, _ = lloyd(vecs, min(S, vecs.shape[0]), kmeans_iters, seed)
+        cent = np.clip(np.sort(cent.astype(np.float16).astype(np.float32), axis=1), -1.0, 1.0)
+        cent = cent.astype(np.float16).astype(np.float32)
+        p, sym, _ = assign_groups(xs, cent, t_sample)
+        counts = np.zeros((xs.shape[0], 16), dtype=np.int64)
+        np.add.at(counts, (np.repeat(np.arange(xs.shape[0]), GROUP), sym.ravel()), 1)
+        for H in H_list:
+            code_len = np.stack([learn_codebooks(counts[p == k], H, huff_iters) for k in range(cent.shape[0])])
+            out[(S, H)] = design_point(x, cent, code_len, t)
+    return out
+
+
+def main_design_space():
+    import workloads as W
+    from .codec import tensor_scale
+    gate = W.c2_layer(0, names=["gate"])["gate"].numpy()
+    tw = tensor_scale(float(np.max(np.abs(gate.astype(np.float32)))))[0]
+    smp = W.c2_sample("gate").numpy()
+    ts = tensor_scale(float(np.max(np.abs(smp.astype(np.float32)))))[0]
+    ksmp = W.kv_sample("k").numpy()
+    tk = tensor_scale(float(np.max(np.abs(ksmp.astype(np.float32)))))[0]
+    kx = W.kv_tensor("k", shape=(1, 8, 1024, 128)).numpy().reshape(-1, GROUP)
+    for name, sample, x, t_s, t in (("llama3-8b gate weights", smp, gate.reshape(-1, GROUP)[:8192], ts, tw),
+                                    ("kv-cache K", ksmp, kx, tk, tk)):
+        res = design_space(sample, x, t_s, t)
+        for (S, H), r in sorted(res.items()):
+            print("%-24s S=%3d H=%d  header %2d b  MSE %.5g  bits/group %.1f  clipped %.1f %%"
+                  % (name, S, H, r["header_bits"], r["mse"], r["bits_per_group"], 100 * r["clipped"]), flush=True)
+
+
 def main():
     import workloads as W
     from .train import train_tables
@@ -107,4 +200,8 @@ def main():
 
 
 if __name__ == "__main__":
-    main()
+    import sys
+    if len(sys.argv) > 1 and sys.argv[1] == "design-space":
+        main_design_space()
+    else:
+        main()

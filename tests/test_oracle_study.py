@@ -80,3 +80,38 @@ def test_sixteen_pattern_tables_repeat_and_never_choose_a_repeat():
     x, t = _case(500)
     _, info = codec.encode_groups(x, tb, t, return_info=True)
     assert info["p"].max() < 16
+
+
+def test_design_point_agrees_with_the_codec_at_64_patterns_4_codebooks():
+    """At S = 64, H = 4 the sweep's coded length and clip decision are the
+    codec's own (header 16 bits)."""
+    tb = _golden()
+    x, t = _case(800)
+    r = study.design_point(x, tb.centroids, tb.code_len, t)
+    _, info = codec.encode_groups(x, tb, t, return_info=True)
+    assert r["header_bits"] == 16
+    assert np.isclose(r["bits_per_group"], np.mean(16 + info["L"]))
+    assert np.isclose(r["clipped"], info["clipped"].mean())
+    err = study.pattern_errors(x, tb, t)
+    assert np.isclose(r["mse"], err[np.arange(len(x)), info["p"]].sum() / (len(x) * 127), rtol=1e-12)
+
+
+def test_assign_groups_matches_the_codec_choice():
+    tb = _golden()
+    x, t = _case(500)
+    p, sym, _ = study.assign_groups(x, tb.centroids, t)
+    _, info = codec.encode_groups(x, tb, t, return_info=True)
+    assert np.array_equal(p, info["p"]) and np.array_equal(sym, info["sym"])
+
+
+def test_design_space_small_sweep():
+    """Every configuration yields finite numbers, and the header takes
+    log2 S + log2 H + 8 bits."""
+    sample = W.c1_sample(n_values=128 * 128).numpy()
+    x, t = _case(200)
+    ts = codec.tensor_scale(float(np.max(np.abs(sample.astype(np.float32)))))[0]
+    res = study.design_space(sample, x, ts, t, S_list=(16, 64), H_list=(1, 4), kmeans_iters=3, huff_iters=3)
+    assert set(res) == {(16, 1), (16, 4), (64, 1), (64, 4)}
+    assert res[(16, 1)]["header_bits"] == 12 and res[(64, 4)]["header_bits"] == 16
+    for r in res.values():
+        assert np.isfinite(r["mse"]) and 0 <= r["clipped"] <= 1 and r["bits_per_group"] > 0
