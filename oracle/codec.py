@@ -59,6 +59,16 @@ LEN_MIN, LEN_MAX = 2, 8
 F32 = np.float32
 
 
+def record_layout(group):
+    """(position bits, record bits) of the outlier records for a group size:
+    log2(group) bits of position plus the 8-bit FP8 value (15 bits for the
+    128-value weight / KV-cache groups, 14 for the 64-value activation groups)."""
+    if group not in (64, 128):
+        raise ValueError("group must be 64 or 128")
+    pb = int(group).bit_length() - 1
+    return pb, pb + 8
+
+
 @dataclass
 class Tables:
     """Per-tensor side data: pattern centroids and codebook code lengths."""
@@ -110,7 +120,7 @@ def _bits_of(value, nbits):
     return ((value[..., None] >> np.arange(nbits)) & 1).astype(np.uint8)
 
 
-def encode_groups(x, tables, t, return_info=False):
+def encode_groups(x, tables, t, return_info=False, group=GROUP):
     """Encode FP16 groups x [G, 128] into blocks [G, 64] uint8.
 
     Steps (per group, vectorised over groups):
@@ -126,7 +136,8 @@ def encode_groups(x, tables, t, return_info=False):
     x = np.asarray(x)
     if x.dtype != np.float16:
         raise TypeError("x must be float16")
-    x = x.reshape(-1, GROUP)
+    pos_bits, rec_bits = record_layout(group)
+    x = x.reshape(-1, group)
     G = x.shape[0]
     t = F32(t)
     inv_t = F32(F32(1.0) / t)
@@ -147,7 +158,7 @@ def encode_groups(x, tables, t, return_info=False):
     S = (fp.fp8_decode(s8) * t).astype(np.float32)
     a = np.abs(S)
     # 3. min/max pattern selection over the other 127 values
-    others = np.ones((G, GROUP), dtype=bool)
+    others = np.ones((G, group), dtype=bool)
     others[rows, istar] = False
     gmin = np.min(np.where(others, x32, F32(np.inf)), axis=1).astype(np.float32)
     gmax = np.max(np.where(others, x32, F32(-np.inf)), axis=1).astype(np.float32)
@@ -184,17 +195,17 @@ def encode_groups(x, tables, t, return_info=False):
     bits = bits[:, :BLOCK_BITS]
     # 7. outlier padding in unclipped blocks
     free = np.where(clipped, 0, BLOCK_BITS - HEADER_BITS - L)
-    n = np.where(clipped, 0, np.minimum(MAX_OUTLIERS, free // RECORD_BITS))
+    n = np.where(clipped, 0, np.minimum(MAX_OUTLIERS, free // rec_bits))
     key = np.where(others, -ax, F32(np.inf))                       # larger |x| first
     order = np.argsort(key, axis=1, kind="stable")                 # ties: lower j first
     rec_val = fp.fp8_encode((x32 * inv_t).astype(np.float32)).astype(np.int64)
     for r in range(MAX_OUTLIERS):
         j = order[:, r]
-        rec = j | (rec_val[rows, j] << 7)
-        rb = _bits_of(rec, RECORD_BITS)                            # [G, 15]
-        lo = BLOCK_BITS - RECORD_BITS * (r + 1)
+        rec = j | (rec_val[rows, j] << pos_bits)
+        rb = _bits_of(rec, rec_bits)                               # [G, rec_bits]
+        lo = BLOCK_BITS - rec_bits * (r + 1)
         use = (r < n)[:, None]
-        bits[:, lo:lo + RECORD_BITS] = np.where(use, rb, bits[:, lo:lo + RECORD_BITS])
+        bits[:, lo:lo + rec_bits] = np.where(use, rb, bits[:, lo:lo + rec_bits])
     blocks = np.packbits(bits, axis=1, bitorder="little")
     blocks[:, 0] = (p | (h << 6)).astype(np.uint8)
     blocks[:, 1] = s8
@@ -206,16 +217,16 @@ def encode_groups(x, tables, t, return_info=False):
     info["stats"] = dict(
         groups=int(G),
         clipped_groups=int(np.sum(clipped)),
-        clipped_values=int(np.sum(GROUP - k)),
+        clipped_values=int(np.sum(group - k)),
         padded_outliers=int(np.sum(n)),
-        pad_bits=int(np.sum(RECORD_BITS * n)),
-        fill_bits=int(np.sum(np.where(clipped, 0, free - RECORD_BITS * n))),
+        pad_bits=int(np.sum(rec_bits * n)),
+        fill_bits=int(np.sum(np.where(clipped, 0, free - rec_bits * n))),
         nonfinite_groups=int(np.sum(nonfinite)),
     )
     return blocks, info
 
 
-def decode_blocks(blocks, tables, t, return_info=False):
+def decode_blocks(blocks, tables, t, return_info=False, group=GROUP):
     """Decode blocks [G, 64] uint8 into FP16 groups [G, 128].
 
     Steps (per block, vectorised over blocks):
@@ -229,6 +240,7 @@ def decode_blocks(blocks, tables, t, return_info=False):
          applied in order r = 0..n-1: out[pos_r] = fp16(f32(v8_r) * t)
     Any 512-bit input is accepted.
     """
+    pos_bits, rec_bits = record_layout(group)
     blocks = np.ascontiguousarray(np.asarray(blocks, dtype=np.uint8).reshape(-1, BLOCK_BYTES))
     G = blocks.shape[0]
     t = F32(t)
@@ -253,9 +265,9 @@ def decode_blocks(blocks, tables, t, return_info=False):
 
     pos = np.full(G, HEADER_BITS, dtype=np.int64)
     alive = np.ones(G, dtype=bool)
-    k = np.full(G, GROUP, dtype=np.int64)
-    sym = np.zeros((G, GROUP), dtype=np.int64)
-    for j in range(GROUP):
+    k = np.full(G, group, dtype=np.int64)
+    sym = np.zeros((G, group), dtype=np.int64)
+    for j in range(group):
         win = bits[rows[:, None], pos[:, None] + b_idx]           # [G, 8]
         match = np.all((win[:, None, :] == expect) | ~care, axis=2)
         match &= (pos[:, None] + ln) <= BLOCK_BITS
@@ -270,17 +282,17 @@ def decode_blocks(blocks, tables, t, return_info=False):
     cidx = np.minimum(sym, N_CENTROIDS - 1)
     cval = (c[p[:, None], cidx] * a[:, None]).astype(np.float32)
     vals = np.where(sym == SCALE_SYMBOL, fp.fp16_rne(S)[:, None], fp.fp16_rne(cval))
-    jj = np.arange(GROUP)[None, :]
+    jj = np.arange(group)[None, :]
     out = np.where(jj < k[:, None], vals, np.float16(0.0)).astype(np.float16)
 
-    full = k == GROUP
-    n = np.where(full, np.minimum(MAX_OUTLIERS, (BLOCK_BITS - pos) // RECORD_BITS), 0)
-    weights = (1 << np.arange(RECORD_BITS)).astype(np.int64)
+    full = k == group
+    n = np.where(full, np.minimum(MAX_OUTLIERS, (BLOCK_BITS - pos) // rec_bits), 0)
+    weights = (1 << np.arange(rec_bits)).astype(np.int64)
     for r in range(MAX_OUTLIERS):
-        lo = BLOCK_BITS - RECORD_BITS * (r + 1)
-        rec = (bits[:, lo:lo + RECORD_BITS].astype(np.int64) * weights).sum(axis=1)
-        j = rec & 127
-        v8 = (rec >> 7).astype(np.uint8)
+        lo = BLOCK_BITS - rec_bits * (r + 1)
+        rec = (bits[:, lo:lo + rec_bits].astype(np.int64) * weights).sum(axis=1)
+        j = rec & (group - 1)
+        v8 = (rec >> pos_bits).astype(np.uint8)
         val = fp.fp16_rne((fp.fp8_decode(v8) * t).astype(np.float32))
         use = r < n
         out[rows[use], j[use]] = val[use]

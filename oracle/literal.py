@@ -27,20 +27,27 @@ def _h(v):
     return np.float16(F32(v))
 
 
-def encode_group(x, centroids, code_len, t):
-    """x: 128 float16 values -> 64-byte block (bytes)."""
+def _layout(group):
+    # outlier record: log2(group) position bits, then the 8-bit FP8 value
+    pos_bits = {128: 7, 64: 6}[group]
+    return pos_bits, pos_bits + 8
+
+
+def encode_group(x, centroids, code_len, t, group=128):
+    """x: group (128, or 64 for the activation format) float16 values -> 64-byte block (bytes)."""
+    pos_bits, rec_bits = _layout(group)
     t = F32(t)
     inv_t = F32(F32(1.0) / t)
     xs = [F32(v) for v in np.asarray(x, dtype=np.float16)]
     # the scale element: first index of the largest magnitude
     istar = 0
-    for j in range(1, 128):
+    for j in range(1, group):
         if abs(xs[j]) > abs(xs[istar]):
             istar = j
     s8 = _f8(F32(xs[istar] * inv_t))
     S = F32(_f8val(s8) * t)
     a = F32(abs(S))
-    rest = [xs[j] for j in range(128) if j != istar]
+    rest = [xs[j] for j in range(group) if j != istar]
     gmin, gmax = min(rest), max(rest)
     # pattern: smallest min/max squared error, first on ties
     best_p, best_f = None, None
@@ -54,7 +61,7 @@ def encode_group(x, centroids, code_len, t):
     mids = [F32(F32(F32(centroids[pp][i]) + F32(centroids[pp][i + 1])) * F32(0.5))
             for i in range(14)]
     syms = []
-    for j in range(128):
+    for j in range(group):
         if j == istar:
             syms.append(15)
             continue
@@ -90,13 +97,13 @@ def encode_group(x, centroids, code_len, t):
         bits[16 + i] = ch
     if not clipped:
         free = 512 - 16 - len(stream)
-        n = min(16, free // 15)
-        cand = sorted((j for j in range(128) if j != istar), key=lambda j: (-abs(xs[j]), j))
+        n = min(16, free // rec_bits)
+        cand = sorted((j for j in range(group) if j != istar), key=lambda j: (-abs(xs[j]), j))
         for r in range(n):
             j = cand[r]
-            rec = j | (_f8(F32(xs[j] * inv_t)) << 7)
-            lo = 512 - 15 * (r + 1)
-            for i in range(15):
+            rec = j | (_f8(F32(xs[j] * inv_t)) << pos_bits)
+            lo = 512 - rec_bits * (r + 1)
+            for i in range(rec_bits):
                 bits[lo + i] = str((rec >> i) & 1)
     out = bytearray(64)
     for i in range(512):
@@ -105,8 +112,9 @@ def encode_group(x, centroids, code_len, t):
     return bytes(out)
 
 
-def decode_block(block, centroids, code_len, t):
-    """64-byte block -> 128 float16 values (numpy array)."""
+def decode_block(block, centroids, code_len, t, group=128):
+    """64-byte block -> group float16 values (numpy array)."""
+    pos_bits, rec_bits = _layout(group)
     t = F32(t)
     block = bytes(bytearray(block))
     bits = "".join(str((block[i >> 3] >> (i & 7)) & 1) for i in range(512))
@@ -117,10 +125,10 @@ def decode_block(block, centroids, code_len, t):
     a = F32(abs(S))
     lens = [int(v) for v in code_len[pp][hh]]
     words = {format(c, "0%db" % l): s for s, (c, l) in enumerate(zip(canonical_codes(lens), lens))}
-    out = [np.float16(0.0)] * 128
+    out = [np.float16(0.0)] * group
     pos = 16
     k = 0
-    while k < 128:
+    while k < group:
         hit = None
         for ln in range(2, 9):
             if pos + ln <= 512 and bits[pos:pos + ln] in words and lens[words[bits[pos:pos + ln]]] == ln:
@@ -132,10 +140,10 @@ def decode_block(block, centroids, code_len, t):
         out[k] = _h(S) if s == 15 else _h(F32(F32(centroids[pp][s]) * a))
         pos += ln
         k += 1
-    if k == 128:
-        n = min(16, (512 - pos) // 15)
+    if k == group:
+        n = min(16, (512 - pos) // rec_bits)
         for r in range(n):
-            lo = 512 - 15 * (r + 1)
-            rec = sum(int(bits[lo + i]) << i for i in range(15))
-            out[rec & 127] = _h(F32(_f8val(rec >> 7) * t))
+            lo = 512 - rec_bits * (r + 1)
+            rec = sum(int(bits[lo + i]) << i for i in range(rec_bits))
+            out[rec & (group - 1)] = _h(F32(_f8val(rec >> pos_bits) * t))
     return np.array(out, dtype=np.float16)

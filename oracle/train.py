@@ -30,9 +30,9 @@ from .huffman import limited_lengths
 from .kmeans import kmeans_1d_exact, lloyd
 
 
-def normalised_groups(x, t):
-    """x [G,128] float16 -> [G,127] float64 values divided by the group scale a.
-    Groups with a == 0 are dropped."""
+def normalised_groups(x, t, group=GROUP):
+    """x [G, group] float16 -> [G, group - 1] float64 values divided by the
+    group scale a.  Groups with a == 0 are dropped."""
     x32 = x.astype(np.float32)
     G = x32.shape[0]
     rows = np.arange(G)
@@ -43,7 +43,7 @@ def normalised_groups(x, t):
     keep = a > 0
     mask = np.ones_like(x32, dtype=bool)
     mask[rows, istar] = False
-    others = x32[mask].reshape(G, GROUP - 1).astype(np.float64)
+    others = x32[mask].reshape(G, group - 1).astype(np.float64)
     return others[keep] / a[keep, None]
 
 
@@ -73,7 +73,8 @@ def learn_codebooks(counts, n_codebooks=4, iters=10):
     return lengths.astype(np.uint8)
 
 
-def train_tables(sample_fp16, n_patterns=64, n_codebooks=4, kmeans_iters=25, huff_iters=10, seed=0, distinct=None):
+def train_tables(sample_fp16, n_patterns=64, n_codebooks=4, kmeans_iters=25, huff_iters=10, seed=0, distinct=None,
+                 group=GROUP):
     """Learn Tables from an FP16 sample whose size is a multiple of 128.
 
     distinct (default: n_patterns) patterns are learned and slot p of the
@@ -84,10 +85,10 @@ def train_tables(sample_fp16, n_patterns=64, n_codebooks=4, kmeans_iters=25, huf
     D = n_patterns if distinct is None else int(distinct)
     if D < 1 or D > n_patterns:
         raise ValueError("distinct must be in 1..n_patterns")
-    x = np.asarray(sample_fp16, dtype=np.float16).reshape(-1, GROUP)
+    x = np.asarray(sample_fp16, dtype=np.float16).reshape(-1, group)
     amax = float(np.max(np.abs(x.astype(np.float32)))) if x.size else 0.0
     t, _ = tensor_scale(amax)
-    y = normalised_groups(x, t)
+    y = normalised_groups(x, t, group)
     if y.shape[0] == 0:
         cent = np.tile(np.linspace(-1, 1, N_CENTROIDS), (n_patterns, 1))
     else:
@@ -100,9 +101,9 @@ def train_tables(sample_fp16, n_patterns=64, n_codebooks=4, kmeans_iters=25, huf
     cent = np.clip(np.sort(cent.astype(np.float16).astype(np.float32), axis=1), -1.0, 1.0)
     cent = cent.astype(np.float16).astype(np.float32)
     flat = Tables(cent, np.full((n_patterns, n_codebooks, 16), 4, dtype=np.uint8))
-    _, info = encode_groups(x, flat, t, return_info=True)
+    _, info = encode_groups(x, flat, t, return_info=True, group=group)
     counts = np.zeros((x.shape[0], 16), dtype=np.int64)
-    np.add.at(counts, (np.repeat(np.arange(x.shape[0]), GROUP), info["sym"].ravel()), 1)
+    np.add.at(counts, (np.repeat(np.arange(x.shape[0]), group), info["sym"].ravel()), 1)
     code_len = np.zeros((n_patterns, n_codebooks, 16), dtype=np.uint8)
     for p in range(n_patterns):
         code_len[p] = learn_codebooks(counts[info["p"] == p], n_codebooks, huff_iters)

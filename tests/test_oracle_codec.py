@@ -389,7 +389,7 @@ MUTATIONS = [
     ("longest codebook", "h = np.argmin(Lh, axis=1)", "h = np.argmax(Lh, axis=1)"),
     ("unsigned scale", "s8 = fp.fp8_encode((xs * inv_t)", "s8 = fp.fp8_encode((np.abs(xs) * inv_t)"),
     ("smallest outliers", "key = np.where(others, -ax,", "key = np.where(others, ax,"),
-    ("one record too many", "free // RECORD_BITS", "free // RECORD_BITS + 1"),
+    ("one record too many", "free // rec_bits", "free // rec_bits + 1"),
     ("codeword bits reversed", "bit = (cw >> np.maximum(ln - 1 - b, 0)) & 1", "bit = (cw >> b) & 1"),
 ]
 
