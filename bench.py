@@ -1,6 +1,6 @@
 """Benchmark of the Ecco block codec on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload layer|kv|model|ffn|attn|copy] [--gpus 1]
+    python bench.py [--steps K] [--warmup W] [--workload layer|kv|model|ffn|attn|act|copy] [--gpus 1]
 
 Default workload ("layer"): one LLaMA-3-8B-shaped decoder layer in FP16 --
 q, o [4096, 4096], k, v [1024, 4096], gate, up [14336, 4096], down
@@ -29,6 +29,8 @@ Other workloads (run separately, same JSON line shape):
   attn   decode-phase attention over the compressed K and V caches
          [16, 8, 8192, 128] with 4 query heads per kv head: the fused
          ecco_attention_decode against decode followed by torch's SDPA
+  act    the 2x activation format (groups of 64) on LLaMA-3-8B hidden
+         states [16384, 4096]: amax, encode and decode
   copy   a plain 1 GiB device-to-device copy (the achievable-bandwidth
          reference, and the known-size kernel that calibrates the HBM
          traffic counters FETCH_SIZE / WRITE_SIZE)
@@ -57,7 +59,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="layer", choices=["layer", "kv", "model", "ffn", "attn", "copy"])
+    ap.add_argument("--workload", default="layer", choices=["layer", "kv", "model", "ffn", "attn", "act", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-groups", type=int, default=65536)
     return ap.parse_args()

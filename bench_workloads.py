@@ -1,4 +1,4 @@
-"""Secondary workloads of bench.py (see its docstring): kv, model, ffn."""
+"""Secondary workloads of bench.py (see its docstring): kv, model, ffn, attn, act, copy."""
 
 import os
 import time
@@ -235,6 +235,61 @@ def bench_attn(args, torch, ecco, W):
                  compressed_bytes=comp)
 
 
+def bench_act(args, torch, ecco, W):
+    """2x activation format on LLaMA-3-8B hidden states [16384, 4096] (1,048,576
+    groups of 64): per-tensor scale from the tensor's own amax, encode, decode.
+    A step is amax + encode + decode; each is also timed on its own."""
+    T, D = W.ACT_SHAPE
+    G = T * D // W.ACT_GROUP
+    blob = ecco.ecco_train_patterns(W.act_sample(), threads=min(16, os.cpu_count() or 1), group=W.ACT_GROUP)
+    tdev = ecco.tables_to_device(blob)
+    x = W.act_tensor().cuda()
+    amax = torch.zeros(1, dtype=torch.float32, device="cuda")
+    ecco.ecco_amax(x, x.numel(), amax)
+    torch.cuda.synchronize()
+    t = ecco.ecco_tensor_scale_from_amax(amax.item())
+    blocks = torch.empty((G, 64), dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(x)
+    stats = torch.zeros(7, dtype=torch.int64, device="cuda")
+    ecco.ecco_encode_act(x, 1, G, G * 64, G, tdev, t, blocks, stats)
+    torch.cuda.synchronize()
+    st = dict(zip(ecco.STATS_FIELDS, stats.cpu().tolist()))
+
+    def do_amax():
+        ecco.ecco_amax(x, x.numel(), amax)
+
+    def encode():
+        ecco.ecco_encode_act(x, 1, G, G * 64, G, tdev, t, blocks)
+
+    def decode():
+        ecco.ecco_decode_act(blocks, 1, G, G, G * 64, tdev, t, y)
+
+    def step():
+        # the scale of this step's tensor is the one computed on the host once:
+        # the amax pass is timed as the work it is, without a host round trip
+        do_amax()
+        encode()
+        decode()
+
+    t_step = _timed(torch, step, args.steps, args.warmup)
+    t_amax = _timed(torch, do_amax, args.steps, args.warmup)
+    t_enc = _timed(torch, encode, args.steps, args.warmup)
+    t_dec = _timed(torch, decode, args.steps, args.warmup)
+    bpg = 64 + 2 * W.ACT_GROUP                              # compressed block + fp16 group
+    dec = G * bpg / np.mean(t_dec) / 1e9
+    enc = G * bpg / np.mean(t_enc) / 1e9
+    xf = x.float()
+    err = float(torch.sqrt(((y.float() - xf) ** 2).mean() / (xf ** 2).mean()))
+    return _line("activation decode GB/s (compressed in + fp16 out), 1 GPU", dec, "GB/s", args,
+                 np.mean(t_step) * 1e3,
+                 {"workload": "2x activation format, LLaMA-3-8B hidden states [16384, 4096] fp16 "
+                              "(groups of 64): amax + encode + decode per step", "groups": G},
+                 decode_frac_of_hbm_peak=round(dec / HBM_PEAK_GBPS, 4), decode_us=round(np.mean(t_dec) * 1e6, 2),
+                 encode_GBps=round(enc, 1), encode_us=round(np.mean(t_enc) * 1e6, 2),
+                 amax_us=round(np.mean(t_amax) * 1e6, 2), relative_rms_error=round(err, 5),
+                 clipped_groups=st["clipped_groups"], mean_outliers_per_group=round(st["padded_outliers"] / G, 3))
+
+
 def bench_copy(args, torch, ecco, W):
     nbytes = 1 << 30
     a = torch.ones(nbytes // 2, dtype=torch.float16, device="cuda")
@@ -248,4 +303,4 @@ def bench_copy(args, torch, ecco, W):
 
 def run_workload(args, torch, ecco, W):
     return {"kv": bench_kv, "model": bench_model, "ffn": bench_ffn, "attn": bench_attn,
-            "copy": bench_copy}[args.workload](args, torch, ecco, W)
+            "act": bench_act, "copy": bench_copy}[args.workload](args, torch, ecco, W)

@@ -19,7 +19,7 @@ __all__ = [
     "EccoError", "lib", "library_path",
     "ecco_tables_size", "ecco_tables_build", "ecco_tables_validate", "ecco_tables_get",
     "ecco_train_patterns", "ecco_tensor_scale_from_amax", "ecco_amax", "ecco_encode",
-    "ecco_decode", "ecco_decode_many", "ecco_decode_gemv", "ecco_attention_workspace_size",
+    "ecco_decode", "ecco_encode_act", "ecco_decode_act", "ecco_decode_many", "ecco_decode_gemv", "ecco_attention_workspace_size",
     "ecco_attention_decode", "ecco_strerror", "ecco_version",
     "STATS_FIELDS", "DECODE_MAX_JOBS", "tables_to_device",
 ]
@@ -45,7 +45,7 @@ class EccoError(RuntimeError):
 class TrainOpts(ctypes.Structure):
     _fields_ = [("kmeans_iters", ctypes.c_uint32), ("huff_iters", ctypes.c_uint32),
                 ("seed", ctypes.c_uint64), ("max_groups", ctypes.c_uint32), ("threads", ctypes.c_uint32),
-                ("n_patterns", ctypes.c_uint32)]
+                ("n_patterns", ctypes.c_uint32), ("group", ctypes.c_uint32)]
 
 
 DECODE_MAX_JOBS = 16
@@ -80,6 +80,8 @@ def lib():
             "ecco_amax": (i32, [vp, u64, vp, vp]),
             "ecco_encode": (i32, [vp, u64, u64, u64, u64, vp, f32, vp, vp, vp]),
             "ecco_decode": (i32, [vp, u64, u64, u64, u64, vp, f32, vp, vp]),
+            "ecco_encode_act": (i32, [vp, u64, u64, u64, u64, vp, f32, vp, vp, vp]),
+            "ecco_decode_act": (i32, [vp, u64, u64, u64, u64, vp, f32, vp, vp]),
             "ecco_decode_many": (i32, [vp, ctypes.c_uint32, vp]),
             "ecco_decode_gemv": (i32, [vp, vp, f32, i64, i64, vp, i64, vp, vp]),
             "ecco_attention_workspace_size": (ctypes.c_size_t, [u64, u64, u64, u64]),
@@ -153,13 +155,13 @@ def ecco_tables_get(blob):
 
 
 def ecco_train_patterns(sample_fp16, kmeans_iters=25, huff_iters=10, seed=0, max_groups=0, threads=0,
-                        n_patterns=0):
+                        n_patterns=0, group=0):
     """Learn a host blob from an FP16 sample (NumPy float16/uint16 or CPU torch tensor);
     n_patterns distinct patterns (16, 32 or 64; 0 = 64) repeated over the 64 slots."""
     if hasattr(sample_fp16, "numpy"):
         sample_fp16 = sample_fp16.contiguous().numpy()
     s = np.ascontiguousarray(sample_fp16).view(np.uint16).ravel()
-    opts = TrainOpts(kmeans_iters, huff_iters, seed, max_groups, threads, n_patterns)
+    opts = TrainOpts(kmeans_iters, huff_iters, seed, max_groups, threads, n_patterns, group)
     blob = _aligned_host(ecco_tables_size())
     _check(lib().ecco_train_patterns(_ptr(s), s.size, ctypes.byref(opts), _ptr(blob)), "ecco_train_patterns")
     return blob
@@ -202,6 +204,22 @@ def ecco_decode(blocks, n_rows, groups_per_row, blk_row_stride_blocks, y_row_str
     _check(lib().ecco_decode(_ptr(blocks), int(n_rows), int(groups_per_row), int(blk_row_stride_blocks),
                              int(y_row_stride_elems), _ptr(tables_dev), float(tensor_scale), _ptr(y),
                              _stream(stream)), "ecco_decode")
+
+
+def ecco_encode_act(x, n_rows, groups_per_row, x_row_stride_elems, blk_row_stride_blocks, tables_dev,
+                    tensor_scale, blocks, stats=None, stream=None):
+    """ecco_encode for the 2x activation format (groups of 64 values)."""
+    _check(lib().ecco_encode_act(_ptr(x), int(n_rows), int(groups_per_row), int(x_row_stride_elems),
+                                 int(blk_row_stride_blocks), _ptr(tables_dev), float(tensor_scale), _ptr(blocks),
+                                 _ptr(stats), _stream(stream)), "ecco_encode_act")
+
+
+def ecco_decode_act(blocks, n_rows, groups_per_row, blk_row_stride_blocks, y_row_stride_elems, tables_dev,
+                    tensor_scale, y, stream=None):
+    """ecco_decode for the 2x activation format (groups of 64 values)."""
+    _check(lib().ecco_decode_act(_ptr(blocks), int(n_rows), int(groups_per_row), int(blk_row_stride_blocks),
+                                 int(y_row_stride_elems), _ptr(tables_dev), float(tensor_scale), _ptr(y),
+                                 _stream(stream)), "ecco_decode_act")
 
 
 def ecco_decode_many(jobs, stream=None):

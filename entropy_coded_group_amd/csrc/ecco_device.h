@@ -186,6 +186,11 @@ __device__ __forceinline__ uint4 load_stream(const void* p) {
   const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
   return make_uint4(w.x, w.y, w.z, w.w);
 }
+__device__ __forceinline__ uint2 load_stream8(const void* p) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 w = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+  return make_uint2(w.x, w.y);
+}
 
 // 64-bit window shift: bits [r, r + 32) of hi:lo, r < 64.
 __device__ __forceinline__ uint32_t window(uint32_t lo, uint32_t hi, uint32_t r) {
@@ -214,7 +219,8 @@ __device__ __forceinline__ uint32_t div_magic(uint32_t n, DivMagic q) {
 // LDS for the whole workgroup; each wave has a private staging area:
 //   blk   64 x 17 dwords: the batch's blocks; after a lane has decoded its
 //         block, the block's 32-entry FP16 value table overwrites its words
-//   qsym  16 x 36 dwords: the 128 symbol bytes of 16 blocks at a time
+//   qsym  16 x 36 dwords: the symbol bytes of 16 blocks at a time (128 per
+//         block, or 64 in a row of 20 dwords for 64-value groups)
 
 constexpr int kDecWaves = 12;                    // decode kernel: waves per workgroup (one workgroup per CU)
 constexpr int kGemvWaves = 12;                   // fused decode+GEMV: waves per workgroup
@@ -225,7 +231,22 @@ constexpr int kSymStride = 36;                   // dwords per staged symbol row
                                                  // row writes of several lanes off a single group of banks
 constexpr int kPassBlocks = 16;                  // blocks whose symbols are staged at a time
 constexpr int kPasses = 64 / kPassBlocks;
-constexpr int kPassIters = kPassBlocks / 4;      // the transposed step handles 4 blocks per instruction
+
+// Geometry of a group size: 128 values (weights, KV cache: 15-bit outlier
+// records with a 7-bit position) or 64 (activations: 14-bit records, 6-bit
+// position).  Eight values per lane in the transposed step, so a block's
+// output row takes GS / 8 lanes.
+template <int GS>
+struct GroupGeom {
+  static_assert(GS == 128 || GS == 64, "group of 128 or 64 values");
+  static constexpr uint32_t kPosBits = GS == 128 ? 7 : 6;
+  static constexpr uint32_t kRecBits = kPosBits + 8;
+  static constexpr int kChunks = GS / 4;                     // 4-codeword refill steps per block
+  static constexpr int kSymStride = GS == 128 ? 36 : 20;     // dwords per staged symbol row (GS bytes + 16 pad bytes + pad)
+  static constexpr int kLanesPerBlock = GS / 8;
+  static constexpr int kBlocksPerIter = 64 / kLanesPerBlock;
+  static constexpr int kPassIters = kPassBlocks / kBlocksPerIter;
+};
 
 template <int NW>
 struct DecodeSmem {
@@ -270,8 +291,8 @@ __device__ __forceinline__ BatchRegs fetch_batch(uint32_t lane, uint32_t n_valid
   return r;
 }
 
-// Decode one staged batch (FULL: all 64 blocks exist, so no store is
-// predicated).
+// Decode one staged batch of GS-value blocks (FULL: all 64 blocks exist, so
+// no store is predicated).
 //   sink(b, j0, v, k)         8 decoded FP16 values of block b at positions
 //                             j0 .. j0 + 7 (v.x holds values j0, j0 + 1, ...)
 // Steps: stage the batch in LDS; each lane decodes one block's codeword
@@ -281,11 +302,16 @@ __device__ __forceinline__ BatchRegs fetch_batch(uint32_t lane, uint32_t n_valid
 // block); then, 16 blocks at a time, stages the symbol bytes -- each as the
 // byte offset of its value-table entry, outlier positions overwritten by that
 // of entry 16 + r -- and hands 8 values per lane to the sink,
-// sixteen lanes per block and four blocks per instruction, so every store
-// instruction writes four whole 256-byte rows.
-template <bool FULL, int NW, class Sink>
+// GS / 8 lanes per block, so every store instruction writes whole rows (four
+// of 256 bytes, or eight of 128).
+template <bool FULL, int NW, int GS = 128, class Sink>
 __device__ __forceinline__ void decode_batch(DecodeSmem<NW>& sm, uint32_t wave, uint32_t lane, uint32_t n_valid,
                                              float t, const BatchRegs& in, Sink sink) {
+  using Geo = GroupGeom<GS>;
+  constexpr uint32_t RB = Geo::kRecBits;
+  constexpr int SST = Geo::kSymStride;
+  constexpr int LPB = Geo::kLanesPerBlock;
+  constexpr int BPI = Geo::kBlocksPerIter;
   uint32_t* blk = sm.blk[wave];
   uint32_t* qs = sm.qsym[wave];
 #pragma unroll
@@ -304,9 +330,9 @@ __device__ __forceinline__ void decode_batch(DecodeSmem<NW>& sm, uint32_t wave, 
   const uint32_t head = lo;
   uint32_t lutb = ((head & 63u) * 4u + ((head >> 6) & 3u)) * 256u;   // lut[p][h]
   uint32_t r = 16, kw = 2, lim = 512;
-  uint32_t E[32];
+  uint32_t E[Geo::kChunks];
 #pragma unroll
-  for (int c = 0; c < 32; ++c) {
+  for (int c = 0; c < Geo::kChunks; ++c) {
     const uint32_t nxt = W[kw];
     const uint32_t base = (kw - 2u) * 32u;
     uint32_t x = window(lo, hi, r);
@@ -340,7 +366,7 @@ __device__ __forceinline__ void decode_batch(DecodeSmem<NW>& sm, uint32_t wave, 
   }
   const bool full = lim == 512u;
   const uint32_t end = (kw - 2u) * 32u + r;
-  const uint32_t n = full ? min(16u, (512u - end) / 15u) : 0u;
+  const uint32_t n = full ? min(16u, (512u - end) / RB) : 0u;
 
   // 2. value table: [0..14] fp16(c * a), [15] fp16(S), [16 + r] outlier r (or +0 if clipped)
   const uint32_t p = head & 63u;
@@ -362,20 +388,20 @@ __device__ __forceinline__ void decode_batch(DecodeSmem<NW>& sm, uint32_t wave, 
 #pragma unroll
   for (int i = 0; i < 9; ++i) tail[i] = W[8 + i];
   // jp: byte r of jp[r / 4] is the symbol-row byte that slot r patches: the
-  // record's position, or a pad byte past the row's 128 symbols if r >= n
+  // record's position, or a pad byte past the row's GS symbols if r >= n
   uint32_t jp[4] = {0, 0, 0, 0};
 #pragma unroll
   for (int i = 8; i < 16; ++i) vtab[i] = 0;
 #pragma unroll
   for (int rr = 0; rr < 16; ++rr) {
     if ((rr & 3) == 0 && !__any((uint32_t)rr < n)) break;
-    const uint32_t pos = 512u - 15u * (rr + 1);
+    const uint32_t pos = 512u - RB * (rr + 1);
     const uint32_t wi = (pos >> 5) - 8u, sh = pos & 31u;
-    const uint32_t rec = window(tail[wi], tail[wi + 1], sh) & 0x7fffu;
-    const uint32_t hv = f16_bits(fp8_decode<0>(rec >> 7) * t);
+    const uint32_t rec = window(tail[wi], tail[wi + 1], sh) & ((1u << RB) - 1u);
+    const uint32_t hv = f16_bits(fp8_decode<0>(rec >> Geo::kPosBits) * t);
     const bool use = (uint32_t)rr < n;
     vtab[8 + rr / 2] |= (use ? hv : 0u) << (16 * (rr & 1));
-    jp[rr / 4] |= (use ? (rec & 127u) : 128u + (uint32_t)rr) << (8 * (rr & 3));
+    jp[rr / 4] |= (use ? (rec & (GS - 1u)) : GS + (uint32_t)rr) << (8 * (rr & 3));
   }
   // the block's words are consumed: its value table takes their place
 #pragma unroll
@@ -385,9 +411,10 @@ __device__ __forceinline__ void decode_batch(DecodeSmem<NW>& sm, uint32_t wave, 
 #pragma unroll
   for (int k = 0; k < kPasses; ++k) {
     if (lane / kPassBlocks == (uint32_t)k) {
-      uint32_t* Q = qs + (lane % kPassBlocks) * kSymStride;
+      uint32_t* Q = qs + (lane % kPassBlocks) * SST;
 #pragma unroll
-      for (int i = 0; i < 32; i += 4) *reinterpret_cast<uint4*>(Q + i) = make_uint4(E[i], E[i + 1], E[i + 2], E[i + 3]);
+      for (int i = 0; i < Geo::kChunks; i += 4)
+        *reinterpret_cast<uint4*>(Q + i) = make_uint4(E[i], E[i + 1], E[i + 2], E[i + 3]);
       // outlier positions take value-table entry 16 + r, in record order so
       // that a later record wins a repeated position
       uint8_t* Qb = reinterpret_cast<uint8_t*>(Q);
@@ -398,14 +425,14 @@ __device__ __forceinline__ void decode_batch(DecodeSmem<NW>& sm, uint32_t wave, 
       }
     }
     wave_sync();
-    uint2 sv[kPassIters];
+    uint2 sv[Geo::kPassIters];
 #pragma unroll
-    for (int it = 0; it < kPassIters; ++it)
-      sv[it] = *reinterpret_cast<const uint2*>(qs + (it * 4u + (lane >> 4)) * kSymStride + 2u * (lane & 15u));
-    uint4 o[kPassIters];
+    for (int it = 0; it < Geo::kPassIters; ++it)
+      sv[it] = *reinterpret_cast<const uint2*>(qs + (it * BPI + lane / LPB) * SST + 2u * (lane % LPB));
+    uint4 o[Geo::kPassIters];
 #pragma unroll
-    for (int it = 0; it < kPassIters; ++it) {
-      const uint32_t bl = kPassBlocks * k + it * 4u + (lane >> 4);
+    for (int it = 0; it < Geo::kPassIters; ++it) {
+      const uint32_t bl = kPassBlocks * k + it * BPI + lane / LPB;
       const uint8_t* tb = reinterpret_cast<const uint8_t*>(blk + bl * kBlkStride);
       // each staged byte is already the entry's byte offset (< 64)
       typedef _Float16 h2 __attribute__((ext_vector_type(2)));
@@ -426,9 +453,9 @@ __device__ __forceinline__ void decode_batch(DecodeSmem<NW>& sm, uint32_t wave, 
     }
     wave_sync();
 #pragma unroll
-    for (int it = 0; it < kPassIters; ++it) {
-      const uint32_t bl = kPassBlocks * k + it * 4u + (lane >> 4);
-      if (FULL || bl < n_valid) sink(bl, 8u * (lane & 15u), o[it], (uint32_t)k);
+    for (int it = 0; it < Geo::kPassIters; ++it) {
+      const uint32_t bl = kPassBlocks * k + it * BPI + lane / LPB;
+      if (FULL || bl < n_valid) sink(bl, 8u * (lane % LPB), o[it], (uint32_t)k);
     }
   }
 }

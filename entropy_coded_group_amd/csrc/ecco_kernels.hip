@@ -62,8 +62,8 @@ struct DecodeArgs {
 };
 
 // Decode of workgroup lw's share of one job: a contiguous range of the
-// job's batches, interleaved over the waves.
-template <bool CONTIG>
+// job's batches, interleaved over the waves.  GS values per group.
+template <int GS, bool CONTIG>
 __device__ __forceinline__ void decode_job(DecodeSmem<kDecWaves>& sm, const DecodeJob& a, uint32_t lw) {
   const uint32_t lane = lane_id(), wave = threadIdx.x >> 6;
   const uint32_t b_end = (uint32_t)((uint64_t)a.n_batches * (lw + 1) / a.wg_count);
@@ -93,24 +93,25 @@ __device__ __forceinline__ void decode_job(DecodeSmem<kDecWaves>& sm, const Deco
       const uint32_t gidx = g0 + b;
       uint64_t yoff;
       if (CONTIG) {
-        yoff = (uint64_t)gidx * 128u;
+        yoff = (uint64_t)gidx * GS;
       } else {
         const uint32_t r = div_magic(gidx, a.gpr), g = gidx - r * a.gpr.d;
-        yoff = (uint64_t)r * a.y_stride + (uint64_t)g * 128u;
+        yoff = (uint64_t)r * a.y_stride + (uint64_t)g * GS;
       }
       store_stream(a.y + yoff + j0, v);
     };
     const uint32_t n_valid = min(64u, a.n_groups - g0);
     if (n_valid == 64u)
-      decode_batch<true>(sm, wave, lane, 64u, a.t, cur, sink);
+      decode_batch<true, kDecWaves, GS>(sm, wave, lane, 64u, a.t, cur, sink);
     else
-      decode_batch<false>(sm, wave, lane, n_valid, a.t, cur, sink);
+      decode_batch<false, kDecWaves, GS>(sm, wave, lane, n_valid, a.t, cur, sink);
     cur = nxt;
   }
 }
 
 // Each workgroup decodes one tensor, so the look-up tables it stages in LDS
 // serve every block it sees.
+template <int GS>
 __global__ __launch_bounds__(kDecWaves * 64) void decode_kernel(DecodeArgs args) {
   __shared__ DecodeSmem<kDecWaves> sm;
   uint32_t j = 0;
@@ -120,9 +121,9 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_kernel(DecodeArgs args)
   __syncthreads();
   const uint32_t lw = blockIdx.x - a.wg_first;
   if (a.contiguous)
-    decode_job<true>(sm, a, lw);
+    decode_job<GS, true>(sm, a, lw);
   else
-    decode_job<false>(sm, a, lw);
+    decode_job<GS, false>(sm, a, lw);
 }
 
 // -------------------------------------------------------------------- encode
@@ -151,7 +152,12 @@ struct EncodeSmem {
   uint32_t out[kEncWaves][4][16];
 };
 
+// GS values per group: lane t16 of a group's row holds NV = GS / 16 of them.
+template <int GS>
 __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(EncodeArgs a) {
+  using Geo = GroupGeom<GS>;
+  constexpr int NV = GS / 16;
+  constexpr uint32_t RB = Geo::kRecBits;
   __shared__ EncodeSmem sm;
   const uint32_t tid = threadIdx.x;
   for (uint32_t i = tid; i < S * 16; i += blockDim.x) sm.mid[i] = (&a.tab->midpoints[0][0])[i];
@@ -172,11 +178,17 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(EncodeArgs a) {
   // per-lane statistics (kept by lane t16 == 0 of each group)
   uint64_t st_groups = 0, st_clip = 0, st_clipv = 0, st_pad = 0, st_fill = 0, st_nonfin = 0;
 
-  // the 16 bytes of group g (clamped to the last group) that lane t16 holds
+  // the NV values of group g (clamped to the last group) that lane t16 holds
   auto load_group = [&](uint32_t g) -> uint4 {
     g = min(g, a.n_groups - 1u);
     const uint32_t row = div_magic(g, a.gpr), col = g - row * a.gpr.d;
-    return load_stream(a.x + (uint64_t)row * a.x_stride + (uint64_t)col * 128u + 8u * t16);
+    const uint16_t* src = a.x + (uint64_t)row * a.x_stride + (uint64_t)col * GS + NV * t16;
+    if constexpr (NV == 8) {
+      return load_stream(src);
+    } else {
+      const uint2 v = load_stream8(src);
+      return make_uint4(v.x, v.y, 0u, 0u);
+    }
   };
   const uint32_t qstride = gridDim.x * kEncWaves;
   uint32_t quad = blockIdx.x * kEncWaves + wave;
@@ -191,37 +203,40 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(EncodeArgs a) {
       row = div_magic(gidx, a.gpr);
       col = gidx - row * a.gpr.d;
     }
-    uint32_t hb[8] = {raw.x & 0xffffu, raw.x >> 16, raw.y & 0xffffu, raw.y >> 16,
-                      raw.z & 0xffffu, raw.z >> 16, raw.w & 0xffffu, raw.w >> 16};
-    float xf[8];
-    uint32_t key[8];
+    const uint32_t hb[8] = {raw.x & 0xffffu, raw.x >> 16, raw.y & 0xffffu, raw.y >> 16,
+                            raw.z & 0xffffu, raw.z >> 16, raw.w & 0xffffu, raw.w >> 16};
+    float xf[NV];
+    uint32_t key[NV];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < NV; ++i) {
       xf[i] = f16_value(hb[i]);
-      const uint32_t j = 8u * t16 + i;
+      const uint32_t j = NV * t16 + i;
       key[i] = ((hb[i] & 0x7fffu) << 8) | ((127u - j) << 1) | (hb[i] >> 15);
     }
     // 1. scale element: largest |x|, lowest index on ties
     uint32_t km = key[0];
 #pragma unroll
-    for (int i = 1; i < 8; ++i) km = max(km, key[i]);
+    for (int i = 1; i < NV; ++i) km = max(km, key[i]);
     km = row_max_u32(km);
-    const uint32_t jstar = 127u - ((km >> 1) & 127u);
     const float xs = f16_value((km >> 8) | ((km & 1u) << 15));
     const uint32_t s8 = fp8_encode(xs * inv_t);
     const float S = fp8_decode<0>(s8) * t;
     const float aa = fabsf(S);
-    // 2. min / max of the other 127 values (the scale element, whose key is
-    //    km, counts as +inf for the min and -inf for the max)
-    float lo[8], hi[8];
+    // 2. min / max of the other GS - 1 values (the scale element, whose key
+    //    is km, counts as +inf for the min and -inf for the max)
+    float lo[NV], hi[NV];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < NV; ++i) {
       const bool s = key[i] == km;
       lo[i] = s ? __builtin_inff() : xf[i];
       hi[i] = s ? -__builtin_inff() : xf[i];
     }
-    float mn = fminf(fminf(fminf(lo[0], lo[1]), fminf(lo[2], lo[3])), fminf(fminf(lo[4], lo[5]), fminf(lo[6], lo[7])));
-    float mx = fmaxf(fmaxf(fmaxf(hi[0], hi[1]), fmaxf(hi[2], hi[3])), fmaxf(fmaxf(hi[4], hi[5]), fmaxf(hi[6], hi[7])));
+    float mn = fminf(fminf(lo[0], lo[1]), fminf(lo[2], lo[3]));
+    float mx = fmaxf(fmaxf(hi[0], hi[1]), fmaxf(hi[2], hi[3]));
+    if constexpr (NV == 8) {
+      mn = fminf(mn, fminf(fminf(lo[4], lo[5]), fminf(lo[6], lo[7])));
+      mx = fmaxf(mx, fmaxf(fmaxf(hi[4], hi[5]), fmaxf(hi[6], hi[7])));
+    }
     mn = row_min_f32(mn);
     mx = row_max_f32(mx);
     // 3. pattern: min/max squared error, lowest p on ties.  Each lane keeps its
@@ -252,10 +267,10 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(EncodeArgs a) {
     if (t16 < 15u) thr[enode] = t16 < 14u ? sm.mid[pstar * 16u + t16] * aa : __builtin_inff();
     wave_sync();
     const float root = thr[1];
-    uint32_t sym[8];
+    uint32_t sym[NV];
     uint32_t l4 = 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < NV; ++i) {
       uint32_t u = xf[i] > root ? 3u : 2u;
       u = u + u + (xf[i] > thr[u] ? 1u : 0u);
       u = u + u + (xf[i] > thr[u] ? 1u : 0u);
@@ -276,7 +291,7 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(EncodeArgs a) {
     uint32_t ends = 0;                     // codewords of this lane ending within the block (stats)
     const uint32_t eb = (pstar * 4u + hstar) * 16u;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < NV; ++i) {
       const uint32_t e = sm.enc[eb + sym[i]];
       acc |= (uint64_t)(e & 0xffu) << off;
       off += e >> 8;
@@ -296,7 +311,7 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(EncodeArgs a) {
       if (w + 2u < 16u && top) atomicOr(&out[w + 2u], top);
     }
     const bool clipped = 16u + L > 512u;
-    const uint32_t n = clipped ? 0u : min(16u, (496u - L) / 15u);
+    const uint32_t n = clipped ? 0u : min(16u, (496u - L) / RB);
     // 7. outliers: n largest |x| (j != i*), lower j first on ties.  Keys are
     //    unique and the scale element holds the row's largest (km), so the
     //    outliers are the next n keys: after removing km, each round takes
@@ -305,24 +320,25 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(EncodeArgs a) {
     uint32_t mykey = 0;
     if (__any(n > 0u)) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) key[i] = key[i] == km ? 0u : key[i];
+      for (int i = 0; i < NV; ++i) key[i] = key[i] == km ? 0u : key[i];
       for (uint32_t rr = 0;; ++rr) {
-        uint32_t m = max(max(max(key[0], key[1]), max(key[2], key[3])), max(max(key[4], key[5]), max(key[6], key[7])));
+        uint32_t m = max(max(key[0], key[1]), max(key[2], key[3]));
+        if constexpr (NV == 8) m = max(m, max(max(key[4], key[5]), max(key[6], key[7])));
         m = row_max_u32(m);
         mykey = t16 == rr ? m : mykey;
         if (!__any(rr + 1u < n)) break;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) key[i] = key[i] == m ? 0u : key[i];
+        for (int i = 0; i < NV; ++i) key[i] = key[i] == m ? 0u : key[i];
       }
     }
     if (t16 < n) {
       const uint32_t j = 127u - ((mykey >> 1) & 127u);
       const float xv = f16_value((mykey >> 8) | ((mykey & 1u) << 15));
-      const uint32_t myrec = j | (fp8_encode(xv * inv_t) << 7);
-      const uint32_t rp = 497u - 15u * t16;
+      const uint32_t myrec = j | (fp8_encode(xv * inv_t) << Geo::kPosBits);
+      const uint32_t rp = 512u - RB * (t16 + 1u);
       const uint32_t w = rp >> 5, sh = rp & 31u;
       atomicOr(&out[w], myrec << sh);
-      if (sh > 17u) atomicOr(&out[w + 1u], myrec >> (32u - sh));
+      if (sh + RB > 32u) atomicOr(&out[w + 1u], myrec >> (32u - sh));
     }
     if (t16 == 0) atomicOr(&out[0], pstar | (hstar << 6) | (s8 << 8));
     wave_sync();
@@ -334,21 +350,21 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(EncodeArgs a) {
       // whole codewords inside the block (k of a clipped group)
       uint32_t e = pos;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < NV; ++i) {
         e += sm.enc[eb + sym[i]] >> 8;
         ends += e <= 512u ? 1u : 0u;
       }
       const uint32_t k = row_add_u32(ends);
       bool nonfin = false;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) nonfin |= (hb[i] & 0x7c00u) == 0x7c00u;
+      for (int i = 0; i < NV; ++i) nonfin |= (hb[i] & 0x7c00u) == 0x7c00u;
       const uint32_t nf = row_max_u32(nonfin ? 1u : 0u);
       if (valid && t16 == 0) {
         st_groups += 1;
         st_clip += clipped;
-        st_clipv += 128u - k;
+        st_clipv += GS - k;
         st_pad += n;
-        st_fill += clipped ? 0u : (496u - L - 15u * n);
+        st_fill += clipped ? 0u : (496u - L - RB * n);
         st_nonfin += nf;
       }
     }
@@ -360,7 +376,7 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(EncodeArgs a) {
     atomicAdd(&a.stats->clipped_groups, (unsigned long long)st_clip);
     atomicAdd(&a.stats->clipped_values, (unsigned long long)st_clipv);
     atomicAdd(&a.stats->padded_outliers, (unsigned long long)st_pad);
-    atomicAdd(&a.stats->pad_bits, (unsigned long long)(15u * st_pad));
+    atomicAdd(&a.stats->pad_bits, (unsigned long long)(RB * st_pad));
     atomicAdd(&a.stats->fill_bits, (unsigned long long)st_fill);
     atomicAdd(&a.stats->nonfinite_groups, (unsigned long long)st_nonfin);
   }
@@ -470,14 +486,16 @@ extern "C" int ecco_amax(const uint16_t* x, uint64_t n, float* amax, void* strea
   return launch_status();
 }
 
-extern "C" int ecco_encode(const uint16_t* x, uint64_t n_rows, uint64_t gpr, uint64_t x_stride,
-                           uint64_t blk_stride, const void* tables, float tensor_scale, void* blocks,
-                           ecco_stats_t* stats, void* stream) {
+namespace {
+
+template <int GS>
+int encode_impl(const uint16_t* x, uint64_t n_rows, uint64_t gpr, uint64_t x_stride, uint64_t blk_stride,
+                const void* tables, float tensor_scale, void* blocks, ecco_stats_t* stats, void* stream) {
   if (!x || !tables || !blocks) return ECCO_EINVAL;
   if (!(tensor_scale > 0.0f) || !(tensor_scale < __builtin_huge_valf())) return ECCO_EINVAL;
   const uint64_t total = n_rows * gpr;
   if (n_rows == 0 || gpr == 0 || total >= (1ull << 32) || gpr >= (1ull << 32)) return ECCO_ESIZE;
-  if (n_rows > 1 && (x_stride < gpr * 128 || blk_stride < gpr)) return ECCO_ESIZE;
+  if (n_rows > 1 && (x_stride < gpr * GS || blk_stride < gpr)) return ECCO_ESIZE;
   if (!host_aligned(x, 16) || (x_stride % 8) != 0 || !host_aligned(blocks, 64) || !host_aligned(tables, 256) ||
       (stats && !host_aligned(stats, 8)))
     return ECCO_EALIGN;
@@ -499,21 +517,35 @@ extern "C" int ecco_encode(const uint16_t* x, uint64_t n_rows, uint64_t gpr, uin
   uint32_t want = (a.n_quads + kEncWaves - 1) / kEncWaves;
   uint32_t grid = std::max<uint32_t>(1, std::min<uint32_t>(want, (uint32_t)cus * 8));
   (void)hipGetLastError();
-  hipLaunchKernelGGL(encode_kernel, dim3(grid), dim3(kEncWaves * 64), 0, static_cast<hipStream_t>(stream), a);
+  hipLaunchKernelGGL(encode_kernel<GS>, dim3(grid), dim3(kEncWaves * 64), 0, static_cast<hipStream_t>(stream), a);
   return launch_status();
+}
+
+}  // namespace
+
+extern "C" int ecco_encode(const uint16_t* x, uint64_t n_rows, uint64_t gpr, uint64_t x_stride,
+                           uint64_t blk_stride, const void* tables, float tensor_scale, void* blocks,
+                           ecco_stats_t* stats, void* stream) {
+  return encode_impl<128>(x, n_rows, gpr, x_stride, blk_stride, tables, tensor_scale, blocks, stats, stream);
+}
+
+extern "C" int ecco_encode_act(const uint16_t* x, uint64_t n_rows, uint64_t gpr, uint64_t x_stride,
+                               uint64_t blk_stride, const void* tables, float tensor_scale, void* blocks,
+                               ecco_stats_t* stats, void* stream) {
+  return encode_impl<64>(x, n_rows, gpr, x_stride, blk_stride, tables, tensor_scale, blocks, stats, stream);
 }
 
 namespace {
 
-// Checks one decode job and fills its kernel descriptor (all but the
-// workgroup range).
+// Checks one decode job of GS-value groups and fills its kernel descriptor
+// (all but the workgroup range).
 int make_decode_job(const void* blocks, uint64_t n_rows, uint64_t gpr, uint64_t blk_stride, uint64_t y_stride,
-                    const void* tables, float tensor_scale, uint16_t* y, DecodeJob* out) {
+                    const void* tables, float tensor_scale, uint16_t* y, DecodeJob* out, uint32_t GS = 128) {
   if (!blocks || !tables || !y) return ECCO_EINVAL;
   if (!(tensor_scale > 0.0f) || !(tensor_scale < __builtin_huge_valf())) return ECCO_EINVAL;
   const uint64_t total = n_rows * gpr;
   if (n_rows == 0 || gpr == 0 || total >= (1ull << 32) || gpr >= (1ull << 32)) return ECCO_ESIZE;
-  if (n_rows > 1 && (y_stride < gpr * 128 || blk_stride < gpr)) return ECCO_ESIZE;
+  if (n_rows > 1 && (y_stride < gpr * GS || blk_stride < gpr)) return ECCO_ESIZE;
   if (!host_aligned(y, 16) || (y_stride % 8) != 0 || !host_aligned(blocks, 64) || !host_aligned(tables, 256)) return ECCO_EALIGN;
   DecodeJob& a = *out;
   a.blocks = static_cast<const uint8_t*>(blocks);
@@ -525,7 +557,7 @@ int make_decode_job(const void* blocks, uint64_t n_rows, uint64_t gpr, uint64_t 
   a.n_groups = (uint32_t)total;
   a.n_batches = (uint32_t)((total + 63) / 64);
   a.t = tensor_scale;
-  a.contiguous = (n_rows == 1 || (blk_stride == gpr && y_stride == gpr * 128)) ? 1u : 0u;
+  a.contiguous = (n_rows == 1 || (blk_stride == gpr && y_stride == gpr * GS)) ? 1u : 0u;
   a.wg_first = a.wg_count = 0;
   return ECCO_OK;
 }
@@ -557,6 +589,7 @@ void assign_workgroups(DecodeArgs& args, uint32_t cus) {
   }
 }
 
+template <int GS>
 int launch_decode(DecodeArgs& args, void* stream) {
   int cus = 0, rc = check_gfx950(&cus);
   if (rc) return rc;
@@ -564,7 +597,7 @@ int launch_decode(DecodeArgs& args, void* stream) {
   const DecodeJob& last = args.job[args.n_jobs - 1];
   const uint32_t grid = last.wg_first + last.wg_count;
   (void)hipGetLastError();
-  hipLaunchKernelGGL(decode_kernel, dim3(grid), dim3(kDecWaves * 64), 0, static_cast<hipStream_t>(stream), args);
+  hipLaunchKernelGGL(decode_kernel<GS>, dim3(grid), dim3(kDecWaves * 64), 0, static_cast<hipStream_t>(stream), args);
   return launch_status();
 }
 
@@ -577,7 +610,17 @@ extern "C" int ecco_decode(const void* blocks, uint64_t n_rows, uint64_t gpr, ui
   args.n_jobs = 1;
   int rc = make_decode_job(blocks, n_rows, gpr, blk_stride, y_stride, tables, tensor_scale, y, &args.job[0]);
   if (rc) return rc;
-  return launch_decode(args, stream);
+  return launch_decode<128>(args, stream);
+}
+
+extern "C" int ecco_decode_act(const void* blocks, uint64_t n_rows, uint64_t gpr, uint64_t blk_stride,
+                               uint64_t y_stride, const void* tables, float tensor_scale, uint16_t* y, void* stream) {
+  DecodeArgs args;
+  std::memset(&args, 0, sizeof(args));
+  args.n_jobs = 1;
+  int rc = make_decode_job(blocks, n_rows, gpr, blk_stride, y_stride, tables, tensor_scale, y, &args.job[0], 64);
+  if (rc) return rc;
+  return launch_decode<64>(args, stream);
 }
 
 extern "C" int ecco_decode_many(const ecco_decode_job_t* jobs, uint32_t n_jobs, void* stream) {
@@ -593,5 +636,5 @@ extern "C" int ecco_decode_many(const ecco_decode_job_t* jobs, uint32_t n_jobs, 
                              q.y_row_stride_elems, q.tables_dev, q.tensor_scale, q.y_dev, &args.job[j]);
     if (rc) return rc;
   }
-  return launch_decode(args, stream);
+  return launch_decode<128>(args, stream);
 }

@@ -198,34 +198,37 @@ using namespace ecco;
 extern "C" int ecco_train_patterns(const uint16_t* sample, uint64_t n_values, const ecco_train_opts_t* opts,
                                    void* tables_host) {
   if (!sample || !tables_host) return ECCO_EINVAL;
-  if (n_values == 0 || n_values % G != 0) return ECCO_ESIZE;
-  ecco_train_opts_t o = {25, 10, 0, 0, 0, 0};
+  ecco_train_opts_t o = {25, 10, 0, 0, 0, 0, 0};
   if (opts) o = *opts;
+  if (o.group == 0) o.group = G;
+  if (o.group != 64 && o.group != (uint32_t)G) return ECCO_EINVAL;
+  const int gs = int(o.group);                 // values per group: 128, or 64 for the activation format
+  if (n_values == 0 || n_values % gs != 0) return ECCO_ESIZE;
   if (o.n_patterns == 0) o.n_patterns = S;
   if (o.n_patterns != 16 && o.n_patterns != 32 && o.n_patterns != (uint32_t)S) return ECCO_EINVAL;
   const int D = int(o.n_patterns);
   if (o.kmeans_iters == 0) o.kmeans_iters = 25;
   if (o.huff_iters == 0) o.huff_iters = 10;
   unsigned threads = o.threads ? o.threads : std::max(1u, std::thread::hardware_concurrency());
-  size_t ng = n_values / G;
+  size_t ng = n_values / gs;
   if (o.max_groups && ng > o.max_groups) ng = o.max_groups;
 
   // 1. per-tensor scale and group normalisation
   float amax = 0;
-  for (size_t i = 0; i < ng * G; ++i) {
+  for (size_t i = 0; i < ng * gs; ++i) {
     float v = std::fabs(half_to_float(sample[i]));
     if (v > amax) amax = v;
   }
   float t = ecco_tensor_scale_from_amax(amax);
   volatile float inv_t_v = 1.0f / t;
   float inv_t = inv_t_v;
-  std::vector<float> xs(ng * G), a(ng);
+  std::vector<float> xs(ng * gs), a(ng);
   std::vector<int> istar(ng);
   for (size_t g = 0; g < ng; ++g) {
-    float* x = &xs[g * G];
+    float* x = &xs[g * gs];
     int is = 0;
-    for (int j = 0; j < G; ++j) {
-      x[j] = half_to_float(sample[g * G + j]);
+    for (int j = 0; j < gs; ++j) {
+      x[j] = half_to_float(sample[g * gs + j]);
       if (std::fabs(x[j]) > std::fabs(x[is])) is = j;
     }
     istar[g] = is;
@@ -242,10 +245,10 @@ extern "C" int ecco_train_patterns(const uint16_t* sample, uint64_t n_values, co
   parallel_for(used.size(), threads, [&](size_t u) {
     thread_local std::vector<double> work;
     size_t g = used[u];
-    double v[G - 1];
+    double v[G];
     int n = 0;
-    for (int j = 0; j < G; ++j)
-      if (j != istar[g]) v[n++] = double(xs[g * G + j]) / double(a[g]);
+    for (int j = 0; j < gs; ++j)
+      if (j != istar[g]) v[n++] = double(xs[g * gs + j]) / double(a[g]);
     std::sort(v, v + n);
     kmeans_1d(v, n, C, &vec[u * C], work);
   });
@@ -330,10 +333,10 @@ extern "C" int ecco_train_patterns(const uint16_t* sample, uint64_t n_values, co
       mid[p * 14 + k] = s * 0.5f;
     }
   parallel_for(ng, threads, [&](size_t g) {
-    const float* x = &xs[g * G];
+    const float* x = &xs[g * gs];
     float aa = a[g];
     float gmin = std::numeric_limits<float>::infinity(), gmax = -gmin;
-    for (int j = 0; j < G; ++j)
+    for (int j = 0; j < gs; ++j)
       if (j != istar[g]) { gmin = std::min(gmin, x[j]); gmax = std::max(gmax, x[j]); }
     int bp = 0;
     float bf = std::numeric_limits<float>::infinity();
@@ -345,7 +348,7 @@ extern "C" int ecco_train_patterns(const uint16_t* sample, uint64_t n_values, co
       if (f < bf || p == 0) { bf = f; bp = p; }
     }
     pat[g] = bp;
-    for (int j = 0; j < G; ++j) {
+    for (int j = 0; j < gs; ++j) {
       int s = 15;
       if (j != istar[g]) {
         s = 0;
@@ -372,7 +375,7 @@ extern "C" int ecco_train_patterns(const uint16_t* sample, uint64_t n_values, co
       const uint64_t* c = &counts[mem[i] * A];
       double e = 0;
       for (int s = 0; s < A; ++s)
-        if (c[s]) { double q = c[s] / double(G); e -= q * std::log2(q); }
+        if (c[s]) { double q = c[s] / double(gs); e -= q * std::log2(q); }
       ent[i] = e;
     }
     std::vector<size_t> order(M);

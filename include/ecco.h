@@ -56,6 +56,19 @@
  * r = 0..n-1: value[j_r] = fp16(f32(v8_r) * t).  Any 512 bits decode.
  *
  * ------------------------------------------------------------------------
+ * ACTIVATION FORMAT (64 bytes per group of 64 values, about 8 bits/value)
+ * ------------------------------------------------------------------------
+ * The 2x format for activations: groups of 64 values ("free parameters":
+ * activation group size 64 for a 2x target) coded by the same steps
+ * and the same kind of table blob (the low-ratio compressor reuses the
+ * high-ratio one's hardware, Fig. 9 caption).  Everything above holds with
+ * 128 replaced by 64, except the records: 14 bits each, bits 0..5 = position
+ * j, bits 6..13 = FP8 value; bits 512-14(r+1) .. 512-14r-1 hold record r and
+ * n = min(16, floor((512 - E) / 14)).  Symmetric like the 4x format: the
+ * "zero points" that one figure caption mentions are not defined on the
+ * pages and are not stored.
+ *
+ * ------------------------------------------------------------------------
  * CONVENTIONS
  * ------------------------------------------------------------------------
  * - "_dev" pointers are HIP device memory owned by the caller; "_host"
@@ -105,9 +118,9 @@ enum {
 typedef struct {
   unsigned long long groups;           /* groups encoded                                */
   unsigned long long clipped_groups;   /* groups with 16 + L > 512                      */
-  unsigned long long clipped_values;   /* sum over groups of 128 - k                    */
+  unsigned long long clipped_values;   /* sum over groups of 128 - k (64 - k)           */
   unsigned long long padded_outliers;  /* sum of n                                      */
-  unsigned long long pad_bits;         /* sum of 15 n                                   */
+  unsigned long long pad_bits;         /* sum of 15 n (14 n in the activation format)   */
   unsigned long long fill_bits;        /* zero bits between stream end and records      */
   unsigned long long nonfinite_groups; /* groups holding Inf/NaN (their blocks are unspecified) */
 } ecco_stats_t;
@@ -124,6 +137,9 @@ typedef struct {
                              pattern p mod n_patterns), so blocks keep the
                              6-bit pattern field and the encoder searches only
                              the distinct ones                                  */
+  uint32_t group;         /* values per group of the sample: 128 (weights, KV
+                             cache) or 64 (the 2x activation format of
+                             ecco_encode_act); 0 = 128 (0)                       */
 } ecco_train_opts_t;
 
 /* ---- tables --------------------------------------------------------------
@@ -189,6 +205,19 @@ int ecco_encode(const uint16_t* x_dev, uint64_t n_rows, uint64_t groups_per_row,
 int ecco_decode(const void* blocks_dev, uint64_t n_rows, uint64_t groups_per_row,
                 uint64_t blk_row_stride_blocks, uint64_t y_row_stride_elems,
                 const void* tables_dev, float tensor_scale, uint16_t* y_dev, void* stream);
+
+/* Activation format: encode / decode groups of 64 values.  Arguments, layout
+ * (with 128 replaced by 64: group (r, g) is the 64 FP16 values at
+ * x_dev + r * x_row_stride_elems + g * 64), size rules, statistics and errors
+ * as for ecco_encode / ecco_decode.  The tables should come from
+ * ecco_train_patterns with group = 64; any valid blob is accepted. */
+int ecco_encode_act(const uint16_t* x_dev, uint64_t n_rows, uint64_t groups_per_row,
+                    uint64_t x_row_stride_elems, uint64_t blk_row_stride_blocks,
+                    const void* tables_dev, float tensor_scale, void* blocks_dev,
+                    ecco_stats_t* stats_dev, void* stream);
+int ecco_decode_act(const void* blocks_dev, uint64_t n_rows, uint64_t groups_per_row,
+                    uint64_t blk_row_stride_blocks, uint64_t y_row_stride_elems,
+                    const void* tables_dev, float tensor_scale, uint16_t* y_dev, void* stream);
 
 /* One tensor of an ecco_decode_many call: the arguments of ecco_decode. */
 typedef struct {

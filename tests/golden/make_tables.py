@@ -13,6 +13,9 @@ sample with the tensor's own recipe):
                 per-tensor scale t is fixed from the sample (online codec) and
                 stored as c3_<kind>_t
   c5_w1, c5_w2  70B-shaped FFN matrices
+  act           LLaMA-3-8B hidden states in the 2x activation format (groups
+                of 64; a 256-token sample); activations take their per-tensor
+                scale from each tensor's own amax
 """
 
 import os
@@ -36,6 +39,7 @@ def samples():
         yield "c3_" + kind, W.kv_sample(kind)
     for nm in ("w1", "w2"):
         yield "c5_" + nm, W.c5_sample(nm)
+    yield "act", W.act_sample()
 
 
 def main(out=os.path.join(HERE, "tables.npz"), only=None):
@@ -47,7 +51,8 @@ def main(out=os.path.join(HERE, "tables.npz"), only=None):
             continue
         t0 = time.time()
         x = s.numpy().reshape(-1)
-        tab = oracle.train.train_tables(x, seed=0)
+        group = W.ACT_GROUP if name == "act" else W.GROUP
+        tab = oracle.train.train_tables(x, seed=0, group=group)
         tab.check()
         arrays[name + "_centroids"] = tab.centroids
         arrays[name + "_code_len"] = tab.code_len

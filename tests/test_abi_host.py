@@ -128,6 +128,16 @@ def test_device_entry_points_check_arguments_before_touching_the_device():
     assert L.ecco_decode_gemv(A, A, 1.0, 16, 100, A, 1, A, None) == -3          # in % 128
     assert L.ecco_decode_gemv(A, A, 1.0, 16, 128, A, 9, A, None) == -3          # batch > 8
     assert L.ecco_amax(A, 0, A, None) == -3
+    # activation format: the same checks with 64-value groups
+    assert L.ecco_encode_act(None, 1, 1, 64, 1, A, 1.0, A, None, None) == -1
+    assert L.ecco_encode_act(A, 1, 1, 64, 1, A, float("nan"), A, None, None) == -1
+    assert L.ecco_encode_act(A, 0, 1, 64, 1, A, 1.0, A, None, None) == -3
+    assert L.ecco_encode_act(A, 2, 4, 200, 4, A, 1.0, A, None, None) == -3       # row stride < 4 * 64
+    assert L.ecco_encode_act(A, 1, 1, 64, 1, A + 128, 1.0, A, None, None) == -2  # tables 256-aligned
+    assert L.ecco_decode_act(A, 1, 1, 1, 64, A, 1.0, None, None) == -1
+    assert L.ecco_decode_act(A, 2, 4, 4, 260, A, 1.0, A, None) == -2             # stride % 8
+    assert L.ecco_decode_act(A, 2, 4, 4, 240, A, 1.0, A, None) == -3             # stride < 4 * 64
+    assert L.ecco_decode_act(A, 2, 4, 3, 256, A, 1.0, A, None) == -3
     # ecco_decode_many: count, reserved field, and every job checked before launch
     jobs = (ecco.DecodeJob * 3)()
     for j in jobs:
@@ -202,6 +212,30 @@ def test_library_trainer_sixteen_patterns():
     assert np.array_equal(c, c[np.arange(64) % 16])
     with pytest.raises(ecco.EccoError):
         ecco.ecco_train_patterns(sample, kmeans_iters=2, huff_iters=2, threads=2, n_patterns=8)
+
+
+def test_library_trainer_activation_groups():
+    """group=64 trains on 64-value groups: valid tables, within the oracle's
+    quality on the 2x activation format; other group sizes are rejected."""
+    sample = W.act_sample(n_tokens=64).numpy()
+    blob = ecco.ecco_train_patterns(sample, kmeans_iters=10, huff_iters=5, threads=4, group=64)
+    assert ecco.ecco_tables_validate(blob) == 0
+    c, l = ecco.ecco_tables_get(blob)
+    lib_tabs = codec.Tables(c, l)
+    lib_tabs.check()
+    ora_tabs = oracle.train.train_tables(sample, kmeans_iters=10, huff_iters=5, group=64)
+    x = W.act_tensor((16, 4096), seed=620).numpy().reshape(-1, 64)
+    t, _ = codec.tensor_scale(float(np.max(np.abs(x.astype(np.float32)))))
+    mse = []
+    for tb in (lib_tabs, ora_tabs):
+        y = codec.decode_blocks(codec.encode_groups(x, tb, t, group=64), tb, t, group=64)
+        mse.append(oracle.metrics.reconstruction(x, y)["mse"])
+    assert mse[0] <= 1.25 * mse[1], mse
+    for bad in (32, 96, 256):
+        with pytest.raises(ecco.EccoError):
+            ecco.ecco_train_patterns(sample, kmeans_iters=2, huff_iters=2, threads=2, group=bad)
+    with pytest.raises(ecco.EccoError):                     # not a whole number of groups
+        ecco.ecco_train_patterns(sample.ravel()[:100], kmeans_iters=2, huff_iters=2, threads=2, group=64)
 
 
 def test_attention_checks_arguments_before_touching_the_device():

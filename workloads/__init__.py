@@ -38,6 +38,11 @@ FFN70B = {"w1": (28672, 8192), "w2": (8192, 28672)}
 KV_SHAPE = (16, 8, 8192, 128)
 KV_APPEND = 256
 
+# Activations (2x format, groups of 64): LLaMA-3-8B hidden states
+# [tokens, hidden] of one 16k-token prefill
+ACT_SHAPE = (16384, 4096)
+ACT_GROUP = 64
+
 
 def _gen(seed):
     g = torch.Generator(device="cpu")
@@ -126,6 +131,26 @@ def kv_sample(kind, n_vectors=8192):
     B, H, S, D = KV_SHAPE
     s = max(1, n_vectors // H)
     return kv_tensor(kind, shape=(1, H, s, D), seed=seed)
+
+
+def act_tensor(shape=ACT_SHAPE, seed=600, n_outlier_ch=6, boost=30.0):
+    """Hidden states [tokens, hidden]: Laplace(0, 1) values times a per-token
+    scale exp(N(0, 0.25)), with n_outlier_ch fixed channels (the same for every
+    token) scaled by `boost` -- the few very large activation channels of
+    LLM hidden states."""
+    g = _gen(seed)
+    T, D = shape
+    x = _laplace(T * D, 1.0, g).reshape(T, D)
+    x *= torch.exp(0.5 * torch.randn(T, 1, generator=g, dtype=torch.float32))
+    ch = torch.randperm(D, generator=_gen(610))[:n_outlier_ch]
+    x[:, ch] *= boost
+    return x.to(torch.float16)
+
+
+def act_sample(n_tokens=256):
+    """Calibration sample for the activation codec: n_tokens hidden-state rows
+    of the same recipe (seed 601), with the same outlier channels."""
+    return act_tensor(shape=(n_tokens, ACT_SHAPE[1]), seed=601)
 
 
 def c5_matrix(name):
