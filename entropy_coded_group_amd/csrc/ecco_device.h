@@ -134,6 +134,50 @@ __device__ __forceinline__ float wave_max_f32(float v) {
   return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
+// All-reduce over aligned segments of LPG = 16 lanes (a DPP row) or 8 lanes
+// (half a row: the quad swaps and the half-row mirror stay inside it).
+template <int LPG>
+__device__ __forceinline__ uint32_t seg_max_u32(uint32_t v) {
+  static_assert(LPG == 8 || LPG == 16, "segment of 8 or 16 lanes");
+  v = max(v, dpp_u32<kQuadXor1>(v));
+  v = max(v, dpp_u32<kQuadXor2>(v));
+  v = max(v, dpp_u32<kRowHalfMirror>(v));
+  if constexpr (LPG == 16) v = max(v, dpp_u32<kRowMirror>(v));
+  return v;
+}
+template <int LPG>
+__device__ __forceinline__ uint32_t seg_min_u32(uint32_t v) {
+  v = min(v, dpp_u32<kQuadXor1>(v));
+  v = min(v, dpp_u32<kQuadXor2>(v));
+  v = min(v, dpp_u32<kRowHalfMirror>(v));
+  if constexpr (LPG == 16) v = min(v, dpp_u32<kRowMirror>(v));
+  return v;
+}
+template <int LPG>
+__device__ __forceinline__ uint32_t seg_add_u32(uint32_t v) {
+  v += dpp_u32<kQuadXor1>(v);
+  v += dpp_u32<kQuadXor2>(v);
+  v += dpp_u32<kRowHalfMirror>(v);
+  if constexpr (LPG == 16) v += dpp_u32<kRowMirror>(v);
+  return v;
+}
+template <int LPG>
+__device__ __forceinline__ float seg_min_f32(float v) {
+  v = fminf(v, dpp_f32<kQuadXor1>(v));
+  v = fminf(v, dpp_f32<kQuadXor2>(v));
+  v = fminf(v, dpp_f32<kRowHalfMirror>(v));
+  if constexpr (LPG == 16) v = fminf(v, dpp_f32<kRowMirror>(v));
+  return v;
+}
+template <int LPG>
+__device__ __forceinline__ float seg_max_f32(float v) {
+  v = fmaxf(v, dpp_f32<kQuadXor1>(v));
+  v = fmaxf(v, dpp_f32<kQuadXor2>(v));
+  v = fmaxf(v, dpp_f32<kRowHalfMirror>(v));
+  if constexpr (LPG == 16) v = fmaxf(v, dpp_f32<kRowMirror>(v));
+  return v;
+}
+
 // Inclusive prefix sum over the 16 lanes of a row (Hillis-Steele).
 __device__ __forceinline__ uint32_t row_scan_add(uint32_t v) {
   v += dpp_u32<kRowShr1>(v);
@@ -141,6 +185,22 @@ __device__ __forceinline__ uint32_t row_scan_add(uint32_t v) {
   v += dpp_u32<kRowShr4>(v);
   v += dpp_u32<kRowShr8>(v);
   return v;
+}
+// The same over aligned segments of LPG lanes; tl = lane index in the segment
+// (a shifted-in value from the previous segment is dropped).
+template <int LPG>
+__device__ __forceinline__ uint32_t seg_scan_add(uint32_t v, uint32_t tl) {
+  if constexpr (LPG == 16) {
+    return row_scan_add(v);
+  } else {
+    uint32_t u = dpp_u32<kRowShr1>(v);
+    v += tl >= 1u ? u : 0u;
+    u = dpp_u32<kRowShr2>(v);
+    v += tl >= 2u ? u : 0u;
+    u = dpp_u32<kRowShr4>(v);
+    v += tl >= 4u ? u : 0u;
+    return v;
+  }
 }
 
 // OCP FP8 E4M3FN encode of a non-NaN float: saturate to +-448, round to
@@ -185,11 +245,6 @@ __device__ __forceinline__ void store_stream(void* p, uint4 v) {
 __device__ __forceinline__ uint4 load_stream(const void* p) {
   const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
   return make_uint4(w.x, w.y, w.z, w.w);
-}
-__device__ __forceinline__ uint2 load_stream8(const void* p) {
-  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-  const u32x2 w = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
-  return make_uint2(w.x, w.y);
 }
 
 // 64-bit window shift: bits [r, r + 32) of hi:lo, r < 64.

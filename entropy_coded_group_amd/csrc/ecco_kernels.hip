@@ -137,7 +137,7 @@ struct EncodeArgs {
   uint64_t blk_stride;   // blocks per row
   DivMagic gpr;
   uint32_t n_groups;
-  uint32_t n_quads;      // groups / 4, rounded up
+  uint32_t n_units;      // groups / (groups per wave), rounded up
   float t, inv_t;
 };
 
@@ -148,16 +148,21 @@ struct EncodeSmem {
   float c0c14[S * 2];
   uint32_t len4[S * A];
   uint16_t enc[S * H * A];
-  float thr[kEncWaves][4][16];
-  uint32_t out[kEncWaves][4][16];
+  float thr[kEncWaves][8][16];
+  uint32_t out[kEncWaves][8][16];
 };
 
-// GS values per group: lane t16 of a group's row holds NV = GS / 16 of them.
+// Eight values per lane: a group of GS values takes LPG = GS / 8 lanes (a DPP
+// row for 128, half a row for 64) and a wave encodes GPW = 64 / LPG groups at
+// a time.
 template <int GS>
 __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(EncodeArgs a) {
   using Geo = GroupGeom<GS>;
-  constexpr int NV = GS / 16;
+  constexpr int NV = 8;
+  constexpr int LPG = GS / NV;
+  constexpr int GPW = 64 / LPG;
   constexpr uint32_t RB = Geo::kRecBits;
+  constexpr int NSLOT = 16 / LPG;           // outlier records (and thresholds) per lane
   __shared__ EncodeSmem sm;
   const uint32_t tid = threadIdx.x;
   for (uint32_t i = tid; i < S * 16; i += blockDim.x) sm.mid[i] = (&a.tab->midpoints[0][0])[i];
@@ -167,37 +172,31 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(EncodeArgs a) {
   __syncthreads();
 
   const uint32_t lane = lane_id(), wave = tid >> 6;
-  const uint32_t q = lane >> 4, t16 = lane & 15u;
+  const uint32_t q = lane / LPG, tl = lane % LPG;
   const float t = a.t, inv_t = a.inv_t;
-  const int n_search16 = (int)(a.tab->n_search / 16u);
+  const int n_search_lane = (int)(a.tab->n_search / LPG);
   float* thr = sm.thr[wave][q];
-  // tree node of threshold t16 (t16 < 15): with v = t16 + 1 = odd * 2^z, the
-  // node sits on level 3 - z at index 2^(3 - z) + (v >> (z + 1))
-  const uint32_t enode = (8u >> __builtin_ctz(t16 + 1u)) + ((t16 + 1u) >> (__builtin_ctz(t16 + 1u) + 1u));
+  // tree node of threshold k (k < 15): with v = k + 1 = odd * 2^z, the node
+  // sits on level 3 - z at index 2^(3 - z) + (v >> (z + 1))
+  auto enode = [](uint32_t k) { return (8u >> __builtin_ctz(k + 1u)) + ((k + 1u) >> (__builtin_ctz(k + 1u) + 1u)); };
   uint32_t* out = sm.out[wave][q];
-  // per-lane statistics (kept by lane t16 == 0 of each group)
+  // per-lane statistics (kept by lane tl == 0 of each group)
   uint64_t st_groups = 0, st_clip = 0, st_clipv = 0, st_pad = 0, st_fill = 0, st_nonfin = 0;
 
-  // the NV values of group g (clamped to the last group) that lane t16 holds
+  // the 8 values of group g (clamped to the last group) that lane tl holds
   auto load_group = [&](uint32_t g) -> uint4 {
     g = min(g, a.n_groups - 1u);
     const uint32_t row = div_magic(g, a.gpr), col = g - row * a.gpr.d;
-    const uint16_t* src = a.x + (uint64_t)row * a.x_stride + (uint64_t)col * GS + NV * t16;
-    if constexpr (NV == 8) {
-      return load_stream(src);
-    } else {
-      const uint2 v = load_stream8(src);
-      return make_uint4(v.x, v.y, 0u, 0u);
-    }
+    return load_stream(a.x + (uint64_t)row * a.x_stride + (uint64_t)col * GS + NV * tl);
   };
-  const uint32_t qstride = gridDim.x * kEncWaves;
-  uint32_t quad = blockIdx.x * kEncWaves + wave;
-  uint4 raw = load_group(quad * 4u + q);
-  for (; quad < a.n_quads; quad += qstride) {
-    const uint32_t gidx = quad * 4u + q;
+  const uint32_t ustride = gridDim.x * kEncWaves;
+  uint32_t unit = blockIdx.x * kEncWaves + wave;
+  uint4 raw = load_group(unit * GPW + q);
+  for (; unit < a.n_units; unit += ustride) {
+    const uint32_t gidx = unit * GPW + q;
     const bool valid = gidx < a.n_groups;
-    // the next quad's input is loaded before this one is worked on
-    const uint4 nraw = load_group((quad + qstride) * 4u + q);
+    // the next unit's input is loaded before this one is worked on
+    const uint4 nraw = load_group((unit + ustride) * GPW + q);
     uint32_t row = 0, col = 0;
     if (valid) {
       row = div_magic(gidx, a.gpr);
@@ -210,14 +209,14 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(EncodeArgs a) {
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       xf[i] = f16_value(hb[i]);
-      const uint32_t j = NV * t16 + i;
+      const uint32_t j = NV * tl + i;
       key[i] = ((hb[i] & 0x7fffu) << 8) | ((127u - j) << 1) | (hb[i] >> 15);
     }
     // 1. scale element: largest |x|, lowest index on ties
     uint32_t km = key[0];
 #pragma unroll
     for (int i = 1; i < NV; ++i) km = max(km, key[i]);
-    km = row_max_u32(km);
+    km = seg_max_u32<LPG>(km);
     const float xs = f16_value((km >> 8) | ((km & 1u) << 15));
     const uint32_t s8 = fp8_encode(xs * inv_t);
     const float S = fp8_decode<0>(s8) * t;
@@ -231,24 +230,20 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(EncodeArgs a) {
       lo[i] = s ? __builtin_inff() : xf[i];
       hi[i] = s ? -__builtin_inff() : xf[i];
     }
-    float mn = fminf(fminf(lo[0], lo[1]), fminf(lo[2], lo[3]));
-    float mx = fmaxf(fmaxf(hi[0], hi[1]), fmaxf(hi[2], hi[3]));
-    if constexpr (NV == 8) {
-      mn = fminf(mn, fminf(fminf(lo[4], lo[5]), fminf(lo[6], lo[7])));
-      mx = fmaxf(mx, fmaxf(fmaxf(hi[4], hi[5]), fmaxf(hi[6], hi[7])));
-    }
-    mn = row_min_f32(mn);
-    mx = row_max_f32(mx);
+    float mn = fminf(fminf(fminf(lo[0], lo[1]), fminf(lo[2], lo[3])), fminf(fminf(lo[4], lo[5]), fminf(lo[6], lo[7])));
+    float mx = fmaxf(fmaxf(fmaxf(hi[0], hi[1]), fmaxf(hi[2], hi[3])), fmaxf(fmaxf(hi[4], hi[5]), fmaxf(hi[6], hi[7])));
+    mn = seg_min_f32<LPG>(mn);
+    mx = seg_max_f32<LPG>(mx);
     // 3. pattern: min/max squared error, lowest p on ties.  Each lane keeps its
-    //    best of 4 (p rising, so a strict < keeps the lowest); the row then
-    //    takes the least fitness (non-negative, so its bits order like it)
-    //    and the least p among the lanes that reach it.
+    //    best of 64 / LPG (p rising, so a strict < keeps the lowest); the
+    //    segment then takes the least fitness (non-negative, so its bits
+    //    order like it) and the least p among the lanes that reach it.
     float bf = __builtin_inff();
-    uint32_t bp = t16;
+    uint32_t bp = tl;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      if (k >= n_search16) break;       // later patterns repeat earlier ones' end centroids
-      const uint32_t p = t16 + 16u * k;
+    for (int k = 0; k < 64 / LPG; ++k) {
+      if (k >= n_search_lane) break;    // later patterns repeat earlier ones' end centroids
+      const uint32_t p = tl + LPG * k;
       const float d1 = mn - sm.c0c14[2 * p] * aa;
       const float d2 = mx - sm.c0c14[2 * p + 1] * aa;
       const float f = d1 * d1 + d2 * d2;
@@ -257,14 +252,18 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(EncodeArgs a) {
         bp = p;
       }
     }
-    const uint32_t fmin = row_min_u32(__float_as_uint(bf));
-    const uint32_t pstar = row_min_u32(__float_as_uint(bf) == fmin ? bp : 63u) & 63u;
+    const uint32_t fmin = seg_min_u32<LPG>(__float_as_uint(bf));
+    const uint32_t pstar = seg_min_u32<LPG>(__float_as_uint(bf) == fmin ? bp : 63u) & 63u;
     // 4. quantise: sym = #{k : x > m_pk * a}.  The 15 thresholds (m_p14 * a
     //    taken as +inf) sit in LDS as an implicit binary tree, node 1 the
-    //    root and node u's children 2u and 2u + 1 (lane k writes threshold k
-    //    to its node, precomputed as enode); four compares walk it, the root
+    //    root and node u's children 2u and 2u + 1 (lane tl writes thresholds
+    //    tl, tl + LPG, ... to their nodes); four compares walk it, the root
     //    one against a register copy.
-    if (t16 < 15u) thr[enode] = t16 < 14u ? sm.mid[pstar * 16u + t16] * aa : __builtin_inff();
+#pragma unroll
+    for (int sl = 0; sl < NSLOT; ++sl) {
+      const uint32_t k = tl + LPG * sl;
+      if (k < 15u) thr[enode(k)] = k < 14u ? sm.mid[pstar * 16u + k] * aa : __builtin_inff();
+    }
     wave_sync();
     const float root = thr[1];
     uint32_t sym[NV];
@@ -279,13 +278,14 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(EncodeArgs a) {
       l4 += sm.len4[pstar * 16u + sym[i]];
     }
     // 5. codebook with the shortest stream, lowest h on ties
-    uint32_t l02 = row_add_u32(l4 & 0x00ff00ffu), l13 = row_add_u32((l4 >> 8) & 0x00ff00ffu);
+    uint32_t l02 = seg_add_u32<LPG>(l4 & 0x00ff00ffu), l13 = seg_add_u32<LPG>((l4 >> 8) & 0x00ff00ffu);
     uint32_t Lh[4] = {l02 & 0xffffu, l13 & 0xffffu, l02 >> 16, l13 >> 16};
     uint32_t hstar = 0, L = Lh[0];
 #pragma unroll
     for (int h = 1; h < 4; ++h)
       if (Lh[h] < L) { L = Lh[h]; hstar = h; }
-    // 6. codewords: lane-local concatenation, row scan for positions, OR into the block
+    // 6. codewords: lane-local concatenation, segment scan for positions, OR
+    //    into the block
     uint64_t acc = 0;
     uint32_t off = 0;
     uint32_t ends = 0;                     // codewords of this lane ending within the block (stats)
@@ -296,8 +296,9 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(EncodeArgs a) {
       acc |= (uint64_t)(e & 0xffu) << off;
       off += e >> 8;
     }
-    out[t16] = 0;
-    const uint32_t incl = row_scan_add(off);
+#pragma unroll
+    for (int sl = 0; sl < NSLOT; ++sl) out[tl + LPG * sl] = 0;
+    const uint32_t incl = seg_scan_add<LPG>(off, tl);
     const uint32_t pos = 16u + incl - off;
     wave_sync();
     {
@@ -313,38 +314,49 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(EncodeArgs a) {
     const bool clipped = 16u + L > 512u;
     const uint32_t n = clipped ? 0u : min(16u, (496u - L) / RB);
     // 7. outliers: n largest |x| (j != i*), lower j first on ties.  Keys are
-    //    unique and the scale element holds the row's largest (km), so the
+    //    unique and the scale element holds the group's largest (km), so the
     //    outliers are the next n keys: after removing km, each round takes
-    //    the row's largest remaining key (lane r keeps round r's) and removes
-    //    it unless no group of the wave needs another round.
-    uint32_t mykey = 0;
+    //    the group's largest remaining key (lane rr % LPG keeps round rr's in
+    //    slot rr / LPG) and removes it unless no group of the wave needs
+    //    another round.
+    uint32_t mykey[NSLOT];
+#pragma unroll
+    for (int sl = 0; sl < NSLOT; ++sl) mykey[sl] = 0;
     if (__any(n > 0u)) {
 #pragma unroll
       for (int i = 0; i < NV; ++i) key[i] = key[i] == km ? 0u : key[i];
       for (uint32_t rr = 0;; ++rr) {
-        uint32_t m = max(max(key[0], key[1]), max(key[2], key[3]));
-        if constexpr (NV == 8) m = max(m, max(max(key[4], key[5]), max(key[6], key[7])));
-        m = row_max_u32(m);
-        mykey = t16 == rr ? m : mykey;
+        uint32_t m = max(max(max(key[0], key[1]), max(key[2], key[3])), max(max(key[4], key[5]), max(key[6], key[7])));
+        m = seg_max_u32<LPG>(m);
+#pragma unroll
+        for (int sl = 0; sl < NSLOT; ++sl) mykey[sl] = rr == tl + LPG * sl ? m : mykey[sl];
         if (!__any(rr + 1u < n)) break;
 #pragma unroll
         for (int i = 0; i < NV; ++i) key[i] = key[i] == m ? 0u : key[i];
       }
     }
-    if (t16 < n) {
-      const uint32_t j = 127u - ((mykey >> 1) & 127u);
-      const float xv = f16_value((mykey >> 8) | ((mykey & 1u) << 15));
-      const uint32_t myrec = j | (fp8_encode(xv * inv_t) << Geo::kPosBits);
-      const uint32_t rp = 512u - RB * (t16 + 1u);
-      const uint32_t w = rp >> 5, sh = rp & 31u;
-      atomicOr(&out[w], myrec << sh);
-      if (sh + RB > 32u) atomicOr(&out[w + 1u], myrec >> (32u - sh));
+#pragma unroll
+    for (int sl = 0; sl < NSLOT; ++sl) {
+      const uint32_t r = tl + LPG * sl;
+      if (r < n) {
+        const uint32_t j = 127u - ((mykey[sl] >> 1) & 127u);
+        const float xv = f16_value((mykey[sl] >> 8) | ((mykey[sl] & 1u) << 15));
+        const uint32_t myrec = j | (fp8_encode(xv * inv_t) << Geo::kPosBits);
+        const uint32_t rp = 512u - RB * (r + 1u);
+        const uint32_t w = rp >> 5, sh = rp & 31u;
+        atomicOr(&out[w], myrec << sh);
+        if (sh + RB > 32u) atomicOr(&out[w + 1u], myrec >> (32u - sh));
+      }
     }
-    if (t16 == 0) atomicOr(&out[0], pstar | (hstar << 6) | (s8 << 8));
+    if (tl == 0) atomicOr(&out[0], pstar | (hstar << 6) | (s8 << 8));
     wave_sync();
     if (valid) {
-      uint32_t* dst = reinterpret_cast<uint32_t*>(a.blocks + ((uint64_t)row * a.blk_stride + col) * 64u);
-      dst[t16] = out[t16];
+      uint8_t* dst = a.blocks + ((uint64_t)row * a.blk_stride + col) * 64u;
+      if constexpr (LPG == 16) {
+        reinterpret_cast<uint32_t*>(dst)[tl] = out[tl];
+      } else {
+        reinterpret_cast<uint2*>(dst)[tl] = make_uint2(out[2u * tl], out[2u * tl + 1u]);
+      }
     }
     if (a.stats) {
       // whole codewords inside the block (k of a clipped group)
@@ -354,12 +366,12 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(EncodeArgs a) {
         e += sm.enc[eb + sym[i]] >> 8;
         ends += e <= 512u ? 1u : 0u;
       }
-      const uint32_t k = row_add_u32(ends);
+      const uint32_t k = seg_add_u32<LPG>(ends);
       bool nonfin = false;
 #pragma unroll
       for (int i = 0; i < NV; ++i) nonfin |= (hb[i] & 0x7c00u) == 0x7c00u;
-      const uint32_t nf = row_max_u32(nonfin ? 1u : 0u);
-      if (valid && t16 == 0) {
+      const uint32_t nf = seg_max_u32<LPG>(nonfin ? 1u : 0u);
+      if (valid && tl == 0) {
         st_groups += 1;
         st_clip += clipped;
         st_clipv += GS - k;
@@ -371,7 +383,7 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(EncodeArgs a) {
     raw = nraw;
     wave_sync();
   }
-  if (a.stats && t16 == 0 && st_groups) {
+  if (a.stats && tl == 0 && st_groups) {
     atomicAdd(&a.stats->groups, (unsigned long long)st_groups);
     atomicAdd(&a.stats->clipped_groups, (unsigned long long)st_clip);
     atomicAdd(&a.stats->clipped_values, (unsigned long long)st_clipv);
@@ -510,11 +522,12 @@ int encode_impl(const uint16_t* x, uint64_t n_rows, uint64_t gpr, uint64_t x_str
   a.blk_stride = blk_stride;
   a.gpr = make_magic((uint32_t)gpr);
   a.n_groups = (uint32_t)total;
-  a.n_quads = (uint32_t)((total + 3) / 4);
+  constexpr uint32_t kGroupsPerWave = 64 / (GS / 8);
+  a.n_units = (uint32_t)((total + kGroupsPerWave - 1) / kGroupsPerWave);
   a.t = tensor_scale;
   volatile float inv = 1.0f / tensor_scale;
   a.inv_t = inv;
-  uint32_t want = (a.n_quads + kEncWaves - 1) / kEncWaves;
+  uint32_t want = (a.n_units + kEncWaves - 1) / kEncWaves;
   uint32_t grid = std::max<uint32_t>(1, std::min<uint32_t>(want, (uint32_t)cus * 8));
   (void)hipGetLastError();
   hipLaunchKernelGGL(encode_kernel<GS>, dim3(grid), dim3(kEncWaves * 64), 0, static_cast<hipStream_t>(stream), a);
