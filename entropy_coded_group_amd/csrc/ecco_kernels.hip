@@ -142,6 +142,22 @@ struct EncodeArgs {
 };
 
 constexpr int kEncWaves = 4;
+constexpr uint32_t kOutlierSortRounds = 3;   // more outlier rounds than this: sort each lane's keys first
+
+// Sorts 8 keys into descending order (an optimal 19-comparator network).
+__device__ __forceinline__ void sort8_desc(uint32_t (&k)[8]) {
+  auto ce = [&](int i, int j) {
+    const uint32_t a = max(k[i], k[j]), b = min(k[i], k[j]);
+    k[i] = a;
+    k[j] = b;
+  };
+  ce(0, 2); ce(1, 3); ce(4, 6); ce(5, 7);
+  ce(0, 4); ce(1, 5); ce(2, 6); ce(3, 7);
+  ce(0, 1); ce(2, 3); ce(4, 5); ce(6, 7);
+  ce(2, 4); ce(3, 5);
+  ce(1, 4); ce(3, 6);
+  ce(1, 2); ce(3, 4); ce(5, 6);
+}
 
 struct EncodeSmem {
   float mid[S * 16];
@@ -317,12 +333,33 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(EncodeArgs a) {
     //    unique and the scale element holds the group's largest (km), so the
     //    outliers are the next n keys: after removing km, each round takes
     //    the group's largest remaining key (lane rr % LPG keeps round rr's in
-    //    slot rr / LPG) and removes it unless no group of the wave needs
-    //    another round.
+    //    slot rr / LPG) and removes it, until no group of the wave needs
+    //    another round.  For a few rounds the lane's keys are searched and
+    //    cleared in place; for more, each lane first sorts its 8 keys
+    //    (descending, 19 compare-exchanges) so that a round only compares the
+    //    lanes' heads and the owner of the largest shifts its list.
     uint32_t mykey[NSLOT];
 #pragma unroll
     for (int sl = 0; sl < NSLOT; ++sl) mykey[sl] = 0;
-    if (__any(n > 0u)) {
+    if (__any(n > kOutlierSortRounds)) {
+      uint32_t k8[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) k8[i] = key[i];
+      sort8_desc(k8);
+      auto pop = [&](bool own) {
+#pragma unroll
+        for (int i = 0; i < 7; ++i) k8[i] = own ? k8[i + 1] : k8[i];
+        k8[7] = own ? 0u : k8[7];
+      };
+      pop(k8[0] == km);                    // the scale element heads one lane's list
+      for (uint32_t rr = 0;; ++rr) {
+        const uint32_t m = seg_max_u32<LPG>(k8[0]);
+#pragma unroll
+        for (int sl = 0; sl < NSLOT; ++sl) mykey[sl] = rr == tl + LPG * sl ? m : mykey[sl];
+        if (!__any(rr + 1u < n)) break;
+        pop(k8[0] == m);
+      }
+    } else if (__any(n > 0u)) {
 #pragma unroll
       for (int i = 0; i < NV; ++i) key[i] = key[i] == km ? 0u : key[i];
       for (uint32_t rr = 0;; ++rr) {
