@@ -11,13 +11,15 @@ ecco_train_patterns from a separate seeded 2**20-value sample of the same
 recipe (offline, outside the timed region).
 
 One step runs every row of the hot path over the whole layer, inputs resident
-in HBM: per matrix ecco_amax, ecco_encode and ecco_decode_gemv at batch 1, and
-one ecco_decode_many launch that decodes all seven matrices (each with its own
-tables and scale).  Each launch is bracketed by HIP events on the stream it
+in HBM: per matrix ecco_amax and ecco_encode, one ecco_decode_many launch that
+decodes all seven matrices (each with its own tables and scale), and the fused
+decode+GEMV at batch 1 as a decode step issues it: ecco_decode_gemv_many over
+q, k, v (same x), then o, then gate and up (same x), then down.  Each launch is bracketed by HIP events on the stream it
 runs on.  The reported value is decode throughput -- (64 B compressed in +
 256 B FP16 out) per group over the summed decode kernel time of the timed
 steps; encode (256 B in + 64 B out per group) and the fused GEMV are reported
-beside it, and so is each matrix decoded by an ecco_decode launch of its own.
+beside it, and so are each matrix decoded by an ecco_decode launch of its own
+and each GEMV issued by a call of its own.
 
 Other workloads (run separately, same JSON line shape):
   kv     K and V caches [16, 8, 8192, 128]: append-encode of the last 256
@@ -177,6 +179,11 @@ def bench_layer(args, torch, ecco, W):
         m["t"] = ecco.ecco_tensor_scale_from_amax(m["amax"].item())
     decode_jobs = [(m["blocks"], m["out_f"], m["gpr"], m["gpr"], m["in_f"], m["tdev"], m["t"], m["y"])
                    for m in mats.values()]
+    # the GEMVs of a decode step: q, k, v read the same x, and so do gate and
+    # up; o and down each wait for their own input
+    gemv_groups = [[mats[nm] for nm in grp] for grp in (["q", "k", "v"], ["o"], ["gate", "up"], ["down"])]
+    gemv_jobs = [[(m["blocks"], m["tdev"], m["t"], m["out_f"], m["in_f"], xin[m["in_f"]], m["gy"]) for m in grp]
+                 for grp in gemv_groups]
     timer = Timer(torch, stream)
 
     def step():
@@ -186,9 +193,8 @@ def bench_layer(args, torch, ecco, W):
             timer.run("encode", lambda: ecco.ecco_encode(m["w"], m["out_f"], m["gpr"], m["in_f"], m["gpr"],
                                                          m["tdev"], m["t"], m["blocks"]))
         timer.run("decode", lambda: ecco.ecco_decode_many(decode_jobs))
-        for m in mats.values():
-            timer.run("gemv", lambda: ecco.ecco_decode_gemv(m["blocks"], m["tdev"], m["t"], m["out_f"], m["in_f"],
-                                                            xin[m["in_f"]], 1, m["gy"]))
+        for jobs in gemv_jobs:
+            timer.run("gemv", lambda: ecco.ecco_decode_gemv_many(jobs, 1))
 
     for _ in range(args.warmup):
         step()
@@ -208,8 +214,14 @@ def bench_layer(args, torch, ecco, W):
         for m in mats.values():
             timer.run("decode_single", lambda: ecco.ecco_decode(m["blocks"], m["out_f"], m["gpr"], m["gpr"],
                                                                 m["in_f"], m["tdev"], m["t"], m["y"]))
+    # and each GEMV by a launch of its own
+    for _ in range(3):
+        for m in mats.values():
+            timer.run("gemv_single", lambda: ecco.ecco_decode_gemv(m["blocks"], m["tdev"], m["t"], m["out_f"],
+                                                                   m["in_f"], xin[m["in_f"]], 1, m["gy"]))
     torch.cuda.synchronize()
-    single = timer.collect()["decode_single"]
+    diag = timer.collect()
+    single = diag["decode_single"]
     res = dict(
         wall=wall, groups=groups,
         decode_GBps=groups * args.steps * BYTES_PER_GROUP / dec_t / 1e9,
@@ -221,6 +233,7 @@ def bench_layer(args, torch, ecco, W):
         gemv_b1_us_per_layer=sum(ph["gemv"]) / args.steps * 1e6,
         amax_us_per_layer=sum(ph["amax"]) / args.steps * 1e6,
         per_matrix_decode_us={nm: float(np.mean(single[i::len(mats)]) * 1e6) for i, nm in enumerate(mats)},
+        gemv_separate_us_per_layer=sum(diag["gemv_single"]) / 3 * 1e6,
     )
     x0 = mats["q"]["w"].cpu().numpy().reshape(-1, 128)
     return res, (x0, mats["q"]["blob"], mats["q"]["t"])
@@ -261,7 +274,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": "llama3-8b-layer (q,k,v,o,gate,up,down; 1,703,936 groups)",
                    "groups": res["groups"],
-                   "step": "per matrix amax, encode, decode_gemv(b=1); the 7 matrices decoded in one launch",
+                   "step": "per matrix amax and encode; the 7 matrices decoded in one launch; fused "
+                           "decode+GEMV at b=1 in four calls (q+k+v, o, gate+up, down)",
                    "tables": "ecco_train_patterns on seeded 2^20-value samples"},
         "encode_GBps": round(res["encode_GBps"], 1),
         "decode_frac_of_hbm_peak": round(res["decode_GBps"] / HBM_PEAK_GBPS, 4),
@@ -269,6 +283,7 @@ def main():
         "decode_us_per_layer": round(res["decode_us_per_layer"], 2),
         "encode_us_per_layer": round(res["encode_us_per_layer"], 2),
         "gemv_b1_us_per_layer": round(res["gemv_b1_us_per_layer"], 2),
+        "gemv_b1_us_per_layer_one_call_per_matrix": round(res["gemv_separate_us_per_layer"], 2),
         "amax_us_per_layer": round(res["amax_us_per_layer"], 2),
         "decode_us_per_matrix_separate_launches": {k: round(v, 2) for k, v in res["per_matrix_decode_us"].items()},
         "d2d_copy_GBps": round(copy, 1),

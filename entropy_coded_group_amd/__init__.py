@@ -19,7 +19,7 @@ __all__ = [
     "EccoError", "lib", "library_path",
     "ecco_tables_size", "ecco_tables_build", "ecco_tables_validate", "ecco_tables_get",
     "ecco_train_patterns", "ecco_tensor_scale_from_amax", "ecco_amax", "ecco_encode",
-    "ecco_decode", "ecco_encode_act", "ecco_decode_act", "ecco_decode_many", "ecco_decode_gemv", "ecco_attention_workspace_size",
+    "ecco_decode", "ecco_encode_act", "ecco_decode_act", "ecco_decode_many", "ecco_decode_gemv", "ecco_decode_gemv_many", "ecco_attention_workspace_size",
     "ecco_attention_decode", "ecco_strerror", "ecco_version",
     "STATS_FIELDS", "DECODE_MAX_JOBS", "tables_to_device",
 ]
@@ -49,6 +49,7 @@ class TrainOpts(ctypes.Structure):
 
 
 DECODE_MAX_JOBS = 16
+GEMV_MAX_JOBS = 16
 
 
 class DecodeJob(ctypes.Structure):
@@ -56,6 +57,13 @@ class DecodeJob(ctypes.Structure):
     _fields_ = [("blocks_dev", ctypes.c_void_p), ("y_dev", ctypes.c_void_p), ("tables_dev", ctypes.c_void_p),
                 ("n_rows", ctypes.c_uint64), ("groups_per_row", ctypes.c_uint64),
                 ("blk_row_stride_blocks", ctypes.c_uint64), ("y_row_stride_elems", ctypes.c_uint64),
+                ("tensor_scale", ctypes.c_float), ("reserved", ctypes.c_uint32)]
+
+
+class GemvJob(ctypes.Structure):
+    """ecco_gemv_job_t."""
+    _fields_ = [("blocks_dev", ctypes.c_void_p), ("tables_dev", ctypes.c_void_p), ("x_dev", ctypes.c_void_p),
+                ("y_dev", ctypes.c_void_p), ("out_features", ctypes.c_int64), ("in_features", ctypes.c_int64),
                 ("tensor_scale", ctypes.c_float), ("reserved", ctypes.c_uint32)]
 
 
@@ -84,6 +92,7 @@ def lib():
             "ecco_decode_act": (i32, [vp, u64, u64, u64, u64, vp, f32, vp, vp]),
             "ecco_decode_many": (i32, [vp, ctypes.c_uint32, vp]),
             "ecco_decode_gemv": (i32, [vp, vp, f32, i64, i64, vp, i64, vp, vp]),
+            "ecco_decode_gemv_many": (i32, [vp, ctypes.c_uint32, i64, vp]),
             "ecco_attention_workspace_size": (ctypes.c_size_t, [u64, u64, u64, u64]),
             "ecco_attention_decode": (i32, [vp, vp, f32, vp, vp, f32, vp, u64, u64, u64, u64, u64, f32, vp, vp,
                                             vp]),
@@ -238,6 +247,17 @@ def ecco_decode_gemv(blocks, tables_dev, tensor_scale, out_features, in_features
     _check(lib().ecco_decode_gemv(_ptr(blocks), _ptr(tables_dev), float(tensor_scale), int(out_features),
                                   int(in_features), _ptr(x), int(batch), _ptr(y), _stream(stream)),
            "ecco_decode_gemv")
+
+
+def ecco_decode_gemv_many(jobs, batch, stream=None):
+    """jobs: a sequence of (blocks, tables_dev, tensor_scale, out_features,
+    in_features, x, y) tuples -- the arguments of ecco_decode_gemv, one tuple
+    per matrix -- with a common batch."""
+    arr = (GemvJob * max(1, len(jobs)))()
+    for i, (blocks, tables_dev, t, out_f, in_f, x, y) in enumerate(jobs):
+        arr[i] = GemvJob(_ptr(blocks), _ptr(tables_dev), _ptr(x), _ptr(y), int(out_f), int(in_f), float(t), 0)
+    _check(lib().ecco_decode_gemv_many(ctypes.cast(arr, ctypes.c_void_p), len(jobs), int(batch), _stream(stream)),
+           "ecco_decode_gemv_many")
 
 
 def ecco_attention_workspace_size(batch, kv_heads, group, seq):

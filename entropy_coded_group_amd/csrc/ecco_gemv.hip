@@ -15,29 +15,50 @@
 // decodes its blocks 64 at a time (the last batch of a row partly filled).
 // Either way each lane accumulates the products of the 8 weights it is
 // handed, and the sums are taken in a fixed order.
+//
+// One launch can cover several matrices (the q, k and v projections of a
+// layer read the same x): each workgroup stages one matrix's tables and the
+// CUs are shared out in proportion to the matrices' work, so small matrices
+// run beside large ones instead of leaving most CUs idle.
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
 
 #include "ecco_device.h"
 
 namespace ecco {
 
-struct GemvArgs {
+// One matrix of a launch, and the contiguous range of workgroups that work
+// on it.
+struct GemvJob {
   const uint8_t* blocks;
   const Tables* tab;
   const uint16_t* x;
   float* y;
-  uint32_t out_f, in_f, gpr, batch;
+  uint32_t out_f, in_f, gpr;
+  uint32_t rb;         // whole rows per 64-block batch (1, 2 or 4), or 0: one row per wave
+  uint32_t n_units;    // 64-block batches (rb > 0) or rows (rb == 0)
+  uint32_t wg_first, wg_count;
   float t;
 };
 
+constexpr int kMaxGemvJobs = ECCO_GEMV_MAX_JOBS;
+
+struct GemvArgs {
+  GemvJob job[kMaxGemvJobs];
+  uint32_t n_jobs, batch;
+};
+
+// A wavefront owns one output row at a time and decodes its blocks 64 at a
+// time (the last batch of a row partly filled).  Rows go round the job's
+// workgroups first, then their waves.
 template <int BM>
-__global__ __launch_bounds__(kGemvWaves * 64) void gemv_kernel(GemvArgs a) {
-  __shared__ DecodeSmem<kGemvWaves> sm;
-  stage_decode_tables(sm, a.tab);
-  __syncthreads();
+__device__ __forceinline__ void gemv_rows_per_wave(DecodeSmem<kGemvWaves>& sm, const GemvJob& a, uint32_t lw,
+                                                   uint32_t batch) {
   const uint32_t lane = lane_id(), wave = threadIdx.x >> 6;
-  const uint32_t stride = gridDim.x * kGemvWaves;
-  uint32_t row = wave * gridDim.x + blockIdx.x;   // rows go round the CUs first
+  const uint32_t stride = a.wg_count * kGemvWaves;
+  uint32_t row = wave * a.wg_count + lw;
   if (row >= a.out_f) return;
   auto fetch = [&](uint32_t rw, uint32_t c0) {
     const uint8_t* rowblk = a.blocks + ((uint64_t)rw * a.gpr + c0) * 64u;
@@ -61,7 +82,7 @@ __global__ __launch_bounds__(kGemvWaves * 64) void gemv_kernel(GemvArgs a) {
       const uint16_t* xp = a.x + (uint64_t)(c0 + b) * 128u + j0;
 #pragma unroll
       for (int b2 = 0; b2 < BM; ++b2) {
-        if ((uint32_t)b2 < a.batch) {
+        if ((uint32_t)b2 < batch) {
           const uint4 xv = *reinterpret_cast<const uint4*>(xp + (uint64_t)b2 * a.in_f);
           part[b2] = dot8(w, xv, part[b2]);
         }
@@ -76,7 +97,7 @@ __global__ __launch_bounds__(kGemvWaves * 64) void gemv_kernel(GemvArgs a) {
 #pragma unroll
       for (int b = 0; b < BM; ++b) {
         const float v = wave_sum_f32(part[b]);
-        if (lane == 0 && (uint32_t)b < a.batch) a.y[(uint64_t)b * a.out_f + row] = v;
+        if (lane == 0 && (uint32_t)b < batch) a.y[(uint64_t)b * a.out_f + row] = v;
         part[b] = 0.0f;
       }
     }
@@ -87,18 +108,19 @@ __global__ __launch_bounds__(kGemvWaves * 64) void gemv_kernel(GemvArgs a) {
   }
 }
 
-// Rows of 64 / RB blocks: RB whole rows per 64-block batch.
-template <int BM, int RB>
-__global__ __launch_bounds__(kGemvWaves * 64) void gemv_rows_kernel(GemvArgs a) {
-  __shared__ DecodeSmem<kGemvWaves> sm;
-  stage_decode_tables(sm, a.tab);
-  __syncthreads();
+// Batch 1, rows of 64 / RB blocks: RB whole rows per 64-block batch.  The
+// decode core hands the weights over in four passes of 16 blocks and each
+// pass lies inside one row (pass k: row k * RB / 4 of the batch), so every
+// lane keeps one accumulator per row; wave sums finish the rows.
+template <int RB>
+__device__ __forceinline__ void gemv_whole_rows(DecodeSmem<kGemvWaves>& sm, const GemvJob& a, uint32_t lw,
+                                                uint32_t batch_cols) {
   constexpr uint32_t kGpr = 64 / RB;
   const uint32_t lane = lane_id(), wave = threadIdx.x >> 6;
   const uint32_t n_groups = a.out_f * kGpr;
-  const uint32_t n_batches = (n_groups + 63u) / 64u;
-  const uint32_t stride = gridDim.x * kGemvWaves;
-  uint32_t batch = wave * gridDim.x + blockIdx.x;   // batches go round the CUs first
+  const uint32_t n_batches = a.n_units;
+  const uint32_t stride = a.wg_count * kGemvWaves;
+  uint32_t batch = wave * a.wg_count + lw;          // batches go round the workgroups first
   if (batch >= n_batches) return;
   auto fetch = [&](uint32_t bt) {
     const uint32_t g0 = bt * 64u;
@@ -110,12 +132,9 @@ __global__ __launch_bounds__(kGemvWaves * 64) void gemv_rows_kernel(GemvArgs a) 
   for (; batch < n_batches; batch += stride) {
     const uint32_t nb = batch + stride;
     const BatchRegs nxt = fetch(nb < n_batches ? nb : batch);
-    float acc[RB][BM];
+    float acc[RB];
 #pragma unroll
-    for (int r = 0; r < RB; ++r)
-#pragma unroll
-      for (int b2 = 0; b2 < BM; ++b2) acc[r][b2] = 0.0f;
-    // pass k covers blocks 16 k .. 16 k + 15: row k * RB / 4 of the batch
+    for (int r = 0; r < RB; ++r) acc[r] = 0.0f;
     // an opaque copy of x per batch: otherwise the compiler hoists the 16
     // loop-invariant x addresses of a batch out of the loop (32 registers)
     const uint16_t* xb = a.x;
@@ -123,14 +142,14 @@ __global__ __launch_bounds__(kGemvWaves * 64) void gemv_rows_kernel(GemvArgs a) 
     auto sink = [&](uint32_t b, uint32_t j0, uint4 w, uint32_t k) {
       const uint16_t* xp = xb + (uint64_t)(b & (kGpr - 1u)) * 128u + j0;
       const uint32_t r = k * RB / 4u;
+      // (a load under a run-time condition is not started ahead of the
+      // decode; unconditional, the batch's 16 x loads would all be issued
+      // first and held across it)
+      if (batch_cols != 0u) {
+        const uint4 xv = *reinterpret_cast<const uint4*>(xp);
 #pragma unroll
-      for (int b2 = 0; b2 < BM; ++b2) {
-        if ((uint32_t)b2 < a.batch) {
-          const uint4 xv = *reinterpret_cast<const uint4*>(xp + (uint64_t)b2 * a.in_f);
-#pragma unroll
-          for (int rr = 0; rr < RB; ++rr)
-            if ((uint32_t)rr == r) acc[rr][b2] = dot8(w, xv, acc[rr][b2]);
-        }
+        for (int rr = 0; rr < RB; ++rr)
+          if ((uint32_t)rr == r) acc[rr] = dot8(w, xv, acc[rr]);
       }
     };
     const uint32_t n_valid = min(64u, n_groups - batch * 64u);
@@ -141,13 +160,31 @@ __global__ __launch_bounds__(kGemvWaves * 64) void gemv_rows_kernel(GemvArgs a) 
 #pragma unroll
     for (int r = 0; r < RB; ++r) {
       const uint32_t row = batch * RB + r;
-#pragma unroll
-      for (int b2 = 0; b2 < BM; ++b2) {
-        const float v = wave_sum_f32(acc[r][b2]);
-        if (lane == 0 && (uint32_t)b2 < a.batch && row < a.out_f) a.y[(uint64_t)b2 * a.out_f + row] = v;
-      }
+      const float v = wave_sum_f32(acc[r]);
+      if (lane == 0 && row < a.out_f) a.y[row] = v;
     }
     cur = nxt;
+  }
+}
+
+// Each workgroup works on one matrix, so the look-up tables it stages in LDS
+// serve every block it sees.  BM: accumulators per lane (batch <= BM); RB:
+// whole rows per batch (every job of the launch alike), 0 for a row per wave.
+// (One kernel per work split: a kernel holding both splits spills.)
+template <int BM, int RB>
+__global__ __launch_bounds__(kGemvWaves * 64) void gemv_kernel(GemvArgs args) {
+  __shared__ DecodeSmem<kGemvWaves> sm;
+  uint32_t j = 0;
+  while (j + 1 < args.n_jobs && blockIdx.x >= args.job[j + 1].wg_first) ++j;
+  const GemvJob a = args.job[j];            // one copy, kept in scalar registers
+  stage_decode_tables(sm, a.tab);
+  __syncthreads();
+  const uint32_t lw = blockIdx.x - a.wg_first;
+  if constexpr (RB > 0) {
+    static_assert(BM == 1, "whole rows per batch at batch 1 only");
+    gemv_whole_rows<RB>(sm, a, lw, args.batch);
+  } else {
+    gemv_rows_per_wave<BM>(sm, a, lw, args.batch);
   }
 }
 
@@ -156,40 +193,17 @@ __global__ __launch_bounds__(kGemvWaves * 64) void gemv_rows_kernel(GemvArgs a) 
 using namespace ecco;
 
 namespace {
-template <int BM>
-void launch_gemv(const GemvArgs& a, uint32_t cus, hipStream_t s) {
-  // (one accumulator per row and batch column: with more columns the
-  // registers run out, and those launches use the row-per-wave kernel)
-  if constexpr (BM == 1) {
-    if (a.gpr == 16 || a.gpr == 32 || a.gpr == 64) {
-      const uint32_t rb = 64u / a.gpr;
-      const uint32_t n_batches = (a.out_f * a.gpr + 63u) / 64u;
-      const uint32_t grid = std::max<uint32_t>(1, std::min<uint32_t>(n_batches, cus));
-      if (rb == 4)
-        hipLaunchKernelGGL((gemv_rows_kernel<1, 4>), dim3(grid), dim3(kGemvWaves * 64), 0, s, a);
-      else if (rb == 2)
-        hipLaunchKernelGGL((gemv_rows_kernel<1, 2>), dim3(grid), dim3(kGemvWaves * 64), 0, s, a);
-      else
-        hipLaunchKernelGGL((gemv_rows_kernel<1, 1>), dim3(grid), dim3(kGemvWaves * 64), 0, s, a);
-      return;
-    }
-  }
-  const uint32_t grid = std::max<uint32_t>(1, std::min<uint32_t>(a.out_f, cus));
-  hipLaunchKernelGGL(gemv_kernel<BM>, dim3(grid), dim3(kGemvWaves * 64), 0, s, a);
-}
-}  // namespace
 
-extern "C" int ecco_decode_gemv(const void* blocks, const void* tables, float tensor_scale, int64_t out_f,
-                                int64_t in_f, const uint16_t* x, int64_t batch, float* y, void* stream) {
+// Checks one matrix and fills its descriptor (all but the workgroup range).
+int make_gemv_job(const void* blocks, const void* tables, float tensor_scale, int64_t out_f, int64_t in_f,
+                  const uint16_t* x, float* y, int64_t batch, GemvJob* out) {
   if (!blocks || !tables || !x || !y) return ECCO_EINVAL;
   if (!(tensor_scale > 0.0f) || !(tensor_scale < __builtin_huge_valf())) return ECCO_EINVAL;
   if (out_f < 1 || in_f < 128 || in_f % 128 != 0 || batch < 1 || batch > ECCO_GEMV_MAX_BATCH) return ECCO_ESIZE;
   if ((uint64_t)out_f * (uint64_t)(in_f / 128) >= (1ull << 32) || out_f >= (1ll << 31)) return ECCO_ESIZE;
   if (!host_aligned(blocks, 64) || !host_aligned(tables, 256) || !host_aligned(x, 16) || !host_aligned(y, 4))
     return ECCO_EALIGN;
-  int cus = 0, rc = check_gfx950(&cus);
-  if (rc) return rc;
-  GemvArgs a;
+  GemvJob& a = *out;
   a.blocks = static_cast<const uint8_t*>(blocks);
   a.tab = static_cast<const Tables*>(tables);
   a.x = x;
@@ -197,17 +211,112 @@ extern "C" int ecco_decode_gemv(const void* blocks, const void* tables, float te
   a.out_f = (uint32_t)out_f;
   a.in_f = (uint32_t)in_f;
   a.gpr = (uint32_t)(in_f / 128);
-  a.batch = (uint32_t)batch;
   a.t = tensor_scale;
+  // batch 1 with rows of 16, 32 or 64 blocks packs whole rows into a batch (with
+  // more batch columns the registers run out for one accumulator per row and
+  // column, and those launches go one row per wave)
+  const bool whole = batch == 1 && (a.gpr == 16 || a.gpr == 32 || a.gpr == 64);
+  a.rb = whole ? 64u / a.gpr : 0u;
+  a.n_units = whole ? (a.out_f * a.gpr + 63u) / 64u : a.out_f;
+  a.wg_first = a.wg_count = 0;
+  return ECCO_OK;
+}
+
+// 64-block batches of decode work in a job.
+uint64_t gemv_cost(const GemvJob& a) {
+  return a.rb ? a.n_units : (uint64_t)a.out_f * ((a.gpr + 63u) / 64u);
+}
+
+// Splits the workgroups (at most one per CU) among the jobs: one each, then
+// each further workgroup to the job whose workgroups carry the most work; a
+// job gets no more workgroups than it has units.
+void assign_gemv_workgroups(GemvArgs& args, uint32_t cus) {
+  uint64_t total = 0;
+  for (uint32_t j = 0; j < args.n_jobs; ++j) total += args.job[j].n_units;
+  const uint32_t grid = (uint32_t)std::max<uint64_t>(args.n_jobs, std::min<uint64_t>(total, cus));
+  for (uint32_t j = 0; j < args.n_jobs; ++j) args.job[j].wg_count = 1;
+  for (uint32_t k = args.n_jobs; k < grid; ++k) {
+    uint32_t best = 0;
+    uint64_t best_load = 0;
+    for (uint32_t j = 0; j < args.n_jobs; ++j) {
+      const GemvJob& a = args.job[j];
+      if (a.wg_count >= a.n_units) continue;
+      const uint64_t load = (gemv_cost(a) + a.wg_count - 1) / a.wg_count;
+      if (load > best_load) best_load = load, best = j;
+    }
+    if (best_load == 0) break;
+    args.job[best].wg_count++;
+  }
+  uint32_t first = 0;
+  for (uint32_t j = 0; j < args.n_jobs; ++j) {
+    args.job[j].wg_first = first;
+    first += args.job[j].wg_count;
+  }
+}
+
+// One launch per work split present among the jobs (jobs of one split share
+// the GPU's workgroups); launches follow each other on the stream.
+int launch_gemv(const GemvArgs& all, void* stream) {
+  int cus = 0, rc = check_gfx950(&cus);
+  if (rc) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const dim3 block(kGemvWaves * 64);
   (void)hipGetLastError();
-  if (batch == 1)
-    launch_gemv<1>(a, (uint32_t)cus, s);
-  else if (batch <= 2)
-    launch_gemv<2>(a, (uint32_t)cus, s);
-  else if (batch <= 4)
-    launch_gemv<4>(a, (uint32_t)cus, s);
-  else
-    launch_gemv<8>(a, (uint32_t)cus, s);
-  return hipGetLastError() == hipSuccess ? ECCO_OK : ECCO_EHIP;
+  for (uint32_t rb : {0u, 1u, 2u, 4u}) {
+    GemvArgs args;
+    std::memset(&args, 0, sizeof(args));
+    args.batch = all.batch;
+    for (uint32_t j = 0; j < all.n_jobs; ++j)
+      if (all.job[j].rb == rb) args.job[args.n_jobs++] = all.job[j];
+    if (args.n_jobs == 0) continue;
+    assign_gemv_workgroups(args, (uint32_t)cus);
+    const GemvJob& last = args.job[args.n_jobs - 1];
+    const dim3 grid(last.wg_first + last.wg_count);
+    if (rb == 4)
+      hipLaunchKernelGGL((gemv_kernel<1, 4>), grid, block, 0, s, args);
+    else if (rb == 2)
+      hipLaunchKernelGGL((gemv_kernel<1, 2>), grid, block, 0, s, args);
+    else if (rb == 1)
+      hipLaunchKernelGGL((gemv_kernel<1, 1>), grid, block, 0, s, args);
+    else if (args.batch == 1)
+      hipLaunchKernelGGL((gemv_kernel<1, 0>), grid, block, 0, s, args);
+    else if (args.batch <= 2)
+      hipLaunchKernelGGL((gemv_kernel<2, 0>), grid, block, 0, s, args);
+    else if (args.batch <= 4)
+      hipLaunchKernelGGL((gemv_kernel<4, 0>), grid, block, 0, s, args);
+    else
+      hipLaunchKernelGGL((gemv_kernel<8, 0>), grid, block, 0, s, args);
+    if (hipGetLastError() != hipSuccess) return ECCO_EHIP;
+  }
+  return ECCO_OK;
+}
+
+}  // namespace
+
+extern "C" int ecco_decode_gemv(const void* blocks, const void* tables, float tensor_scale, int64_t out_f,
+                                int64_t in_f, const uint16_t* x, int64_t batch, float* y, void* stream) {
+  GemvArgs args;
+  std::memset(&args, 0, sizeof(args));
+  args.n_jobs = 1;
+  args.batch = (uint32_t)std::max<int64_t>(0, std::min<int64_t>(batch, 1 << 16));
+  int rc = make_gemv_job(blocks, tables, tensor_scale, out_f, in_f, x, y, batch, &args.job[0]);
+  if (rc) return rc;
+  return launch_gemv(args, stream);
+}
+
+extern "C" int ecco_decode_gemv_many(const ecco_gemv_job_t* jobs, uint32_t n_jobs, int64_t batch, void* stream) {
+  if (!jobs) return ECCO_EINVAL;
+  if (n_jobs == 0 || n_jobs > (uint32_t)kMaxGemvJobs) return ECCO_ESIZE;
+  GemvArgs args;
+  std::memset(&args, 0, sizeof(args));
+  args.n_jobs = n_jobs;
+  args.batch = (uint32_t)std::max<int64_t>(0, std::min<int64_t>(batch, 1 << 16));
+  for (uint32_t j = 0; j < n_jobs; ++j) {
+    const ecco_gemv_job_t& q = jobs[j];
+    if (q.reserved != 0) return ECCO_EINVAL;
+    int rc = make_gemv_job(q.blocks_dev, q.tables_dev, q.tensor_scale, q.out_features, q.in_features, q.x_dev,
+                           q.y_dev, batch, &args.job[j]);
+    if (rc) return rc;
+  }
+  return launch_gemv(args, stream);
 }

@@ -103,6 +103,7 @@ extern "C" {
 #define ECCO_LEN_MAX 8
 #define ECCO_GEMV_MAX_BATCH 8
 #define ECCO_DECODE_MAX_JOBS 16
+#define ECCO_GEMV_MAX_JOBS 16
 
 enum {
   ECCO_OK = 0,
@@ -253,6 +254,33 @@ int ecco_decode_many(const ecco_decode_job_t* jobs_host, uint32_t n_jobs, void* 
 int ecco_decode_gemv(const void* blocks_dev, const void* tables_dev, float tensor_scale,
                      int64_t out_features, int64_t in_features,
                      const uint16_t* x_dev, int64_t batch, float* y_dev, void* stream);
+
+/* One matrix of an ecco_decode_gemv_many call: the arguments of
+ * ecco_decode_gemv except the batch, which all jobs share. */
+typedef struct {
+  const void* blocks_dev;
+  const void* tables_dev;
+  const uint16_t* x_dev;
+  float* y_dev;
+  int64_t out_features;
+  int64_t in_features;
+  float tensor_scale;
+  uint32_t reserved;          /* must be 0 */
+} ecco_gemv_job_t;
+
+/* Fused decode + GEMV of several matrices in one launch, each with its own
+ * blocks, tables, scale, x and y -- e.g. the q, k and v projections of a
+ * layer, which read the same x.  Each job follows the rules of
+ * ecco_decode_gemv with the common batch; jobs_host (n_jobs in
+ * 1..ECCO_GEMV_MAX_JOBS) is read before the call returns.  If any job is
+ * invalid the call returns that job's error and enqueues nothing.  The y
+ * outputs of different jobs must not overlap.  Jobs whose rows split the same
+ * way -- at batch 1, rows of 16, 32 or 64 blocks pack 4, 2 or 1 whole rows
+ * into a 64-block batch; otherwise one row per wave -- share one launch, the
+ * GPU's workgroups shared out in proportion to their decode work; each other
+ * split present takes a launch of its own, in order on the stream.  Results
+ * are identical to one ecco_decode_gemv call per job. */
+int ecco_decode_gemv_many(const ecco_gemv_job_t* jobs_host, uint32_t n_jobs, int64_t batch, void* stream);
 
 /* Decode-phase attention over Ecco-compressed K and V caches, one query token
  * per sequence -- the consumer of the online KV codec ("Core claim": KV cache

@@ -128,6 +128,28 @@ def test_device_entry_points_check_arguments_before_touching_the_device():
     assert L.ecco_decode_gemv(A, A, 1.0, 16, 100, A, 1, A, None) == -3          # in % 128
     assert L.ecco_decode_gemv(A, A, 1.0, 16, 128, A, 9, A, None) == -3          # batch > 8
     assert L.ecco_amax(A, 0, A, None) == -3
+    # ecco_decode_gemv_many: count, batch, reserved field, every job checked
+    gj = (ecco.GemvJob * 3)()
+    for j in gj:
+        j.blocks_dev, j.tables_dev, j.x_dev, j.y_dev = A, A, A, A
+        j.out_features, j.in_features, j.tensor_scale = 16, 4096, 1.0
+    gp = ctypes.cast(gj, ctypes.c_void_p)
+    assert L.ecco_decode_gemv_many(None, 1, 1, None) == -1
+    assert L.ecco_decode_gemv_many(gp, 0, 1, None) == -3
+    assert L.ecco_decode_gemv_many(gp, ecco.GEMV_MAX_JOBS + 1, 1, None) == -3
+    assert L.ecco_decode_gemv_many(gp, 3, 0, None) == -3
+    assert L.ecco_decode_gemv_many(gp, 3, 9, None) == -3
+    gj[2].reserved = 7
+    assert L.ecco_decode_gemv_many(gp, 3, 1, None) == -1
+    gj[2].reserved = 0
+    gj[1].in_features = 4000
+    assert L.ecco_decode_gemv_many(gp, 3, 1, None) == -3
+    gj[1].in_features = 4096
+    gj[2].y_dev = A + 2
+    assert L.ecco_decode_gemv_many(gp, 3, 1, None) == -2
+    gj[2].y_dev = A
+    gj[0].tables_dev = None
+    assert L.ecco_decode_gemv_many(gp, 3, 1, None) == -1
     # activation format: the same checks with 64-value groups
     assert L.ecco_encode_act(None, 1, 1, 64, 1, A, 1.0, A, None, None) == -1
     assert L.ecco_encode_act(A, 1, 1, 64, 1, A, float("nan"), A, None, None) == -1

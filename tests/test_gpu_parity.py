@@ -353,6 +353,42 @@ def test_gemv_small(dev, out_f, in_f, batch):
     assert ok, "worst error / bound = %g" % worst
 
 
+GEMV_MANY_SHAPES = [(37, 4096), (1000, 2048), (33, 8192), (50, 14336), (5, 1024), (1, 128), (300, 4096)]
+
+
+@pytest.mark.parametrize("batch", [1, 3, 8])
+def test_gemv_many_mixed_jobs(dev, batch):
+    """Seven matrices of different shapes, tables and scales in one call (at
+    batch 1 they split four ways: 1, 2 or 4 whole rows per batch and one row
+    per wave): every y within the bound of the float64 reference, and bit for
+    bit what a call per matrix gives."""
+    names = ["c5_w1", "c5_w2", "c1"]
+    cases = []
+    for i, (out_f, in_f) in enumerate(GEMV_MANY_SHAPES):
+        tb = golden(names[i % 3])
+        w = W.llama_matrix((out_f, in_f), seed=720 + i).numpy()
+        t = scale_of(w)
+        blocks = codec.encode_groups(w.reshape(-1, 128), tb, t)
+        x = W.c5_x(batch, in_f, seed=730 + i).numpy()
+        cases.append(dict(tb=tb, tdev=dev_tables(tb), t=t, blocks=blocks, bd=torch.from_numpy(blocks).cuda(),
+                          x=x, xd=torch.from_numpy(x).cuda(), out_f=out_f, in_f=in_f,
+                          y=torch.full((batch, out_f), float("nan"), dtype=torch.float32, device="cuda"),
+                          y1=torch.full((batch, out_f), float("nan"), dtype=torch.float32, device="cuda")))
+    say("gemv_many %d jobs b=%d" % (len(cases), batch))
+    ecco.ecco_decode_gemv_many([(c["bd"], c["tdev"], c["t"], c["out_f"], c["in_f"], c["xd"], c["y"]) for c in cases],
+                               batch)
+    for c in cases:
+        ecco.ecco_decode_gemv(c["bd"], c["tdev"], c["t"], c["out_f"], c["in_f"], c["xd"], batch, c["y1"])
+    torch.cuda.synchronize()
+    for c in cases:
+        y = c["y"].cpu().numpy()
+        assert np.array_equal(y.view(np.uint32), c["y1"].cpu().numpy().view(np.uint32)), (c["out_f"], c["in_f"])
+        w_hat = codec.decode_blocks(c["blocks"], c["tb"], c["t"]).reshape(c["out_f"], c["in_f"])
+        y_ref, mag = ogemv.gemv_ref(w_hat, c["x"])
+        ok, worst = ogemv.gemv_tolerance_ok(y, y_ref, mag, c["in_f"])
+        assert ok, "%dx%d b=%d worst error / bound = %g" % (c["out_f"], c["in_f"], batch, worst)
+
+
 # -------------------------------------------------------------- full-size, sampled
 
 def sample_index(G, stride=97):
@@ -417,6 +453,85 @@ def test_kv_cache_full_size_sampled(dev):
         assert_fp16_equal(y.cpu().numpy().reshape(-1, 128)[idx], codec.decode_blocks(ob, tb, t),
                           "kv %s decode (sampled)" % kind)
         del kvd, y, blocks
+        torch.cuda.empty_cache()
+
+
+def test_beyond_2_pow_32_elements_strided_sampled(dev):
+    """Two strided rows of 16,779,267 groups each: the second row starts past
+    2^31 elements and its end lies past 2^32, so every element and block offset
+    needs 64-bit arithmetic (8.6 GB of FP16 in and out)."""
+    tb = golden("c1")
+    tdev = dev_tables(tb)
+    gpr = (1 << 24) + 2051
+    xs, bs = gpr * 128 + 8, gpr + 1
+    say("2^32: generate 2 x %d groups on the device" % gpr)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(4242)
+    x = torch.randn(2 * xs, generator=gen, dtype=torch.float16, device="cuda")
+    t = np.float32(1.0)
+    blocks = torch.full((2 * bs, 64), 0xAB, dtype=torch.uint8, device="cuda")
+    say("2^32: encode")
+    ecco.ecco_encode(x, 2, gpr, xs, bs, tdev, t, blocks)
+    y = torch.full((2 * xs,), 0x7FFF, dtype=torch.int16, device="cuda")
+    say("2^32: decode")
+    ecco.ecco_decode(blocks, 2, gpr, bs, xs, tdev, t, y)
+    torch.cuda.synchronize()
+    cols = np.unique(np.r_[np.arange(0, gpr, 104729), gpr - 64 + np.arange(64), np.arange(64)])
+    for r in (0, 1):
+        say("2^32: check row %d" % r)
+        xi = torch.from_numpy(r * xs + cols[:, None] * 128 + np.arange(128)[None, :]).cuda()
+        xg = x[xi].cpu().numpy()
+        ob = codec.encode_groups(xg, tb, t)
+        bi = torch.from_numpy(r * bs + cols).cuda()
+        assert_blocks_equal(blocks[bi].cpu().numpy(), ob, "row %d encode (sampled)" % r)
+        assert_fp16_equal(y[xi].cpu().numpy().view(np.float16), codec.decode_blocks(ob, tb, t),
+                          "row %d decode (sampled)" % r)
+    # the gaps between rows are untouched
+    assert int(blocks[gpr].min()) == 0xAB and int(blocks[2 * bs - 1].min()) == 0xAB
+    assert torch.all(y[gpr * 128:xs] == 0x7FFF) and torch.all(y[xs + gpr * 128:] == 0x7FFF)
+    del x, y, blocks
+    torch.cuda.empty_cache()
+
+
+def test_gemv_many_layer_groups_full_size_sampled(dev):
+    """A LLaMA-3-8B layer's GEMVs as a decode step issues them at batch 1: q, k
+    and v in one call (they read the same x), gate and up in another; sampled
+    rows against the float64 reference over oracle-decoded weights, and every
+    row bit for bit what a call per matrix gives."""
+    for group in (["q", "k", "v"], ["gate", "up"]):
+        in_f = W.LLAMA3_8B_LAYER[group[0]][1]
+        x = W.c5_x(1, in_f, seed=740).numpy()
+        xd = torch.from_numpy(x).cuda()
+        mats = []
+        for nm in group:
+            tb = golden("c2_" + nm)
+            say("layer %s generate + encode" % nm)
+            w = W.c2_layer(0, [nm])[nm]
+            out_f = w.shape[0]
+            t = scale_of(w.numpy())
+            wd = w.cuda()
+            bd = torch.empty((out_f, in_f // 128, 64), dtype=torch.uint8, device="cuda")
+            tdev = dev_tables(tb)
+            ecco.ecco_encode(wd, out_f, in_f // 128, in_f, in_f // 128, tdev, t, bd)
+            mats.append(dict(nm=nm, w=w.numpy(), tb=tb, tdev=tdev, t=t, bd=bd, out_f=out_f,
+                             y=torch.full((1, out_f), float("nan"), dtype=torch.float32, device="cuda"),
+                             y1=torch.full((1, out_f), float("nan"), dtype=torch.float32, device="cuda")))
+            del wd
+        say("gemv_many %s" % "+".join(group))
+        ecco.ecco_decode_gemv_many([(m["bd"], m["tdev"], m["t"], m["out_f"], in_f, xd, m["y"]) for m in mats], 1)
+        for m in mats:
+            ecco.ecco_decode_gemv(m["bd"], m["tdev"], m["t"], m["out_f"], in_f, xd, 1, m["y1"])
+        torch.cuda.synchronize()
+        for m in mats:
+            y = m["y"].cpu().numpy()
+            assert np.array_equal(y.view(np.uint32), m["y1"].cpu().numpy().view(np.uint32)), m["nm"]
+            rows = np.unique(np.r_[np.arange(0, m["out_f"], 97), m["out_f"] - 1])
+            ob = codec.encode_groups(m["w"][rows].reshape(-1, 128), m["tb"], m["t"])
+            w_hat = codec.decode_blocks(ob, m["tb"], m["t"]).reshape(len(rows), in_f)
+            y_ref, mag = ogemv.gemv_ref(w_hat, x)
+            ok, worst = ogemv.gemv_tolerance_ok(y[:, rows], y_ref, mag, in_f)
+            assert ok, "%s worst error / bound = %g" % (m["nm"], worst)
+        del mats
         torch.cuda.empty_cache()
 
 
