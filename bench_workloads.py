@@ -175,8 +175,12 @@ def bench_ffn(args, torch, ecco, W):
                 torch.matmul(x, wbuf.t())
 
             tu = _timed(torch, unfused, args.steps, args.warmup)
+            # the uncompressed reference: the dense GEMV alone on FP16 weights
+            # already in HBM (reads 4x the bytes of the fused path)
+            td = _timed(torch, lambda: torch.matmul(x, wbuf.t()), args.steps, args.warmup)
             out["%s_b%d" % (name, b)] = dict(fused_us=round(np.mean(tf) * 1e6, 2),
                                              decode_then_gemv_us=round(np.mean(tu) * 1e6, 2),
+                                             fp16_dense_gemv_us=round(np.mean(td) * 1e6, 2),
                                              compressed_GBps=round(out_f * in_f / 2 / np.mean(tf) / 1e9, 1))
         del wbuf
     tot_f = sum(v["fused_us"] for v in out.values())
