@@ -19,10 +19,6 @@ constexpr int S = ECCO_N_PATTERNS;
 constexpr int C = ECCO_N_CENTROIDS;
 constexpr int H = ECCO_N_CODEBOOKS;
 constexpr int A = ECCO_N_SYMBOLS;
-constexpr int kBlockBits = 512;
-constexpr int kHeaderBits = 16;
-constexpr int kRecordBits = 15;
-constexpr int kMaxOutliers = 16;
 
 // Decode look-up table entry for an 8-bit window of stream bits read LSB
 // first: bits 0..4 = symbol (0..15), bits 5..7 = code length - 1.  Every

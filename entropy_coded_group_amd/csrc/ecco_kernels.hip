@@ -7,6 +7,9 @@
 // Huffman codewords of the 128 centroid indices, clipped at the block end or
 // followed by zero fill and 15-bit outlier records ("What carries the
 // argument"; "Core claim"; Fig. 4 caption; referee report major comment 1).
+// The activation format codes groups of 64 values the same way, with 14-bit
+// records ("free parameters": activation group size; Fig. 9 caption); the
+// encode and decode kernels are templates on the group size.
 //
 // Kernel design (the pages' decoder is a 64-way hardware unit; on a GPU the
 // parallelism comes from decoding many independent blocks at once):
@@ -15,14 +18,15 @@
 //           block's codeword stream through an 8-bit-window look-up table
 //           staged in LDS (all 256 codebooks, 64 KiB), four codewords per
 //           64-bit bit-window refill.  Symbols are written back to LDS and the
-//           wave turns around: sixteen lanes per block look up reconstruction
-//           values from a per-block 32-entry FP16 table (15 centroids * a, the
-//           scale, outliers) and write 128-bit stores, four whole rows per
-//           store instruction.
-//   encode  sixteen lanes (one DPP row) per group, four groups per wave:
-//           row-wide max/min/argmin/sum/scan through DPP, LDS-resident
-//           thresholds for a branch-free binary search, codewords merged into
-//           the block with LDS atomic OR.
+//           wave turns around: eight values per lane (sixteen lanes per
+//           128-value block) are looked up in a per-block 32-entry FP16 table
+//           (15 centroids * a, the scale, outliers) and written with 128-bit
+//           stores, whole rows per store instruction.
+//   encode  eight values per lane, so sixteen lanes (one DPP row) per
+//           128-value group and four groups per wave (8 lanes and 8 groups for
+//           64-value groups): segment-wide max/min/argmin/sum/scan through
+//           DPP, LDS-resident thresholds for a branch-free binary search,
+//           codewords merged into the block with LDS atomic OR.
 //   amax    grid-stride max of |x|.
 // All floating-point steps that decide a bit of the output are single IEEE
 // binary32 operations (the library is built with -ffp-contract=off).
