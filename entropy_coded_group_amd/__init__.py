@@ -19,7 +19,7 @@ __all__ = [
     "EccoError", "lib", "library_path",
     "ecco_tables_size", "ecco_tables_build", "ecco_tables_validate", "ecco_tables_get",
     "ecco_train_patterns", "ecco_tensor_scale_from_amax", "ecco_amax", "ecco_encode",
-    "ecco_decode", "ecco_encode_act", "ecco_decode_act", "ecco_decode_many", "ecco_decode_gemv", "ecco_decode_gemv_many", "ecco_attention_workspace_size",
+    "ecco_decode", "ecco_encode_many", "ecco_encode_act", "ecco_decode_act", "ecco_decode_many", "ecco_decode_gemv", "ecco_decode_gemv_many", "ecco_attention_workspace_size",
     "ecco_attention_decode", "ecco_strerror", "ecco_version",
     "STATS_FIELDS", "DECODE_MAX_JOBS", "tables_to_device",
 ]
@@ -60,6 +60,14 @@ class DecodeJob(ctypes.Structure):
                 ("tensor_scale", ctypes.c_float), ("reserved", ctypes.c_uint32)]
 
 
+class EncodeJob(ctypes.Structure):
+    """ecco_encode_job_t."""
+    _fields_ = [("x_dev", ctypes.c_void_p), ("blocks_dev", ctypes.c_void_p), ("tables_dev", ctypes.c_void_p),
+                ("stats_dev", ctypes.c_void_p), ("n_rows", ctypes.c_uint64), ("groups_per_row", ctypes.c_uint64),
+                ("x_row_stride_elems", ctypes.c_uint64), ("blk_row_stride_blocks", ctypes.c_uint64),
+                ("tensor_scale", ctypes.c_float), ("reserved", ctypes.c_uint32)]
+
+
 class GemvJob(ctypes.Structure):
     """ecco_gemv_job_t."""
     _fields_ = [("blocks_dev", ctypes.c_void_p), ("tables_dev", ctypes.c_void_p), ("x_dev", ctypes.c_void_p),
@@ -88,6 +96,7 @@ def lib():
             "ecco_amax": (i32, [vp, u64, vp, vp]),
             "ecco_encode": (i32, [vp, u64, u64, u64, u64, vp, f32, vp, vp, vp]),
             "ecco_decode": (i32, [vp, u64, u64, u64, u64, vp, f32, vp, vp]),
+            "ecco_encode_many": (i32, [vp, ctypes.c_uint32, vp]),
             "ecco_encode_act": (i32, [vp, u64, u64, u64, u64, vp, f32, vp, vp, vp]),
             "ecco_decode_act": (i32, [vp, u64, u64, u64, u64, vp, f32, vp, vp]),
             "ecco_decode_many": (i32, [vp, ctypes.c_uint32, vp]),
@@ -213,6 +222,19 @@ def ecco_decode(blocks, n_rows, groups_per_row, blk_row_stride_blocks, y_row_str
     _check(lib().ecco_decode(_ptr(blocks), int(n_rows), int(groups_per_row), int(blk_row_stride_blocks),
                              int(y_row_stride_elems), _ptr(tables_dev), float(tensor_scale), _ptr(y),
                              _stream(stream)), "ecco_decode")
+
+
+def ecco_encode_many(jobs, stream=None):
+    """jobs: a sequence of (x, n_rows, groups_per_row, x_row_stride_elems,
+    blk_row_stride_blocks, tables_dev, tensor_scale, blocks, stats) tuples --
+    the arguments of ecco_encode, one tuple per tensor -- encoded in one
+    launch (stats may be None)."""
+    arr = (EncodeJob * max(1, len(jobs)))()
+    for i, (x, n_rows, gpr, xstride, bstride, tables_dev, t, blocks, stats) in enumerate(jobs):
+        arr[i] = EncodeJob(_ptr(x), _ptr(blocks), _ptr(tables_dev), _ptr(stats), int(n_rows), int(gpr), int(xstride),
+                           int(bstride), float(t), 0)
+    _check(lib().ecco_encode_many(ctypes.cast(arr, ctypes.c_void_p), len(jobs), _stream(stream)),
+           "ecco_encode_many")
 
 
 def ecco_encode_act(x, n_rows, groups_per_row, x_row_stride_elems, blk_row_stride_blocks, tables_dev,

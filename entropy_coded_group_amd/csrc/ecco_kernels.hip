@@ -132,7 +132,9 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_kernel(DecodeArgs args)
 
 // -------------------------------------------------------------------- encode
 
-struct EncodeArgs {
+// One tensor of an encode launch, and the contiguous range of workgroups
+// that encode it.
+struct EncodeJob {
   const uint16_t* x;
   uint8_t* blocks;
   const Tables* tab;
@@ -143,6 +145,12 @@ struct EncodeArgs {
   uint32_t n_groups;
   uint32_t n_units;      // groups / (groups per wave), rounded up
   float t, inv_t;
+  uint32_t wg_first, wg_count;
+};
+
+struct EncodeArgs {
+  EncodeJob job[kMaxJobs];
+  uint32_t n_jobs;
 };
 
 constexpr int kEncWaves = 4;
@@ -176,7 +184,11 @@ struct EncodeSmem {
 // row for 128, half a row for 64) and a wave encodes GPW = 64 / LPG groups at
 // a time.
 template <int GS>
-__global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(EncodeArgs a) {
+__global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(EncodeArgs args) {
+  uint32_t jj = 0;
+  while (jj + 1 < args.n_jobs && blockIdx.x >= args.job[jj + 1].wg_first) ++jj;
+  const EncodeJob a = args.job[jj];         // one copy, kept in scalar registers
+  const uint32_t lw = blockIdx.x - a.wg_first;
   using Geo = GroupGeom<GS>;
   constexpr int NV = 8;
   constexpr int LPG = GS / NV;
@@ -209,8 +221,8 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(EncodeArgs a) {
     const uint32_t row = div_magic(g, a.gpr), col = g - row * a.gpr.d;
     return load_stream(a.x + (uint64_t)row * a.x_stride + (uint64_t)col * GS + NV * tl);
   };
-  const uint32_t ustride = gridDim.x * kEncWaves;
-  uint32_t unit = blockIdx.x * kEncWaves + wave;
+  const uint32_t ustride = a.wg_count * kEncWaves;
+  uint32_t unit = lw * kEncWaves + wave;
   uint4 raw = load_group(unit * GPW + q);
   for (; unit < a.n_units; unit += ustride) {
     const uint32_t gidx = unit * GPW + q;
@@ -541,9 +553,11 @@ extern "C" int ecco_amax(const uint16_t* x, uint64_t n, float* amax, void* strea
 
 namespace {
 
+// Checks one encode job of GS-value groups and fills its kernel descriptor
+// (all but the workgroup range).
 template <int GS>
-int encode_impl(const uint16_t* x, uint64_t n_rows, uint64_t gpr, uint64_t x_stride, uint64_t blk_stride,
-                const void* tables, float tensor_scale, void* blocks, ecco_stats_t* stats, void* stream) {
+int make_encode_job(const uint16_t* x, uint64_t n_rows, uint64_t gpr, uint64_t x_stride, uint64_t blk_stride,
+                    const void* tables, float tensor_scale, void* blocks, ecco_stats_t* stats, EncodeJob* out) {
   if (!x || !tables || !blocks) return ECCO_EINVAL;
   if (!(tensor_scale > 0.0f) || !(tensor_scale < __builtin_huge_valf())) return ECCO_EINVAL;
   const uint64_t total = n_rows * gpr;
@@ -552,9 +566,7 @@ int encode_impl(const uint16_t* x, uint64_t n_rows, uint64_t gpr, uint64_t x_str
   if (!host_aligned(x, 16) || (x_stride % 8) != 0 || !host_aligned(blocks, 64) || !host_aligned(tables, 256) ||
       (stats && !host_aligned(stats, 8)))
     return ECCO_EALIGN;
-  int cus = 0, rc = check_gfx950(&cus);
-  if (rc) return rc;
-  EncodeArgs a;
+  EncodeJob& a = *out;
   a.x = x;
   a.blocks = static_cast<uint8_t*>(blocks);
   a.tab = static_cast<const Tables*>(tables);
@@ -568,11 +580,59 @@ int encode_impl(const uint16_t* x, uint64_t n_rows, uint64_t gpr, uint64_t x_str
   a.t = tensor_scale;
   volatile float inv = 1.0f / tensor_scale;
   a.inv_t = inv;
-  uint32_t want = (a.n_units + kEncWaves - 1) / kEncWaves;
-  uint32_t grid = std::max<uint32_t>(1, std::min<uint32_t>(want, (uint32_t)cus * 8));
+  a.wg_first = a.wg_count = 0;
+  return ECCO_OK;
+}
+
+// Up to 8 workgroups of kEncWaves waves per CU, no more than a job has units
+// for; split among the jobs one each, then each further workgroup to the job
+// whose workgroups carry the most units.
+void assign_encode_workgroups(EncodeArgs& args, uint32_t cus) {
+  uint64_t want = 0;
+  for (uint32_t j = 0; j < args.n_jobs; ++j) want += (args.job[j].n_units + kEncWaves - 1) / kEncWaves;
+  const uint32_t grid = (uint32_t)std::max<uint64_t>(args.n_jobs, std::min<uint64_t>(want, (uint64_t)cus * 8));
+  for (uint32_t j = 0; j < args.n_jobs; ++j) args.job[j].wg_count = 1;
+  for (uint32_t k = args.n_jobs; k < grid; ++k) {
+    uint32_t best = 0;
+    uint64_t best_load = 0;
+    for (uint32_t j = 0; j < args.n_jobs; ++j) {
+      const EncodeJob& a = args.job[j];
+      if ((uint64_t)a.wg_count * kEncWaves >= a.n_units) continue;
+      const uint64_t load = (a.n_units + a.wg_count - 1) / a.wg_count;
+      if (load > best_load) best_load = load, best = j;
+    }
+    if (best_load == 0) break;
+    args.job[best].wg_count++;
+  }
+  uint32_t first = 0;
+  for (uint32_t j = 0; j < args.n_jobs; ++j) {
+    args.job[j].wg_first = first;
+    first += args.job[j].wg_count;
+  }
+}
+
+template <int GS>
+int launch_encode(EncodeArgs& args, void* stream) {
+  int cus = 0, rc = check_gfx950(&cus);
+  if (rc) return rc;
+  assign_encode_workgroups(args, (uint32_t)cus);
+  const EncodeJob& last = args.job[args.n_jobs - 1];
+  const uint32_t grid = last.wg_first + last.wg_count;
   (void)hipGetLastError();
-  hipLaunchKernelGGL(encode_kernel<GS>, dim3(grid), dim3(kEncWaves * 64), 0, static_cast<hipStream_t>(stream), a);
+  hipLaunchKernelGGL(encode_kernel<GS>, dim3(grid), dim3(kEncWaves * 64), 0, static_cast<hipStream_t>(stream), args);
   return launch_status();
+}
+
+template <int GS>
+int encode_one(const uint16_t* x, uint64_t n_rows, uint64_t gpr, uint64_t x_stride, uint64_t blk_stride,
+               const void* tables, float tensor_scale, void* blocks, ecco_stats_t* stats, void* stream) {
+  EncodeArgs args;
+  std::memset(&args, 0, sizeof(args));
+  args.n_jobs = 1;
+  int rc = make_encode_job<GS>(x, n_rows, gpr, x_stride, blk_stride, tables, tensor_scale, blocks, stats,
+                               &args.job[0]);
+  if (rc) return rc;
+  return launch_encode<GS>(args, stream);
 }
 
 }  // namespace
@@ -580,13 +640,29 @@ int encode_impl(const uint16_t* x, uint64_t n_rows, uint64_t gpr, uint64_t x_str
 extern "C" int ecco_encode(const uint16_t* x, uint64_t n_rows, uint64_t gpr, uint64_t x_stride,
                            uint64_t blk_stride, const void* tables, float tensor_scale, void* blocks,
                            ecco_stats_t* stats, void* stream) {
-  return encode_impl<128>(x, n_rows, gpr, x_stride, blk_stride, tables, tensor_scale, blocks, stats, stream);
+  return encode_one<128>(x, n_rows, gpr, x_stride, blk_stride, tables, tensor_scale, blocks, stats, stream);
+}
+
+extern "C" int ecco_encode_many(const ecco_encode_job_t* jobs, uint32_t n_jobs, void* stream) {
+  if (!jobs) return ECCO_EINVAL;
+  if (n_jobs == 0 || n_jobs > (uint32_t)kMaxJobs) return ECCO_ESIZE;
+  EncodeArgs args;
+  std::memset(&args, 0, sizeof(args));
+  args.n_jobs = n_jobs;
+  for (uint32_t j = 0; j < n_jobs; ++j) {
+    const ecco_encode_job_t& q = jobs[j];
+    if (q.reserved != 0) return ECCO_EINVAL;
+    int rc = make_encode_job<128>(q.x_dev, q.n_rows, q.groups_per_row, q.x_row_stride_elems, q.blk_row_stride_blocks,
+                                  q.tables_dev, q.tensor_scale, q.blocks_dev, q.stats_dev, &args.job[j]);
+    if (rc) return rc;
+  }
+  return launch_encode<128>(args, stream);
 }
 
 extern "C" int ecco_encode_act(const uint16_t* x, uint64_t n_rows, uint64_t gpr, uint64_t x_stride,
                                uint64_t blk_stride, const void* tables, float tensor_scale, void* blocks,
                                ecco_stats_t* stats, void* stream) {
-  return encode_impl<64>(x, n_rows, gpr, x_stride, blk_stride, tables, tensor_scale, blocks, stats, stream);
+  return encode_one<64>(x, n_rows, gpr, x_stride, blk_stride, tables, tensor_scale, blocks, stats, stream);
 }
 
 namespace {

@@ -200,6 +200,30 @@ int ecco_encode(const uint16_t* x_dev, uint64_t n_rows, uint64_t groups_per_row,
                 const void* tables_dev, float tensor_scale, void* blocks_dev,
                 ecco_stats_t* stats_dev, void* stream);
 
+/* One tensor of an ecco_encode_many call: the arguments of ecco_encode. */
+typedef struct {
+  const uint16_t* x_dev;
+  void* blocks_dev;
+  const void* tables_dev;
+  ecco_stats_t* stats_dev;    /* may be NULL */
+  uint64_t n_rows;
+  uint64_t groups_per_row;
+  uint64_t x_row_stride_elems;
+  uint64_t blk_row_stride_blocks;
+  float tensor_scale;
+  uint32_t reserved;          /* must be 0 */
+} ecco_encode_job_t;
+
+/* Encode several tensors, each with its own tables and scale, in one launch
+ * -- e.g. the K and V rows a decode step appends to the caches.  Each job
+ * follows the rules of ecco_encode; jobs_host (n_jobs in
+ * 1..ECCO_DECODE_MAX_JOBS) is read before the call returns.  If any job is
+ * invalid the call returns that job's error and enqueues nothing.  Blocks of
+ * different jobs must not overlap (statistics buffers may be shared).  The
+ * workgroups are shared out in proportion to the jobs' sizes.  Results are
+ * identical to one ecco_encode call per job. */
+int ecco_encode_many(const ecco_encode_job_t* jobs_host, uint32_t n_jobs, void* stream);
+
 /* Decode: the inverse layout of ecco_encode; group (r, g) is written to
  * y_dev + r * y_row_stride_elems + g * 128.  Every block decodes (the
  * decoder is total on arbitrary bits).  Same size rules as ecco_encode. */

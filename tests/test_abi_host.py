@@ -128,6 +128,27 @@ def test_device_entry_points_check_arguments_before_touching_the_device():
     assert L.ecco_decode_gemv(A, A, 1.0, 16, 100, A, 1, A, None) == -3          # in % 128
     assert L.ecco_decode_gemv(A, A, 1.0, 16, 128, A, 9, A, None) == -3          # batch > 8
     assert L.ecco_amax(A, 0, A, None) == -3
+    # ecco_encode_many: count, reserved field, every job checked
+    ej = (ecco.EncodeJob * 2)()
+    for j in ej:
+        j.x_dev, j.blocks_dev, j.tables_dev = A, A, A
+        j.n_rows, j.groups_per_row, j.x_row_stride_elems, j.blk_row_stride_blocks = 2, 4, 512, 4
+        j.tensor_scale = 1.0
+    ep = ctypes.cast(ej, ctypes.c_void_p)
+    assert L.ecco_encode_many(None, 1, None) == -1
+    assert L.ecco_encode_many(ep, 0, None) == -3
+    assert L.ecco_encode_many(ep, ecco.DECODE_MAX_JOBS + 1, None) == -3
+    ej[1].reserved = 3
+    assert L.ecco_encode_many(ep, 2, None) == -1
+    ej[1].reserved = 0
+    ej[1].x_row_stride_elems = 500                                             # < 4 * 128
+    assert L.ecco_encode_many(ep, 2, None) == -3
+    ej[1].x_row_stride_elems = 512
+    ej[0].stats_dev = A + 4
+    assert L.ecco_encode_many(ep, 2, None) == -2
+    ej[0].stats_dev = None
+    ej[1].tensor_scale = 0.0
+    assert L.ecco_encode_many(ep, 2, None) == -1
     # ecco_decode_gemv_many: count, batch, reserved field, every job checked
     gj = (ecco.GemvJob * 3)()
     for j in gj:

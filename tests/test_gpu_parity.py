@@ -227,6 +227,35 @@ def test_fuzz_decode_random_blocks(dev):
                               "fuzz %s t=%g" % (name, t))
 
 
+def test_kv_append_k_and_v_in_one_call(dev):
+    """The K and V rows of a decode step appended by one ecco_encode_many call
+    (strided rows of the [B, H, S, 128] caches, each tensor with its own tables
+    and fixed scale): the same blocks as one ecco_encode call per tensor and as
+    the oracle."""
+    B, H, S, D = 2, 3, 512, 128
+    first, ntok = 300, 37
+    jobs, sep, data = [], [], []
+    for kind, seed in (("k", 31), ("v", 32)):
+        tb, t = golden("c3_" + kind), golden_t("c3_" + kind)
+        tdev = dev_tables(tb)
+        kv = W.kv_tensor(kind, shape=(B, H, S, D), seed=seed)
+        kvd = kv.cuda()
+        b1 = torch.full((B, H, S, 64), 0xAB, dtype=torch.uint8, device="cuda")
+        b2 = torch.full((B, H, S, 64), 0xAB, dtype=torch.uint8, device="cuda")
+        jobs.append((kvd[:, :, first:], B * H, ntok, S * D, S, tdev, t, b1[:, :, first:], None))
+        ecco.ecco_encode(kvd[:, :, first:], B * H, ntok, S * D, S, tdev, t, b2[:, :, first:])
+        data.append((kind, kv, tb, t, tdev, kvd, b1, b2))
+    say("kv append K+V in one call")
+    ecco.ecco_encode_many(jobs)
+    torch.cuda.synchronize()
+    for kind, kv, tb, t, _, _, b1, b2 in data:
+        g1, g2 = b1.cpu().numpy(), b2.cpu().numpy()
+        assert np.array_equal(g1, g2), kind
+        ob = codec.encode_groups(kv.numpy()[:, :, first:first + ntok].reshape(-1, 128), tb, t)
+        assert_blocks_equal(g1[:, :, first:first + ntok].reshape(-1, 64), ob, "kv append %s" % kind)
+        assert np.all(g1[:, :, :first] == 0xAB) and np.all(g1[:, :, first + ntok:] == 0xAB)
+
+
 def test_strided_kv_append_and_decode(dev):
     tb = golden("c3_k")
     t = golden_t("c3_k")
@@ -300,6 +329,56 @@ def test_decode_many_mixed_jobs_exact(dev):
     assert_fp16_equal(g2[:, :gpr * 128].reshape(-1, 128).view(np.float16), codec.decode_blocks(ob, tb, t),
                       "decode_many strided job")
     assert np.all(g2[:, gpr * 128:] == 0x7FFF)
+
+
+def test_encode_many_mixed_jobs_exact(dev):
+    """Several tensors with their own tables, scales and layouts encoded in one
+    launch (one group to several units with ragged tails, clipping tables, a
+    strided job); every block against the oracle, nothing written outside the
+    jobs' blocks, and statistics summed over the jobs that share a buffer."""
+    specs = [("golden", 1, 1), ("random", 3, 2), ("adversarial", 64, 3), ("random", 65, 4),
+             ("golden", 1000, 5), ("random", 4097, 6), ("adversarial", 777, 7)]
+    jobs, refs, keep = [], [], []
+    stats = torch.zeros(7, dtype=torch.int64, device="cuda")
+    want = dict.fromkeys(ecco.STATS_FIELDS, 0)
+    for i, (kind, n, seed) in enumerate(specs):
+        tb = {"golden": lambda s: golden("c1"), "random": random_tables,
+              "adversarial": adversarial_tables}[kind](seed)
+        x = W.random_groups(n, 400 + seed, ("normal", "laplace", "wide")[i % 3]).numpy()
+        t = scale_of(x) * np.float32(1.0 + 0.25 * i)
+        ob, info = codec.encode_groups(x, tb, t, return_info=True)
+        for k, v in info["stats"].items():
+            want[k] += v
+        tdev = dev_tables(tb)
+        xd = torch.from_numpy(x).cuda()
+        bd = torch.full((n + 2, 64), 0xAB, dtype=torch.uint8, device="cuda")
+        jobs.append((xd, 1, n, n * 128, n, tdev, t, bd[1:n + 1], stats))
+        refs.append(ob)
+        keep.append((tdev, xd, bd))
+    # a strided job: 5 rows of 300 groups inside rows of 320*128 + 64 elements / 320 blocks
+    tb = random_tables(8)
+    rows, gpr, xstride, bstride = 5, 300, 320 * 128 + 64, 320
+    xs = W.random_groups(rows * gpr, 408, "laplace").numpy()
+    t = scale_of(xs)
+    xfull = np.zeros((rows, xstride), np.float16)
+    xfull[:, :gpr * 128] = xs.reshape(rows, gpr * 128)
+    ob_s = codec.encode_groups(xs, tb, t)
+    tdev = dev_tables(tb)
+    xd = torch.from_numpy(xfull).cuda()
+    bd = torch.full((rows, bstride, 64), 0xAB, dtype=torch.uint8, device="cuda")
+    jobs.append((xd, rows, gpr, xstride, bstride, tdev, t, bd, None))
+    keep.append((tdev, xd, bd))
+    say("encode_many %d jobs" % len(jobs))
+    ecco.ecco_encode_many(jobs)
+    torch.cuda.synchronize()
+    for i, (ref, (_, _, bd)) in enumerate(zip(refs, keep)):
+        got = bd.cpu().numpy()
+        assert np.all(got[0] == 0xAB) and np.all(got[-1] == 0xAB), "job %d wrote outside its blocks" % i
+        assert_blocks_equal(got[1:-1], ref, "encode_many job %d" % i)
+    assert dict(zip(ecco.STATS_FIELDS, stats.cpu().tolist())) == want
+    got = keep[-1][2].cpu().numpy()
+    assert_blocks_equal(got[:, :gpr].reshape(-1, 64), ob_s, "encode_many strided job")
+    assert np.all(got[:, gpr:] == 0xAB)
 
 
 def test_decode_many_full_layer_sampled(dev):
