@@ -413,7 +413,8 @@ def test_decode_many_full_layer_sampled(dev):
 
 @pytest.mark.parametrize("out_f,in_f,batch", [(1, 128, 1), (37, 1024, 3), (300, 1024, 8), (64, 8192, 4),
                                               (20, 28672, 2), (1, 4096, 1), (999, 4096, 1), (5, 2048, 1),
-                                              (1000, 2048, 1), (33, 8192, 1), (50, 14336, 1)])
+                                              (1000, 2048, 1), (33, 8192, 1), (50, 14336, 1), (7, 12416, 1),
+                                              (3, 8320, 1), (1, 16384, 1), (300, 14336, 1)])
 def test_gemv_small(dev, out_f, in_f, batch):
     tb = golden("c5_w1")
     tdev = dev_tables(tb)
@@ -574,10 +575,11 @@ def test_beyond_2_pow_32_elements_strided_sampled(dev):
 
 def test_gemv_many_layer_groups_full_size_sampled(dev):
     """A LLaMA-3-8B layer's GEMVs as a decode step issues them at batch 1: q, k
-    and v in one call (they read the same x), gate and up in another; sampled
-    rows against the float64 reference over oracle-decoded weights, and every
-    row bit for bit what a call per matrix gives."""
-    for group in (["q", "k", "v"], ["gate", "up"]):
+    and v in one call (they read the same x), gate and up in another, down (rows
+    of 112 blocks, one row per wave) alone; sampled rows against the float64
+    reference over oracle-decoded weights, and every row bit for bit what a
+    call per matrix gives."""
+    for group in (["q", "k", "v"], ["gate", "up"], ["down"]):
         in_f = W.LLAMA3_8B_LAYER[group[0]][1]
         x = W.c5_x(1, in_f, seed=740).numpy()
         xd = torch.from_numpy(x).cuda()
