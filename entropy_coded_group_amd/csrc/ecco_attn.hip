@@ -85,9 +85,19 @@ __global__ __launch_bounds__(kScoreWaves * 64) void attn_scores_kernel(AttnArgs 
       float d[G];
 #pragma unroll
       for (int g = 0; g < G; ++g) d[g] = row_sum_f32(dot8(w, qv[g], 0.0f)) * a.scale;
+      // one vector store of the token's G scores (whole 16-byte pieces, so the
+      // four tokens of an instruction fill their 64 bytes without partial writes)
       if ((lane & 15u) == 0) {
+        float* dst = sp + (uint64_t)b * G;
+        if constexpr (G == 1) {
+          dst[0] = d[0];
+        } else if constexpr (G == 2) {
+          *reinterpret_cast<float2*>(dst) = make_float2(d[0], d[1]);
+        } else {
 #pragma unroll
-        for (int g = 0; g < G; ++g) sp[(uint64_t)b * G + g] = d[g];
+          for (int g = 0; g < G; g += 4)
+            *reinterpret_cast<float4*>(dst + g) = make_float4(d[g], d[g + 1], d[g + 2], d[g + 3]);
+        }
       }
     };
     if (n_valid == 64u)
@@ -99,9 +109,10 @@ __global__ __launch_bounds__(kScoreWaves * 64) void attn_scores_kernel(AttnArgs 
 }
 
 // Softmax of one pair's G rows, [S][G] with g innermost, by one workgroup:
-// three coalesced passes over the pair's scores (max, sum of exp,
-// normalise), which stay in the L2 cache between them; workgroup reductions
-// through LDS.
+// three coalesced passes over the pair's scores (max, sum of exp, then exp
+// again divided by the sum, written in place), which stay in the L2 cache
+// between them; workgroup reductions through LDS.  Recomputing exp in the
+// last pass gives the same values as the second and saves a write pass.
 constexpr int kSmThreads = 1024;
 
 template <int G>
@@ -139,18 +150,17 @@ __global__ __launch_bounds__(kSmThreads) void attn_softmax_kernel(AttnArgs a) {
   for (int g = 0; g < G; ++g) z[g] = 0.0f;
   for (uint32_t t = tid; t < a.S; t += kSmThreads)
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float e = expf(base[(uint64_t)t * G + g] - m[g]);
-      base[(uint64_t)t * G + g] = e;
-      z[g] += e;
-    }
+    for (int g = 0; g < G; ++g) z[g] += expf(base[(uint64_t)t * G + g] - m[g]);
   wg_reduce(z, false);
   float inv[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) inv[g] = 1.0f / z[g];
   for (uint32_t t = tid; t < a.S; t += kSmThreads)
 #pragma unroll
-    for (int g = 0; g < G; ++g) base[(uint64_t)t * G + g] *= inv[g];
+    for (int g = 0; g < G; ++g) {
+      float* q = base + (uint64_t)t * G + g;
+      *q = expf(*q - m[g]) * inv[g];
+    }
 }
 
 // p . V for heads g_off .. g_off + GH - 1 of G.
