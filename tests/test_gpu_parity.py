@@ -381,6 +381,45 @@ def test_encode_many_mixed_jobs_exact(dev):
     assert np.all(got[:, gpr:] == 0xAB)
 
 
+def test_many_calls_at_the_job_limit(dev):
+    """ecco_encode_many, ecco_decode_many and ecco_decode_gemv_many with the
+    maximum of 16 jobs, each with its own tables and size (1 to 301 groups):
+    every job's result equal to the oracle's (blocks, FP16) or within the GEMV
+    bound."""
+    n_jobs = 16
+    assert n_jobs == ecco.DECODE_MAX_JOBS == ecco.GEMV_MAX_JOBS
+    enc, dec, gem, refs = [], [], [], []
+    for i in range(n_jobs):
+        tb = random_tables(600 + i)
+        n = 1 + 20 * i
+        x = W.random_groups(n, 610 + i, ("normal", "laplace", "wide")[i % 3]).numpy()
+        t = scale_of(x)
+        ob = codec.encode_groups(x, tb, t)
+        tdev = dev_tables(tb)
+        xd = torch.from_numpy(x).cuda()
+        bd = torch.full((n, 64), 0xAB, dtype=torch.uint8, device="cuda")
+        yd = torch.full((n, 128), 0x7FFF, dtype=torch.int16, device="cuda")
+        enc.append((xd, 1, n, n * 128, n, tdev, t, bd, None))
+        dec.append((torch.from_numpy(ob).cuda(), 1, n, n, n * 128, tdev, t, yd))
+        # GEMV: the job's groups as a [rows, 128] matrix times one x vector
+        xv = W.c5_x(1, 128, seed=620 + i).numpy()
+        gy = torch.full((1, n), float("nan"), dtype=torch.float32, device="cuda")
+        gem.append((dec[-1][0], tdev, t, n, 128, torch.from_numpy(xv).cuda(), gy))
+        refs.append((tb, t, ob, xv, bd, yd, gy))
+    say("encode_many / decode_many / gemv_many with %d jobs" % n_jobs)
+    ecco.ecco_encode_many(enc)
+    ecco.ecco_decode_many(dec)
+    ecco.ecco_decode_gemv_many(gem, 1)
+    torch.cuda.synchronize()
+    for i, (tb, t, ob, xv, bd, yd, gy) in enumerate(refs):
+        assert_blocks_equal(bd.cpu().numpy(), ob, "encode_many job %d" % i)
+        w_hat = codec.decode_blocks(ob, tb, t)
+        assert_fp16_equal(yd.cpu().numpy().view(np.float16), w_hat, "decode_many job %d" % i)
+        y_ref, mag = ogemv.gemv_ref(w_hat, xv)
+        ok, worst = ogemv.gemv_tolerance_ok(gy.cpu().numpy(), y_ref, mag, 128)
+        assert ok, "gemv_many job %d worst error / bound = %g" % (i, worst)
+
+
 def test_decode_many_full_layer_sampled(dev):
     """All seven matrices of a LLaMA-3-8B layer decoded in one launch, each
     with its own tables and scale (the layer workload's decode step)."""
