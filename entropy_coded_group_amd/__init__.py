@@ -19,9 +19,10 @@ __all__ = [
     "EccoError", "lib", "library_path",
     "ecco_tables_size", "ecco_tables_build", "ecco_tables_validate", "ecco_tables_get",
     "ecco_train_patterns", "ecco_tensor_scale_from_amax", "ecco_amax", "ecco_encode",
-    "ecco_decode", "ecco_encode_many", "ecco_encode_act", "ecco_decode_act", "ecco_decode_many", "ecco_decode_gemv", "ecco_decode_gemv_many", "ecco_attention_workspace_size",
+    "ecco_decode", "ecco_encode_many", "ecco_encode_act", "ecco_decode_act", "ecco_decode_many",
+    "ecco_decode_gemv", "ecco_decode_gemv_many", "ecco_attention_workspace_size",
     "ecco_attention_decode", "ecco_strerror", "ecco_version",
-    "STATS_FIELDS", "DECODE_MAX_JOBS", "tables_to_device",
+    "STATS_FIELDS", "DECODE_MAX_JOBS", "GEMV_MAX_JOBS", "tables_to_device",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -136,6 +137,21 @@ def _ptr(obj):
     raise TypeError("expected a torch tensor, NumPy array or address, got %r" % type(obj))
 
 
+def _dptr(obj, dense=False):
+    """Address of a device argument: a torch tensor on the GPU (dense=True: also
+    contiguous, for arguments whose layout the call fixes), or a raw address.
+    Host memory handed to a kernel would fault the GPU, so it is refused here."""
+    if obj is None or isinstance(obj, int):
+        return obj
+    if hasattr(obj, "data_ptr"):
+        if not obj.is_cuda:
+            raise ValueError("device argument must be a GPU tensor, got one on %s" % obj.device)
+        if dense and not obj.is_contiguous():
+            raise ValueError("this argument must be a contiguous tensor")
+        return obj.data_ptr()
+    raise TypeError("expected a GPU tensor or a device address, got %r" % type(obj))
+
+
 def _stream(stream):
     if stream is not None:
         return stream if isinstance(stream, int) else stream.cuda_stream
@@ -207,20 +223,20 @@ def tables_to_device(blob, device="cuda"):
 # ----------------------------------------------------------------- device
 
 def ecco_amax(x, n_values, amax_out, stream=None):
-    _check(lib().ecco_amax(_ptr(x), int(n_values), _ptr(amax_out), _stream(stream)), "ecco_amax")
+    _check(lib().ecco_amax(_dptr(x), int(n_values), _dptr(amax_out), _stream(stream)), "ecco_amax")
 
 
 def ecco_encode(x, n_rows, groups_per_row, x_row_stride_elems, blk_row_stride_blocks, tables_dev,
                 tensor_scale, blocks, stats=None, stream=None):
-    _check(lib().ecco_encode(_ptr(x), int(n_rows), int(groups_per_row), int(x_row_stride_elems),
-                             int(blk_row_stride_blocks), _ptr(tables_dev), float(tensor_scale), _ptr(blocks),
-                             _ptr(stats), _stream(stream)), "ecco_encode")
+    _check(lib().ecco_encode(_dptr(x), int(n_rows), int(groups_per_row), int(x_row_stride_elems),
+                             int(blk_row_stride_blocks), _dptr(tables_dev), float(tensor_scale), _dptr(blocks),
+                             _dptr(stats), _stream(stream)), "ecco_encode")
 
 
 def ecco_decode(blocks, n_rows, groups_per_row, blk_row_stride_blocks, y_row_stride_elems, tables_dev,
                 tensor_scale, y, stream=None):
-    _check(lib().ecco_decode(_ptr(blocks), int(n_rows), int(groups_per_row), int(blk_row_stride_blocks),
-                             int(y_row_stride_elems), _ptr(tables_dev), float(tensor_scale), _ptr(y),
+    _check(lib().ecco_decode(_dptr(blocks), int(n_rows), int(groups_per_row), int(blk_row_stride_blocks),
+                             int(y_row_stride_elems), _dptr(tables_dev), float(tensor_scale), _dptr(y),
                              _stream(stream)), "ecco_decode")
 
 
@@ -231,7 +247,7 @@ def ecco_encode_many(jobs, stream=None):
     launch (stats may be None)."""
     arr = (EncodeJob * max(1, len(jobs)))()
     for i, (x, n_rows, gpr, xstride, bstride, tables_dev, t, blocks, stats) in enumerate(jobs):
-        arr[i] = EncodeJob(_ptr(x), _ptr(blocks), _ptr(tables_dev), _ptr(stats), int(n_rows), int(gpr), int(xstride),
+        arr[i] = EncodeJob(_dptr(x), _dptr(blocks), _dptr(tables_dev), _dptr(stats), int(n_rows), int(gpr), int(xstride),
                            int(bstride), float(t), 0)
     _check(lib().ecco_encode_many(ctypes.cast(arr, ctypes.c_void_p), len(jobs), _stream(stream)),
            "ecco_encode_many")
@@ -240,16 +256,16 @@ def ecco_encode_many(jobs, stream=None):
 def ecco_encode_act(x, n_rows, groups_per_row, x_row_stride_elems, blk_row_stride_blocks, tables_dev,
                     tensor_scale, blocks, stats=None, stream=None):
     """ecco_encode for the 2x activation format (groups of 64 values)."""
-    _check(lib().ecco_encode_act(_ptr(x), int(n_rows), int(groups_per_row), int(x_row_stride_elems),
-                                 int(blk_row_stride_blocks), _ptr(tables_dev), float(tensor_scale), _ptr(blocks),
-                                 _ptr(stats), _stream(stream)), "ecco_encode_act")
+    _check(lib().ecco_encode_act(_dptr(x), int(n_rows), int(groups_per_row), int(x_row_stride_elems),
+                                 int(blk_row_stride_blocks), _dptr(tables_dev), float(tensor_scale), _dptr(blocks),
+                                 _dptr(stats), _stream(stream)), "ecco_encode_act")
 
 
 def ecco_decode_act(blocks, n_rows, groups_per_row, blk_row_stride_blocks, y_row_stride_elems, tables_dev,
                     tensor_scale, y, stream=None):
     """ecco_decode for the 2x activation format (groups of 64 values)."""
-    _check(lib().ecco_decode_act(_ptr(blocks), int(n_rows), int(groups_per_row), int(blk_row_stride_blocks),
-                                 int(y_row_stride_elems), _ptr(tables_dev), float(tensor_scale), _ptr(y),
+    _check(lib().ecco_decode_act(_dptr(blocks), int(n_rows), int(groups_per_row), int(blk_row_stride_blocks),
+                                 int(y_row_stride_elems), _dptr(tables_dev), float(tensor_scale), _dptr(y),
                                  _stream(stream)), "ecco_decode_act")
 
 
@@ -259,15 +275,15 @@ def ecco_decode_many(jobs, stream=None):
     ecco_decode, one tuple per tensor -- decoded in one launch."""
     arr = (DecodeJob * max(1, len(jobs)))()
     for i, (blocks, n_rows, gpr, bstride, ystride, tables_dev, t, y) in enumerate(jobs):
-        arr[i] = DecodeJob(_ptr(blocks), _ptr(y), _ptr(tables_dev), int(n_rows), int(gpr), int(bstride),
+        arr[i] = DecodeJob(_dptr(blocks), _dptr(y), _dptr(tables_dev), int(n_rows), int(gpr), int(bstride),
                            int(ystride), float(t), 0)
     _check(lib().ecco_decode_many(ctypes.cast(arr, ctypes.c_void_p), len(jobs), _stream(stream)),
            "ecco_decode_many")
 
 
 def ecco_decode_gemv(blocks, tables_dev, tensor_scale, out_features, in_features, x, batch, y, stream=None):
-    _check(lib().ecco_decode_gemv(_ptr(blocks), _ptr(tables_dev), float(tensor_scale), int(out_features),
-                                  int(in_features), _ptr(x), int(batch), _ptr(y), _stream(stream)),
+    _check(lib().ecco_decode_gemv(_dptr(blocks, True), _dptr(tables_dev), float(tensor_scale), int(out_features),
+                                  int(in_features), _dptr(x, True), int(batch), _dptr(y, True), _stream(stream)),
            "ecco_decode_gemv")
 
 
@@ -277,7 +293,8 @@ def ecco_decode_gemv_many(jobs, batch, stream=None):
     per matrix -- with a common batch."""
     arr = (GemvJob * max(1, len(jobs)))()
     for i, (blocks, tables_dev, t, out_f, in_f, x, y) in enumerate(jobs):
-        arr[i] = GemvJob(_ptr(blocks), _ptr(tables_dev), _ptr(x), _ptr(y), int(out_f), int(in_f), float(t), 0)
+        arr[i] = GemvJob(_dptr(blocks, True), _dptr(tables_dev), _dptr(x, True), _dptr(y, True), int(out_f),
+                         int(in_f), float(t), 0)
     _check(lib().ecco_decode_gemv_many(ctypes.cast(arr, ctypes.c_void_p), len(jobs), int(batch), _stream(stream)),
            "ecco_decode_gemv_many")
 
@@ -288,10 +305,10 @@ def ecco_attention_workspace_size(batch, kv_heads, group, seq):
 
 def ecco_attention_decode(k_blocks, k_tables_dev, k_scale, v_blocks, v_tables_dev, v_scale, q, batch, kv_heads,
                           group, seq, kv_stride_tokens, scale, workspace, out, stream=None):
-    _check(lib().ecco_attention_decode(_ptr(k_blocks), _ptr(k_tables_dev), float(k_scale), _ptr(v_blocks),
-                                       _ptr(v_tables_dev), float(v_scale), _ptr(q), int(batch), int(kv_heads),
-                                       int(group), int(seq), int(kv_stride_tokens), float(scale), _ptr(workspace),
-                                       _ptr(out), _stream(stream)), "ecco_attention_decode")
+    _check(lib().ecco_attention_decode(_dptr(k_blocks), _dptr(k_tables_dev), float(k_scale), _dptr(v_blocks),
+                                       _dptr(v_tables_dev), float(v_scale), _dptr(q, True), int(batch), int(kv_heads),
+                                       int(group), int(seq), int(kv_stride_tokens), float(scale), _dptr(workspace),
+                                       _dptr(out, True), _stream(stream)), "ecco_attention_decode")
 
 
 def ecco_strerror(code):

@@ -205,6 +205,26 @@ def test_device_entry_points_check_arguments_before_touching_the_device():
     del blob
 
 
+def test_binding_refuses_host_memory_for_device_arguments():
+    """Host memory passed to a kernel would fault the GPU: the binding refuses
+    NumPy arrays and CPU tensors for device arguments before calling the
+    library, and non-contiguous tensors where the call fixes the layout."""
+    import torch
+    host = np.zeros(1024, np.uint16)
+    cpu = torch.zeros(1024, dtype=torch.float16)
+    with pytest.raises(TypeError):
+        ecco.ecco_amax(host, 1024, 1 << 20)
+    with pytest.raises(ValueError):
+        ecco.ecco_amax(cpu, 1024, 1 << 20)
+    with pytest.raises(ValueError):
+        ecco.ecco_decode(1 << 20, 1, 8, 8, 1024, 1 << 20, 1.0, cpu)
+    with pytest.raises(ValueError):
+        ecco.ecco_decode_gemv_many([(1 << 20, 1 << 20, 1.0, 4, 128, cpu, 1 << 20)], 1)
+    with pytest.raises(ValueError):
+        ecco.ecco_attention_decode(1 << 20, 1 << 20, 1.0, 1 << 20, 1 << 20, 1.0, cpu, 1, 1, 1, 8, 8, 0.1,
+                                   1 << 20, 1 << 20)
+
+
 def test_library_training_gives_valid_tables_of_oracle_quality():
     sample = W.c1_sample(n_values=512 * 128).numpy()
     blob = ecco.ecco_train_patterns(sample, kmeans_iters=10, huff_iters=5, threads=4)
