@@ -18,8 +18,9 @@ q, k, v (same x), then o, then gate and up (same x), then down.  Each launch is 
 runs on.  The reported value is decode throughput -- (64 B compressed in +
 256 B FP16 out) per group over the summed decode kernel time of the timed
 steps; encode (256 B in + 64 B out per group) and the fused GEMV are reported
-beside it, and so are each matrix decoded by an ecco_decode launch of its own
-and each GEMV issued by a call of its own.
+beside it, and so are each matrix decoded by an ecco_decode launch of its own,
+the same by ecco_decode_speculative (the pages' segment-parallel decode), and
+each GEMV issued by a call of its own.
 
 Other workloads (run separately, same JSON line shape):
   kv     K and V caches [16, 8, 8192, 128]: append-encode of the last 256
@@ -257,6 +258,11 @@ def bench_layer(args, torch, ecco, W):
         for m in mats.values():
             timer.run("decode_single", lambda: ecco.ecco_decode(m["blocks"], m["out_f"], m["gpr"], m["gpr"],
                                                                 m["in_f"], m["tdev"], m["t"], m["y"]))
+    # the same matrices by the speculative segment decoder (the pages' method)
+    for _ in range(3):
+        for m in mats.values():
+            timer.run("decode_spec", lambda: ecco.ecco_decode_speculative(m["blocks"], m["out_f"], m["gpr"], m["gpr"],
+                                                                          m["in_f"], m["tdev"], m["t"], m["y"]))
     # and each GEMV by a launch of its own
     for _ in range(3):
         for m in mats.values():
@@ -277,6 +283,7 @@ def bench_layer(args, torch, ecco, W):
         amax_us_per_layer=sum(ph["amax"]) / args.steps * 1e6,
         per_matrix_decode_us={nm: float(np.mean(single[i::len(mats)]) * 1e6) for i, nm in enumerate(mats)},
         gemv_separate_us_per_layer=sum(diag["gemv_single"]) / 3 * 1e6,
+        spec_decode_us_per_layer=sum(diag["decode_spec"]) / 3 * 1e6,
     )
     x0 = mats["q"]["w"].cpu().numpy().reshape(-1, 128)
     return res, (x0, mats["q"]["blob"], mats["q"]["t"])
@@ -329,6 +336,9 @@ def main():
         "gemv_b1_us_per_layer_one_call_per_matrix": round(res["gemv_separate_us_per_layer"], 2),
         "amax_us_per_layer": round(res["amax_us_per_layer"], 2),
         "decode_us_per_matrix_separate_launches": {k: round(v, 2) for k, v in res["per_matrix_decode_us"].items()},
+        "speculative_decode_us_per_layer": round(res["spec_decode_us_per_layer"], 2),
+        "speculative_decode_GBps": round(res["groups"] * BYTES_PER_GROUP / (res["spec_decode_us_per_layer"] * 1e-6) / 1e9,
+                                         1),
         "d2d_copy_GBps": round(copy, 1),
         "roofline": {"bound": "hbm", "kernel": "decode_kernel",
                      "achieved": round(res["decode_GBps"], 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",

@@ -19,7 +19,8 @@ __all__ = [
     "EccoError", "lib", "library_path",
     "ecco_tables_size", "ecco_tables_build", "ecco_tables_validate", "ecco_tables_get",
     "ecco_train_patterns", "ecco_tensor_scale_from_amax", "ecco_amax", "ecco_encode",
-    "ecco_decode", "ecco_encode_many", "ecco_encode_act", "ecco_decode_act", "ecco_decode_many",
+    "ecco_decode", "ecco_decode_speculative", "ecco_encode_many", "ecco_encode_act", "ecco_decode_act",
+    "ecco_decode_many",
     "ecco_decode_gemv", "ecco_decode_gemv_many", "ecco_attention_workspace_size",
     "ecco_attention_decode", "ecco_strerror", "ecco_version",
     "STATS_FIELDS", "DECODE_MAX_JOBS", "GEMV_MAX_JOBS", "tables_to_device",
@@ -97,6 +98,7 @@ def lib():
             "ecco_amax": (i32, [vp, u64, vp, vp]),
             "ecco_encode": (i32, [vp, u64, u64, u64, u64, vp, f32, vp, vp, vp]),
             "ecco_decode": (i32, [vp, u64, u64, u64, u64, vp, f32, vp, vp]),
+            "ecco_decode_speculative": (i32, [vp, u64, u64, u64, u64, vp, f32, vp, vp]),
             "ecco_encode_many": (i32, [vp, ctypes.c_uint32, vp]),
             "ecco_encode_act": (i32, [vp, u64, u64, u64, u64, vp, f32, vp, vp, vp]),
             "ecco_decode_act": (i32, [vp, u64, u64, u64, u64, vp, f32, vp, vp]),
@@ -238,6 +240,14 @@ def ecco_decode(blocks, n_rows, groups_per_row, blk_row_stride_blocks, y_row_str
     _check(lib().ecco_decode(_dptr(blocks), int(n_rows), int(groups_per_row), int(blk_row_stride_blocks),
                              int(y_row_stride_elems), _dptr(tables_dev), float(tensor_scale), _dptr(y),
                              _stream(stream)), "ecco_decode")
+
+
+def ecco_decode_speculative(blocks, n_rows, groups_per_row, blk_row_stride_blocks, y_row_stride_elems,
+                            tables_dev, tensor_scale, y, stream=None):
+    """ecco_decode by the speculative segment method (same output, slower)."""
+    _check(lib().ecco_decode_speculative(_dptr(blocks), int(n_rows), int(groups_per_row),
+                                         int(blk_row_stride_blocks), int(y_row_stride_elems), _dptr(tables_dev),
+                                         float(tensor_scale), _dptr(y), _stream(stream)), "ecco_decode_speculative")
 
 
 def ecco_encode_many(jobs, stream=None):

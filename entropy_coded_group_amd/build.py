@@ -18,7 +18,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libecco.so")
 ARCH = "gfx950"
 
-SOURCES = ["ecco_tables.cpp", "ecco_train.cpp", "ecco_kernels.hip", "ecco_gemv.hip", "ecco_attn.hip"]
+SOURCES = ["ecco_tables.cpp", "ecco_train.cpp", "ecco_kernels.hip", "ecco_gemv.hip", "ecco_attn.hip",
+           "ecco_spec.hip"]
 
 # -ffp-contract=off: every float step that decides an output bit is a single
 # IEEE operation (no fused multiply-add).  Packed FP32 instructions are

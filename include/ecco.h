@@ -244,6 +244,17 @@ int ecco_decode_act(const void* blocks_dev, uint64_t n_rows, uint64_t groups_per
                     uint64_t blk_row_stride_blocks, uint64_t y_row_stride_elems,
                     const void* tables_dev, float tensor_scale, uint16_t* y_dev, void* stream);
 
+/* Decode by the pages' parallel method (Fig. 8 caption, 64-way parallel
+ * decoder): one wavefront per block, the codeword stream cut into 62 segments
+ * of 8 bits, each segment decoded speculatively from all 8 start offsets, the
+ * true entries resolved by following the exit offsets from bit 16, then each
+ * segment emitted at its running symbol count.  Arguments, layout, rules and
+ * output as ecco_decode, and the same output bit for bit; it does about 16
+ * times the table look-ups per block, so ecco_decode is the one to use. */
+int ecco_decode_speculative(const void* blocks_dev, uint64_t n_rows, uint64_t groups_per_row,
+                            uint64_t blk_row_stride_blocks, uint64_t y_row_stride_elems,
+                            const void* tables_dev, float tensor_scale, uint16_t* y_dev, void* stream);
+
 /* One tensor of an ecco_decode_many call: the arguments of ecco_decode. */
 typedef struct {
   const void* blocks_dev;

@@ -125,6 +125,9 @@ def test_device_entry_points_check_arguments_before_touching_the_device():
     assert L.ecco_encode(A, 1, 1, 128, 1, A, 1.0, A + 16, None, None) == -2
     assert L.ecco_decode(A, 1, 1, 1, 128, A + 64, 1.0, A, None) == -2
     assert L.ecco_decode(A, 2, 4, 3, 512, A, 1.0, A, None) == -3                 # row stride < groups
+    assert L.ecco_decode_speculative(A, 1, 1, 1, 128, A + 64, 1.0, A, None) == -2
+    assert L.ecco_decode_speculative(A, 2, 4, 3, 512, A, 1.0, A, None) == -3
+    assert L.ecco_decode_speculative(None, 1, 1, 1, 128, A, 1.0, A, None) == -1
     assert L.ecco_decode_gemv(A, A, 1.0, 16, 100, A, 1, A, None) == -3          # in % 128
     assert L.ecco_decode_gemv(A, A, 1.0, 16, 128, A, 9, A, None) == -3          # batch > 8
     assert L.ecco_amax(A, 0, A, None) == -3
