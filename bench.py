@@ -11,16 +11,17 @@ ecco_train_patterns from a separate seeded 2**20-value sample of the same
 recipe (offline, outside the timed region).
 
 One step runs every row of the hot path over the whole layer, inputs resident
-in HBM: per matrix ecco_amax and ecco_encode, one ecco_decode_many launch that
-decodes all seven matrices (each with its own tables and scale), and the fused
+in HBM: one ecco_amax_many call over the seven matrices, per matrix
+ecco_encode, one ecco_decode_many launch that decodes all seven matrices (each
+with its own tables and scale), and the fused
 decode+GEMV at batch 1 as a decode step issues it: ecco_decode_gemv_many over
 q, k, v (same x), then o, then gate and up (same x), then down.  Each launch is bracketed by HIP events on the stream it
 runs on.  The reported value is decode throughput -- (64 B compressed in +
 256 B FP16 out) per group over the summed decode kernel time of the timed
 steps; encode (256 B in + 64 B out per group) and the fused GEMV are reported
 beside it, and so are each matrix decoded by an ecco_decode launch of its own,
-the same by ecco_decode_speculative (the pages' segment-parallel decode), and
-each GEMV issued by a call of its own.
+the same by ecco_decode_speculative (the pages' segment-parallel decode), each
+GEMV issued by a call of its own and each amax by an ecco_amax call of its own.
 
 Other workloads (run separately, same JSON line shape):
   kv     K and V caches [16, 8, 8192, 128]: append-encode of the last 256
@@ -230,9 +231,10 @@ def bench_layer(args, torch, ecco, W):
                  for grp in gemv_groups]
     timer = Timer(torch, stream)
 
+    amax_jobs = [(m["w"], m["w"].numel(), m["amax"]) for m in mats.values()]
+
     def step():
-        for m in mats.values():
-            timer.run("amax", lambda: ecco.ecco_amax(m["w"], m["w"].numel(), m["amax"]))
+        timer.run("amax", lambda: ecco.ecco_amax_many(amax_jobs))
         for m in mats.values():
             timer.run("encode", lambda: ecco.ecco_encode(m["w"], m["out_f"], m["gpr"], m["in_f"], m["gpr"],
                                                          m["tdev"], m["t"], m["blocks"]))
@@ -263,6 +265,10 @@ def bench_layer(args, torch, ecco, W):
         for m in mats.values():
             timer.run("decode_spec", lambda: ecco.ecco_decode_speculative(m["blocks"], m["out_f"], m["gpr"], m["gpr"],
                                                                           m["in_f"], m["tdev"], m["t"], m["y"]))
+    # each amax by a call of its own
+    for _ in range(3):
+        for m in mats.values():
+            timer.run("amax_single", lambda: ecco.ecco_amax(m["w"], m["w"].numel(), m["amax"]))
     # and each GEMV by a launch of its own
     for _ in range(3):
         for m in mats.values():
@@ -281,6 +287,7 @@ def bench_layer(args, torch, ecco, W):
         decode_us_per_layer=dec_t / args.steps * 1e6,
         gemv_b1_us_per_layer=sum(ph["gemv"]) / args.steps * 1e6,
         amax_us_per_layer=sum(ph["amax"]) / args.steps * 1e6,
+        amax_separate_us_per_layer=sum(diag["amax_single"]) / 3 * 1e6,
         per_matrix_decode_us={nm: float(np.mean(single[i::len(mats)]) * 1e6) for i, nm in enumerate(mats)},
         gemv_separate_us_per_layer=sum(diag["gemv_single"]) / 3 * 1e6,
         spec_decode_us_per_layer=sum(diag["decode_spec"]) / 3 * 1e6,
@@ -324,8 +331,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": "llama3-8b-layer (q,k,v,o,gate,up,down; 1,703,936 groups)",
                    "groups": res["groups"],
-                   "step": "per matrix amax and encode; the 7 matrices decoded in one launch; fused "
-                           "decode+GEMV at b=1 in four calls (q+k+v, o, gate+up, down)",
+                   "step": "amax of the 7 matrices in one call; per matrix encode; the 7 matrices decoded "
+                           "in one launch; fused decode+GEMV at b=1 in four calls (q+k+v, o, gate+up, down)",
                    "tables": "ecco_train_patterns on seeded 2^20-value samples"},
         "encode_GBps": round(res["encode_GBps"], 1),
         "decode_frac_of_hbm_peak": round(res["decode_GBps"] / HBM_PEAK_GBPS, 4),
@@ -335,6 +342,8 @@ def main():
         "gemv_b1_us_per_layer": round(res["gemv_b1_us_per_layer"], 2),
         "gemv_b1_us_per_layer_one_call_per_matrix": round(res["gemv_separate_us_per_layer"], 2),
         "amax_us_per_layer": round(res["amax_us_per_layer"], 2),
+        "amax_us_per_layer_one_call_per_matrix": round(res["amax_separate_us_per_layer"], 2),
+        "amax_GBps": round(res["groups"] * 256 / (res["amax_us_per_layer"] * 1e-6) / 1e9, 1),
         "decode_us_per_matrix_separate_launches": {k: round(v, 2) for k, v in res["per_matrix_decode_us"].items()},
         "speculative_decode_us_per_layer": round(res["spec_decode_us_per_layer"], 2),
         "speculative_decode_GBps": round(res["groups"] * BYTES_PER_GROUP / (res["spec_decode_us_per_layer"] * 1e-6) / 1e9,

@@ -18,12 +18,12 @@ import numpy as np
 __all__ = [
     "EccoError", "lib", "library_path",
     "ecco_tables_size", "ecco_tables_build", "ecco_tables_validate", "ecco_tables_get",
-    "ecco_train_patterns", "ecco_tensor_scale_from_amax", "ecco_amax", "ecco_encode",
+    "ecco_train_patterns", "ecco_tensor_scale_from_amax", "ecco_amax", "ecco_amax_many", "ecco_encode",
     "ecco_decode", "ecco_decode_speculative", "ecco_encode_many", "ecco_encode_act", "ecco_decode_act",
     "ecco_decode_many",
     "ecco_decode_gemv", "ecco_decode_gemv_many", "ecco_attention_workspace_size",
     "ecco_attention_decode", "ecco_strerror", "ecco_version",
-    "STATS_FIELDS", "DECODE_MAX_JOBS", "GEMV_MAX_JOBS", "tables_to_device",
+    "STATS_FIELDS", "DECODE_MAX_JOBS", "GEMV_MAX_JOBS", "AMAX_MAX_JOBS", "tables_to_device",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -52,6 +52,12 @@ class TrainOpts(ctypes.Structure):
 
 DECODE_MAX_JOBS = 16
 GEMV_MAX_JOBS = 16
+AMAX_MAX_JOBS = 16
+
+
+class AmaxJob(ctypes.Structure):
+    """ecco_amax_job_t."""
+    _fields_ = [("x_dev", ctypes.c_void_p), ("n_values", ctypes.c_uint64), ("amax_dev", ctypes.c_void_p)]
 
 
 class DecodeJob(ctypes.Structure):
@@ -96,6 +102,7 @@ def lib():
             "ecco_train_patterns": (i32, [vp, u64, vp, vp]),
             "ecco_tensor_scale_from_amax": (f32, [f32]),
             "ecco_amax": (i32, [vp, u64, vp, vp]),
+            "ecco_amax_many": (i32, [vp, ctypes.c_uint32, vp]),
             "ecco_encode": (i32, [vp, u64, u64, u64, u64, vp, f32, vp, vp, vp]),
             "ecco_decode": (i32, [vp, u64, u64, u64, u64, vp, f32, vp, vp]),
             "ecco_decode_speculative": (i32, [vp, u64, u64, u64, u64, vp, f32, vp, vp]),
@@ -226,6 +233,15 @@ def tables_to_device(blob, device="cuda"):
 
 def ecco_amax(x, n_values, amax_out, stream=None):
     _check(lib().ecco_amax(_dptr(x), int(n_values), _dptr(amax_out), _stream(stream)), "ecco_amax")
+
+
+def ecco_amax_many(jobs, stream=None):
+    """jobs: a sequence of (x, n_values, amax_out) tuples -- the arguments of
+    ecco_amax, one per tensor -- reduced in one launch."""
+    arr = (AmaxJob * max(1, len(jobs)))()
+    for i, (x, n_values, amax_out) in enumerate(jobs):
+        arr[i] = AmaxJob(_dptr(x), int(n_values), _dptr(amax_out))
+    _check(lib().ecco_amax_many(ctypes.cast(arr, ctypes.c_void_p), len(jobs), _stream(stream)), "ecco_amax_many")
 
 
 def ecco_encode(x, n_rows, groups_per_row, x_row_stride_elems, blk_row_stride_blocks, tables_dev,

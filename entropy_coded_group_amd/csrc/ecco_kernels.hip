@@ -59,6 +59,7 @@ struct DecodeJob {
 };
 
 constexpr int kMaxJobs = ECCO_DECODE_MAX_JOBS;
+static_assert(ECCO_AMAX_MAX_JOBS == kMaxJobs && kMaxJobs <= 64, "amax jobs: one array size, outputs zeroed by one wave");
 
 struct DecodeArgs {
   DecodeJob job[kMaxJobs];
@@ -449,9 +450,26 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(EncodeArgs args)
 
 // ---------------------------------------------------------------------- amax
 
-__global__ void amax_init_kernel(float* out) { *out = 0.0f; }
+// One tensor of a launch; its workgroups are wg_first .. wg_first + wg_count - 1.
+struct AmaxJob {
+  const uint16_t* x;
+  uint64_t n;
+  float* out;
+  uint32_t wg_first, wg_count;
+};
 
-constexpr int kAmaxUnroll = 8;   // 16-byte loads in flight per thread
+struct AmaxArgs {
+  AmaxJob job[kMaxJobs];
+  uint32_t n_jobs;
+};
+
+__global__ void amax_init_kernel(AmaxArgs a) {
+  if (threadIdx.x < a.n_jobs) *a.job[threadIdx.x].out = 0.0f;
+}
+
+constexpr int kAmaxUnroll = 16;      // 16-byte loads in flight per thread
+constexpr uint32_t kAmaxThreads = 256;
+constexpr uint32_t kAmaxWgPerCu = 2;
 
 __device__ __forceinline__ uint32_t abs_max_bits(uint32_t m, uint32_t w) {
   uint32_t a0 = w & 0x7fffu, a1 = (w >> 16) & 0x7fffu;
@@ -460,14 +478,18 @@ __device__ __forceinline__ uint32_t abs_max_bits(uint32_t m, uint32_t w) {
   return max(m, max(a0, a1));
 }
 
-__global__ __launch_bounds__(256) void amax_kernel(const uint16_t* x, uint64_t n, float* out) {
+__global__ __launch_bounds__(kAmaxThreads) void amax_kernel(AmaxArgs args) {
+  uint32_t jj = 0;
+  while (jj + 1 < args.n_jobs && blockIdx.x >= args.job[jj + 1].wg_first) ++jj;
+  const AmaxJob a = args.job[jj];
   // |x| bit patterns of finite FP16 values order like the values (NaN ignored)
-  __shared__ uint32_t red[4];
+  __shared__ uint32_t red[kAmaxThreads / 64];
   uint32_t m = 0;
-  const uint4* x4 = reinterpret_cast<const uint4*>(x);
-  const uint64_t n8 = n / 8;
-  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
-  uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const uint4* x4 = reinterpret_cast<const uint4*>(a.x);
+  const uint64_t n8 = a.n / 8;
+  const uint64_t stride = (uint64_t)a.wg_count * kAmaxThreads;
+  const uint64_t first = (uint64_t)(blockIdx.x - a.wg_first) * kAmaxThreads + threadIdx.x;
+  uint64_t i = first;
   // several independent loads per thread before any is used
   for (; i + (kAmaxUnroll - 1) * stride < n8; i += kAmaxUnroll * stride) {
     uint4 v[kAmaxUnroll];
@@ -486,8 +508,7 @@ __global__ __launch_bounds__(256) void amax_kernel(const uint16_t* x, uint64_t n
     m = abs_max_bits(abs_max_bits(m, v.x), v.y);
     m = abs_max_bits(abs_max_bits(m, v.z), v.w);
   }
-  for (uint64_t k = n8 * 8 + (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; k < n; k += stride)
-    m = abs_max_bits(m, x[k]);
+  for (uint64_t k = n8 * 8 + first; k < a.n; k += stride) m = abs_max_bits(m, a.x[k]);
   // wave, then workgroup reduction: one atomic per workgroup
   for (int o = 32; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
   if (lane_id() == 0) red[threadIdx.x >> 6] = m;
@@ -496,7 +517,7 @@ __global__ __launch_bounds__(256) void amax_kernel(const uint16_t* x, uint64_t n
     m = max(max(red[0], red[1]), max(red[2], red[3]));
     // the result only grows, so a workgroup whose maximum does not exceed a
     // value already read from it has nothing to add (saves most atomics)
-    unsigned int* o = reinterpret_cast<unsigned int*>(out);
+    unsigned int* o = reinterpret_cast<unsigned int*>(a.out);
     const uint32_t mb = __float_as_uint(f16_value(m));
     if (m && mb > __hip_atomic_load(o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) atomicMax(o, mb);
   }
@@ -536,19 +557,69 @@ int check_gfx950(int* cus) {
 }
 }  // namespace ecco
 
-extern "C" int ecco_amax(const uint16_t* x, uint64_t n, float* amax, void* stream) {
+namespace {
+
+// Checks one amax job and fills its descriptor (all but the workgroup range).
+int make_amax_job(const uint16_t* x, uint64_t n, float* amax, AmaxJob* out) {
   if (!x || !amax) return ECCO_EINVAL;
   if (n == 0) return ECCO_ESIZE;
   if (!host_aligned(x, 16) || !host_aligned(amax, 4)) return ECCO_EALIGN;
-  int cus = 0, rc = check_gfx950(&cus);
-  if (rc) return rc;
+  out->x = x;
+  out->n = n;
+  out->out = amax;
+  return ECCO_OK;
+}
+
+// Zeroes the outputs, then reads every job in one launch: kAmaxWgPerCu
+// workgroups per CU shared out in proportion to the jobs' sizes (at least one
+// each, and no more than a job has 16-byte loads for).
+int launch_amax(AmaxArgs& args, int cus, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
+  uint64_t total = 0;
+  for (uint32_t k = 0; k < args.n_jobs; ++k) total += args.job[k].n;
+  const uint64_t budget = (uint64_t)cus * kAmaxWgPerCu;
+  uint32_t first = 0;
+  for (uint32_t k = 0; k < args.n_jobs; ++k) {
+    AmaxJob& j = args.job[k];
+    const uint64_t want = std::max<uint64_t>(1, (j.n / 8 + kAmaxThreads - 1) / kAmaxThreads);
+    // budget * n / total without overflow (budget < 2^20, n < 2^64)
+    const uint64_t share = (uint64_t)((unsigned __int128)budget * j.n / total);
+    j.wg_first = first;
+    j.wg_count = (uint32_t)std::min<uint64_t>(want, std::max<uint64_t>(1, share));
+    first += j.wg_count;
+  }
   (void)hipGetLastError();
-  hipLaunchKernelGGL(amax_init_kernel, dim3(1), dim3(1), 0, s, amax);
-  uint64_t want = (n / 8 + 255) / 256;
-  uint32_t grid = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(want, (uint64_t)cus * 2));
-  hipLaunchKernelGGL(amax_kernel, dim3(grid), dim3(256), 0, s, x, n, amax);
+  hipLaunchKernelGGL(amax_init_kernel, dim3(1), dim3(64), 0, s, args);
+  hipLaunchKernelGGL(amax_kernel, dim3(first), dim3(kAmaxThreads), 0, s, args);
   return launch_status();
+}
+
+}  // namespace
+
+extern "C" int ecco_amax(const uint16_t* x, uint64_t n, float* amax, void* stream) {
+  AmaxArgs args{};
+  args.n_jobs = 1;
+  int rc = make_amax_job(x, n, amax, &args.job[0]);
+  if (rc) return rc;
+  int cus = 0;
+  rc = check_gfx950(&cus);
+  if (rc) return rc;
+  return launch_amax(args, cus, stream);
+}
+
+extern "C" int ecco_amax_many(const ecco_amax_job_t* jobs, uint32_t n_jobs, void* stream) {
+  if (!jobs) return ECCO_EINVAL;
+  if (n_jobs == 0 || n_jobs > (uint32_t)kMaxJobs) return ECCO_ESIZE;
+  AmaxArgs args{};
+  args.n_jobs = n_jobs;
+  for (uint32_t k = 0; k < n_jobs; ++k) {
+    const int rc = make_amax_job(jobs[k].x_dev, jobs[k].n_values, jobs[k].amax_dev, &args.job[k]);
+    if (rc) return rc;
+  }
+  int cus = 0;
+  const int rc = check_gfx950(&cus);
+  if (rc) return rc;
+  return launch_amax(args, cus, stream);
 }
 
 namespace {

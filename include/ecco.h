@@ -104,6 +104,7 @@ extern "C" {
 #define ECCO_GEMV_MAX_BATCH 8
 #define ECCO_DECODE_MAX_JOBS 16
 #define ECCO_GEMV_MAX_JOBS 16
+#define ECCO_AMAX_MAX_JOBS 16
 
 enum {
   ECCO_OK = 0,
@@ -186,6 +187,24 @@ float ecco_tensor_scale_from_amax(float amax);
 
 /* amax_dev[0] = max |x| over n_values FP16 values (n_values >= 1; NaN ignored). */
 int ecco_amax(const uint16_t* x_dev, uint64_t n_values, float* amax_dev, void* stream);
+
+/* One tensor of an ecco_amax_many call: the arguments of ecco_amax. */
+typedef struct {
+  const uint16_t* x_dev;
+  uint64_t n_values;
+  float* amax_dev;
+} ecco_amax_job_t;
+
+/* The maxima of several tensors (the amax each per-tensor scale is derived
+ * from) in two launches in all -- one that zeroes the outputs and one that
+ * reads every tensor -- e.g. all matrices of a layer before they are
+ * encoded.  Each job follows the rules of ecco_amax; jobs_host (n_jobs in
+ * 1..ECCO_AMAX_MAX_JOBS) is read before the call returns.  If any job is
+ * invalid the call returns that job's error and enqueues nothing.  Jobs that
+ * name the same amax_dev leave there the maximum over all of them.  The
+ * workgroups are shared out in proportion to the jobs' sizes.  Results are
+ * identical to one ecco_amax call per job. */
+int ecco_amax_many(const ecco_amax_job_t* jobs_host, uint32_t n_jobs, void* stream);
 
 /* Encode n_rows x groups_per_row groups.  Group (r, g) is the 128 FP16
  * values at x_dev + r * x_row_stride_elems + g * 128; its block goes to

@@ -152,6 +152,24 @@ def test_device_entry_points_check_arguments_before_touching_the_device():
     ej[0].stats_dev = None
     ej[1].tensor_scale = 0.0
     assert L.ecco_encode_many(ep, 2, None) == -1
+    # ecco_amax_many: count, every job checked
+    aj = (ecco.AmaxJob * 3)()
+    for j in aj:
+        j.x_dev, j.n_values, j.amax_dev = A, 1000, A
+    ap = ctypes.cast(aj, ctypes.c_void_p)
+    assert L.ecco_amax_many(None, 1, None) == -1
+    assert L.ecco_amax_many(ap, 0, None) == -3
+    assert L.ecco_amax_many(ap, ecco.AMAX_MAX_JOBS + 1, None) == -3
+    aj[2].n_values = 0
+    assert L.ecco_amax_many(ap, 3, None) == -3
+    aj[2].n_values = 7
+    aj[1].x_dev = A + 2
+    assert L.ecco_amax_many(ap, 3, None) == -2
+    aj[1].x_dev = A
+    aj[0].amax_dev = A + 2
+    assert L.ecco_amax_many(ap, 3, None) == -2
+    aj[0].amax_dev = None
+    assert L.ecco_amax_many(ap, 3, None) == -1
     # ecco_decode_gemv_many: count, batch, reserved field, every job checked
     gj = (ecco.GemvJob * 3)()
     for j in gj:
@@ -219,6 +237,8 @@ def test_binding_refuses_host_memory_for_device_arguments():
         ecco.ecco_amax(host, 1024, 1 << 20)
     with pytest.raises(ValueError):
         ecco.ecco_amax(cpu, 1024, 1 << 20)
+    with pytest.raises(ValueError):
+        ecco.ecco_amax_many([(1 << 20, 1024, 1 << 20), (cpu, 1024, 1 << 20)])
     with pytest.raises(ValueError):
         ecco.ecco_decode(1 << 20, 1, 8, 8, 1024, 1 << 20, 1.0, cpu)
     with pytest.raises(ValueError):

@@ -139,6 +139,39 @@ def test_amax_and_tensor_scale(dev):
         assert out.item() == np.max(np.abs(y.astype(np.float32))), n
 
 
+def test_amax_many_matches_one_call_per_tensor(dev):
+    """ecco_amax_many: sixteen tensors of ragged sizes (1 value to 2^20 + 3)
+    in one call, outputs pre-filled with garbage, one tensor with NaNs (ignored)
+    and one whose extreme is negative; then a second, smaller call in which two
+    jobs share an output (it gets the maximum over both)."""
+    say("amax_many 16 jobs")
+    rng = np.random.default_rng(41)
+    sizes = [1, 7, 8, 9, 1000, 4099, 65536, 1 << 20, (1 << 20) + 3, 12345, 777, 3, 2048, 100003, 64, 5]
+    xs = []
+    for k, n in enumerate(sizes):
+        y = (rng.standard_normal(n) * 10.0 ** rng.uniform(-3, 2)).astype(np.float16)
+        if k == 4:
+            y[[3, 500]] = np.float16("nan")
+        if k == 5:
+            y[77] = -np.abs(y).max() * 2
+        xs.append(y)
+    xd = [torch.from_numpy(y).cuda() for y in xs]
+    out = torch.full((16,), 1e30, dtype=torch.float32, device="cuda")
+    ecco.ecco_amax_many([(xd[k], sizes[k], out[k:k + 1]) for k in range(16)])
+    one = torch.full((16,), -1.0, dtype=torch.float32, device="cuda")
+    for k in range(16):
+        ecco.ecco_amax(xd[k], sizes[k], one[k:k + 1])
+    torch.cuda.synchronize()
+    ref = np.array([np.nanmax(np.abs(y.astype(np.float32))) for y in xs], np.float32)
+    assert np.array_equal(out.cpu().numpy(), ref)
+    assert np.array_equal(one.cpu().numpy(), ref)
+    # second call: fewer jobs, jobs 0 and 2 share out[0]
+    out2 = torch.full((2,), 1e30, dtype=torch.float32, device="cuda")
+    ecco.ecco_amax_many([(xd[7], sizes[7], out2[0:1]), (xd[9], sizes[9], out2[1:2]), (xd[13], sizes[13], out2[0:1])])
+    torch.cuda.synchronize()
+    assert out2[0].item() == max(ref[7], ref[13]) and out2[1].item() == ref[9]
+
+
 def test_c1_encode_decode_bitexact(dev):
     tb = golden("c1")
     tdev = dev_tables(tb)
