@@ -11,9 +11,9 @@ ecco_train_patterns from a separate seeded 2**20-value sample of the same
 recipe (offline, outside the timed region).
 
 One step runs every row of the hot path over the whole layer, inputs resident
-in HBM: one ecco_amax_many call over the seven matrices, per matrix
-ecco_encode, one ecco_decode_many launch that decodes all seven matrices (each
-with its own tables and scale), and the fused
+in HBM: one ecco_amax_many call over the seven matrices, one ecco_encode_many
+launch that encodes them, one ecco_decode_many launch that decodes them (each
+matrix with its own tables and scale), and the fused
 decode+GEMV at batch 1 as a decode step issues it: ecco_decode_gemv_many over
 q, k, v (same x), then o, then gate and up (same x), then down.  Each launch is bracketed by HIP events on the stream it
 runs on.  The reported value is decode throughput -- (64 B compressed in +
@@ -21,7 +21,7 @@ runs on.  The reported value is decode throughput -- (64 B compressed in +
 steps; encode (256 B in + 64 B out per group) and the fused GEMV are reported
 beside it, and so are each matrix decoded by an ecco_decode launch of its own,
 the same by ecco_decode_speculative (the pages' segment-parallel decode), each
-GEMV issued by a call of its own and each amax by an ecco_amax call of its own.
+GEMV, amax and encode issued by a call of its own.
 
 Other workloads (run separately, same JSON line shape):
   kv     K and V caches [16, 8, 8192, 128]: append-encode of the last 256
@@ -233,11 +233,12 @@ def bench_layer(args, torch, ecco, W):
 
     amax_jobs = [(m["w"], m["w"].numel(), m["amax"]) for m in mats.values()]
 
+    encode_jobs = [(m["w"], m["out_f"], m["gpr"], m["in_f"], m["gpr"], m["tdev"], m["t"], m["blocks"], None)
+                   for m in mats.values()]
+
     def step():
         timer.run("amax", lambda: ecco.ecco_amax_many(amax_jobs))
-        for m in mats.values():
-            timer.run("encode", lambda: ecco.ecco_encode(m["w"], m["out_f"], m["gpr"], m["in_f"], m["gpr"],
-                                                         m["tdev"], m["t"], m["blocks"]))
+        timer.run("encode", lambda: ecco.ecco_encode_many(encode_jobs))
         timer.run("decode", lambda: ecco.ecco_decode_many(decode_jobs))
         for jobs in gemv_jobs:
             timer.run("gemv", lambda: ecco.ecco_decode_gemv_many(jobs, 1))
@@ -265,6 +266,11 @@ def bench_layer(args, torch, ecco, W):
         for m in mats.values():
             timer.run("decode_spec", lambda: ecco.ecco_decode_speculative(m["blocks"], m["out_f"], m["gpr"], m["gpr"],
                                                                           m["in_f"], m["tdev"], m["t"], m["y"]))
+    # each encode by a call of its own
+    for _ in range(3):
+        for m in mats.values():
+            timer.run("encode_single", lambda: ecco.ecco_encode(m["w"], m["out_f"], m["gpr"], m["in_f"], m["gpr"],
+                                                                m["tdev"], m["t"], m["blocks"]))
     # each amax by a call of its own
     for _ in range(3):
         for m in mats.values():
@@ -288,6 +294,7 @@ def bench_layer(args, torch, ecco, W):
         gemv_b1_us_per_layer=sum(ph["gemv"]) / args.steps * 1e6,
         amax_us_per_layer=sum(ph["amax"]) / args.steps * 1e6,
         amax_separate_us_per_layer=sum(diag["amax_single"]) / 3 * 1e6,
+        encode_separate_us_per_layer=sum(diag["encode_single"]) / 3 * 1e6,
         per_matrix_decode_us={nm: float(np.mean(single[i::len(mats)]) * 1e6) for i, nm in enumerate(mats)},
         gemv_separate_us_per_layer=sum(diag["gemv_single"]) / 3 * 1e6,
         spec_decode_us_per_layer=sum(diag["decode_spec"]) / 3 * 1e6,
@@ -331,14 +338,15 @@ def main():
         "data": "synthetic",
         "config": {"workload": "llama3-8b-layer (q,k,v,o,gate,up,down; 1,703,936 groups)",
                    "groups": res["groups"],
-                   "step": "amax of the 7 matrices in one call; per matrix encode; the 7 matrices decoded "
-                           "in one launch; fused decode+GEMV at b=1 in four calls (q+k+v, o, gate+up, down)",
+                   "step": "the 7 matrices' amax in one call, encoded in one launch and decoded in one "
+                           "launch; fused decode+GEMV at b=1 in four calls (q+k+v, o, gate+up, down)",
                    "tables": "ecco_train_patterns on seeded 2^20-value samples"},
         "encode_GBps": round(res["encode_GBps"], 1),
         "decode_frac_of_hbm_peak": round(res["decode_GBps"] / HBM_PEAK_GBPS, 4),
         "encode_frac_of_hbm_peak": round(res["encode_GBps"] / HBM_PEAK_GBPS, 4),
         "decode_us_per_layer": round(res["decode_us_per_layer"], 2),
         "encode_us_per_layer": round(res["encode_us_per_layer"], 2),
+        "encode_us_per_layer_one_call_per_matrix": round(res["encode_separate_us_per_layer"], 2),
         "gemv_b1_us_per_layer": round(res["gemv_b1_us_per_layer"], 2),
         "gemv_b1_us_per_layer_one_call_per_matrix": round(res["gemv_separate_us_per_layer"], 2),
         "amax_us_per_layer": round(res["amax_us_per_layer"], 2),
