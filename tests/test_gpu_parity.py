@@ -454,31 +454,44 @@ def test_many_calls_at_the_job_limit(dev):
 
 
 def test_decode_many_full_layer_sampled(dev):
-    """All seven matrices of a LLaMA-3-8B layer decoded in one launch, each
-    with its own tables and scale (the layer workload's decode step)."""
-    jobs, checks = [], []
+    """The layer workload's step as the bench issues it: the seven matrices of
+    a LLaMA-3-8B layer reduced by one ecco_amax_many call, encoded by one
+    ecco_encode_many launch and decoded by one ecco_decode_many launch, each
+    with its own tables and scale; sampled groups against the oracle."""
+    ws, tbs, tdevs = {}, {}, {}
     for name in W.LAYER_ORDER:
-        tb = golden("c2_" + name)
-        tdev = dev_tables(tb)
-        say("layer %s generate + encode" % name)
-        w = W.c2_layer(0, names=[name])[name]
+        tbs[name] = golden("c2_" + name)
+        tdevs[name] = dev_tables(tbs[name])
+        say("layer %s generate" % name)
+        ws[name] = W.c2_layer(0, names=[name])[name]
+    wds = {name: ws[name].cuda() for name in W.LAYER_ORDER}
+    amax = torch.full((len(W.LAYER_ORDER),), -1.0, dtype=torch.float32, device="cuda")
+    say("layer amax_many")
+    ecco.ecco_amax_many([(wds[name], wds[name].numel(), amax[k:k + 1]) for k, name in enumerate(W.LAYER_ORDER)])
+    torch.cuda.synchronize()
+    enc_jobs, dec_jobs, checks = [], [], []
+    for k, name in enumerate(W.LAYER_ORDER):
+        w = ws[name]
         out_f, in_f = w.shape
         t = scale_of(w.numpy())
-        wd = w.cuda()
+        assert np.float32(ecco.ecco_tensor_scale_from_amax(amax[k].item())) == t, name
         bd = torch.empty((out_f, in_f // 128, 64), dtype=torch.uint8, device="cuda")
-        ecco.ecco_encode(wd, out_f, in_f // 128, in_f, in_f // 128, tdev, t, bd)
-        del wd
         yd = torch.empty((out_f, in_f), dtype=torch.int16, device="cuda")
-        jobs.append((bd, out_f, in_f // 128, in_f // 128, in_f, tdev, t, yd))
+        enc_jobs.append((wds[name], out_f, in_f // 128, in_f, in_f // 128, tdevs[name], t, bd, None))
+        dec_jobs.append((bd, out_f, in_f // 128, in_f // 128, in_f, tdevs[name], t, yd))
         G = out_f * in_f // 128
         idx = sample_index(G, 211)
-        checks.append((name, tb, t, idx, w.numpy().reshape(-1, 128)[idx], bd, yd))
+        checks.append((name, tbs[name], t, idx, w.numpy().reshape(-1, 128)[idx], bd, yd))
+    say("layer encode_many")
+    ecco.ecco_encode_many(enc_jobs)
+    torch.cuda.synchronize()
+    del enc_jobs, wds
     say("layer decode_many")
-    ecco.ecco_decode_many(jobs)
+    ecco.ecco_decode_many(dec_jobs)
     torch.cuda.synchronize()
     for name, tb, t, idx, xg, bd, yd in checks:
         ob = codec.encode_groups(xg, tb, t)
-        assert_blocks_equal(bd.cpu().numpy().reshape(-1, 64)[idx], ob, "layer %s encode (sampled)" % name)
+        assert_blocks_equal(bd.cpu().numpy().reshape(-1, 64)[idx], ob, "layer %s encode_many (sampled)" % name)
         assert_fp16_equal(yd.cpu().numpy().reshape(-1, 128)[idx].view(np.float16), codec.decode_blocks(ob, tb, t),
                           "layer %s decode_many (sampled)" % name)
 
