@@ -41,7 +41,8 @@ Other workloads (run separately, same JSON line shape):
 
 The CPU baseline is the oracle (NumPy) timed on a bounded sample of the same
 workload on this host: split over up to 16 worker processes (the reported
-value), and on one core in-process.
+value), and on one core in-process; beside it, the one-group-at-a-time oracle
+(plain Python) on the first 1,024 groups of that sample, on one core.
 """
 
 import argparse
@@ -144,6 +145,24 @@ def _oracle_chunk(job):
     t1 = time.perf_counter()
     codec.decode_blocks(blocks, tb, t)
     return t1 - t0, time.perf_counter() - t1
+
+
+def literal_baseline(x_groups, tables_blob, t, n_groups):
+    """The one-group-at-a-time oracle (plain Python loops) on the first
+    n_groups groups, one core, in this process."""
+    from oracle import literal
+    import entropy_coded_group_amd as ecco
+    c, l = ecco.ecco_tables_get(tables_blob)
+    x = x_groups[:n_groups]
+    t0 = time.perf_counter()
+    blocks = [literal.encode_group(g, c, l, t) for g in x]
+    t1 = time.perf_counter()
+    for b in blocks:
+        literal.decode_block(b, c, l, t)
+    t2 = time.perf_counter()
+    n = len(blocks)
+    return dict(groups=n, encode_GBps_1core=n * BYTES_PER_GROUP / (t1 - t0) / 1e9,
+                decode_GBps_1core=n * BYTES_PER_GROUP / (t2 - t1) / 1e9, seconds=t2 - t0)
 
 
 def cpu_model():
@@ -376,6 +395,11 @@ def main():
                                 "decode_GBps_1core": round(cb["decode_GBps_1core"], 5),
                                 "encode_GBps_1core": round(cb["encode_GBps_1core"], 5),
                                 "cpu": cpu_model(), "host_cpus": os.cpu_count()}
+        lit = literal_baseline(x0, blob0, t0, 1024)
+        line["cpu_baseline"]["literal_oracle_1core"] = {
+            "sample": "first %d groups of the q matrix, one group at a time in plain Python, %.1f s" % (
+                lit["groups"], lit["seconds"]),
+            "decode_GBps": round(lit["decode_GBps_1core"], 6), "encode_GBps": round(lit["encode_GBps_1core"], 6)}
     print(json.dumps(line))
 
 
