@@ -107,9 +107,9 @@ __device__ __forceinline__ void decode_job(DecodeSmem<kDecWaves>& sm, const Deco
     };
     const uint32_t n_valid = min(64u, a.n_groups - g0);
     if (n_valid == 64u)
-      decode_batch<true, kDecWaves, GS>(sm, wave, lane, 64u, a.t, cur, sink);
+      decode_batch<true, kDecWaves, GS, true>(sm, wave, lane, 64u, a.t, cur, sink);
     else
-      decode_batch<false, kDecWaves, GS>(sm, wave, lane, n_valid, a.t, cur, sink);
+      decode_batch<false, kDecWaves, GS, true>(sm, wave, lane, n_valid, a.t, cur, sink);
     cur = nxt;
   }
 }
