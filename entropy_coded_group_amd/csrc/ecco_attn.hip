@@ -101,9 +101,9 @@ __global__ __launch_bounds__(kScoreWaves * 64) void attn_scores_kernel(AttnArgs 
       }
     };
     if (n_valid == 64u)
-      decode_batch<true>(sm, wave, lane, 64u, a.kts, cur, sink);
+      decode_batch<true, kScoreWaves, 128, true>(sm, wave, lane, 64u, a.kts, cur, sink);
     else
-      decode_batch<false>(sm, wave, lane, n_valid, a.kts, cur, sink);
+      decode_batch<false, kScoreWaves, 128, true>(sm, wave, lane, n_valid, a.kts, cur, sink);
     cur = nxt;
   }
 }
@@ -211,9 +211,9 @@ __global__ __launch_bounds__(kPvWaves * 64) void attn_pv_kernel(AttnArgs a, uint
         }
       };
       if (n_valid == 64u)
-        decode_batch<true>(sm, wave, lane, 64u, a.vts, cur, sink);
+        decode_batch<true, kPvWaves, 128, true>(sm, wave, lane, 64u, a.vts, cur, sink);
       else
-        decode_batch<false>(sm, wave, lane, n_valid, a.vts, cur, sink);
+        decode_batch<false, kPvWaves, 128, true>(sm, wave, lane, n_valid, a.vts, cur, sink);
     }
     cur = nxt;
     if (half == 1u) {
