@@ -13,11 +13,34 @@ def _events(torch, n):
     return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
 
 
+_SLEEP_CYCLES_PER_US = []
+
+
+def _hold_stream(torch, us):
+    """Enqueue a spin kernel (torch.cuda._sleep) that keeps the stream busy for
+    about `us` microseconds, calibrated once."""
+    if not _SLEEP_CYCLES_PER_US:
+        a, b = _events(torch, 2)
+        torch.cuda.synchronize()
+        a.record()
+        torch.cuda._sleep(1 << 20)
+        b.record()
+        torch.cuda.synchronize()
+        _SLEEP_CYCLES_PER_US.append((1 << 20) / max(a.elapsed_time(b) * 1e3, 1.0))
+    torch.cuda._sleep(int(us * _SLEEP_CYCLES_PER_US[0]))
+
+
 def _timed(torch, fn, steps, warmup):
-    """Run fn() warmup + steps times; per-call HIP event durations (seconds)."""
+    """Run fn() warmup + steps times; per-call HIP event durations (seconds).
+    A spin kernel holds the stream while the host enqueues the timed calls
+    (allowing 200 us of host work per call), so each event pair brackets the
+    call's device work, not the Python binding's argument marshalling, which
+    for calls of a few tens of microseconds would otherwise leave the GPU
+    idle in between."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
+    _hold_stream(torch, 200.0 * steps)
     evs = []
     for _ in range(steps):
         a, b = _events(torch, 2)

@@ -138,10 +138,10 @@ __device__ __forceinline__ float wave_max_f32(float v) {
 // (half a row: the quad swaps and the half-row mirror stay inside it).
 template <int LPG>
 __device__ __forceinline__ uint32_t seg_max_u32(uint32_t v) {
-  static_assert(LPG == 8 || LPG == 16, "segment of 8 or 16 lanes");
+  static_assert(LPG == 4 || LPG == 8 || LPG == 16, "segment of 4, 8 or 16 lanes");
   v = max(v, dpp_u32<kQuadXor1>(v));
   v = max(v, dpp_u32<kQuadXor2>(v));
-  v = max(v, dpp_u32<kRowHalfMirror>(v));
+  if constexpr (LPG >= 8) v = max(v, dpp_u32<kRowHalfMirror>(v));
   if constexpr (LPG == 16) v = max(v, dpp_u32<kRowMirror>(v));
   return v;
 }
@@ -149,7 +149,7 @@ template <int LPG>
 __device__ __forceinline__ uint32_t seg_min_u32(uint32_t v) {
   v = min(v, dpp_u32<kQuadXor1>(v));
   v = min(v, dpp_u32<kQuadXor2>(v));
-  v = min(v, dpp_u32<kRowHalfMirror>(v));
+  if constexpr (LPG >= 8) v = min(v, dpp_u32<kRowHalfMirror>(v));
   if constexpr (LPG == 16) v = min(v, dpp_u32<kRowMirror>(v));
   return v;
 }
@@ -157,7 +157,7 @@ template <int LPG>
 __device__ __forceinline__ uint32_t seg_add_u32(uint32_t v) {
   v += dpp_u32<kQuadXor1>(v);
   v += dpp_u32<kQuadXor2>(v);
-  v += dpp_u32<kRowHalfMirror>(v);
+  if constexpr (LPG >= 8) v += dpp_u32<kRowHalfMirror>(v);
   if constexpr (LPG == 16) v += dpp_u32<kRowMirror>(v);
   return v;
 }
@@ -165,7 +165,7 @@ template <int LPG>
 __device__ __forceinline__ float seg_min_f32(float v) {
   v = fminf(v, dpp_f32<kQuadXor1>(v));
   v = fminf(v, dpp_f32<kQuadXor2>(v));
-  v = fminf(v, dpp_f32<kRowHalfMirror>(v));
+  if constexpr (LPG >= 8) v = fminf(v, dpp_f32<kRowHalfMirror>(v));
   if constexpr (LPG == 16) v = fminf(v, dpp_f32<kRowMirror>(v));
   return v;
 }
@@ -173,7 +173,7 @@ template <int LPG>
 __device__ __forceinline__ float seg_max_f32(float v) {
   v = fmaxf(v, dpp_f32<kQuadXor1>(v));
   v = fmaxf(v, dpp_f32<kQuadXor2>(v));
-  v = fmaxf(v, dpp_f32<kRowHalfMirror>(v));
+  if constexpr (LPG >= 8) v = fmaxf(v, dpp_f32<kRowHalfMirror>(v));
   if constexpr (LPG == 16) v = fmaxf(v, dpp_f32<kRowMirror>(v));
   return v;
 }
@@ -197,8 +197,10 @@ __device__ __forceinline__ uint32_t seg_scan_add(uint32_t v, uint32_t tl) {
     v += tl >= 1u ? u : 0u;
     u = dpp_u32<kRowShr2>(v);
     v += tl >= 2u ? u : 0u;
-    u = dpp_u32<kRowShr4>(v);
-    v += tl >= 4u ? u : 0u;
+    if constexpr (LPG == 8) {
+      u = dpp_u32<kRowShr4>(v);
+      v += tl >= 4u ? u : 0u;
+    }
     return v;
   }
 }

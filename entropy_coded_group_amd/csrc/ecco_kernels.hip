@@ -177,23 +177,32 @@ struct EncodeSmem {
   float c0c14[S * 2];
   uint32_t len4[S * A];
   uint16_t enc[S * H * A];
-  float thr[kEncWaves][8][16];
-  uint32_t out[kEncWaves][8][16];
+  float thr[kEncWaves][16][16];      // threshold tree of each group of a wave
+  uint32_t out[kEncWaves][16][16];    // block words of each group of a wave
 };
 
-// Eight values per lane: a group of GS values takes LPG = GS / 8 lanes (a DPP
-// row for 128, half a row for 64) and a wave encodes GPW = 64 / LPG groups at
-// a time.
+// Encoder lane layout: 16 values per lane, so a group takes LPG = GS / 16
+// lanes (8 for 128-value groups, 4 for 64) and a wave encodes GPW = 64 / LPG
+// groups at a time.  Work that every lane of a group repeats (scale,
+// reductions, outlier rounds) costs less per group the fewer lanes share it.
 template <int GS>
-__global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(EncodeArgs args) {
+struct EncGeom {
+  static constexpr int NV = 16;                   // values per lane
+  static constexpr int NL = NV / 8;               // 16-byte loads (8 values) per lane
+  static constexpr int LPG = GS / NV;             // lanes per group
+  static constexpr int GPW = 64 / LPG;            // groups per wave
+};
+
+template <int GS>
+__global__ __launch_bounds__(kEncWaves * 64, 4) void encode_kernel(EncodeArgs args) {
   uint32_t jj = 0;
   while (jj + 1 < args.n_jobs && blockIdx.x >= args.job[jj + 1].wg_first) ++jj;
   const EncodeJob a = args.job[jj];         // one copy, kept in scalar registers
   const uint32_t lw = blockIdx.x - a.wg_first;
   using Geo = GroupGeom<GS>;
-  constexpr int NV = 8;
-  constexpr int LPG = GS / NV;
-  constexpr int GPW = 64 / LPG;
+  using EG = EncGeom<GS>;
+  constexpr int NV = EG::NV, NL = EG::NL, LPG = EG::LPG, GPW = EG::GPW;
+  static_assert((LPG == 8 || LPG == 4) && GPW <= 16, "EncodeSmem holds 16 groups per wave");
   constexpr uint32_t RB = Geo::kRecBits;
   constexpr int NSLOT = 16 / LPG;           // outlier records (and thresholds) per lane
   __shared__ EncodeSmem sm;
@@ -216,27 +225,45 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(EncodeArgs args)
   // per-lane statistics (kept by lane tl == 0 of each group)
   uint64_t st_groups = 0, st_clip = 0, st_clipv = 0, st_pad = 0, st_fill = 0, st_nonfin = 0;
 
-  // the 8 values of group g (clamped to the last group) that lane tl holds
-  auto load_group = [&](uint32_t g) -> uint4 {
+  // the NV values of group g (clamped to the last group) that lane tl holds
+  struct Raw {
+    uint4 v[NL];
+  };
+  auto load_group = [&](uint32_t g) -> Raw {
     g = min(g, a.n_groups - 1u);
     const uint32_t row = div_magic(g, a.gpr), col = g - row * a.gpr.d;
-    return load_stream(a.x + (uint64_t)row * a.x_stride + (uint64_t)col * GS + NV * tl);
+    const uint16_t* src = a.x + (uint64_t)row * a.x_stride + (uint64_t)col * GS + NV * tl;
+    Raw r;
+#pragma unroll
+    for (int c = 0; c < NL; ++c) r.v[c] = load_stream(src + 8 * c);
+    return r;
   };
   const uint32_t ustride = a.wg_count * kEncWaves;
   uint32_t unit = lw * kEncWaves + wave;
-  uint4 raw = load_group(unit * GPW + q);
+  Raw raw = load_group(unit * GPW + q);
   for (; unit < a.n_units; unit += ustride) {
     const uint32_t gidx = unit * GPW + q;
     const bool valid = gidx < a.n_groups;
     // the next unit's input is loaded before this one is worked on
-    const uint4 nraw = load_group((unit + ustride) * GPW + q);
+    const Raw nraw = load_group((unit + ustride) * GPW + q);
     uint32_t row = 0, col = 0;
     if (valid) {
       row = div_magic(gidx, a.gpr);
       col = gidx - row * a.gpr.d;
     }
-    const uint32_t hb[8] = {raw.x & 0xffffu, raw.x >> 16, raw.y & 0xffffu, raw.y >> 16,
-                            raw.z & 0xffffu, raw.z >> 16, raw.w & 0xffffu, raw.w >> 16};
+    uint32_t hb[NV];
+#pragma unroll
+    for (int c = 0; c < NL; ++c) {
+      const uint4 w = raw.v[c];
+      hb[8 * c + 0] = w.x & 0xffffu;
+      hb[8 * c + 1] = w.x >> 16;
+      hb[8 * c + 2] = w.y & 0xffffu;
+      hb[8 * c + 3] = w.y >> 16;
+      hb[8 * c + 4] = w.z & 0xffffu;
+      hb[8 * c + 5] = w.z >> 16;
+      hb[8 * c + 6] = w.w & 0xffffu;
+      hb[8 * c + 7] = w.w >> 16;
+    }
     float xf[NV];
     uint32_t key[NV];
 #pragma unroll
@@ -256,15 +283,13 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(EncodeArgs args)
     const float aa = fabsf(S);
     // 2. min / max of the other GS - 1 values (the scale element, whose key
     //    is km, counts as +inf for the min and -inf for the max)
-    float lo[NV], hi[NV];
+    float mn = __builtin_inff(), mx = -__builtin_inff();
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const bool s = key[i] == km;
-      lo[i] = s ? __builtin_inff() : xf[i];
-      hi[i] = s ? -__builtin_inff() : xf[i];
+      mn = fminf(mn, s ? __builtin_inff() : xf[i]);
+      mx = fmaxf(mx, s ? -__builtin_inff() : xf[i]);
     }
-    float mn = fminf(fminf(fminf(lo[0], lo[1]), fminf(lo[2], lo[3])), fminf(fminf(lo[4], lo[5]), fminf(lo[6], lo[7])));
-    float mx = fmaxf(fmaxf(fmaxf(hi[0], hi[1]), fmaxf(hi[2], hi[3])), fmaxf(fmaxf(hi[4], hi[5]), fmaxf(hi[6], hi[7])));
     mn = seg_min_f32<LPG>(mn);
     mx = seg_max_f32<LPG>(mx);
     // 3. pattern: min/max squared error, lowest p on ties.  Each lane keeps its
@@ -300,7 +325,7 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(EncodeArgs args)
     wave_sync();
     const float root = thr[1];
     uint32_t sym[NV];
-    uint32_t l4 = 0;
+    uint32_t l4 = 0;                       // four byte counters (codebooks 0..3): at most 16 x 8
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       uint32_t u = xf[i] > root ? 3u : 2u;
@@ -317,32 +342,44 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(EncodeArgs args)
 #pragma unroll
     for (int h = 1; h < 4; ++h)
       if (Lh[h] < L) { L = Lh[h]; hstar = h; }
-    // 6. codewords: lane-local concatenation, segment scan for positions, OR
-    //    into the block
-    uint64_t acc = 0;
-    uint32_t off = 0;
-    uint32_t ends = 0;                     // codewords of this lane ending within the block (stats)
+    // 6. codewords: lane-local concatenation (each 8 values at most 64 bits),
+    //    segment scan for positions, OR into the block
+    uint64_t acc[NL];
+    uint32_t offs[NL];
     const uint32_t eb = (pstar * 4u + hstar) * 16u;
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const uint32_t e = sm.enc[eb + sym[i]];
-      acc |= (uint64_t)(e & 0xffu) << off;
-      off += e >> 8;
+    for (int c = 0; c < NL; ++c) {
+      acc[c] = 0;
+      offs[c] = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t e = sm.enc[eb + sym[8 * c + i]];
+        acc[c] |= (uint64_t)(e & 0xffu) << offs[c];
+        offs[c] += e >> 8;
+      }
     }
+    uint32_t off = 0;
+#pragma unroll
+    for (int c = 0; c < NL; ++c) off += offs[c];
 #pragma unroll
     for (int sl = 0; sl < NSLOT; ++sl) out[tl + LPG * sl] = 0;
     const uint32_t incl = seg_scan_add<LPG>(off, tl);
     const uint32_t pos = 16u + incl - off;
     wave_sync();
     {
-      // the lane's <= 64 bits land in words w, w + 1, w + 2; words past 15 are
-      // beyond bit 512 and dropped, which is exactly the clipping rule
-      const uint32_t w = pos >> 5, sh = pos & 31u;
-      const uint64_t low = acc << sh;
-      const uint32_t top = sh ? (uint32_t)(acc >> (64u - sh)) : 0u;
-      if (w < 16u && (uint32_t)low) atomicOr(&out[w], (uint32_t)low);
-      if (w + 1u < 16u && (uint32_t)(low >> 32)) atomicOr(&out[w + 1u], (uint32_t)(low >> 32));
-      if (w + 2u < 16u && top) atomicOr(&out[w + 2u], top);
+      // each part's <= 64 bits land in words w, w + 1, w + 2; words past 15
+      // are beyond bit 512 and dropped, which is exactly the clipping rule
+      uint32_t pp = pos;
+#pragma unroll
+      for (int c = 0; c < NL; ++c) {
+        const uint32_t w = pp >> 5, sh = pp & 31u;
+        const uint64_t low = acc[c] << sh;
+        const uint32_t top = sh ? (uint32_t)(acc[c] >> (64u - sh)) : 0u;
+        if (w < 16u && (uint32_t)low) atomicOr(&out[w], (uint32_t)low);
+        if (w + 1u < 16u && (uint32_t)(low >> 32)) atomicOr(&out[w + 1u], (uint32_t)(low >> 32));
+        if (w + 2u < 16u && top) atomicOr(&out[w + 2u], top);
+        pp += offs[c];
+      }
     }
     const bool clipped = 16u + L > 512u;
     const uint32_t n = clipped ? 0u : min(16u, (496u - L) / RB);
@@ -352,35 +389,47 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(EncodeArgs args)
     //    the group's largest remaining key (lane rr % LPG keeps round rr's in
     //    slot rr / LPG) and removes it, until no group of the wave needs
     //    another round.  For a few rounds the lane's keys are searched and
-    //    cleared in place; for more, each lane first sorts its 8 keys
+    //    cleared in place; for more, the lane first sorts each 8 of its keys
     //    (descending, 19 compare-exchanges) so that a round only compares the
-    //    lanes' heads and the owner of the largest shifts its list.
+    //    lists' heads and the owner of the largest shifts its list.
     uint32_t mykey[NSLOT];
 #pragma unroll
     for (int sl = 0; sl < NSLOT; ++sl) mykey[sl] = 0;
     if (__any(n > kOutlierSortRounds)) {
-      uint32_t k8[8];
+      uint32_t k8[NL][8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) k8[i] = key[i];
-      sort8_desc(k8);
-      auto pop = [&](bool own) {
+      for (int c = 0; c < NL; ++c) {
 #pragma unroll
-        for (int i = 0; i < 7; ++i) k8[i] = own ? k8[i + 1] : k8[i];
-        k8[7] = own ? 0u : k8[7];
+        for (int i = 0; i < 8; ++i) k8[c][i] = key[8 * c + i];
+        sort8_desc(k8[c]);
+      }
+      auto pop = [&](uint32_t m) {
+#pragma unroll
+        for (int c = 0; c < NL; ++c) {
+          const bool own = k8[c][0] == m;
+#pragma unroll
+          for (int i = 0; i < 7; ++i) k8[c][i] = own ? k8[c][i + 1] : k8[c][i];
+          k8[c][7] = own ? 0u : k8[c][7];
+        }
       };
-      pop(k8[0] == km);                    // the scale element heads one lane's list
+      pop(km);                             // the scale element heads one list
       for (uint32_t rr = 0;; ++rr) {
-        const uint32_t m = seg_max_u32<LPG>(k8[0]);
+        uint32_t head = k8[0][0];
+#pragma unroll
+        for (int c = 1; c < NL; ++c) head = max(head, k8[c][0]);
+        const uint32_t m = seg_max_u32<LPG>(head);
 #pragma unroll
         for (int sl = 0; sl < NSLOT; ++sl) mykey[sl] = rr == tl + LPG * sl ? m : mykey[sl];
         if (!__any(rr + 1u < n)) break;
-        pop(k8[0] == m);
+        pop(m);
       }
     } else if (__any(n > 0u)) {
 #pragma unroll
       for (int i = 0; i < NV; ++i) key[i] = key[i] == km ? 0u : key[i];
       for (uint32_t rr = 0;; ++rr) {
-        uint32_t m = max(max(max(key[0], key[1]), max(key[2], key[3])), max(max(key[4], key[5]), max(key[6], key[7])));
+        uint32_t m = key[0];
+#pragma unroll
+        for (int i = 1; i < NV; ++i) m = max(m, key[i]);
         m = seg_max_u32<LPG>(m);
 #pragma unroll
         for (int sl = 0; sl < NSLOT; ++sl) mykey[sl] = rr == tl + LPG * sl ? m : mykey[sl];
@@ -405,16 +454,18 @@ __global__ __launch_bounds__(kEncWaves * 64) void encode_kernel(EncodeArgs args)
     if (tl == 0) atomicOr(&out[0], pstar | (hstar << 6) | (s8 << 8));
     wave_sync();
     if (valid) {
+      // 16 words over LPG lanes: 16 / LPG each
       uint8_t* dst = a.blocks + ((uint64_t)row * a.blk_stride + col) * 64u;
-      if constexpr (LPG == 16) {
-        reinterpret_cast<uint32_t*>(dst)[tl] = out[tl];
-      } else {
+      if constexpr (LPG == 8) {
         reinterpret_cast<uint2*>(dst)[tl] = make_uint2(out[2u * tl], out[2u * tl + 1u]);
+      } else {
+        reinterpret_cast<uint4*>(dst)[tl] =
+            make_uint4(out[4u * tl], out[4u * tl + 1u], out[4u * tl + 2u], out[4u * tl + 3u]);
       }
     }
     if (a.stats) {
       // whole codewords inside the block (k of a clipped group)
-      uint32_t e = pos;
+      uint32_t e = pos, ends = 0;
 #pragma unroll
       for (int i = 0; i < NV; ++i) {
         e += sm.enc[eb + sym[i]] >> 8;
@@ -646,7 +697,7 @@ int make_encode_job(const uint16_t* x, uint64_t n_rows, uint64_t gpr, uint64_t x
   a.blk_stride = blk_stride;
   a.gpr = make_magic((uint32_t)gpr);
   a.n_groups = (uint32_t)total;
-  constexpr uint32_t kGroupsPerWave = 64 / (GS / 8);
+  constexpr uint32_t kGroupsPerWave = EncGeom<GS>::GPW;
   a.n_units = (uint32_t)((total + kGroupsPerWave - 1) / kGroupsPerWave);
   a.t = tensor_scale;
   volatile float inv = 1.0f / tensor_scale;
