@@ -21,7 +21,8 @@ runs on.  The reported value is decode throughput -- (64 B compressed in +
 steps; encode (256 B in + 64 B out per group) and the fused GEMV are reported
 beside it, and so are each matrix decoded by an ecco_decode launch of its own,
 the same by ecco_decode_speculative (the pages' segment-parallel decode), each
-GEMV, amax and encode issued by a call of its own.
+GEMV, amax and encode issued by a call of its own, and the whole step captured
+once into a HIP graph and replayed (step_us_hip_graph_replay).
 
 Other workloads (run separately, same JSON line shape):
   kv     K and V caches [16, 8, 8192, 128]: append-encode of the last 256
@@ -218,6 +219,38 @@ def train_tables(ecco, sample):
     return ecco.ecco_train_patterns(sample, threads=threads)
 
 
+def graph_step_us(torch, stream, amax_jobs, encode_jobs, decode_jobs, gemv_jobs, ecco, reps):
+    """The step's calls captured once into a HIP graph (torch.cuda.graph) and
+    replayed: the library allocates and synchronizes nothing, so the whole
+    step captures, and a replay has no per-call host work between kernels
+    (replays are checked bit for bit against the eager step in the tests).
+    Returns microseconds per replay."""
+    def plain_step():
+        ecco.ecco_amax_many(amax_jobs)
+        ecco.ecco_encode_many(encode_jobs)
+        ecco.ecco_decode_many(decode_jobs)
+        for jobs in gemv_jobs:
+            ecco.ecco_decode_gemv_many(jobs, 1)
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        plain_step()                       # warm-up on a side stream before capture
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        plain_step()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / reps
+
+
 def bench_layer(args, torch, ecco, W):
     stream = torch.cuda.current_stream()
     mats = {}
@@ -302,6 +335,7 @@ def bench_layer(args, torch, ecco, W):
     torch.cuda.synchronize()
     diag = timer.collect()
     single = diag["decode_single"]
+    graph_us = graph_step_us(torch, stream, amax_jobs, encode_jobs, decode_jobs, gemv_jobs, ecco, args.steps)
     res = dict(
         wall=wall, groups=groups,
         decode_GBps=groups * args.steps * BYTES_PER_GROUP / dec_t / 1e9,
@@ -317,6 +351,7 @@ def bench_layer(args, torch, ecco, W):
         per_matrix_decode_us={nm: float(np.mean(single[i::len(mats)]) * 1e6) for i, nm in enumerate(mats)},
         gemv_separate_us_per_layer=sum(diag["gemv_single"]) / 3 * 1e6,
         spec_decode_us_per_layer=sum(diag["decode_spec"]) / 3 * 1e6,
+        graph_step_us=graph_us,
     )
     x0 = mats["q"]["w"].cpu().numpy().reshape(-1, 128)
     return res, (x0, mats["q"]["blob"], mats["q"]["t"])
@@ -368,6 +403,7 @@ def main():
         "encode_us_per_layer_one_call_per_matrix": round(res["encode_separate_us_per_layer"], 2),
         "gemv_b1_us_per_layer": round(res["gemv_b1_us_per_layer"], 2),
         "gemv_b1_us_per_layer_one_call_per_matrix": round(res["gemv_separate_us_per_layer"], 2),
+        "step_us_hip_graph_replay": round(res["graph_step_us"], 2),
         "amax_us_per_layer": round(res["amax_us_per_layer"], 2),
         "amax_us_per_layer_one_call_per_matrix": round(res["amax_separate_us_per_layer"], 2),
         "amax_GBps": round(res["groups"] * 256 / (res["amax_us_per_layer"] * 1e-6) / 1e9, 1),
