@@ -22,12 +22,12 @@
 //           128-value block) are looked up in a per-block 32-entry FP16 table
 //           (15 centroids * a, the scale, outliers) and written with 128-bit
 //           stores, whole rows per store instruction.
-//   encode  eight values per lane, so sixteen lanes (one DPP row) per
-//           128-value group and four groups per wave (8 lanes and 8 groups for
-//           64-value groups): segment-wide max/min/argmin/sum/scan through
-//           DPP, LDS-resident thresholds for a branch-free binary search,
-//           codewords merged into the block with LDS atomic OR.
-//   amax    grid-stride max of |x|.
+//   encode  sixteen values per lane, so eight lanes (half a DPP row) per
+//           128-value group and eight groups per wave (4 lanes and 16 groups
+//           for 64-value groups): segment-wide max/min/argmin/sum/scan
+//           through DPP, LDS-resident thresholds for a branch-free binary
+//           search, codewords merged into the block with LDS atomic OR.
+//   amax    grid-stride max of |x| over up to 16 tensors in one launch.
 // All floating-point steps that decide a bit of the output are single IEEE
 // binary32 operations (the library is built with -ffp-contract=off).
 #include <hip/hip_runtime.h>
