@@ -654,7 +654,18 @@ def test_beyond_2_pow_32_elements_strided_sampled(dev):
     # the gaps between rows are untouched
     assert int(blocks[gpr].min()) == 0xAB and int(blocks[2 * bs - 1].min()) == 0xAB
     assert torch.all(y[gpr * 128:xs] == 0x7FFF) and torch.all(y[xs + gpr * 128:] == 0x7FFF)
-    del x, y, blocks
+    del y, blocks
+    # amax over more than 2^32 values: the largest |x| planted past element
+    # 2^32, a smaller one in the first half
+    say("2^32: amax")
+    x[2 * xs - 5] = 60000.0
+    x[3] = -59008.0
+    out = torch.full((3,), -1.0, dtype=torch.float32, device="cuda")
+    ecco.ecco_amax(x, 2 * xs, out[0:1])
+    ecco.ecco_amax_many([(x, xs, out[1:2]), (x[xs:], xs, out[2:3])])
+    torch.cuda.synchronize()
+    assert out.cpu().tolist() == [60000.0, 59008.0, 60000.0]
+    del x
     torch.cuda.empty_cache()
 
 
