@@ -706,20 +706,30 @@ int make_encode_job(const uint16_t* x, uint64_t n_rows, uint64_t gpr, uint64_t x
   return ECCO_OK;
 }
 
-// Up to 8 workgroups of kEncWaves waves per CU, no more than a job has units
-// for; split among the jobs one each, then each further workgroup to the job
-// whose workgroups carry the most units.
+// Up to 16 workgroups of kEncWaves waves per CU (four are resident at a time;
+// the later ones even out the tail), no more than a job has units for: each
+// job gets its share of the grid in proportion to its units (at least one
+// workgroup), and the few workgroups the rounding leaves go one by one to the
+// job whose workgroups carry the most units.
 void assign_encode_workgroups(EncodeArgs& args, uint32_t cus) {
-  uint64_t want = 0;
-  for (uint32_t j = 0; j < args.n_jobs; ++j) want += (args.job[j].n_units + kEncWaves - 1) / kEncWaves;
-  const uint32_t grid = (uint32_t)std::max<uint64_t>(args.n_jobs, std::min<uint64_t>(want, (uint64_t)cus * 8));
-  for (uint32_t j = 0; j < args.n_jobs; ++j) args.job[j].wg_count = 1;
-  for (uint32_t k = args.n_jobs; k < grid; ++k) {
+  uint64_t want[kMaxJobs], total = 0;
+  for (uint32_t j = 0; j < args.n_jobs; ++j) {
+    want[j] = (args.job[j].n_units + kEncWaves - 1) / kEncWaves;
+    total += want[j];
+  }
+  const uint64_t grid = std::max<uint64_t>(args.n_jobs, std::min<uint64_t>(total, (uint64_t)cus * 16));
+  uint64_t used = 0;
+  for (uint32_t j = 0; j < args.n_jobs; ++j) {
+    const uint64_t share = (uint64_t)((unsigned __int128)grid * want[j] / total);
+    args.job[j].wg_count = (uint32_t)std::min<uint64_t>(want[j], std::max<uint64_t>(1, share));
+    used += args.job[j].wg_count;
+  }
+  for (; used < grid; ++used) {
     uint32_t best = 0;
     uint64_t best_load = 0;
     for (uint32_t j = 0; j < args.n_jobs; ++j) {
       const EncodeJob& a = args.job[j];
-      if ((uint64_t)a.wg_count * kEncWaves >= a.n_units) continue;
+      if (a.wg_count >= want[j]) continue;
       const uint64_t load = (a.n_units + a.wg_count - 1) / a.wg_count;
       if (load > best_load) best_load = load, best = j;
     }
