@@ -193,6 +193,8 @@ struct EncGeom {
   static constexpr int GPW = 64 / LPG;            // groups per wave
 };
 
+// (At least four waves per SIMD: the compiler is held to 128 VGPRs, which the
+// kernel fits without spilling; left to itself it takes 135 and three waves.)
 template <int GS>
 __global__ __launch_bounds__(kEncWaves * 64, 4) void encode_kernel(EncodeArgs args) {
   uint32_t jj = 0;
