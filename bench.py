@@ -335,7 +335,11 @@ def bench_layer(args, torch, ecco, W):
     torch.cuda.synchronize()
     diag = timer.collect()
     single = diag["decode_single"]
-    graph_us = graph_step_us(torch, stream, amax_jobs, encode_jobs, decode_jobs, gemv_jobs, ecco, args.steps)
+    try:
+        graph_us = graph_step_us(torch, stream, amax_jobs, encode_jobs, decode_jobs, gemv_jobs, ecco, args.steps)
+    except Exception as e:                     # a diagnostic: the bench line stands without it
+        print("bench.py: HIP graph replay not measured: %r" % (e,), file=sys.stderr)
+        graph_us = None
     res = dict(
         wall=wall, groups=groups,
         decode_GBps=groups * args.steps * BYTES_PER_GROUP / dec_t / 1e9,
@@ -403,7 +407,7 @@ def main():
         "encode_us_per_layer_one_call_per_matrix": round(res["encode_separate_us_per_layer"], 2),
         "gemv_b1_us_per_layer": round(res["gemv_b1_us_per_layer"], 2),
         "gemv_b1_us_per_layer_one_call_per_matrix": round(res["gemv_separate_us_per_layer"], 2),
-        "step_us_hip_graph_replay": round(res["graph_step_us"], 2),
+        "step_us_hip_graph_replay": None if res["graph_step_us"] is None else round(res["graph_step_us"], 2),
         "amax_us_per_layer": round(res["amax_us_per_layer"], 2),
         "amax_us_per_layer_one_call_per_matrix": round(res["amax_separate_us_per_layer"], 2),
         "amax_GBps": round(res["groups"] * 256 / (res["amax_us_per_layer"] * 1e-6) / 1e9, 1),
