@@ -81,7 +81,7 @@ __global__ __launch_bounds__(kScoreWaves * 64) void attn_scores_kernel(AttnArgs 
 #pragma unroll
     for (int g = 0; g < G; ++g) qv[g] = *reinterpret_cast<const uint4*>(a.q + ((uint64_t)pair * G + g) * 128u + j0);
     float* sp = a.probs + ((uint64_t)pair * a.S + t0) * G;
-    auto sink = [&](uint32_t b, uint32_t, uint4 w, uint32_t) {
+    auto sink = [&](uint32_t b, uint32_t, uint4 w, uint32_t, uint32_t) {
       float d[G];
 #pragma unroll
       for (int g = 0; g < G; ++g) d[g] = row_sum_f32(dot8(w, qv[g], 0.0f)) * a.scale;
@@ -198,7 +198,7 @@ __global__ __launch_bounds__(kPvWaves * 64) void attn_pv_kernel(AttnArgs a, uint
     if (t0 < a.S) {
       const uint32_t n_valid = min(64u, a.S - t0);
       const float* pp = a.probs + ((uint64_t)pair * a.S + t0) * a.G + g_off;
-      auto sink = [&](uint32_t b, uint32_t, uint4 w, uint32_t) {
+      auto sink = [&](uint32_t b, uint32_t, uint4 w, uint32_t, uint32_t) {
         float p[GH];
 #pragma unroll
         for (int g = 0; g < GH; ++g) p[g] = pp[(uint64_t)b * a.G + g];

@@ -348,10 +348,19 @@ __device__ __forceinline__ BatchRegs fetch_batch(uint32_t lane, uint32_t n_valid
   return r;
 }
 
+// The default pass prologue of decode_batch: nothing to load.
+struct NoPrologue {
+  __device__ void operator()(uint32_t) const {}
+};
+
 // Decode one staged batch of GS-value blocks (FULL: all 64 blocks exist, so
 // no store is predicated).
-//   sink(b, j0, v, k)         8 decoded FP16 values of block b at positions
-//                             j0 .. j0 + 7 (v.x holds values j0, j0 + 1, ...)
+//   pre(k)                    called as write-out pass k (0..3) starts, before
+//                             its LDS work: a sink that needs other data for
+//                             the pass (the GEMV's x) loads it here
+//   sink(b, j0, v, k, it)     8 decoded FP16 values of block b at positions
+//                             j0 .. j0 + 7 (v.x holds values j0, j0 + 1, ...),
+//                             in iteration it of pass k
 // Steps: stage the batch in LDS; each lane decodes one block's codeword
 // stream with the 8-bit-window look-up table, four codewords per bit-window
 // refill, and marks a clipped stream; builds the block's value table (15
@@ -366,9 +375,9 @@ __device__ __forceinline__ BatchRegs fetch_batch(uint32_t lane, uint32_t n_valid
 // batch's latency, go first; the write-out passes next; the value-table work
 // last.  (The decode gains 6-8 % from it and the attention kernels 5 %;
 // the GEMV does not.)
-template <bool FULL, int NW, int GS = 128, bool PRIO = false, class Sink>
+template <bool FULL, int NW, int GS = 128, bool PRIO = false, class Sink, class Pre = NoPrologue>
 __device__ __forceinline__ void decode_batch(DecodeSmem<NW>& sm, uint32_t wave, uint32_t lane, uint32_t n_valid,
-                                             float t, const BatchRegs& in, Sink sink) {
+                                             float t, const BatchRegs& in, Sink sink, Pre pre = Pre{}) {
   using Geo = GroupGeom<GS>;
   constexpr uint32_t RB = Geo::kRecBits;
   constexpr int SST = Geo::kSymStride;
@@ -475,6 +484,7 @@ __device__ __forceinline__ void decode_batch(DecodeSmem<NW>& sm, uint32_t wave, 
   // 3. passes of kPassBlocks blocks
 #pragma unroll
   for (int k = 0; k < kPasses; ++k) {
+    pre((uint32_t)k);
     if (lane / kPassBlocks == (uint32_t)k) {
       uint32_t* Q = qs + (lane % kPassBlocks) * SST;
 #pragma unroll
@@ -520,7 +530,7 @@ __device__ __forceinline__ void decode_batch(DecodeSmem<NW>& sm, uint32_t wave, 
 #pragma unroll
     for (int it = 0; it < Geo::kPassIters; ++it) {
       const uint32_t bl = kPassBlocks * k + it * BPI + lane / LPB;
-      if (FULL || bl < n_valid) sink(bl, 8u * (lane % LPB), o[it], (uint32_t)k);
+      if (FULL || bl < n_valid) sink(bl, 8u * (lane % LPB), o[it], (uint32_t)k, (uint32_t)it);
     }
   }
   if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);

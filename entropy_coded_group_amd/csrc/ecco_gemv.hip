@@ -78,7 +78,7 @@ __device__ __forceinline__ void gemv_rows_per_wave(DecodeSmem<kGemvWaves>& sm, c
       nc0 = 0;
     }
     const BatchRegs nxt = nrow < a.out_f ? fetch(nrow, nc0) : fetch(row, c0);
-    auto sink = [&](uint32_t b, uint32_t j0, uint4 w, uint32_t) {
+    auto sink = [&](uint32_t b, uint32_t j0, uint4 w, uint32_t, uint32_t) {
       const uint16_t* xp = a.x + (uint64_t)(c0 + b) * 128u + j0;
 #pragma unroll
       for (int b2 = 0; b2 < BM; ++b2) {
@@ -139,14 +139,34 @@ __device__ __forceinline__ void gemv_whole_rows(DecodeSmem<kGemvWaves>& sm, cons
     // loop-invariant x addresses of a batch out of the loop (32 registers)
     const uint16_t* xb = a.x;
     asm volatile("" : "+s"(xb));
-    auto sink = [&](uint32_t b, uint32_t j0, uint4 w, uint32_t k) {
-      const uint16_t* xp = xb + (uint64_t)(b & (kGpr - 1u)) * 128u + j0;
+    // rows of 32 or 64 blocks: the pass's four x slices are loaded as the
+    // pass starts, so their latency runs under the pass's LDS work (with
+    // four rows per batch the extra registers spill, and the loads stay in
+    // the sink).  A load under a run-time condition is not started earlier
+    // than written; unconditional, all 16 of a batch would be issued first
+    // and held across the decode.
+    constexpr bool kPre = RB <= 2;
+    uint4 xpre[4];
+    auto pre = [&](uint32_t k) {
+      if constexpr (kPre) {
+        if (batch_cols != 0u) {
+#pragma unroll
+          for (int it = 0; it < 4; ++it) {
+            const uint32_t b = 16u * k + 4u * (uint32_t)it + lane / 16u;
+            xpre[it] = *reinterpret_cast<const uint4*>(xb + (uint64_t)(b & (kGpr - 1u)) * 128u + 8u * (lane % 16u));
+          }
+        }
+      }
+    };
+    auto sink = [&](uint32_t b, uint32_t j0, uint4 w, uint32_t k, uint32_t it) {
       const uint32_t r = k * RB / 4u;
-      // (a load under a run-time condition is not started ahead of the
-      // decode; unconditional, the batch's 16 x loads would all be issued
-      // first and held across it)
       if (batch_cols != 0u) {
-        const uint4 xv = *reinterpret_cast<const uint4*>(xp);
+        uint4 xv;
+        if constexpr (kPre) {
+          xv = xpre[it];
+        } else {
+          xv = *reinterpret_cast<const uint4*>(xb + (uint64_t)(b & (kGpr - 1u)) * 128u + j0);
+        }
 #pragma unroll
         for (int rr = 0; rr < RB; ++rr)
           if ((uint32_t)rr == r) acc[rr] = dot8(w, xv, acc[rr]);
@@ -154,9 +174,9 @@ __device__ __forceinline__ void gemv_whole_rows(DecodeSmem<kGemvWaves>& sm, cons
     };
     const uint32_t n_valid = min(64u, n_groups - batch * 64u);
     if (n_valid == 64u)
-      decode_batch<true>(sm, wave, lane, 64u, a.t, cur, sink);
+      decode_batch<true>(sm, wave, lane, 64u, a.t, cur, sink, pre);
     else
-      decode_batch<false>(sm, wave, lane, n_valid, a.t, cur, sink);
+      decode_batch<false>(sm, wave, lane, n_valid, a.t, cur, sink, pre);
 #pragma unroll
     for (int r = 0; r < RB; ++r) {
       const uint32_t row = batch * RB + r;

@@ -94,7 +94,7 @@ __device__ __forceinline__ void decode_job(DecodeSmem<kDecWaves>& sm, const Deco
     const bool more = nb < b_end;
     const BatchRegs nxt = fetch(more ? nb : batch, more);
     const uint32_t g0 = batch * 64u;
-    auto sink = [&](uint32_t b, uint32_t j0, uint4 v, uint32_t) {
+    auto sink = [&](uint32_t b, uint32_t j0, uint4 v, uint32_t, uint32_t) {
       const uint32_t gidx = g0 + b;
       uint64_t yoff;
       if (CONTIG) {
