@@ -215,7 +215,8 @@ def bench_ffn(args, torch, ecco, W):
             out["%s_b%d" % (name, b)] = dict(fused_us=round(np.mean(tf) * 1e6, 2),
                                              decode_then_gemv_us=round(np.mean(tu) * 1e6, 2),
                                              fp16_dense_gemv_us=round(np.mean(td) * 1e6, 2),
-                                             compressed_GBps=round(out_f * in_f / 2 / np.mean(tf) / 1e9, 1))
+                                             compressed_GBps=round(out_f * in_f / 2 / np.mean(tf) / 1e9, 1),
+                                             fp16_equivalent_GBps=round(out_f * in_f * 2 / np.mean(tf) / 1e9, 1))
         del wbuf
     tot_f = sum(v["fused_us"] for v in out.values())
     tot_u = sum(v["decode_then_gemv_us"] for v in out.values())
