@@ -188,7 +188,7 @@ def test_c1_encode_decode_bitexact(dev):
 
 @pytest.mark.parametrize("kind,seed,n", [("normal", 1, 1), ("normal", 2, 63), ("laplace", 3, 64),
                                          ("wide", 4, 65), ("normal", 5, 129), ("laplace", 6, 1000),
-                                         ("wide", 7, 4097)])
+                                         ("wide", 7, 4097), ("ties", 8, 2051), ("ties", 9, 17)])
 def test_random_groups_random_tables(dev, kind, seed, n):
     tb = random_tables(seed)
     tdev = dev_tables(tb)

@@ -311,7 +311,7 @@ def test_forced_clip_at_codeword_boundary_and_inside():
 
 def test_literal_matches_vectorised_encode_decode(trained, tabs, c1_groups):
     cases = [(c1_groups[:120], trained), (W.random_groups(60, 3, "wide").numpy(), tabs),
-             (W.random_groups(60, 4, "laplace").numpy(), tabs)]
+             (W.random_groups(60, 4, "laplace").numpy(), tabs), (W.random_groups(60, 5, "ties").numpy(), tabs)]
     for x, tb in cases:
         t = _t_for(x)
         blocks = codec.encode_groups(x, tb, t)

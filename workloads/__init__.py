@@ -173,7 +173,8 @@ def random_blocks(n_blocks, seed):
 
 
 def random_groups(n_groups, seed, kind="normal"):
-    """Small assorted groups for parity sweeps: normal, heavy-tailed or special."""
+    """Small assorted groups for parity sweeps: normal, heavy-tailed, wide-range
+    or tie-heavy."""
     g = _gen(seed)
     if kind == "normal":
         x = torch.randn(n_groups, GROUP, generator=g, dtype=torch.float32)
@@ -182,6 +183,14 @@ def random_groups(n_groups, seed, kind="normal"):
     elif kind == "wide":
         e = torch.randint(-20, 12, (n_groups, GROUP), generator=g).to(torch.float32)
         x = torch.randn(n_groups, GROUP, generator=g, dtype=torch.float32) * torch.exp2(e)
+    elif kind == "ties":
+        # values from {0, +-1, +-2, +-4} times a per-group power of two: many
+        # equal magnitudes (largest-|x| ties, equal min / max, equal outlier
+        # candidates) and values on exact binary fractions
+        levels = torch.tensor([0.0, 1.0, -1.0, 2.0, -2.0, 4.0, -4.0])
+        idx = torch.randint(0, len(levels), (n_groups, GROUP), generator=g)
+        e = torch.randint(-12, 8, (n_groups, 1), generator=g).to(torch.float32)
+        x = levels[idx] * torch.exp2(e)
     else:
         raise ValueError(kind)
     return x.to(torch.float16)
