@@ -250,6 +250,30 @@ def test_special_groups(dev):
         assert_fp16_equal(gpu_decode(o_blocks, tdev, t), codec.decode_blocks(o_blocks, tb, t), "special decode")
 
 
+def test_nonfinite_groups_counted_and_contained(dev):
+    """Groups holding NaN or +-Inf: their blocks are unspecified, but the
+    launch completes, the statistics count them as the oracle does, every
+    finite group of the same launch is still bit-exact, and every block
+    decodes."""
+    tb = golden("c1")
+    tdev = dev_tables(tb)
+    x = W.random_groups(600, 12, "normal").numpy()
+    bad = np.arange(3, 600, 37)
+    for i, g in enumerate(bad):
+        x[g, (i * 13) % 128] = (np.float16("nan"), np.float16("inf"), np.float16("-inf"))[i % 3]
+    x[bad[-1], :] = np.float16("nan")                       # a group of nothing but NaN
+    t = np.float32(0.01)
+    say("non-finite groups")
+    g_blocks, g_stats = gpu_encode(x, tdev, t, stats=True)
+    o_blocks, info = codec.encode_groups(x, tb, t, return_info=True)
+    assert g_stats["nonfinite_groups"] == info["stats"]["nonfinite_groups"] == len(bad)
+    good = np.setdiff1d(np.arange(600), bad)
+    assert_blocks_equal(g_blocks[good], o_blocks[good], "finite groups beside non-finite ones")
+    y = gpu_decode(g_blocks, tdev, t)
+    assert y.shape == (600, 128)
+    assert_fp16_equal(y[good], codec.decode_blocks(o_blocks[good], tb, t), "finite groups decode")
+
+
 def test_fuzz_decode_random_blocks(dev):
     for name, tb in (("c1", golden("c1")), ("adversarial", adversarial_tables(5))):
         tdev = dev_tables(tb)
