@@ -43,7 +43,9 @@ Other workloads (run separately, same JSON line shape):
 The CPU baseline is the oracle (NumPy) timed on a bounded sample of the same
 workload on this host: split over up to 16 worker processes (the reported
 value), and on one core in-process; beside it, the one-group-at-a-time oracle
-(plain Python) on the first 1,024 groups of that sample, on one core.
+(plain Python) on the first 1,024 groups of that sample, on one core.  The
+codec's quality figures (reconstruction MSE, compression ratio, clipping and
+padding) come from the oracle on the first 8,192 groups of q ("quality").
 """
 
 import argparse
@@ -164,6 +166,25 @@ def literal_baseline(x_groups, tables_blob, t, n_groups):
     n = len(blocks)
     return dict(groups=n, encode_GBps_1core=n * BYTES_PER_GROUP / (t1 - t0) / 1e9,
                 decode_GBps_1core=n * BYTES_PER_GROUP / (t2 - t1) / 1e9, seconds=t2 - t0)
+
+
+def oracle_quality(x_groups, tables_blob, t, n_groups):
+    """The codec's quality figures by the oracle on the first n_groups groups
+    (untimed): reconstruction MSE, the compression ratio with the side tables
+    counted, clipping, padding and index entropy."""
+    from oracle import codec, metrics
+    import entropy_coded_group_amd as ecco
+    c, l = ecco.ecco_tables_get(tables_blob)
+    x = x_groups[:n_groups]
+    tb = codec.Tables(c, l)
+    blocks, info = codec.encode_groups(x, tb, t, return_info=True)
+    y = codec.decode_blocks(blocks, tb, t)
+    rec = metrics.reconstruction(x.astype(np.float64), y.astype(np.float64))
+    out = dict(groups=int(x.shape[0]), mse=rec["mse"], rel_mse=rec["rel_mse"],
+               compression_ratio=metrics.compression_ratio(x_groups.shape[0], metrics.table_bytes_v1()))
+    out.update(metrics.padding_figures(info))
+    out.update(metrics.index_entropy(info))
+    return out
 
 
 def cpu_model():
@@ -440,6 +461,11 @@ def main():
             "sample": "first %d groups of the q matrix, one group at a time in plain Python, %.1f s" % (
                 lit["groups"], lit["seconds"]),
             "decode_GBps": round(lit["decode_GBps_1core"], 6), "encode_GBps": round(lit["encode_GBps_1core"], 6)}
+        q = oracle_quality(x0, blob0, t0, 8192)
+        line["quality"] = dict(
+            {k: (round(v, 6) if isinstance(v, float) else v) for k, v in q.items()},
+            source="oracle encode + decode of the first %d groups of the q matrix; compression ratio of the "
+                   "whole q matrix over FP16, its side tables counted" % q["groups"])
     print(json.dumps(line))
 
 
