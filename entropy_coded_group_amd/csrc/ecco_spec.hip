@@ -12,15 +12,17 @@
 //             bits 16..511); a codeword is at most 8 bits, so for each of the
 //             8 start offsets a lane meets at most 4 codeword starts and the
 //             decode leaves the segment at offset 0..7 of the next one
-//   resolve   from offset 0 in segment 0, the chain of exit offsets picks each
-//             segment's entry; a uniform loop over the 62 segments reads every
-//             lane's 8-entry exit and count tables with readlane (the merge),
-//             and the running count gives each lane its first output index
+//   resolve   a six-step scan over the lanes (Hillis-Steele) composes the
+//             segments' 8-entry exit maps and sums their symbol counts, so
+//             lane i learns where segments 0 .. i - 1 leave the stream when
+//             segment 0 is entered at offset 0 (its own entry) and how many
+//             codewords they hold (its first output index): the pages' merge
+//             stages, one per doubling of the span
 //   emit      each lane decodes its segment again from its true entry and
 //             writes the symbols whose index is below 128; the 128th
 //             codeword's end fixes the outlier-record count as in the format
 // The rest (value table, records, FP16 store) is the format's dequantisation.
-// Every block costs about 32 table look-ups per lane and a 62-step merge,
+// Every block costs about 32 table look-ups per lane and a six-step merge,
 // against 2 look-ups per lane-block for the lane-serial decoder; the latter
 // is the library's decoder because it does far less work per block.
 #include <hip/hip_runtime.h>
@@ -76,57 +78,88 @@ __global__ __launch_bounds__(kSpecWaves * 64) void decode_spec_kernel(SpecArgs a
     const uint32_t head = W[0];
     const uint32_t lutb = ((head & 63u) * 4u + ((head >> 6) & 3u)) * 256u;
     // the two words holding bits seg0 .. seg0 + 15 of this lane's segment
-    const uint32_t seg0 = 16u + 8u * min(lane, (uint32_t)kSegments - 1u), seg1 = seg0 + 8u;
+    const uint32_t seg0 = 16u + 8u * min(lane, (uint32_t)kSegments - 1u);
     const uint32_t wlo = W[seg0 >> 5], whi = W[(seg0 >> 5) + 1u], wbase = seg0 & ~31u;
     const bool last = lane == (uint32_t)kSegments - 1u;
-    // 1. speculative decode from each entry offset: exit offset and count
-    uint32_t F = 0, C = 0;
+    // 1. speculative decode.  A codeword may start at any of the segment's
+    //    8 bits: one look-up each gives its table entry (bytes of Elo, Ehi)
+    //    and the place q + length it ends (bytes of Nlo, Nhi; in the last
+    //    segment 16 marks a codeword that does not fit before bit 512, where
+    //    the stream is clipped).  The 8 decodes, one per entry offset o, then
+    //    run side by side in the bytes of P (position reached from o), a byte
+    //    gather per step; byte o of the map M is where decode o leaves the
+    //    segment (offset into the next one), byte o of K how many codewords
+    //    it read.  A codeword is at least 2 bits, so 4 steps finish them all.
+    uint32_t Elo = 0, Ehi = 0, Nlo = 0, Nhi = 0;
 #pragma unroll
-    for (uint32_t o = 0; o < 8u; ++o) {
-      uint32_t pos = seg0 + o, cnt = 0;
-      bool go = true;
+    for (uint32_t q = 0; q < 8u; ++q) {
+      const uint32_t e = sm.lut[lutb + (window(wlo, whi, seg0 + q - wbase) & 255u)];
+      uint32_t nq = q + (e >> 5) + 1u;
+      if (last && nq > 8u) nq = 16u;
+      const uint32_t sh = 8u * (q & 3u);
+      if (q < 4u) {
+        Elo |= e << sh;
+        Nlo |= nq << sh;
+      } else {
+        Ehi |= e << sh;
+        Nhi |= nq << sh;
+      }
+    }
+    uint32_t Plo = 0x03020100u, Phi = 0x07060504u, Klo = 0, Khi = 0;
+    auto step = [&](uint32_t& P, uint32_t& K) {
+      const uint32_t out = ((P >> 3) | (P >> 4)) & 0x01010101u;      // 1 in each byte whose decode has ended
+      const uint32_t G = __builtin_amdgcn_perm(Nhi, Nlo, P & 0x07070707u);
+      const uint32_t live = (out ^ 0x01010101u) * 0xffu;
+      K += (live & 0x01010101u) & (~G >> 4);                          // a codeword read unless it does not fit
+      P = (G & live) | (P & ~live);
+    };
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        if (go && pos < seg1) {
-          const uint32_t e = sm.lut[lutb + (window(wlo, whi, pos - wbase) & 255u)];
-          const uint32_t len = (e >> 5) + 1u;
-          if (last && pos + len > 512u) {
-            go = false;                            // the codeword does not fit: the stream is clipped
-          } else {
-            pos += len;
-            ++cnt;
-          }
-        }
-      }
-      F |= ((pos - seg1) & 7u) << (3u * o);
-      C |= cnt << (3u * o);
+    for (int k = 0; k < 4; ++k) {
+      step(Plo, Klo);
+      step(Phi, Khi);
     }
-    // 2. resolve: follow the exit offsets from offset 0 of segment 0
-    uint32_t entry = 0, start = 0, my_entry = 0, my_start = 0, my_cnt = 0;
-    for (uint32_t i = 0; i < (uint32_t)kSegments; ++i) {
-      const uint32_t f = __builtin_amdgcn_readlane(F, i), c = __builtin_amdgcn_readlane(C, i);
-      const uint32_t n_i = (c >> (3u * entry)) & 7u;
-      if (lane == i) {
-        my_entry = entry;
-        my_start = start;
-        my_cnt = n_i;
+    uint32_t Mlo = (Plo - 0x08080808u) & 0x07070707u, Mhi = (Phi - 0x08080808u) & 0x07070707u;
+    // 2. resolve.  After the step of span d, lane i holds the map of segments
+    //    i - 2d + 1 .. i (entry offset of the first -> entry offset of the one
+    //    after the last) and their codeword counts per entry offset.  Joining
+    //    the span of lane i - d: M(o) = M_i(M_{i-d}(o)), a byte gather that
+    //    v_perm_b32 does for four entries at once (selectors 0..7 pick bytes
+    //    of the 8-byte map), and K(o) = K_{i-d}(o) + K_i(M_{i-d}(o)), bytewise
+    //    (a count is at most 4 per segment, so no byte carries over)
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const uint32_t plo = __shfl_up(Mlo, d), phi = __shfl_up(Mhi, d);
+      const uint32_t qlo = __shfl_up(Klo, d), qhi = __shfl_up(Khi, d);
+      if (lane >= (uint32_t)d) {
+        const uint32_t nlo = __builtin_amdgcn_perm(Mhi, Mlo, plo), nhi = __builtin_amdgcn_perm(Mhi, Mlo, phi);
+        const uint32_t klo = qlo + __builtin_amdgcn_perm(Khi, Klo, plo);
+        const uint32_t khi = qhi + __builtin_amdgcn_perm(Khi, Klo, phi);
+        Mlo = nlo;
+        Mhi = nhi;
+        Klo = klo;
+        Khi = khi;
       }
-      start += n_i;
-      entry = (f >> (3u * entry)) & 7u;
     }
+    // entry 0 of segment 0: lane i enters where segments 0 .. i - 1 leave
+    const uint32_t pm = __shfl_up(Mlo, 1), pk = __shfl_up(Klo, 1);
+    const uint32_t my_entry = lane ? (pm & 255u) : 0u;
+    const uint32_t my_start = lane ? (pk & 255u) : 0u;
+    const uint32_t my_cnt = (Klo & 255u) - my_start;
+    const uint32_t start = __builtin_amdgcn_readlane(Klo, kSegments - 1) & 255u;
     const bool full = start >= 128u;               // 128 whole codewords fit: not clipped
-    // 3. emit: decode the segment again from its true entry
+    // 3. emit: the codewords of the decode from the true entry, from the
+    //    entries already looked up
     uint32_t end = 0;                               // stream end after codeword 128 (its lane only)
     if (lane < (uint32_t)kSegments) {
-      uint32_t pos = seg0 + my_entry;
+      uint32_t q = my_entry;
 #pragma unroll
       for (uint32_t s = 0; s < 4u; ++s) {
         if (s < my_cnt) {
-          const uint32_t e = sm.lut[lutb + (window(wlo, whi, pos - wbase) & 255u)];
+          const uint32_t e = __builtin_amdgcn_perm(Ehi, Elo, q) & 255u;   // the entry looked up at bit q
           const uint32_t idx = my_start + s;
-          pos += (e >> 5) + 1u;
+          q += (e >> 5) + 1u;
           if (idx < 128u) sym[idx] = (uint8_t)((e & 31u) << 1);
-          if (idx == 127u) end = pos;
+          if (idx == 127u) end = seg0 + q;
         }
       }
     }
