@@ -35,6 +35,10 @@ namespace ecco {
 
 constexpr int kSpecWaves = 8;                     // waves (blocks in flight) per workgroup
 constexpr int kSegments = (512 - 16) / 8;         // 62 segments of 8 stream bits
+// DPP controls (GFX9 encoding) of the merge scan
+constexpr int kRowBcast15 = 0x142;                // lane 15 of each row -> the next row
+constexpr int kRowBcast31 = 0x143;                // lane 31 -> rows 2 and 3
+constexpr int kWaveShr1 = 0x138;                  // lane i - 1 -> lane i, across rows
 
 struct SpecArgs {
   const uint8_t* blocks;
@@ -69,10 +73,19 @@ __global__ __launch_bounds__(kSpecWaves * 64) void decode_spec_kernel(SpecArgs a
   uint8_t* sym = sm.sym[wave];
   uint16_t* vt = sm.vtab[wave];
   const float t = a.t;
-  for (uint32_t g = blockIdx.x * kSpecWaves + wave; g < a.n_groups; g += gridDim.x * kSpecWaves) {
+  const uint32_t stride = gridDim.x * kSpecWaves;
+  // word lane % 16 of block gg; past the last block, the last block's (loaded
+  // unconditionally so that the load overlaps the current block's decode)
+  auto block_word = [&](uint64_t gg) -> uint32_t {
+    const uint32_t gc = (uint32_t)min(gg, (uint64_t)a.n_groups - 1u);
+    const uint32_t r = div_magic(gc, a.gpr), c = gc - r * a.gpr.d;
+    return reinterpret_cast<const uint32_t*>(a.blocks + ((uint64_t)r * a.blk_stride + c) * 64u)[lane & 15u];
+  };
+  uint32_t cur = block_word(blockIdx.x * kSpecWaves + wave);
+  for (uint32_t g = blockIdx.x * kSpecWaves + wave; g < a.n_groups; g += stride) {
     const uint32_t row = div_magic(g, a.gpr), col = g - row * a.gpr.d;
-    if (lane < 16u) W[lane] = reinterpret_cast<const uint32_t*>(a.blocks + ((uint64_t)row * a.blk_stride + col) * 64u)[lane];
-    else if (lane < 20u) W[lane] = 0u;
+    const uint32_t nxt = block_word((uint64_t)g + stride);
+    if (lane < 20u) W[lane] = lane < 16u ? cur : 0u;
     if (lane < 36u) reinterpret_cast<uint32_t*>(sym)[lane] = 0x20202020u;   // entry 16: +0 past a clip
     wave_sync();
     const uint32_t head = W[0];
@@ -119,18 +132,18 @@ __global__ __launch_bounds__(kSpecWaves * 64) void decode_spec_kernel(SpecArgs a
       step(Phi, Khi);
     }
     uint32_t Mlo = (Plo - 0x08080808u) & 0x07070707u, Mhi = (Phi - 0x08080808u) & 0x07070707u;
-    // 2. resolve.  After the step of span d, lane i holds the map of segments
-    //    i - 2d + 1 .. i (entry offset of the first -> entry offset of the one
-    //    after the last) and their codeword counts per entry offset.  Joining
-    //    the span of lane i - d: M(o) = M_i(M_{i-d}(o)), a byte gather that
-    //    v_perm_b32 does for four entries at once (selectors 0..7 pick bytes
-    //    of the 8-byte map), and K(o) = K_{i-d}(o) + K_i(M_{i-d}(o)), bytewise
-    //    (a count is at most 4 per segment, so no byte carries over)
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const uint32_t plo = __shfl_up(Mlo, d), phi = __shfl_up(Mhi, d);
-      const uint32_t qlo = __shfl_up(Klo, d), qhi = __shfl_up(Khi, d);
-      if (lane >= (uint32_t)d) {
+    // 2. resolve.  An inclusive scan over the lanes composes the spans: a
+    //    lane that holds the map of segments j .. i (entry offset of the
+    //    first -> entry offset of the one after the last) and their codeword
+    //    counts per entry offset takes in the span that ends at j - 1 from a
+    //    lower lane: M(o) = M_i(M_prev(o)), a byte gather that v_perm_b32 does
+    //    for four entries at once (selectors 0..7 pick bytes of the 8-byte
+    //    map), and K(o) = K_prev(o) + K_i(M_prev(o)), bytewise (a count is at
+    //    most 4 per segment, so no byte carries over).  Six DPP steps: shifts
+    //    by 1, 2, 4, 8 inside each row of 16 lanes, then the last lane of row
+    //    0 (2) into row 1 (3), then lane 31 into rows 2 and 3.
+    auto join = [&](uint32_t plo, uint32_t phi, uint32_t qlo, uint32_t qhi, bool take) {
+      if (take) {
         const uint32_t nlo = __builtin_amdgcn_perm(Mhi, Mlo, plo), nhi = __builtin_amdgcn_perm(Mhi, Mlo, phi);
         const uint32_t klo = qlo + __builtin_amdgcn_perm(Khi, Klo, plo);
         const uint32_t khi = qhi + __builtin_amdgcn_perm(Khi, Klo, phi);
@@ -139,9 +152,21 @@ __global__ __launch_bounds__(kSpecWaves * 64) void decode_spec_kernel(SpecArgs a
         Klo = klo;
         Khi = khi;
       }
-    }
+    };
+    join(dpp_u32<kRowShr1>(Mlo), dpp_u32<kRowShr1>(Mhi), dpp_u32<kRowShr1>(Klo), dpp_u32<kRowShr1>(Khi),
+         (lane & 15u) >= 1u);
+    join(dpp_u32<kRowShr2>(Mlo), dpp_u32<kRowShr2>(Mhi), dpp_u32<kRowShr2>(Klo), dpp_u32<kRowShr2>(Khi),
+         (lane & 15u) >= 2u);
+    join(dpp_u32<kRowShr4>(Mlo), dpp_u32<kRowShr4>(Mhi), dpp_u32<kRowShr4>(Klo), dpp_u32<kRowShr4>(Khi),
+         (lane & 15u) >= 4u);
+    join(dpp_u32<kRowShr8>(Mlo), dpp_u32<kRowShr8>(Mhi), dpp_u32<kRowShr8>(Klo), dpp_u32<kRowShr8>(Khi),
+         (lane & 15u) >= 8u);
+    join(dpp_u32<kRowBcast15>(Mlo), dpp_u32<kRowBcast15>(Mhi), dpp_u32<kRowBcast15>(Klo),
+         dpp_u32<kRowBcast15>(Khi), (lane & 16u) != 0u);
+    join(dpp_u32<kRowBcast31>(Mlo), dpp_u32<kRowBcast31>(Mhi), dpp_u32<kRowBcast31>(Klo),
+         dpp_u32<kRowBcast31>(Khi), lane >= 32u);
     // entry 0 of segment 0: lane i enters where segments 0 .. i - 1 leave
-    const uint32_t pm = __shfl_up(Mlo, 1), pk = __shfl_up(Klo, 1);
+    const uint32_t pm = dpp_u32<kWaveShr1>(Mlo), pk = dpp_u32<kWaveShr1>(Klo);
     const uint32_t my_entry = lane ? (pm & 255u) : 0u;
     const uint32_t my_start = lane ? (pk & 255u) : 0u;
     const uint32_t my_cnt = (Klo & 255u) - my_start;
@@ -197,6 +222,7 @@ __global__ __launch_bounds__(kSpecWaves * 64) void decode_spec_kernel(SpecArgs a
     const uint32_t v1 = *reinterpret_cast<const uint16_t*>(tb + sym[2u * lane + 1u]);
     reinterpret_cast<uint32_t*>(a.y + (uint64_t)row * a.y_stride + (uint64_t)col * 128u)[lane] = v0 | (v1 << 16);
     wave_sync();
+    cur = nxt;
   }
 }
 
