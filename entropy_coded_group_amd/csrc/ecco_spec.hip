@@ -11,20 +11,23 @@
 //   segments  lane i owns stream bits 16 + 8 i .. 16 + 8 i + 7 (62 lanes cover
 //             bits 16..511); a codeword is at most 8 bits, so for each of the
 //             8 start offsets a lane meets at most 4 codeword starts and the
-//             decode leaves the segment at offset 0..7 of the next one
-//   resolve   a six-step scan over the lanes (Hillis-Steele) composes the
+//             decode leaves the segment at offset 0..7 of the next one; the
+//             lane looks up the codeword at each of its 8 bits once and runs
+//             the 8 decodes from those entries
+//   resolve   a six-step scan over the lanes composes the
 //             segments' 8-entry exit maps and sums their symbol counts, so
 //             lane i learns where segments 0 .. i - 1 leave the stream when
 //             segment 0 is entered at offset 0 (its own entry) and how many
 //             codewords they hold (its first output index): the pages' merge
 //             stages, one per doubling of the span
-//   emit      each lane decodes its segment again from its true entry and
+//   emit      each lane follows its segment's decode from its true entry and
 //             writes the symbols whose index is below 128; the 128th
 //             codeword's end fixes the outlier-record count as in the format
 // The rest (value table, records, FP16 store) is the format's dequantisation.
-// Every block costs about 32 table look-ups per lane and a six-step merge,
-// against 2 look-ups per lane-block for the lane-serial decoder; the latter
-// is the library's decoder because it does far less work per block.
+// Every block costs 8 table look-ups per lane (one per stream bit) and a
+// six-step merge, against one look-up per codeword (2 per lane-block) for
+// the lane-serial decoder; the latter is the library's decoder because it
+// does far less work per block.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
