@@ -276,6 +276,7 @@ uint64_t part_bytes(uint64_t pairs, uint64_t g, uint64_t s) {
 }  // namespace
 
 extern "C" size_t ecco_attention_workspace_size(uint64_t batch, uint64_t kv_heads, uint64_t group, uint64_t seq) {
+  if (batch >= (1ull << 20) || kv_heads >= (1ull << 20) || seq >= (1ull << 24) || group > 8) return 0;
   const uint64_t pairs = batch * kv_heads;
   return (size_t)(probs_bytes(pairs, group, seq) + part_bytes(pairs, group, seq));
 }
@@ -290,6 +291,8 @@ extern "C" int ecco_attention_decode(const void* k_blocks, const void* k_tables,
   if (!(std::fabs(scale) < __builtin_huge_valf())) return ECCO_EINVAL;
   if (batch == 0 || kv_heads == 0 || seq == 0 || kv_stride < seq) return ECCO_ESIZE;
   if (group != 1 && group != 2 && group != 4 && group != 8) return ECCO_ESIZE;
+  // each factor bounded before any product, so none of them wraps
+  if (batch >= (1ull << 20) || kv_heads >= (1ull << 20) || kv_stride >= (1ull << 32)) return ECCO_ESIZE;
   const uint64_t pairs = batch * kv_heads;
   if (pairs >= (1ull << 20) || seq >= (1ull << 24) || pairs * kv_stride >= (1ull << 32) ||
       pairs * ((seq + 63) / 64) >= (1ull << 31))

@@ -220,7 +220,8 @@ int make_gemv_job(const void* blocks, const void* tables, float tensor_scale, in
   if (!blocks || !tables || !x || !y) return ECCO_EINVAL;
   if (!(tensor_scale > 0.0f) || !(tensor_scale < __builtin_huge_valf())) return ECCO_EINVAL;
   if (out_f < 1 || in_f < 128 || in_f % 128 != 0 || batch < 1 || batch > ECCO_GEMV_MAX_BATCH) return ECCO_ESIZE;
-  if ((uint64_t)out_f * (uint64_t)(in_f / 128) >= (1ull << 32) || out_f >= (1ll << 31)) return ECCO_ESIZE;
+  uint64_t n_groups = 0;
+  if (out_f >= (1ll << 31) || !group_count((uint64_t)out_f, (uint64_t)(in_f / 128), &n_groups)) return ECCO_ESIZE;
   if (!host_aligned(blocks, 64) || !host_aligned(tables, 256) || !host_aligned(x, 16) || !host_aligned(y, 4))
     return ECCO_EALIGN;
   GemvJob& a = *out;

@@ -57,4 +57,13 @@ uint32_t search_width(const Tables* t);
 int check_gfx950(int* cus);
 inline bool host_aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
+// Number of groups of an n_rows x groups_per_row job.  False unless both
+// factors are in 1 .. 2^32 - 1 and so is their product; the factors are
+// bounded first, so the 64-bit product cannot wrap.
+inline bool group_count(uint64_t n_rows, uint64_t gpr, uint64_t* total) {
+  if (n_rows == 0 || gpr == 0 || n_rows >= (1ull << 32) || gpr >= (1ull << 32)) return false;
+  *total = n_rows * gpr;
+  return *total < (1ull << 32);
+}
+
 }  // namespace ecco

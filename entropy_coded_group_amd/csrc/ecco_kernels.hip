@@ -684,8 +684,8 @@ int make_encode_job(const uint16_t* x, uint64_t n_rows, uint64_t gpr, uint64_t x
                     const void* tables, float tensor_scale, void* blocks, ecco_stats_t* stats, EncodeJob* out) {
   if (!x || !tables || !blocks) return ECCO_EINVAL;
   if (!(tensor_scale > 0.0f) || !(tensor_scale < __builtin_huge_valf())) return ECCO_EINVAL;
-  const uint64_t total = n_rows * gpr;
-  if (n_rows == 0 || gpr == 0 || total >= (1ull << 32) || gpr >= (1ull << 32)) return ECCO_ESIZE;
+  uint64_t total = 0;
+  if (!group_count(n_rows, gpr, &total)) return ECCO_ESIZE;
   if (n_rows > 1 && (x_stride < gpr * GS || blk_stride < gpr)) return ECCO_ESIZE;
   if (!host_aligned(x, 16) || (x_stride % 8) != 0 || !host_aligned(blocks, 64) || !host_aligned(tables, 256) ||
       (stats && !host_aligned(stats, 8)))
@@ -807,8 +807,8 @@ int make_decode_job(const void* blocks, uint64_t n_rows, uint64_t gpr, uint64_t 
                     const void* tables, float tensor_scale, uint16_t* y, DecodeJob* out, uint32_t GS = 128) {
   if (!blocks || !tables || !y) return ECCO_EINVAL;
   if (!(tensor_scale > 0.0f) || !(tensor_scale < __builtin_huge_valf())) return ECCO_EINVAL;
-  const uint64_t total = n_rows * gpr;
-  if (n_rows == 0 || gpr == 0 || total >= (1ull << 32) || gpr >= (1ull << 32)) return ECCO_ESIZE;
+  uint64_t total = 0;
+  if (!group_count(n_rows, gpr, &total)) return ECCO_ESIZE;
   if (n_rows > 1 && (y_stride < gpr * GS || blk_stride < gpr)) return ECCO_ESIZE;
   if (!host_aligned(y, 16) || (y_stride % 8) != 0 || !host_aligned(blocks, 64) || !host_aligned(tables, 256)) return ECCO_EALIGN;
   DecodeJob& a = *out;

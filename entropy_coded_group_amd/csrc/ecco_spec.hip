@@ -238,8 +238,8 @@ extern "C" int ecco_decode_speculative(const void* blocks, uint64_t n_rows, uint
                                        void* stream) {
   if (!blocks || !tables || !y) return ECCO_EINVAL;
   if (!(tensor_scale > 0.0f) || !(tensor_scale < __builtin_huge_valf())) return ECCO_EINVAL;
-  const uint64_t total = n_rows * gpr;
-  if (n_rows == 0 || gpr == 0 || total >= (1ull << 32) || gpr >= (1ull << 32)) return ECCO_ESIZE;
+  uint64_t total = 0;
+  if (!group_count(n_rows, gpr, &total)) return ECCO_ESIZE;
   if (n_rows > 1 && (y_stride < gpr * 128 || blk_stride < gpr)) return ECCO_ESIZE;
   if (!host_aligned(y, 16) || (y_stride % 8) != 0 || !host_aligned(blocks, 64) || !host_aligned(tables, 256))
     return ECCO_EALIGN;

@@ -64,9 +64,9 @@
  * high-ratio one's hardware, Fig. 9 caption).  Everything above holds with
  * 128 replaced by 64, except the records: 14 bits each, bits 0..5 = position
  * j, bits 6..13 = FP8 value; bits 512-14(r+1) .. 512-14r-1 hold record r and
- * n = min(16, floor((512 - E) / 14)).  Symmetric like the 4x format: the
- * "zero points" that one figure caption mentions are not defined on the
- * pages and are not stored.
+ * n = min(16, floor((512 - E) / 14)).  Symmetric like the 4x format: one
+ * figure caption mentions zero points, but the pages never define them, so
+ * none are stored.
  *
  * ------------------------------------------------------------------------
  * CONVENTIONS
@@ -179,8 +179,8 @@ int ecco_tables_get(const void* tables_host, float* centroids_host, uint8_t* cod
 int ecco_train_patterns(const uint16_t* sample_fp16_host, uint64_t n_values,
                         const ecco_train_opts_t* opts, void* tables_host);
 
-/* Per-tensor scale t = amax / 448 (1 if amax == 0 or not finite) -- the
- * "per-tensor FP16-to-FP8 scale factor" (Fig. 4 caption). */
+/* Per-tensor scale t = amax / 448 (1 if amax == 0 or not finite): the one
+ * scale per tensor that maps FP16 values onto the FP8 range (Fig. 4 caption). */
 float ecco_tensor_scale_from_amax(float amax);
 
 /* ---- device calls ---------------------------------------------------------- */

@@ -8,14 +8,15 @@ What the pages fix (Ecco review, pith.science, arXiv 2505.06901):
     scale; the group is then normalised to (-1, 1) (Fig. 4 caption);
   * 64 shared patterns of 15 sorted centroids; index 15 is reserved for the
     scale factor ("free parameters": centroids per pattern);
-  * the pattern is chosen by comparing only the group's min and max with each
-    pattern's min and max by squared error ("What carries the argument"; free
-    parameter "shared k-means patterns used in the compressor", section 4.3);
-  * the indices are Huffman coded with the shortest of 4 codebooks per
-    pattern; overflow is clipped; spare space is padded with the group's
-    next-largest outliers ("What carries the argument"; "Core claim"); the
-    padded outliers are the top 16 values, up to 240 bits per block ("free
-    parameters": number of padded outlier slots);
+  * a group's pattern is picked from the squared error between the group's
+    two extremes and each pattern's two end centroids, nothing else ("What
+    carries the argument"; the free-parameter row on the shared k-means
+    patterns of the compressor, section 4.3);
+  * each pattern has 4 Huffman codebooks and a group uses whichever codes it
+    in the fewest bits; symbols past the end of the block are cut off, and
+    bits left over carry the group's largest remaining values ("What carries
+    the argument"; "Core claim"); at most 16 such values, 240 bits at most
+    ("free parameters": the row on padded outlier slots);
   * code lengths are limited to 2..8 bits (referee report, major comment 1).
 
 Where the pages are silent the following readings are used (each is listed

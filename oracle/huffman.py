@@ -3,8 +3,8 @@
 The pages: each group's indices are Huffman-coded with one of 4 codebooks per
 pattern, the codebook giving the shortest encoding is chosen (Ecco review,
 "What carries the argument" and "Core claim"), and the parallel decoder relies
-on "limiting the code length to 2-8 bits" (referee report, major comment 1),
-for which no construction is given.
+on code lengths being bounded to between 2 and 8 bits (referee report, major
+comment 1); the pages give no construction for such lengths.
 
 Readings used here:
   * codes are canonical in the DEFLATE sense (RFC 1951 section 3.2.2):

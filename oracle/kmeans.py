@@ -1,11 +1,11 @@
 """k-means used to learn the shared patterns (oracle; test infrastructure only).
 
-The pages: patterns are "a fixed, offline-learned list of 15 sorted centroids,
-with 64 patterns per tensor" (Ecco review, "What carries the argument"),
+The pages: each tensor has 64 patterns, each a list of 15 sorted centroids
+fixed after offline learning (Ecco review, "What carries the argument"),
 learned with k-means on calibration data ("Assumptions & free parameters": S,
-the number of shared k-means patterns, is 64; 15 centroids per pattern).  The
-"activation-aware" weighting is left undefined by the paper (referee report,
-minor comment 4); unweighted k-means is used.
+the count of shared k-means patterns, is 64; 15 centroids per pattern).  The
+paper names a weighting of the k-means by activations but never defines it
+(referee report, minor comment 4); unweighted k-means is used.
 
 Reading: learning has two levels.  (1) Each normalised group's 127 non-scale
 values are clustered into 15 clusters with exact one-dimensional k-means (the

@@ -4,7 +4,7 @@ The pages choose a group's pattern by comparing only the group's min and max
 with each pattern's end centroids, and call a full MSE search too expensive
 for the online (KV-cache) compressor; the referee report asks how often the
 cheap rule picks a different pattern than the MSE-optimal one and what that
-costs, and the free parameter "number of shared patterns" sets S = 64 while
+costs, and the free-parameter row on the pattern count sets S = 64 while
 the online compressor is described with 16 (Ecco review, "What carries the
 argument"; referee report; "Assumptions & free parameters", section 4.3).
 

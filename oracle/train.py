@@ -79,7 +79,7 @@ def train_tables(sample_fp16, n_patterns=64, n_codebooks=4, kmeans_iters=25, huf
 
     distinct (default: n_patterns) patterns are learned and slot p of the
     n_patterns holds pattern p mod distinct -- the 16-pattern variant the pages
-    weigh against 64 (free parameter "number of shared patterns"; section 4.3
+    weigh against 64 (the free-parameter row on the pattern count; section 4.3
     compressor) in a table of the full width, whose extra slots never win the
     min/max search because they tie with a lower slot."""
     D = n_patterns if distinct is None else int(distinct)

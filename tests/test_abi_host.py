@@ -131,6 +131,15 @@ def test_device_entry_points_check_arguments_before_touching_the_device():
     assert L.ecco_decode_gemv(A, A, 1.0, 16, 100, A, 1, A, None) == -3          # in % 128
     assert L.ecco_decode_gemv(A, A, 1.0, 16, 128, A, 9, A, None) == -3          # batch > 8
     assert L.ecco_amax(A, 0, A, None) == -3
+    # group counts whose 64-bit product wraps (2^33 rows x 2^31 groups = 2^64
+    # -> 0, and 2^33 x (2^31 + 1) -> 2^33) are refused, not truncated
+    for n_rows, gpr in ((1 << 33, 1 << 31), (1 << 33, (1 << 31) + 1), (1, 1 << 32), (1 << 32, 1)):
+        assert L.ecco_encode(A, n_rows, gpr, gpr * 128, gpr, A, 1.0, A, None, None) == -3
+        assert L.ecco_encode_act(A, n_rows, gpr, gpr * 64, gpr, A, 1.0, A, None, None) == -3
+        assert L.ecco_decode(A, n_rows, gpr, gpr, gpr * 128, A, 1.0, A, None) == -3
+        assert L.ecco_decode_act(A, n_rows, gpr, gpr, gpr * 64, A, 1.0, A, None) == -3
+        assert L.ecco_decode_speculative(A, n_rows, gpr, gpr, gpr * 128, A, 1.0, A, None) == -3
+    assert L.ecco_decode_gemv(A, A, 1.0, 1 << 10, 128 << 54, A, 1, A, None) == -3   # 2^10 x 2^54 groups
     # ecco_encode_many: count, reserved field, every job checked
     ej = (ecco.EncodeJob * 2)()
     for j in ej:
@@ -343,6 +352,11 @@ def test_attention_checks_arguments_before_touching_the_device():
     assert call(ws=A + 64) == -2
     assert call(q=A + 2) == -2
     assert call(k=A + 32) == -2
+    # sizes whose products would wrap: 2^33 x 2^31 sequence-head pairs, a
+    # 2^63-token row stride
+    assert call(b=1 << 33, h=1 << 31) == -3
+    assert call(stride=1 << 63) == -3
+    assert ecco.ecco_attention_workspace_size(1 << 33, 1 << 31, 4, 100) == 0
     # workspace: scores [B*H][S][G] floats and partial sums [B*H][ceil(S/128)][G][128] floats, 256-aligned
     def up(v):
         return (v + 255) // 256 * 256

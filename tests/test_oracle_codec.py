@@ -425,3 +425,176 @@ def test_pins_catch_planted_mistake(name, old, new, trained, c1_groups):
     except (AssertionError, IndexError, ValueError):
         caught = True
     assert caught, name
+
+
+# ------------------------------------------------- decode pins (hand-built)
+#
+# The decoder's value rule (c * |S| for centroid symbols, S for the scale
+# symbol), its record order (records applied r = 0, 1, ...: a later record
+# wins a repeated position) and its stop rule (no records once the stream
+# stops early) are pinned here on blocks and groups whose decoded values
+# follow from the format alone.
+
+GRID8 = (np.arange(-7, 8) * 0.125).astype(np.float32)     # 15 values exact in FP8 E4M3 and FP16
+
+
+def grid_tables(code_len_row):
+    c = np.tile(GRID8, (64, 1))
+    return codec.Tables(c, np.tile(np.asarray(code_len_row, np.uint8), (64, 4, 1)))
+
+
+# Book with symbol 7 at 2 bits, symbols 6 and 8..15 at 4, symbols 0..5 at 5
+# (Kraft 1/4 + 9/16 + 6/32 = 1).  Its canonical codes, by hand: ordered by
+# (length, symbol), 7 -> 00; then 4-bit codes from (00 + 1) << 2 = 0100:
+# 6 -> 0100, 8 -> 0101, 9 -> 0110, ..., 15 -> 1100; then 5-bit codes from
+# (1100 + 1) << 1 = 11010: 0 -> 11010, 1 -> 11011, ..., 5 -> 11111.
+BOOK = [5, 5, 5, 5, 5, 5, 4, 2, 4, 4, 4, 4, 4, 4, 4, 4]
+BOOK_CODES = {7: "00", 6: "0100", 8: "0101", 9: "0110", 10: "0111", 11: "1000", 12: "1001", 13: "1010",
+              14: "1011", 15: "1100", 0: "11010", 1: "11011", 2: "11100", 3: "11101", 4: "11110", 5: "11111"}
+
+
+class BlockBits:
+    """A 512-bit block written bit by bit in the format's order: bit i is bit
+    (i & 7) of byte i >> 3; integer fields LSB first, codewords MSB first."""
+
+    def __init__(self):
+        self.bits = [0] * 512
+        self.pos = 0
+
+    def field(self, value, nbits):
+        for b in range(nbits):
+            self.bits[self.pos + b] = (value >> b) & 1
+        self.pos += nbits
+
+    def code(self, word):
+        for ch in word:
+            self.bits[self.pos] = int(ch)
+            self.pos += 1
+
+    def record(self, r, value, nbits=15):
+        lo = 512 - nbits * (r + 1)
+        for b in range(nbits):
+            self.bits[lo + b] = (value >> b) & 1
+
+    def block(self):
+        return np.packbits(np.array(self.bits, np.uint8), bitorder="little")[None]
+
+
+def test_hand_codes_are_canonical():
+    codes = huffman.canonical_codes(BOOK)
+    assert {s: format(codes[s], "0%db" % BOOK[s]) for s in range(16)} == BOOK_CODES
+
+
+def check_negative_scale_group(dec):
+    """A group whose largest magnitude is negative: S = -2 (t = 1), a = 2; the
+    other 127 values are centroids times a: 100 zeros and 27 values spread
+    over the grid.  Every centroid value and every record value is exact, so
+    the block decodes to the group itself; writing c * S in place of c * a
+    would flip the signs of the centroid values."""
+    rng = np.random.default_rng(11)
+    others = np.concatenate([np.zeros(100, np.float32), GRID8[rng.integers(0, 15, 27)] * 2])
+    x = np.concatenate([[-2.0], rng.permutation(others)]).astype(np.float16)[None]
+    tb = grid_tables(BOOK)
+    blocks, info = codec.encode_groups(x, tb, F32(1.0), return_info=True)
+    assert info["S"][0] == -2.0 and info["a"][0] == 2.0 and not info["clipped"][0]
+    y = dec(blocks, tb, F32(1.0))
+    assert np.array_equal(y.view(np.uint16), x.view(np.uint16))
+    return True
+
+
+def test_negative_scale_group_decodes_to_itself():
+    assert check_negative_scale_group(codec.decode_blocks)
+
+
+def repeated_record_block():
+    """Symbols: 15 at j = 0, then 127 x symbol 7: L = 4 + 254 = 258 bits,
+    E = 274, n = min(16, floor(238 / 15)) = 15 records.  Records 0 and 1 both
+    name position 5 (FP8 2.0 = 0x40, then 4.0 = 0x48); records 2..14 set
+    positions 10..22 to 0.5 (0x30).  Scale byte 0x38 = 1.0, t = 1."""
+    bb = BlockBits()
+    bb.field(0, 6)
+    bb.field(0, 2)
+    bb.field(0x38, 8)
+    bb.code(BOOK_CODES[15])
+    for _ in range(127):
+        bb.code(BOOK_CODES[7])
+    assert bb.pos == 274
+    bb.record(0, 5 | (0x40 << 7))
+    bb.record(1, 5 | (0x48 << 7))
+    for r in range(2, 15):
+        bb.record(r, (8 + r) | (0x30 << 7))
+    want = np.zeros(128, np.float16)                      # c[7] * a = 0 * 1 = +0
+    want[0] = 1.0
+    want[5] = 4.0                                         # the later record wins
+    want[10:23] = 0.5
+    return bb.block(), want
+
+
+def stopped_stream_block():
+    """A book whose symbol 0 is 8 bits long (Kraft < 1): canonical 8-bit code
+    11111000 after the 5-bit codes 11010..11110 of symbols 1..5 (by hand:
+    (11110 + 1) << 3), so 11111111 prefixes no codeword.  Stream: symbol 15,
+    nine x symbol 7, then 11111111: decoding stops with k = 10 at bit 38.
+    The block's last 240 bits hold 16 records naming position 100 (FP8 1.0);
+    a stopped stream takes none of them, so values 10..127 are +0."""
+    book = list(BOOK)
+    book[0] = 8
+    codes = dict(BOOK_CODES)
+    codes.update({1: "11010", 2: "11011", 3: "11100", 4: "11101", 5: "11110", 0: "11111000"})
+    cc = huffman.canonical_codes(book)
+    assert {s: format(cc[s], "0%db" % book[s]) for s in range(16)} == codes
+    bb = BlockBits()
+    bb.field(0, 6)
+    bb.field(0, 2)
+    bb.field(0x38, 8)
+    bb.code(codes[15])
+    for _ in range(9):
+        bb.code(codes[7])
+    bb.code("11111111")
+    for r in range(16):
+        bb.record(r, 100 | (0x38 << 7))
+    want = np.zeros(128, np.float16)
+    want[0] = 1.0
+    return bb.block(), want, grid_tables(book)
+
+
+def check_hand_built_blocks(dec):
+    blk, want = repeated_record_block()
+    y = dec(blk, grid_tables(BOOK), F32(1.0))
+    assert np.array_equal(y[0].view(np.uint16), want.view(np.uint16)), y[0]
+    blk, want, tb = stopped_stream_block()
+    y = dec(blk, tb, F32(1.0))
+    assert np.array_equal(y[0].view(np.uint16), want.view(np.uint16)), y[0]
+    return True
+
+
+def test_hand_built_blocks_decode_as_the_format_says():
+    assert check_hand_built_blocks(codec.decode_blocks)
+    lit = lambda b, tb, t: literal.decode_block(b[0].tobytes(), tb.centroids, tb.code_len, t)[None]
+    assert check_hand_built_blocks(lit)
+    assert check_negative_scale_group(lit)
+
+
+DECODE_MUTATIONS = [
+    ("centroid times signed scale", "cval = (c[p[:, None], cidx] * a[:, None])", "cval = (c[p[:, None], cidx] * S[:, None])"),
+    ("records in reverse order",
+     "    for r in range(MAX_OUTLIERS):\n        lo = BLOCK_BITS - rec_bits * (r + 1)\n        rec = (bits",
+     "    for r in reversed(range(MAX_OUTLIERS)):\n        lo = BLOCK_BITS - rec_bits * (r + 1)\n        rec = (bits"),
+    ("records on a stopped stream", "full = k == group", "full = k >= 0"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", DECODE_MUTATIONS, ids=[m[0] for m in DECODE_MUTATIONS])
+def test_decode_pins_catch_planted_mistake(name, old, new):
+    mut = _mutant(open(codec.__file__).read(), old, new)
+    caught = False
+    for chk in (lambda: check_negative_scale_group(mut.decode_blocks),
+                lambda: check_hand_built_blocks(mut.decode_blocks)):
+        try:
+            if not chk():
+                caught = True
+        except (AssertionError, IndexError, ValueError):
+            caught = True
+        if caught:
+            break
+    assert caught, name
