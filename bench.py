@@ -1,34 +1,38 @@
 """Benchmark of the Ecco block codec on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload layer|kv|model|ffn|attn|act|copy] [--gpus 1]
+    python bench.py [--steps K] [--warmup W] [--workload model|layer|kv|ffn|attn|act|copy] [--gpus 1]
 
-Default workload ("layer"): one LLaMA-3-8B-shaped decoder layer in FP16 --
-q, o [4096, 4096], k, v [1024, 4096], gate, up [14336, 4096], down
-[4096, 14336] -- with per-output-row LogNormal(0, 0.5) scales times N(0, 1)
-entries and 0.05 % of entries x20, groups of 128 along the input dimension
-(1,703,936 groups, 436 MB).  Tables for each matrix type are learned by
-ecco_train_patterns from a separate seeded 2**20-value sample of the same
-recipe (offline, outside the timed region).
+Default workload ("model"): the 32-layer LLaMA-3-8B-shaped weight set in
+FP16, 6.98e9 parameters (13.96 GB) resident in HBM.  Each layer has q, o
+[4096, 4096], k, v [1024, 4096], gate, up [14336, 4096] and down
+[4096, 14336], drawn on the GPU (workloads.c4_matrix) with per-output-row
+LogNormal(0, 0.5) scales times N(0, 1) entries and 0.05 % of entries x20;
+groups of 128 along the input dimension (1,703,936 groups per layer,
+54,525,952 in all, 3.49 GB of blocks).  Tables for each matrix type are
+learned by ecco_train_patterns from a separate seeded 2**20-value sample of
+the same recipe (offline, outside the timed region) and serve all 32 layers.
 
-One step runs every row of the hot path over the whole layer, inputs resident
-in HBM: one ecco_amax_many call over the seven matrices, one ecco_encode_many
-launch that encodes them, one ecco_decode_many launch that decodes them (each
-matrix with its own tables and scale), and the fused
-decode+GEMV at batch 1 as a decode step issues it: ecco_decode_gemv_many over
-q, k, v (same x), then o, then gate and up (same x), then down.  Each launch is bracketed by HIP events on the stream it
-runs on.  The reported value is decode throughput -- (64 B compressed in +
-256 B FP16 out) per group over the summed decode kernel time of the timed
-steps; encode (256 B in + 64 B out per group) and the fused GEMV are reported
-beside it, and so are each matrix decoded by an ecco_decode launch of its own,
-the same by ecco_decode_speculative (the pages' segment-parallel decode), each
-GEMV, amax and encode issued by a call of its own, and the whole step captured
-once into a HIP graph and replayed (step_us_hip_graph_replay).
+One step runs every row of the hot path over all 32 layers: per layer one
+ecco_amax_many call over the seven matrices; then per layer one
+ecco_encode_many launch; then per layer one ecco_decode_many launch into one
+reused FP16 buffer of a layer's size (a layer's blocks were written 31
+layers -- 3.4 GB of other traffic -- earlier, so they come from HBM, not the
+256 MB last-level cache); then per layer the fused decode+GEMV at batch 1 as
+a decode step issues it: ecco_decode_gemv_many over q, k, v (same x), then
+o, then gate and up (same x), then down.  Each launch is bracketed by HIP
+events on the stream it runs on.  The reported value is decode throughput
+-- (64 B compressed in + 256 B FP16 out) per group over the summed decode
+kernel time of the timed steps; encode (256 B in + 64 B out per group), amax
+and the fused GEMV are reported beside it.
 
 Other workloads (run separately, same JSON line shape):
+  layer  one layer of the set above, drawn on the CPU: the same step on one
+         layer, plus diagnostics (each matrix decoded by a launch of its own
+         and by ecco_decode_speculative, the pages' segment-parallel decode;
+         each amax, encode and GEMV by a call of its own; the step captured
+         into a HIP graph and replayed)
   kv     K and V caches [16, 8, 8192, 128]: append-encode of the last 256
          tokens per row (strided) and decode of the whole cache
-  model  32 layers (~7e9 parameters) encoded once, then every matrix decoded
-         into one reused FP16 buffer (sustained decode)
   ffn    70B-shaped FFN matrices [28672, 8192], [8192, 28672]: fused
          decode+GEMV at batch 1, 4, 8 against decode followed by a dense GEMV
   attn   decode-phase attention over the compressed K and V caches
@@ -41,11 +45,12 @@ Other workloads (run separately, same JSON line shape):
          traffic counters FETCH_SIZE / WRITE_SIZE)
 
 The CPU baseline is the oracle (NumPy) timed on a bounded sample of the same
-workload on this host: split over up to 16 worker processes (the reported
-value), and on one core in-process; beside it, the one-group-at-a-time oracle
-(plain Python) on the first 1,024 groups of that sample, on one core.  The
-codec's quality figures (reconstruction MSE, compression ratio, clipping and
-padding) come from the oracle on the first 8,192 groups of q ("quality").
+workload on this host -- the first 65,536 groups of layer 0's q: split over
+up to 16 worker processes (the reported value), and on one core in-process;
+beside it, the one-group-at-a-time oracle (plain Python) on the first 1,024
+groups of that sample, on one core.  The codec's quality figures
+(reconstruction MSE, compression ratio, clipping and padding) come from the
+oracle on the first 8,192 groups of the same q ("quality").
 """
 
 import argparse
@@ -68,7 +73,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="layer", choices=["layer", "kv", "model", "ffn", "attn", "act", "copy"])
+    ap.add_argument("--workload", default="model", choices=["model", "layer", "kv", "ffn", "attn", "act", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-groups", type=int, default=65536)
     return ap.parse_args()
@@ -110,7 +115,10 @@ def d2d_copy_gbps(torch, nbytes=1 << 30, reps=20):
     return 2 * nbytes / sec / 1e9
 
 
-TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "decode_kernel__llama3-8b-layer__traffic.json")
+TRAFFIC_RECORDS = {
+    "model": os.path.join(ROOT, "profiles", "decode_kernel__llama3-8b-32-layers__traffic.json"),
+    "layer": os.path.join(ROOT, "profiles", "decode_kernel__llama3-8b-layer__traffic.json"),
+}
 DECODE_SOURCES = ["entropy_coded_group_amd/csrc/ecco_device.h", "entropy_coded_group_amd/csrc/ecco_kernels.hip",
                   "entropy_coded_group_amd/csrc/ecco_internal.h"]
 
@@ -124,12 +132,12 @@ def decode_sources_sha256():
     return h.hexdigest()
 
 
-def measured_traffic():
+def measured_traffic(workload):
     """HBM bytes per decode launch from the calibrated FETCH_SIZE / WRITE_SIZE
-    counters of a profiled run, or None when the decode sources have changed
-    since those counters were taken."""
+    counters of a profiled run of the workload, or None when the decode
+    sources have changed since those counters were taken."""
     try:
-        with open(TRAFFIC_RECORD) as fh:
+        with open(TRAFFIC_RECORDS[workload]) as fh:
             rec = json.load(fh)
     except (OSError, ValueError):
         return None
@@ -180,8 +188,14 @@ def oracle_quality(x_groups, tables_blob, t, n_groups):
     blocks, info = codec.encode_groups(x, tb, t, return_info=True)
     y = codec.decode_blocks(blocks, tb, t)
     rec = metrics.reconstruction(x.astype(np.float64), y.astype(np.float64))
+    # the ratio of the whole tensor over FP16, counting the side data the
+    # format needs (centroids, code lengths, t: 6,020 B) and, beside it, the
+    # library's whole table blob (which adds the derived midpoints, codes and
+    # decode look-up tables)
     out = dict(groups=int(x.shape[0]), mse=rec["mse"], rel_mse=rec["rel_mse"],
-               compression_ratio=metrics.compression_ratio(x_groups.shape[0], metrics.table_bytes_v1()))
+               compression_ratio=metrics.compression_ratio(x_groups.shape[0], metrics.table_bytes_v1()),
+               compression_ratio_library_blob=metrics.compression_ratio(x_groups.shape[0],
+                                                                        ecco.ecco_tables_size() + 4))
     out.update(metrics.padding_figures(info))
     out.update(metrics.index_entropy(info))
     return out
@@ -270,6 +284,98 @@ def graph_step_us(torch, stream, amax_jobs, encode_jobs, decode_jobs, gemv_jobs,
     e1.record(stream)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) * 1e3 / reps
+
+
+def bench_model(args, torch, ecco, W):
+    """The 32-layer weight set (see the module docstring).  Returns the timing
+    results and layer 0's q (host copy), its tables and scale for the CPU
+    baseline and the quality figures."""
+    stream = torch.cuda.current_stream()
+    t_setup = time.perf_counter()
+    blobs = {nm: train_tables(ecco, W.c2_sample(nm)) for nm in W.LAYER_ORDER}
+    tdev = {nm: ecco.tables_to_device(b) for nm, b in blobs.items()}
+    amax = torch.zeros((W.N_LAYERS, len(W.LAYER_ORDER)), dtype=torch.float32, device="cuda")
+    layers = []
+    for layer in range(W.N_LAYERS):
+        mats = {}
+        for nm in W.LAYER_ORDER:
+            w = W.c4_matrix(layer, nm)
+            out_f, in_f = w.shape
+            mats[nm] = dict(w=w, out_f=out_f, in_f=in_f, gpr=in_f // 128, groups=out_f * in_f // 128,
+                            blocks=torch.empty((out_f, in_f // 128, 64), dtype=torch.uint8, device="cuda"))
+        layers.append(mats)
+    # per-tensor scales: the step recomputes amax on the device; the scale is a
+    # host argument of the encode / decode calls, so it is fixed here from the
+    # same kernel's result
+    for layer, mats in enumerate(layers):
+        ecco.ecco_amax_many([(m["w"], m["w"].numel(), amax[layer, i:i + 1]) for i, m in enumerate(mats.values())])
+    torch.cuda.synchronize()
+    amax_host = amax.cpu().numpy()
+    for layer, mats in enumerate(layers):
+        for i, m in enumerate(mats.values()):
+            m["t"] = ecco.ecco_tensor_scale_from_amax(float(amax_host[layer, i]))
+    # one reused FP16 buffer of a layer's size; matrix m decodes into its slice
+    offs, o = {}, 0
+    for nm, m in layers[0].items():
+        offs[nm] = o
+        o += m["out_f"] * m["in_f"]
+    ybuf = torch.empty(o, dtype=torch.float16, device="cuda")
+    xin = {f: W.c5_x(1, f).cuda() for f in (4096, 14336)}
+    gy = {nm: torch.empty((1, m["out_f"]), dtype=torch.float32, device="cuda") for nm, m in layers[0].items()}
+    amax_jobs, encode_jobs, decode_jobs, gemv_jobs = [], [], [], []
+    for layer, mats in enumerate(layers):
+        amax_jobs.append([(m["w"], m["w"].numel(), amax[layer, i:i + 1]) for i, m in enumerate(mats.values())])
+        encode_jobs.append([(m["w"], m["out_f"], m["gpr"], m["in_f"], m["gpr"], tdev[nm], m["t"], m["blocks"], None)
+                            for nm, m in mats.items()])
+        decode_jobs.append([(m["blocks"], m["out_f"], m["gpr"], m["gpr"], m["in_f"], tdev[nm], m["t"], ybuf[offs[nm]:])
+                            for nm, m in mats.items()])
+        gemv_jobs.append([[(mats[nm]["blocks"], tdev[nm], mats[nm]["t"], mats[nm]["out_f"], mats[nm]["in_f"],
+                            xin[mats[nm]["in_f"]], gy[nm]) for nm in grp]
+                          for grp in (["q", "k", "v"], ["o"], ["gate", "up"], ["down"])])
+    setup = time.perf_counter() - t_setup
+    timer = Timer(torch, stream)
+
+    def step():
+        for jobs in amax_jobs:
+            timer.run("amax", lambda: ecco.ecco_amax_many(jobs))
+        for jobs in encode_jobs:
+            timer.run("encode", lambda: ecco.ecco_encode_many(jobs))
+        for jobs in decode_jobs:
+            timer.run("decode", lambda: ecco.ecco_decode_many(jobs))
+        for layer_jobs in gemv_jobs:
+            for jobs in layer_jobs:
+                timer.run("gemv", lambda: ecco.ecco_decode_gemv_many(jobs, 1))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    timer.collect()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ph = timer.collect()
+    groups = sum(m["groups"] for mats in layers for m in mats.values())
+    dec_t, enc_t = sum(ph["decode"]), sum(ph["encode"])
+    n_dec = len(ph["decode"])
+    res = dict(
+        wall=wall, groups=groups, setup_s=setup,
+        decode_GBps=groups * args.steps * BYTES_PER_GROUP / dec_t / 1e9,
+        encode_GBps=groups * args.steps * BYTES_PER_GROUP / enc_t / 1e9,
+        amax_GBps=groups * args.steps * 256 / sum(ph["amax"]) / 1e9,
+        decode_launch_us=dec_t / n_dec * 1e6, decode_launches=n_dec,
+        decode_launch_us_min=min(ph["decode"]) * 1e6, decode_launch_us_max=max(ph["decode"]) * 1e6,
+        decode_bytes_per_launch=groups // W.N_LAYERS * BYTES_PER_GROUP,
+        encode_us_per_layer=enc_t / args.steps / W.N_LAYERS * 1e6,
+        decode_us_per_layer=dec_t / args.steps / W.N_LAYERS * 1e6,
+        amax_us_per_layer=sum(ph["amax"]) / args.steps / W.N_LAYERS * 1e6,
+        gemv_b1_us_per_layer=sum(ph["gemv"]) / args.steps / W.N_LAYERS * 1e6,
+        step_device_ms=(dec_t + enc_t + sum(ph["amax"]) + sum(ph["gemv"])) / args.steps * 1e3,
+    )
+    q0 = layers[0]["q"]
+    x0 = q0["w"].cpu().numpy().reshape(-1, 128)
+    return res, (x0, blobs["q"], q0["t"])
 
 
 def bench_layer(args, torch, ecco, W):
@@ -382,6 +488,78 @@ def bench_layer(args, torch, ecco, W):
     return res, (x0, mats["q"]["blob"], mats["q"]["t"])
 
 
+METRIC = "decode GB/s (compressed in + fp16 out) and encode GB/s; % of HBM peak, 1 GPU"
+
+
+def common_line(args, res, workload, config):
+    return {
+        "metric": METRIC,
+        "value": round(res["decode_GBps"], 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["wall"] / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16 tensors, fp32 arithmetic, u8 blocks",
+        "data": "synthetic",
+        "config": config,
+        "encode_GBps": round(res["encode_GBps"], 1),
+        "decode_frac_of_hbm_peak": round(res["decode_GBps"] / HBM_PEAK_GBPS, 4),
+        "encode_frac_of_hbm_peak": round(res["encode_GBps"] / HBM_PEAK_GBPS, 4),
+        "decode_us_per_layer": round(res["decode_us_per_layer"], 2),
+        "encode_us_per_layer": round(res["encode_us_per_layer"], 2),
+        "amax_us_per_layer": round(res["amax_us_per_layer"], 2),
+        "gemv_b1_us_per_layer": round(res["gemv_b1_us_per_layer"], 2),
+        "roofline": {"bound": "hbm", "kernel": "decode_kernel",
+                     "achieved": round(res["decode_GBps"], 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(res["decode_GBps"] / HBM_PEAK_GBPS, 4),
+                     "bytes_per_launch": res["decode_bytes_per_launch"],
+                     "avg_launch_us": round(res["decode_launch_us"], 3),
+                     "traffic": measured_traffic(workload)},
+    }
+
+
+def model_line(args, res):
+    line = common_line(args, res, "model", {
+        "workload": "llama3-8b 32-layer weight set (224 matrices, 6.98e9 fp16 params, 54,525,952 groups)",
+        "groups": res["groups"], "layers": 32,
+        "step": "per layer: the 7 matrices' amax in one call; then per layer one encode launch; then per layer "
+                "one decode launch into a reused fp16 buffer (blocks written 31 layers earlier); then per layer "
+                "the fused decode+GEMV at b=1 in four calls (q+k+v, o, gate+up, down)",
+        "tables": "ecco_train_patterns on seeded 2^20-value samples, one set per matrix type"})
+    line.update({
+        "amax_GBps": round(res["amax_GBps"], 1),
+        "decode_launch_us_min_max": [round(res["decode_launch_us_min"], 2), round(res["decode_launch_us_max"], 2)],
+        "step_device_ms": round(res["step_device_ms"], 3),
+        "setup_s": round(res["setup_s"], 1),
+    })
+    return line
+
+
+def layer_line(args, res):
+    line = common_line(args, res, "layer", {
+        "workload": "llama3-8b-layer (q,k,v,o,gate,up,down; 1,703,936 groups)",
+        "groups": res["groups"],
+        "step": "the 7 matrices' amax in one call, encoded in one launch and decoded in one "
+                "launch; fused decode+GEMV at b=1 in four calls (q+k+v, o, gate+up, down)",
+        "tables": "ecco_train_patterns on seeded 2^20-value samples"})
+    line.update({
+        "encode_us_per_layer_one_call_per_matrix": round(res["encode_separate_us_per_layer"], 2),
+        "gemv_b1_us_per_layer_one_call_per_matrix": round(res["gemv_separate_us_per_layer"], 2),
+        "step_us_hip_graph_replay": None if res["graph_step_us"] is None else round(res["graph_step_us"], 2),
+        "amax_us_per_layer_one_call_per_matrix": round(res["amax_separate_us_per_layer"], 2),
+        "amax_GBps": round(res["groups"] * 256 / (res["amax_us_per_layer"] * 1e-6) / 1e9, 1),
+        "decode_us_per_matrix_separate_launches": {k: round(v, 2) for k, v in res["per_matrix_decode_us"].items()},
+        "speculative_decode_us_per_layer": round(res["spec_decode_us_per_layer"], 2),
+        "speculative_decode_GBps": round(res["groups"] * BYTES_PER_GROUP / (res["spec_decode_us_per_layer"] * 1e-6)
+                                         / 1e9, 1),
+    })
+    return line
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -395,77 +573,44 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     ecco.lib()
-    if args.workload != "layer":
+    if args.workload not in ("model", "layer"):
         from bench_workloads import run_workload          # noqa: E402
         line = run_workload(args, torch, ecco, W)
         print(json.dumps(line))
         return
-    res, (x0, blob0, t0) = bench_layer(args, torch, ecco, W)
-    copy = d2d_copy_gbps(torch)
-    line = {
-        "metric": "decode GB/s (compressed in + fp16 out), 1 GPU",
-        "value": round(res["decode_GBps"], 1),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(res["wall"] / args.steps * 1e3, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "fp16 tensors, fp32 arithmetic, u8 blocks",
-        "data": "synthetic",
-        "config": {"workload": "llama3-8b-layer (q,k,v,o,gate,up,down; 1,703,936 groups)",
-                   "groups": res["groups"],
-                   "step": "the 7 matrices' amax in one call, encoded in one launch and decoded in one "
-                           "launch; fused decode+GEMV at b=1 in four calls (q+k+v, o, gate+up, down)",
-                   "tables": "ecco_train_patterns on seeded 2^20-value samples"},
-        "encode_GBps": round(res["encode_GBps"], 1),
-        "decode_frac_of_hbm_peak": round(res["decode_GBps"] / HBM_PEAK_GBPS, 4),
-        "encode_frac_of_hbm_peak": round(res["encode_GBps"] / HBM_PEAK_GBPS, 4),
-        "decode_us_per_layer": round(res["decode_us_per_layer"], 2),
-        "encode_us_per_layer": round(res["encode_us_per_layer"], 2),
-        "encode_us_per_layer_one_call_per_matrix": round(res["encode_separate_us_per_layer"], 2),
-        "gemv_b1_us_per_layer": round(res["gemv_b1_us_per_layer"], 2),
-        "gemv_b1_us_per_layer_one_call_per_matrix": round(res["gemv_separate_us_per_layer"], 2),
-        "step_us_hip_graph_replay": None if res["graph_step_us"] is None else round(res["graph_step_us"], 2),
-        "amax_us_per_layer": round(res["amax_us_per_layer"], 2),
-        "amax_us_per_layer_one_call_per_matrix": round(res["amax_separate_us_per_layer"], 2),
-        "amax_GBps": round(res["groups"] * 256 / (res["amax_us_per_layer"] * 1e-6) / 1e9, 1),
-        "decode_us_per_matrix_separate_launches": {k: round(v, 2) for k, v in res["per_matrix_decode_us"].items()},
-        "speculative_decode_us_per_layer": round(res["spec_decode_us_per_layer"], 2),
-        "speculative_decode_GBps": round(res["groups"] * BYTES_PER_GROUP / (res["spec_decode_us_per_layer"] * 1e-6) / 1e9,
-                                         1),
-        "d2d_copy_GBps": round(copy, 1),
-        "roofline": {"bound": "hbm", "kernel": "decode_kernel",
-                     "achieved": round(res["decode_GBps"], 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(res["decode_GBps"] / HBM_PEAK_GBPS, 4),
-                     "bytes_per_launch": res["decode_bytes_per_launch"],
-                     "avg_launch_us": round(res["decode_launch_us"], 3),
-                     "traffic": measured_traffic()},
-    }
+    if args.workload == "model":
+        res, (x0, blob0, t0) = bench_model(args, torch, ecco, W)
+        line = model_line(args, res)
+        sample_of = "layer 0's q matrix"
+    else:
+        res, (x0, blob0, t0) = bench_layer(args, torch, ecco, W)
+        line = layer_line(args, res)
+        sample_of = "the q matrix"
+    line["d2d_copy_GBps"] = round(d2d_copy_gbps(torch), 1)
     if not args.no_cpu_baseline:
         workers = max(1, min(16, os.cpu_count() or 1))
         cb = cpu_baseline(x0, blob0, t0, args.cpu_groups, workers)
         line["cpu_baseline"] = {"value": round(cb["decode_GBps"], 5), "unit": "GB/s", "cores": cb["workers"],
                                 "kind": "oracle",
-                                "sample": "first %d groups of the q matrix: oracle encode then decode (NumPy), "
+                                "sample": "first %d groups of %s: oracle encode then decode (NumPy), "
                                           "split over %d process(es), %.2f s; one core in-process %.1f s" % (
-                                              cb["groups"], cb["workers"], cb["seconds"], cb["seconds_1core"]),
+                                              cb["groups"], sample_of, cb["workers"], cb["seconds"],
+                                              cb["seconds_1core"]),
                                 "encode_GBps": round(cb["encode_GBps"], 5),
                                 "decode_GBps_1core": round(cb["decode_GBps_1core"], 5),
                                 "encode_GBps_1core": round(cb["encode_GBps_1core"], 5),
                                 "cpu": cpu_model(), "host_cpus": os.cpu_count()}
         lit = literal_baseline(x0, blob0, t0, 1024)
         line["cpu_baseline"]["literal_oracle_1core"] = {
-            "sample": "first %d groups of the q matrix, one group at a time in plain Python, %.1f s" % (
-                lit["groups"], lit["seconds"]),
+            "sample": "first %d groups of %s, one group at a time in plain Python, %.1f s" % (
+                lit["groups"], sample_of, lit["seconds"]),
             "decode_GBps": round(lit["decode_GBps_1core"], 6), "encode_GBps": round(lit["encode_GBps_1core"], 6)}
         q = oracle_quality(x0, blob0, t0, 8192)
         line["quality"] = dict(
             {k: (round(v, 6) if isinstance(v, float) else v) for k, v in q.items()},
-            source="oracle encode + decode of the first %d groups of the q matrix; compression ratio of the "
-                   "whole q matrix over FP16, its side tables counted" % q["groups"])
+            source="oracle encode + decode of the first %d groups of %s; compression ratios of the whole matrix "
+                   "over FP16, counting the format's side data (6,020 B) or the library's table blob" % (
+                       q["groups"], sample_of))
     print(json.dumps(line))
 
 

@@ -1,7 +1,6 @@
-"""Secondary workloads of bench.py (see its docstring): kv, model, ffn, attn, act, copy."""
+"""Secondary workloads of bench.py (see its docstring): kv, ffn, attn, act, copy."""
 
 import os
-import time
 
 import numpy as np
 
@@ -119,67 +118,6 @@ def bench_kv(args, torch, ecco, W):
                  append_encode_us_16_patterns=round(np.mean(t_app16) * 1e6, 2),
                  append_encode_us_one_call_per_tensor=round(np.mean(t_app_sep) * 1e6, 2),
                  decode_us=round(np.mean(t_dec) * 1e6, 2))
-
-
-def bench_model(args, torch, ecco, W):
-    """32 LLaMA-3-8B-shaped layers encoded once; sustained decode of all 224
-    matrices, one launch per layer, into one reused FP16 buffer of a layer's
-    size.  Weights are drawn on the GPU (the
-    same recipe as workloads.llama_matrix, with torch's device generator) to
-    keep start-up short; the seven table sets of one layer are reused."""
-    tabs = {}
-    for nm in W.LAYER_ORDER:
-        blob = ecco.ecco_train_patterns(W.c2_sample(nm), threads=min(16, os.cpu_count() or 1))
-        tabs[nm] = ecco.tables_to_device(blob)
-    mats = []
-    gen = torch.Generator(device="cuda")
-    amax = torch.zeros(1, dtype=torch.float32, device="cuda")
-    t0 = time.time()
-    for layer in range(32):
-        for m, nm in enumerate(W.LAYER_ORDER):
-            out_f, in_f = W.LLAMA3_8B_LAYER[nm]
-            gen.manual_seed(100 + 10 * layer + m)
-            s = torch.exp(0.5 * torch.randn(out_f, 1, generator=gen, device="cuda"))
-            w = (s * torch.randn(out_f, in_f, generator=gen, device="cuda")).reshape(-1)
-            idx = torch.randint(0, w.numel(), (int(round(0.0005 * w.numel())),), generator=gen, device="cuda")
-            w[idx] *= 20.0
-            w = w.to(torch.float16).reshape(out_f, in_f)
-            ecco.ecco_amax(w, w.numel(), amax)
-            torch.cuda.synchronize()
-            t = ecco.ecco_tensor_scale_from_amax(amax.item())
-            blocks = torch.empty((out_f, in_f // 128, 64), dtype=torch.uint8, device="cuda")
-            ecco.ecco_encode(w, out_f, in_f // 128, in_f, in_f // 128, tabs[nm], t, blocks)
-            mats.append(dict(blocks=blocks, out_f=out_f, in_f=in_f, t=t, tdev=tabs[nm]))
-            del w, s, idx
-    torch.cuda.synchronize()
-    setup = time.time() - t0
-    groups = sum(m["out_f"] * m["in_f"] // 128 for m in mats)
-
-    # one launch per layer; each matrix goes to its own slice of the reused buffer
-    offs, o = [], 0
-    for m in mats[:7]:
-        offs.append(o)
-        o += m["out_f"] * m["in_f"]
-    ybuf = torch.empty(o, dtype=torch.float16, device="cuda")
-    layers = []
-    for layer in range(32):
-        layers.append([(m["blocks"], m["out_f"], m["in_f"] // 128, m["in_f"] // 128, m["in_f"], m["tdev"], m["t"],
-                        ybuf[offs[i]:]) for i, m in enumerate(mats[7 * layer:7 * layer + 7])])
-
-    def decode_all():
-        for jobs in layers:
-            ecco.ecco_decode_many(jobs)
-
-    steps = max(3, args.steps // 4)
-    ts = _timed(torch, decode_all, steps, max(1, args.warmup // 2))
-    dec = groups * BYTES_PER_GROUP / np.mean(ts) / 1e9
-    args.steps = steps
-    return _line("decode GB/s (compressed in + fp16 out), 1 GPU", dec, "GB/s", args, np.mean(ts) * 1e3,
-                 {"workload": "32-layer LLaMA-3-8B-shaped weights (224 matrices), sustained decode, one launch per layer",
-                  "groups": groups, "params": groups * 128,
-                  "weights": "device generator, same recipe as the layer workload"},
-                 decode_frac_of_hbm_peak=round(dec / HBM_PEAK_GBPS, 4),
-                 compressed_GB=round(groups * 64 / 1e9, 3), setup_s=round(setup, 1))
 
 
 def bench_ffn(args, torch, ecco, W):
@@ -341,5 +279,5 @@ def bench_copy(args, torch, ecco, W):
 
 
 def run_workload(args, torch, ecco, W):
-    return {"kv": bench_kv, "model": bench_model, "ffn": bench_ffn, "attn": bench_attn,
+    return {"kv": bench_kv, "ffn": bench_ffn, "attn": bench_attn,
             "act": bench_act, "copy": bench_copy}[args.workload](args, torch, ecco, W)

@@ -153,7 +153,11 @@ typedef struct {
  */
 size_t ecco_tables_size(void);
 
-/* Build a blob from centroids[64][15] (float32, each exactly representable in
+/* Build a blob from the per-tensor side data the pages describe: 64 shared
+ * patterns of 15 sorted centroids and 4 Huffman codebooks per pattern ("What
+ * carries the argument"; "Assumptions & free parameters": S = 64, H = 4),
+ * with code lengths of 2..8 bits (referee report, major comment 1).
+ * Build it from centroids[64][15] (float32, each exactly representable in
  * FP16, non-decreasing per pattern, within [-1, 1]) and code_len[64][4][16]
  * (each in [2, 8], every codebook a complete prefix code: Kraft sum exactly
  * 1).  Returns ECCO_ETABLES if the contents violate these rules (the blob is
@@ -171,11 +175,14 @@ int ecco_tables_validate(const void* tables_host);
 int ecco_tables_get(const void* tables_host, float* centroids_host, uint8_t* code_len_host);
 
 /* Learn tables offline from an FP16 sample (n_values a positive multiple of
- * 128) -- the calibration step of the pages ("patterns ... learned once on a
- * calibration set"; S = 64, H = 4): exact 1-D k-means of each normalised
+ * 128) -- the pages' calibration step, in which patterns and codebooks are
+ * learned once, offline, and then kept fixed ("Load-bearing premise";
+ * "Assumptions & free parameters": S = 64, H = 4; the pages give no
+ * procedure).  The steps taken here: exact 1-D k-means of each normalised
  * group, Lloyd k-means of those 15-vectors into 64 patterns, then per pattern
  * 4 codebooks by Lloyd iterations on code length with optimal 2..8-bit
- * lengths.  Host only; writes a valid blob to tables_host. */
+ * lengths (referee report, major comment 1).  Host only; writes a valid blob
+ * to tables_host. */
 int ecco_train_patterns(const uint16_t* sample_fp16_host, uint64_t n_values,
                         const ecco_train_opts_t* opts, void* tables_host);
 
@@ -185,7 +192,10 @@ float ecco_tensor_scale_from_amax(float amax);
 
 /* ---- device calls ---------------------------------------------------------- */
 
-/* amax_dev[0] = max |x| over n_values FP16 values (n_values >= 1; NaN ignored). */
+/* amax_dev[0] = max |x| over n_values FP16 values (n_values >= 1; NaN
+ * ignored): the tensor's largest magnitude, from which its FP16-to-FP8 scale
+ * t is taken (Fig. 4 caption; see ecco_tensor_scale_from_amax).  amax_dev is
+ * overwritten. */
 int ecco_amax(const uint16_t* x_dev, uint64_t n_values, float* amax_dev, void* stream);
 
 /* One tensor of an ecco_amax_many call: the arguments of ecco_amax. */
@@ -206,14 +216,24 @@ typedef struct {
  * identical to one ecco_amax call per job. */
 int ecco_amax_many(const ecco_amax_job_t* jobs_host, uint32_t n_jobs, void* stream);
 
-/* Encode n_rows x groups_per_row groups.  Group (r, g) is the 128 FP16
+/* Encode: each group of 128 FP16 values becomes one self-contained 64-byte
+ * block -- FP8 group scale, pattern chosen from the group's min and max,
+ * centroid indices coded with the shortest of the pattern's 4 codebooks,
+ * overflow clipped and spare bits filled with the largest remaining values
+ * ("Core claim"; "What carries the argument"; "Assumptions & free
+ * parameters": 128-value groups, 64-byte blocks, up to 16 padded values;
+ * compressor of Fig. 9 caption).  The rules are those of the block format
+ * above.
+ * Encode n_rows x groups_per_row groups.  Group (r, g) is the 128 FP16
  * values at x_dev + r * x_row_stride_elems + g * 128; its block goes to
  * blocks_dev + (r * blk_row_stride_blocks + g) * 64.  Weights [out, in]:
  * n_rows = out, groups_per_row = in / 128.  KV append in [B, H, S, D=128]:
  * n_rows = B * H, groups_per_row = tokens, x_row_stride_elems = S * 128,
  * blk_row_stride_blocks = S, pointers offset to the first new token.
  * tensor_scale must be finite and > 0.  stats_dev may be NULL.
- * ECCO_ESIZE if n_rows * groups_per_row is 0 or >= 2^32. */
+ * ECCO_ESIZE if n_rows or groups_per_row is 0 or >= 2^32, or their product
+ * is >= 2^32; ECCO_ESIZE also if n_rows > 1 and a row stride is shorter than
+ * a row. */
 int ecco_encode(const uint16_t* x_dev, uint64_t n_rows, uint64_t groups_per_row,
                 uint64_t x_row_stride_elems, uint64_t blk_row_stride_blocks,
                 const void* tables_dev, float tensor_scale, void* blocks_dev,
@@ -243,7 +263,12 @@ typedef struct {
  * identical to one ecco_encode call per job. */
 int ecco_encode_many(const ecco_encode_job_t* jobs_host, uint32_t n_jobs, void* stream);
 
-/* Decode: the inverse layout of ecco_encode; group (r, g) is written to
+/* Decode: every block is expanded back to 128 FP16 values on load, from its
+ * own bits and the tensor's side data alone ("The pith"; "Core claim";
+ * decompressor of Fig. 8 caption): codewords read while they fit, values
+ * c * |S| or S, clipped positions +0, then the padded values, exactly as the
+ * block format above states.
+ * The inverse layout of ecco_encode; group (r, g) is written to
  * y_dev + r * y_row_stride_elems + g * 128.  Every block decodes (the
  * decoder is total on arbitrary bits).  Same size rules as ecco_encode. */
 int ecco_decode(const void* blocks_dev, uint64_t n_rows, uint64_t groups_per_row,
@@ -299,12 +324,17 @@ typedef struct {
  * them. */
 int ecco_decode_many(const ecco_decode_job_t* jobs_host, uint32_t n_jobs, void* stream);
 
-/* Fused decode + GEMV: y[b][o] = sum_i W[o][i] * x[b][i] with W the decoded
+/* Fused decode + GEMV -- the decode-phase matrix-vector product whose weight
+ * traffic the format cuts (Fig. 12 caption: memory requests of a GEMM
+ * kernel; Fig. 11 caption and "If this is right": the gain is largest at
+ * small batch): the blocks are decoded on load and never written out.
+ * y[b][o] = sum_i W[o][i] * x[b][i] with W the decoded
  * FP16 weights, products and sums in FP32 (plain FMA on the vector ALUs).
  * blocks_dev holds W as [out_features][in_features / 128] blocks; x_dev is
  * [batch][in_features] FP16; y_dev is [batch][out_features] FP32 and is
  * overwritten.  ECCO_ESIZE unless in_features is a positive multiple of 128,
- * out_features >= 1 and 1 <= batch <= ECCO_GEMV_MAX_BATCH. */
+ * out_features in 1 .. 2^31 - 1, 1 <= batch <= ECCO_GEMV_MAX_BATCH and
+ * out_features * in_features / 128 < 2^32. */
 int ecco_decode_gemv(const void* blocks_dev, const void* tables_dev, float tensor_scale,
                      int64_t out_features, int64_t in_features,
                      const uint16_t* x_dev, int64_t batch, float* y_dev, void* stream);
@@ -350,7 +380,10 @@ int ecco_decode_gemv_many(const ecco_gemv_job_t* jobs_host, uint32_t n_jobs, int
  * FP32, overwritten.  workspace_dev (256-byte aligned) holds
  * ecco_attention_workspace_size(B, H_kv, G, S) bytes of caller memory that
  * the call uses for scores and partial sums; its contents are unspecified
- * afterwards.  ECCO_ESIZE unless B, H_kv, S >= 1 and G is 1, 2, 4 or 8. */
+ * afterwards.  ECCO_ESIZE unless B, H_kv, S >= 1, G is 1, 2, 4 or 8,
+ * B, H_kv and B * H_kv are below 2^20, S is below 2^24, S <= kv_stride_tokens
+ * < 2^32 and B * H_kv * kv_stride_tokens < 2^32.  The workspace size is 0 for
+ * B, H_kv or G beyond those limits. */
 size_t ecco_attention_workspace_size(uint64_t batch, uint64_t kv_heads, uint64_t group, uint64_t seq);
 int ecco_attention_decode(const void* k_blocks_dev, const void* k_tables_dev, float k_scale,
                           const void* v_blocks_dev, const void* v_tables_dev, float v_scale,

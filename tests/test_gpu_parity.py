@@ -6,7 +6,10 @@ fused decode+GEMV within |y - y_ref| <= 1e-3 * max(|y_ref|, sum|w x| / sqrt(in))
 of a float64 GEMV over oracle-decoded weights.  Small cases are compared
 element by element over several tiles and ragged tails; the full-size
 workloads (a LLaMA-3-8B layer's matrices, a 16x8x8192x128 KV cache, 70B FFN
-matrices) are compared on deterministic samples of groups / rows.
+matrices) have every block compared (the oracle's encode split over worker
+processes), and their decoded values on a deterministic sample of groups
+plus every group the oracle clips; the fused GEMV on sampled rows plus the
+rows holding the most clipped groups.
 """
 
 import os
@@ -17,6 +20,7 @@ import pytest
 
 import oracle
 from oracle import codec, gemv as ogemv
+import oracle_pool
 import workloads as W
 
 pytestmark = pytest.mark.gpu
@@ -604,13 +608,14 @@ def test_llama_layer_matrix_full_size_sampled(dev, name):
     yd = torch.empty_like(wd)
     ecco.ecco_decode(bd, out_f, in_f // 128, in_f // 128, in_f, tdev, t, yd)
     torch.cuda.synchronize()
-    idx = sample_index(G)
-    xg = w.numpy().reshape(-1, 128)[idx]
-    ob = codec.encode_groups(xg, tb, t)
+    say("c2 %s oracle encode of every group" % name)
+    ob, clipped, _ = oracle_pool.encode(w.numpy().reshape(-1, 128), tb, t)
     gb = bd.cpu().numpy().reshape(-1, 64)
-    assert_blocks_equal(gb[idx], ob, "c2 %s encode (sampled)" % name)
-    assert_fp16_equal(yd.cpu().numpy().reshape(-1, 128)[idx], codec.decode_blocks(ob, tb, t),
-                      "c2 %s decode (sampled)" % name)
+    assert_blocks_equal(gb, ob, "c2 %s encode" % name)
+    idx = np.union1d(sample_index(G), np.nonzero(clipped)[0])
+    say("c2 %s oracle decode of %d groups (%d clipped)" % (name, idx.size, int(clipped.sum())))
+    assert_fp16_equal(yd.cpu().numpy().reshape(-1, 128)[idx], oracle_pool.decode(ob[idx], tb, t),
+                      "c2 %s decode (sampled + clipped)" % name)
 
 
 def test_kv_cache_full_size_sampled(dev):
@@ -635,12 +640,13 @@ def test_kv_cache_full_size_sampled(dev):
         app = kv.numpy()[:, :, S - W.KV_APPEND:].reshape(-1, 128)
         ob_app = codec.encode_groups(app, tb, t)
         assert_blocks_equal(gb[:, :, S - W.KV_APPEND:].reshape(-1, 64), ob_app, "kv %s append" % kind)
-        idx = sample_index(B * H * S, 193)
-        xg = kv.numpy().reshape(-1, 128)[idx]
-        ob = codec.encode_groups(xg, tb, t)
-        assert_blocks_equal(gb.reshape(-1, 64)[idx], ob, "kv %s prefix (sampled)" % kind)
-        assert_fp16_equal(y.cpu().numpy().reshape(-1, 128)[idx], codec.decode_blocks(ob, tb, t),
-                          "kv %s decode (sampled)" % kind)
+        say("kv %s oracle encode of every group" % kind)
+        ob, clipped, _ = oracle_pool.encode(kv.numpy().reshape(-1, 128), tb, t)
+        assert_blocks_equal(gb.reshape(-1, 64), ob, "kv %s whole cache" % kind)
+        idx = np.union1d(sample_index(B * H * S, 193), np.nonzero(clipped)[0])
+        say("kv %s oracle decode of %d groups (%d clipped)" % (kind, idx.size, int(clipped.sum())))
+        assert_fp16_equal(y.cpu().numpy().reshape(-1, 128)[idx], oracle_pool.decode(ob[idx], tb, t),
+                          "kv %s decode (sampled + clipped)" % kind)
         del kvd, y, blocks
         torch.cuda.empty_cache()
 
@@ -750,11 +756,15 @@ def test_ffn70b_gemv_full_size_sampled(dev, name):
     ecco.ecco_encode(wd, out_f, in_f // 128, in_f, in_f // 128, tdev, t, bd)
     torch.cuda.synchronize()
     gb = bd.cpu().numpy()
-    rows = np.unique(np.r_[np.arange(0, out_f, 131 if name == "w1" else 41), out_f - 1])
-    wr = w.numpy()[rows].reshape(-1, 128)
-    ob = codec.encode_groups(wr, tb, t)
-    assert_blocks_equal(gb[rows].reshape(-1, 64), ob, "c5 %s encode (sampled rows)" % name)
-    w_hat = codec.decode_blocks(ob, tb, t).reshape(len(rows), in_f)
+    say("c5 %s oracle encode of every group" % name)
+    ob_all, clipped, _ = oracle_pool.encode(w.numpy().reshape(-1, 128), tb, t)
+    assert_blocks_equal(gb.reshape(-1, 64), ob_all, "c5 %s encode" % name)
+    # sampled rows plus the 16 rows that hold the most clipped groups
+    per_row = clipped.reshape(out_f, in_f // 128).sum(axis=1)
+    most_clipped = np.argsort(-per_row, kind="stable")[:16]
+    rows = np.unique(np.r_[np.arange(0, out_f, 131 if name == "w1" else 41), out_f - 1, most_clipped])
+    ob = ob_all.reshape(out_f, in_f // 128, 64)[rows].reshape(-1, 64)
+    w_hat = oracle_pool.decode(ob, tb, t).reshape(len(rows), in_f)
     for batch in (1, 4, 8):
         x = W.c5_x(batch, in_f).numpy()
         say("c5 %s gemv b=%d" % (name, batch))

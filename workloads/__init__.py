@@ -9,9 +9,11 @@ with heavy-tailed value distributions (per-channel scales, sparse large
 outliers, outlier channels in K).
 
 This module holds no arithmetic of the codec: it only draws numbers.  Every
-tensor is drawn on the CPU with a seeded ``torch.Generator`` in float32 and
-cast to float16 with round-to-nearest-even, so both the GPU path and the CPU
-oracle see identical inputs on any machine.
+tensor is drawn with a seeded ``torch.Generator`` in float32 and cast to
+float16 with round-to-nearest-even, so both the GPU path and the CPU oracle
+see identical inputs on any machine.  All are drawn on the CPU except the
+32-layer weight set (c4_matrix), which is drawn on the GPU it is encoded on;
+the oracle then reads a host copy of the same FP16 tensor.
 """
 
 import numpy as np
@@ -100,6 +102,29 @@ def c2_layer(layer=0, names=None):
     names = names or LAYER_ORDER
     return {nm: llama_matrix(LLAMA3_8B_LAYER[nm], 100 + 10 * layer + LAYER_ORDER.index(nm))
             for nm in names}
+
+
+N_LAYERS = 32
+
+
+def c4_matrix(layer, name, device="cuda"):
+    """Matrix `name` of layer `layer` of the 32-layer LLaMA-3-8B-shaped weight
+    set, drawn on `device` by torch's generator for that device (seed
+    100 + 10 layer + m, m the matrix's place in LAYER_ORDER): the layer
+    recipe of llama_matrix -- per-output-row LogNormal(0, 0.5) scales times
+    N(0, 1) entries, then 0.05 % of the entries (a randperm prefix) x20 --
+    drawn where the weights will live, so that 7e9 values take seconds to
+    make.  The same call gives the same tensor on any MI355X; a host copy of
+    it is what the oracle sees."""
+    m = LAYER_ORDER.index(name)
+    out_f, in_f = LLAMA3_8B_LAYER[name]
+    g = torch.Generator(device=device)
+    g.manual_seed(100 + 10 * int(layer) + m)
+    s = torch.exp(0.5 * torch.randn(out_f, 1, generator=g, device=device, dtype=torch.float32))
+    w = (s * torch.randn(out_f, in_f, generator=g, device=device, dtype=torch.float32)).reshape(-1)
+    idx = torch.randperm(w.numel(), generator=g, device=device)[:int(round(0.0005 * w.numel()))]
+    w[idx] = w[idx] * 20.0
+    return w.to(torch.float16).reshape(out_f, in_f)
 
 
 def c2_sample(name):
