@@ -22,7 +22,8 @@ __all__ = [
     "ecco_decode", "ecco_decode_speculative", "ecco_encode_many", "ecco_encode_act", "ecco_decode_act",
     "ecco_decode_many",
     "ecco_decode_gemv", "ecco_decode_gemv_many", "ecco_attention_workspace_size",
-    "ecco_attention_decode", "ecco_strerror", "ecco_version",
+    "ecco_attention_decode", "ecco_attention_decode_noalloc", "ecco_strerror", "ecco_version",
+    "ATTENTION_NOALLOC_MAX_WORKSPACE",
     "STATS_FIELDS", "DECODE_MAX_JOBS", "GEMV_MAX_JOBS", "AMAX_MAX_JOBS", "tables_to_device",
 ]
 
@@ -53,6 +54,7 @@ class TrainOpts(ctypes.Structure):
 DECODE_MAX_JOBS = 16
 GEMV_MAX_JOBS = 16
 AMAX_MAX_JOBS = 16
+ATTENTION_NOALLOC_MAX_WORKSPACE = 64 << 20
 
 
 class AmaxJob(ctypes.Structure):
@@ -115,6 +117,8 @@ def lib():
             "ecco_attention_workspace_size": (ctypes.c_size_t, [u64, u64, u64, u64]),
             "ecco_attention_decode": (i32, [vp, vp, f32, vp, vp, f32, vp, u64, u64, u64, u64, u64, f32, vp, vp,
                                             vp]),
+            "ecco_attention_decode_noalloc": (i32, [vp, vp, f32, vp, vp, f32, vp, u64, u64, u64, u64, u64, f32, vp,
+                                                    vp]),
             "ecco_strerror": (ctypes.c_char_p, [i32]),
             "ecco_version": (ctypes.c_char_p, []),
         }
@@ -335,6 +339,17 @@ def ecco_attention_decode(k_blocks, k_tables_dev, k_scale, v_blocks, v_tables_de
                                        _dptr(v_tables_dev), float(v_scale), _dptr(q, True), int(batch), int(kv_heads),
                                        int(group), int(seq), int(kv_stride_tokens), float(scale), _dptr(workspace),
                                        _dptr(out, True), _stream(stream)), "ecco_attention_decode")
+
+
+def ecco_attention_decode_noalloc(k_blocks, k_tables_dev, k_scale, v_blocks, v_tables_dev, v_scale, q, batch,
+                                  kv_heads, group, seq, kv_stride_tokens, scale, out, stream=None):
+    """ecco_attention_decode with the library's own static scratch in place of
+    a caller workspace (allocates nothing)."""
+    _check(lib().ecco_attention_decode_noalloc(_dptr(k_blocks), _dptr(k_tables_dev), float(k_scale), _dptr(v_blocks),
+                                               _dptr(v_tables_dev), float(v_scale), _dptr(q, True), int(batch),
+                                               int(kv_heads), int(group), int(seq), int(kv_stride_tokens),
+                                               float(scale), _dptr(out, True), _stream(stream)),
+           "ecco_attention_decode_noalloc")
 
 
 def ecco_strerror(code):

@@ -20,6 +20,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 
 #include "ecco_device.h"
 
@@ -281,11 +282,15 @@ extern "C" size_t ecco_attention_workspace_size(uint64_t batch, uint64_t kv_head
   return (size_t)(probs_bytes(pairs, group, seq) + part_bytes(pairs, group, seq));
 }
 
-extern "C" int ecco_attention_decode(const void* k_blocks, const void* k_tables, float k_scale, const void* v_blocks,
-                                     const void* v_tables, float v_scale, const uint16_t* q, uint64_t batch,
-                                     uint64_t kv_heads, uint64_t group, uint64_t seq, uint64_t kv_stride,
-                                     float scale, void* workspace, float* out, void* stream) {
-  if (!k_blocks || !k_tables || !v_blocks || !v_tables || !q || !workspace || !out) return ECCO_EINVAL;
+namespace {
+
+// Checks the arguments of an attention call (all but the workspace);
+// *pairs_out = batch * kv_heads.
+int check_attention_args(const void* k_blocks, const void* k_tables, float k_scale, const void* v_blocks,
+                         const void* v_tables, float v_scale, const uint16_t* q, uint64_t batch,
+                         uint64_t kv_heads, uint64_t group, uint64_t seq, uint64_t kv_stride, float scale,
+                         float* out, uint64_t* pairs_out) {
+  if (!k_blocks || !k_tables || !v_blocks || !v_tables || !q || !out) return ECCO_EINVAL;
   for (float t : {k_scale, v_scale})
     if (!(t > 0.0f) || !(t < __builtin_huge_valf())) return ECCO_EINVAL;
   if (!(std::fabs(scale) < __builtin_huge_valf())) return ECCO_EINVAL;
@@ -298,9 +303,17 @@ extern "C" int ecco_attention_decode(const void* k_blocks, const void* k_tables,
       pairs * ((seq + 63) / 64) >= (1ull << 31))
     return ECCO_ESIZE;
   if (!host_aligned(k_blocks, 64) || !host_aligned(v_blocks, 64) || !host_aligned(k_tables, 256) ||
-      !host_aligned(v_tables, 256) || !host_aligned(q, 16) || !host_aligned(workspace, kWsAlign) ||
-      !host_aligned(out, 16))
+      !host_aligned(v_tables, 256) || !host_aligned(q, 16) || !host_aligned(out, 16))
     return ECCO_EALIGN;
+  *pairs_out = pairs;
+  return ECCO_OK;
+}
+
+// Enqueues the four attention kernels with `workspace` (device memory of
+// ecco_attention_workspace_size bytes) for the scores and partial sums.
+int launch_attention(const void* k_blocks, const void* k_tables, float k_scale, const void* v_blocks,
+                     const void* v_tables, float v_scale, const uint16_t* q, uint64_t pairs, uint64_t group,
+                     uint64_t seq, uint64_t kv_stride, float scale, void* workspace, float* out, void* stream) {
   int cus = 0, rc = check_gfx950(&cus);
   if (rc) return rc;
   AttnArgs a;
@@ -350,4 +363,70 @@ extern "C" int ecco_attention_decode(const void* k_blocks, const void* k_tables,
   const uint64_t n = (uint64_t)rows * 128u;
   hipLaunchKernelGGL(attn_combine_kernel, dim3((uint32_t)((n + 255) / 256)), dim3(256), 0, s, a);
   return hipGetLastError() == hipSuccess ? ECCO_OK : ECCO_EHIP;
+}
+
+constexpr uint64_t kScratchBytes = ECCO_ATTENTION_NOALLOC_MAX_WORKSPACE;
+static_assert(kScratchBytes % kWsAlign == 0, "scratch size");
+
+}  // namespace
+
+namespace ecco {
+// Scratch of the allocation-free entry point: one array per GPU the library
+// runs on, held until the process ends.  In host code `scratch` only names
+// the symbol; its device address comes from hipGetSymbolAddress, once per
+// device, and only that address is ever handed to a kernel.
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+}  // namespace ecco
+
+namespace {
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64];
+
+// The calling thread's current device's copy of `scratch`, or nullptr.
+void* scratch_address() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" int ecco_attention_decode(const void* k_blocks, const void* k_tables, float k_scale, const void* v_blocks,
+                                     const void* v_tables, float v_scale, const uint16_t* q, uint64_t batch,
+                                     uint64_t kv_heads, uint64_t group, uint64_t seq, uint64_t kv_stride,
+                                     float scale, void* workspace, float* out, void* stream) {
+  uint64_t pairs = 0;
+  const int rc = check_attention_args(k_blocks, k_tables, k_scale, v_blocks, v_tables, v_scale, q, batch, kv_heads,
+                                      group, seq, kv_stride, scale, out, &pairs);
+  if (rc) return rc;
+  if (!workspace) return ECCO_EINVAL;
+  if (!host_aligned(workspace, kWsAlign)) return ECCO_EALIGN;
+  return launch_attention(k_blocks, k_tables, k_scale, v_blocks, v_tables, v_scale, q, pairs, group, seq, kv_stride,
+                          scale, workspace, out, stream);
+}
+
+extern "C" int ecco_attention_decode_noalloc(const void* k_blocks, const void* k_tables, float k_scale,
+                                             const void* v_blocks, const void* v_tables, float v_scale,
+                                             const uint16_t* q, uint64_t batch, uint64_t kv_heads, uint64_t group,
+                                             uint64_t seq, uint64_t kv_stride, float scale, float* out,
+                                             void* stream) {
+  uint64_t pairs = 0;
+  int rc = check_attention_args(k_blocks, k_tables, k_scale, v_blocks, v_tables, v_scale, q, batch, kv_heads, group,
+                                seq, kv_stride, scale, out, &pairs);
+  if (rc) return rc;
+  if (probs_bytes(pairs, group, seq) + part_bytes(pairs, group, seq) > kScratchBytes) return ECCO_ESIZE;
+  int cus = 0;
+  rc = check_gfx950(&cus);
+  if (rc) return rc;
+  void* ws = scratch_address();
+  if (!ws) return ECCO_EHIP;
+  return launch_attention(k_blocks, k_tables, k_scale, v_blocks, v_tables, v_scale, q, pairs, group, seq, kv_stride,
+                          scale, ws, out, stream);
 }

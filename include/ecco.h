@@ -391,6 +391,26 @@ int ecco_attention_decode(const void* k_blocks_dev, const void* k_tables_dev, fl
                           uint64_t seq, uint64_t kv_stride_tokens, float scale,
                           void* workspace_dev, float* out_dev, void* stream);
 
+/* ecco_attention_decode without the workspace argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  The scores and partial sums go to
+ * a static device array of ECCO_ATTENTION_NOALLOC_MAX_WORKSPACE bytes that
+ * the library holds on each GPU it runs on until the process ends; the call
+ * allocates and frees nothing.  Everything else -- arguments, layout,
+ * results, errors -- is as for ecco_attention_decode; in addition
+ * ECCO_ESIZE when ecco_attention_workspace_size(B, H_kv, G, S) exceeds
+ * ECCO_ATTENTION_NOALLOC_MAX_WORKSPACE, and ECCO_EHIP if the array's device
+ * address cannot be obtained.  Calls on one GPU share its array: calls that
+ * overlap on that GPU (different streams, or host threads) race, so a
+ * caller orders them on one stream.  Every byte a call reads from the array
+ * it has written earlier in the same call, so nothing needs clearing. */
+#define ECCO_ATTENTION_NOALLOC_MAX_WORKSPACE (64ull << 20)
+int ecco_attention_decode_noalloc(const void* k_blocks_dev, const void* k_tables_dev, float k_scale,
+                                  const void* v_blocks_dev, const void* v_tables_dev, float v_scale,
+                                  const uint16_t* q_dev, uint64_t batch, uint64_t kv_heads, uint64_t group,
+                                  uint64_t seq, uint64_t kv_stride_tokens, float scale, float* out_dev,
+                                  void* stream);
+
 const char* ecco_strerror(int code);
 
 /* Library version string, e.g. "ecco 1.0 (format v1, gfx950)". */

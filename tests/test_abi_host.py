@@ -357,6 +357,19 @@ def test_attention_checks_arguments_before_touching_the_device():
     assert call(b=1 << 33, h=1 << 31) == -3
     assert call(stride=1 << 63) == -3
     assert ecco.ecco_attention_workspace_size(1 << 33, 1 << 31, 4, 100) == 0
+    # the allocation-free variant: the same checks, and a workspace beyond its
+    # static scratch (16 x 8 pairs, G = 8, 16,384 tokens: 128 MiB) refused
+    # before the device is touched
+    args_na = args[:13] + args[14:]
+    assert L.ecco_attention_decode_noalloc(*[None] + args_na[1:]) == -1
+    big = list(args_na)
+    big[7:12] = [16, 8, 8, 16384, 16384]
+    assert ecco.ecco_attention_workspace_size(16, 8, 8, 16384) > ecco.ATTENTION_NOALLOC_MAX_WORKSPACE
+    assert L.ecco_attention_decode_noalloc(*big) == -3
+    fits = list(args_na)
+    fits[7:12] = [16, 8, 4, 8192, 8192]
+    assert ecco.ecco_attention_workspace_size(16, 8, 4, 8192) <= ecco.ATTENTION_NOALLOC_MAX_WORKSPACE
+    assert L.ecco_attention_decode_noalloc(*fits) not in (0, -1, -2, -3)   # a device error here: no GPU
     # workspace: scores [B*H][S][G] floats and partial sums [B*H][ceil(S/128)][G][128] floats, 256-aligned
     def up(v):
         return (v + 255) // 256 * 256
