@@ -13,7 +13,7 @@
 namespace ecco {
 
 constexpr uint32_t kMagic = 0x31434345u;   // "ECC1"
-constexpr uint32_t kVersion = 1;
+constexpr uint32_t kVersion = 2;
 constexpr int G = ECCO_GROUP;
 constexpr int S = ECCO_N_PATTERNS;
 constexpr int C = ECCO_N_CENTROIDS;
@@ -40,7 +40,8 @@ struct alignas(256) Tables {
   float midpoints[S][16];       // [p][0..13] (c_k + c_k+1) * 0.5f, [14], [15] = +inf
   float c0c14[S][2];            // first and last centroid of each pattern
   uint32_t len4[S][A];          // byte h = code_len[p][h][s]
-  uint16_t enc[S][H][A];        // bits 0..7 codeword in stream order (bit-reversed), bits 8..11 length
+  uint32_t enc[S][H][A];        // canonical codeword left-aligned (bits 32 - len .. 31, most significant
+                                // code bit at bit 31), 32 - len in bits 0..4
   float fp8_value[256];         // exact value of every E4M3FN code (NaN for 0x7F, 0xFF)
   uint8_t lut[S][H][256];       // decode look-up table
 };

@@ -175,8 +175,8 @@ __device__ __forceinline__ void sort8_desc(uint32_t (&k)[8]) {
 struct EncodeSmem {
   float mid[S * 16];
   float c0c14[S * 2];
-  uint32_t len4[S * A];
-  uint16_t enc[S * H * A];
+  uint32_t len4[16 + S * A];         // entry (p, s) at 16 + 16 p + s: index 16 p + u for tree leaf u = 16 + s
+  uint32_t enc[16 + S * H * A];      // entry (p, h, s) at 16 + 16 (4 p + h) + s, likewise
   float thr[kEncWaves][16][16];      // threshold tree of each group of a wave
   uint32_t out[kEncWaves][16][16];    // block words of each group of a wave
 };
@@ -193,8 +193,30 @@ struct EncGeom {
   static constexpr int GPW = 64 / LPG;            // groups per wave
 };
 
-// (At least four waves per SIMD: the compiler is held to 128 VGPRs, which the
-// kernel fits without spilling; left to itself it takes 135 and three waves.)
+// One step down the quantiser's threshold tree: u' = 2 u + (x > t).  The
+// compare writes VCC and the add-with-carry reads it, two instructions where
+// a compare, a select and a shift-or would take three.
+__device__ __forceinline__ uint32_t tree_step(uint32_t u, float x, float t) {
+  uint32_t r;
+  asm("v_cmp_gt_f32 vcc, %1, %2\n\tv_addc_co_u32 %0, vcc, %3, %3, vcc" : "=v"(r) : "v"(x), "v"(t), "v"(u) : "vcc");
+  return r;
+}
+
+// Sort key of one FP16 value of a group, from the 32-bit word holding it
+// (HI: the upper half): |x| in bits 17..31, the sign in bit 0, and
+// (15 - i) << 1 for the value's place i among the lane's 16.  A funnel shift
+// brings |x| and the sign into place (the other half's bits land in 1..16 and
+// are masked off).  The lane's part of the group index is OR-ed in where keys
+// of different lanes meet (OR of (7 - lane) << 5): keys then order by |x|,
+// ties going to the lower index, and are unique within a group.
+template <bool HI>
+__device__ __forceinline__ uint32_t value_key(uint32_t w, uint32_t i) {
+  const uint32_t f = __builtin_amdgcn_alignbit(w, w, HI ? 31u : 15u);
+  return (f & 0xfffe0001u) | ((15u - i) << 1);
+}
+__device__ __forceinline__ float key_value(uint32_t k) { return f16_value((k >> 17) | ((k & 1u) << 15)); }
+
+// (At least four waves per SIMD: the compiler is held to 128 VGPRs.)
 template <int GS>
 __global__ __launch_bounds__(kEncWaves * 64, 4) void encode_kernel(EncodeArgs args) {
   uint32_t jj = 0;
@@ -205,18 +227,20 @@ __global__ __launch_bounds__(kEncWaves * 64, 4) void encode_kernel(EncodeArgs ar
   using EG = EncGeom<GS>;
   constexpr int NV = EG::NV, NL = EG::NL, LPG = EG::LPG, GPW = EG::GPW;
   static_assert((LPG == 8 || LPG == 4) && GPW <= 16, "EncodeSmem holds 16 groups per wave");
+  static_assert(NV == 16, "value_key places 16 values per lane");
   constexpr uint32_t RB = Geo::kRecBits;
   constexpr int NSLOT = 16 / LPG;           // outlier records (and thresholds) per lane
   __shared__ EncodeSmem sm;
   const uint32_t tid = threadIdx.x;
   for (uint32_t i = tid; i < S * 16; i += blockDim.x) sm.mid[i] = (&a.tab->midpoints[0][0])[i];
   for (uint32_t i = tid; i < S * 2; i += blockDim.x) sm.c0c14[i] = (&a.tab->c0c14[0][0])[i];
-  for (uint32_t i = tid; i < S * A; i += blockDim.x) sm.len4[i] = (&a.tab->len4[0][0])[i];
-  for (uint32_t i = tid; i < S * H * A; i += blockDim.x) sm.enc[i] = (&a.tab->enc[0][0][0])[i];
+  for (uint32_t i = tid; i < S * A; i += blockDim.x) sm.len4[16 + i] = (&a.tab->len4[0][0])[i];
+  for (uint32_t i = tid; i < S * H * A; i += blockDim.x) sm.enc[16 + i] = (&a.tab->enc[0][0][0])[i];
   __syncthreads();
 
   const uint32_t lane = lane_id(), wave = tid >> 6;
   const uint32_t q = lane / LPG, tl = lane % LPG;
+  const uint32_t lane_bits = (7u - tl) << 5;    // the lane's part of a key's index field
   const float t = a.t, inv_t = a.inv_t;
   const int n_search_lane = (int)(a.tab->n_search / LPG);
   float* thr = sm.thr[wave][q];
@@ -253,43 +277,46 @@ __global__ __launch_bounds__(kEncWaves * 64, 4) void encode_kernel(EncodeArgs ar
       row = div_magic(gidx, a.gpr);
       col = gidx - row * a.gpr.d;
     }
-    uint32_t hb[NV];
+    uint32_t wd[NV / 2];                   // the lane's values as 8 words of two FP16 each
 #pragma unroll
     for (int c = 0; c < NL; ++c) {
-      const uint4 w = raw.v[c];
-      hb[8 * c + 0] = w.x & 0xffffu;
-      hb[8 * c + 1] = w.x >> 16;
-      hb[8 * c + 2] = w.y & 0xffffu;
-      hb[8 * c + 3] = w.y >> 16;
-      hb[8 * c + 4] = w.z & 0xffffu;
-      hb[8 * c + 5] = w.z >> 16;
-      hb[8 * c + 6] = w.w & 0xffffu;
-      hb[8 * c + 7] = w.w >> 16;
+      wd[4 * c + 0] = raw.v[c].x;
+      wd[4 * c + 1] = raw.v[c].y;
+      wd[4 * c + 2] = raw.v[c].z;
+      wd[4 * c + 3] = raw.v[c].w;
     }
     float xf[NV];
     uint32_t key[NV];
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      xf[i] = f16_value(hb[i]);
-      const uint32_t j = NV * tl + i;
-      key[i] = ((hb[i] & 0x7fffu) << 8) | ((127u - j) << 1) | (hb[i] >> 15);
+    for (int k = 0; k < NV / 2; ++k) {
+      xf[2 * k] = f16_value(wd[k] & 0xffffu);
+      xf[2 * k + 1] = f16_value(wd[k] >> 16);
+      key[2 * k] = value_key<false>(wd[k], 2 * k);
+      key[2 * k + 1] = value_key<true>(wd[k], 2 * k + 1);
     }
     // 1. scale element: largest |x|, lowest index on ties
     uint32_t km = key[0];
 #pragma unroll
     for (int i = 1; i < NV; ++i) km = max(km, key[i]);
-    km = seg_max_u32<LPG>(km);
-    const float xs = f16_value((km >> 8) | ((km & 1u) << 15));
+    km = seg_max_u32<LPG>(km | lane_bits);
+    // the lane that holds it compares its own keys with km's lane-free part;
+    // the others with a value no key takes
+    const uint32_t km_own = ((km ^ lane_bits) & 0xe0u) == 0u ? (km & ~0xe0u) : 0xffffffffu;
+    const float xs = key_value(km);
     const uint32_t s8 = fp8_encode(xs * inv_t);
     const float S = fp8_decode<0>(s8) * t;
     const float aa = fabsf(S);
-    // 2. min / max of the other GS - 1 values (the scale element, whose key
-    //    is km, counts as +inf for the min and -inf for the max)
+    // 2. min / max of the other GS - 1 values: the scale element counts as
+    //    +inf for the min and -inf for the max.  xq, the quantiser's input,
+    //    also holds +inf there: it then walks to the tree's last leaf, which
+    //    no finite value reaches, and that leaf is symbol 15.
     float mn = __builtin_inff(), mx = -__builtin_inff();
+    float xq[NV];
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      const bool s = key[i] == km;
-      mn = fminf(mn, s ? __builtin_inff() : xf[i]);
+      const bool s = key[i] == km_own;
+      xq[i] = s ? __builtin_inff() : xf[i];
+      mn = fminf(mn, xq[i]);
       mx = fmaxf(mx, s ? -__builtin_inff() : xf[i]);
     }
     mn = seg_min_f32<LPG>(mn);
@@ -315,72 +342,75 @@ __global__ __launch_bounds__(kEncWaves * 64, 4) void encode_kernel(EncodeArgs ar
     const uint32_t fmin = seg_min_u32<LPG>(__float_as_uint(bf));
     const uint32_t pstar = seg_min_u32<LPG>(__float_as_uint(bf) == fmin ? bp : 63u) & 63u;
     // 4. quantise: sym = #{k : x > m_pk * a}.  The 15 thresholds (m_p14 * a
-    //    taken as +inf) sit in LDS as an implicit binary tree, node 1 the
-    //    root and node u's children 2u and 2u + 1 (lane tl writes thresholds
-    //    tl, tl + LPG, ... to their nodes); four compares walk it, the root
-    //    one against a register copy.
+    //    taken as the largest finite float) sit in LDS as an implicit binary
+    //    tree, node 1 the root and node u's children 2u and 2u + 1 (lane tl
+    //    writes thresholds tl, tl + LPG, ... to their nodes); four compares
+    //    walk it, the root one against a register copy, ending at leaf
+    //    u = 16 + sym.  For finite x, x > m_p14 * a never holds either way.
 #pragma unroll
     for (int sl = 0; sl < NSLOT; ++sl) {
       const uint32_t k = tl + LPG * sl;
-      if (k < 15u) thr[enode(k)] = k < 14u ? sm.mid[pstar * 16u + k] * aa : __builtin_inff();
+      if (k < 15u) thr[enode(k)] = k < 14u ? sm.mid[pstar * 16u + k] * aa : 3.40282347e38f;
     }
     wave_sync();
     const float root = thr[1];
-    uint32_t sym[NV];
-    uint32_t l4 = 0;                       // four byte counters (codebooks 0..3): at most 16 x 8
+    const uint32_t* len_p = sm.len4 + 16u * pstar;       // len_p[u] = lengths of symbol u - 16
+    uint32_t leaf[NV];
+    uint32_t l4c[NL * 2];                  // per 4 values: four byte counters (codebooks 0..3)
+#pragma unroll
+    for (int c = 0; c < NL * 2; ++c) l4c[c] = 0;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      uint32_t u = xf[i] > root ? 3u : 2u;
-      u = u + u + (xf[i] > thr[u] ? 1u : 0u);
-      u = u + u + (xf[i] > thr[u] ? 1u : 0u);
-      u = u + u + (xf[i] > thr[u] ? 1u : 0u);
-      sym[i] = key[i] == km ? 15u : u - 16u;
-      l4 += sm.len4[pstar * 16u + sym[i]];
+      uint32_t u = xq[i] > root ? 3u : 2u;
+      u = tree_step(u, xq[i], thr[u]);
+      u = tree_step(u, xq[i], thr[u]);
+      u = tree_step(u, xq[i], thr[u]);
+      leaf[i] = u;
+      l4c[i / 4] += len_p[u];
     }
     // 5. codebook with the shortest stream, lowest h on ties
+    const uint32_t l4 = (l4c[0] + l4c[1]) + (l4c[2] + l4c[3]);
     uint32_t l02 = seg_add_u32<LPG>(l4 & 0x00ff00ffu), l13 = seg_add_u32<LPG>((l4 >> 8) & 0x00ff00ffu);
     uint32_t Lh[4] = {l02 & 0xffffu, l13 & 0xffffu, l02 >> 16, l13 >> 16};
     uint32_t hstar = 0, L = Lh[0];
 #pragma unroll
     for (int h = 1; h < 4; ++h)
       if (Lh[h] < L) { L = Lh[h]; hstar = h; }
-    // 6. codewords: lane-local concatenation (each 8 values at most 64 bits),
-    //    segment scan for positions, OR into the block
-    uint64_t acc[NL];
-    uint32_t offs[NL];
-    const uint32_t eb = (pstar * 4u + hstar) * 16u;
-#pragma unroll
-    for (int c = 0; c < NL; ++c) {
-      acc[c] = 0;
-      offs[c] = 0;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t e = sm.enc[eb + sym[8 * c + i]];
-        acc[c] |= (uint64_t)(e & 0xffu) << offs[c];
-        offs[c] += e >> 8;
-      }
-    }
+    // 6. codewords, four values (at most 32 bits) at a time: an entry holds
+    //    the canonical codeword left-aligned and 32 - len in its low bits, so
+    //    one funnel shift appends it (acc = acc << len | code); the part's
+    //    bits are then reversed into stream order.  A segment scan gives each
+    //    lane's position; the parts are OR-ed into the block's words, and
+    //    bits past 511 fall off, which is exactly the clipping rule.
+    const uint32_t* enc_ph = sm.enc + 16u * (pstar * 4u + hstar);   // enc_ph[u] for symbol u - 16
+    uint32_t part[NL * 2], plen[NL * 2];
     uint32_t off = 0;
 #pragma unroll
-    for (int c = 0; c < NL; ++c) off += offs[c];
+    for (int c = 0; c < NL * 2; ++c) {
+      uint32_t acc = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t e = enc_ph[leaf[4 * c + i]];
+        acc = __builtin_amdgcn_alignbit(acc, e, e);
+      }
+      plen[c] = (l4c[c] >> (8u * hstar)) & 0xffu;
+      part[c] = __builtin_bitreverse32(acc) >> ((0u - plen[c]) & 31u);
+      off += plen[c];
+    }
 #pragma unroll
     for (int sl = 0; sl < NSLOT; ++sl) out[tl + LPG * sl] = 0;
     const uint32_t incl = seg_scan_add<LPG>(off, tl);
     const uint32_t pos = 16u + incl - off;
     wave_sync();
     {
-      // each part's <= 64 bits land in words w, w + 1, w + 2; words past 15
-      // are beyond bit 512 and dropped, which is exactly the clipping rule
       uint32_t pp = pos;
 #pragma unroll
-      for (int c = 0; c < NL; ++c) {
-        const uint32_t w = pp >> 5, sh = pp & 31u;
-        const uint64_t low = acc[c] << sh;
-        const uint32_t top = sh ? (uint32_t)(acc[c] >> (64u - sh)) : 0u;
-        if (w < 16u && (uint32_t)low) atomicOr(&out[w], (uint32_t)low);
-        if (w + 1u < 16u && (uint32_t)(low >> 32)) atomicOr(&out[w + 1u], (uint32_t)(low >> 32));
-        if (w + 2u < 16u && top) atomicOr(&out[w + 2u], top);
-        pp += offs[c];
+      for (int c = 0; c < NL * 2; ++c) {
+        const uint32_t w = pp >> 5;
+        const uint64_t v = (uint64_t)part[c] << (pp & 31u);
+        if (w < 16u && (uint32_t)v) atomicOr(&out[w], (uint32_t)v);
+        if (w + 1u < 16u && (uint32_t)(v >> 32)) atomicOr(&out[w + 1u], (uint32_t)(v >> 32));
+        pp += plen[c];
       }
     }
     const bool clipped = 16u + L > 512u;
@@ -393,7 +423,8 @@ __global__ __launch_bounds__(kEncWaves * 64, 4) void encode_kernel(EncodeArgs ar
     //    another round.  For a few rounds the lane's keys are searched and
     //    cleared in place; for more, the lane first sorts each 8 of its keys
     //    (descending, 19 compare-exchanges) so that a round only compares the
-    //    lists' heads and the owner of the largest shifts its list.
+    //    lists' heads and the owner of the largest shifts its list.  Here the
+    //    keys carry their lane's index bits, so they are unique in the group.
     uint32_t mykey[NSLOT];
 #pragma unroll
     for (int sl = 0; sl < NSLOT; ++sl) mykey[sl] = 0;
@@ -402,7 +433,7 @@ __global__ __launch_bounds__(kEncWaves * 64, 4) void encode_kernel(EncodeArgs ar
 #pragma unroll
       for (int c = 0; c < NL; ++c) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) k8[c][i] = key[8 * c + i];
+        for (int i = 0; i < 8; ++i) k8[c][i] = key[8 * c + i] == km_own ? 0u : key[8 * c + i] | lane_bits;
         sort8_desc(k8[c]);
       }
       auto pop = [&](uint32_t m) {
@@ -414,7 +445,6 @@ __global__ __launch_bounds__(kEncWaves * 64, 4) void encode_kernel(EncodeArgs ar
           k8[c][7] = own ? 0u : k8[c][7];
         }
       };
-      pop(km);                             // the scale element heads one list
       for (uint32_t rr = 0;; ++rr) {
         uint32_t head = k8[0][0];
 #pragma unroll
@@ -427,7 +457,7 @@ __global__ __launch_bounds__(kEncWaves * 64, 4) void encode_kernel(EncodeArgs ar
       }
     } else if (__any(n > 0u)) {
 #pragma unroll
-      for (int i = 0; i < NV; ++i) key[i] = key[i] == km ? 0u : key[i];
+      for (int i = 0; i < NV; ++i) key[i] = key[i] == km_own ? 0u : key[i] | lane_bits;
       for (uint32_t rr = 0;; ++rr) {
         uint32_t m = key[0];
 #pragma unroll
@@ -445,8 +475,7 @@ __global__ __launch_bounds__(kEncWaves * 64, 4) void encode_kernel(EncodeArgs ar
       const uint32_t r = tl + LPG * sl;
       if (r < n) {
         const uint32_t j = 127u - ((mykey[sl] >> 1) & 127u);
-        const float xv = f16_value((mykey[sl] >> 8) | ((mykey[sl] & 1u) << 15));
-        const uint32_t myrec = j | (fp8_encode(xv * inv_t) << Geo::kPosBits);
+        const uint32_t myrec = j | (fp8_encode(key_value(mykey[sl]) * inv_t) << Geo::kPosBits);
         const uint32_t rp = 512u - RB * (r + 1u);
         const uint32_t w = rp >> 5, sh = rp & 31u;
         atomicOr(&out[w], myrec << sh);
@@ -470,13 +499,14 @@ __global__ __launch_bounds__(kEncWaves * 64, 4) void encode_kernel(EncodeArgs ar
       uint32_t e = pos, ends = 0;
 #pragma unroll
       for (int i = 0; i < NV; ++i) {
-        e += sm.enc[eb + sym[i]] >> 8;
+        e += 32u - (enc_ph[leaf[i]] & 31u);
         ends += e <= 512u ? 1u : 0u;
       }
       const uint32_t k = seg_add_u32<LPG>(ends);
       bool nonfin = false;
 #pragma unroll
-      for (int i = 0; i < NV; ++i) nonfin |= (hb[i] & 0x7c00u) == 0x7c00u;
+      for (int i = 0; i < NV / 2; ++i)
+        nonfin |= (wd[i] & 0x7c00u) == 0x7c00u || (wd[i] & 0x7c000000u) == 0x7c000000u;
       const uint32_t nf = seg_max_u32<LPG>(nonfin ? 1u : 0u);
       if (valid && tl == 0) {
         st_groups += 1;

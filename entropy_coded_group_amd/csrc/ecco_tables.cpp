@@ -88,9 +88,10 @@ int check_inputs(const float* c, const uint8_t* len) {
 
 // Canonical codewords of one codebook: symbols taken in (length, symbol)
 // order receive consecutive code values, shifted left whenever the length
-// grows.  Returned in stream order: the code's most significant bit is the
-// first stream bit, so the value is bit-reversed into the low bits.
-void canonical_stream_codes(const uint8_t* len, uint32_t* rev) {
+// grows.  value[s] is the codeword as a number (most significant code bit
+// first); rev[s] is it in stream order: the code's most significant bit is
+// the first stream bit, so the value is bit-reversed into the low bits.
+void canonical_stream_codes(const uint8_t* len, uint32_t* value, uint32_t* rev) {
   uint32_t code = 0;
   int prev = 0;
   bool first = true;
@@ -104,6 +105,7 @@ void canonical_stream_codes(const uint8_t* len, uint32_t* rev) {
         code = (code + 1) << (l - prev);
       }
       prev = l;
+      value[s] = code;
       uint32_t r = 0;
       for (int i = 0; i < l; ++i) r |= ((code >> (l - 1 - i)) & 1u) << i;
       rev[s] = r;
@@ -141,11 +143,11 @@ extern "C" int ecco_tables_build(const float* centroids, const uint8_t* code_len
     t->c0c14[p][1] = t->centroids[p][C - 1];
     for (int h = 0; h < H; ++h) {
       const uint8_t* L = code_len + (p * H + h) * A;
-      uint32_t rev[A];
-      canonical_stream_codes(L, rev);
+      uint32_t code[A], rev[A];
+      canonical_stream_codes(L, code, rev);
       for (int s = 0; s < A; ++s) {
         t->code_len[p][h][s] = L[s];
-        t->enc[p][h][s] = uint16_t(rev[s] | (uint32_t(L[s]) << 8));
+        t->enc[p][h][s] = (code[s] << (32 - L[s])) | uint32_t(32 - L[s]);
         for (int w = int(rev[s]); w < 256; w += 1 << L[s]) t->lut[p][h][w] = lut_entry(s, L[s]);
       }
     }

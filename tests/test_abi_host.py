@@ -40,9 +40,9 @@ def test_strerror_covers_codes():
 
 
 # byte offsets of the blob (ecco_internal.h): header 256, centroids 4096,
-# code_len 4096, midpoints 4096, c0c14 512, len4 4096, enc 8192, fp8 1024, lut 65536
+# code_len 4096, midpoints 4096, c0c14 512, len4 4096, enc 16384, fp8 1024, lut 65536
 OFF_CENT, OFF_LEN, OFF_MID, OFF_C0, OFF_LEN4, OFF_ENC, OFF_FP8, OFF_LUT = (
-    256, 4352, 8448, 12544, 13056, 17152, 25344, 26368)
+    256, 4352, 8448, 12544, 13056, 17152, 33536, 34560)
 
 
 def test_blob_size_and_layout():
@@ -58,7 +58,7 @@ def test_tables_build_roundtrip_and_derived_tables_match_oracle():
     mids = np.frombuffer(blob[OFF_MID:OFF_MID + 4096].tobytes(), np.float32).reshape(64, 16)
     assert np.array_equal(mids[:, :14].view(np.uint32), tb.midpoints().view(np.uint32))
     assert np.all(np.isinf(mids[:, 14:]))
-    enc = np.frombuffer(blob[OFF_ENC:OFF_ENC + 8192].tobytes(), np.uint16).reshape(64, 4, 16)
+    enc = np.frombuffer(blob[OFF_ENC:OFF_ENC + 16384].tobytes(), np.uint32).reshape(64, 4, 16)
     lut = blob[OFF_LUT:OFF_LUT + 65536].reshape(64, 4, 256)
     codes = tb.codes()
     for p in range(0, 64, 7):
@@ -66,7 +66,8 @@ def test_tables_build_roundtrip_and_derived_tables_match_oracle():
             for s in range(16):
                 ln = int(tb.code_len[p, h, s])
                 rev = int(format(int(codes[p, h, s]), "0%db" % ln)[::-1], 2)   # stream order
-                assert enc[p, h, s] == (rev | (ln << 8))
+                # the codeword left-aligned in 32 bits, 32 - len in the low 5 bits
+                assert enc[p, h, s] == ((int(codes[p, h, s]) << (32 - ln)) | (32 - ln))
                 for w in range(rev, 256, 1 << ln):
                     assert lut[p, h, w] == (s | ((ln - 1) << 5))
     fp8 = np.frombuffer(blob[OFF_FP8:OFF_FP8 + 1024].tobytes(), np.float32)
