@@ -419,7 +419,9 @@ __device__ __forceinline__ void decode_batch(DecodeSmem<NW>& sm, uint32_t wave, 
     x = window(lo, hi, r3);
     const uint32_t e3 = sm.lut[lutb + (x & 255u)];
     const uint32_t r4 = r3 + (e3 >> 5) + 1u;
-    uint32_t ev = e0 | (e1 << 8) | (e2 << 16) | (e3 << 24);
+    // the four entries' low bytes, packed by three byte permutes
+    uint32_t ev = __builtin_amdgcn_perm(__builtin_amdgcn_perm(e3, e2, 0x0c0c0400u),
+                                        __builtin_amdgcn_perm(e1, e0, 0x0c0c0400u), 0x05040100u);
     asm volatile("" : "+v"(ev));                 // pack now: keeps one register per 4 symbols
     if (base + r4 > lim) {
       // a codeword of this chunk ends past bit 512: the stream is clipped here
