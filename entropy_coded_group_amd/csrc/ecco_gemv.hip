@@ -6,15 +6,26 @@
 // are multiplied on the vector ALUs (v_dot2_f32_f16: two FP16 products summed
 // into an FP32 accumulator) straight out of the decoder, without writing W.
 //
-// Work split at batch 1 with rows of 16, 32 or 64 blocks (in_features 2048,
-// 4096, 8192): the matrix is cut into batches of 64 consecutive blocks, i.e.
-// 4, 2 or 1 whole rows, dealt round the waves of all CUs.  The decode core
-// hands the weights over in four passes of 16 blocks and each pass lies inside
-// one row, so every lane keeps one accumulator per row of the batch; wave sums
-// finish the rows.  Otherwise a wavefront owns one output row at a time and
-// decodes its blocks 64 at a time (the last batch of a row partly filled).
-// Either way each lane accumulates the products of the 8 weights it is
-// handed, and the sums are taken in a fixed order.
+// Work splits:
+//  * batch 1 with rows of 16, 32 or 64 blocks (in_features 2048, 4096,
+//    8192): the matrix is cut into batches of 64 consecutive blocks, i.e. 4,
+//    2 or 1 whole rows, dealt round the waves of all CUs.  The decode core
+//    hands the weights over in four passes of 16 blocks and each pass lies
+//    inside one row, so every lane keeps one accumulator per row of the
+//    batch; wave sums finish the rows.
+//  * otherwise, with out_features a multiple of 4 and rows a multiple of 16
+//    blocks: row groups.  A wavefront owns 4 rows and walks their columns 16
+//    blocks at a time; a 64-block batch holds the 4 x 16 blocks in
+//    column-major order (block 4c + r), so the decode core's write-out hands
+//    lane l always a weight slice of row l / 16, and the four blocks of one
+//    write-out step share their column: the x slices a step needs are the
+//    same for the four rows, so every x load instruction touches a quarter
+//    of the bytes it would with one row per batch.  DPP row sums (one DPP row
+//    = one output row) finish the rows.
+//  * otherwise a wavefront owns one output row at a time and decodes its
+//    blocks 64 at a time (the last batch of a row partly filled).
+// Each lane accumulates the products of the 8 weights it is handed, and the
+// sums are taken in a fixed order.
 //
 // One launch can cover several matrices (the q, k and v projections of a
 // layer read the same x): each workgroup stages one matrix's tables and the
@@ -37,13 +48,14 @@ struct GemvJob {
   const uint16_t* x;
   float* y;
   uint32_t out_f, in_f, gpr;
-  uint32_t rb;         // whole rows per 64-block batch (1, 2 or 4), or 0: one row per wave
-  uint32_t n_units;    // 64-block batches (rb > 0) or rows (rb == 0)
+  uint32_t rb;         // whole rows per 64-block batch (1, 2 or 4); kRowGroups: row groups; 0: one row per wave
+  uint32_t n_units;    // 64-block batches (rb 1, 2, 4), row groups of 4 (kRowGroups) or rows (0)
   uint32_t wg_first, wg_count;
   float t;
 };
 
 constexpr int kMaxGemvJobs = ECCO_GEMV_MAX_JOBS;
+constexpr uint32_t kRowGroups = 8;   // GemvJob::rb of the row-group split
 
 struct GemvArgs {
   GemvJob job[kMaxGemvJobs];
@@ -187,6 +199,73 @@ __device__ __forceinline__ void gemv_whole_rows(DecodeSmem<kGemvWaves>& sm, cons
   }
 }
 
+// Row groups: 4 rows x 16 block columns per 64-block batch, column-major (see
+// the file header).  Lane l's row is l / 16 and its 8 weights are positions
+// 8 (l % 16) .. + 7 of its block; block b of the batch is column b / 4.
+template <int BM>
+__device__ __forceinline__ void gemv_row_groups(DecodeSmem<kGemvWaves>& sm, const GemvJob& a, uint32_t lw,
+                                                uint32_t batch) {
+  const uint32_t lane = lane_id(), wave = threadIdx.x >> 6;
+  const uint32_t n_cc = a.gpr / 16u;              // column chunks of a row group
+  const uint32_t stride = a.wg_count * kGemvWaves;
+  uint32_t g = wave * a.wg_count + lw;            // row groups go round the workgroups first
+  if (g >= a.n_units) return;
+  // The decode core takes chunk i of lane l as bytes 16 (l & 3) .. + 15 of
+  // batch block (l >> 2) + 16 i, i.e. column (l >> 4) + 4 i of row (l >> 2) & 3:
+  // one offset per lane, then 256 bytes (4 columns) per chunk.  A prefetch
+  // past the wave's last batch reads the (cached) table blob instead.
+  const uint32_t lane_off = (((lane >> 2) & 3u) * a.gpr + (lane >> 4)) * 64u + 16u * (lane & 3u);
+  const uint8_t* idle = reinterpret_cast<const uint8_t*>(a.tab) + 64u * (lane >> 2) + 16u * (lane & 3u);
+  auto fetch = [&](uint32_t gg, uint32_t cc, bool live) {
+    const uint8_t* p = live ? a.blocks + ((uint64_t)gg * 4u * a.gpr + (uint64_t)cc * 16u) * 64u + lane_off
+                            : idle;
+    BatchRegs r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r.v[i] = load_stream(p + (live ? 256u : 1024u) * (uint32_t)i);
+    return r;
+  };
+  const uint32_t j0 = 8u * (lane & 15u);
+  float acc[BM];
+#pragma unroll
+  for (int b = 0; b < BM; ++b) acc[b] = 0.0f;
+  uint32_t cc = 0;
+  BatchRegs cur = fetch(g, 0, true);
+  while (true) {
+    uint32_t ng = g, ncc = cc + 1u;
+    if (ncc == n_cc) {
+      ng = g + stride;
+      ncc = 0;
+    }
+    const bool more = ng < a.n_units;
+    const BatchRegs nxt = fetch(more ? ng : g, more ? ncc : cc, more);
+    const uint16_t* xc = a.x + (uint64_t)cc * (16u * 128u) + j0;
+    auto sink = [&](uint32_t b, uint32_t, uint4 w, uint32_t, uint32_t) {
+      const uint16_t* xp = xc + (uint64_t)(b >> 2) * 128u;
+#pragma unroll
+      for (int b2 = 0; b2 < BM; ++b2) {
+        if ((uint32_t)b2 < batch) {
+          const uint4 xv = *reinterpret_cast<const uint4*>(xp + (uint64_t)b2 * a.in_f);
+          acc[b2] = dot8(w, xv, acc[b2]);
+        }
+      }
+    };
+    decode_batch<true>(sm, wave, lane, 64u, a.t, cur, sink);
+    if (ncc == 0u) {
+      const uint32_t row = 4u * g + (lane >> 4);
+#pragma unroll
+      for (int b2 = 0; b2 < BM; ++b2) {
+        const float v = row_sum_f32(acc[b2]);
+        if ((lane & 15u) == 0u && (uint32_t)b2 < batch) a.y[(uint64_t)b2 * a.out_f + row] = v;
+        acc[b2] = 0.0f;
+      }
+    }
+    if (!more) break;
+    g = ng;
+    cc = ncc;
+    cur = nxt;
+  }
+}
+
 // Each workgroup works on one matrix, so the look-up tables it stages in LDS
 // serve every block it sees.  BM: accumulators per lane (batch <= BM); RB:
 // whole rows per batch (every job of the launch alike), 0 for a row per wave.
@@ -200,7 +279,9 @@ __global__ __launch_bounds__(kGemvWaves * 64) void gemv_kernel(GemvArgs args) {
   stage_decode_tables(sm, a.tab);
   __syncthreads();
   const uint32_t lw = blockIdx.x - a.wg_first;
-  if constexpr (RB > 0) {
+  if constexpr (RB == (int)kRowGroups) {
+    gemv_row_groups<BM>(sm, a, lw, args.batch);
+  } else if constexpr (RB > 0) {
     static_assert(BM == 1, "whole rows per batch at batch 1 only");
     gemv_whole_rows<RB>(sm, a, lw, args.batch);
   } else {
@@ -237,14 +318,16 @@ int make_gemv_job(const void* blocks, const void* tables, float tensor_scale, in
   // more batch columns the registers run out for one accumulator per row and
   // column, and those launches go one row per wave)
   const bool whole = batch == 1 && (a.gpr == 16 || a.gpr == 32 || a.gpr == 64);
-  a.rb = whole ? 64u / a.gpr : 0u;
-  a.n_units = whole ? (a.out_f * a.gpr + 63u) / 64u : a.out_f;
+  const bool groups = !whole && a.out_f % 4u == 0u && a.gpr % 16u == 0u;
+  a.rb = whole ? 64u / a.gpr : groups ? kRowGroups : 0u;
+  a.n_units = whole ? (a.out_f * a.gpr + 63u) / 64u : groups ? a.out_f / 4u : a.out_f;
   a.wg_first = a.wg_count = 0;
   return ECCO_OK;
 }
 
 // 64-block batches of decode work in a job.
 uint64_t gemv_cost(const GemvJob& a) {
+  if (a.rb == kRowGroups) return (uint64_t)a.n_units * (a.gpr / 16u);
   return a.rb ? a.n_units : (uint64_t)a.out_f * ((a.gpr + 63u) / 64u);
 }
 
@@ -283,7 +366,7 @@ int launch_gemv(const GemvArgs& all, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   const dim3 block(kGemvWaves * 64);
   (void)hipGetLastError();
-  for (uint32_t rb : {0u, 1u, 2u, 4u}) {
+  for (uint32_t rb : {0u, 1u, 2u, 4u, kRowGroups}) {
     GemvArgs args;
     std::memset(&args, 0, sizeof(args));
     args.batch = all.batch;
@@ -293,7 +376,16 @@ int launch_gemv(const GemvArgs& all, void* stream) {
     assign_gemv_workgroups(args, (uint32_t)cus);
     const GemvJob& last = args.job[args.n_jobs - 1];
     const dim3 grid(last.wg_first + last.wg_count);
-    if (rb == 4)
+    if (rb == kRowGroups) {
+      if (args.batch == 1)
+        hipLaunchKernelGGL((gemv_kernel<1, kRowGroups>), grid, block, 0, s, args);
+      else if (args.batch <= 2)
+        hipLaunchKernelGGL((gemv_kernel<2, kRowGroups>), grid, block, 0, s, args);
+      else if (args.batch <= 4)
+        hipLaunchKernelGGL((gemv_kernel<4, kRowGroups>), grid, block, 0, s, args);
+      else
+        hipLaunchKernelGGL((gemv_kernel<8, kRowGroups>), grid, block, 0, s, args);
+    } else if (rb == 4)
       hipLaunchKernelGGL((gemv_kernel<1, 4>), grid, block, 0, s, args);
     else if (rb == 2)
       hipLaunchKernelGGL((gemv_kernel<1, 2>), grid, block, 0, s, args);
