@@ -40,6 +40,10 @@ Other workloads (run separately, same JSON line shape):
          ecco_attention_decode against decode followed by torch's SDPA
   act    the 2x activation format (groups of 64) on LLaMA-3-8B hidden
          states [16384, 4096]: amax, encode and decode
+  design the S x H design points the v1 block holds (S in {16, 32, 64}
+         patterns, H in {1, 2, 4} codebooks): encode and decode time and the
+         codec's quality per point on the gate projection, K, V and the
+         1024x1024 weight
   copy   a plain 1 GiB device-to-device copy (the achievable-bandwidth
          reference, and the known-size kernel that calibrates the HBM
          traffic counters FETCH_SIZE / WRITE_SIZE)
@@ -73,7 +77,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="model", choices=["model", "layer", "kv", "ffn", "attn", "act", "copy"])
+    ap.add_argument("--workload", default="model",
+                    choices=["model", "layer", "kv", "ffn", "attn", "act", "design", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-groups", type=int, default=65536)
     return ap.parse_args()

@@ -1,4 +1,4 @@
-"""Secondary workloads of bench.py (see its docstring): kv, ffn, attn, act, copy."""
+"""Secondary workloads of bench.py (see its docstring): kv, ffn, attn, act, design, copy."""
 
 import os
 
@@ -267,6 +267,78 @@ def bench_act(args, torch, ecco, W):
                  clipped_groups=st["clipped_groups"], mean_outliers_per_group=round(st["padded_outliers"] / G, 3))
 
 
+def bench_design(args, torch, ecco, W):
+    """The S x H design points the v1 block can hold (S in {16, 32, 64}
+    patterns, H in {1, 2, 4} codebooks; tables from
+    tests/golden/design_tables.npz written into the block's 64 x 4 slots by
+    repetition) on full-size tensors: the LLaMA-3-8B gate projection
+    [14336, 4096], the KV cache's K and V [16, 8, 8192, 128] and the
+    1024x1024 weight.  Per point: encode and decode time, and the codec's
+    quality from the GPU's own output (relative MSE of the round trip,
+    clipped groups, mean coded bits per group including the 16-bit header)."""
+    z = np.load(os.path.join(os.path.dirname(os.path.abspath(__file__)), "tests", "golden", "design_tables.npz"))
+    cases = []
+    x = W.c1_weight().cuda()
+    cases.append(("c1", "1024x1024 weight", x, None))
+    x = W.llama_matrix(W.LLAMA3_8B_LAYER["gate"], 104).cuda()
+    cases.append(("gate", "llama3-8b gate [14336, 4096]", x, None))
+    for kind in ("k", "v"):
+        smp = W.kv_sample(kind).numpy()
+        t = ecco.ecco_tensor_scale_from_amax(float(np.max(np.abs(smp.astype(np.float32)))))
+        cases.append((kind, "kv-cache %s [16, 8, 8192, 128]" % kind.upper(), W.kv_tensor(kind).cuda(), t))
+    out = {}
+    for name, label, x, t in cases:
+        G = x.numel() // 128
+        if t is None:
+            amax = torch.zeros(1, dtype=torch.float32, device="cuda")
+            ecco.ecco_amax(x, x.numel(), amax)
+            torch.cuda.synchronize()
+            t = ecco.ecco_tensor_scale_from_amax(amax.item())
+        blocks = torch.empty((G, 64), dtype=torch.uint8, device="cuda")
+        y = torch.empty_like(x)
+        st = torch.zeros(7, dtype=torch.int64, device="cuda")
+        xf = x.float()
+        var = float(((xf - xf.mean()) ** 2).mean())
+        rows = {}
+        for S in (16, 32, 64):
+            for H in (1, 2, 4):
+                key = "%s_S%d_H%d" % (name, S, H)
+                # slot p holds pattern p mod S, book h of a pattern book h mod H
+                c, L = z[key + "_centroids"], z[key + "_code_len"]
+                c64 = np.ascontiguousarray(c[np.arange(64) % S], np.float32)
+                L64 = np.ascontiguousarray(L[np.arange(64) % S][:, np.arange(4) % H], np.uint8)
+                tdev = ecco.tables_to_device(ecco.ecco_tables_build(c64, L64))
+                st.zero_()
+                ecco.ecco_encode(x, 1, G, G * 128, G, tdev, t, blocks, st)
+                ecco.ecco_decode(blocks, 1, G, G, G * 128, tdev, t, y)
+                torch.cuda.synchronize()
+                s = dict(zip(ecco.STATS_FIELDS, st.cpu().tolist()))
+                unclipped = G - s["clipped_groups"]
+                # stream bits of the unclipped groups: 496 - pad - fill each; clipped ones fill the block
+                bits = 512.0 * s["clipped_groups"] + 16.0 * unclipped + (496.0 * unclipped - s["pad_bits"] -
+                                                                          s["fill_bits"])
+                mse = float(((y.float() - xf) ** 2).mean())
+                te = _timed(torch, lambda: ecco.ecco_encode(x, 1, G, G * 128, G, tdev, t, blocks), args.steps,
+                            args.warmup)
+                td = _timed(torch, lambda: ecco.ecco_decode(blocks, 1, G, G, G * 128, tdev, t, y), args.steps,
+                            args.warmup)
+                rows["S%d_H%d" % (S, H)] = dict(
+                    rel_mse=round(mse / var, 6), clipped_frac=round(s["clipped_groups"] / G, 4),
+                    coded_bits_per_group=round(bits / G, 1),
+                    outliers_per_group=round(s["padded_outliers"] / G, 3),
+                    encode_us=round(np.mean(te) * 1e6, 2), decode_us=round(np.mean(td) * 1e6, 2),
+                    encode_GBps=round(G * BYTES_PER_GROUP / np.mean(te) / 1e9, 1),
+                    decode_GBps=round(G * BYTES_PER_GROUP / np.mean(td) / 1e9, 1))
+        out[name] = dict(workload=label, groups=G, points=rows)
+        del x, y, xf, blocks
+        torch.cuda.empty_cache()
+    g = out["gate"]["points"]["S64_H4"]
+    return _line("decode GB/s at S=64, H=4, gate projection", g["decode_GBps"], "GB/s", args,
+                 (g["encode_us"] + g["decode_us"]) / 1e3,
+                 {"workload": "S x H design points held by the v1 block: S in {16, 32, 64}, H in {1, 2, 4}"},
+                 design_points=out)
+
+
 def bench_copy(args, torch, ecco, W):
     nbytes = 1 << 30
     a = torch.ones(nbytes // 2, dtype=torch.float16, device="cuda")
@@ -279,5 +351,5 @@ def bench_copy(args, torch, ecco, W):
 
 
 def run_workload(args, torch, ecco, W):
-    return {"kv": bench_kv, "ffn": bench_ffn, "attn": bench_attn,
+    return {"kv": bench_kv, "ffn": bench_ffn, "attn": bench_attn, "design": bench_design,
             "act": bench_act, "copy": bench_copy}[args.workload](args, torch, ecco, W)

@@ -30,7 +30,7 @@ those errors.
 import numpy as np
 
 from . import fp
-from .codec import encode_groups, decode_blocks, GROUP
+from .codec import encode_groups, decode_blocks, GROUP, Tables
 
 F32 = np.float32
 
@@ -134,11 +134,12 @@ def design_point(x, centroids, code_len, t):
                 clipped=float(np.mean(header + L > 512)), header_bits=header)
 
 
-def design_space(sample, x, t_sample, t, S_list=(16, 32, 64, 128), H_list=(1, 2, 4, 8), kmeans_iters=25,
-                 huff_iters=10, seed=0):
-    """Learn tables for every (S, H) from one sample (the 1-D k-means runs
-    once) and evaluate each on x.  Codebooks are learned with the trainer's
-    rule (oracle/train.py) on the groups the min/max rule gives each pattern."""
+def design_tables(sample, t_sample, S_list=(16, 32, 64, 128), H_list=(1, 2, 4, 8), kmeans_iters=25,
+                  huff_iters=10, seed=0):
+    """Tables for every (S, H) from one sample (the 1-D k-means runs once):
+    {(S, H): (centroids [S, 15], code_len [S, H, 16])}.  Codebooks are
+    learned with the trainer's rule (oracle/train.py) on the groups the
+    min/max rule gives each pattern."""
     from .kmeans import kmeans_1d_exact, lloyd
     from .train import normalised_groups, learn_codebooks
     xs = np.asarray(sample, np.float16).reshape(-1, GROUP)
@@ -153,8 +154,29 @@ def design_space(sample, x, t_sample, t, S_list=(16, 32, 64, 128), H_list=(1, 2,
         np.add.at(counts, (np.repeat(np.arange(xs.shape[0]), GROUP), sym.ravel()), 1)
         for H in H_list:
             code_len = np.stack([learn_codebooks(counts[p == k], H, huff_iters) for k in range(cent.shape[0])])
-            out[(S, H)] = design_point(x, cent, code_len, t)
+            out[(S, H)] = (cent, code_len)
     return out
+
+
+def design_space(sample, x, t_sample, t, S_list=(16, 32, 64, 128), H_list=(1, 2, 4, 8), kmeans_iters=25,
+                 huff_iters=10, seed=0):
+    """Learn tables for every (S, H) from one sample and evaluate each on x."""
+    tabs = design_tables(sample, t_sample, S_list, H_list, kmeans_iters, huff_iters, seed)
+    return {k: design_point(x, c, l, t) for k, (c, l) in tabs.items()}
+
+
+def v1_tables(centroids, code_len):
+    """A design point with S <= 64 patterns and H <= 4 codebooks written into
+    the v1 block's 64 x 4 table slots: slot p holds pattern p mod S and book h
+    of a pattern holds book h mod H.  A repeated slot ties in the min/max
+    fitness (or in the coded length) with a lower one and loses, so blocks use
+    only p < S and h < H and the codec behaves as the design point's own."""
+    c = np.asarray(centroids, np.float32)
+    L = np.asarray(code_len, np.uint8)
+    S, H = L.shape[:2]
+    if 64 % S or 4 % H:
+        raise ValueError("S must divide 64 and H must divide 4")
+    return Tables(c[np.arange(64) % S], L[np.arange(64) % S][:, np.arange(4) % H])
 
 
 def main_design_space():

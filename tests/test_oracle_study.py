@@ -115,3 +115,30 @@ def test_design_space_small_sweep():
     assert res[(16, 1)]["header_bits"] == 12 and res[(64, 4)]["header_bits"] == 16
     for r in res.values():
         assert np.isfinite(r["mse"]) and 0 <= r["clipped"] <= 1 and r["bits_per_group"] > 0
+
+
+def test_v1_tables_hold_every_design_point_the_block_can_carry():
+    """Design points with S in {16, 32, 64} and H in {1, 2, 4} written into the
+    v1 table slots: the codec uses only p < S and h < H, and its coded length
+    of every group is the design point's (the shortest of the H books of the
+    min/max pattern), so only the header's fixed 16 bits differ."""
+    sample = W.c1_sample(n_values=128 * 128).numpy()
+    x, t = _case(300)
+    ts = codec.tensor_scale(float(np.max(np.abs(sample.astype(np.float32)))))[0]
+    tabs = study.design_tables(sample, ts, S_list=(16, 32, 64), H_list=(1, 2, 4), kmeans_iters=3, huff_iters=3)
+    for (S, H), (c, L) in sorted(tabs.items()):
+        tb = study.v1_tables(c, L)
+        tb.check()
+        blocks, info = codec.encode_groups(x, tb, t, return_info=True)
+        assert info["p"].max() < S and info["h"].max() < H, (S, H)
+        assert np.all((blocks[:, 0] & 63) < S) and np.all((blocks[:, 0] >> 6) < H)
+        p, sym, _ = study.assign_groups(x, c, t)
+        assert np.array_equal(p, info["p"] % S)
+        lens = np.asarray(L, np.int64)[p]
+        Lh = np.stack([np.take_along_axis(lens[:, h, :], sym, axis=1).sum(axis=1) for h in range(H)], axis=1)
+        assert np.array_equal(Lh.min(axis=1), info["L"]), (S, H)
+        r = study.design_point(x, c, L, t)
+        assert np.isclose(r["clipped"], np.mean(r["header_bits"] + info["L"] > 512))
+    import pytest
+    with pytest.raises(ValueError):
+        study.v1_tables(tabs[(16, 1)][0][:12], tabs[(16, 1)][1][:12])
