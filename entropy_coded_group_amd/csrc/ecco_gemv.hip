@@ -202,22 +202,36 @@ __device__ __forceinline__ void gemv_whole_rows(DecodeSmem<kGemvWaves>& sm, cons
 // Row groups: 4 rows x 16 block columns per 64-block batch, column-major (see
 // the file header).  Lane l's row is l / 16 and its 8 weights are positions
 // 8 (l % 16) .. + 7 of its block; block b of the batch is column b / 4.
+//
+// A unit is one batch: (row group, column chunk).  Each workgroup takes a
+// contiguous share of the job's row groups and works through it in rounds of
+// up to kGemvUnits units (whole row groups); the units of a round are dealt
+// round the workgroup's waves, so every wave gets as many batches as the
+// others give or take one, whatever the rows' length.  Each unit's row sums
+// go to LDS; after a barrier the sums of a row group's chunks are added in
+// chunk order.  The order of every sum depends only on the matrix, not on
+// how many workgroups the launch gives the job, so a call with several jobs
+// gives the same bits as one call per job.
+constexpr uint32_t kGemvUnits = 84;     // units per round (row sums of a round in LDS)
+
 template <int BM>
 __device__ __forceinline__ void gemv_row_groups(DecodeSmem<kGemvWaves>& sm, const GemvJob& a, uint32_t lw,
                                                 uint32_t batch) {
-  const uint32_t lane = lane_id(), wave = threadIdx.x >> 6;
+  __shared__ float part[kGemvUnits][4][BM];
+  // the wave index is uniform: held in a scalar register, so are the unit counters
+  const uint32_t lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t n_cc = a.gpr / 16u;              // column chunks of a row group
-  const uint32_t stride = a.wg_count * kGemvWaves;
-  uint32_t g = wave * a.wg_count + lw;            // row groups go round the workgroups first
-  if (g >= a.n_units) return;
+  const uint32_t rg_lo = (uint32_t)((uint64_t)a.n_units * lw / a.wg_count);
+  const uint32_t rg_hi = (uint32_t)((uint64_t)a.n_units * (lw + 1u) / a.wg_count);
+  const uint32_t R = kGemvUnits / n_cc;           // row groups per round (>= 1: the host checks n_cc)
   // The decode core takes chunk i of lane l as bytes 16 (l & 3) .. + 15 of
   // batch block (l >> 2) + 16 i, i.e. column (l >> 4) + 4 i of row (l >> 2) & 3:
   // one offset per lane, then 256 bytes (4 columns) per chunk.  A prefetch
-  // past the wave's last batch reads the (cached) table blob instead.
+  // past the wave's last unit reads the (cached) table blob instead.
   const uint32_t lane_off = (((lane >> 2) & 3u) * a.gpr + (lane >> 4)) * 64u + 16u * (lane & 3u);
   const uint8_t* idle = reinterpret_cast<const uint8_t*>(a.tab) + 64u * (lane >> 2) + 16u * (lane & 3u);
-  auto fetch = [&](uint32_t gg, uint32_t cc, bool live) {
-    const uint8_t* p = live ? a.blocks + ((uint64_t)gg * 4u * a.gpr + (uint64_t)cc * 16u) * 64u + lane_off
+  auto fetch = [&](uint32_t rg, uint32_t cc, bool live) {
+    const uint8_t* p = live ? a.blocks + ((uint64_t)rg * 4u * a.gpr + (uint64_t)cc * 16u) * 64u + lane_off
                             : idle;
     BatchRegs r;
 #pragma unroll
@@ -225,44 +239,62 @@ __device__ __forceinline__ void gemv_row_groups(DecodeSmem<kGemvWaves>& sm, cons
     return r;
   };
   const uint32_t j0 = 8u * (lane & 15u);
-  float acc[BM];
-#pragma unroll
-  for (int b = 0; b < BM; ++b) acc[b] = 0.0f;
-  uint32_t cc = 0;
-  BatchRegs cur = fetch(g, 0, true);
+  uint32_t g0 = rg_lo;
+  if (g0 >= rg_hi) return;                        // the whole workgroup has no share (uniform)
+  // units of the round starting at row group g0; this wave's are wave, wave + kGemvWaves, ...
+  uint32_t U = min(R, rg_hi - g0) * n_cc, u = wave;
+  BatchRegs cur = fetch(g0 + u / n_cc, u % n_cc, u < U);
   while (true) {
-    uint32_t ng = g, ncc = cc + 1u;
-    if (ncc == n_cc) {
-      ng = g + stride;
-      ncc = 0;
-    }
-    const bool more = ng < a.n_units;
-    const BatchRegs nxt = fetch(more ? ng : g, more ? ncc : cc, more);
-    const uint16_t* xc = a.x + (uint64_t)cc * (16u * 128u) + j0;
-    auto sink = [&](uint32_t b, uint32_t, uint4 w, uint32_t, uint32_t) {
-      const uint16_t* xp = xc + (uint64_t)(b >> 2) * 128u;
-#pragma unroll
-      for (int b2 = 0; b2 < BM; ++b2) {
-        if ((uint32_t)b2 < batch) {
-          const uint4 xv = *reinterpret_cast<const uint4*>(xp + (uint64_t)b2 * a.in_f);
-          acc[b2] = dot8(w, xv, acc[b2]);
-        }
+    for (; u < U; u += kGemvWaves) {
+      // the next unit: this round's, else this wave's first of the next round
+      uint32_t nu = u + kGemvWaves, ng = g0, nU = U;
+      if (nu >= U && g0 + R < rg_hi) {
+        ng = g0 + R;
+        nU = min(R, rg_hi - ng) * n_cc;
+        nu = wave;
       }
-    };
-    decode_batch<true>(sm, wave, lane, 64u, a.t, cur, sink);
-    if (ncc == 0u) {
-      const uint32_t row = 4u * g + (lane >> 4);
+      const bool live = nu < nU;
+      const BatchRegs nxt = fetch(ng + (live ? nu / n_cc : 0u), live ? nu % n_cc : 0u, live);
+      const uint32_t cc = u % n_cc;
+      const uint16_t* xc = a.x + (uint64_t)cc * (16u * 128u) + j0;
+      float acc[BM];
+#pragma unroll
+      for (int b = 0; b < BM; ++b) acc[b] = 0.0f;
+      auto sink = [&](uint32_t b, uint32_t, uint4 w, uint32_t, uint32_t) {
+        const uint16_t* xp = xc + (uint64_t)(b >> 2) * 128u;
+#pragma unroll
+        for (int b2 = 0; b2 < BM; ++b2) {
+          if ((uint32_t)b2 < batch) {
+            const uint4 xv = *reinterpret_cast<const uint4*>(xp + (uint64_t)b2 * a.in_f);
+            acc[b2] = dot8(w, xv, acc[b2]);
+          }
+        }
+      };
+      decode_batch<true>(sm, wave, lane, 64u, a.t, cur, sink);
 #pragma unroll
       for (int b2 = 0; b2 < BM; ++b2) {
         const float v = row_sum_f32(acc[b2]);
-        if ((lane & 15u) == 0u && (uint32_t)b2 < batch) a.y[(uint64_t)b2 * a.out_f + row] = v;
-        acc[b2] = 0.0f;
+        if ((lane & 15u) == 0u) part[u][lane >> 4][b2] = v;
       }
+      cur = nxt;
     }
-    if (!more) break;
-    g = ng;
-    cc = ncc;
-    cur = nxt;
+    __syncthreads();
+    // row (g0 + j, q), batch column b2: its chunks' sums in chunk order
+    const uint32_t n_rg = U / n_cc;
+    for (uint32_t o = threadIdx.x; o < n_rg * 4u * batch; o += blockDim.x) {
+      const uint32_t b2 = o % batch, q = (o / batch) & 3u, jg = o / (4u * batch);
+      float s = 0.0f;
+      for (uint32_t cc = 0; cc < n_cc; ++cc) s += part[jg * n_cc + cc][q][b2];
+      a.y[(uint64_t)b2 * a.out_f + 4u * (g0 + jg) + q] = s;
+    }
+    __syncthreads();
+    g0 += R;
+    if (g0 >= rg_hi) break;
+    // a wave that had a unit in the round has prefetched its first of this one
+    const bool prefetched = wave < U;
+    U = min(R, rg_hi - g0) * n_cc;
+    u = wave;
+    if (!prefetched) cur = fetch(g0 + u / n_cc, u % n_cc, u < U);
   }
 }
 
@@ -318,7 +350,11 @@ int make_gemv_job(const void* blocks, const void* tables, float tensor_scale, in
   // more batch columns the registers run out for one accumulator per row and
   // column, and those launches go one row per wave)
   const bool whole = batch == 1 && (a.gpr == 16 || a.gpr == 32 || a.gpr == 64);
-  const bool groups = !whole && a.out_f % 4u == 0u && a.gpr % 16u == 0u;
+  // row groups where a row is not a whole number of batches (a row per wave
+  // would leave lanes idle, or its waves would each read x at another place);
+  // rows of 64k blocks keep a row per wave, which measures a little faster
+  const bool groups = !whole && a.gpr % 64u != 0u && a.out_f % 4u == 0u && a.gpr % 16u == 0u &&
+                      a.gpr / 16u <= kGemvUnits;
   a.rb = whole ? 64u / a.gpr : groups ? kRowGroups : 0u;
   a.n_units = whole ? (a.out_f * a.gpr + 63u) / 64u : groups ? a.out_f / 4u : a.out_f;
   a.wg_first = a.wg_count = 0;

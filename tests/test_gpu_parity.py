@@ -528,7 +528,8 @@ def test_decode_many_full_layer_sampled(dev):
                                               (20, 28672, 2), (1, 4096, 1), (999, 4096, 1), (5, 2048, 1),
                                               (1000, 2048, 1), (33, 8192, 1), (50, 14336, 1), (7, 12416, 1),
                                               (3, 8320, 1), (1, 16384, 1), (300, 14336, 1),
-                                              (4, 2048, 8), (8, 4096, 5), (12, 6144, 7), (1024, 2048, 2)])
+                                              (4, 2048, 8), (8, 4096, 5), (12, 6144, 7), (1024, 2048, 2),
+                                              (500, 10240, 4)])
 def test_gemv_small(dev, out_f, in_f, batch):
     tb = golden("c5_w1")
     tdev = dev_tables(tb)
