@@ -739,14 +739,15 @@ int make_encode_job(const uint16_t* x, uint64_t n_rows, uint64_t gpr, uint64_t x
 }
 
 // Up to 16 workgroups of kEncWaves waves per CU (four are resident at a time;
-// the later ones even out the tail), no more than a job has units for: each
+// the later ones even out the tail), and at least two units per wave, so a
+// small launch does not stage the tables in LDS more often than it needs: each
 // job gets its share of the grid in proportion to its units (at least one
 // workgroup), and the few workgroups the rounding leaves go one by one to the
 // job whose workgroups carry the most units.
 void assign_encode_workgroups(EncodeArgs& args, uint32_t cus) {
   uint64_t want[kMaxJobs], total = 0;
   for (uint32_t j = 0; j < args.n_jobs; ++j) {
-    want[j] = (args.job[j].n_units + kEncWaves - 1) / kEncWaves;
+    want[j] = (args.job[j].n_units + 2 * kEncWaves - 1) / (2 * kEncWaves);
     total += want[j];
   }
   const uint64_t grid = std::max<uint64_t>(args.n_jobs, std::min<uint64_t>(total, (uint64_t)cus * 16));
