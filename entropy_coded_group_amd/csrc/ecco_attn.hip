@@ -60,7 +60,9 @@ __global__ __launch_bounds__(kScoreWaves * 64) void attn_scores_kernel(AttnArgs 
   __shared__ DecodeSmem<kScoreWaves> sm;
   stage_decode_tables(sm, a.kt);
   __syncthreads();
-  const uint32_t lane = lane_id(), wave = threadIdx.x >> 6;
+  // the wave index is uniform: held in a scalar register, so are the batch
+  // counters and the addresses derived from them
+  const uint32_t lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t total = a.pairs * a.n_kb;
   const uint32_t stride = gridDim.x * kScoreWaves;
   const uint8_t* idle = reinterpret_cast<const uint8_t*>(a.kt);
@@ -78,10 +80,24 @@ __global__ __launch_bounds__(kScoreWaves * 64) void attn_scores_kernel(AttnArgs 
     const BatchRegs nxt = fetch(more ? nb : batch, more);
     const uint32_t pair = batch / a.n_kb, t0 = (batch % a.n_kb) * 64u;
     const uint32_t n_valid = min(64u, a.S - t0);
+    // The G query slices (8 values each) are loaded as each write-out pass
+    // starts, from an opaque copy of their address: held across the whole
+    // batch (the lane-serial chain included), they made the kernel spill.
+    // A load under a run-time condition is not moved earlier than written.
+    const uint16_t* qb = a.q + (uint64_t)pair * G * 128u;
     uint4 qv[G];
+    auto pre = [&](uint32_t) {
+      const uint16_t* qp = qb;
+      asm volatile("" : "+s"(qp));
+      if (n_valid != 0u) {
 #pragma unroll
-    for (int g = 0; g < G; ++g) qv[g] = *reinterpret_cast<const uint4*>(a.q + ((uint64_t)pair * G + g) * 128u + j0);
-    float* sp = a.probs + ((uint64_t)pair * a.S + t0) * G;
+        for (int g = 0; g < G; ++g) qv[g] = *reinterpret_cast<const uint4*>(qp + (uint32_t)g * 128u + j0);
+      }
+    };
+    // this lane's token's scores within a write-out step; step (k, it) adds
+    // 16 k + 4 it tokens, a constant that the store's offset field takes
+    // (written as one 64-bit product, the 16 offsets were kept in registers)
+    float* sp = a.probs + ((uint64_t)pair * a.S + t0 + lane / 16u) * G;
     auto sink = [&](uint32_t b, uint32_t, uint4 w, uint32_t, uint32_t) {
       float d[G];
 #pragma unroll
@@ -89,7 +105,7 @@ __global__ __launch_bounds__(kScoreWaves * 64) void attn_scores_kernel(AttnArgs 
       // one vector store of the token's G scores (whole 16-byte pieces, so the
       // four tokens of an instruction fill their 64 bytes without partial writes)
       if ((lane & 15u) == 0) {
-        float* dst = sp + (uint64_t)b * G;
+        float* dst = sp + (b - lane / 16u) * G;
         if constexpr (G == 1) {
           dst[0] = d[0];
         } else if constexpr (G == 2) {
@@ -102,9 +118,9 @@ __global__ __launch_bounds__(kScoreWaves * 64) void attn_scores_kernel(AttnArgs 
       }
     };
     if (n_valid == 64u)
-      decode_batch<true, kScoreWaves, 128, true>(sm, wave, lane, 64u, a.kts, cur, sink);
+      decode_batch<true, kScoreWaves, 128, true>(sm, wave, lane, 64u, a.kts, cur, sink, pre);
     else
-      decode_batch<false, kScoreWaves, 128, true>(sm, wave, lane, n_valid, a.kts, cur, sink);
+      decode_batch<false, kScoreWaves, 128, true>(sm, wave, lane, n_valid, a.kts, cur, sink, pre);
     cur = nxt;
   }
 }
@@ -170,7 +186,9 @@ __global__ __launch_bounds__(kPvWaves * 64) void attn_pv_kernel(AttnArgs a, uint
   __shared__ DecodeSmem<kPvWaves> sm;
   stage_decode_tables(sm, a.vt);
   __syncthreads();
-  const uint32_t lane = lane_id(), wave = threadIdx.x >> 6;
+  // the wave index is uniform: held in a scalar register, so are the batch
+  // counters and the addresses derived from them
+  const uint32_t lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t total = a.pairs * a.n_units;
   const uint32_t stride = gridDim.x * kPvWaves;
   const uint8_t* idle = reinterpret_cast<const uint8_t*>(a.vt);
@@ -198,11 +216,35 @@ __global__ __launch_bounds__(kPvWaves * 64) void attn_pv_kernel(AttnArgs a, uint
     const uint32_t t0 = u * kUnitTokens + 64u * half;
     if (t0 < a.S) {
       const uint32_t n_valid = min(64u, a.S - t0);
-      const float* pp = a.probs + ((uint64_t)pair * a.S + t0) * a.G + g_off;
-      auto sink = [&](uint32_t b, uint32_t, uint4 w, uint32_t, uint32_t) {
+      // the probabilities of a pass's four tokens per lane, loaded as the
+      // pass starts (from an opaque copy of the address, under a run-time
+      // condition, so the loads are neither hoisted to the batch's start
+      // nor held across the decode).  Step (k, it) takes token 16 k + 4 it +
+      // lane / 16; tl is an opaque copy of lane / 16, so that the compiler
+      // does not keep the 16 token indices of a batch in registers; a token
+      // past n_valid reads token 0 (its products are never used).
+      const float* pb = a.probs + ((uint64_t)pair * a.S + t0) * a.G + g_off;
+      uint32_t tl = lane / 16u;
+      asm volatile("" : "+v"(tl));
+      const float* pl = pb + tl * a.G;
+      float pq[4][GH];
+      auto pre = [&](uint32_t k) {
+        const float* pp = pl;
+        asm volatile("" : "+v"(pp));
+        if (n_valid != 0u) {
+#pragma unroll
+          for (int it = 0; it < 4; ++it) {
+            const int c = (int)(16u * k) + 4 * it;
+            const float* src = (int)tl < (int)n_valid - c ? pp + (uint32_t)c * a.G : pb;
+#pragma unroll
+            for (int g = 0; g < GH; ++g) pq[it][g] = src[g];
+          }
+        }
+      };
+      auto sink = [&](uint32_t, uint32_t, uint4 w, uint32_t, uint32_t it) {
         float p[GH];
 #pragma unroll
-        for (int g = 0; g < GH; ++g) p[g] = pp[(uint64_t)b * a.G + g];
+        for (int g = 0; g < GH; ++g) p[g] = pq[it][g];
         const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -211,10 +253,9 @@ __global__ __launch_bounds__(kPvWaves * 64) void attn_pv_kernel(AttnArgs a, uint
           for (int g = 0; g < GH; ++g) acc[g][i] = fmaf(p[g], v, acc[g][i]);
         }
       };
-      if (n_valid == 64u)
-        decode_batch<true, kPvWaves, 128, true>(sm, wave, lane, 64u, a.vts, cur, sink);
-      else
-        decode_batch<false, kPvWaves, 128, true>(sm, wave, lane, n_valid, a.vts, cur, sink);
+      // one instantiation of the decode core (with a second one for whole
+      // batches, the accumulators were copied between the two and spilled)
+      decode_batch<false, kPvWaves, 128, true>(sm, wave, lane, n_valid, a.vts, cur, sink, pre);
     }
     cur = nxt;
     if (half == 1u) {
