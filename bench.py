@@ -1,6 +1,6 @@
 """Benchmark of the Ecco block codec on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload model|layer|kv|ffn|attn|act|copy] [--gpus 1]
+    python bench.py [--steps K] [--warmup W] [--workload model|layer|weight|kv|ffn|attn|act|design|copy] [--gpus 1]
 
 Default workload ("model"): the 32-layer LLaMA-3-8B-shaped weight set in
 FP16, 6.98e9 parameters (13.96 GB) resident in HBM.  Each layer has q, o
@@ -31,6 +31,9 @@ Other workloads (run separately, same JSON line shape):
          and by ecco_decode_speculative, the pages' segment-parallel decode;
          each amax, encode and GEMV by a call of its own; the step captured
          into a HIP graph and replayed)
+  weight one 1024x1024 weight (8,192 groups; launch-bound): amax, encode
+         and decode, one call each, device time per call and the
+         host-inclusive time of a step
   kv     K and V caches [16, 8, 8192, 128]: append-encode of the last 256
          tokens per row (strided) and decode of the whole cache
   ffn    70B-shaped FFN matrices [28672, 8192], [8192, 28672]: fused
@@ -78,7 +81,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="model",
-                    choices=["model", "layer", "kv", "ffn", "attn", "act", "design", "copy"])
+                    choices=["model", "layer", "weight", "kv", "ffn", "attn", "act", "design", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-groups", type=int, default=65536)
     return ap.parse_args()

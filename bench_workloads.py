@@ -1,6 +1,7 @@
-"""Secondary workloads of bench.py (see its docstring): kv, ffn, attn, act, design, copy."""
+"""Secondary workloads of bench.py (see its docstring): weight, kv, ffn, attn, act, design, copy."""
 
 import os
+import time
 
 import numpy as np
 
@@ -58,6 +59,61 @@ def _line(metric, value, unit, args, ms_per_step, config, **extra):
          "data": "synthetic", "config": config}
     d.update(extra)
     return d
+
+
+def bench_weight(args, torch, ecco, W):
+    """One 1024x1024 weight (8,192 groups): small enough that each call is
+    bound by launch latency, not by HBM.  Per step: amax, encode, decode,
+    each a call of its own.  Device time per call comes from HIP events
+    around calls enqueued behind a spin kernel; the host-inclusive time per
+    step is the wall clock of `steps` back-to-back steps (amax, scale
+    read-back, encode, decode) with one synchronisation per step, as a caller
+    that needs the scale on the host sees it."""
+    x = W.c1_weight().cuda()
+    n_rows, n_cols = x.shape
+    gpr = n_cols // 128
+    blob = ecco.ecco_train_patterns(W.c1_sample(), threads=min(16, os.cpu_count() or 1))
+    tdev = ecco.tables_to_device(blob)
+    amax = torch.zeros(1, dtype=torch.float32, device="cuda")
+    ecco.ecco_amax(x, x.numel(), amax)
+    torch.cuda.synchronize()
+    t = ecco.ecco_tensor_scale_from_amax(amax.item())
+    blocks = torch.empty((n_rows, gpr, 64), dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(x)
+
+    def f_amax():
+        ecco.ecco_amax(x, x.numel(), amax)
+
+    def f_enc():
+        ecco.ecco_encode(x, n_rows, gpr, n_cols, gpr, tdev, t, blocks)
+
+    def f_dec():
+        ecco.ecco_decode(blocks, n_rows, gpr, gpr, n_cols, tdev, t, y)
+
+    t_amax = _timed(torch, f_amax, args.steps, args.warmup)
+    t_enc = _timed(torch, f_enc, args.steps, args.warmup)
+    t_dec = _timed(torch, f_dec, args.steps, args.warmup)
+    for _ in range(args.warmup):
+        f_amax(); f_enc(); f_dec()
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for _ in range(args.steps):
+        ecco.ecco_amax(x, x.numel(), amax)
+        tt = ecco.ecco_tensor_scale_from_amax(amax.item())
+        ecco.ecco_encode(x, n_rows, gpr, n_cols, gpr, tdev, tt, blocks)
+        ecco.ecco_decode(blocks, n_rows, gpr, gpr, n_cols, tdev, tt, y)
+        torch.cuda.synchronize()
+    wall = (time.perf_counter() - w0) / args.steps
+    groups = n_rows * gpr
+    dev = np.mean(t_amax) + np.mean(t_enc) + np.mean(t_dec)
+    dec = groups * BYTES_PER_GROUP / np.mean(t_dec) / 1e9
+    return _line("decode GB/s (compressed in + fp16 out), 1 GPU", dec, "GB/s", args, wall * 1e3,
+                 {"workload": "one 1024x1024 weight (8,192 groups): amax, encode, decode, one call each",
+                  "groups": groups},
+                 decode_us=round(np.mean(t_dec) * 1e6, 2), encode_us=round(np.mean(t_enc) * 1e6, 2),
+                 amax_us=round(np.mean(t_amax) * 1e6, 2), device_us_per_step=round(dev * 1e6, 2),
+                 host_inclusive_us_per_step=round(wall * 1e6, 1),
+                 encode_GBps=round(groups * BYTES_PER_GROUP / np.mean(t_enc) / 1e9, 1))
 
 
 def bench_kv(args, torch, ecco, W):
@@ -351,5 +407,5 @@ def bench_copy(args, torch, ecco, W):
 
 
 def run_workload(args, torch, ecco, W):
-    return {"kv": bench_kv, "ffn": bench_ffn, "attn": bench_attn, "design": bench_design,
+    return {"weight": bench_weight, "kv": bench_kv, "ffn": bench_ffn, "attn": bench_attn, "design": bench_design,
             "act": bench_act, "copy": bench_copy}[args.workload](args, torch, ecco, W)
