@@ -28,7 +28,8 @@ and the fused GEMV are reported beside it.
 Other workloads (run separately, same JSON line shape):
   layer  one layer of the set above, drawn on the CPU: the same step on one
          layer, plus diagnostics (each matrix decoded by a launch of its own
-         and by ecco_decode_speculative, the pages' segment-parallel decode;
+         and by ecco_decode_speculative, the pages' segment-parallel decode,
+         and by ecco_decode_segmented with 2, 4 and 8 lanes per block;
          each amax, encode and GEMV by a call of its own; the step captured
          into a HIP graph and replayed)
   weight one 1024x1024 weight (8,192 groups; launch-bound): amax, encode
@@ -453,6 +454,13 @@ def bench_layer(args, torch, ecco, W):
         for m in mats.values():
             timer.run("decode_spec", lambda: ecco.ecco_decode_speculative(m["blocks"], m["out_f"], m["gpr"], m["gpr"],
                                                                           m["in_f"], m["tdev"], m["t"], m["y"]))
+    # and by the segment decoder with 2, 4 and 8 lanes per block
+    for lanes in (2, 4, 8):
+        for _ in range(3):
+            for m in mats.values():
+                timer.run("decode_seg%d" % lanes,
+                          lambda: ecco.ecco_decode_segmented(m["blocks"], m["out_f"], m["gpr"], m["gpr"], m["in_f"],
+                                                             m["tdev"], m["t"], m["y"], lanes))
     # each encode by a call of its own
     for _ in range(3):
         for m in mats.values():
@@ -490,6 +498,7 @@ def bench_layer(args, torch, ecco, W):
         per_matrix_decode_us={nm: float(np.mean(single[i::len(mats)]) * 1e6) for i, nm in enumerate(mats)},
         gemv_separate_us_per_layer=sum(diag["gemv_single"]) / 3 * 1e6,
         spec_decode_us_per_layer=sum(diag["decode_spec"]) / 3 * 1e6,
+        seg_decode_us_per_layer={L: sum(diag["decode_seg%d" % L]) / 3 * 1e6 for L in (2, 4, 8)},
         graph_step_us=graph_us,
     )
     x0 = mats["q"]["w"].cpu().numpy().reshape(-1, 128)
@@ -564,6 +573,8 @@ def layer_line(args, res):
         "speculative_decode_us_per_layer": round(res["spec_decode_us_per_layer"], 2),
         "speculative_decode_GBps": round(res["groups"] * BYTES_PER_GROUP / (res["spec_decode_us_per_layer"] * 1e-6)
                                          / 1e9, 1),
+        "segmented_decode_us_per_layer": {"%d_lanes_per_block" % L: round(v, 2)
+                                          for L, v in res["seg_decode_us_per_layer"].items()},
     })
     return line
 

@@ -19,7 +19,7 @@ __all__ = [
     "EccoError", "lib", "library_path",
     "ecco_tables_size", "ecco_tables_build", "ecco_tables_validate", "ecco_tables_get",
     "ecco_train_patterns", "ecco_tensor_scale_from_amax", "ecco_amax", "ecco_amax_many", "ecco_encode",
-    "ecco_decode", "ecco_decode_speculative", "ecco_encode_many", "ecco_encode_act", "ecco_decode_act",
+    "ecco_decode", "ecco_decode_speculative", "ecco_decode_segmented", "ecco_encode_many", "ecco_encode_act", "ecco_decode_act",
     "ecco_decode_many",
     "ecco_decode_gemv", "ecco_decode_gemv_many", "ecco_attention_workspace_size",
     "ecco_attention_decode", "ecco_attention_decode_noalloc", "ecco_strerror", "ecco_version",
@@ -108,6 +108,7 @@ def lib():
             "ecco_encode": (i32, [vp, u64, u64, u64, u64, vp, f32, vp, vp, vp]),
             "ecco_decode": (i32, [vp, u64, u64, u64, u64, vp, f32, vp, vp]),
             "ecco_decode_speculative": (i32, [vp, u64, u64, u64, u64, vp, f32, vp, vp]),
+            "ecco_decode_segmented": (i32, [vp, u64, u64, u64, u64, vp, f32, vp, ctypes.c_uint32, vp]),
             "ecco_encode_many": (i32, [vp, ctypes.c_uint32, vp]),
             "ecco_encode_act": (i32, [vp, u64, u64, u64, u64, vp, f32, vp, vp, vp]),
             "ecco_decode_act": (i32, [vp, u64, u64, u64, u64, vp, f32, vp, vp]),
@@ -268,6 +269,16 @@ def ecco_decode_speculative(blocks, n_rows, groups_per_row, blk_row_stride_block
     _check(lib().ecco_decode_speculative(_dptr(blocks), int(n_rows), int(groups_per_row),
                                          int(blk_row_stride_blocks), int(y_row_stride_elems), _dptr(tables_dev),
                                          float(tensor_scale), _dptr(y), _stream(stream)), "ecco_decode_speculative")
+
+
+def ecco_decode_segmented(blocks, n_rows, groups_per_row, blk_row_stride_blocks, y_row_stride_elems,
+                          tables_dev, tensor_scale, y, lanes_per_block, stream=None):
+    """ecco_decode with 2, 4 or 8 lanes per block, each decoding a segment
+    speculatively (same output, slower)."""
+    _check(lib().ecco_decode_segmented(_dptr(blocks), int(n_rows), int(groups_per_row),
+                                       int(blk_row_stride_blocks), int(y_row_stride_elems), _dptr(tables_dev),
+                                       float(tensor_scale), _dptr(y), int(lanes_per_block), _stream(stream)),
+           "ecco_decode_segmented")
 
 
 def ecco_encode_many(jobs, stream=None):

@@ -229,6 +229,264 @@ __global__ __launch_bounds__(kSpecWaves * 64) void decode_spec_kernel(SpecArgs a
   }
 }
 
+
+// ------------------------------------------------ segments of 2, 4 or 8 lanes
+//
+// The middle ground between one lane per block (ecco_decode) and one wave per
+// block (above): L lanes share a block, lane k owning stream bits
+// 16 + k * SB .. 16 + (k + 1) * SB - 1 (SB = 496 / L: 248, 124 or 62 bits).
+//   speculate  each lane decodes its segment from its first bit, as if a
+//              codeword started there, keeping the look-up entries (symbol
+//              and length) in LDS, until a codeword ends at or past the
+//              segment's end (in the last segment: until the next codeword
+//              would end past bit 512, the clip rule); the overshoot is the
+//              exit offset into the next segment
+//   resolve    segment k's true entry is segment k - 1's exit.  A lane whose
+//              entry differs from its guess decodes again from the true
+//              entry until the new path meets a codeword boundary of the
+//              speculative one (prefix codes fall back into step within a
+//              few codewords, and from there the two paths agree), keeping
+//              only the new prefix.  If the new path leaves the segment
+//              without meeting the old one, its exit differs too, and the
+//              next segment redoes its decode in the next round; L rounds
+//              settle every block (the pages' merge, one segment at a time)
+//   emit       a segmented scan of the lanes' codeword counts gives each
+//              lane its first output index; each lane writes the value-table
+//              offsets of its codewords below index 128 and the one holding
+//              codeword 127 reports where it ends (the outlier records'
+//              start); then the value table, the records and the FP16 store
+//              as in the other decoders
+// One look-up per codeword as in the lane-serial decoder, plus the re-decoded
+// prefixes, an LDS write and read per codeword, and a wave holds 64 / L
+// blocks instead of 64.
+template <int L>
+struct SegGeom {
+  static_assert(L == 2 || L == 4 || L == 8, "2, 4 or 8 lanes per block");
+  static constexpr uint32_t kBlocks = 64 / L;                 // blocks per wave pass
+  static constexpr uint32_t kSegBits = (512 - 16) / L;        // stream bits per segment
+  static constexpr int kWaves = L == 2 ? 2 : L == 4 ? 4 : 8;  // waves per workgroup (LDS bound)
+  static constexpr uint32_t kChunks = kBlocks * 4;            // 16-byte pieces of a pass
+  static constexpr uint32_t kChunksPerLane = (kChunks + 63) / 64;
+};
+
+template <int L>
+struct SegSmem {
+  using G = SegGeom<L>;
+  uint8_t lut[S * H * 256];
+  float cent[S * 16];
+  uint32_t blk[G::kWaves][G::kBlocks][20];            // 16 block words + zero pad (windows past bit 512)
+  uint8_t spec[G::kWaves][64][G::kSegBits];           // speculative look-up entries per lane
+  uint8_t pre[G::kWaves][64][G::kSegBits];            // re-decoded prefix per lane
+  uint32_t sym[G::kWaves][G::kBlocks][36];            // value-table byte offset per position (+ pad)
+  uint16_t vt[G::kWaves][G::kBlocks][32];
+};
+
+template <int L>
+__global__ __launch_bounds__(SegGeom<L>::kWaves * 64) void decode_seg_kernel(SpecArgs a) {
+  using G = SegGeom<L>;
+  constexpr uint32_t SB = G::kSegBits, NB = G::kBlocks;
+  __shared__ SegSmem<L> sm;
+  {
+    const uint4* src = reinterpret_cast<const uint4*>(&a.tab->lut[0][0][0]);
+    uint4* dst = reinterpret_cast<uint4*>(sm.lut);
+    for (uint32_t i = threadIdx.x; i < S * H * 256 / 16; i += blockDim.x) dst[i] = src[i];
+    const float* c = &a.tab->centroids[0][0];
+    for (uint32_t i = threadIdx.x; i < S * 16; i += blockDim.x) sm.cent[i] = c[i];
+  }
+  __syncthreads();
+  const uint32_t lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint64_t stride = (uint64_t)gridDim.x * G::kWaves * NB;
+  const uint64_t n_groups = a.n_groups;
+  // piece c of the pass starting at group gb: bytes 16 (c & 3) .. + 15 of
+  // group gb + (c >> 2); past the last group, the last group's (never stored)
+  auto load = [&](uint64_t gb, uint32_t c) -> uint4 {
+    const uint32_t gg = (uint32_t)min(gb + min(c, G::kChunks - 1u) / 4u, n_groups - 1u);
+    const uint32_t r = div_magic(gg, a.gpr), col = gg - r * a.gpr.d;
+    return load_stream(a.blocks + ((uint64_t)r * a.blk_stride + col) * 64u + 16u * (c & 3u));
+  };
+  uint64_t g0 = ((uint64_t)blockIdx.x * G::kWaves + wave) * NB;
+  uint4 cur[G::kChunksPerLane];
+#pragma unroll
+  for (uint32_t i = 0; i < G::kChunksPerLane; ++i) cur[i] = load(g0, lane + 64u * i);
+  uint32_t (*B)[20] = sm.blk[wave];
+  uint8_t* sp = sm.spec[wave][lane];
+  uint8_t* pr = sm.pre[wave][lane];
+  const uint32_t bi = lane / L, k = lane % L;
+  const bool last = k == L - 1u;
+  const uint32_t s = 16u + k * SB, ek = last ? 512u : s + SB;
+  const float t = a.t;
+  for (; g0 < n_groups; g0 += stride) {
+    uint4 nxt[G::kChunksPerLane];
+#pragma unroll
+    for (uint32_t i = 0; i < G::kChunksPerLane; ++i) nxt[i] = load(g0 + stride, lane + 64u * i);
+#pragma unroll
+    for (uint32_t i = 0; i < G::kChunksPerLane; ++i) {
+      const uint32_t c = lane + 64u * i;
+      if (c < G::kChunks) {
+        uint32_t* d = &B[c >> 2][4u * (c & 3u)];
+        d[0] = cur[i].x;
+        d[1] = cur[i].y;
+        d[2] = cur[i].z;
+        d[3] = cur[i].w;
+      }
+    }
+    if (lane < NB) {
+      B[lane][16] = 0u;
+      B[lane][17] = 0u;
+      B[lane][18] = 0u;
+      B[lane][19] = 0u;
+    }
+    for (uint32_t i = lane; i < NB * 36u; i += 64u) (&sm.sym[wave][0][0])[i] = 0x20202020u;  // entry 16: +0
+    wave_sync();
+    const uint32_t* W = B[bi];
+    const uint32_t head = W[0];
+    const uint32_t lutb = ((head & 63u) * 4u + ((head >> 6) & 3u)) * 256u;
+    // decodes from bit `pos` while pos < ek and the codeword fits before bit
+    // 512, handing each entry to put(); returns the position reached
+    auto run = [&](uint32_t pos, auto put) -> uint32_t {
+      uint32_t kw = pos >> 5, lo = W[kw], hi = W[kw + 1u];
+      while (pos < ek) {
+        const uint32_t e = sm.lut[lutb + (window(lo, hi, pos - 32u * kw) & 255u)];
+        const uint32_t np = pos + (e >> 5) + 1u;
+        if (np > 512u) break;
+        put(e);
+        pos = np;
+        if (pos - 32u * kw >= 32u) {
+          ++kw;
+          lo = hi;
+          hi = W[kw + 1u];
+        }
+      }
+      return pos;
+    };
+    // 1. speculate
+    uint32_t cnt = 0;
+    const uint32_t spos = run(s, [&](uint32_t e) { sp[cnt++] = (uint8_t)e; });
+    uint32_t xit = last ? 0u : spos - ek;           // exit offset into the next segment
+    // 2. resolve: final codewords = pr[0 .. n_new) then sp[jo .. cnt)
+    uint32_t ent = 0, n_new = 0, jo = 0;
+    for (uint32_t round = 0; round < (uint32_t)L; ++round) {
+      const uint32_t left = __shfl(xit, k == 0u ? lane : lane - 1u);
+      const uint32_t want = k == 0u ? 0u : left;
+      const bool redo = want != ent;
+      if (!__any(redo)) break;
+      if (redo) {
+        ent = want;
+        n_new = 0;
+        uint32_t end;
+        if (round == 0u) {
+          // meet the speculative path: po walks its codeword boundaries
+          uint32_t pn = s + ent, po = s;
+          jo = 0;
+          uint32_t kw = pn >> 5, lo = W[kw], hi = W[kw + 1u];
+          while (true) {
+            while (po < pn && jo < cnt) po += (uint32_t)(sp[jo++] >> 5) + 1u;
+            if (po == pn || pn >= ek) break;
+            const uint32_t e = sm.lut[lutb + (window(lo, hi, pn - 32u * kw) & 255u)];
+            const uint32_t np = pn + (e >> 5) + 1u;
+            if (np > 512u) break;
+            pr[n_new++] = (uint8_t)e;
+            pn = np;
+            if (pn - 32u * kw >= 32u) {
+              ++kw;
+              lo = hi;
+              hi = W[kw + 1u];
+            }
+          }
+          if (po == pn) {
+            end = spos;                              // met: the rest is the speculative decode
+          } else {
+            end = pn;
+            jo = cnt;
+          }
+        } else {
+          end = run(s + ent, [&](uint32_t e) { pr[n_new++] = (uint8_t)e; });
+          jo = cnt;
+        }
+        if (!last) xit = end - ek;
+      }
+    }
+    // 3. output indices: inclusive scan of the codeword counts over the block's lanes
+    const uint32_t mine = n_new + (cnt - jo);
+    uint32_t incl = mine;
+#pragma unroll
+    for (uint32_t d = 1; d < (uint32_t)L; d <<= 1) {
+      const uint32_t v = __shfl_up(incl, d, L);
+      if (k >= d) incl += v;
+    }
+    const uint32_t base = incl - mine;
+    const uint32_t total = __shfl(incl, L - 1, L);
+    const bool full = total >= 128u;
+    uint8_t* row = reinterpret_cast<uint8_t*>(sm.sym[wave][bi]);
+    uint32_t E = 0;                                  // end of codeword 127 (its lane only)
+    {
+      uint32_t pe = s + ent;
+      const uint32_t m = base < 128u ? min(mine, 128u - base) : 0u;
+      for (uint32_t i = 0; i < m; ++i) {
+        const uint32_t e = i < n_new ? pr[i] : sp[jo + i - n_new];
+        row[base + i] = (uint8_t)((e & 31u) << 1);
+        pe += (e >> 5) + 1u;
+        if (base + i == 127u) E = pe;
+      }
+    }
+#pragma unroll
+    for (uint32_t d = 1; d < (uint32_t)L; d <<= 1) E = max(E, (uint32_t)__shfl_xor(E, d, L));
+    // 4. value table: [0..14] fp16(c * a), [15] fp16(S), [16 + r] record r or +0
+    const uint32_t n = full ? min(16u, (512u - E) / 15u) : 0u;
+    const uint32_t p = head & 63u;
+    const float Sv = fp8_decode<1>(head) * t;
+    const float aa = fabsf(Sv);
+    uint16_t* vt = sm.vt[wave][bi];
+    for (uint32_t j = k; j < 32u; j += L) {
+      uint32_t hv;
+      if (j < 15u) {
+        hv = f16_bits(sm.cent[p * 16u + j] * aa);
+      } else if (j == 15u) {
+        hv = f16_bits(Sv);
+      } else {
+        const uint32_t r = j - 16u;
+        hv = 0u;
+        if (r < n) {
+          const uint32_t bpos = 512u - 15u * (r + 1u);
+          const uint32_t rec = window(W[bpos >> 5], W[(bpos >> 5) + 1u], bpos & 31u) & 0x7fffu;
+          hv = f16_bits(fp8_decode<0>(rec >> 7) * t);
+        }
+      }
+      vt[j] = (uint16_t)hv;
+    }
+    wave_sync();
+    // outlier positions take entry 16 + r, in record order (a later record wins)
+    if (k == 0u) {
+      for (uint32_t r = 0; r < n; ++r) {
+        const uint32_t bpos = 512u - 15u * (r + 1u);
+        const uint32_t rec = window(W[bpos >> 5], W[(bpos >> 5) + 1u], bpos & 31u) & 0x7fffu;
+        row[rec & 127u] = (uint8_t)(2u * (16u + r));
+      }
+    }
+    wave_sync();
+    // 5. FP16 store: 8 values per lane, four 256-byte rows per step
+#pragma unroll
+    for (uint32_t it = 0; it < NB / 4u; ++it) {
+      const uint32_t b = 4u * it + lane / 16u, j0 = 8u * (lane % 16u);
+      const uint64_t gg = g0 + b;
+      const uint2 sv = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(sm.sym[wave][b]) + j0);
+      const uint8_t* tb = reinterpret_cast<const uint8_t*>(sm.vt[wave][b]);
+      auto v = [&](uint32_t w, int q) -> uint32_t {
+        return *reinterpret_cast<const uint16_t*>(tb + ((w >> (8 * q)) & 0xffu));
+      };
+      const uint4 o = make_uint4(v(sv.x, 0) | (v(sv.x, 1) << 16), v(sv.x, 2) | (v(sv.x, 3) << 16),
+                                 v(sv.y, 0) | (v(sv.y, 1) << 16), v(sv.y, 2) | (v(sv.y, 3) << 16));
+      if (gg < n_groups) {
+        const uint32_t r = div_magic((uint32_t)gg, a.gpr), col = (uint32_t)gg - r * a.gpr.d;
+        store_stream(a.y + (uint64_t)r * a.y_stride + (uint64_t)col * 128u + j0, o);
+      }
+    }
+    wave_sync();
+#pragma unroll
+    for (uint32_t i = 0; i < G::kChunksPerLane; ++i) cur[i] = nxt[i];
+  }
+}
+
 }  // namespace ecco
 
 using namespace ecco;
@@ -258,5 +516,44 @@ extern "C" int ecco_decode_speculative(const void* blocks, uint64_t n_rows, uint
   const uint32_t grid = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(want, (uint64_t)cus * 2));
   (void)hipGetLastError();
   hipLaunchKernelGGL(decode_spec_kernel, dim3(grid), dim3(kSpecWaves * 64), 0, static_cast<hipStream_t>(stream), a);
+  return hipGetLastError() == hipSuccess ? ECCO_OK : ECCO_EHIP;
+}
+
+
+extern "C" int ecco_decode_segmented(const void* blocks, uint64_t n_rows, uint64_t gpr, uint64_t blk_stride,
+                                     uint64_t y_stride, const void* tables, float tensor_scale, uint16_t* y,
+                                     uint32_t lanes_per_block, void* stream) {
+  if (!blocks || !tables || !y) return ECCO_EINVAL;
+  if (!(tensor_scale > 0.0f) || !(tensor_scale < __builtin_huge_valf())) return ECCO_EINVAL;
+  if (lanes_per_block != 2 && lanes_per_block != 4 && lanes_per_block != 8) return ECCO_EINVAL;
+  uint64_t total = 0;
+  if (!group_count(n_rows, gpr, &total)) return ECCO_ESIZE;
+  if (n_rows > 1 && (y_stride < gpr * 128 || blk_stride < gpr)) return ECCO_ESIZE;
+  if (!host_aligned(y, 16) || (y_stride % 8) != 0 || !host_aligned(blocks, 64) || !host_aligned(tables, 256))
+    return ECCO_EALIGN;
+  int cus = 0, rc = check_gfx950(&cus);
+  if (rc) return rc;
+  SpecArgs a;
+  a.blocks = static_cast<const uint8_t*>(blocks);
+  a.y = y;
+  a.tab = static_cast<const Tables*>(tables);
+  a.blk_stride = n_rows > 1 ? blk_stride : gpr;
+  a.y_stride = n_rows > 1 ? y_stride : gpr * 128;
+  a.gpr = make_magic((uint32_t)gpr);
+  a.n_groups = (uint32_t)total;
+  a.t = tensor_scale;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  // one workgroup per CU (the LDS holds one), each wave 64 / L blocks per pass
+  auto launch = [&](auto kernel, uint64_t per_wg, int waves) {
+    const uint64_t want = (total + per_wg - 1) / per_wg;
+    const uint32_t grid = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(want, (uint64_t)cus));
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(waves * 64), 0, s, a);
+  };
+  switch (lanes_per_block) {
+    case 2: launch(decode_seg_kernel<2>, SegGeom<2>::kWaves * SegGeom<2>::kBlocks, SegGeom<2>::kWaves); break;
+    case 4: launch(decode_seg_kernel<4>, SegGeom<4>::kWaves * SegGeom<4>::kBlocks, SegGeom<4>::kWaves); break;
+    default: launch(decode_seg_kernel<8>, SegGeom<8>::kWaves * SegGeom<8>::kBlocks, SegGeom<8>::kWaves); break;
+  }
   return hipGetLastError() == hipSuccess ? ECCO_OK : ECCO_EHIP;
 }

@@ -299,6 +299,22 @@ int ecco_decode_speculative(const void* blocks_dev, uint64_t n_rows, uint64_t gr
                             uint64_t blk_row_stride_blocks, uint64_t y_row_stride_elems,
                             const void* tables_dev, float tensor_scale, uint16_t* y_dev, void* stream);
 
+/* Decode by speculation over a few long segments (the pages' overlapping
+ * segments and merge, Fig. 8 caption and "What carries the argument", with
+ * fewer, longer segments): lanes_per_block (2, 4 or 8) lanes share a block,
+ * each decoding 496 / lanes_per_block stream bits from their first bit as if
+ * a codeword started there; a lane whose true entry (the exit of the segment
+ * before it) differs decodes again from it until its path meets a codeword
+ * boundary of the first one; the symbol counts, scanned over the block's
+ * lanes, place each segment's symbols.  Arguments, layout, rules and output
+ * as ecco_decode, and the same output bit for bit; ECCO_EINVAL for another
+ * lanes_per_block.  A comparison decoder: each block costs more look-ups and
+ * LDS traffic than in ecco_decode, which is the one to use. */
+int ecco_decode_segmented(const void* blocks_dev, uint64_t n_rows, uint64_t groups_per_row,
+                          uint64_t blk_row_stride_blocks, uint64_t y_row_stride_elems,
+                          const void* tables_dev, float tensor_scale, uint16_t* y_dev,
+                          uint32_t lanes_per_block, void* stream);
+
 /* One tensor of an ecco_decode_many call: the arguments of ecco_decode. */
 typedef struct {
   const void* blocks_dev;

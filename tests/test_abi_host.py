@@ -129,6 +129,10 @@ def test_device_entry_points_check_arguments_before_touching_the_device():
     assert L.ecco_decode_speculative(A, 1, 1, 1, 128, A + 64, 1.0, A, None) == -2
     assert L.ecco_decode_speculative(A, 2, 4, 3, 512, A, 1.0, A, None) == -3
     assert L.ecco_decode_speculative(None, 1, 1, 1, 128, A, 1.0, A, None) == -1
+    for lanes in (0, 1, 3, 16, 64):
+        assert L.ecco_decode_segmented(A, 1, 1, 1, 128, A, 1.0, A, lanes, None) == -1
+    assert L.ecco_decode_segmented(A, 1, 1, 1, 128, A + 64, 1.0, A, 4, None) == -2
+    assert L.ecco_decode_segmented(A, 2, 4, 3, 512, A, 1.0, A, 4, None) == -3
     assert L.ecco_decode_gemv(A, A, 1.0, 16, 100, A, 1, A, None) == -3          # in % 128
     assert L.ecco_decode_gemv(A, A, 1.0, 16, 128, A, 9, A, None) == -3          # batch > 8
     assert L.ecco_amax(A, 0, A, None) == -3
@@ -140,6 +144,7 @@ def test_device_entry_points_check_arguments_before_touching_the_device():
         assert L.ecco_decode(A, n_rows, gpr, gpr, gpr * 128, A, 1.0, A, None) == -3
         assert L.ecco_decode_act(A, n_rows, gpr, gpr, gpr * 64, A, 1.0, A, None) == -3
         assert L.ecco_decode_speculative(A, n_rows, gpr, gpr, gpr * 128, A, 1.0, A, None) == -3
+        assert L.ecco_decode_segmented(A, n_rows, gpr, gpr, gpr * 128, A, 1.0, A, 2, None) == -3
     assert L.ecco_decode_gemv(A, A, 1.0, 1 << 10, 128 << 54, A, 1, A, None) == -3   # 2^10 x 2^54 groups
     # ecco_encode_many: count, reserved field, every job checked
     ej = (ecco.EncodeJob * 2)()

@@ -1,6 +1,7 @@
-"""GPU parity of the speculative decoder (ecco_decode_speculative, the pages'
-segment-parallel method on one wavefront per block) against the oracle and
-against ecco_decode: decoded FP16 bits identical.  Cases: the 1024x1024 weight
+"""GPU parity of the speculative decoders (ecco_decode_speculative, the pages'
+segment-parallel method on one wavefront per block, and ecco_decode_segmented
+with 2, 4 and 8 lanes per block) against the oracle and against ecco_decode:
+decoded FP16 bits identical.  Cases: the 1024x1024 weight
 matrix, random and clipping tables over ragged sizes, special groups, 40,000
 random blocks (invalid windows, clipping, NaN scale bytes), strided rows."""
 
@@ -64,12 +65,23 @@ def random_tables(seed, adversarial=False):
     return codec.Tables(c, L)
 
 
-def both_decodes(blocks, tdev, t):
+SEG_LANES = (2, 4, 8)
+
+
+def spec_decode(bd, n_rows, gpr, bs, ys, tdev, t, y, lanes):
+    """lanes 64: ecco_decode_speculative; 2, 4, 8: ecco_decode_segmented."""
+    if lanes == 64:
+        ecco.ecco_decode_speculative(bd, n_rows, gpr, bs, ys, tdev, t, y)
+    else:
+        ecco.ecco_decode_segmented(bd, n_rows, gpr, bs, ys, tdev, t, y, lanes)
+
+
+def both_decodes(blocks, tdev, t, lanes=64):
     G = blocks.shape[0]
     bd = torch.from_numpy(np.ascontiguousarray(blocks)).cuda()
     ys = torch.full((G, 128), 0x7FFF, dtype=torch.int16, device="cuda")
     yl = torch.full((G, 128), 0x7FFF, dtype=torch.int16, device="cuda")
-    ecco.ecco_decode_speculative(bd, 1, G, G, G * 128, tdev, t, ys)
+    spec_decode(bd, 1, G, G, G * 128, tdev, t, ys, lanes)
     ecco.ecco_decode(bd, 1, G, G, G * 128, tdev, t, yl)
     torch.cuda.synchronize()
     return ys.cpu().numpy().view(np.float16), yl.cpu().numpy().view(np.float16)
@@ -87,9 +99,13 @@ def assert_fp16_equal(a, b, what):
 
 
 def check(blocks, tb, t, what):
-    ys, yl = both_decodes(blocks, dev_tables(tb), t)
-    assert_fp16_equal(ys, codec.decode_blocks(blocks, tb, t), what + " vs oracle")
-    assert_fp16_equal(ys, yl, what + " vs ecco_decode")
+    tdev = dev_tables(tb)
+    ref = codec.decode_blocks(blocks, tb, t)
+    for lanes in (64,) + SEG_LANES:
+        say("  %d lanes per block" % lanes)
+        ys, yl = both_decodes(blocks, tdev, t, lanes)
+        assert_fp16_equal(ys, ref, "%s, %d lanes per block, vs oracle" % (what, lanes))
+        assert_fp16_equal(ys, yl, "%s, %d lanes per block, vs ecco_decode" % (what, lanes))
 
 
 def test_spec_c1_weight(dev):
@@ -132,7 +148,8 @@ def test_spec_random_blocks(dev):
             check(blocks, tb, t, "fuzz %s t=%g" % (name, t))
 
 
-def test_spec_strided_rows(dev):
+@pytest.mark.parametrize("lanes", (64,) + SEG_LANES)
+def test_spec_strided_rows(dev, lanes):
     tb = golden("c1")
     tdev = dev_tables(tb)
     rows, gpr, bs, ys = 3, 50, 53, 50 * 128 + 40
@@ -143,8 +160,8 @@ def test_spec_strided_rows(dev):
     bfull[:, :gpr] = ob.reshape(rows, gpr, 64)
     bd = torch.from_numpy(bfull).cuda()
     yd = torch.full((rows, ys), 0x7FFF, dtype=torch.int16, device="cuda")
-    say("speculative decode, strided rows")
-    ecco.ecco_decode_speculative(bd, rows, gpr, bs, ys, tdev, t, yd)
+    say("speculative decode, strided rows, %d lanes per block" % lanes)
+    spec_decode(bd, rows, gpr, bs, ys, tdev, t, yd, lanes)
     torch.cuda.synchronize()
     got = yd.cpu().numpy()
     assert_fp16_equal(got[:, :gpr * 128].view(np.float16).reshape(-1, 128), codec.decode_blocks(ob, tb, t),
