@@ -8,12 +8,17 @@
 //   scores   one wave per 64 tokens of one (sequence, kv head): the shared
 //            decode core hands each lane 8 values of one token's K row;
 //            v_dot2_f32_f16 against the G query heads' matching 8 values, a
-//            DPP row sum over the token's 16 lanes, scale -> s[pair][t][g]
-//   softmax  one workgroup per pair: max, sum of exp, normalise in place
-//   p . V    one wave per 128 tokens of one pair: decoded V values times the
-//            token's probabilities, FP32 accumulators for the G heads and the
-//            lane's 8 positions, a cross-row reduction, partial sums per unit
-//   combine  the units' partial sums of each output row added in order
+//            DPP row sum over the token's 16 lanes, times scale * log2(e)
+//            -> s[pair][t][g] (scores in base-2 units), and each head's
+//            largest score of the 64 tokens -> bmax[pair][t / 64][g]
+//   p . V    one wave per 128 tokens (a unit) of one pair: with m the unit's
+//            largest score (of its two bmax entries), p_t = 2^(s_t - m)
+//            times the decoded V values, FP32 accumulators for the G heads
+//            and the lane's 8 positions, a cross-row reduction; the unit's
+//            partial sums, m and z = sum of its p_t
+//   combine  per output row: M = the largest unit m, then the units' partial
+//            sums and z, each weighted by 2^(m - M), added in unit order;
+//            out = sum / z (the softmax normalisation, applied once)
 //
 // Every sum is taken in a fixed order, so results do not depend on timing.
 #include <hip/hip_runtime.h>
@@ -27,10 +32,14 @@
 namespace ecco {
 
 constexpr uint32_t kUnitTokens = 128;   // tokens per p . V work unit (two batches)
-constexpr int kScoreWaves = 12;         // waves per workgroup of the scores kernel (at G = 4 the compiler
-                                        // spills 24 registers to fit 3 waves per SIMD, still 4.5 % faster
-                                        // than 2 waves per SIMD without spills)
+// waves per workgroup of the scores kernel: three per SIMD; at G = 8 the
+// eight scores per token need more registers than that leaves, so two
+template <int G>
+constexpr int score_waves() { return G > 4 ? 8 : 12; }
 constexpr int kPvWaves = 8;             // waves per workgroup of the p . V kernel
+
+// DPP row rotations (GFX9 encoding)
+constexpr int kRowRor1 = 0x121, kRowRor2 = 0x122, kRowRor4 = 0x124, kRowRor8 = 0x128;
 
 struct AttnArgs {
   const uint8_t* kb;
@@ -38,8 +47,10 @@ struct AttnArgs {
   const Tables* kt;
   const Tables* vt;
   const uint16_t* q;
-  float* probs;          // [pairs][S][G]
-  float* part;           // [pairs][n_units][G][128]
+  float* probs;          // [pairs][S][G] scores, base-2 units
+  float* part;           // [pairs][n_units][G][128] unnormalised partial sums
+  float* bmax;           // [pairs][n_kb][G] largest score of each 64-token batch
+  float* mz;             // [pairs][n_units][G] (m, z) of each unit
   float* out;            // [pairs * G][128]
   uint32_t pairs, S, stride, n_kb, n_units, G;
   float kts, vts, scale;
@@ -48,15 +59,20 @@ struct AttnArgs {
 // The 64 blocks of batch t0 .. t0 + 63 of one pair (clamped at S); with
 // live == false the cached table blob is read instead (a prefetch past the
 // end that must stay unconditional).
+// The lane index goes through an opaque copy, so that the four block
+// indices (lane / 4 + 16 i) are computed at each fetch rather than kept in
+// registers across the batch (the score kernel spilled them).
 __device__ __forceinline__ BatchRegs fetch_tokens(uint32_t lane, const uint8_t* rows, const uint8_t* idle,
                                                   uint32_t n_valid, bool live) {
+  asm volatile("" : "+v"(lane));
   return fetch_batch(lane, n_valid, [&](uint32_t i, uint32_t q) {
     return load_stream((live ? rows + (uint64_t)i * 64u : idle + 64u * (i & 63u)) + 16u * q);
   });
 }
 
 template <int G>
-__global__ __launch_bounds__(kScoreWaves * 64) void attn_scores_kernel(AttnArgs a) {
+__global__ __launch_bounds__(score_waves<G>() * 64) void attn_scores_kernel(AttnArgs a) {
+  constexpr int kScoreWaves = score_waves<G>();
   __shared__ DecodeSmem<kScoreWaves> sm;
   stage_decode_tables(sm, a.kt);
   __syncthreads();
@@ -86,7 +102,7 @@ __global__ __launch_bounds__(kScoreWaves * 64) void attn_scores_kernel(AttnArgs 
     // A load under a run-time condition is not moved earlier than written.
     const uint16_t* qb = a.q + (uint64_t)pair * G * 128u;
     uint4 qv[G];
-    auto pre = [&](uint32_t) {
+    auto load_q = [&]() {
       const uint16_t* qp = qb;
       asm volatile("" : "+s"(qp));
       if (n_valid != 0u) {
@@ -94,14 +110,23 @@ __global__ __launch_bounds__(kScoreWaves * 64) void attn_scores_kernel(AttnArgs 
         for (int g = 0; g < G; ++g) qv[g] = *reinterpret_cast<const uint4*>(qp + (uint32_t)g * 128u + j0);
       }
     };
+    auto pre = [&](uint32_t) { load_q(); };
     // this lane's token's scores within a write-out step; step (k, it) adds
     // 16 k + 4 it tokens, a constant that the store's offset field takes
     // (written as one 64-bit product, the 16 offsets were kept in registers)
     float* sp = a.probs + ((uint64_t)pair * a.S + t0 + lane / 16u) * G;
+    // the largest score of head lane % G over the tokens this lane sees
+    // (every lane of a row holds all G scores of the row's token; one
+    // register instead of G)
+    float mloc = -__builtin_inff();
     auto sink = [&](uint32_t b, uint32_t, uint4 w, uint32_t, uint32_t) {
       float d[G];
 #pragma unroll
       for (int g = 0; g < G; ++g) d[g] = row_sum_f32(dot8(w, qv[g], 0.0f)) * a.scale;
+      float mine = d[0];
+#pragma unroll
+      for (int g = 1; g < G; ++g) mine = (lane & (G - 1u)) == (uint32_t)g ? d[g] : mine;
+      mloc = fmaxf(mloc, mine);
       // one vector store of the token's G scores (whole 16-byte pieces, so the
       // four tokens of an instruction fill their 64 bytes without partial writes)
       if ((lane & 15u) == 0) {
@@ -121,63 +146,26 @@ __global__ __launch_bounds__(kScoreWaves * 64) void attn_scores_kernel(AttnArgs 
       decode_batch<true, kScoreWaves, 128, true>(sm, wave, lane, 64u, a.kts, cur, sink, pre);
     else
       decode_batch<false, kScoreWaves, 128, true>(sm, wave, lane, n_valid, a.kts, cur, sink, pre);
+    // the batch's largest score per head: rotations of each row by G, 2G,
+    // ... keep a lane's residue mod G, so lane g of every row ends with its
+    // row's maximum of head g (a lane that saw no token holds -inf); then
+    // the four rows' values of each head, read out as scalars
+    if constexpr (G < 2) mloc = fmaxf(mloc, dpp_f32<kRowRor1>(mloc));
+    if constexpr (G < 4) mloc = fmaxf(mloc, dpp_f32<kRowRor2>(mloc));
+    if constexpr (G < 8) mloc = fmaxf(mloc, dpp_f32<kRowRor4>(mloc));
+    mloc = fmaxf(mloc, dpp_f32<kRowRor8>(mloc));
+    float bm[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      auto rd = [&](int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mloc), l)); };
+      bm[g] = fmaxf(fmaxf(rd(g), rd(16 + g)), fmaxf(rd(32 + g), rd(48 + g)));
+    }
+    if (lane == 0u) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) a.bmax[(uint64_t)batch * G + g] = bm[g];
+    }
     cur = nxt;
   }
-}
-
-// Softmax of one pair's G rows, [S][G] with g innermost, by one workgroup:
-// three coalesced passes over the pair's scores (max, sum of exp, then exp
-// again divided by the sum, written in place), which stay in the L2 cache
-// between them; workgroup reductions through LDS.  Recomputing exp in the
-// last pass gives the same values as the second and saves a write pass.
-constexpr int kSmThreads = 1024;
-
-template <int G>
-__global__ __launch_bounds__(kSmThreads) void attn_softmax_kernel(AttnArgs a) {
-  __shared__ float red[kSmThreads / 64][G];
-  __shared__ float fin[G];
-  const uint32_t tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-  float* base = a.probs + (uint64_t)blockIdx.x * a.S * G;
-  auto wg_reduce = [&](float (&v)[G], bool is_max) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float w = is_max ? wave_max_f32(v[g]) : wave_sum_f32(v[g]);
-      if (lane == 0) red[wave][g] = w;
-    }
-    __syncthreads();
-    if (tid < (uint32_t)G) {
-      float r = red[0][tid];
-      for (int w = 1; w < kSmThreads / 64; ++w) r = is_max ? fmaxf(r, red[w][tid]) : r + red[w][tid];
-      fin[tid] = r;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int g = 0; g < G; ++g) v[g] = fin[g];
-    __syncthreads();
-  };
-  float m[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) m[g] = -__builtin_inff();
-  for (uint32_t t = tid; t < a.S; t += kSmThreads)
-#pragma unroll
-    for (int g = 0; g < G; ++g) m[g] = fmaxf(m[g], base[(uint64_t)t * G + g]);
-  wg_reduce(m, true);
-  float z[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) z[g] = 0.0f;
-  for (uint32_t t = tid; t < a.S; t += kSmThreads)
-#pragma unroll
-    for (int g = 0; g < G; ++g) z[g] += expf(base[(uint64_t)t * G + g] - m[g]);
-  wg_reduce(z, false);
-  float inv[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) inv[g] = 1.0f / z[g];
-  for (uint32_t t = tid; t < a.S; t += kSmThreads)
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float* q = base + (uint64_t)t * G + g;
-      *q = expf(*q - m[g]) * inv[g];
-    }
 }
 
 // p . V for heads g_off .. g_off + GH - 1 of G.
@@ -203,23 +191,34 @@ __global__ __launch_bounds__(kPvWaves * 64) void attn_pv_kernel(AttnArgs a, uint
   };
   BatchRegs cur = fetch(unit, 0, true);
   const uint32_t j0 = 8u * (lane & 15u);
-  float acc[GH][8];
+  float acc[GH][8], z[GH];
 #pragma unroll
-  for (int g = 0; g < GH; ++g)
+  for (int g = 0; g < GH; ++g) {
+    z[g] = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[g][i] = 0.0f;
+  }
   // slots (unit, half) in order; a unit's sums are flushed after its second half
   for (uint32_t half = 0; unit < total;) {
     const uint32_t pair = unit / a.n_units, u = unit % a.n_units;
     const uint32_t nu = unit + stride;
+    // the unit's largest score per head: the larger of its batches' maxima
+    // (the second batch only if the unit reaches past 64 tokens)
+    float m[GH];
+    {
+      const float* bm = a.bmax + ((uint64_t)pair * a.n_kb + 2u * u) * a.G + g_off;
+      const bool two = u * kUnitTokens + 64u < a.S;
+#pragma unroll
+      for (int g = 0; g < GH; ++g) m[g] = two ? fmaxf(bm[g], bm[a.G + g]) : bm[g];
+    }
     const BatchRegs nxt = half == 0u ? fetch(unit, 1, true) : fetch(nu < total ? nu : unit, 0, nu < total);
     const uint32_t t0 = u * kUnitTokens + 64u * half;
     if (t0 < a.S) {
       const uint32_t n_valid = min(64u, a.S - t0);
-      // the probabilities of a pass's four tokens per lane, loaded as the
-      // pass starts (from an opaque copy of the address, under a run-time
-      // condition, so the loads are neither hoisted to the batch's start
-      // nor held across the decode).  Step (k, it) takes token 16 k + 4 it +
+      // the weights p = 2^(s - m) of a pass's four tokens per lane, their
+      // scores loaded as the pass starts (from an opaque copy of the address,
+      // under a run-time condition, so the loads are neither hoisted to the
+      // batch's start nor held across the decode).  Step (k, it) takes token 16 k + 4 it +
       // lane / 16; tl is an opaque copy of lane / 16, so that the compiler
       // does not keep the 16 token indices of a batch in registers; a token
       // past n_valid reads token 0 (its products are never used).
@@ -237,14 +236,17 @@ __global__ __launch_bounds__(kPvWaves * 64) void attn_pv_kernel(AttnArgs a, uint
             const int c = (int)(16u * k) + 4 * it;
             const float* src = (int)tl < (int)n_valid - c ? pp + (uint32_t)c * a.G : pb;
 #pragma unroll
-            for (int g = 0; g < GH; ++g) pq[it][g] = src[g];
+            for (int g = 0; g < GH; ++g) pq[it][g] = __builtin_amdgcn_exp2f(src[g] - m[g]);
           }
         }
       };
       auto sink = [&](uint32_t, uint32_t, uint4 w, uint32_t, uint32_t it) {
         float p[GH];
 #pragma unroll
-        for (int g = 0; g < GH; ++g) p[g] = pq[it][g];
+        for (int g = 0; g < GH; ++g) {
+          p[g] = pq[it][g];
+          z[g] += p[g];
+        }
         const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -269,6 +271,12 @@ __global__ __launch_bounds__(kPvWaves * 64) void attn_pv_kernel(AttnArgs a, uint
           v += __shfl_xor(v, 32);
           acc[g][i] = v;
         }
+      // the lanes of a row summed the same tokens' weights: add the rows
+#pragma unroll
+      for (int g = 0; g < GH; ++g) {
+        z[g] += __shfl_xor(z[g], 16);
+        z[g] += __shfl_xor(z[g], 32);
+      }
       if (lane < 16u) {
 #pragma unroll
         for (int g = 0; g < GH; ++g) {
@@ -277,10 +285,18 @@ __global__ __launch_bounds__(kPvWaves * 64) void attn_pv_kernel(AttnArgs a, uint
           *reinterpret_cast<float4*>(dst + 4) = make_float4(acc[g][4], acc[g][5], acc[g][6], acc[g][7]);
         }
       }
+      if (lane == 0u) {
 #pragma unroll
-      for (int g = 0; g < GH; ++g)
+        for (int g = 0; g < GH; ++g)
+          *reinterpret_cast<float2*>(a.mz + (((uint64_t)pair * a.n_units + u) * a.G + g_off + g) * 2u) =
+              make_float2(m[g], z[g]);
+      }
+#pragma unroll
+      for (int g = 0; g < GH; ++g) {
+        z[g] = 0.0f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[g][i] = 0.0f;
+      }
       unit = nu;
       half = 0;
     } else {
@@ -289,19 +305,31 @@ __global__ __launch_bounds__(kPvWaves * 64) void attn_pv_kernel(AttnArgs a, uint
   }
 }
 
-// out[pair * G + g][d] = sum over units, in unit order.
+// out[pair * G + g][d]: with M the largest of the units' maxima m_u, the
+// units' partial sums and weight sums z_u, each times 2^(m_u - M), added in
+// unit order; then the partial-sum total over the z total.
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   const uint64_t idx = (uint64_t)blockIdx.x * 256u + threadIdx.x;
   const uint64_t rows = (uint64_t)a.pairs * a.G;
   if (idx >= rows * 128u) return;
   const uint32_t d = (uint32_t)(idx & 127u);
-  const uint64_t row = idx >> 7;
+  // a wave's 64 threads share a row: its (m, z) loads are scalar
+  const uint64_t row = __builtin_amdgcn_readfirstlane((uint32_t)(idx >> 7));
   const uint32_t pair = (uint32_t)(row / a.G), g = (uint32_t)(row % a.G);
   const float* src = a.part + ((uint64_t)pair * a.n_units * a.G + g) * 128u + d;
-  float s = 0.0f;
+  const float2* mz = reinterpret_cast<const float2*>(a.mz) + (uint64_t)pair * a.n_units * a.G + g;
+  float M = -__builtin_inff();
 #pragma unroll 8
-  for (uint32_t u = 0; u < a.n_units; ++u) s += src[(uint64_t)u * a.G * 128u];
-  a.out[row * 128u + d] = s;
+  for (uint32_t u = 0; u < a.n_units; ++u) M = fmaxf(M, mz[(uint64_t)u * a.G].x);
+  float s = 0.0f, zt = 0.0f;
+#pragma unroll 8
+  for (uint32_t u = 0; u < a.n_units; ++u) {
+    const float2 e = mz[(uint64_t)u * a.G];
+    const float w = __builtin_amdgcn_exp2f(e.x - M);
+    s += src[(uint64_t)u * a.G * 128u] * w;
+    zt += e.y * w;
+  }
+  a.out[row * 128u + d] = s / zt;
 }
 
 }  // namespace ecco
@@ -312,15 +340,23 @@ namespace {
 constexpr uint64_t kWsAlign = 256;
 uint64_t round_up(uint64_t v) { return (v + kWsAlign - 1) / kWsAlign * kWsAlign; }
 uint64_t probs_bytes(uint64_t pairs, uint64_t g, uint64_t s) { return round_up(pairs * s * g * 4u); }
+uint64_t bmax_bytes(uint64_t pairs, uint64_t g, uint64_t s) { return round_up(pairs * ((s + 63) / 64) * g * 4u); }
+uint64_t mz_bytes(uint64_t pairs, uint64_t g, uint64_t s) {
+  return round_up(pairs * ((s + kUnitTokens - 1) / kUnitTokens) * g * 8u);
+}
 uint64_t part_bytes(uint64_t pairs, uint64_t g, uint64_t s) {
   return round_up(pairs * ((s + kUnitTokens - 1) / kUnitTokens) * g * 128u * 4u);
+}
+// workspace: scores, partial sums, batch maxima, unit (m, z), each 256-aligned
+uint64_t workspace_bytes(uint64_t pairs, uint64_t g, uint64_t s) {
+  return probs_bytes(pairs, g, s) + part_bytes(pairs, g, s) + bmax_bytes(pairs, g, s) + mz_bytes(pairs, g, s);
 }
 }  // namespace
 
 extern "C" size_t ecco_attention_workspace_size(uint64_t batch, uint64_t kv_heads, uint64_t group, uint64_t seq) {
   if (batch >= (1ull << 20) || kv_heads >= (1ull << 20) || seq >= (1ull << 24) || group > 8) return 0;
   const uint64_t pairs = batch * kv_heads;
-  return (size_t)(probs_bytes(pairs, group, seq) + part_bytes(pairs, group, seq));
+  return (size_t)workspace_bytes(pairs, group, seq);
 }
 
 namespace {
@@ -350,8 +386,9 @@ int check_attention_args(const void* k_blocks, const void* k_tables, float k_sca
   return ECCO_OK;
 }
 
-// Enqueues the four attention kernels with `workspace` (device memory of
-// ecco_attention_workspace_size bytes) for the scores and partial sums.
+// Enqueues the attention kernels (scores, p . V, combine) with `workspace`
+// (device memory of ecco_attention_workspace_size bytes) for the scores,
+// partial sums and maxima.
 int launch_attention(const void* k_blocks, const void* k_tables, float k_scale, const void* v_blocks,
                      const void* v_tables, float v_scale, const uint16_t* q, uint64_t pairs, uint64_t group,
                      uint64_t seq, uint64_t kv_stride, float scale, void* workspace, float* out, void* stream) {
@@ -364,7 +401,11 @@ int launch_attention(const void* k_blocks, const void* k_tables, float k_scale, 
   a.vt = static_cast<const Tables*>(v_tables);
   a.q = q;
   a.probs = static_cast<float*>(workspace);
-  a.part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + probs_bytes(pairs, group, seq));
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  a.part = reinterpret_cast<float*>(ws + probs_bytes(pairs, group, seq));
+  a.bmax = reinterpret_cast<float*>(ws + probs_bytes(pairs, group, seq) + part_bytes(pairs, group, seq));
+  a.mz = reinterpret_cast<float*>(ws + probs_bytes(pairs, group, seq) + part_bytes(pairs, group, seq) +
+                                  bmax_bytes(pairs, group, seq));
   a.out = out;
   a.pairs = (uint32_t)pairs;
   a.S = (uint32_t)seq;
@@ -374,23 +415,17 @@ int launch_attention(const void* k_blocks, const void* k_tables, float k_scale, 
   a.G = (uint32_t)group;
   a.kts = k_scale;
   a.vts = v_scale;
-  a.scale = scale;
+  a.scale = (float)((double)scale * 1.4426950408889634);   // scores in base-2 units: exp(x) = 2^(x log2 e)
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   const uint32_t kgrid = std::max<uint32_t>(1, std::min<uint32_t>(a.pairs * a.n_kb, (uint32_t)cus));
   switch (group) {
-    case 1: hipLaunchKernelGGL(attn_scores_kernel<1>, dim3(kgrid), dim3(kScoreWaves * 64), 0, s, a); break;
-    case 2: hipLaunchKernelGGL(attn_scores_kernel<2>, dim3(kgrid), dim3(kScoreWaves * 64), 0, s, a); break;
-    case 4: hipLaunchKernelGGL(attn_scores_kernel<4>, dim3(kgrid), dim3(kScoreWaves * 64), 0, s, a); break;
-    default: hipLaunchKernelGGL(attn_scores_kernel<8>, dim3(kgrid), dim3(kScoreWaves * 64), 0, s, a); break;
+    case 1: hipLaunchKernelGGL(attn_scores_kernel<1>, dim3(kgrid), dim3(score_waves<1>() * 64), 0, s, a); break;
+    case 2: hipLaunchKernelGGL(attn_scores_kernel<2>, dim3(kgrid), dim3(score_waves<2>() * 64), 0, s, a); break;
+    case 4: hipLaunchKernelGGL(attn_scores_kernel<4>, dim3(kgrid), dim3(score_waves<4>() * 64), 0, s, a); break;
+    default: hipLaunchKernelGGL(attn_scores_kernel<8>, dim3(kgrid), dim3(score_waves<8>() * 64), 0, s, a); break;
   }
   const uint32_t rows = a.pairs * a.G;
-  switch (group) {
-    case 1: hipLaunchKernelGGL(attn_softmax_kernel<1>, dim3(a.pairs), dim3(kSmThreads), 0, s, a); break;
-    case 2: hipLaunchKernelGGL(attn_softmax_kernel<2>, dim3(a.pairs), dim3(kSmThreads), 0, s, a); break;
-    case 4: hipLaunchKernelGGL(attn_softmax_kernel<4>, dim3(a.pairs), dim3(kSmThreads), 0, s, a); break;
-    default: hipLaunchKernelGGL(attn_softmax_kernel<8>, dim3(a.pairs), dim3(kSmThreads), 0, s, a); break;
-  }
   const uint32_t vgrid = std::max<uint32_t>(1, std::min<uint32_t>(a.pairs * a.n_units, (uint32_t)cus));
   switch (group) {
     case 1: hipLaunchKernelGGL(attn_pv_kernel<1>, dim3(vgrid), dim3(kPvWaves * 64), 0, s, a, 0u); break;
@@ -462,7 +497,7 @@ extern "C" int ecco_attention_decode_noalloc(const void* k_blocks, const void* k
   int rc = check_attention_args(k_blocks, k_tables, k_scale, v_blocks, v_tables, v_scale, q, batch, kv_heads, group,
                                 seq, kv_stride, scale, out, &pairs);
   if (rc) return rc;
-  if (probs_bytes(pairs, group, seq) + part_bytes(pairs, group, seq) > kScratchBytes) return ECCO_ESIZE;
+  if (workspace_bytes(pairs, group, seq) > kScratchBytes) return ECCO_ESIZE;
   int cus = 0;
   rc = check_gfx950(&cus);
   if (rc) return rc;

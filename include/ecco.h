@@ -395,8 +395,9 @@ int ecco_decode_gemv_many(const ecco_gemv_job_t* jobs_host, uint32_t n_jobs, int
  * S_max >= S); q_dev: [B][H_kv * G][128] FP16; out_dev: [B][H_kv * G][128]
  * FP32, overwritten.  workspace_dev (256-byte aligned) holds
  * ecco_attention_workspace_size(B, H_kv, G, S) bytes of caller memory that
- * the call uses for scores and partial sums; its contents are unspecified
- * afterwards.  ECCO_ESIZE unless B, H_kv, S >= 1, G is 1, 2, 4 or 8,
+ * the call uses for scores, per-unit partial sums and the maxima and weight
+ * sums of the softmax (taken per 64- and 128-token block, combined at the
+ * end); its contents are unspecified afterwards.  ECCO_ESIZE unless B, H_kv, S >= 1, G is 1, 2, 4 or 8,
  * B, H_kv and B * H_kv are below 2^20, S is below 2^24, S <= kv_stride_tokens
  * < 2^32 and B * H_kv * kv_stride_tokens < 2^32.  The workspace size is 0 for
  * B, H_kv or G beyond those limits. */
@@ -409,7 +410,7 @@ int ecco_attention_decode(const void* k_blocks_dev, const void* k_tables_dev, fl
 
 /* ecco_attention_decode without the workspace argument, for callers that
  * cannot allocate device memory: code under HIP graph capture, tight serving
- * loops, harnesses that forbid hipMalloc.  The scores and partial sums go to
+ * loops, harnesses that forbid hipMalloc.  The workspace contents go to
  * a static device array of ECCO_ATTENTION_NOALLOC_MAX_WORKSPACE bytes that
  * the library holds on each GPU it runs on until the process ends; the call
  * allocates and frees nothing.  Everything else -- arguments, layout,

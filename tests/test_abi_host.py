@@ -376,9 +376,13 @@ def test_attention_checks_arguments_before_touching_the_device():
     fits[7:12] = [16, 8, 4, 8192, 8192]
     assert ecco.ecco_attention_workspace_size(16, 8, 4, 8192) <= ecco.ATTENTION_NOALLOC_MAX_WORKSPACE
     assert L.ecco_attention_decode_noalloc(*fits) not in (0, -1, -2, -3)   # a device error here: no GPU
-    # workspace: scores [B*H][S][G] floats and partial sums [B*H][ceil(S/128)][G][128] floats, 256-aligned
+    # workspace: scores [B*H][S][G] floats, partial sums [B*H][ceil(S/128)][G][128] floats, batch maxima
+    # [B*H][ceil(S/64)][G] floats and unit (max, weight sum) pairs [B*H][ceil(S/128)][G][2] floats, each
+    # 256-aligned
     def up(v):
         return (v + 255) // 256 * 256
     for (b, h, g, s) in [(2, 3, 4, 100), (16, 8, 4, 8192), (1, 1, 1, 1), (1, 2, 8, 129)]:
-        want = up(b * h * s * g * 4) + up(b * h * ((s + 127) // 128) * g * 128 * 4)
+        units, batches = (s + 127) // 128, (s + 63) // 64
+        want = (up(b * h * s * g * 4) + up(b * h * units * g * 128 * 4) + up(b * h * batches * g * 4)
+                + up(b * h * units * g * 2 * 4))
         assert ecco.ecco_attention_workspace_size(b, h, g, s) == want
