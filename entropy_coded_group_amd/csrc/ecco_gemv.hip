@@ -62,6 +62,27 @@ struct GemvArgs {
   uint32_t n_jobs, batch;
 };
 
+// acc[b2] += the 8 weights w . x[b2][the same 8 columns] for b2 < BM, x[b2]
+// at xp + b2 * in_f.  The BM loads sit together under one run-time
+// condition (always true: batch >= 1), so they issue together and their
+// latency is paid once, and the compiler does not move them (or their
+// addresses) ahead of the write-out pass they belong to; a column past the
+// batch reads the last row, and its sums are never stored.  Under a
+// condition per column, each load was waited for on its own, and each wait
+// also covered the next batch's block prefetch.
+template <int BM>
+__device__ __forceinline__ void gemv_dot_x(float (&acc)[BM], uint4 w, const uint16_t* xp, uint32_t in_f,
+                                           uint32_t batch) {
+  if (batch != 0u) {
+    uint4 xv[BM];
+#pragma unroll
+    for (int b2 = 0; b2 < BM; ++b2)
+      xv[b2] = *reinterpret_cast<const uint4*>(xp + (uint64_t)min((uint32_t)b2, batch - 1u) * in_f);
+#pragma unroll
+    for (int b2 = 0; b2 < BM; ++b2) acc[b2] = dot8(w, xv[b2], acc[b2]);
+  }
+}
+
 // A wavefront owns one output row at a time and decodes its blocks 64 at a
 // time (the last batch of a row partly filled).  Rows go round the job's
 // workgroups first, then their waves.
@@ -92,13 +113,7 @@ __device__ __forceinline__ void gemv_rows_per_wave(DecodeSmem<kGemvWaves>& sm, c
     const BatchRegs nxt = nrow < a.out_f ? fetch(nrow, nc0) : fetch(row, c0);
     auto sink = [&](uint32_t b, uint32_t j0, uint4 w, uint32_t, uint32_t) {
       const uint16_t* xp = a.x + (uint64_t)(c0 + b) * 128u + j0;
-#pragma unroll
-      for (int b2 = 0; b2 < BM; ++b2) {
-        if ((uint32_t)b2 < batch) {
-          const uint4 xv = *reinterpret_cast<const uint4*>(xp + (uint64_t)b2 * a.in_f);
-          part[b2] = dot8(w, xv, part[b2]);
-        }
-      }
+      gemv_dot_x<BM>(part, w, xp, a.in_f, batch);
     };
     const uint32_t n_valid = min(64u, a.gpr - c0);
     if (n_valid == 64u)
@@ -261,14 +276,7 @@ __device__ __forceinline__ void gemv_row_groups(DecodeSmem<kGemvWaves>& sm, cons
 #pragma unroll
       for (int b = 0; b < BM; ++b) acc[b] = 0.0f;
       auto sink = [&](uint32_t b, uint32_t, uint4 w, uint32_t, uint32_t) {
-        const uint16_t* xp = xc + (uint64_t)(b >> 2) * 128u;
-#pragma unroll
-        for (int b2 = 0; b2 < BM; ++b2) {
-          if ((uint32_t)b2 < batch) {
-            const uint4 xv = *reinterpret_cast<const uint4*>(xp + (uint64_t)b2 * a.in_f);
-            acc[b2] = dot8(w, xv, acc[b2]);
-          }
-        }
+        gemv_dot_x<BM>(acc, w, xc + (uint64_t)(b >> 2) * 128u, a.in_f, batch);
       };
       decode_batch<true>(sm, wave, lane, 64u, a.t, cur, sink);
 #pragma unroll
