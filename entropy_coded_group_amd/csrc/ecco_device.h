@@ -424,9 +424,13 @@ __device__ __forceinline__ void decode_batch(DecodeSmem<NW>& sm, uint32_t wave, 
                                         __builtin_amdgcn_perm(e1, e0, 0x0c0c0400u), 0x05040100u);
     asm volatile("" : "+v"(ev));                 // pack now: keeps one register per 4 symbols
     if (base + r4 > lim) {
-      // a codeword of this chunk ends past bit 512: the stream is clipped here
-      const uint32_t m = (base + r1 > 512u ? 0x000000ffu : 0u) | (base + r2 > 512u ? 0x0000ff00u : 0u) |
-                         (base + r3 > 512u ? 0x00ff0000u : 0u) | 0xff000000u;
+      // a codeword of this chunk ends past bit 512: the stream is clipped
+      // here.  The ends rise, so the codewords that fit are a prefix of f
+      // (8 f counted by inline constants: the byte masks, as literals, took
+      // four registers of the whole kernel); the bytes from f on become 16.
+      const uint32_t f8 = (base + r1 <= 512u ? 8u : 0u) + (base + r2 <= 512u ? 8u : 0u) +
+                          (base + r3 <= 512u ? 8u : 0u);
+      const uint32_t m = 0xffffffffu << f8;
       ev = (ev & ~m) | (0x10101010u & m);
       lim = 0xffffffffu;
       lutb = kDeadLut;
