@@ -19,11 +19,12 @@ reused FP16 buffer of a layer's size (a layer's blocks were written 31
 layers -- 3.4 GB of other traffic -- earlier, so they come from HBM, not the
 256 MB last-level cache); then per layer the fused decode+GEMV at batch 1 as
 a decode step issues it: ecco_decode_gemv_many over q, k, v (same x), then
-o, then gate and up (same x), then down.  Each launch is bracketed by HIP
-events on the stream it runs on.  The reported value is decode throughput
--- (64 B compressed in + 256 B FP16 out) per group over the summed decode
-kernel time of the timed steps; encode (256 B in + 64 B out per group), amax
-and the fused GEMV are reported beside it.
+o, then gate and up (same x), then down.  Each phase of a step (its 32 or
+128 launches, back to back) is bracketed by one pair of HIP events on the
+stream it runs on.  The reported value is decode throughput -- (64 B
+compressed in + 256 B FP16 out) per group over the summed decode phase time
+of the timed steps; encode (256 B in + 64 B out per group), amax and the
+fused GEMV are reported beside it.
 
 Other workloads (run separately, same JSON line shape):
   layer  one layer of the set above, drawn on the CPU: the same step on one
@@ -344,16 +345,31 @@ def bench_model(args, torch, ecco, W):
     setup = time.perf_counter() - t_setup
     timer = Timer(torch, stream)
 
-    def step():
+    # each phase's 32 launches run back to back between one pair of events
+    # (an event pair around every launch added its own few microseconds to
+    # each launch); a launch's time is the phase's over 32
+    def amax_phase():
         for jobs in amax_jobs:
-            timer.run("amax", lambda: ecco.ecco_amax_many(jobs))
+            ecco.ecco_amax_many(jobs)
+
+    def encode_phase():
         for jobs in encode_jobs:
-            timer.run("encode", lambda: ecco.ecco_encode_many(jobs))
+            ecco.ecco_encode_many(jobs)
+
+    def decode_phase():
         for jobs in decode_jobs:
-            timer.run("decode", lambda: ecco.ecco_decode_many(jobs))
+            ecco.ecco_decode_many(jobs)
+
+    def gemv_phase():
         for layer_jobs in gemv_jobs:
             for jobs in layer_jobs:
-                timer.run("gemv", lambda: ecco.ecco_decode_gemv_many(jobs, 1))
+                ecco.ecco_decode_gemv_many(jobs, 1)
+
+    def step():
+        timer.run("amax", amax_phase)
+        timer.run("encode", encode_phase)
+        timer.run("decode", decode_phase)
+        timer.run("gemv", gemv_phase)
 
     for _ in range(args.warmup):
         step()
@@ -367,14 +383,15 @@ def bench_model(args, torch, ecco, W):
     ph = timer.collect()
     groups = sum(m["groups"] for mats in layers for m in mats.values())
     dec_t, enc_t = sum(ph["decode"]), sum(ph["encode"])
-    n_dec = len(ph["decode"])
+    n_dec = len(ph["decode"]) * W.N_LAYERS
     res = dict(
         wall=wall, groups=groups, setup_s=setup,
         decode_GBps=groups * args.steps * BYTES_PER_GROUP / dec_t / 1e9,
         encode_GBps=groups * args.steps * BYTES_PER_GROUP / enc_t / 1e9,
         amax_GBps=groups * args.steps * 256 / sum(ph["amax"]) / 1e9,
         decode_launch_us=dec_t / n_dec * 1e6, decode_launches=n_dec,
-        decode_launch_us_min=min(ph["decode"]) * 1e6, decode_launch_us_max=max(ph["decode"]) * 1e6,
+        decode_launch_us_min=min(ph["decode"]) / W.N_LAYERS * 1e6,
+        decode_launch_us_max=max(ph["decode"]) / W.N_LAYERS * 1e6,
         decode_bytes_per_launch=groups // W.N_LAYERS * BYTES_PER_GROUP,
         encode_us_per_layer=enc_t / args.steps / W.N_LAYERS * 1e6,
         decode_us_per_layer=dec_t / args.steps / W.N_LAYERS * 1e6,
@@ -549,7 +566,8 @@ def model_line(args, res):
         "tables": "ecco_train_patterns on seeded 2^20-value samples, one set per matrix type"})
     line.update({
         "amax_GBps": round(res["amax_GBps"], 1),
-        "decode_launch_us_min_max": [round(res["decode_launch_us_min"], 2), round(res["decode_launch_us_max"], 2)],
+        "decode_launch_us_min_max_over_steps": [round(res["decode_launch_us_min"], 2),
+                                                round(res["decode_launch_us_max"], 2)],
         "step_device_ms": round(res["step_device_ms"], 3),
         "setup_s": round(res["setup_s"], 1),
     })
