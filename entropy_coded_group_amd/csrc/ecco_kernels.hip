@@ -154,7 +154,7 @@ struct EncodeArgs {
   uint32_t n_jobs;
 };
 
-constexpr int kEncWaves = 4;
+constexpr int kEncWaves = 8;        // waves per workgroup (two workgroups resident per CU)
 constexpr uint32_t kOutlierSortRounds = 3;   // more outlier rounds than this: sort each lane's keys first
 
 // Sorts 8 keys into descending order (an optimal 19-comparator network).
@@ -738,9 +738,10 @@ int make_encode_job(const uint16_t* x, uint64_t n_rows, uint64_t gpr, uint64_t x
   return ECCO_OK;
 }
 
-// Up to 16 workgroups of kEncWaves waves per CU (four are resident at a time;
-// the later ones even out the tail), and at least two units per wave, so a
-// small launch does not stage the tables in LDS more often than it needs: each
+// Up to 8 workgroups of kEncWaves = 8 waves per CU (two are resident at a
+// time; the later ones even out the tail), and at least two units per wave,
+// so a small launch does not stage the tables in LDS more often than it
+// needs (eight waves share one staging): each
 // job gets its share of the grid in proportion to its units (at least one
 // workgroup), and the few workgroups the rounding leaves go one by one to the
 // job whose workgroups carry the most units.
@@ -750,7 +751,7 @@ void assign_encode_workgroups(EncodeArgs& args, uint32_t cus) {
     want[j] = (args.job[j].n_units + 2 * kEncWaves - 1) / (2 * kEncWaves);
     total += want[j];
   }
-  const uint64_t grid = std::max<uint64_t>(args.n_jobs, std::min<uint64_t>(total, (uint64_t)cus * 16));
+  const uint64_t grid = std::max<uint64_t>(args.n_jobs, std::min<uint64_t>(total, (uint64_t)cus * 8));
   uint64_t used = 0;
   for (uint32_t j = 0; j < args.n_jobs; ++j) {
     const uint64_t share = (uint64_t)((unsigned __int128)grid * want[j] / total);
