@@ -36,7 +36,7 @@ constexpr uint32_t kUnitTokens = 128;   // tokens per p . V work unit (two batch
 // eight scores per token need more registers than that leaves, so two
 template <int G>
 constexpr int score_waves() { return G > 4 ? 8 : 12; }
-constexpr int kPvWaves = 8;             // waves per workgroup of the p . V kernel
+constexpr int kPvWaves = 12;            // waves per workgroup of the p . V kernel
 
 // DPP row rotations (GFX9 encoding)
 constexpr int kRowRor1 = 0x121, kRowRor2 = 0x122, kRowRor4 = 0x124, kRowRor8 = 0x128;

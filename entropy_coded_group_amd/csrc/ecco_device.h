@@ -513,12 +513,15 @@ __device__ __forceinline__ void decode_batch(DecodeSmem<NW>& sm, uint32_t wave, 
     uint4 o[Geo::kPassIters];
 #pragma unroll
     for (int it = 0; it < Geo::kPassIters; ++it) {
-      const uint32_t bl = kPassBlocks * k + it * BPI + lane / LPB;
-      const uint8_t* tb = reinterpret_cast<const uint8_t*>(blk + bl * kBlkStride);
+      // the block's value table: this lane's row base plus a constant
+      // (k, it) offset, which goes last so that the look-up instruction's
+      // offset field takes it (a per-step address per lane cost registers)
+      const uint8_t* tb = reinterpret_cast<const uint8_t*>(blk + (lane / LPB) * kBlkStride);
+      const uint32_t off = (kPassBlocks * (uint32_t)k + (uint32_t)(it * BPI)) * kBlkStride * 4u;
       // each staged byte is already the entry's byte offset (< 64)
       typedef _Float16 h2 __attribute__((ext_vector_type(2)));
       auto v = [&](uint32_t s, int b) -> _Float16 {
-        return *reinterpret_cast<const _Float16*>(tb + ((s >> (8 * b)) & 0xffu));
+        return *reinterpret_cast<const _Float16*>(tb + ((s >> (8 * b)) & 0xffu) + off);
       };
       auto pr = [&](uint32_t s, int b) -> uint32_t {
         h2 q;
