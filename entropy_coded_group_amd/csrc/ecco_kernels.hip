@@ -327,12 +327,18 @@ __global__ __launch_bounds__(kEncWaves * 64, 4) void encode_kernel(EncodeArgs ar
     //    order like it) and the least p among the lanes that reach it.
     float bf = __builtin_inff();
     uint32_t bp = tl;
+    // the lane's end-centroid pairs: one address from an opaque copy of tl,
+    // each pattern's offset a constant the load's offset field takes (kept
+    // addresses per pattern cost registers)
+    uint32_t tl_op = tl;
+    asm volatile("" : "+v"(tl_op));
+    const float* cb = sm.c0c14 + 2u * tl_op;
 #pragma unroll
     for (int k = 0; k < 64 / LPG; ++k) {
       if (k >= n_search_lane) break;    // later patterns repeat earlier ones' end centroids
       const uint32_t p = tl + LPG * k;
-      const float d1 = mn - sm.c0c14[2 * p] * aa;
-      const float d2 = mx - sm.c0c14[2 * p + 1] * aa;
+      const float d1 = mn - cb[2 * LPG * k] * aa;
+      const float d2 = mx - cb[2 * LPG * k + 1] * aa;
       const float f = d1 * d1 + d2 * d2;
       if (f < bf) {
         bf = f;
@@ -415,16 +421,23 @@ __global__ __launch_bounds__(kEncWaves * 64, 4) void encode_kernel(EncodeArgs ar
     }
     const bool clipped = 16u + L > 512u;
     const uint32_t n = clipped ? 0u : min(16u, (496u - L) / RB);
-    // 7. outliers: n largest |x| (j != i*), lower j first on ties.  Keys are
-    //    unique and the scale element holds the group's largest (km), so the
-    //    outliers are the next n keys: after removing km, each round takes
-    //    the group's largest remaining key (lane rr % LPG keeps round rr's in
-    //    slot rr / LPG) and removes it, until no group of the wave needs
-    //    another round.  For a few rounds the lane's keys are searched and
-    //    cleared in place; for more, the lane first sorts each 8 of its keys
-    //    (descending, 19 compare-exchanges) so that a round only compares the
-    //    lists' heads and the owner of the largest shifts its list.  Here the
-    //    keys carry their lane's index bits, so they are unique in the group.
+    // 7. outliers: n largest |x| (j != i*), lower j first on ties.  With the
+    //    lane's index bits OR-ed in, keys are unique in the group and order
+    //    like that rule, and the scale element holds the largest (km); so the
+    //    outliers are the n keys that follow km, and round rr takes the
+    //    group's largest key below the previous round's (km for the first):
+    //    each lane offers its own largest key below it, a segment max picks
+    //    the round's key, and lane rr % LPG keeps it in slot rr / LPG.  The
+    //    rounds are unrolled, so that each updates one slot and compares the
+    //    lane with a constant.  For at most kOutlierSortRounds rounds a lane
+    //    finds its offer by one pass over its keys (the largest key below m
+    //    is m - 1 - min(m - 1 - key), unsigned: keys not below m wrap to
+    //    values above m - 1; m, one of the group's 17 largest keys, which
+    //    are unique, is never 0).  For more, the lane first sorts its two 8-key
+    //    halves (descending, 19 compare-exchanges each); a round then
+    //    compares the two heads, and the half that held the previous round's
+    //    key shifts up by one (km's half first).  Rounds go on until no group
+    //    of the wave needs another.
     uint32_t mykey[NSLOT];
 #pragma unroll
     for (int sl = 0; sl < NSLOT; ++sl) mykey[sl] = 0;
@@ -433,10 +446,12 @@ __global__ __launch_bounds__(kEncWaves * 64, 4) void encode_kernel(EncodeArgs ar
 #pragma unroll
       for (int c = 0; c < NL; ++c) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) k8[c][i] = key[8 * c + i] == km_own ? 0u : key[8 * c + i] | lane_bits;
+        for (int i = 0; i < 8; ++i) k8[c][i] = key[8 * c + i] | lane_bits;
         sort8_desc(k8[c]);
       }
-      auto pop = [&](uint32_t m) {
+      uint32_t m = km;
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
 #pragma unroll
         for (int c = 0; c < NL; ++c) {
           const bool own = k8[c][0] == m;
@@ -444,38 +459,35 @@ __global__ __launch_bounds__(kEncWaves * 64, 4) void encode_kernel(EncodeArgs ar
           for (int i = 0; i < 7; ++i) k8[c][i] = own ? k8[c][i + 1] : k8[c][i];
           k8[c][7] = own ? 0u : k8[c][7];
         }
-      };
-      for (uint32_t rr = 0;; ++rr) {
         uint32_t head = k8[0][0];
 #pragma unroll
         for (int c = 1; c < NL; ++c) head = max(head, k8[c][0]);
-        const uint32_t m = seg_max_u32<LPG>(head);
-#pragma unroll
-        for (int sl = 0; sl < NSLOT; ++sl) mykey[sl] = rr == tl + LPG * sl ? m : mykey[sl];
-        if (!__any(rr + 1u < n)) break;
-        pop(m);
+        m = seg_max_u32<LPG>(head);
+        mykey[rr / LPG] = tl == (uint32_t)(rr % LPG) ? m : mykey[rr / LPG];
+        if (!__any((uint32_t)rr + 1u < n)) break;
       }
     } else if (__any(n > 0u)) {
 #pragma unroll
-      for (int i = 0; i < NV; ++i) key[i] = key[i] == km_own ? 0u : key[i] | lane_bits;
-      for (uint32_t rr = 0;; ++rr) {
-        uint32_t m = key[0];
+      for (int i = 0; i < NV; ++i) key[i] |= lane_bits;
+      uint32_t m = km;
 #pragma unroll
-        for (int i = 1; i < NV; ++i) m = max(m, key[i]);
-        m = seg_max_u32<LPG>(m);
+      for (int rr = 0; rr < (int)kOutlierSortRounds; ++rr) {
+        const uint32_t m1 = m - 1u;
+        uint32_t d = m1 - key[0];
 #pragma unroll
-        for (int sl = 0; sl < NSLOT; ++sl) mykey[sl] = rr == tl + LPG * sl ? m : mykey[sl];
-        if (!__any(rr + 1u < n)) break;
-#pragma unroll
-        for (int i = 0; i < NV; ++i) key[i] = key[i] == m ? 0u : key[i];
+        for (int i = 1; i < NV; ++i) d = min(d, m1 - key[i]);
+        m = seg_max_u32<LPG>(d <= m1 ? m1 - d : 0u);
+        mykey[rr / LPG] = tl == (uint32_t)(rr % LPG) ? m : mykey[rr / LPG];
+        if (!__any((uint32_t)rr + 1u < n)) break;
       }
     }
 #pragma unroll
     for (int sl = 0; sl < NSLOT; ++sl) {
       const uint32_t r = tl + LPG * sl;
       if (r < n) {
-        const uint32_t j = 127u - ((mykey[sl] >> 1) & 127u);
-        const uint32_t myrec = j | (fp8_encode(key_value(mykey[sl]) * inv_t) << Geo::kPosBits);
+        const uint32_t mk = mykey[sl];
+        const uint32_t j = 127u - ((mk >> 1) & 127u);
+        const uint32_t myrec = j | (fp8_encode(key_value(mk) * inv_t) << Geo::kPosBits);
         const uint32_t rp = 512u - RB * (r + 1u);
         const uint32_t w = rp >> 5, sh = rp & 31u;
         atomicOr(&out[w], myrec << sh);
