@@ -161,20 +161,40 @@ __device__ __forceinline__ uint32_t seg_add_u32(uint32_t v) {
   if constexpr (LPG == 16) v += dpp_u32<kRowMirror>(v);
   return v;
 }
+// Float min / max over a segment of non-NaN values.  Written with the DPP
+// form of v_min_f32 / v_max_f32 directly: through fminf the compiler moves
+// the neighbour's value and quiets it (a possible signalling NaN) before the
+// min, three instructions a step instead of one.  Each step waits the two
+// cycles a DPP read of a just-written register needs.
+#define ECCO_DPP_STEP(op, ctrl) "s_nop 1\n\t" op " %0, %0, %0 " ctrl " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+#define ECCO_DPP_QX1 "quad_perm:[1,0,3,2]"
+#define ECCO_DPP_QX2 "quad_perm:[2,3,0,1]"
+#define ECCO_DPP_RHM "row_half_mirror"
+#define ECCO_DPP_RM "row_mirror"
 template <int LPG>
 __device__ __forceinline__ float seg_min_f32(float v) {
-  v = fminf(v, dpp_f32<kQuadXor1>(v));
-  v = fminf(v, dpp_f32<kQuadXor2>(v));
-  if constexpr (LPG >= 8) v = fminf(v, dpp_f32<kRowHalfMirror>(v));
-  if constexpr (LPG == 16) v = fminf(v, dpp_f32<kRowMirror>(v));
+  static_assert(LPG == 4 || LPG == 8 || LPG == 16, "segment of 4, 8 or 16 lanes");
+  if constexpr (LPG == 4)
+    asm(ECCO_DPP_STEP("v_min_f32_dpp", ECCO_DPP_QX1) ECCO_DPP_STEP("v_min_f32_dpp", ECCO_DPP_QX2) : "+v"(v));
+  else if constexpr (LPG == 8)
+    asm(ECCO_DPP_STEP("v_min_f32_dpp", ECCO_DPP_QX1) ECCO_DPP_STEP("v_min_f32_dpp", ECCO_DPP_QX2)
+        ECCO_DPP_STEP("v_min_f32_dpp", ECCO_DPP_RHM) : "+v"(v));
+  else
+    asm(ECCO_DPP_STEP("v_min_f32_dpp", ECCO_DPP_QX1) ECCO_DPP_STEP("v_min_f32_dpp", ECCO_DPP_QX2)
+        ECCO_DPP_STEP("v_min_f32_dpp", ECCO_DPP_RHM) ECCO_DPP_STEP("v_min_f32_dpp", ECCO_DPP_RM) : "+v"(v));
   return v;
 }
 template <int LPG>
 __device__ __forceinline__ float seg_max_f32(float v) {
-  v = fmaxf(v, dpp_f32<kQuadXor1>(v));
-  v = fmaxf(v, dpp_f32<kQuadXor2>(v));
-  if constexpr (LPG >= 8) v = fmaxf(v, dpp_f32<kRowHalfMirror>(v));
-  if constexpr (LPG == 16) v = fmaxf(v, dpp_f32<kRowMirror>(v));
+  static_assert(LPG == 4 || LPG == 8 || LPG == 16, "segment of 4, 8 or 16 lanes");
+  if constexpr (LPG == 4)
+    asm(ECCO_DPP_STEP("v_max_f32_dpp", ECCO_DPP_QX1) ECCO_DPP_STEP("v_max_f32_dpp", ECCO_DPP_QX2) : "+v"(v));
+  else if constexpr (LPG == 8)
+    asm(ECCO_DPP_STEP("v_max_f32_dpp", ECCO_DPP_QX1) ECCO_DPP_STEP("v_max_f32_dpp", ECCO_DPP_QX2)
+        ECCO_DPP_STEP("v_max_f32_dpp", ECCO_DPP_RHM) : "+v"(v));
+  else
+    asm(ECCO_DPP_STEP("v_max_f32_dpp", ECCO_DPP_QX1) ECCO_DPP_STEP("v_max_f32_dpp", ECCO_DPP_QX2)
+        ECCO_DPP_STEP("v_max_f32_dpp", ECCO_DPP_RHM) ECCO_DPP_STEP("v_max_f32_dpp", ECCO_DPP_RM) : "+v"(v));
   return v;
 }
 

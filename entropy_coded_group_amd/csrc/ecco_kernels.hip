@@ -174,7 +174,7 @@ __device__ __forceinline__ void sort8_desc(uint32_t (&k)[8]) {
 
 struct EncodeSmem {
   float mid[S * 16];
-  float c0c14[S * 2];
+  alignas(8) float c0c14[S * 2];      // pattern p's first and last centroid at 2p, 2p + 1
   uint32_t len4[16 + S * A];         // entry (p, s) at 16 + 16 p + s: index 16 p + u for tree leaf u = 16 + s
   uint32_t enc[16 + S * H * A];      // entry (p, h, s) at 16 + 16 (4 p + h) + s, likewise
   float thr[kEncWaves][16][16];      // threshold tree of each group of a wave
@@ -193,12 +193,13 @@ struct EncGeom {
   static constexpr int GPW = 64 / LPG;            // groups per wave
 };
 
-// One step down the quantiser's threshold tree: u' = 2 u + (x > t).  The
-// compare writes VCC and the add-with-carry reads it, two instructions where
-// a compare, a select and a shift-or would take three.
+// One step down the quantiser's threshold tree: u' = 2 u + !(x <= t), which
+// is x > t for every x but NaN, and 1 for NaN.  The compare writes VCC and
+// the add-with-carry reads it, two instructions where a compare, a select
+// and a shift-or would take three.
 __device__ __forceinline__ uint32_t tree_step(uint32_t u, float x, float t) {
   uint32_t r;
-  asm("v_cmp_gt_f32 vcc, %1, %2\n\tv_addc_co_u32 %0, vcc, %3, %3, vcc" : "=v"(r) : "v"(x), "v"(t), "v"(u) : "vcc");
+  asm("v_cmp_nle_f32 vcc, %1, %2\n\tv_addc_co_u32 %0, vcc, %3, %3, vcc" : "=v"(r) : "v"(x), "v"(t), "v"(u) : "vcc");
   return r;
 }
 
@@ -255,10 +256,17 @@ __global__ __launch_bounds__(kEncWaves * 64, 4) void encode_kernel(EncodeArgs ar
   struct Raw {
     uint4 v[NL];
   };
+  // whole rows back to back (input and blocks): a group's place is its
+  // index times its size, with no row / column split
+  const bool contig = a.x_stride == (uint64_t)a.gpr.d * GS && a.blk_stride == a.gpr.d;
   auto load_group = [&](uint32_t g) -> Raw {
     g = min(g, a.n_groups - 1u);
-    const uint32_t row = div_magic(g, a.gpr), col = g - row * a.gpr.d;
-    const uint16_t* src = a.x + (uint64_t)row * a.x_stride + (uint64_t)col * GS + NV * tl;
+    uint64_t off = (uint64_t)g * GS;
+    if (!contig) {
+      const uint32_t row = div_magic(g, a.gpr), col = g - row * a.gpr.d;
+      off = (uint64_t)row * a.x_stride + (uint64_t)col * GS;
+    }
+    const uint16_t* src = a.x + off + NV * tl;
     Raw r;
 #pragma unroll
     for (int c = 0; c < NL; ++c) r.v[c] = load_stream(src + 8 * c);
@@ -272,10 +280,10 @@ __global__ __launch_bounds__(kEncWaves * 64, 4) void encode_kernel(EncodeArgs ar
     const bool valid = gidx < a.n_groups;
     // the next unit's input is loaded before this one is worked on
     const Raw nraw = load_group((unit + ustride) * GPW + q);
-    uint32_t row = 0, col = 0;
-    if (valid) {
-      row = div_magic(gidx, a.gpr);
-      col = gidx - row * a.gpr.d;
+    uint64_t bidx = gidx;                  // the block's index in a.blocks
+    if (valid && !contig) {
+      const uint32_t row = div_magic(gidx, a.gpr), col = gidx - row * a.gpr.d;
+      bidx = (uint64_t)row * a.blk_stride + col;
     }
     uint32_t wd[NV / 2];                   // the lane's values as 8 words of two FP16 each
 #pragma unroll
@@ -306,18 +314,19 @@ __global__ __launch_bounds__(kEncWaves * 64, 4) void encode_kernel(EncodeArgs ar
     const uint32_t s8 = fp8_encode(xs * inv_t);
     const float S = fp8_decode<0>(s8) * t;
     const float aa = fabsf(S);
-    // 2. min / max of the other GS - 1 values: the scale element counts as
-    //    +inf for the min and -inf for the max.  xq, the quantiser's input,
-    //    also holds +inf there: it then walks to the tree's last leaf, which
-    //    no finite value reaches, and that leaf is symbol 15.
+    // 2. min / max of the other GS - 1 values.  xq, the values with a quiet
+    //    NaN in the scale element's place, serves both: fminf and fmaxf
+    //    return the other operand of a NaN.  It is also the quantiser's
+    //    input, whose steps test "not x <= t" (true for NaN, x > t for the
+    //    rest): the NaN walks to the tree's last leaf, which no finite value
+    //    reaches, and that leaf is symbol 15.
     float mn = __builtin_inff(), mx = -__builtin_inff();
     float xq[NV];
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      const bool s = key[i] == km_own;
-      xq[i] = s ? __builtin_inff() : xf[i];
+      xq[i] = key[i] == km_own ? __builtin_nanf("") : xf[i];
       mn = fminf(mn, xq[i]);
-      mx = fmaxf(mx, s ? -__builtin_inff() : xf[i]);
+      mx = fmaxf(mx, xq[i]);
     }
     mn = seg_min_f32<LPG>(mn);
     mx = seg_max_f32<LPG>(mx);
@@ -326,25 +335,30 @@ __global__ __launch_bounds__(kEncWaves * 64, 4) void encode_kernel(EncodeArgs ar
     //    segment then takes the least fitness (non-negative, so its bits
     //    order like it) and the least p among the lanes that reach it.
     float bf = __builtin_inff();
-    uint32_t bp = tl;
+    uint32_t bk = 0;                       // the lane's best pattern is tl + LPG * bk
     // the lane's end-centroid pairs: one address from an opaque copy of tl,
-    // each pattern's offset a constant the load's offset field takes (kept
-    // addresses per pattern cost registers)
+    // each pattern's offset a constant that the 8-byte load's offset field
+    // takes (kept addresses per pattern cost registers); the pattern count
+    // also goes through an opaque copy, so that each step's test is one
+    // scalar compare rather than a mask kept from before the loop
     uint32_t tl_op = tl;
     asm volatile("" : "+v"(tl_op));
-    const float* cb = sm.c0c14 + 2u * tl_op;
+    const float2* cb = reinterpret_cast<const float2*>(sm.c0c14) + tl_op;
+    int nsl = n_search_lane;
+    asm volatile("" : "+s"(nsl));
 #pragma unroll
     for (int k = 0; k < 64 / LPG; ++k) {
-      if (k >= n_search_lane) break;    // later patterns repeat earlier ones' end centroids
-      const uint32_t p = tl + LPG * k;
-      const float d1 = mn - cb[2 * LPG * k] * aa;
-      const float d2 = mx - cb[2 * LPG * k + 1] * aa;
+      if (k >= nsl) break;              // later patterns repeat earlier ones' end centroids
+      const float2 c = cb[LPG * k];
+      const float d1 = mn - c.x * aa;
+      const float d2 = mx - c.y * aa;
       const float f = d1 * d1 + d2 * d2;
       if (f < bf) {
         bf = f;
-        bp = p;
+        bk = k;
       }
     }
+    const uint32_t bp = tl + LPG * bk;
     const uint32_t fmin = seg_min_u32<LPG>(__float_as_uint(bf));
     const uint32_t pstar = seg_min_u32<LPG>(__float_as_uint(bf) == fmin ? bp : 63u) & 63u;
     // 4. quantise: sym = #{k : x > m_pk * a}.  The 15 thresholds (m_p14 * a
@@ -367,7 +381,7 @@ __global__ __launch_bounds__(kEncWaves * 64, 4) void encode_kernel(EncodeArgs ar
     for (int c = 0; c < NL * 2; ++c) l4c[c] = 0;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      uint32_t u = xq[i] > root ? 3u : 2u;
+      uint32_t u = !(xq[i] <= root) ? 3u : 2u;
       u = tree_step(u, xq[i], thr[u]);
       u = tree_step(u, xq[i], thr[u]);
       u = tree_step(u, xq[i], thr[u]);
@@ -498,7 +512,7 @@ __global__ __launch_bounds__(kEncWaves * 64, 4) void encode_kernel(EncodeArgs ar
     wave_sync();
     if (valid) {
       // 16 words over LPG lanes: 16 / LPG each
-      uint8_t* dst = a.blocks + ((uint64_t)row * a.blk_stride + col) * 64u;
+      uint8_t* dst = a.blocks + bidx * 64u;
       if constexpr (LPG == 8) {
         reinterpret_cast<uint2*>(dst)[tl] = make_uint2(out[2u * tl], out[2u * tl + 1u]);
       } else {
