@@ -156,6 +156,11 @@ struct EncodeArgs {
 
 constexpr int kEncWaves = 8;        // waves per workgroup (two workgroups resident per CU)
 constexpr uint32_t kOutlierSortRounds = 3;   // more outlier rounds than this: sort each lane's keys first
+// Words per group in the encoder's block staging: the block's 16, then a sink
+// for the bits of a clipped stream past bit 511 (a group's codewords end by
+// bit 16 + 128 * 8, word 32; the sink takes them, so the packing needs no
+// bounds test), rounded up to a multiple of 4 for the 16-byte reads.
+constexpr int kOutWords = 36;
 
 // Sorts 8 keys into descending order (an optimal 19-comparator network).
 __device__ __forceinline__ void sort8_desc(uint32_t (&k)[8]) {
@@ -178,7 +183,7 @@ struct EncodeSmem {
   uint32_t len4[16 + S * A];         // entry (p, s) at 16 + 16 p + s: index 16 p + u for tree leaf u = 16 + s
   uint32_t enc[16 + S * H * A];      // entry (p, h, s) at 16 + 16 (4 p + h) + s, likewise
   float thr[kEncWaves][16][16];      // threshold tree of each group of a wave
-  uint32_t out[kEncWaves][16][16];    // block words of each group of a wave
+  uint32_t out[kEncWaves][16][kOutWords];   // block words of each group of a wave (then a sink)
 };
 
 // Encoder lane layout: 16 values per lane, so a group takes LPG = GS / 16
@@ -274,12 +279,10 @@ __global__ __launch_bounds__(kEncWaves * 64, 4) void encode_kernel(EncodeArgs ar
   };
   const uint32_t ustride = a.wg_count * kEncWaves;
   uint32_t unit = lw * kEncWaves + wave;
-  Raw raw = load_group(unit * GPW + q);
-  for (; unit < a.n_units; unit += ustride) {
+  // one unit of GPW groups, whose input raw was loaded one unit ahead
+  auto encode_unit = [&](uint32_t unit, const Raw& raw) {
     const uint32_t gidx = unit * GPW + q;
     const bool valid = gidx < a.n_groups;
-    // the next unit's input is loaded before this one is worked on
-    const Raw nraw = load_group((unit + ustride) * GPW + q);
     uint64_t bidx = gidx;                  // the block's index in a.blocks
     if (valid && !contig) {
       const uint32_t row = div_magic(gidx, a.gpr), col = gidx - row * a.gpr.d;
@@ -401,7 +404,8 @@ __global__ __launch_bounds__(kEncWaves * 64, 4) void encode_kernel(EncodeArgs ar
     //    one funnel shift appends it (acc = acc << len | code); the part's
     //    bits are then reversed into stream order.  A segment scan gives each
     //    lane's position; the parts are OR-ed into the block's words, and
-    //    bits past 511 fall off, which is exactly the clipping rule.
+    //    bits past 511 land in the sink words after them and are never
+    //    stored, which is exactly the clipping rule.
     const uint32_t* enc_ph = sm.enc + 16u * (pstar * 4u + hstar);   // enc_ph[u] for symbol u - 16
     uint32_t part[NL * 2], plen[NL * 2];
     uint32_t off = 0;
@@ -428,8 +432,8 @@ __global__ __launch_bounds__(kEncWaves * 64, 4) void encode_kernel(EncodeArgs ar
       for (int c = 0; c < NL * 2; ++c) {
         const uint32_t w = pp >> 5;
         const uint64_t v = (uint64_t)part[c] << (pp & 31u);
-        if (w < 16u && (uint32_t)v) atomicOr(&out[w], (uint32_t)v);
-        if (w + 1u < 16u && (uint32_t)(v >> 32)) atomicOr(&out[w + 1u], (uint32_t)(v >> 32));
+        if ((uint32_t)v) atomicOr(&out[w], (uint32_t)v);
+        if ((uint32_t)(v >> 32)) atomicOr(&out[w + 1u], (uint32_t)(v >> 32));
         pp += plen[c];
       }
     }
@@ -543,8 +547,30 @@ __global__ __launch_bounds__(kEncWaves * 64, 4) void encode_kernel(EncodeArgs ar
         st_nonfin += nf;
       }
     }
-    raw = nraw;
     wave_sync();
+  };
+  // the next unit's input is loaded before this one is worked on, into the
+  // other of two register sets: unrolled by two, the loop copies neither.
+  // (64-value groups keep the plain loop and one copy: unrolled, their
+  // kernel spills a threshold address.)
+  Raw ra = load_group(unit * GPW + q);
+  if constexpr (GS == 128) {
+    Raw rb;
+    while (unit < a.n_units) {
+      rb = load_group((unit + ustride) * GPW + q);
+      encode_unit(unit, ra);
+      unit += ustride;
+      if (unit >= a.n_units) break;
+      ra = load_group((unit + ustride) * GPW + q);
+      encode_unit(unit, rb);
+      unit += ustride;
+    }
+  } else {
+    for (; unit < a.n_units; unit += ustride) {
+      const Raw nraw = load_group((unit + ustride) * GPW + q);
+      encode_unit(unit, ra);
+      ra = nraw;
+    }
   }
   if (a.stats && tl == 0 && st_groups) {
     atomicAdd(&a.stats->groups, (unsigned long long)st_groups);
