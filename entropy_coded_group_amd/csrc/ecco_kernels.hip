@@ -432,7 +432,7 @@ __global__ __launch_bounds__(kEncWaves * 64, 4) void encode_kernel(EncodeArgs ar
       for (int c = 0; c < NL * 2; ++c) {
         const uint32_t w = pp >> 5;
         const uint64_t v = (uint64_t)part[c] << (pp & 31u);
-        if ((uint32_t)v) atomicOr(&out[w], (uint32_t)v);
+        atomicOr(&out[w], (uint32_t)v);          // (rarely 0, and OR-ing 0 changes nothing)
         if ((uint32_t)(v >> 32)) atomicOr(&out[w + 1u], (uint32_t)(v >> 32));
         pp += plen[c];
       }
