@@ -306,30 +306,63 @@ __global__ __launch_bounds__(kPvWaves * 64) void attn_pv_kernel(AttnArgs a, uint
 }
 
 // out[pair * G + g][d]: with M the largest of the units' maxima m_u, the
-// units' partial sums and weight sums z_u, each times 2^(m_u - M), added in
-// unit order; then the partial-sum total over the z total.
-__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
-  const uint64_t idx = (uint64_t)blockIdx.x * 256u + threadIdx.x;
-  const uint64_t rows = (uint64_t)a.pairs * a.G;
-  if (idx >= rows * 128u) return;
-  const uint32_t d = (uint32_t)(idx & 127u);
-  // a wave's 64 threads share a row: its (m, z) loads are scalar
-  const uint64_t row = __builtin_amdgcn_readfirstlane((uint32_t)(idx >> 7));
-  const uint32_t pair = (uint32_t)(row / a.G), g = (uint32_t)(row % a.G);
-  const float* src = a.part + ((uint64_t)pair * a.n_units * a.G + g) * 128u + d;
-  const float2* mz = reinterpret_cast<const float2*>(a.mz) + (uint64_t)pair * a.n_units * a.G + g;
+// units' partial sums and weight sums z_u, each times 2^(m_u - M), summed;
+// then the partial-sum total over the z total.  One workgroup per output
+// row: thread t adds units t / 32, t / 32 + 8, ... (in that order) for the
+// four values 4 (t % 32) .. + 3 with 16-byte loads, and one pass over the
+// eight threads' sums (in order) finishes the row; so the order of the
+// additions is fixed.
+constexpr int kCombineThreads = 256;
+__global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(AttnArgs a) {
+  __shared__ float4 red[kCombineThreads / 32][32];
+  __shared__ float zred[kCombineThreads / 32];
+  __shared__ float mred[kCombineThreads / 64];
+  const uint32_t row = blockIdx.x;        // < pairs * G
+  const uint32_t pair = row / a.G, g = row % a.G;
+  const uint32_t t = threadIdx.x, q = t & 31u, ug = t >> 5;
+  const uint64_t base = (uint64_t)pair * a.n_units * a.G + g;     // unit 0's (pair, g) entry
+  const float2* mz = reinterpret_cast<const float2*>(a.mz) + base;
+  // M: each thread's units t, t + 256, ..., then a butterfly over the wave
+  // and the waves' maxima (max is exact, so its order does not matter)
   float M = -__builtin_inff();
-#pragma unroll 8
-  for (uint32_t u = 0; u < a.n_units; ++u) M = fmaxf(M, mz[(uint64_t)u * a.G].x);
-  float s = 0.0f, zt = 0.0f;
-#pragma unroll 8
-  for (uint32_t u = 0; u < a.n_units; ++u) {
+  for (uint32_t u = t; u < a.n_units; u += kCombineThreads) M = fmaxf(M, mz[(uint64_t)u * a.G].x);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  if ((t & 63u) == 0) mred[t >> 6] = M;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kCombineThreads / 64; ++i) M = fmaxf(M, mred[i]);
+  const float4* src = reinterpret_cast<const float4*>(a.part + base * 128u) + q;
+  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  float zt = 0.0f;
+#pragma unroll 4
+  for (uint32_t u = ug; u < a.n_units; u += kCombineThreads / 32) {
     const float2 e = mz[(uint64_t)u * a.G];
     const float w = __builtin_amdgcn_exp2f(e.x - M);
-    s += src[(uint64_t)u * a.G * 128u] * w;
+    const float4 v = src[(uint64_t)u * a.G * 32u];
+    acc.x += v.x * w;
+    acc.y += v.y * w;
+    acc.z += v.z * w;
+    acc.w += v.w * w;
     zt += e.y * w;
   }
-  a.out[row * 128u + d] = s / zt;
+  red[ug][q] = acc;
+  if (q == 0) zred[ug] = zt;
+  __syncthreads();
+  if (t < 32) {
+    float4 s4 = red[0][t];
+    float z = zred[0];
+#pragma unroll
+    for (int i = 1; i < kCombineThreads / 32; ++i) {
+      const float4 r = red[i][t];
+      s4.x += r.x;
+      s4.y += r.y;
+      s4.z += r.z;
+      s4.w += r.w;
+      z += zred[i];
+    }
+    reinterpret_cast<float4*>(a.out + (uint64_t)row * 128u)[t] = make_float4(s4.x / z, s4.y / z, s4.z / z, s4.w / z);
+  }
 }
 
 }  // namespace ecco
@@ -436,8 +469,7 @@ int launch_attention(const void* k_blocks, const void* k_tables, float k_scale, 
       hipLaunchKernelGGL(attn_pv_kernel<4>, dim3(vgrid), dim3(kPvWaves * 64), 0, s, a, 4u);
       break;
   }
-  const uint64_t n = (uint64_t)rows * 128u;
-  hipLaunchKernelGGL(attn_combine_kernel, dim3((uint32_t)((n + 255) / 256)), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(attn_combine_kernel, dim3(rows), dim3(kCombineThreads), 0, s, a);
   return hipGetLastError() == hipSuccess ? ECCO_OK : ECCO_EHIP;
 }
 
