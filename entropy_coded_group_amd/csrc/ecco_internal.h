@@ -13,12 +13,23 @@
 namespace ecco {
 
 constexpr uint32_t kMagic = 0x31434345u;   // "ECC1"
-constexpr uint32_t kVersion = 2;
+constexpr uint32_t kVersion = 3;
 constexpr int G = ECCO_GROUP;
 constexpr int S = ECCO_N_PATTERNS;
 constexpr int C = ECCO_N_CENTROIDS;
 constexpr int H = ECCO_N_CODEBOOKS;
 constexpr int A = ECCO_N_SYMBOLS;
+
+// Quantiser bins of a pattern (see Tables::qbin): kQBins - 1 equal bins over
+// the normalised range of its midpoints, then one bin for everything above it.
+constexpr int kQBins = 128;
+// Margin, in units of the group scale a, by which a bin's edges are widened
+// when it is decided which midpoints a value in it may fall on either side
+// of.  It covers the rounding of the bin position x * (B / a) + C in binary32
+// (B / a from an approximate reciprocal, within 2^-22) and of the thresholds
+// m_k * a: below 1e-6 for values near the midpoints' range, |x / a| <= 1 +
+// 3 * margin (a value far outside it lands in the first or last bin anyway).
+constexpr double kQBinMargin = 1e-5;
 
 // Decode look-up table entry for an 8-bit window of stream bits read LSB
 // first: bits 0..4 = symbol (0..15), bits 5..7 = code length - 1.  Every
@@ -44,6 +55,16 @@ struct alignas(256) Tables {
                                 // code bit at bit 31), 32 - len in bits 0..4
   float fp8_value[256];         // exact value of every E4M3FN code (NaN for 0x7F, 0xFF)
   uint8_t lut[S][H][256];       // decode look-up table
+  // Quantiser bins (used when qbins_ok): for pattern p, a value x of a group
+  // with scale a > 0 falls in bin j = min(floor(x * (qaxis[p][0] / a) +
+  // qaxis[p][1]), kQBins - 1) (j = 0 below the range, kQBins - 1 above it and
+  // for NaN); qbin[p][j] midpoints lie surely below every x of the bin, and
+  // at most one more (midpoint qbin[p][j]) may lie on either side, so that
+  // #{k : x > m_k a} = qbin[p][j] + (x > m_qbin a).  The last bin has all
+  // 14 below it and compares with the largest finite float instead.
+  uint8_t qbin[S][kQBins];
+  float qaxis[S][2];            // [p][0] = B, bins per unit of x / a; [p][1] = C = -L * B
+  uint32_t qbins_ok;            // 1 if every pattern's bins meet the rule above
 };
 
 static_assert(sizeof(Tables) % 256 == 0, "blob size");
@@ -52,6 +73,8 @@ static_assert(offsetof(Tables, centroids) % 16 == 0, "centroid alignment");
 
 uint32_t checksum_of(const Tables* t);
 uint32_t search_width(const Tables* t);
+// The quantiser bins (Tables::qbin, qaxis) of the midpoints; returns qbins_ok.
+uint32_t build_quantiser_bins(const float (*mid)[16], uint8_t (*qbin)[kQBins], float (*qaxis)[2]);
 
 // Device checks used by every device entry point (defined with the kernels):
 // ECCO_OK and the current device's compute-unit count if it is a gfx950.

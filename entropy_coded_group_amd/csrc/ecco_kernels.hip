@@ -184,6 +184,8 @@ struct EncodeSmem {
   uint32_t enc[16 + S * H * A];      // entry (p, h, s) at 16 + 16 (4 p + h) + s, likewise
   float thr[kEncWaves][16][16];      // threshold tree of each group of a wave
   uint32_t out[kEncWaves][16][kOutWords];   // block words of each group of a wave (then a sink)
+  alignas(16) uint8_t qbin[S * kQBins];      // quantiser bins of each pattern
+  alignas(8) float qaxis[S * 2];             // their B and C
 };
 
 // Encoder lane layout: 16 values per lane, so a group takes LPG = GS / 16
@@ -205,6 +207,13 @@ struct EncGeom {
 __device__ __forceinline__ uint32_t tree_step(uint32_t u, float x, float t) {
   uint32_t r;
   asm("v_cmp_nle_f32 vcc, %1, %2\n\tv_addc_co_u32 %0, vcc, %3, %3, vcc" : "=v"(r) : "v"(x), "v"(t), "v"(u) : "vcc");
+  return r;
+}
+// The last step of the binned quantiser: leaf 16 + s + !(x <= t), again a
+// compare into VCC and one add-with-carry.
+__device__ __forceinline__ uint32_t bin_step(uint32_t s, float x, float t) {
+  uint32_t r;
+  asm("v_cmp_nle_f32 vcc, %1, %2\n\tv_addc_co_u32 %0, vcc, 16, %3, vcc" : "=v"(r) : "v"(x), "v"(t), "v"(s) : "vcc");
   return r;
 }
 
@@ -242,6 +251,12 @@ __global__ __launch_bounds__(kEncWaves * 64, 4) void encode_kernel(EncodeArgs ar
   for (uint32_t i = tid; i < S * 2; i += blockDim.x) sm.c0c14[i] = (&a.tab->c0c14[0][0])[i];
   for (uint32_t i = tid; i < S * A; i += blockDim.x) sm.len4[16 + i] = (&a.tab->len4[0][0])[i];
   for (uint32_t i = tid; i < S * H * A; i += blockDim.x) sm.enc[16 + i] = (&a.tab->enc[0][0][0])[i];
+  const bool qbins_ok = a.tab->qbins_ok != 0u;
+  if (qbins_ok) {
+    for (uint32_t i = tid; i < S * kQBins / 16; i += blockDim.x)
+      reinterpret_cast<uint4*>(sm.qbin)[i] = reinterpret_cast<const uint4*>(&a.tab->qbin[0][0])[i];
+    for (uint32_t i = tid; i < S * 2; i += blockDim.x) sm.qaxis[i] = (&a.tab->qaxis[0][0])[i];
+  }
   __syncthreads();
 
   const uint32_t lane = lane_id(), wave = tid >> 6;
@@ -364,32 +379,64 @@ __global__ __launch_bounds__(kEncWaves * 64, 4) void encode_kernel(EncodeArgs ar
     const uint32_t bp = tl + LPG * bk;
     const uint32_t fmin = seg_min_u32<LPG>(__float_as_uint(bf));
     const uint32_t pstar = seg_min_u32<LPG>(__float_as_uint(bf) == fmin ? bp : 63u) & 63u;
-    // 4. quantise: sym = #{k : x > m_pk * a}.  The 15 thresholds (m_p14 * a
-    //    taken as the largest finite float) sit in LDS as an implicit binary
-    //    tree, node 1 the root and node u's children 2u and 2u + 1 (lane tl
-    //    writes thresholds tl, tl + LPG, ... to their nodes); four compares
-    //    walk it, the root one against a register copy, ending at leaf
-    //    u = 16 + sym.  For finite x, x > m_p14 * a never holds either way.
-#pragma unroll
-    for (int sl = 0; sl < NSLOT; ++sl) {
-      const uint32_t k = tl + LPG * sl;
-      if (k < 15u) thr[enode(k)] = k < 14u ? sm.mid[pstar * 16u + k] * aa : 3.40282347e38f;
-    }
-    wave_sync();
-    const float root = thr[1];
+    // 4. quantise: sym = #{k : x > m_pk * a}, as leaf u = 16 + sym.  The 15
+    //    thresholds (m_p14 * a taken as the largest finite float, which no
+    //    finite x exceeds) are written to LDS by the group's lanes (lane tl:
+    //    thresholds tl, tl + LPG, ...).
+    //    With the tables' quantiser bins (and no group of the wave at a = 0),
+    //    a value's bin j = min(floor(x * B / a + C), last) gives the count of
+    //    thresholds surely below it, s = qbin[p][j], and one compare with
+    //    threshold s finishes the count; the NaN in the scale element's place
+    //    goes to the last bin (s = 14), whose compare it passes: symbol 15.
+    //    Otherwise the thresholds form an implicit binary tree, node 1 the
+    //    root and node u's children 2u and 2u + 1, which four compares walk,
+    //    the root one against a register copy.
     const uint32_t* len_p = sm.len4 + 16u * pstar;       // len_p[u] = lengths of symbol u - 16
     uint32_t leaf[NV];
     uint32_t l4c[NL * 2];                  // per 4 values: four byte counters (codebooks 0..3)
 #pragma unroll
     for (int c = 0; c < NL * 2; ++c) l4c[c] = 0;
+    // (the lane's threshold slots are addressed from an opaque copy of tl:
+    // addresses kept from before the loop cost registers)
+    uint32_t tlq = tl;
+    asm volatile("" : "+v"(tlq));
+    if (qbins_ok && !__any(aa == 0.0f)) {
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      uint32_t u = !(xq[i] <= root) ? 3u : 2u;
-      u = tree_step(u, xq[i], thr[u]);
-      u = tree_step(u, xq[i], thr[u]);
-      u = tree_step(u, xq[i], thr[u]);
-      leaf[i] = u;
-      l4c[i / 4] += len_p[u];
+      for (int sl = 0; sl < NSLOT; ++sl) {
+        const uint32_t k = tl + LPG * sl;
+        if (k < 15u) thr[tlq + LPG * sl] = k < 14u ? sm.mid[pstar * 16u + k] * aa : 3.40282347e38f;
+      }
+      wave_sync();
+      const float2 ax = reinterpret_cast<const float2*>(sm.qaxis)[pstar];
+      const float qa = ax.x * __builtin_amdgcn_rcpf(aa);
+      const uint8_t* qb = sm.qbin + pstar * (uint32_t)kQBins;
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const float pos = fminf(fmaf(xq[i], qa, ax.y), (float)(kQBins - 1));
+        uint32_t j;
+        asm("v_cvt_u32_f32 %0, %1" : "=v"(j) : "v"(pos));   // saturates: below 0 -> bin 0
+        const uint32_t sb = qb[j];
+        const uint32_t u = bin_step(sb, xq[i], thr[sb]);
+        leaf[i] = u;
+        l4c[i / 4] += len_p[u];
+      }
+    } else {
+#pragma unroll
+      for (int sl = 0; sl < NSLOT; ++sl) {
+        const uint32_t k = tl + LPG * sl;
+        if (k < 15u) thr[enode(tlq + LPG * sl)] = k < 14u ? sm.mid[pstar * 16u + k] * aa : 3.40282347e38f;
+      }
+      wave_sync();
+      const float root = thr[1];
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        uint32_t u = !(xq[i] <= root) ? 3u : 2u;
+        u = tree_step(u, xq[i], thr[u]);
+        u = tree_step(u, xq[i], thr[u]);
+        u = tree_step(u, xq[i], thr[u]);
+        leaf[i] = u;
+        l4c[i / 4] += len_p[u];
+      }
     }
     // 5. codebook with the shortest stream, lowest h on ties
     const uint32_t l4 = (l4c[0] + l4c[1]) + (l4c[2] + l4c[3]);

@@ -2,8 +2,8 @@
 //
 // The blob holds the caller's centroids and code lengths plus what the
 // kernels derive from them: canonical codewords in stream order, an 8-bit
-// window decode table, midpoints, packed code lengths and the exact value of
-// every FP8 E4M3FN code.  Codes are canonical in the DEFLATE sense (RFC 1951
+// window decode table, midpoints, the encoder's quantiser bins, packed code
+// lengths and the exact value of every FP8 E4M3FN code.  Codes are canonical in the DEFLATE sense (RFC 1951
 // section 3.2.2); code lengths are limited to 2..8 bits as the pages' parallel
 // decoder requires (Ecco review, referee report major comment 1).
 #include <cmath>
@@ -25,6 +25,38 @@ uint32_t search_width(const Tables* t) {
     if (rep) return n;
   }
   return S;
+}
+
+// Bins B, C of each pattern over [m_0 - 2 margin, m_13 + 2 margin], and per
+// bin the midpoints surely below it; checks that at most one midpoint is
+// within the margin of any bin (the last bin: none, all 14 below it).  The
+// bin edges are taken from the binary32 B and C the kernel uses.
+uint32_t build_quantiser_bins(const float (*mid)[16], uint8_t (*qbin)[kQBins], float (*qaxis)[2]) {
+  const double d = kQBinMargin, inf = std::numeric_limits<double>::infinity();
+  bool ok = true;
+  for (int p = 0; p < S; ++p) {
+    double m[14];
+    for (int k = 0; k < 14; ++k) m[k] = mid[p][k];
+    const double lo_all = m[0] - 2.0 * d, hi_all = m[13] + 2.0 * d;
+    const float B = (float)((kQBins - 1) / (hi_all - lo_all));
+    const float Cq = (float)(-lo_all * (double)B);
+    qaxis[p][0] = B;
+    qaxis[p][1] = Cq;
+    for (int j = 0; j < kQBins; ++j) {
+      const double lo = j == 0 ? -inf : (j - (double)Cq) / (double)B;
+      const double hi = j == kQBins - 1 ? inf : (j + 1 - (double)Cq) / (double)B;
+      int below = 0, unsure = 0;
+      for (int k = 0; k < 14; ++k) {
+        if (m[k] < lo - d)
+          ++below;
+        else if (m[k] <= hi + d)
+          ++unsure;
+      }
+      if (j == kQBins - 1 ? below != 14 : unsure > 1) ok = false;
+      qbin[p][j] = (uint8_t)below;
+    }
+  }
+  return ok ? 1u : 0u;
 }
 
 uint32_t checksum_of(const Tables* t) {
@@ -158,6 +190,7 @@ extern "C" int ecco_tables_build(const float* centroids, const uint8_t* code_len
     }
   }
   for (int b = 0; b < 256; ++b) t->fp8_value[b] = fp8_code_value(b);
+  t->qbins_ok = build_quantiser_bins(t->midpoints, t->qbin, t->qaxis);
   t->n_search = search_width(t);
   t->checksum = checksum_of(t);
   return ECCO_OK;
@@ -169,6 +202,14 @@ extern "C" int ecco_tables_validate(const void* blob) {
   if (t->magic != kMagic || t->version != kVersion || t->size != sizeof(Tables)) return ECCO_ETABLES;
   if (t->checksum != checksum_of(t)) return ECCO_ETABLES;
   if (t->n_search != search_width(t)) return ECCO_ETABLES;
+  {
+    // the quantiser bins are derived from the midpoints: rebuild and compare
+    uint8_t qbin[S][kQBins];
+    float qaxis[S][2];
+    const uint32_t ok = build_quantiser_bins(t->midpoints, qbin, qaxis);
+    if (ok != t->qbins_ok || std::memcmp(qbin, t->qbin, sizeof(qbin)) || std::memcmp(qaxis, t->qaxis, sizeof(qaxis)))
+      return ECCO_ETABLES;
+  }
   float c[S * C];
   uint8_t l[S * H * A];
   for (int p = 0; p < S; ++p)

@@ -40,13 +40,79 @@ def test_strerror_covers_codes():
 
 
 # byte offsets of the blob (ecco_internal.h): header 256, centroids 4096,
-# code_len 4096, midpoints 4096, c0c14 512, len4 4096, enc 16384, fp8 1024, lut 65536
+# code_len 4096, midpoints 4096, c0c14 512, len4 4096, enc 16384, fp8 1024,
+# lut 65536, quantiser bins 8192, their axes 512, their flag 4 (+ padding)
 OFF_CENT, OFF_LEN, OFF_MID, OFF_C0, OFF_LEN4, OFF_ENC, OFF_FP8, OFF_LUT = (
     256, 4352, 8448, 12544, 13056, 17152, 33536, 34560)
+OFF_QBIN, OFF_QAXIS, OFF_QOK = 100096, 108288, 108800
+QBINS, QMARGIN = 128, 1e-5
 
 
 def test_blob_size_and_layout():
-    assert ecco.ecco_tables_size() == OFF_LUT + 65536
+    assert ecco.ecco_tables_size() == 109056        # 108804 rounded up to 256
+
+
+def _bins(blob):
+    qbin = blob[OFF_QBIN:OFF_QBIN + 64 * QBINS].reshape(64, QBINS).astype(np.int64)
+    qaxis = np.frombuffer(blob[OFF_QAXIS:OFF_QAXIS + 512].tobytes(), np.float32).reshape(64, 2)
+    ok = int(np.frombuffer(blob[OFF_QOK:OFF_QOK + 4].tobytes(), np.uint32)[0])
+    return qbin, qaxis, ok
+
+
+def _bins_meet_rule(mids, qbin, qaxis):
+    """Per pattern and bin: the bin's x / a interval from the stored binary32
+    B and C, widened by the margin; qbin = the midpoints below it, at most one
+    midpoint inside it (the last bin: all 14 below).  Computed here in exact
+    rational terms of the stored floats (fractions), not as the library does."""
+    from fractions import Fraction as F
+    d = F(QMARGIN)
+    for p in range(64):
+        B, C = F(float(qaxis[p, 0])), F(float(qaxis[p, 1]))
+        m = [F(float(v)) for v in mids[p]]
+        for j in range(QBINS):
+            lo = None if j == 0 else (j - C) / B
+            hi = None if j == QBINS - 1 else (j + 1 - C) / B
+            below = sum(1 for v in m if lo is not None and v < lo - d)
+            inside = sum(1 for v in m if (lo is None or v >= lo - d) and (hi is None or v <= hi + d))
+            if qbin[p, j] != below:
+                return False
+            if (j == QBINS - 1 and below != 14) or inside > 1:
+                return False
+    return True
+
+
+def test_quantiser_bins_of_trained_tables():
+    """Trained tables get bins (every bin at most one midpoint within the
+    margin), and a value's bin then decides all thresholds but one."""
+    tb = _golden()
+    blob = ecco.ecco_tables_build(tb.centroids, tb.code_len)
+    qbin, qaxis, ok = _bins(blob)
+    assert ok == 1
+    assert _bins_meet_rule(tb.midpoints(), qbin, qaxis)
+    # spot check with values: x / a at every midpoint and just beside it
+    rng = np.random.default_rng(5)
+    for p in rng.choice(64, 8, replace=False):
+        mids = tb.midpoints()[p].astype(np.float64)
+        for a in (np.float32(1.0), np.float32(0.0173), np.float32(300.0)):
+            thr = (tb.midpoints()[p] * a).astype(np.float32)
+            xs = np.concatenate([thr, np.nextafter(thr, np.float32(np.inf)), np.nextafter(thr, np.float32(-np.inf)),
+                                 (rng.uniform(-1.2, 1.2, 64) * a).astype(np.float32)])
+            for x in xs.astype(np.float32):
+                pos = np.float32(np.float32(x) * np.float32(qaxis[p, 0] / a) + qaxis[p, 1])
+                j = int(min(max(np.floor(min(pos, QBINS - 1)), 0), QBINS - 1))
+                s = int(qbin[p, j])
+                t = thr[s] if s < 14 else np.float32(3.4028235e38)
+                assert s + int(x > t) == int(np.sum(x > thr)), (p, float(a), float(x))
+
+
+def test_quantiser_bins_off_for_crowded_midpoints():
+    """Tables with two midpoints closer than a bin get no bins (the encoder
+    then walks its threshold tree)."""
+    tb = _golden()
+    c = tb.centroids.copy()
+    c[3, 5] = c[3, 6] = c[3, 7]                         # three equal centroids: two equal midpoints
+    blob = ecco.ecco_tables_build(c, tb.code_len)
+    assert _bins(blob)[2] == 0
 
 
 def test_tables_build_roundtrip_and_derived_tables_match_oracle():
@@ -104,6 +170,13 @@ def test_tables_validate_detects_corruption():
     assert ecco.ecco_tables_validate(bad) == -4
     bad = blob.copy()
     bad[0] ^= 1
+    assert ecco.ecco_tables_validate(bad) == -4
+    bad = blob.copy()                                   # a bin changed, checksum recomputed: still caught
+    bad[OFF_QBIN + 77] ^= 1
+    h = 2166136261
+    for v in bad[OFF_CENT:].tobytes():
+        h = ((h ^ v) * 16777619) & 0xffffffff
+    bad[12:16] = np.frombuffer(np.uint32(h).tobytes(), np.uint8)
     assert ecco.ecco_tables_validate(bad) == -4
 
 

@@ -254,6 +254,51 @@ def test_special_groups(dev):
         assert_fp16_equal(gpu_decode(o_blocks, tdev, t), codec.decode_blocks(o_blocks, tb, t), "special decode")
 
 
+def _near_threshold_groups(tb, scales, rng):
+    """Groups whose values sit on the quantiser's thresholds m_k * a and on
+    their FP16 neighbours: value 0 is the scale element +-a (an exact FP8
+    value, t = 1), values 1 and 2 are pattern p's end centroids times a (so
+    that p is the pattern chosen), the rest FP16 values at, just above and
+    just below each threshold, in a shuffled order."""
+    rows = []
+    mids = tb.midpoints()
+    for a in scales:
+        for p in rng.choice(64, 16, replace=False):
+            thr = (mids[p] * np.float32(a)).astype(np.float32)
+            near = []
+            for tk in thr:
+                h = np.float16(tk)
+                near += [h, np.nextafter(h, np.float16(np.inf)), np.nextafter(h, np.float16(-np.inf))]
+            body = np.resize(np.array(near, np.float16), 125)
+            rng.shuffle(body)
+            ends = (tb.centroids[p, [0, 14]] * np.float32(a)).astype(np.float16)
+            sign = np.float16(a) if rng.random() < 0.5 else -np.float16(a)
+            rows.append(np.r_[sign, ends, body].astype(np.float16))
+    return np.array(rows, np.float16)
+
+
+def test_quantiser_bins_at_thresholds(dev):
+    """Values on and beside every threshold, through the binned quantiser
+    (trained tables have bins) and through the threshold tree (tables whose
+    crowded midpoints leave them without bins): blocks equal the oracle's."""
+    rng = np.random.default_rng(23)
+    tb = golden("c1")
+    assert ecco.ecco_tables_build(tb.centroids, tb.code_len)[108800] == 1          # bins on
+    crowded = codec.Tables(tb.centroids.copy(), tb.code_len)
+    crowded.centroids[3, 5] = crowded.centroids[3, 6] = crowded.centroids[3, 7]
+    assert ecco.ecco_tables_build(crowded.centroids, crowded.code_len)[108800] == 0  # bins off
+    scales = (1.0, 0.0625, 4.0, 448.0, 2.0 ** -9)       # exact FP8 values: a = |x_0| with t = 1
+    for name, tables in (("bins", tb), ("tree", crowded)):
+        tdev = dev_tables(tables)
+        x = _near_threshold_groups(tables, scales, rng)
+        t = np.float32(1.0)
+        say("threshold groups, %s, %d groups" % (name, len(x)))
+        g_blocks, g_stats = gpu_encode(x, tdev, t, stats=True)
+        o_blocks, info = codec.encode_groups(x, tables, t, return_info=True)
+        assert_blocks_equal(g_blocks, o_blocks, "threshold groups, %s" % name)
+        assert g_stats == info["stats"]
+
+
 def test_nonfinite_groups_counted_and_contained(dev):
     """Groups holding NaN or +-Inf: their blocks are unspecified, but the
     launch completes, the statistics count them as the oracle does, every
