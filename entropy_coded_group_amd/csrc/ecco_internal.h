@@ -31,6 +31,23 @@ constexpr int kQBins = 128;
 // 3 * margin (a value far outside it lands in the first or last bin anyway).
 constexpr double kQBinMargin = 1e-5;
 
+// Pattern candidates (see Tables::pcand): a kPGrid x kPGrid grid, in units
+// of the group scale a, over (min, max) of a group's other values, spanning
+// the patterns' first and last centroids and an eighth of their spread on
+// each side; per cell the patterns that can have the least min/max fitness
+// somewhere in it.
+constexpr int kPGrid = 32;
+constexpr int kPCand = 8;                  // candidates a cell can list
+constexpr uint8_t kPCandNone = 0xff;       // an empty slot
+constexpr uint8_t kPCandMany = 0xfe;       // in slot 0: more than kPCand candidates
+// Margins in units of a (and a^2 for fitness): a cell is widened by
+// kPCellMargin on every side, and a pattern is a candidate where its fitness
+// is within kPFitMargin of the least.  They cover the rounding of the cell
+// position and of the binary32 fitness (d1^2 + d2^2 with d = min - c0 * a,
+// each within 2^-23 (|c| + |d / a|) a of exact): below 1e-6 in the grid.
+constexpr double kPCellMargin = 1e-5;
+constexpr double kPFitMargin = 1e-5;
+
 // Decode look-up table entry for an 8-bit window of stream bits read LSB
 // first: bits 0..4 = symbol (0..15), bits 5..7 = code length - 1.  Every
 // window decodes because codebooks are complete prefix codes.
@@ -65,16 +82,30 @@ struct alignas(256) Tables {
   uint8_t qbin[S][kQBins];
   float qaxis[S][2];            // [p][0] = B, bins per unit of x / a; [p][1] = C = -L * B
   uint32_t qbins_ok;            // 1 if every pattern's bins meet the rule above
+  // Pattern candidates of each grid cell, lowest first (kPCandNone after the
+  // last; kPCandMany in slot 0 if more than kPCand): every pattern whose
+  // fitness (x - c0)^2 + (y - c14)^2, at some (x, y) of the widened cell, is
+  // within kPFitMargin of the least there, less any pattern whose end
+  // centroids repeat a lower one's.
+  alignas(16) uint8_t pcand[kPGrid * kPGrid][kPCand];
+  // The grid: cell (i, j) holds x = min / a in [x0 + i / sx, x0 + (i + 1) / sx)
+  // and y = max / a likewise; {sx, -x0 * sx, sy, -y0 * sy}, so a cell index
+  // is floor(min * (sx / a) + [1]).
+  float pgrid[4];
 };
 
 static_assert(sizeof(Tables) % 256 == 0, "blob size");
 static_assert(offsetof(Tables, lut) % 256 == 0, "lut alignment");
 static_assert(offsetof(Tables, centroids) % 16 == 0, "centroid alignment");
+static_assert(offsetof(Tables, qbin) % 16 == 0 && offsetof(Tables, pcand) % 16 == 0, "16-byte staging");
 
 uint32_t checksum_of(const Tables* t);
 uint32_t search_width(const Tables* t);
 // The quantiser bins (Tables::qbin, qaxis) of the midpoints; returns qbins_ok.
 uint32_t build_quantiser_bins(const float (*mid)[16], uint8_t (*qbin)[kQBins], float (*qaxis)[2]);
+// The pattern candidates (Tables::pcand) and grid (Tables::pgrid) of the end
+// centroids.
+void build_pattern_candidates(const float (*c0c14)[2], uint8_t (*pcand)[kPCand], float* pgrid);
 
 // Device checks used by every device entry point (defined with the kernels):
 // ECCO_OK and the current device's compute-unit count if it is a gfx950.

@@ -186,6 +186,7 @@ struct EncodeSmem {
   uint32_t out[kEncWaves][16][kOutWords];   // block words of each group of a wave (then a sink)
   alignas(16) uint8_t qbin[S * kQBins];      // quantiser bins of each pattern
   alignas(8) float qaxis[S * 2];             // their B and C
+  alignas(16) uint8_t pcand[kPGrid * kPGrid * kPCand];   // pattern candidates of each grid cell
 };
 
 // Encoder lane layout: 16 values per lane, so a group takes LPG = GS / 16
@@ -252,10 +253,15 @@ __global__ __launch_bounds__(kEncWaves * 64, 4) void encode_kernel(EncodeArgs ar
   for (uint32_t i = tid; i < S * A; i += blockDim.x) sm.len4[16 + i] = (&a.tab->len4[0][0])[i];
   for (uint32_t i = tid; i < S * H * A; i += blockDim.x) sm.enc[16 + i] = (&a.tab->enc[0][0][0])[i];
   const bool qbins_ok = a.tab->qbins_ok != 0u;
+  const float4 pgrid = make_float4(a.tab->pgrid[0], a.tab->pgrid[1], a.tab->pgrid[2], a.tab->pgrid[3]);
   if (qbins_ok) {
     for (uint32_t i = tid; i < S * kQBins / 16; i += blockDim.x)
       reinterpret_cast<uint4*>(sm.qbin)[i] = reinterpret_cast<const uint4*>(&a.tab->qbin[0][0])[i];
     for (uint32_t i = tid; i < S * 2; i += blockDim.x) sm.qaxis[i] = (&a.tab->qaxis[0][0])[i];
+  }
+  if constexpr (GS == 64) {
+    for (uint32_t i = tid; i < kPGrid * kPGrid * kPCand / 16; i += blockDim.x)
+      reinterpret_cast<uint4*>(sm.pcand)[i] = reinterpret_cast<const uint4*>(&a.tab->pcand[0][0])[i];
   }
   __syncthreads();
 
@@ -352,31 +358,72 @@ __global__ __launch_bounds__(kEncWaves * 64, 4) void encode_kernel(EncodeArgs ar
     //    best of 64 / LPG (p rising, so a strict < keeps the lowest); the
     //    segment then takes the least fitness (non-negative, so its bits
     //    order like it) and the least p among the lanes that reach it.
+    //    64-value groups (four lanes, 16 patterns each) need not try all 64:
+    //    the tables list, for each cell of a grid over (min / a, max / a), the
+    //    patterns that can have the least fitness in it (the fitness
+    //    differences are affine there), at most eight, which the group's
+    //    lanes try (lane tl: slots tl, tl + LPG; the list rises, so a strict
+    //    < still keeps the lowest p).  A wave with a group off the grid, at
+    //    a = 0, or in a cell of more candidates tries every pattern.  (With
+    //    eight lanes a group tries only eight patterns a lane anyway, and the
+    //    two dependent LDS reads of the cell's list cost the 128-value
+    //    encoder more time than the instructions they save: 278 -> 287 us on
+    //    the layer, 18.9 -> 20.0 us on the KV append.)
     float bf = __builtin_inff();
-    uint32_t bk = 0;                       // the lane's best pattern is tl + LPG * bk
-    // the lane's end-centroid pairs: one address from an opaque copy of tl,
-    // each pattern's offset a constant that the 8-byte load's offset field
-    // takes (kept addresses per pattern cost registers); the pattern count
-    // also goes through an opaque copy, so that each step's test is one
-    // scalar compare rather than a mask kept from before the loop
-    uint32_t tl_op = tl;
-    asm volatile("" : "+v"(tl_op));
-    const float2* cb = reinterpret_cast<const float2*>(sm.c0c14) + tl_op;
-    int nsl = n_search_lane;
-    asm volatile("" : "+s"(nsl));
-#pragma unroll
-    for (int k = 0; k < 64 / LPG; ++k) {
-      if (k >= nsl) break;              // later patterns repeat earlier ones' end centroids
-      const float2 c = cb[LPG * k];
-      const float d1 = mn - c.x * aa;
-      const float d2 = mx - c.y * aa;
-      const float f = d1 * d1 + d2 * d2;
-      if (f < bf) {
-        bf = f;
-        bk = k;
-      }
+    uint32_t bp;
+    bool grid = false;
+    const uint8_t* cand = sm.pcand;
+    if constexpr (GS == 64) {
+      const float ra = __builtin_amdgcn_rcpf(aa);
+      int gx, gy;                          // floor, saturating (and 0 for NaN)
+      asm("v_cvt_flr_i32_f32 %0, %1" : "=v"(gx) : "v"(fmaf(mn, ra * pgrid.x, pgrid.y)));
+      asm("v_cvt_flr_i32_f32 %0, %1" : "=v"(gy) : "v"(fmaf(mx, ra * pgrid.z, pgrid.w)));
+      const bool on_grid = aa > 0.0f && (uint32_t)gx < (uint32_t)kPGrid && (uint32_t)gy < (uint32_t)kPGrid;
+      cand += (on_grid ? (uint32_t)(gy * kPGrid + gx) : 0u) * kPCand;
+      grid = !__any(!on_grid || cand[0] == kPCandMany);
     }
-    const uint32_t bp = tl + LPG * bk;
+    if (grid) {
+      bp = 63u;
+#pragma unroll
+      for (int k = 0; k < kPCand / LPG; ++k) {
+        const uint32_t p = cand[tl + LPG * k];
+        if (p != kPCandNone) {
+          const float2 c = reinterpret_cast<const float2*>(sm.c0c14)[p];
+          const float d1 = mn - c.x * aa;
+          const float d2 = mx - c.y * aa;
+          const float f = d1 * d1 + d2 * d2;
+          if (f < bf) {
+            bf = f;
+            bp = p;
+          }
+        }
+      }
+    } else {
+      uint32_t bk = 0;                     // the lane's best pattern is tl + LPG * bk
+      // the lane's end-centroid pairs: one address from an opaque copy of tl,
+      // each pattern's offset a constant that the 8-byte load's offset field
+      // takes (kept addresses per pattern cost registers); the pattern count
+      // also goes through an opaque copy, so that each step's test is one
+      // scalar compare rather than a mask kept from before the loop
+      uint32_t tl_op = tl;
+      asm volatile("" : "+v"(tl_op));
+      const float2* cb = reinterpret_cast<const float2*>(sm.c0c14) + tl_op;
+      int nsl = n_search_lane;
+      asm volatile("" : "+s"(nsl));
+#pragma unroll
+      for (int k = 0; k < 64 / LPG; ++k) {
+        if (k >= nsl) break;            // later patterns repeat earlier ones' end centroids
+        const float2 c = cb[LPG * k];
+        const float d1 = mn - c.x * aa;
+        const float d2 = mx - c.y * aa;
+        const float f = d1 * d1 + d2 * d2;
+        if (f < bf) {
+          bf = f;
+          bk = k;
+        }
+      }
+      bp = tl + LPG * bk;
+    }
     const uint32_t fmin = seg_min_u32<LPG>(__float_as_uint(bf));
     const uint32_t pstar = seg_min_u32<LPG>(__float_as_uint(bf) == fmin ? bp : 63u) & 63u;
     // 4. quantise: sym = #{k : x > m_pk * a}, as leaf u = 16 + sym.  The 15

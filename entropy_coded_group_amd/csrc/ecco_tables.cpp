@@ -2,8 +2,9 @@
 //
 // The blob holds the caller's centroids and code lengths plus what the
 // kernels derive from them: canonical codewords in stream order, an 8-bit
-// window decode table, midpoints, the encoder's quantiser bins, packed code
-// lengths and the exact value of every FP8 E4M3FN code.  Codes are canonical in the DEFLATE sense (RFC 1951
+// window decode table, midpoints, the encoder's quantiser bins and pattern
+// candidates, packed code lengths and the exact value of every FP8 E4M3FN
+// code.  Codes are canonical in the DEFLATE sense (RFC 1951
 // section 3.2.2); code lengths are limited to 2..8 bits as the pages' parallel
 // decoder requires (Ecco review, referee report major comment 1).
 #include <cmath>
@@ -57,6 +58,96 @@ uint32_t build_quantiser_bins(const float (*mid)[16], uint8_t (*qbin)[kQBins], f
     }
   }
   return ok ? 1u : 0u;
+}
+
+// Cell by cell: start from the widened cell's rectangle and, for pattern q,
+// cut it by every half-plane F_q - F_p <= margin (F_q - F_p is affine in
+// (x, y): the squares cancel); q is a candidate if anything is left.  A
+// quick test first drops the patterns whose nearest point of the cell is
+// farther than the farthest point from the pattern nearest the centre.
+void build_pattern_candidates(const float (*c0c14)[2], uint8_t (*pcand)[kPCand], float* pgrid) {
+  const double cm = kPCellMargin, fm = kPFitMargin;
+  double ax[S], by[S];
+  bool dup[S];
+  double xlo = 1e9, xhi = -1e9, ylo = 1e9, yhi = -1e9;
+  for (int p = 0; p < S; ++p) {
+    ax[p] = c0c14[p][0];
+    by[p] = c0c14[p][1];
+    xlo = std::fmin(xlo, ax[p]);
+    xhi = std::fmax(xhi, ax[p]);
+    ylo = std::fmin(ylo, by[p]);
+    yhi = std::fmax(yhi, by[p]);
+    dup[p] = false;
+    for (int r = 0; r < p && !dup[p]; ++r) dup[p] = c0c14[r][0] == c0c14[p][0] && c0c14[r][1] == c0c14[p][1];
+  }
+  // the grid: the centroids' range and an eighth of it on each side (at
+  // least 1/16), with binary32 scales; cells are placed as the kernel
+  // places them, from the stored floats
+  const double ex = std::fmax(0.125 * (xhi - xlo), 0.0625), ey = std::fmax(0.125 * (yhi - ylo), 0.0625);
+  const float sx = (float)(kPGrid / (xhi - xlo + 2 * ex)), sy = (float)(kPGrid / (yhi - ylo + 2 * ey));
+  const float ox = (float)(-(xlo - ex) * (double)sx), oy = (float)(-(ylo - ey) * (double)sy);
+  pgrid[0] = sx;
+  pgrid[1] = ox;
+  pgrid[2] = sy;
+  pgrid[3] = oy;
+  struct Pt {
+    double x, y;
+  };
+  for (int cy = 0; cy < kPGrid; ++cy) {
+    for (int cx = 0; cx < kPGrid; ++cx) {
+      const double x0 = (cx - (double)ox) / sx - cm, x1 = (cx + 1 - (double)ox) / sx + cm;
+      const double y0 = (cy - (double)oy) / sy - cm, y1 = (cy + 1 - (double)oy) / sy + cm;
+      const double xc = 0.5 * (x0 + x1), yc = 0.5 * (y0 + y1);
+      // the farthest-point distance of the pattern nearest the centre
+      int pn = 0;
+      double dn = 1e300;
+      for (int p = 0; p < S; ++p) {
+        const double d = (xc - ax[p]) * (xc - ax[p]) + (yc - by[p]) * (yc - by[p]);
+        if (d < dn) { dn = d; pn = p; }
+      }
+      const double fx = std::fmax(std::fabs(x0 - ax[pn]), std::fabs(x1 - ax[pn]));
+      const double fy = std::fmax(std::fabs(y0 - by[pn]), std::fabs(y1 - by[pn]));
+      const double far = fx * fx + fy * fy;
+      uint8_t* out = pcand[cy * kPGrid + cx];
+      int n = 0;
+      bool many = false;
+      for (int q = 0; q < S && !many; ++q) {
+        if (dup[q]) continue;
+        const double nx = std::fmax(0.0, std::fmax(x0 - ax[q], ax[q] - x1));
+        const double ny = std::fmax(0.0, std::fmax(y0 - by[q], by[q] - y1));
+        if (nx * nx + ny * ny > far + fm) continue;
+        Pt poly[4 + S], next[4 + S];
+        int np = 4;
+        poly[0] = {x0, y0}; poly[1] = {x1, y0}; poly[2] = {x1, y1}; poly[3] = {x0, y1};
+        for (int p = 0; p < S && np > 0; ++p) {
+          if (p == q || dup[p]) continue;
+          // F_q - F_p = gx * x + gy * y + g0 <= fm
+          const double gx = -2.0 * (ax[q] - ax[p]), gy = -2.0 * (by[q] - by[p]);
+          const double g0 = ax[q] * ax[q] + by[q] * by[q] - ax[p] * ax[p] - by[p] * by[p] - fm;
+          int nn = 0;
+          for (int i = 0; i < np; ++i) {
+            const Pt a = poly[i], b = poly[(i + 1) % np];
+            const double va = gx * a.x + gy * a.y + g0, vb = gx * b.x + gy * b.y + g0;
+            if (va <= 0.0) next[nn++] = a;
+            if ((va <= 0.0) != (vb <= 0.0)) {
+              const double t = va / (va - vb);
+              next[nn++] = {a.x + t * (b.x - a.x), a.y + t * (b.y - a.y)};
+            }
+          }
+          np = nn;
+          for (int i = 0; i < np; ++i) poly[i] = next[i];
+        }
+        if (np == 0) continue;
+        if (n == kPCand) {
+          many = true;
+        } else {
+          out[n++] = (uint8_t)q;
+        }
+      }
+      for (int i = n; i < kPCand; ++i) out[i] = kPCandNone;
+      if (many) out[0] = kPCandMany;
+    }
+  }
 }
 
 uint32_t checksum_of(const Tables* t) {
@@ -191,6 +282,7 @@ extern "C" int ecco_tables_build(const float* centroids, const uint8_t* code_len
   }
   for (int b = 0; b < 256; ++b) t->fp8_value[b] = fp8_code_value(b);
   t->qbins_ok = build_quantiser_bins(t->midpoints, t->qbin, t->qaxis);
+  build_pattern_candidates(t->c0c14, t->pcand, t->pgrid);
   t->n_search = search_width(t);
   t->checksum = checksum_of(t);
   return ECCO_OK;
@@ -209,6 +301,10 @@ extern "C" int ecco_tables_validate(const void* blob) {
     const uint32_t ok = build_quantiser_bins(t->midpoints, qbin, qaxis);
     if (ok != t->qbins_ok || std::memcmp(qbin, t->qbin, sizeof(qbin)) || std::memcmp(qaxis, t->qaxis, sizeof(qaxis)))
       return ECCO_ETABLES;
+    uint8_t pcand[kPGrid * kPGrid][kPCand];
+    float pgrid[4];
+    build_pattern_candidates(t->c0c14, pcand, pgrid);
+    if (std::memcmp(pcand, t->pcand, sizeof(pcand)) || std::memcmp(pgrid, t->pgrid, sizeof(pgrid))) return ECCO_ETABLES;
   }
   float c[S * C];
   uint8_t l[S * H * A];

@@ -44,12 +44,13 @@ def test_strerror_covers_codes():
 # lut 65536, quantiser bins 8192, their axes 512, their flag 4 (+ padding)
 OFF_CENT, OFF_LEN, OFF_MID, OFF_C0, OFF_LEN4, OFF_ENC, OFF_FP8, OFF_LUT = (
     256, 4352, 8448, 12544, 13056, 17152, 33536, 34560)
-OFF_QBIN, OFF_QAXIS, OFF_QOK = 100096, 108288, 108800
+OFF_QBIN, OFF_QAXIS, OFF_QOK, OFF_PCAND, OFF_PGRID = 100096, 108288, 108800, 108816, 117008
 QBINS, QMARGIN = 128, 1e-5
+PGRID, PCAND = 32, 8
 
 
 def test_blob_size_and_layout():
-    assert ecco.ecco_tables_size() == 109056        # 108804 rounded up to 256
+    assert ecco.ecco_tables_size() == 117248        # 117024 rounded up to 256
 
 
 def _bins(blob):
@@ -103,6 +104,55 @@ def test_quantiser_bins_of_trained_tables():
                 s = int(qbin[p, j])
                 t = thr[s] if s < 14 else np.float32(3.4028235e38)
                 assert s + int(x > t) == int(np.sum(x > thr)), (p, float(a), float(x))
+
+
+def _pattern_argmin_f32(tb, mn, mx, a):
+    """The oracle's pattern choice for one group (binary32 fitness, lowest
+    index on ties), written out here."""
+    c = tb.centroids
+    c0a = (c[:, 0] * np.float32(a)).astype(np.float32)
+    c14a = (c[:, 14] * np.float32(a)).astype(np.float32)
+    d1 = (np.float32(mn) - c0a).astype(np.float32)
+    d2 = (np.float32(mx) - c14a).astype(np.float32)
+    return int(np.argmin((d1 * d1 + d2 * d2).astype(np.float32)))
+
+
+def test_pattern_candidates_hold_the_oracles_choice():
+    """For points all over the grid, and on the bisectors of pattern pairs,
+    the cell that the encoder computes lists the pattern the oracle picks."""
+    rng = np.random.default_rng(31)
+    for name, tb in (("c1", _golden()), ("random", codec.Tables(
+            np.sort(rng.uniform(-1, 1, (64, 15)), axis=1).astype(np.float16).astype(np.float32), _golden().code_len))):
+        blob = ecco.ecco_tables_build(tb.centroids, tb.code_len)
+        cand = blob[OFF_PCAND:OFF_PCAND + PGRID * PGRID * PCAND].reshape(PGRID * PGRID, PCAND)
+        sx, ox, sy, oy = np.frombuffer(blob[OFF_PGRID:OFF_PGRID + 16].tobytes(), np.float32)
+        many = cand[:, 0] == 0xfe
+        assert many.mean() < 0.05, (name, many.mean())
+        c0, c14 = tb.centroids[:, 0].astype(np.float64), tb.centroids[:, 14].astype(np.float64)
+        xr = (-float(ox) / float(sx), (PGRID - float(ox)) / float(sx))
+        yr = (-float(oy) / float(sy), (PGRID - float(oy)) / float(sy))
+        pts = [np.array([rng.uniform(*xr), rng.uniform(*yr)]) for _ in range(3000)]
+        for _ in range(3000):                              # points on the bisector of two patterns
+            p, q = rng.choice(64, 2, replace=False)
+            mid = np.array([c0[p] + c0[q], c14[p] + c14[q]]) / 2
+            dirn = np.array([-(c14[q] - c14[p]), c0[q] - c0[p]])
+            pts.append(mid + rng.uniform(-0.3, 0.3) * dirn)
+        checked = 0
+        for pt in pts:
+            for a in (np.float32(1.0), np.float32(0.037), np.float32(211.0)):
+                mn, mx = np.float32(pt[0] * a), np.float32(pt[1] * a)
+                ra = np.float32(np.float32(1.0) / a)
+                gx = int(np.floor(np.float32(mn * np.float32(ra * sx) + ox)))
+                gy = int(np.floor(np.float32(mx * np.float32(ra * sy) + oy)))
+                if not (0 <= gx < PGRID and 0 <= gy < PGRID):
+                    continue
+                row = cand[gy * PGRID + gx]
+                if row[0] == 0xfe:
+                    continue
+                best = _pattern_argmin_f32(tb, mn, mx, a)
+                assert best in set(int(v) for v in row if v != 0xff), (name, pt, float(a), best, row)
+                checked += 1
+        assert checked > 10000
 
 
 def test_quantiser_bins_off_for_crowded_midpoints():

@@ -259,3 +259,27 @@ def test_act_full_size_sampled(dev):
     assert_blocks_equal(gb, ob, "full-size encode (sampled)")
     gy = yd.cpu().numpy().reshape(-1, G64)[idx]
     assert_fp16_equal(gy, codec.decode_blocks(ob, tb, t, group=G64), "full-size decode (sampled)")
+
+
+def test_act_pattern_choice_near_bisectors(dev):
+    """64-value groups whose (min, max) lie on the bisector of two patterns'
+    end centroids (in units of a), where the binary32 fitness decides: the
+    encoder tries only the pattern grid's candidates for these, and its blocks
+    must equal the oracle's (trained and random tables)."""
+    rng = np.random.default_rng(47)
+    for name, tb in (("trained", act_tables()), ("random", random_tables(49))):
+        c0, c14 = tb.centroids[:, 0].astype(np.float64), tb.centroids[:, 14].astype(np.float64)
+        rows = []
+        for a in (1.0, 0.0625, 4.0):
+            for _ in range(400):
+                p, q = rng.choice(64, 2, replace=False)
+                mid = np.array([c0[p] + c0[q], c14[p] + c14[q]]) / 2
+                dirn = np.array([-(c14[q] - c14[p]), c0[q] - c0[p]])
+                lo, hi = sorted(mid + rng.uniform(-0.2, 0.2) * dirn)
+                lo, hi = max(lo, -0.99), min(hi, 0.99)
+                body = np.r_[lo, hi, rng.uniform(lo, hi, G64 - 3)] * a
+                sign = a if rng.random() < 0.5 else -a
+                rows.append(np.r_[sign, body])
+        x = np.array(rows, dtype=np.float16)
+        say("act bisector groups, %s tables, %d groups" % (name, len(x)))
+        check_roundtrip(x, tb, np.float32(1.0), "act bisectors, %s" % name)

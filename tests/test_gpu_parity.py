@@ -299,6 +299,35 @@ def test_quantiser_bins_at_thresholds(dev):
         assert g_stats == info["stats"]
 
 
+def test_pattern_choice_near_bisectors(dev):
+    """Groups whose (min, max) lie on the bisector of two patterns' end
+    centroids (in units of a), where the binary32 fitness decides: blocks
+    equal the oracle's whether the grid's candidates or the full search
+    choose (random tables, golden tables)."""
+    rng = np.random.default_rng(41)
+    for name, tb in (("golden", golden("c1")), ("random", random_tables(43))):
+        tdev = dev_tables(tb)
+        c0, c14 = tb.centroids[:, 0].astype(np.float64), tb.centroids[:, 14].astype(np.float64)
+        rows = []
+        for a in (1.0, 0.0625, 4.0):
+            for _ in range(300):
+                p, q = rng.choice(64, 2, replace=False)
+                mid = np.array([c0[p] + c0[q], c14[p] + c14[q]]) / 2
+                dirn = np.array([-(c14[q] - c14[p]), c0[q] - c0[p]])
+                lo, hi = sorted(mid + rng.uniform(-0.2, 0.2) * dirn)
+                lo, hi = max(lo, -0.99), min(hi, 0.99)
+                body = np.r_[lo, hi, rng.uniform(lo, hi, 125)] * a
+                sign = a if rng.random() < 0.5 else -a
+                rows.append(np.r_[sign, body])
+        x = np.array(rows, dtype=np.float16)
+        t = np.float32(1.0)
+        say("bisector groups, %s tables, %d groups" % (name, len(x)))
+        g_blocks, g_stats = gpu_encode(x, tdev, t, stats=True)
+        o_blocks, info = codec.encode_groups(x, tb, t, return_info=True)
+        assert_blocks_equal(g_blocks, o_blocks, "bisector groups, %s" % name)
+        assert g_stats == info["stats"]
+
+
 def test_nonfinite_groups_counted_and_contained(dev):
     """Groups holding NaN or +-Inf: their blocks are unspecified, but the
     launch completes, the statistics count them as the oracle does, every
