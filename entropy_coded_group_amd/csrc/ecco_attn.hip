@@ -70,12 +70,11 @@ __device__ __forceinline__ BatchRegs fetch_tokens(uint32_t lane, const uint8_t* 
   });
 }
 
-template <int G>
-__global__ __launch_bounds__(score_waves<G>() * 64) void attn_scores_kernel(AttnArgs a) {
+// The scores kernel's work; STOP: the decode core's instance for tables
+// with an incomplete codebook.
+template <int G, bool STOP>
+__device__ __forceinline__ void attn_scores_body(const AttnArgs& a, DecodeSmem<score_waves<G>()>& sm) {
   constexpr int kScoreWaves = score_waves<G>();
-  __shared__ DecodeSmem<kScoreWaves> sm;
-  stage_decode_tables(sm, a.kt);
-  __syncthreads();
   // the wave index is uniform: held in a scalar register, so are the batch
   // counters and the addresses derived from them
   const uint32_t lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -143,9 +142,9 @@ __global__ __launch_bounds__(score_waves<G>() * 64) void attn_scores_kernel(Attn
       }
     };
     if (n_valid == 64u)
-      decode_batch<true, kScoreWaves, 128, true>(sm, wave, lane, 64u, a.kts, cur, sink, pre);
+      decode_batch<true, kScoreWaves, 128, true, STOP>(sm, wave, lane, 64u, a.kts, cur, sink, pre);
     else
-      decode_batch<false, kScoreWaves, 128, true>(sm, wave, lane, n_valid, a.kts, cur, sink, pre);
+      decode_batch<false, kScoreWaves, 128, true, STOP>(sm, wave, lane, n_valid, a.kts, cur, sink, pre);
     // the batch's largest score per head: rotations of each row by G, 2G,
     // ... keep a lane's residue mod G, so lane g of every row ends with its
     // row's maximum of head g (a lane that saw no token holds -inf); then
@@ -168,12 +167,21 @@ __global__ __launch_bounds__(score_waves<G>() * 64) void attn_scores_kernel(Attn
   }
 }
 
-// p . V for heads g_off .. g_off + GH - 1 of G.
-template <int GH>
-__global__ __launch_bounds__(kPvWaves * 64) void attn_pv_kernel(AttnArgs a, uint32_t g_off) {
-  __shared__ DecodeSmem<kPvWaves> sm;
-  stage_decode_tables(sm, a.vt);
+template <int G>
+__global__ __launch_bounds__(score_waves<G>() * 64) void attn_scores_kernel(AttnArgs a) {
+  __shared__ DecodeSmem<score_waves<G>()> sm;
+  stage_decode_tables(sm, a.kt);
   __syncthreads();
+  if (a.kt->complete)
+    attn_scores_body<G, false>(a, sm);
+  else
+    attn_scores_body<G, true>(a, sm);
+}
+
+// p . V for heads g_off .. g_off + GH - 1 of G.
+// The value kernel's work; STOP as for the scores.
+template <int GH, bool STOP>
+__device__ __forceinline__ void attn_pv_body(const AttnArgs& a, uint32_t g_off, DecodeSmem<kPvWaves>& sm) {
   // the wave index is uniform: held in a scalar register, so are the batch
   // counters and the addresses derived from them
   const uint32_t lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -257,7 +265,7 @@ __global__ __launch_bounds__(kPvWaves * 64) void attn_pv_kernel(AttnArgs a, uint
       };
       // one instantiation of the decode core (with a second one for whole
       // batches, the accumulators were copied between the two and spilled)
-      decode_batch<false, kPvWaves, 128, true>(sm, wave, lane, n_valid, a.vts, cur, sink, pre);
+      decode_batch<false, kPvWaves, 128, true, STOP>(sm, wave, lane, n_valid, a.vts, cur, sink, pre);
     }
     cur = nxt;
     if (half == 1u) {
@@ -303,6 +311,17 @@ __global__ __launch_bounds__(kPvWaves * 64) void attn_pv_kernel(AttnArgs a, uint
       half = 1;
     }
   }
+}
+
+template <int GH>
+__global__ __launch_bounds__(kPvWaves * 64) void attn_pv_kernel(AttnArgs a, uint32_t g_off) {
+  __shared__ DecodeSmem<kPvWaves> sm;
+  stage_decode_tables(sm, a.vt);
+  __syncthreads();
+  if (a.vt->complete)
+    attn_pv_body<GH, false>(a, g_off, sm);
+  else
+    attn_pv_body<GH, true>(a, g_off, sm);
 }
 
 // out[pair * G + g][d]: with M the largest of the units' maxima m_u, the

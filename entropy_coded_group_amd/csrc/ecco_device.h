@@ -390,12 +390,15 @@ struct NoPrologue {
 // of entry 16 + r -- and hands 8 values per lane to the sink,
 // GS / 8 lanes per block, so every store instruction writes whole rows (four
 // of 256 bytes, or eight of 128).
+// STOP adds the stop at a window that no codeword starts, which only tables
+// with an incomplete codebook have (kLutNoCode entries); complete tables run
+// the instance without it.
 // PRIO sets the wave's issue priority by step: the staging and the
 // lane-serial chain, a dependent series of LDS look-ups that bounds the
 // batch's latency, go first; the write-out passes next; the value-table work
 // last.  (The decode gains 6-8 % from it and the attention kernels 5 %;
 // the GEMV does not.)
-template <bool FULL, int NW, int GS = 128, bool PRIO = false, class Sink, class Pre = NoPrologue>
+template <bool FULL, int NW, int GS = 128, bool PRIO = false, bool STOP = false, class Sink, class Pre = NoPrologue>
 __device__ __forceinline__ void decode_batch(DecodeSmem<NW>& sm, uint32_t wave, uint32_t lane, uint32_t n_valid,
                                              float t, const BatchRegs& in, Sink sink, Pre pre = Pre{}) {
   using Geo = GroupGeom<GS>;
@@ -443,13 +446,21 @@ __device__ __forceinline__ void decode_batch(DecodeSmem<NW>& sm, uint32_t wave, 
     uint32_t ev = __builtin_amdgcn_perm(__builtin_amdgcn_perm(e3, e2, 0x0c0c0400u),
                                         __builtin_amdgcn_perm(e1, e0, 0x0c0c0400u), 0x05040100u);
     asm volatile("" : "+v"(ev));                 // pack now: keeps one register per 4 symbols
-    if (base + r4 > lim) {
-      // a codeword of this chunk ends past bit 512: the stream is clipped
-      // here.  The ends rise, so the codewords that fit are a prefix of f
-      // (8 f counted by inline constants: the byte masks, as literals, took
-      // four registers of the whole kernel); the bytes from f on become 16.
-      const uint32_t f8 = (base + r1 <= 512u ? 8u : 0u) + (base + r2 <= 512u ? 8u : 0u) +
-                          (base + r3 <= 512u ? 8u : 0u);
+    // The stream stops in this chunk if a codeword of it ends past bit 512
+    // (clipped) or, with STOP (tables with an incomplete codebook), a window
+    // has no codeword: the kLutNoCode entry, the only one with bit 4 set
+    // while the stream is live (~lim masks the test off once it stopped).
+    if (base + r4 > lim || (STOP && (ev & ~lim & 0x10101010u) != 0u)) {
+      // The codewords read are a prefix of f: the ends rise, so those that
+      // fit come first (8 f counted by inline constants: the byte masks, as
+      // literals, took four registers of the whole kernel), and none is
+      // read from the first window without a codeword on.  The bytes from f
+      // on become 16.
+      uint32_t f8 = (base + r1 <= 512u ? 8u : 0u) + (base + r2 <= 512u ? 8u : 0u) + (base + r3 <= 512u ? 8u : 0u);
+      if constexpr (STOP) {
+        const uint32_t nc = ev & 0x10101010u;    // bit 8 i + 4: codeword i's window has no codeword
+        f8 = min(f8 + (base + r4 <= 512u ? 8u : 0u), nc ? ((uint32_t)__builtin_ctz(nc) & 0x38u) : 32u);
+      }
       const uint32_t m = 0xffffffffu << f8;
       ev = (ev & ~m) | (0x10101010u & m);
       lim = 0xffffffffu;

@@ -86,7 +86,7 @@ __device__ __forceinline__ void gemv_dot_x(float (&acc)[BM], uint4 w, const uint
 // A wavefront owns one output row at a time and decodes its blocks 64 at a
 // time (the last batch of a row partly filled).  Rows go round the job's
 // workgroups first, then their waves.
-template <int BM>
+template <int BM, bool STOP>
 __device__ __forceinline__ void gemv_rows_per_wave(DecodeSmem<kGemvWaves>& sm, const GemvJob& a, uint32_t lw,
                                                    uint32_t batch) {
   const uint32_t lane = lane_id(), wave = threadIdx.x >> 6;
@@ -117,9 +117,9 @@ __device__ __forceinline__ void gemv_rows_per_wave(DecodeSmem<kGemvWaves>& sm, c
     };
     const uint32_t n_valid = min(64u, a.gpr - c0);
     if (n_valid == 64u)
-      decode_batch<true>(sm, wave, lane, 64u, a.t, cur, sink);
+      decode_batch<true, kGemvWaves, 128, false, STOP>(sm, wave, lane, 64u, a.t, cur, sink);
     else
-      decode_batch<false>(sm, wave, lane, n_valid, a.t, cur, sink);
+      decode_batch<false, kGemvWaves, 128, false, STOP>(sm, wave, lane, n_valid, a.t, cur, sink);
     if (c0 + 64u >= a.gpr) {
 #pragma unroll
       for (int b = 0; b < BM; ++b) {
@@ -139,7 +139,7 @@ __device__ __forceinline__ void gemv_rows_per_wave(DecodeSmem<kGemvWaves>& sm, c
 // decode core hands the weights over in four passes of 16 blocks and each
 // pass lies inside one row (pass k: row k * RB / 4 of the batch), so every
 // lane keeps one accumulator per row; wave sums finish the rows.
-template <int RB>
+template <int RB, bool STOP>
 __device__ __forceinline__ void gemv_whole_rows(DecodeSmem<kGemvWaves>& sm, const GemvJob& a, uint32_t lw,
                                                 uint32_t batch_cols) {
   constexpr uint32_t kGpr = 64 / RB;
@@ -201,9 +201,9 @@ __device__ __forceinline__ void gemv_whole_rows(DecodeSmem<kGemvWaves>& sm, cons
     };
     const uint32_t n_valid = min(64u, n_groups - batch * 64u);
     if (n_valid == 64u)
-      decode_batch<true>(sm, wave, lane, 64u, a.t, cur, sink, pre);
+      decode_batch<true, kGemvWaves, 128, false, STOP>(sm, wave, lane, 64u, a.t, cur, sink, pre);
     else
-      decode_batch<false>(sm, wave, lane, n_valid, a.t, cur, sink, pre);
+      decode_batch<false, kGemvWaves, 128, false, STOP>(sm, wave, lane, n_valid, a.t, cur, sink, pre);
 #pragma unroll
     for (int r = 0; r < RB; ++r) {
       const uint32_t row = batch * RB + r;
@@ -229,10 +229,17 @@ __device__ __forceinline__ void gemv_whole_rows(DecodeSmem<kGemvWaves>& sm, cons
 // gives the same bits as one call per job.
 constexpr uint32_t kGemvUnits = 84;     // units per round (row sums of a round in LDS)
 
+// The row sums of a round (one array for both decode instances of a kernel).
 template <int BM>
+__device__ __forceinline__ float (&gemv_round_sums())[kGemvUnits][4][BM] {
+  __shared__ float part[kGemvUnits][4][BM];
+  return part;
+}
+
+template <int BM, bool STOP>
 __device__ __forceinline__ void gemv_row_groups(DecodeSmem<kGemvWaves>& sm, const GemvJob& a, uint32_t lw,
                                                 uint32_t batch) {
-  __shared__ float part[kGemvUnits][4][BM];
+  float (&part)[kGemvUnits][4][BM] = gemv_round_sums<BM>();
   // the wave index is uniform: held in a scalar register, so are the unit counters
   const uint32_t lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t n_cc = a.gpr / 16u;              // column chunks of a row group
@@ -278,7 +285,7 @@ __device__ __forceinline__ void gemv_row_groups(DecodeSmem<kGemvWaves>& sm, cons
       auto sink = [&](uint32_t b, uint32_t, uint4 w, uint32_t, uint32_t) {
         gemv_dot_x<BM>(acc, w, xc + (uint64_t)(b >> 2) * 128u, a.in_f, batch);
       };
-      decode_batch<true>(sm, wave, lane, 64u, a.t, cur, sink);
+      decode_batch<true, kGemvWaves, 128, false, STOP>(sm, wave, lane, 64u, a.t, cur, sink);
 #pragma unroll
       for (int b2 = 0; b2 < BM; ++b2) {
         const float v = row_sum_f32(acc[b2]);
@@ -306,6 +313,24 @@ __device__ __forceinline__ void gemv_row_groups(DecodeSmem<kGemvWaves>& sm, cons
   }
 }
 
+// The kernel's work split.  Tables with an incomplete codebook take the
+// decode core's STOP instance, in the simplest split only (a row per wave,
+// which serves every shape): a second instance of the larger splits made
+// the kernels spill.
+template <int BM, int RB>
+__device__ __forceinline__ void gemv_split(DecodeSmem<kGemvWaves>& sm, const GemvJob& a, uint32_t lw, uint32_t batch) {
+  if (!a.tab->complete) {
+    gemv_rows_per_wave<BM, true>(sm, a, lw, batch);
+  } else if constexpr (RB == (int)kRowGroups) {
+    gemv_row_groups<BM, false>(sm, a, lw, batch);
+  } else if constexpr (RB > 0) {
+    static_assert(BM == 1, "whole rows per batch at batch 1 only");
+    gemv_whole_rows<RB, false>(sm, a, lw, batch);
+  } else {
+    gemv_rows_per_wave<BM, false>(sm, a, lw, batch);
+  }
+}
+
 // Each workgroup works on one matrix, so the look-up tables it stages in LDS
 // serve every block it sees.  BM: accumulators per lane (batch <= BM); RB:
 // whole rows per batch (every job of the launch alike), 0 for a row per wave.
@@ -319,14 +344,7 @@ __global__ __launch_bounds__(kGemvWaves * 64) void gemv_kernel(GemvArgs args) {
   stage_decode_tables(sm, a.tab);
   __syncthreads();
   const uint32_t lw = blockIdx.x - a.wg_first;
-  if constexpr (RB == (int)kRowGroups) {
-    gemv_row_groups<BM>(sm, a, lw, args.batch);
-  } else if constexpr (RB > 0) {
-    static_assert(BM == 1, "whole rows per batch at batch 1 only");
-    gemv_whole_rows<RB>(sm, a, lw, args.batch);
-  } else {
-    gemv_rows_per_wave<BM>(sm, a, lw, args.batch);
-  }
+  gemv_split<BM, RB>(sm, a, lw, args.batch);
 }
 
 }  // namespace ecco

@@ -13,7 +13,7 @@
 namespace ecco {
 
 constexpr uint32_t kMagic = 0x31434345u;   // "ECC1"
-constexpr uint32_t kVersion = 3;
+constexpr uint32_t kVersion = 4;
 constexpr int G = ECCO_GROUP;
 constexpr int S = ECCO_N_PATTERNS;
 constexpr int C = ECCO_N_CENTROIDS;
@@ -49,9 +49,12 @@ constexpr double kPCellMargin = 1e-5;
 constexpr double kPFitMargin = 1e-5;
 
 // Decode look-up table entry for an 8-bit window of stream bits read LSB
-// first: bits 0..4 = symbol (0..15), bits 5..7 = code length - 1.  Every
-// window decodes because codebooks are complete prefix codes.
+// first: bits 0..4 = symbol (0..15), bits 5..7 = code length - 1.  A window
+// that no codeword prefixes (an incomplete codebook: Kraft sum below 1) holds
+// kLutNoCode, the only entry with bit 4 set besides the clipped-stream
+// table's symbol 16: the decoder stops the stream there.
 constexpr uint8_t lut_entry(int sym, int len) { return (uint8_t)(sym | ((len - 1) << 5)); }
+constexpr uint8_t kLutNoCode = lut_entry(17, 1);
 
 struct alignas(256) Tables {
   // header
@@ -60,7 +63,8 @@ struct alignas(256) Tables {
   uint32_t size;
   uint32_t checksum;        // FNV-1a over every byte after the header
   uint32_t n_search;        // patterns the encoder searches (16, 32 or 64), derived from the centroids
-  uint32_t reserved[59];
+  uint32_t complete;        // 1 if every codebook is complete (Kraft sum 1): no window lacks a codeword
+  uint32_t reserved[58];
   // inputs
   float centroids[S][16];       // [p][0..14] centroid, [15] = 0
   uint8_t code_len[S][H][A];    // 2..8

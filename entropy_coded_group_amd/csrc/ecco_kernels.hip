@@ -67,8 +67,9 @@ struct DecodeArgs {
 };
 
 // Decode of workgroup lw's share of one job: a contiguous range of the
-// job's batches, interleaved over the waves.  GS values per group.
-template <int GS, bool CONTIG>
+// job's batches, interleaved over the waves.  GS values per group; STOP for
+// tables with an incomplete codebook.
+template <int GS, bool CONTIG, bool STOP>
 __device__ __forceinline__ void decode_job(DecodeSmem<kDecWaves>& sm, const DecodeJob& a, uint32_t lw) {
   const uint32_t lane = lane_id(), wave = threadIdx.x >> 6;
   const uint32_t b_end = (uint32_t)((uint64_t)a.n_batches * (lw + 1) / a.wg_count);
@@ -107,9 +108,9 @@ __device__ __forceinline__ void decode_job(DecodeSmem<kDecWaves>& sm, const Deco
     };
     const uint32_t n_valid = min(64u, a.n_groups - g0);
     if (n_valid == 64u)
-      decode_batch<true, kDecWaves, GS, true>(sm, wave, lane, 64u, a.t, cur, sink);
+      decode_batch<true, kDecWaves, GS, true, STOP>(sm, wave, lane, 64u, a.t, cur, sink);
     else
-      decode_batch<false, kDecWaves, GS, true>(sm, wave, lane, n_valid, a.t, cur, sink);
+      decode_batch<false, kDecWaves, GS, true, STOP>(sm, wave, lane, n_valid, a.t, cur, sink);
     cur = nxt;
   }
 }
@@ -125,10 +126,12 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_kernel(DecodeArgs args)
   stage_decode_tables(sm, a.tab);
   __syncthreads();
   const uint32_t lw = blockIdx.x - a.wg_first;
-  if (a.contiguous)
-    decode_job<GS, true>(sm, a, lw);
+  if (!a.tab->complete)
+    decode_job<GS, false, true>(sm, a, lw);        // (strided addressing serves contiguous tensors too)
+  else if (a.contiguous)
+    decode_job<GS, true, false>(sm, a, lw);
   else
-    decode_job<GS, false>(sm, a, lw);
+    decode_job<GS, false, false>(sm, a, lw);
 }
 
 // -------------------------------------------------------------------- encode

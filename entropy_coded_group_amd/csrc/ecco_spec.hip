@@ -93,106 +93,132 @@ __global__ __launch_bounds__(kSpecWaves * 64) void decode_spec_kernel(SpecArgs a
     wave_sync();
     const uint32_t head = W[0];
     const uint32_t lutb = ((head & 63u) * 4u + ((head >> 6) & 3u)) * 256u;
-    // the two words holding bits seg0 .. seg0 + 15 of this lane's segment
-    const uint32_t seg0 = 16u + 8u * min(lane, (uint32_t)kSegments - 1u);
-    const uint32_t wlo = W[seg0 >> 5], whi = W[(seg0 >> 5) + 1u], wbase = seg0 & ~31u;
-    const bool last = lane == (uint32_t)kSegments - 1u;
-    // 1. speculative decode.  A codeword may start at any of the segment's
-    //    8 bits: one look-up each gives its table entry (bytes of Elo, Ehi)
-    //    and the place q + length it ends (bytes of Nlo, Nhi; in the last
-    //    segment 16 marks a codeword that does not fit before bit 512, where
-    //    the stream is clipped).  The 8 decodes, one per entry offset o, then
-    //    run side by side in the bytes of P (position reached from o), a byte
-    //    gather per step; byte o of the map M is where decode o leaves the
-    //    segment (offset into the next one), byte o of K how many codewords
-    //    it read.  A codeword is at least 2 bits, so 4 steps finish them all.
-    uint32_t Elo = 0, Ehi = 0, Nlo = 0, Nhi = 0;
-#pragma unroll
-    for (uint32_t q = 0; q < 8u; ++q) {
-      const uint32_t e = sm.lut[lutb + (window(wlo, whi, seg0 + q - wbase) & 255u)];
-      uint32_t nq = q + (e >> 5) + 1u;
-      if (last && nq > 8u) nq = 16u;
-      const uint32_t sh = 8u * (q & 3u);
-      if (q < 4u) {
-        Elo |= e << sh;
-        Nlo |= nq << sh;
-      } else {
-        Ehi |= e << sh;
-        Nhi |= nq << sh;
-      }
-    }
-    uint32_t Plo = 0x03020100u, Phi = 0x07060504u, Klo = 0, Khi = 0;
-    auto step = [&](uint32_t& P, uint32_t& K) {
-      const uint32_t out = ((P >> 3) | (P >> 4)) & 0x01010101u;      // 1 in each byte whose decode has ended
-      const uint32_t G = __builtin_amdgcn_perm(Nhi, Nlo, P & 0x07070707u);
-      const uint32_t live = (out ^ 0x01010101u) * 0xffu;
-      K += (live & 0x01010101u) & (~G >> 4);                          // a codeword read unless it does not fit
-      P = (G & live) | (P & ~live);
-    };
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      step(Plo, Klo);
-      step(Phi, Khi);
-    }
-    uint32_t Mlo = (Plo - 0x08080808u) & 0x07070707u, Mhi = (Phi - 0x08080808u) & 0x07070707u;
-    // 2. resolve.  An inclusive scan over the lanes composes the spans: a
-    //    lane that holds the map of segments j .. i (entry offset of the
-    //    first -> entry offset of the one after the last) and their codeword
-    //    counts per entry offset takes in the span that ends at j - 1 from a
-    //    lower lane: M(o) = M_i(M_prev(o)), a byte gather that v_perm_b32 does
-    //    for four entries at once (selectors 0..7 pick bytes of the 8-byte
-    //    map), and K(o) = K_prev(o) + K_i(M_prev(o)), bytewise (a count is at
-    //    most 4 per segment, so no byte carries over).  Six DPP steps: shifts
-    //    by 1, 2, 4, 8 inside each row of 16 lanes, then the last lane of row
-    //    0 (2) into row 1 (3), then lane 31 into rows 2 and 3.
-    auto join = [&](uint32_t plo, uint32_t phi, uint32_t qlo, uint32_t qhi, bool take) {
-      if (take) {
-        const uint32_t nlo = __builtin_amdgcn_perm(Mhi, Mlo, plo), nhi = __builtin_amdgcn_perm(Mhi, Mlo, phi);
-        const uint32_t klo = qlo + __builtin_amdgcn_perm(Khi, Klo, plo);
-        const uint32_t khi = qhi + __builtin_amdgcn_perm(Khi, Klo, phi);
-        Mlo = nlo;
-        Mhi = nhi;
-        Klo = klo;
-        Khi = khi;
-      }
-    };
-    join(dpp_u32<kRowShr1>(Mlo), dpp_u32<kRowShr1>(Mhi), dpp_u32<kRowShr1>(Klo), dpp_u32<kRowShr1>(Khi),
-         (lane & 15u) >= 1u);
-    join(dpp_u32<kRowShr2>(Mlo), dpp_u32<kRowShr2>(Mhi), dpp_u32<kRowShr2>(Klo), dpp_u32<kRowShr2>(Khi),
-         (lane & 15u) >= 2u);
-    join(dpp_u32<kRowShr4>(Mlo), dpp_u32<kRowShr4>(Mhi), dpp_u32<kRowShr4>(Klo), dpp_u32<kRowShr4>(Khi),
-         (lane & 15u) >= 4u);
-    join(dpp_u32<kRowShr8>(Mlo), dpp_u32<kRowShr8>(Mhi), dpp_u32<kRowShr8>(Klo), dpp_u32<kRowShr8>(Khi),
-         (lane & 15u) >= 8u);
-    join(dpp_u32<kRowBcast15>(Mlo), dpp_u32<kRowBcast15>(Mhi), dpp_u32<kRowBcast15>(Klo),
-         dpp_u32<kRowBcast15>(Khi), (lane & 16u) != 0u);
-    join(dpp_u32<kRowBcast31>(Mlo), dpp_u32<kRowBcast31>(Mhi), dpp_u32<kRowBcast31>(Klo),
-         dpp_u32<kRowBcast31>(Khi), lane >= 32u);
-    // entry 0 of segment 0: lane i enters where segments 0 .. i - 1 leave
-    const uint32_t pm = dpp_u32<kWaveShr1>(Mlo), pk = dpp_u32<kWaveShr1>(Klo);
-    const uint32_t my_entry = lane ? (pm & 255u) : 0u;
-    const uint32_t my_start = lane ? (pk & 255u) : 0u;
-    const uint32_t my_cnt = (Klo & 255u) - my_start;
-    const uint32_t start = __builtin_amdgcn_readlane(Klo, kSegments - 1) & 255u;
-    const bool full = start >= 128u;               // 128 whole codewords fit: not clipped
-    // 3. emit: the codewords of the decode from the true entry, from the
-    //    entries already looked up
-    uint32_t end = 0;                               // stream end after codeword 128 (its lane only)
-    if (lane < (uint32_t)kSegments) {
-      uint32_t q = my_entry;
-#pragma unroll
-      for (uint32_t s = 0; s < 4u; ++s) {
-        if (s < my_cnt) {
-          const uint32_t e = __builtin_amdgcn_perm(Ehi, Elo, q) & 255u;   // the entry looked up at bit q
-          const uint32_t idx = my_start + s;
-          q += (e >> 5) + 1u;
-          if (idx < 128u) sym[idx] = (uint8_t)((e & 31u) << 1);
-          if (idx == 127u) end = seg0 + q;
+    bool full;                                      // 128 codewords read
+    uint32_t E;                                     // stream end after codeword 128
+    if (a.tab->complete) {
+      // the two words holding bits seg0 .. seg0 + 15 of this lane's segment
+      const uint32_t seg0 = 16u + 8u * min(lane, (uint32_t)kSegments - 1u);
+      const uint32_t wlo = W[seg0 >> 5], whi = W[(seg0 >> 5) + 1u], wbase = seg0 & ~31u;
+      const bool last = lane == (uint32_t)kSegments - 1u;
+      // 1. speculative decode.  A codeword may start at any of the segment's
+      //    8 bits: one look-up each gives its table entry (bytes of Elo, Ehi)
+      //    and the place q + length it ends (bytes of Nlo, Nhi; in the last
+      //    segment 16 marks a codeword that does not fit before bit 512, where
+      //    the stream is clipped).  The 8 decodes, one per entry offset o, then
+      //    run side by side in the bytes of P (position reached from o), a byte
+      //    gather per step; byte o of the map M is where decode o leaves the
+      //    segment (offset into the next one), byte o of K how many codewords
+      //    it read.  A codeword is at least 2 bits, so 4 steps finish them all.
+      uint32_t Elo = 0, Ehi = 0, Nlo = 0, Nhi = 0;
+  #pragma unroll
+      for (uint32_t q = 0; q < 8u; ++q) {
+        const uint32_t e = sm.lut[lutb + (window(wlo, whi, seg0 + q - wbase) & 255u)];
+        uint32_t nq = q + (e >> 5) + 1u;
+        if (last && nq > 8u) nq = 16u;
+        const uint32_t sh = 8u * (q & 3u);
+        if (q < 4u) {
+          Elo |= e << sh;
+          Nlo |= nq << sh;
+        } else {
+          Ehi |= e << sh;
+          Nhi |= nq << sh;
         }
       }
+      uint32_t Plo = 0x03020100u, Phi = 0x07060504u, Klo = 0, Khi = 0;
+      auto step = [&](uint32_t& P, uint32_t& K) {
+        const uint32_t out = ((P >> 3) | (P >> 4)) & 0x01010101u;      // 1 in each byte whose decode has ended
+        const uint32_t G = __builtin_amdgcn_perm(Nhi, Nlo, P & 0x07070707u);
+        const uint32_t live = (out ^ 0x01010101u) * 0xffu;
+        K += (live & 0x01010101u) & (~G >> 4);                          // a codeword read unless it does not fit
+        P = (G & live) | (P & ~live);
+      };
+  #pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        step(Plo, Klo);
+        step(Phi, Khi);
+      }
+      uint32_t Mlo = (Plo - 0x08080808u) & 0x07070707u, Mhi = (Phi - 0x08080808u) & 0x07070707u;
+      // 2. resolve.  An inclusive scan over the lanes composes the spans: a
+      //    lane that holds the map of segments j .. i (entry offset of the
+      //    first -> entry offset of the one after the last) and their codeword
+      //    counts per entry offset takes in the span that ends at j - 1 from a
+      //    lower lane: M(o) = M_i(M_prev(o)), a byte gather that v_perm_b32 does
+      //    for four entries at once (selectors 0..7 pick bytes of the 8-byte
+      //    map), and K(o) = K_prev(o) + K_i(M_prev(o)), bytewise (a count is at
+      //    most 4 per segment, so no byte carries over).  Six DPP steps: shifts
+      //    by 1, 2, 4, 8 inside each row of 16 lanes, then the last lane of row
+      //    0 (2) into row 1 (3), then lane 31 into rows 2 and 3.
+      auto join = [&](uint32_t plo, uint32_t phi, uint32_t qlo, uint32_t qhi, bool take) {
+        if (take) {
+          const uint32_t nlo = __builtin_amdgcn_perm(Mhi, Mlo, plo), nhi = __builtin_amdgcn_perm(Mhi, Mlo, phi);
+          const uint32_t klo = qlo + __builtin_amdgcn_perm(Khi, Klo, plo);
+          const uint32_t khi = qhi + __builtin_amdgcn_perm(Khi, Klo, phi);
+          Mlo = nlo;
+          Mhi = nhi;
+          Klo = klo;
+          Khi = khi;
+        }
+      };
+      join(dpp_u32<kRowShr1>(Mlo), dpp_u32<kRowShr1>(Mhi), dpp_u32<kRowShr1>(Klo), dpp_u32<kRowShr1>(Khi),
+           (lane & 15u) >= 1u);
+      join(dpp_u32<kRowShr2>(Mlo), dpp_u32<kRowShr2>(Mhi), dpp_u32<kRowShr2>(Klo), dpp_u32<kRowShr2>(Khi),
+           (lane & 15u) >= 2u);
+      join(dpp_u32<kRowShr4>(Mlo), dpp_u32<kRowShr4>(Mhi), dpp_u32<kRowShr4>(Klo), dpp_u32<kRowShr4>(Khi),
+           (lane & 15u) >= 4u);
+      join(dpp_u32<kRowShr8>(Mlo), dpp_u32<kRowShr8>(Mhi), dpp_u32<kRowShr8>(Klo), dpp_u32<kRowShr8>(Khi),
+           (lane & 15u) >= 8u);
+      join(dpp_u32<kRowBcast15>(Mlo), dpp_u32<kRowBcast15>(Mhi), dpp_u32<kRowBcast15>(Klo),
+           dpp_u32<kRowBcast15>(Khi), (lane & 16u) != 0u);
+      join(dpp_u32<kRowBcast31>(Mlo), dpp_u32<kRowBcast31>(Mhi), dpp_u32<kRowBcast31>(Klo),
+           dpp_u32<kRowBcast31>(Khi), lane >= 32u);
+      // entry 0 of segment 0: lane i enters where segments 0 .. i - 1 leave
+      const uint32_t pm = dpp_u32<kWaveShr1>(Mlo), pk = dpp_u32<kWaveShr1>(Klo);
+      const uint32_t my_entry = lane ? (pm & 255u) : 0u;
+      const uint32_t my_start = lane ? (pk & 255u) : 0u;
+      const uint32_t my_cnt = (Klo & 255u) - my_start;
+      const uint32_t start = __builtin_amdgcn_readlane(Klo, kSegments - 1) & 255u;
+      full = start >= 128u;               // 128 whole codewords fit: not clipped
+      // 3. emit: the codewords of the decode from the true entry, from the
+      //    entries already looked up
+      uint32_t end = 0;                               // stream end after codeword 128 (its lane only)
+      if (lane < (uint32_t)kSegments) {
+        uint32_t q = my_entry;
+  #pragma unroll
+        for (uint32_t s = 0; s < 4u; ++s) {
+          if (s < my_cnt) {
+            const uint32_t e = __builtin_amdgcn_perm(Ehi, Elo, q) & 255u;   // the entry looked up at bit q
+            const uint32_t idx = my_start + s;
+            q += (e >> 5) + 1u;
+            if (idx < 128u) sym[idx] = (uint8_t)((e & 31u) << 1);
+            if (idx == 127u) end = seg0 + q;
+          }
+        }
+      }
+      const uint64_t has_end = __ballot(end != 0u);
+      E = has_end ? __builtin_amdgcn_readlane(end, (int)__builtin_ctzll(has_end)) : 0u;
+    } else {
+      // tables with an incomplete codebook: lane 0 reads the stream alone,
+      // stopping at a codeword that does not fit before bit 512 or at a
+      // window that no codeword starts (kLutNoCode, bit 4 of the entry)
+      uint32_t k = 0, pos = 16;
+      if (lane == 0u) {
+        uint32_t kw = 0, lo = W[0], hi = W[1];
+        for (; k < 128u; ++k) {
+          const uint32_t e = sm.lut[lutb + (window(lo, hi, pos - 32u * kw) & 255u)];
+          const uint32_t np = pos + (e >> 5) + 1u;
+          if ((e & 0x10u) != 0u || np > 512u) break;
+          sym[k] = (uint8_t)((e & 31u) << 1);
+          pos = np;
+          if (pos - 32u * kw >= 32u) {              // pos <= 512: kw <= 16, W[kw + 1] within the 20 words
+            ++kw;
+            lo = hi;
+            hi = W[kw + 1u];
+          }
+        }
+      }
+      full = __builtin_amdgcn_readfirstlane(k) == 128u;
+      E = __builtin_amdgcn_readfirstlane(pos);
     }
-    const uint64_t has_end = __ballot(end != 0u);
-    const uint32_t E = has_end ? __builtin_amdgcn_readlane(end, (int)__builtin_ctzll(has_end)) : 0u;
     const uint32_t RB = 15u;
     const uint32_t n = full ? min(16u, (512u - E) / RB) : 0u;
     // 4. value table: [0..14] fp16(c * a), [15] fp16(S), [16 + r] record r or +0
@@ -359,78 +385,104 @@ __global__ __launch_bounds__(SegGeom<L>::kWaves * 64) void decode_seg_kernel(Spe
       }
       return pos;
     };
-    // 1. speculate
-    uint32_t cnt = 0;
-    const uint32_t spos = run(s, [&](uint32_t e) { sp[cnt++] = (uint8_t)e; });
-    uint32_t xit = last ? 0u : spos - ek;           // exit offset into the next segment
-    // 2. resolve: final codewords = pr[0 .. n_new) then sp[jo .. cnt)
-    uint32_t ent = 0, n_new = 0, jo = 0;
-    for (uint32_t round = 0; round < (uint32_t)L; ++round) {
-      const uint32_t left = __shfl(xit, k == 0u ? lane : lane - 1u);
-      const uint32_t want = k == 0u ? 0u : left;
-      const bool redo = want != ent;
-      if (!__any(redo)) break;
-      if (redo) {
-        ent = want;
-        n_new = 0;
-        uint32_t end;
-        if (round == 0u) {
-          // meet the speculative path: po walks its codeword boundaries
-          uint32_t pn = s + ent, po = s;
-          jo = 0;
-          uint32_t kw = pn >> 5, lo = W[kw], hi = W[kw + 1u];
-          while (true) {
-            while (po < pn && jo < cnt) po += (uint32_t)(sp[jo++] >> 5) + 1u;
-            if (po == pn || pn >= ek) break;
-            const uint32_t e = sm.lut[lutb + (window(lo, hi, pn - 32u * kw) & 255u)];
-            const uint32_t np = pn + (e >> 5) + 1u;
-            if (np > 512u) break;
-            pr[n_new++] = (uint8_t)e;
-            pn = np;
-            if (pn - 32u * kw >= 32u) {
-              ++kw;
-              lo = hi;
-              hi = W[kw + 1u];
+    uint8_t* row = reinterpret_cast<uint8_t*>(sm.sym[wave][bi]);
+    bool full;                                       // 128 codewords read
+    uint32_t E;                                      // stream end after codeword 128
+    if (a.tab->complete) {
+      // 1. speculate
+      uint32_t cnt = 0;
+      const uint32_t spos = run(s, [&](uint32_t e) { sp[cnt++] = (uint8_t)e; });
+      uint32_t xit = last ? 0u : spos - ek;           // exit offset into the next segment
+      // 2. resolve: final codewords = pr[0 .. n_new) then sp[jo .. cnt)
+      uint32_t ent = 0, n_new = 0, jo = 0;
+      for (uint32_t round = 0; round < (uint32_t)L; ++round) {
+        const uint32_t left = __shfl(xit, k == 0u ? lane : lane - 1u);
+        const uint32_t want = k == 0u ? 0u : left;
+        const bool redo = want != ent;
+        if (!__any(redo)) break;
+        if (redo) {
+          ent = want;
+          n_new = 0;
+          uint32_t end;
+          if (round == 0u) {
+            // meet the speculative path: po walks its codeword boundaries
+            uint32_t pn = s + ent, po = s;
+            jo = 0;
+            uint32_t kw = pn >> 5, lo = W[kw], hi = W[kw + 1u];
+            while (true) {
+              while (po < pn && jo < cnt) po += (uint32_t)(sp[jo++] >> 5) + 1u;
+              if (po == pn || pn >= ek) break;
+              const uint32_t e = sm.lut[lutb + (window(lo, hi, pn - 32u * kw) & 255u)];
+              const uint32_t np = pn + (e >> 5) + 1u;
+              if (np > 512u) break;
+              pr[n_new++] = (uint8_t)e;
+              pn = np;
+              if (pn - 32u * kw >= 32u) {
+                ++kw;
+                lo = hi;
+                hi = W[kw + 1u];
+              }
             }
-          }
-          if (po == pn) {
-            end = spos;                              // met: the rest is the speculative decode
+            if (po == pn) {
+              end = spos;                              // met: the rest is the speculative decode
+            } else {
+              end = pn;
+              jo = cnt;
+            }
           } else {
-            end = pn;
+            end = run(s + ent, [&](uint32_t e) { pr[n_new++] = (uint8_t)e; });
             jo = cnt;
           }
-        } else {
-          end = run(s + ent, [&](uint32_t e) { pr[n_new++] = (uint8_t)e; });
-          jo = cnt;
+          if (!last) xit = end - ek;
         }
-        if (!last) xit = end - ek;
       }
-    }
-    // 3. output indices: inclusive scan of the codeword counts over the block's lanes
-    const uint32_t mine = n_new + (cnt - jo);
-    uint32_t incl = mine;
-#pragma unroll
-    for (uint32_t d = 1; d < (uint32_t)L; d <<= 1) {
-      const uint32_t v = __shfl_up(incl, d, L);
-      if (k >= d) incl += v;
-    }
-    const uint32_t base = incl - mine;
-    const uint32_t total = __shfl(incl, L - 1, L);
-    const bool full = total >= 128u;
-    uint8_t* row = reinterpret_cast<uint8_t*>(sm.sym[wave][bi]);
-    uint32_t E = 0;                                  // end of codeword 127 (its lane only)
-    {
-      uint32_t pe = s + ent;
-      const uint32_t m = base < 128u ? min(mine, 128u - base) : 0u;
-      for (uint32_t i = 0; i < m; ++i) {
-        const uint32_t e = i < n_new ? pr[i] : sp[jo + i - n_new];
-        row[base + i] = (uint8_t)((e & 31u) << 1);
-        pe += (e >> 5) + 1u;
-        if (base + i == 127u) E = pe;
+      // 3. output indices: inclusive scan of the codeword counts over the block's lanes
+      const uint32_t mine = n_new + (cnt - jo);
+      uint32_t incl = mine;
+  #pragma unroll
+      for (uint32_t d = 1; d < (uint32_t)L; d <<= 1) {
+        const uint32_t v = __shfl_up(incl, d, L);
+        if (k >= d) incl += v;
       }
+      const uint32_t base = incl - mine;
+      const uint32_t total = __shfl(incl, L - 1, L);
+      full = total >= 128u;
+      E = 0;                                           // end of codeword 127 (its lane only)
+      {
+        uint32_t pe = s + ent;
+        const uint32_t m = base < 128u ? min(mine, 128u - base) : 0u;
+        for (uint32_t i = 0; i < m; ++i) {
+          const uint32_t e = i < n_new ? pr[i] : sp[jo + i - n_new];
+          row[base + i] = (uint8_t)((e & 31u) << 1);
+          pe += (e >> 5) + 1u;
+          if (base + i == 127u) E = pe;
+        }
+      }
+  #pragma unroll
+      for (uint32_t d = 1; d < (uint32_t)L; d <<= 1) E = max(E, (uint32_t)__shfl_xor(E, d, L));
+    } else {
+      // tables with an incomplete codebook: the block's first lane reads the
+      // stream alone, stopping at a codeword that does not fit before bit
+      // 512 or at a window that no codeword starts (kLutNoCode, bit 4)
+      uint32_t nk = 0, pos = 16;
+      if (k == 0u) {
+        uint32_t kw = 0, lo = W[0], hi = W[1];
+        for (; nk < 128u; ++nk) {
+          const uint32_t e = sm.lut[lutb + (window(lo, hi, pos - 32u * kw) & 255u)];
+          const uint32_t np = pos + (e >> 5) + 1u;
+          if ((e & 0x10u) != 0u || np > 512u) break;
+          row[nk] = (uint8_t)((e & 31u) << 1);
+          pos = np;
+          if (pos - 32u * kw >= 32u) {               // pos <= 512: kw <= 16, W[kw + 1] within the 20 words
+            ++kw;
+            lo = hi;
+            hi = W[kw + 1u];
+          }
+        }
+      }
+      full = (uint32_t)__shfl(nk, 0, L) == 128u;
+      E = (uint32_t)__shfl(pos, 0, L);
     }
-#pragma unroll
-    for (uint32_t d = 1; d < (uint32_t)L; d <<= 1) E = max(E, (uint32_t)__shfl_xor(E, d, L));
     // 4. value table: [0..14] fp16(c * a), [15] fp16(S), [16 + r] record r or +0
     const uint32_t n = full ? min(16u, (512u - E) / 15u) : 0u;
     const uint32_t p = head & 63u;

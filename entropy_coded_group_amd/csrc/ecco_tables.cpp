@@ -203,10 +203,20 @@ int check_inputs(const float* c, const uint8_t* len) {
         if (l < ECCO_LEN_MIN || l > ECCO_LEN_MAX) return ECCO_ETABLES;
         kraft += 1u << (8 - l);
       }
-      if (kraft != 256u) return ECCO_ETABLES;   // complete prefix code
+      if (kraft > 256u) return ECCO_ETABLES;    // a prefix code exists (complete or not)
     }
   }
   return ECCO_OK;
+}
+
+// 1 if every codebook's Kraft sum is 1 (lengths already checked).
+uint32_t all_complete(const uint8_t* len) {
+  for (int b = 0; b < S * H; ++b) {
+    uint32_t kraft = 0;
+    for (int s = 0; s < A; ++s) kraft += 1u << (8 - len[b * A + s]);
+    if (kraft != 256u) return 0u;
+  }
+  return 1u;
 }
 
 // Canonical codewords of one codebook: symbols taken in (length, symbol)
@@ -268,6 +278,7 @@ extern "C" int ecco_tables_build(const float* centroids, const uint8_t* code_len
       const uint8_t* L = code_len + (p * H + h) * A;
       uint32_t code[A], rev[A];
       canonical_stream_codes(L, code, rev);
+      std::memset(t->lut[p][h], kLutNoCode, 256);   // windows no codeword prefixes
       for (int s = 0; s < A; ++s) {
         t->code_len[p][h][s] = L[s];
         t->enc[p][h][s] = (code[s] << (32 - L[s])) | uint32_t(32 - L[s]);
@@ -284,6 +295,7 @@ extern "C" int ecco_tables_build(const float* centroids, const uint8_t* code_len
   t->qbins_ok = build_quantiser_bins(t->midpoints, t->qbin, t->qaxis);
   build_pattern_candidates(t->c0c14, t->pcand, t->pgrid);
   t->n_search = search_width(t);
+  t->complete = all_complete(code_len);
   t->checksum = checksum_of(t);
   return ECCO_OK;
 }
@@ -311,7 +323,9 @@ extern "C" int ecco_tables_validate(const void* blob) {
   for (int p = 0; p < S; ++p)
     for (int k = 0; k < C; ++k) c[p * C + k] = t->centroids[p][k];
   std::memcpy(l, t->code_len, sizeof(l));
-  return check_inputs(c, l);
+  const int rc = check_inputs(c, l);
+  if (rc) return rc;
+  return t->complete == all_complete(l) ? ECCO_OK : ECCO_ETABLES;
 }
 
 extern "C" int ecco_tables_get(const void* blob, float* centroids, uint8_t* code_len) {

@@ -51,9 +51,11 @@
  *   outliers: the n values j != i* of largest |x_j| (lower j first on ties),
  *            record r holding the r-th of them
  * Decode: symbols are read while a whole codeword fits in bits 16..511, at
- * most 128 of them; value j = fp16(S) for symbol 15, fp16(c[p][sym] * a)
- * otherwise, +0 for j >= k; if k == 128 the n records are applied in order
- * r = 0..n-1: value[j_r] = fp16(f32(v8_r) * t).  Any 512 bits decode.
+ * most 128 of them (with an incomplete codebook, reading also stops where
+ * no codeword starts the remaining bits); k = the symbols read; value
+ * j = fp16(S) for symbol 15, fp16(c[p][sym] * a) otherwise, +0 for j >= k;
+ * if k == 128 the n records are applied in order r = 0..n-1:
+ * value[j_r] = fp16(f32(v8_r) * t).  Any 512 bits decode.
  *
  * ------------------------------------------------------------------------
  * ACTIVATION FORMAT (64 bytes per group of 64 values, about 8 bits/value)
@@ -159,9 +161,11 @@ size_t ecco_tables_size(void);
  * with code lengths of 2..8 bits (referee report, major comment 1).
  * Build it from centroids[64][15] (float32, each exactly representable in
  * FP16, non-decreasing per pattern, within [-1, 1]) and code_len[64][4][16]
- * (each in [2, 8], every codebook a complete prefix code: Kraft sum exactly
- * 1).  Returns ECCO_ETABLES if the contents violate these rules (the blob is
- * then left unspecified), ECCO_EINVAL for NULL pointers.
+ * (each in [2, 8], every codebook a prefix code: Kraft sum at most 1; an
+ * incomplete codebook leaves bit strings that no codeword starts, where the
+ * decoder stops the stream, see ecco_decode).  Returns ECCO_ETABLES if the
+ * contents violate these rules (the blob is then left unspecified),
+ * ECCO_EINVAL for NULL pointers.
  * The blob records how many patterns the encoder has to search: the least
  * of 16, 32 and 64 such that every later pattern p has the same first and
  * last centroid as pattern p mod that number (the min/max fitness then ties
@@ -265,9 +269,10 @@ int ecco_encode_many(const ecco_encode_job_t* jobs_host, uint32_t n_jobs, void* 
 
 /* Decode: every block is expanded back to 128 FP16 values on load, from its
  * own bits and the tensor's side data alone ("The pith"; "Core claim";
- * decompressor of Fig. 8 caption): codewords read while they fit, values
- * c * |S| or S, clipped positions +0, then the padded values, exactly as the
- * block format above states.
+ * decompressor of Fig. 8 caption): codewords read while they fit (and,
+ * with an incomplete codebook, while one starts the remaining bits), values
+ * c * |S| or S, positions past the last codeword read +0, then the padded
+ * values, exactly as the block format above states.
  * The inverse layout of ecco_encode; group (r, g) is written to
  * y_dev + r * y_row_stride_elems + g * 128.  Every block decodes (the
  * decoder is total on arbitrary bits).  Same size rules as ecco_encode. */

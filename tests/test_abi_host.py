@@ -198,10 +198,15 @@ def test_tables_build_rejects_bad_inputs():
     bad_len[3, 1, 5] = 1
     with pytest.raises(ecco.EccoError):
         ecco.ecco_tables_build(tb.centroids, bad_len)
-    incomplete = tb.code_len.copy()
-    incomplete[0, 0, :] = 8                               # Kraft 1/16 < 1
+    over = tb.code_len.copy()
+    over[0, 0, :] = 2                                     # Kraft 4 > 1: no prefix code
     with pytest.raises(ecco.EccoError):
-        ecco.ecco_tables_build(tb.centroids, incomplete)
+        ecco.ecco_tables_build(tb.centroids, over)
+    over = tb.code_len.copy()
+    s = int(np.argmax(over[4, 2]))                        # one codeword a bit shorter: Kraft just above 1
+    over[4, 2, s] -= 1
+    with pytest.raises(ecco.EccoError):
+        ecco.ecco_tables_build(tb.centroids, over)
     unsorted = tb.centroids.copy()
     unsorted[2, [4, 5]] = unsorted[2, [5, 4]] + np.float32([0.5, 0])
     with pytest.raises(ecco.EccoError):
@@ -210,6 +215,45 @@ def test_tables_build_rejects_bad_inputs():
     not_half[1, 7] = np.float32(0.1)                       # not exact in FP16
     with pytest.raises(ecco.EccoError):
         ecco.ecco_tables_build(not_half, tb.code_len)
+
+
+def test_incomplete_codebooks_get_no_codeword_entries():
+    """Codebooks with Kraft sum below 1 are accepted; every window that a
+    codeword prefixes holds (symbol, length) as for a complete book, every
+    other window the no-codeword entry (symbol 17, length 1: 0x11), and their
+    share is 1 - Kraft sum.  The windows are found here by brute force over
+    the oracle's canonical codes."""
+    tb = _golden()
+    L = tb.code_len.copy()
+    L[0, 0, :] = 8                                         # Kraft 1/16
+    s = int(np.argmin(L[9, 3]))                            # one codeword a bit longer: Kraft just below 1
+    L[9, 3, s] += 1
+    assert L[20, 1, 3] < 8
+    L[20, 1, 3] = 8                                        # one codeword lengthened to 8 bits
+    from fractions import Fraction
+    blob = ecco.ecco_tables_build(tb.centroids, L)
+    assert ecco.ecco_tables_validate(blob) == 0
+    lut = blob[OFF_LUT:OFF_LUT + 65536].reshape(64, 4, 256)
+    codes = codec.Tables(tb.centroids, L).codes()
+    for p, h in ((0, 0), (9, 3), (20, 1), (5, 2)):
+        expect = np.full(256, 0x11, np.uint8)
+        for sym in range(16):
+            ln = int(L[p, h, sym])
+            rev = int(format(int(codes[p, h, sym]), "0%db" % ln)[::-1], 2)   # stream order, LSB first
+            for w in range(256):
+                if w & ((1 << ln) - 1) == rev:
+                    assert expect[w] == 0x11, (p, h, w)            # prefix-free: no window twice
+                    expect[w] = sym | ((ln - 1) << 5)
+        assert np.array_equal(lut[p, h], expect), (p, h)
+        share = Fraction(int(np.sum(expect == 0x11)), 256)
+        assert share == 1 - huffman.kraft_sum(L[p, h]), (p, h)
+    # the header's completeness flag (byte 20): 0 here, 1 for the trained tables;
+    # validation recomputes it
+    assert int(blob[20]) == 0
+    assert int(ecco.ecco_tables_build(tb.centroids, tb.code_len)[20]) == 1
+    bad = blob.copy()
+    bad[20] = 1
+    assert ecco.ecco_tables_validate(bad) == -4
 
 
 def test_tables_validate_detects_corruption():

@@ -190,8 +190,22 @@ def test_act_special_groups(dev):
                           "special decode t=%g" % t)
 
 
+def incomplete_act_tables(seed):
+    """The activation tables with one to three codewords of each book made
+    one or two bits longer (at most 8): Kraft sums below 1, so random bits
+    often start with no codeword, where decoding stops."""
+    tb = act_tables()
+    rng = np.random.default_rng(seed)
+    L = tb.code_len.copy()
+    for p in range(64):
+        for h in range(4):
+            for s in rng.choice(16, int(rng.integers(1, 4)), replace=False):
+                L[p, h, s] = min(8, int(L[p, h, s]) + int(rng.integers(1, 3)))
+    return codec.Tables(tb.centroids, L)
+
+
 def test_act_fuzz_decode_random_blocks(dev):
-    for name, tb in (("act", act_tables()), ("clipping", clipping_tables(3))):
+    for name, tb in (("act", act_tables()), ("clipping", clipping_tables(3)), ("incomplete", incomplete_act_tables(4))):
         tdev = dev_tables(tb)
         blocks = W.random_blocks(40000, 140).numpy()
         for t in (np.float32(1.0), np.float32(0.0173)):

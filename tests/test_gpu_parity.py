@@ -113,6 +113,24 @@ def adversarial_tables(seed):
     return codec.Tables(c, L)
 
 
+def incomplete_tables(seed, base=None):
+    """Codebooks with Kraft sum below 1: one to three codewords of each book
+    made one or two bits longer (at most 8), so random bits often start with
+    no codeword, where decoding stops.  Books whose lengthened codewords were
+    all 8 bits already stay complete."""
+    tb = base if base is not None else adversarial_tables(seed)
+    rng = np.random.default_rng(seed + 1000)
+    L = tb.code_len.copy()
+    for p in range(64):
+        for h in range(4):
+            for s in rng.choice(16, int(rng.integers(1, 4)), replace=False):
+                L[p, h, s] = min(8, int(L[p, h, s]) + int(rng.integers(1, 3)))
+    out = codec.Tables(tb.centroids, L)
+    ks = [oracle.huffman.kraft_sum(L[p, h]) for p in range(64) for h in range(4)]
+    assert max(ks) <= 1 and sum(k < 1 for k in ks) > 200
+    return out
+
+
 def random_tables(seed):
     rng = np.random.default_rng(seed)
     c = np.sort(rng.uniform(-1, 1, (64, 15)), axis=1).astype(np.float16).astype(np.float32)
@@ -254,6 +272,9 @@ def test_special_groups(dev):
         assert_fp16_equal(gpu_decode(o_blocks, tdev, t), codec.decode_blocks(o_blocks, tb, t), "special decode")
 
 
+QBINS_OK_AT = 108800        # byte offset of the blob's quantiser-bins flag (Tables::qbins_ok)
+
+
 def _near_threshold_groups(tb, scales, rng):
     """Groups whose values sit on the quantiser's thresholds m_k * a and on
     their FP16 neighbours: value 0 is the scale element +-a (an exact FP8
@@ -283,10 +304,10 @@ def test_quantiser_bins_at_thresholds(dev):
     crowded midpoints leave them without bins): blocks equal the oracle's."""
     rng = np.random.default_rng(23)
     tb = golden("c1")
-    assert ecco.ecco_tables_build(tb.centroids, tb.code_len)[108800] == 1          # bins on
+    assert ecco.ecco_tables_build(tb.centroids, tb.code_len)[QBINS_OK_AT] == 1          # bins on
     crowded = codec.Tables(tb.centroids.copy(), tb.code_len)
     crowded.centroids[3, 5] = crowded.centroids[3, 6] = crowded.centroids[3, 7]
-    assert ecco.ecco_tables_build(crowded.centroids, crowded.code_len)[108800] == 0  # bins off
+    assert ecco.ecco_tables_build(crowded.centroids, crowded.code_len)[QBINS_OK_AT] == 0  # bins off
     scales = (1.0, 0.0625, 4.0, 448.0, 2.0 ** -9)       # exact FP8 values: a = |x_0| with t = 1
     for name, tables in (("bins", tb), ("tree", crowded)):
         tdev = dev_tables(tables)
@@ -353,13 +374,62 @@ def test_nonfinite_groups_counted_and_contained(dev):
 
 
 def test_fuzz_decode_random_blocks(dev):
-    for name, tb in (("c1", golden("c1")), ("adversarial", adversarial_tables(5))):
+    for name, tb in (("c1", golden("c1")), ("adversarial", adversarial_tables(5)),
+                     ("incomplete", incomplete_tables(6))):
         tdev = dev_tables(tb)
         blocks = W.random_blocks(40000, 99).numpy()
         for t in (np.float32(1.0), np.float32(0.0173)):
             say("fuzz decode %s t=%g" % (name, t))
             assert_fp16_equal(gpu_decode(blocks, tdev, t), codec.decode_blocks(blocks, tb, t),
                               "fuzz %s t=%g" % (name, t))
+
+
+def test_incomplete_codebooks_encode_and_decode(dev):
+    """Trained centroids with incomplete codebooks: the GPU's blocks and
+    statistics equal the oracle's, and the blocks decode to the oracle's
+    values; so do random blocks, most of which stop at a window with no
+    codeword (k below 128, no records applied)."""
+    tb = incomplete_tables(8, base=golden("c1"))
+    tdev = dev_tables(tb)
+    x = W.c1_weight().numpy().reshape(-1, 128)
+    t = scale_of(x)
+    say("incomplete codebooks: encode %d groups" % len(x))
+    g_blocks, g_stats = gpu_encode(x, tdev, t, stats=True)
+    o_blocks, info = codec.encode_groups(x, tb, t, return_info=True)
+    assert_blocks_equal(g_blocks, o_blocks, "incomplete codebooks")
+    assert g_stats == info["stats"]
+    say("incomplete codebooks: decode")
+    assert_fp16_equal(gpu_decode(g_blocks, tdev, t), codec.decode_blocks(o_blocks, tb, t), "incomplete decode")
+    blocks = W.random_blocks(20000, 123).numpy()
+    _, dinfo = codec.decode_blocks(blocks, tb, t, return_info=True)
+    k = np.asarray(dinfo["k"])
+    assert np.mean(k < 128) > 0.5                       # most random streams stop early
+    assert_fp16_equal(gpu_decode(blocks, tdev, t), codec.decode_blocks(blocks, tb, t), "incomplete random blocks")
+
+
+@pytest.mark.parametrize("out_f,in_f,batch", [(300, 1024, 1), (64, 4096, 4), (9, 2048, 8)])
+def test_gemv_over_incomplete_codebooks(dev, out_f, in_f, batch):
+    """The fused decode+GEMV over random blocks of incomplete codebooks (many
+    streams stop early): within tolerance of the float64 product over the
+    oracle's decode."""
+    tb = incomplete_tables(9)
+    tdev = dev_tables(tb)
+    blocks = W.random_blocks(out_f * in_f // 128, 400 + out_f).numpy()
+    blocks[:, 1] = 0x38                                 # scale byte 1.0: weights of moderate size
+    t = np.float32(0.5)
+    w_hat = codec.decode_blocks(blocks, tb, t)
+    blocks[~np.all(np.isfinite(w_hat.astype(np.float32)), axis=1)] = 0   # no NaN records (an all-zero block decodes to 0)
+    x = W.c5_x(batch, in_f, seed=402).numpy()
+    say("gemv incomplete %dx%d b=%d" % (out_f, in_f, batch))
+    y = torch.full((batch, out_f), float("nan"), dtype=torch.float32, device="cuda")
+    ecco.ecco_decode_gemv(torch.from_numpy(blocks).cuda(), tdev, t, out_f, in_f,
+                          torch.from_numpy(x).cuda(), batch, y)
+    torch.cuda.synchronize()
+    w_hat = codec.decode_blocks(blocks, tb, t).reshape(out_f, in_f)
+    assert np.all(np.isfinite(w_hat.astype(np.float32)))
+    y_ref, mag = ogemv.gemv_ref(w_hat, x)
+    ok, worst = ogemv.gemv_tolerance_ok(y.cpu().numpy(), y_ref, mag, in_f)
+    assert ok, "worst error / bound = %g" % worst
 
 
 def test_kv_append_k_and_v_in_one_call(dev):

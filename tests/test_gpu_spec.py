@@ -65,6 +65,20 @@ def random_tables(seed, adversarial=False):
     return codec.Tables(c, L)
 
 
+def incomplete_tables(seed):
+    """Random lengths with one to three codewords per book made one or two
+    bits longer (at most 8): Kraft sums below 1, so random bits often start
+    with no codeword, where decoding stops."""
+    tb = random_tables(seed, adversarial=True)
+    rng = np.random.default_rng(seed + 1)
+    L = tb.code_len.copy()
+    for p in range(64):
+        for h in range(4):
+            for s in rng.choice(16, int(rng.integers(1, 4)), replace=False):
+                L[p, h, s] = min(8, int(L[p, h, s]) + int(rng.integers(1, 3)))
+    return codec.Tables(tb.centroids, L)
+
+
 SEG_LANES = (2, 4, 8)
 
 
@@ -141,7 +155,8 @@ def test_spec_special_groups(dev):
 
 
 def test_spec_random_blocks(dev):
-    for name, tb in (("c1", golden("c1")), ("adversarial", random_tables(720, adversarial=True))):
+    for name, tb in (("c1", golden("c1")), ("adversarial", random_tables(720, adversarial=True)),
+                     ("incomplete", incomplete_tables(722))):
         blocks = W.random_blocks(40000, 721).numpy()
         for t in (np.float32(1.0), np.float32(0.0173)):
             say("speculative decode, random blocks %s t=%g" % (name, t))
