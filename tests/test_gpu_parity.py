@@ -520,6 +520,15 @@ def test_decode_many_mixed_jobs_exact(dev):
     tdev = dev_tables(tb)
     bd = torch.from_numpy(bfull).cuda()
     yd = torch.full((rows * ystride,), 0x7FFF, dtype=torch.int16, device="cuda")
+    # random blocks under tables with incomplete codebooks: this job's
+    # workgroups take the decode core's stopping instance, the others not
+    tbi = incomplete_tables(10)
+    rbi = W.random_blocks(3000, 311).numpy()
+    tdi = dev_tables(tbi)
+    ydi = torch.full((3002, 128), 0x7FFF, dtype=torch.int16, device="cuda")
+    jobs.insert(2, (torch.from_numpy(rbi).cuda(), 1, 3000, 3000, 3000 * 128, tdi, np.float32(0.5), ydi[1:3001]))
+    refs.insert(2, codec.decode_blocks(rbi, tbi, np.float32(0.5)))
+    keep.insert(2, (tdi, ydi))
     jobs.append((bd, rows, gpr, bstride, ystride, tdev, t, yd))
     keep.append((tdev, yd))
     say("decode_many %d jobs" % len(jobs))
@@ -925,15 +934,28 @@ def test_ffn70b_gemv_full_size_sampled(dev, name):
 
 # ------------------------------------------------------------ fused attention
 
-def _attention_case(B, H, G, S, stride, seed):
+def _attention_case(B, H, G, S, stride, seed, incomplete=False):
     """Oracle-encoded K/V caches [B, H, stride] x 64 B (first S tokens used),
-    their oracle-decoded values, q, and the scales."""
+    their oracle-decoded values, q, and the scales.  incomplete: the V tables'
+    codebooks made incomplete, and a third of the K blocks replaced by random
+    bytes under K tables with incomplete codebooks (their streams mostly stop
+    early)."""
     tbk, tbv = golden("c3_k"), golden("c3_v")
+    if incomplete:
+        tbk, tbv = incomplete_tables(seed, base=tbk), incomplete_tables(seed + 1, base=tbv)
     tk, tv = golden_t("c3_k"), golden_t("c3_v")
     k = W.kv_tensor("k", shape=(B, H, S, 128), seed=seed).numpy()
     v = W.kv_tensor("v", shape=(B, H, S, 128), seed=seed + 1).numpy()
     kb = codec.encode_groups(k.reshape(-1, 128), tbk, tk).reshape(B, H, S, 64)
     vb = codec.encode_groups(v.reshape(-1, 128), tbv, tv).reshape(B, H, S, 64)
+    if incomplete:
+        rb = W.random_blocks(B * H * S, seed + 3).numpy().reshape(B, H, S, 64)
+        rb[..., 1] = 0x30                                   # scale byte 0.5: moderate scores
+        pick = (np.arange(S) % 3 == 1)
+        kb[:, :, pick] = rb[:, :, pick]
+        kd_chk = codec.decode_blocks(kb.reshape(-1, 64), tbk, tk)
+        bad = ~np.all(np.isfinite(kd_chk.astype(np.float32)), axis=1).reshape(B, H, S)
+        kb[bad] = codec.encode_groups(k.reshape(B, H, S, 128)[bad], tbk, tk)   # no NaN records
     kd = codec.decode_blocks(kb.reshape(-1, 64), tbk, tk).reshape(B, H, S, 128)
     vd = codec.decode_blocks(vb.reshape(-1, 64), tbv, tv).reshape(B, H, S, 128)
     full_k = np.zeros((B, H, stride, 64), np.uint8)
@@ -964,6 +986,22 @@ def test_attention_small(dev, B, H, G, S, extra):
     scale = 1.0 / np.sqrt(128.0)
     say("attention B=%d H=%d G=%d S=%d" % (B, H, G, S))
     got = _gpu_attention(c, B, H, G, S, stride, scale)
+    ref, mag = attention.attention_ref(c["kd"], c["vd"], c["q"], scale)
+    ok, worst = attention.attention_tolerance_ok(got, ref, mag)
+    assert ok, "attention outside tolerance: worst error / bound = %g" % worst
+
+
+def test_attention_incomplete_codebooks(dev):
+    """Attention over caches whose tables have incomplete codebooks (K: a third
+    of the blocks random bytes, whose streams mostly stop early): the kernels
+    take the decode core's stopping instance; within tolerance of the float64
+    oracle over the oracle's decode."""
+    from oracle import attention
+    B, H, G, S = 2, 2, 4, 700
+    c = _attention_case(B, H, G, S, S + 3, 90, incomplete=True)
+    scale = 1.0 / np.sqrt(128.0)
+    say("attention, incomplete codebooks")
+    got = _gpu_attention(c, B, H, G, S, S + 3, scale)
     ref, mag = attention.attention_ref(c["kd"], c["vd"], c["q"], scale)
     ok, worst = attention.attention_tolerance_ok(got, ref, mag)
     assert ok, "attention outside tolerance: worst error / bound = %g" % worst
