@@ -327,23 +327,35 @@ struct GroupGeom {
 
 template <int NW>
 struct DecodeSmem {
-  uint8_t lut[S * H * 256 + 256];   // decode look-up tables + the clipped-stream table
-  float cent[S * 16];
-  uint32_t blk[NW][kBlkWords];
+  alignas(16) uint8_t lut[S * H * 256 + 256];   // decode look-up tables + the clipped-stream table
+  alignas(16) float cent[S * 16];
+  alignas(16) uint32_t blk[NW][kBlkWords];
   uint32_t qsym[NW][kPassBlocks * kSymStride];
 };
 
+// The look-up tables' global loads of the full rounds are issued before the
+// first LDS write, so their latencies overlap instead of adding up one loop
+// trip at a time (NW * 64 threads at most, so each full round stays in
+// bounds; the remainder loop covers the rest at any workgroup size).
 template <int NW>
 __device__ __forceinline__ void stage_decode_tables(DecodeSmem<NW>& sm, const Tables* tab) {
-  const uint32_t tid = threadIdx.x;
+  const uint32_t tid = threadIdx.x, nt = blockDim.x;
+  constexpr uint32_t NL = S * H * 256 / 16;                  // 16-byte pieces of the look-up tables
+  constexpr uint32_t IT = NL / (NW * 64);                    // full rounds
   const uint4* src = reinterpret_cast<const uint4*>(&tab->lut[0][0][0]);
   uint4* dst = reinterpret_cast<uint4*>(sm.lut);
-  for (uint32_t i = tid; i < S * H * 256 / 16; i += blockDim.x) dst[i] = src[i];
+  uint4 v[IT];
+#pragma unroll
+  for (uint32_t k = 0; k < IT; ++k) v[k] = src[tid + k * nt];
+  for (uint32_t i = tid + IT * nt; i < NL; i += nt) dst[i] = src[i];
+  const uint4* csrc = reinterpret_cast<const uint4*>(&tab->centroids[0][0]);
+  for (uint32_t i = tid; i < S * 16 / 4; i += nt) reinterpret_cast<uint4*>(sm.cent)[i] = csrc[i];
   // a clipped stream reads as symbol 16 ("+0" in a clipped block), one bit per step
-  if (tid < 16) dst[S * H * 256 / 16 + tid] = make_uint4(0x10101010u, 0x10101010u, 0x10101010u, 0x10101010u);
-  const float* c = &tab->centroids[0][0];
-  for (uint32_t i = tid; i < S * 16; i += blockDim.x) sm.cent[i] = c[i];
-  for (uint32_t i = tid; i < NW * kBlkWords; i += blockDim.x) (&sm.blk[0][0])[i] = 0;
+  if (tid < 16) dst[NL + tid] = make_uint4(0x10101010u, 0x10101010u, 0x10101010u, 0x10101010u);
+  uint4* blk = reinterpret_cast<uint4*>(&sm.blk[0][0]);
+  for (uint32_t i = tid; i < NW * kBlkWords / 4; i += nt) blk[i] = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+  for (uint32_t k = 0; k < IT; ++k) dst[tid + k * nt] = v[k];
 }
 
 // The 64 blocks of a batch as four 16-byte chunks per lane: chunk i of lane l
