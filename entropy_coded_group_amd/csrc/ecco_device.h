@@ -269,6 +269,18 @@ __device__ __forceinline__ uint4 load_stream(const void* p) {
   return make_uint4(w.x, w.y, w.z, w.w);
 }
 
+// Index of the job whose workgroup range holds workgroup w: the number of
+// jobs after the first whose range starts at or before w (the ranges are in
+// order).  Every job's first workgroup is read at once, so the search waits
+// for one scalar load instead of one per job passed.
+template <int MAXJ, class Args>
+__device__ __forceinline__ uint32_t find_job(const Args& args, uint32_t w) {
+  uint32_t j = 0;
+#pragma unroll
+  for (int k = 1; k < MAXJ; ++k) j += ((uint32_t)k < args.n_jobs && w >= args.job[k].wg_first) ? 1u : 0u;
+  return __builtin_amdgcn_readfirstlane(j);      // uniform: the job descriptor stays in scalar registers
+}
+
 // 64-bit window shift: bits [r, r + 32) of hi:lo, r < 64.
 __device__ __forceinline__ uint32_t window(uint32_t lo, uint32_t hi, uint32_t r) {
   return (uint32_t)((((uint64_t)hi << 32) | lo) >> r);

@@ -165,6 +165,27 @@ constexpr uint32_t kOutlierSortRounds = 3;   // more outlier rounds than this: s
 // bounds test), rounded up to a multiple of 4 for the 16-byte reads.
 constexpr int kOutWords = 36;
 
+// N 16-byte pieces of a table, copied from global memory to LDS by NT
+// threads: every thread's loads first (index clamped to the last piece, so
+// each load is unconditional and the pieces stay in registers), then its
+// LDS writes.
+template <uint32_t N, uint32_t NT>
+struct Stage16 {
+  static constexpr uint32_t K = (N + NT - 1) / NT;
+  uint4 v[K];
+  __device__ __forceinline__ void load(const void* src, uint32_t tid) {
+    const uint4* p = reinterpret_cast<const uint4*>(src);
+#pragma unroll
+    for (uint32_t k = 0; k < K; ++k) v[k] = p[min(tid + k * NT, N - 1u)];
+  }
+  __device__ __forceinline__ void store(void* dst, uint32_t tid) const {
+    uint4* p = reinterpret_cast<uint4*>(dst);
+#pragma unroll
+    for (uint32_t k = 0; k < K; ++k)
+      if (tid + k * NT < N) p[tid + k * NT] = v[k];
+  }
+};
+
 // Sorts 8 keys into descending order (an optimal 19-comparator network).
 __device__ __forceinline__ void sort8_desc(uint32_t (&k)[8]) {
   auto ce = [&](int i, int j) {
@@ -181,14 +202,14 @@ __device__ __forceinline__ void sort8_desc(uint32_t (&k)[8]) {
 }
 
 struct EncodeSmem {
-  float mid[S * 16];
-  alignas(8) float c0c14[S * 2];      // pattern p's first and last centroid at 2p, 2p + 1
-  uint32_t len4[16 + S * A];         // entry (p, s) at 16 + 16 p + s: index 16 p + u for tree leaf u = 16 + s
-  uint32_t enc[16 + S * H * A];      // entry (p, h, s) at 16 + 16 (4 p + h) + s, likewise
+  alignas(16) float mid[S * 16];
+  alignas(16) float c0c14[S * 2];    // pattern p's first and last centroid at 2p, 2p + 1
+  alignas(16) uint32_t len4[16 + S * A];     // entry (p, s) at 16 + 16 p + s: index 16 p + u for tree leaf u = 16 + s
+  alignas(16) uint32_t enc[16 + S * H * A];  // entry (p, h, s) at 16 + 16 (4 p + h) + s, likewise
   float thr[kEncWaves][16][16];      // threshold tree of each group of a wave
   uint32_t out[kEncWaves][16][kOutWords];   // block words of each group of a wave (then a sink)
   alignas(16) uint8_t qbin[S * kQBins];      // quantiser bins of each pattern
-  alignas(8) float qaxis[S * 2];             // their B and C
+  alignas(16) float qaxis[S * 2];            // their B and C
   alignas(16) uint8_t pcand[kPGrid * kPGrid * kPCand];   // pattern candidates of each grid cell
 };
 
@@ -238,9 +259,7 @@ __device__ __forceinline__ float key_value(uint32_t k) { return f16_value((k >> 
 // (At least four waves per SIMD: the compiler is held to 128 VGPRs.)
 template <int GS>
 __global__ __launch_bounds__(kEncWaves * 64, 4) void encode_kernel(EncodeArgs args) {
-  uint32_t jj = 0;
-  while (jj + 1 < args.n_jobs && blockIdx.x >= args.job[jj + 1].wg_first) ++jj;
-  const EncodeJob a = args.job[jj];         // one copy, kept in scalar registers
+  const EncodeJob a = args.job[find_job<kMaxJobs>(args, blockIdx.x)];         // one copy, kept in scalar registers
   const uint32_t lw = blockIdx.x - a.wg_first;
   using Geo = GroupGeom<GS>;
   using EG = EncGeom<GS>;
@@ -251,21 +270,33 @@ __global__ __launch_bounds__(kEncWaves * 64, 4) void encode_kernel(EncodeArgs ar
   constexpr int NSLOT = 16 / LPG;           // outlier records (and thresholds) per lane
   __shared__ EncodeSmem sm;
   const uint32_t tid = threadIdx.x;
-  for (uint32_t i = tid; i < S * 16; i += blockDim.x) sm.mid[i] = (&a.tab->midpoints[0][0])[i];
-  for (uint32_t i = tid; i < S * 2; i += blockDim.x) sm.c0c14[i] = (&a.tab->c0c14[0][0])[i];
-  for (uint32_t i = tid; i < S * A; i += blockDim.x) sm.len4[16 + i] = (&a.tab->len4[0][0])[i];
-  for (uint32_t i = tid; i < S * H * A; i += blockDim.x) sm.enc[16 + i] = (&a.tab->enc[0][0][0])[i];
+  // Table staging: every global load is issued before the first LDS write,
+  // so the loads' latencies overlap (the quantiser bins are copied whether
+  // or not they are used).
+  constexpr uint32_t NT = kEncWaves * 64;
+  Stage16<S * 16 / 4, NT> st_mid;
+  Stage16<S * 2 / 4, NT> st_c;
+  Stage16<S * A / 4, NT> st_len;
+  Stage16<S * H * A / 4, NT> st_enc;
+  Stage16<S * kQBins / 16, NT> st_qb;
+  Stage16<S * 2 / 4, NT> st_qa;
+  Stage16<(GS == 64 ? kPGrid * kPGrid * kPCand / 16 : 1), NT> st_pc;
+  st_mid.load(&a.tab->midpoints[0][0], tid);
+  st_c.load(&a.tab->c0c14[0][0], tid);
+  st_len.load(&a.tab->len4[0][0], tid);
+  st_enc.load(&a.tab->enc[0][0][0], tid);
+  st_qb.load(&a.tab->qbin[0][0], tid);
+  st_qa.load(&a.tab->qaxis[0][0], tid);
+  if constexpr (GS == 64) st_pc.load(&a.tab->pcand[0][0], tid);
   const bool qbins_ok = a.tab->qbins_ok != 0u;
   const float4 pgrid = make_float4(a.tab->pgrid[0], a.tab->pgrid[1], a.tab->pgrid[2], a.tab->pgrid[3]);
-  if (qbins_ok) {
-    for (uint32_t i = tid; i < S * kQBins / 16; i += blockDim.x)
-      reinterpret_cast<uint4*>(sm.qbin)[i] = reinterpret_cast<const uint4*>(&a.tab->qbin[0][0])[i];
-    for (uint32_t i = tid; i < S * 2; i += blockDim.x) sm.qaxis[i] = (&a.tab->qaxis[0][0])[i];
-  }
-  if constexpr (GS == 64) {
-    for (uint32_t i = tid; i < kPGrid * kPGrid * kPCand / 16; i += blockDim.x)
-      reinterpret_cast<uint4*>(sm.pcand)[i] = reinterpret_cast<const uint4*>(&a.tab->pcand[0][0])[i];
-  }
+  st_mid.store(sm.mid, tid);
+  st_c.store(sm.c0c14, tid);
+  st_len.store(sm.len4 + 16, tid);
+  st_enc.store(sm.enc + 16, tid);
+  st_qb.store(sm.qbin, tid);
+  st_qa.store(sm.qaxis, tid);
+  if constexpr (GS == 64) st_pc.store(sm.pcand, tid);
   __syncthreads();
 
   const uint32_t lane = lane_id(), wave = tid >> 6;
